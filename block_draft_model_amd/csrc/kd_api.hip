@@ -1,0 +1,562 @@
+// C ABI of libkdraft: context, load-time weight repacking, workspace and the
+// launch sequences of a round and of a context ingest.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "../../include/kdraft.h"
+#include "../../include/kdraft_debug.h"
+#include "kd_device.h"
+#include "kd_runtime.h"
+
+struct kd_ctx {
+  kd_config cfg{};
+  hipStream_t stream = nullptr;
+  int device = 0;
+  kd::Work w;
+  kd::DevWeights d;
+  std::vector<void*> work_allocs;
+  std::vector<void*> weight_allocs;
+  bool loaded = false;
+  int debug_layers = -1;
+  int last_streams = 0;
+  std::string err;
+};
+
+namespace {
+
+kd_status fail(kd_ctx* c, kd_status s, const std::string& msg) {
+  if (c) c->err = msg;
+  return s;
+}
+
+kd_status hip_fail(kd_ctx* c, hipError_t e, const char* what) {
+  return fail(c, KD_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+template <typename T>
+bool dev_alloc(std::vector<void*>& list, T** p, size_t elems) {
+  void* q = nullptr;
+  if (hipMalloc(&q, std::max<size_t>(elems * sizeof(T), 256)) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  list.push_back(q);
+  *p = static_cast<T*>(q);
+  return true;
+}
+
+void free_all(std::vector<void*>& list) {
+  for (void* p : list) (void)hipFree(p);
+  list.clear();
+}
+
+bool shape_is_supported(const kd_config& c) {
+  return c.hidden == kd::H && c.heads == kd::NH && c.head_dim == kd::DH && c.ffn == kd::FF &&
+         c.layers == kd::NL && c.block == kd::BLK && c.rank == kd::RK && c.taps == kd::NTAP;
+}
+
+// The GEMM calls a round and an ingest make, as (K, N, rows per stream).
+struct GemmUse {
+  int K, N, rows_per_stream;
+};
+const GemmUse kRoundUses[] = {
+    {kd::NTAP * kd::H, kd::H, 1}, {2 * kd::H, kd::H, 1},  {2 * kd::H, kd::RK, 3},
+    {kd::RK, kd::H, 3},           {kd::H, kd::RK, 3},     {kd::H, kd::QKV, 4},
+    {kd::H, kd::H, 4},            {kd::H, kd::GU, 4},     {kd::FF, kd::H, 4}};
+const GemmUse kIngestUses[] = {
+    {kd::NTAP * kd::H, kd::H, 1}, {2 * kd::H, kd::H, 1}, {kd::H, 2 * kd::H, 1}};
+
+size_t part_region_elems(int Bmax) {
+  size_t best = 0;
+  for (int B = 1; B <= Bmax; ++B) {
+    for (const GemmUse& u : kRoundUses) {
+      const int R = B * u.rows_per_stream;
+      best = std::max(best, (size_t)kd::gemm_splits(u.K, u.N, R) * R * u.N);
+    }
+    for (int n = 1; n <= KD_MAX_INGEST; ++n)
+      for (const GemmUse& u : kIngestUses) {
+        const int R = B * n;
+        best = std::max(best, (size_t)kd::gemm_splits(u.K, u.N, R) * R * u.N);
+      }
+  }
+  return best;
+}
+
+// Block-FP8 repack (layout documented in kd_device.h). q: [N][K], s: [N][K/64].
+void repack_fp8(const uint8_t* q, const float* s, int N, int K, uint8_t* wo, float* so) {
+  const int KB = K / 64;
+  for (int nt = 0; nt < N / 16; ++nt)
+    for (int b = 0; b < KB; ++b) {
+      uint8_t* dst = wo + ((size_t)nt * KB + b) * 1024;
+      for (int lane = 0; lane < 64; ++lane) {
+        const int n = nt * 16 + (lane & 15), g = lane >> 4;
+        const uint8_t* src = q + (size_t)n * K + 64 * b + 8 * g;
+        memcpy(dst + lane * 16, src, 8);
+        memcpy(dst + lane * 16 + 8, src + 32, 8);
+      }
+      for (int j = 0; j < 16; ++j) so[((size_t)nt * KB + b) * 16 + j] = s[(size_t)(nt * 16 + j) * KB + b];
+    }
+}
+
+bool fp8_codes_ok(const uint8_t* q, size_t n) {
+  for (size_t i = 0; i < n; ++i)
+    if ((q[i] & 0x7f) == 0x7f) return false;
+  return true;
+}
+bool floats_ok(const float* s, size_t n) {
+  for (size_t i = 0; i < n; ++i)
+    if (!std::isfinite(s[i])) return false;
+  return true;
+}
+
+// Host staging of a (possibly concatenated) block-FP8 matrix before upload.
+struct HostMat {
+  std::vector<uint8_t> q;
+  std::vector<float> s;
+  int N = 0, K = 0;
+};
+
+bool append_rows(HostMat& m, const kd_fp8_matrix& src, int rows, int cols) {
+  if (!src.q || !src.s) return false;
+  if (m.K == 0) m.K = cols;
+  if (m.K != cols) return false;
+  if (!fp8_codes_ok(src.q, (size_t)rows * cols) || !floats_ok(src.s, (size_t)rows * cols / 64))
+    return false;
+  m.q.insert(m.q.end(), src.q, src.q + (size_t)rows * cols);
+  m.s.insert(m.s.end(), src.s, src.s + (size_t)rows * cols / 64);
+  m.N += rows;
+  return true;
+}
+
+// [a | b] along the input dimension (same row count).
+bool concat_cols(HostMat& m, const kd_fp8_matrix& a, const kd_fp8_matrix& b, int rows, int ca,
+                 int cb) {
+  if (!a.q || !a.s || !b.q || !b.s) return false;
+  if (!fp8_codes_ok(a.q, (size_t)rows * ca) || !fp8_codes_ok(b.q, (size_t)rows * cb) ||
+      !floats_ok(a.s, (size_t)rows * ca / 64) || !floats_ok(b.s, (size_t)rows * cb / 64))
+    return false;
+  m.N = rows;
+  m.K = ca + cb;
+  m.q.resize((size_t)rows * m.K);
+  m.s.resize((size_t)rows * m.K / 64);
+  for (int r = 0; r < rows; ++r) {
+    memcpy(&m.q[(size_t)r * m.K], a.q + (size_t)r * ca, ca);
+    memcpy(&m.q[(size_t)r * m.K + ca], b.q + (size_t)r * cb, cb);
+    memcpy(&m.s[(size_t)r * m.K / 64], a.s + (size_t)r * ca / 64, ca / 64 * sizeof(float));
+    memcpy(&m.s[(size_t)r * m.K / 64 + ca / 64], b.s + (size_t)r * cb / 64,
+           cb / 64 * sizeof(float));
+  }
+  return true;
+}
+
+kd_status upload_mat(kd_ctx* c, const HostMat& m, kd::Fp8Mat* out) {
+  std::vector<uint8_t> wq((size_t)m.N * m.K);
+  std::vector<float> ws((size_t)m.N * m.K / 64);
+  repack_fp8(m.q.data(), m.s.data(), m.N, m.K, wq.data(), ws.data());
+  uint8_t* dw;
+  float* ds;
+  if (!dev_alloc(c->weight_allocs, &dw, wq.size()) || !dev_alloc(c->weight_allocs, &ds, ws.size()))
+    return fail(c, KD_ERR_OOM, "weight allocation failed");
+  hipError_t e = hipMemcpy(dw, wq.data(), wq.size(), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(ds, ws.data(), ws.size() * sizeof(float), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(c, e, "weight upload");
+  out->w = dw;
+  out->s = ds;
+  out->N = m.N;
+  out->K = m.K;
+  return KD_OK;
+}
+
+kd_status upload_vec(kd_ctx* c, const float* src, size_t n, const float** out) {
+  if (!src) return fail(c, KD_ERR_ARG, "NULL vector in weights");
+  if (!floats_ok(src, n)) return fail(c, KD_ERR_ARG, "non-finite vector in weights");
+  float* d;
+  if (!dev_alloc(c->weight_allocs, &d, n)) return fail(c, KD_ERR_OOM, "weight allocation failed");
+  hipError_t e = hipMemcpy(d, src, n * sizeof(float), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(c, e, "weight upload");
+  *out = d;
+  return KD_OK;
+}
+
+kd::KV make_kv(const kd_kv* kv) {
+  kd::KV k;
+  for (int l = 0; l < 4; ++l) {
+    k.k[l] = static_cast<const uint16_t*>(kv->k[l]);
+    k.v[l] = static_cast<const uint16_t*>(kv->v[l]);
+  }
+  k.ss = kv->stride_stream;
+  k.sh = kv->stride_head;
+  k.sl = kv->stride_slot;
+  k.cap = kv->capacity;
+  return k;
+}
+
+kd_status check_kv(kd_ctx* c, const kd_kv* kv) {
+  if (!kv) return fail(c, KD_ERR_ARG, "ctx_kv is NULL");
+  for (int l = 0; l < 4; ++l)
+    if (!kv->k[l] || !kv->v[l]) return fail(c, KD_ERR_ARG, "NULL K/V tensor");
+  if (kv->capacity < c->cfg.window)
+    return fail(c, KD_ERR_ARG, "K/V capacity is smaller than the window");
+  if (kv->stride_slot < kd::DH || kv->stride_head < 1 || kv->stride_stream < 1)
+    return fail(c, KD_ERR_ARG, "bad K/V strides");
+  for (int l = 0; l < 4; ++l)
+    if ((reinterpret_cast<uintptr_t>(kv->k[l]) | reinterpret_cast<uintptr_t>(kv->v[l])) & 15)
+      return fail(c, KD_ERR_ARG, "K/V tensors must be 16-byte aligned");
+  if ((kv->stride_slot | kv->stride_head | kv->stride_stream) & 7)
+    return fail(c, KD_ERR_ARG, "K/V strides must be multiples of 8 elements");
+  return KD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void kd_default_config(kd_config* cfg) {
+  if (!cfg) return;
+  cfg->hidden = kd::H;
+  cfg->heads = kd::NH;
+  cfg->head_dim = kd::DH;
+  cfg->ffn = kd::FF;
+  cfg->layers = kd::NL;
+  cfg->block = kd::BLK;
+  cfg->rank = kd::RK;
+  cfg->taps = kd::NTAP;
+  cfg->window = 2048;
+  cfg->draft_vocab = 60614;
+  cfg->full_vocab = 131072;
+  cfg->max_streams = 256;
+  cfg->rope_theta = 10000.0f;
+  cfg->rms_eps = 1e-6f;
+  cfg->body_quant = KD_QUANT_FP8_BLOCK64;
+  cfg->head_quant = KD_QUANT_NVFP4;
+}
+
+const char* kd_status_string(kd_status s) {
+  switch (s) {
+    case KD_OK: return "ok";
+    case KD_ERR_ARG: return "invalid argument";
+    case KD_ERR_STATE: return "invalid state";
+    case KD_ERR_OOM: return "out of device memory";
+    case KD_ERR_HIP: return "HIP runtime error";
+    case KD_ERR_UNSUPPORTED: return "unsupported configuration";
+  }
+  return "unknown status";
+}
+
+const char* kd_last_error(const kd_ctx* ctx) { return ctx ? ctx->err.c_str() : ""; }
+
+kd_status kd_create(const kd_config* cfg, void* hip_stream, kd_ctx** out) {
+  if (!out) return KD_ERR_ARG;
+  *out = nullptr;
+  if (!cfg) return KD_ERR_ARG;
+  if (!shape_is_supported(*cfg)) return KD_ERR_UNSUPPORTED;
+  if (cfg->body_quant != KD_QUANT_FP8_BLOCK64 || cfg->head_quant != KD_QUANT_NVFP4)
+    return KD_ERR_UNSUPPORTED;
+  if (cfg->window < 1 || cfg->draft_vocab < 1 || cfg->full_vocab < 1 || cfg->max_streams < 1 ||
+      !(cfg->rms_eps >= 0.f) || !(cfg->rope_theta > 0.f))
+    return KD_ERR_ARG;
+  if (cfg->max_streams > (1 << 20) || cfg->draft_vocab > (1 << 28) || cfg->window > (1 << 24))
+    return KD_ERR_OOM;
+  kd_ctx* c = new kd_ctx;
+  c->cfg = *cfg;
+  c->stream = static_cast<hipStream_t>(hip_stream);
+  (void)hipGetDevice(&c->device);
+  kd::Work& w = c->w;
+  w.Bmax = cfg->max_streams;
+  w.Rmax = kd::BLK * w.Bmax;
+  w.Imax = KD_MAX_INGEST * w.Bmax;
+  w.att_nch = (cfg->window + kd::ATT_CH - 1) / kd::ATT_CH;
+  const int BI = std::max(w.Bmax, w.Imax), RI = std::max(w.Rmax, w.Imax);
+  w.part_elems = 2 * part_region_elems(w.Bmax);
+  bool ok = dev_alloc(c->work_allocs, &w.f, (size_t)BI * kd::H) &&
+            dev_alloc(c->work_allocs, &w.x, (size_t)w.Rmax * kd::H) &&
+            dev_alloc(c->work_allocs, &w.c, (size_t)w.Imax * kd::H) &&
+            dev_alloc(c->work_allocs, &w.part, w.part_elems) &&
+            dev_alloc(c->work_allocs, &w.af_in, kd::afrag_elems(BI, kd::NTAP * kd::H)) &&
+            dev_alloc(c->work_allocs, &w.af_fc, kd::afrag_elems(BI, 2 * kd::H)) &&
+            dev_alloc(c->work_allocs, &w.af_ab, kd::afrag_elems(3 * w.Bmax, 2 * kd::H)) &&
+            dev_alloc(c->work_allocs, &w.af_rank, kd::afrag_elems(3 * w.Bmax, kd::RK)) &&
+            dev_alloc(c->work_allocs, &w.af_x, kd::afrag_elems(RI, kd::H)) &&
+            dev_alloc(c->work_allocs, &w.af_sp, kd::afrag_elems(3 * w.Bmax, kd::H)) &&
+            dev_alloc(c->work_allocs, &w.af_h, kd::afrag_elems(w.Rmax, kd::FF)) &&
+            dev_alloc(c->work_allocs, &w.af_o, kd::afrag_elems(w.Rmax, kd::H)) &&
+            dev_alloc(c->work_allocs, &w.q, (size_t)w.Rmax * kd::H) &&
+            dev_alloc(c->work_allocs, &w.kb, (size_t)w.Rmax * kd::H) &&
+            dev_alloc(c->work_allocs, &w.vb, (size_t)w.Rmax * kd::H) &&
+            dev_alloc(c->work_allocs, &w.rope, (size_t)w.Bmax * kd::BLK * kd::DH) &&
+            dev_alloc(c->work_allocs, &w.att_m, (size_t)w.Bmax * kd::NH * w.att_nch * kd::BLK) &&
+            dev_alloc(c->work_allocs, &w.att_l, (size_t)w.Bmax * kd::NH * w.att_nch * kd::BLK) &&
+            dev_alloc(c->work_allocs, &w.att_o,
+                      (size_t)w.Bmax * kd::NH * w.att_nch * kd::BLK * kd::DH) &&
+            dev_alloc(c->work_allocs, &w.keys, (size_t)w.Rmax);
+  if (!ok) {
+    free_all(c->work_allocs);
+    delete c;
+    return KD_ERR_OOM;
+  }
+  *out = c;
+  return KD_OK;
+}
+
+kd_status kd_set_stream(kd_ctx* ctx, void* hip_stream) {
+  if (!ctx) return KD_ERR_ARG;
+  ctx->stream = static_cast<hipStream_t>(hip_stream);
+  return KD_OK;
+}
+
+void kd_destroy(kd_ctx* ctx) {
+  if (!ctx) return;
+  (void)hipStreamSynchronize(ctx->stream);
+  free_all(ctx->work_allocs);
+  free_all(ctx->weight_allocs);
+  delete ctx;
+}
+
+kd_status kd_load_weights(kd_ctx* c, const kd_weights* wt) {
+  if (!c) return KD_ERR_ARG;
+  if (!wt) return fail(c, KD_ERR_ARG, "weights is NULL");
+  const int H = kd::H, F = kd::FF, r = kd::RK;
+  const int VD = c->cfg.draft_vocab;
+  if (!wt->head_q4 || !wt->head_s4 || !wt->draft_vocab || !wt->embed_table || !wt->mask_row ||
+      !wt->final_norm)
+    return fail(c, KD_ERR_ARG, "NULL pointer in weights");
+  if (!std::isfinite(wt->head_g)) return fail(c, KD_ERR_ARG, "non-finite head scale");
+  for (int i = 0; i < VD; ++i)
+    if (wt->draft_vocab[i] < 0 || wt->draft_vocab[i] >= c->cfg.full_vocab)
+      return fail(c, KD_ERR_ARG, "draft vocabulary id out of range");
+  (void)hipStreamSynchronize(c->stream);
+  free_all(c->weight_allocs);
+  c->loaded = false;
+  kd::DevWeights& d = c->d;
+
+  kd_status st;
+  {
+    HostMat m;
+    if (!append_rows(m, wt->fuse, H, kd::NTAP * H)) return fail(c, KD_ERR_ARG, "bad fuse matrix");
+    if ((st = upload_mat(c, m, &d.fuse)) != KD_OK) return st;
+  }
+  {
+    HostMat m;
+    if (!append_rows(m, wt->fc, H, 2 * H)) return fail(c, KD_ERR_ARG, "bad fc matrix");
+    if ((st = upload_mat(c, m, &d.fc)) != KD_OK) return st;
+  }
+  {
+    HostMat m;
+    if (!concat_cols(m, wt->pred_a, wt->pred_b, r, H, H))
+      return fail(c, KD_ERR_ARG, "bad predecessor A/B matrix");
+    if ((st = upload_mat(c, m, &d.pred_ab)) != KD_OK) return st;
+  }
+  {
+    HostMat m;
+    if (!append_rows(m, wt->pred_u, H, r)) return fail(c, KD_ERR_ARG, "bad predecessor U matrix");
+    if ((st = upload_mat(c, m, &d.pred_u)) != KD_OK) return st;
+  }
+  if ((st = upload_vec(c, wt->mask_row, H, &d.mask)) != KD_OK) return st;
+  for (int l = 0; l < kd::NL; ++l) {
+    const kd_layer_weights& L = wt->layer[l];
+    kd::DevLayer& D = d.layer[l];
+    HostMat qkv, wo, gu, dn;
+    if (!append_rows(qkv, L.wq, H, H) || !append_rows(qkv, L.wk, H, H) ||
+        !append_rows(qkv, L.wv, H, H))
+      return fail(c, KD_ERR_ARG, "bad q/k/v matrix");
+    if (!append_rows(wo, L.wo, H, H)) return fail(c, KD_ERR_ARG, "bad o matrix");
+    if (!append_rows(gu, L.w_gate, F, H) || !append_rows(gu, L.w_up, F, H))
+      return fail(c, KD_ERR_ARG, "bad gate/up matrix");
+    if (!append_rows(dn, L.w_down, H, F)) return fail(c, KD_ERR_ARG, "bad down matrix");
+    if ((st = upload_mat(c, qkv, &D.qkv)) != KD_OK || (st = upload_mat(c, wo, &D.wo)) != KD_OK ||
+        (st = upload_mat(c, gu, &D.gu)) != KD_OK || (st = upload_mat(c, dn, &D.down)) != KD_OK)
+      return st;
+    if ((st = upload_vec(c, L.attn_norm, H, &D.attn_norm)) != KD_OK ||
+        (st = upload_vec(c, L.ffn_norm, H, &D.ffn_norm)) != KD_OK)
+      return st;
+    if (l >= 1) {
+      HostMat sa, su;
+      if (!append_rows(sa, L.spine_a, r, H) || !append_rows(su, L.spine_u, H, r))
+        return fail(c, KD_ERR_ARG, "bad spine matrix");
+      if ((st = upload_mat(c, sa, &D.sa)) != KD_OK || (st = upload_mat(c, su, &D.su)) != KD_OK)
+        return st;
+      if ((st = upload_vec(c, L.spine_norm, H, &D.spine_norm)) != KD_OK) return st;
+    }
+  }
+  if ((st = upload_vec(c, wt->final_norm, H, &d.final_norm)) != KD_OK) return st;
+
+  // NVFP4 head, repacked to 16-row vocab tiles (layout in kd_device.h).
+  const int VT = (VD + 15) / 16, KG = H / 128;
+  for (size_t i = 0; i < (size_t)VD * H / 16; ++i)
+    if ((wt->head_s4[i] & 0x7f) == 0x7f) return fail(c, KD_ERR_ARG, "NaN head block scale");
+  std::vector<uint8_t> hq((size_t)VT * KG * 64 * 16, 0), hs((size_t)VT * KG * 64 * 4, 0);
+  for (int vt = 0; vt < VT; ++vt)
+    for (int kg = 0; kg < KG; ++kg)
+      for (int lane = 0; lane < 64; ++lane) {
+        const int row = vt * 16 + (lane & 15), g = lane >> 4;
+        if (row >= VD) continue;
+        const size_t o = ((size_t)vt * KG + kg) * 64 + lane;
+        for (int i = 0; i < 4; ++i) {
+          const int kbase = 32 * (4 * kg + i) + 8 * g;
+          memcpy(&hq[o * 16 + 4 * i], wt->head_q4 + (size_t)row * (H / 2) + kbase / 2, 4);
+          hs[o * 4 + i] = wt->head_s4[(size_t)row * (H / 16) + kbase / 16];
+        }
+      }
+  uint8_t *dq, *ds;
+  int32_t* dv;
+  if (!dev_alloc(c->weight_allocs, &dq, hq.size()) || !dev_alloc(c->weight_allocs, &ds, hs.size()) ||
+      !dev_alloc(c->weight_allocs, &dv, (size_t)VD))
+    return fail(c, KD_ERR_OOM, "weight allocation failed");
+  hipError_t e = hipMemcpy(dq, hq.data(), hq.size(), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(ds, hs.data(), hs.size(), hipMemcpyHostToDevice);
+  if (e == hipSuccess)
+    e = hipMemcpy(dv, wt->draft_vocab, (size_t)VD * sizeof(int32_t), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(c, e, "head upload");
+  d.hq = dq;
+  d.hs = ds;
+  d.hg = wt->head_g;
+  d.VD = VD;
+  d.VT = VT;
+  d.vocab = dv;
+  d.table = static_cast<const uint16_t*>(wt->embed_table);
+  c->loaded = true;
+  c->err.clear();
+  return KD_OK;
+}
+
+kd_status kd_round(kd_ctx* c, int B, const void* taps, const int32_t* anchor, const int32_t* pred,
+                   const kd_kv* kv, const int32_t* lens, int32_t* out_ids, float* out_logits) {
+  if (!c) return KD_ERR_ARG;
+  if (!c->loaded) return fail(c, KD_ERR_STATE, "kd_round before kd_load_weights");
+  if (B < 1 || B > c->cfg.max_streams) return fail(c, KD_ERR_ARG, "streams out of range");
+  if (!taps || !anchor || !pred || !lens || !out_ids)
+    return fail(c, KD_ERR_ARG, "NULL device pointer");
+  if (reinterpret_cast<uintptr_t>(taps) & 15)
+    return fail(c, KD_ERR_ARG, "tapped_states must be 16-byte aligned");
+  kd_status s = check_kv(c, kv);
+  if (s != KD_OK) return s;
+  const kd::KV k = make_kv(kv);
+  const kd::Work& w = c->w;
+  const kd::DevWeights& d = c->d;
+  const hipStream_t st = c->stream;
+  const float eps = c->cfg.rms_eps;
+  const int R = kd::BLK * B, B3 = 3 * B;
+  float* partA = w.part;
+  float* partB = w.part + w.part_elems / 2;
+  const int nl = c->debug_layers < 0 ? kd::NL : c->debug_layers;
+  (void)hipGetLastError();
+
+  kd::launch_prep(st, w, d, B, static_cast<const uint16_t*>(taps), lens, c->cfg.rope_theta);
+  const int s_fuse = kd::gemm_splits(d.fuse.K, d.fuse.N, B);
+  kd::launch_gemm(st, w.af_in, B, d.fuse, 0, d.fuse.N, partA, s_fuse);
+  kd::launch_post_fuse(st, w, d, B, s_fuse, anchor, pred);
+  const int s_fc = kd::gemm_splits(d.fc.K, d.fc.N, B);
+  kd::launch_gemm(st, w.af_fc, B, d.fc, 0, d.fc.N, partA, s_fc);
+  const int s_ab = kd::gemm_splits(d.pred_ab.K, d.pred_ab.N, B3);
+  kd::launch_gemm(st, w.af_ab, B3, d.pred_ab, 0, d.pred_ab.N, partB, s_ab);
+  kd::launch_silu_rank(st, partB, s_ab, B3, w.af_rank);
+  const int s_u = kd::gemm_splits(d.pred_u.K, d.pred_u.N, B3);
+  kd::launch_gemm(st, w.af_rank, B3, d.pred_u, 0, d.pred_u.N, partB, s_u);
+  kd::launch_rowbuild(st, w, d, B, s_fc, s_u, d.layer[0].attn_norm, eps);
+
+  for (int l = 0; l < nl; ++l) {
+    const kd::DevLayer& L = d.layer[l];
+    if (l >= 1) {
+      const int s_sa = kd::gemm_splits(L.sa.K, L.sa.N, B3);
+      kd::launch_gemm(st, w.af_sp, B3, L.sa, 0, L.sa.N, partA, s_sa);
+      kd::launch_silu_rank(st, partA, s_sa, B3, w.af_rank);
+      const int s_su = kd::gemm_splits(L.su.K, L.su.N, B3);
+      kd::launch_gemm(st, w.af_rank, B3, L.su, 0, L.su.N, partA, s_su);
+      kd::launch_spine_add_norm(st, w, B, s_su, L.attn_norm, eps);
+    }
+    const int s_qkv = kd::gemm_splits(L.qkv.K, L.qkv.N, R);
+    kd::launch_gemm(st, w.af_x, R, L.qkv, 0, L.qkv.N, partA, s_qkv);
+    kd::launch_qkv_post(st, w, B, s_qkv);
+    kd::launch_attention(st, w, B, k, l, lens, c->cfg.window);
+    const int s_o = kd::gemm_splits(L.wo.K, L.wo.N, R);
+    kd::launch_gemm(st, w.af_o, R, L.wo, 0, L.wo.N, partA, s_o);
+    kd::launch_resid_norm(st, w, R, s_o, L.ffn_norm, eps, w.af_x, 0);
+    const int s_gu = kd::gemm_splits(L.gu.K, L.gu.N, R);
+    kd::launch_gemm(st, w.af_x, R, L.gu, 0, L.gu.N, partA, s_gu);
+    kd::launch_swiglu(st, w, R, s_gu);
+    const int s_d = kd::gemm_splits(L.down.K, L.down.N, R);
+    kd::launch_gemm(st, w.af_h, R, L.down, 0, L.down.N, partA, s_d);
+    if (l + 1 < nl)
+      kd::launch_resid_norm(st, w, R, s_d, d.layer[l + 1].spine_norm, eps, w.af_sp, 1);
+    else
+      kd::launch_resid_norm(st, w, R, s_d, d.final_norm, eps, w.af_x, 0);
+  }
+  if (nl == 0) kd::launch_norm_rows(st, w.x, R, d.final_norm, eps, w.af_x);
+  kd::launch_head(st, w, d, R, out_logits);
+  kd::launch_finalize(st, w, d, R, out_ids);
+  c->last_streams = B;
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(c, e, "kd_round launch");
+  return KD_OK;
+}
+
+kd_status kd_ingest(kd_ctx* c, int B, int n_new, const void* taps, const int32_t* next_ids,
+                    const kd_kv* kv, int32_t* lens) {
+  if (!c) return KD_ERR_ARG;
+  if (!c->loaded) return fail(c, KD_ERR_STATE, "kd_ingest before kd_load_weights");
+  if (B < 1 || B > c->cfg.max_streams) return fail(c, KD_ERR_ARG, "streams out of range");
+  if (n_new < 1 || n_new > KD_MAX_INGEST) return fail(c, KD_ERR_ARG, "n_new out of range");
+  if (!taps || !next_ids || !lens) return fail(c, KD_ERR_ARG, "NULL device pointer");
+  if (reinterpret_cast<uintptr_t>(taps) & 15)
+    return fail(c, KD_ERR_ARG, "taps must be 16-byte aligned");
+  kd_status s = check_kv(c, kv);
+  if (s != KD_OK) return s;
+  const kd::KV k = make_kv(kv);
+  const kd::Work& w = c->w;
+  const kd::DevWeights& d = c->d;
+  const hipStream_t st = c->stream;
+  const int rows = B * n_new;
+  (void)hipGetLastError();
+  kd::launch_ingest_prep(st, w, rows, static_cast<const uint16_t*>(taps));
+  const int s_fuse = kd::gemm_splits(d.fuse.K, d.fuse.N, rows);
+  kd::launch_gemm(st, w.af_in, rows, d.fuse, 0, d.fuse.N, w.part, s_fuse);
+  kd::launch_ingest_post_fuse(st, w, d, rows, s_fuse, next_ids);
+  const int s_fc = kd::gemm_splits(d.fc.K, d.fc.N, rows);
+  kd::launch_gemm(st, w.af_fc, rows, d.fc, 0, d.fc.N, w.part, s_fc);
+  kd::launch_ingest_c(st, w, rows, s_fc);
+  for (int l = 0; l < kd::NL; ++l) {
+    const kd::DevLayer& L = d.layer[l];
+    kd::launch_norm_rows(st, w.c, rows, L.attn_norm, c->cfg.rms_eps, w.af_x);
+    const int s_kv = kd::gemm_splits(L.qkv.K, 2 * kd::H, rows);
+    kd::launch_gemm(st, w.af_x, rows, L.qkv, kd::H / 16, 2 * kd::H, w.part, s_kv);
+    kd::launch_ingest_store(st, w, B, n_new, s_kv, k, l, lens, c->cfg.rope_theta);
+  }
+  kd::launch_bump_lens(st, lens, B, n_new);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(c, e, "kd_ingest launch");
+  return KD_OK;
+}
+
+// ---- debug / probes ----
+
+kd_status kd_probe_decode_e4m3(uint16_t* out) {
+  if (!out) return KD_ERR_ARG;
+  kd::launch_probe_e4m3(nullptr, out);
+  return hipDeviceSynchronize() == hipSuccess ? KD_OK : KD_ERR_HIP;
+}
+
+kd_status kd_probe_decode_nvfp4(uint16_t* out) {
+  if (!out) return KD_ERR_ARG;
+  kd::launch_probe_nvfp4(nullptr, out);
+  return hipDeviceSynchronize() == hipSuccess ? KD_OK : KD_ERR_HIP;
+}
+
+kd_status kd_debug_set_layers(kd_ctx* c, int n) {
+  if (!c) return KD_ERR_ARG;
+  if (n > kd::NL) return fail(c, KD_ERR_ARG, "more layers than the model has");
+  c->debug_layers = n < 0 ? -1 : n;
+  return KD_OK;
+}
+
+kd_status kd_debug_buffers(kd_ctx* c, const float** hidden, const float** fused) {
+  if (!c || !hidden || !fused) return KD_ERR_ARG;
+  *hidden = c->w.x;
+  *fused = c->w.f;
+  return KD_OK;
+}
+
+}  // extern "C"

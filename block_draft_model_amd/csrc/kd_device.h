@@ -1,0 +1,175 @@
+// Device-side building blocks of libkdraft for gfx950 (CDNA4).
+//
+// Data layouts shared by the kernels:
+//
+//  * Activation fragments ("afrag"): an activation matrix X[R][K] (fp32 in
+//    value) is stored as two bf16 planes, hi = bf16(x) and lo = bf16(x - hi),
+//    arranged as the A operand of v_mfma_f32_16x16x32_bf16. For row tile mt
+//    (16 rows) and k tile t (32 inputs) the plane holds 64 lanes x 8 bf16;
+//    lane l, element e is X[16*mt + l%16][32*t + 8*(l/16) + e]. Element offset
+//    of (mt, t): ((mt*KT + t)*2 + plane) * 512 with KT = K/32. hi + lo carries
+//    ~16 significant bits, so each product with an exact bf16 weight keeps
+//    fp32-level accuracy at twice the (cheap) matrix-core work.
+//
+//  * Block-FP8 weights W[N][K] are repacked once at load to the B operand of
+//    the same instruction: [N/16][K/64][64 lanes][16 bytes]. Lane l's 16 bytes
+//    are W[16*nt + l%16][64*b + 8*(l/16) + e] for e = 0..7 (k tile 2b), then
+//    the same for k tile 2b+1 (+32). Scales: [N/16][K/64][16] fp32.
+//
+//  * NVFP4 head rows are repacked to [V/16][K/128][64 lanes][16 bytes] of
+//    e2m1 nibbles (lane l, k tile t = 4*g + i: bytes 4i..4i+3 hold
+//    W[16*vt + l%16][32*t + 8*(l/16) + e], e = 0..7, even e in the low
+//    nibble) and [V/16][K/128][64][4] e4m3 scale codes (byte i is the scale of
+//    the 16-input block holding those 8 values).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kd {
+
+constexpr int H = 2560;      // hidden
+constexpr int NH = 20;       // heads
+constexpr int DH = 128;      // head dim
+constexpr int FF = 6144;     // SwiGLU width
+constexpr int NL = 4;        // layers
+constexpr int BLK = 4;       // block rows per stream
+constexpr int RK = 256;      // adapter rank
+constexpr int NTAP = 3;      // tapped target layers
+constexpr int QKV = 3 * H;   // fused q|k|v output width
+constexpr int GU = 2 * FF;   // fused gate|up output width
+constexpr int ATT_CH = 128;  // context keys per attention workgroup
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t f2u(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ float u2f(uint32_t x) { return __builtin_bit_cast(float, x); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  uint32_t u = f2u(x);
+  if ((u & 0x7f800000u) == 0x7f800000u) return (u >> 16) | ((u & 0xffffu) ? 0x40u : 0u);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return u2f(b << 16); }
+
+// Two fp32 values whose low 16 bits are zero -> packed bf16x2 (element 0 low).
+__device__ __forceinline__ uint32_t pack_hi16(float e0, float e1) {
+  return __builtin_amdgcn_perm(f2u(e1), f2u(e0), 0x07060302u);
+}
+
+// 8 e4m3 codes (little-endian in two dwords) -> 8 exact bf16 values.
+// v_cvt_pk_f32_fp8 decodes OCP e4m3 on gfx950; every e4m3 value has at most
+// 4 significant bits, so the bf16 truncation below is exact.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+  f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
+  f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
+  f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+  f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+  u32x4 r;
+  r.x = pack_hi16(a.x, a.y);
+  r.y = pack_hi16(b.x, b.y);
+  r.z = pack_hi16(c.x, c.y);
+  r.w = pack_hi16(d.x, d.y);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
+}
+
+// e2m1 nibble -> fp32, exact: magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6.
+__device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
+  uint32_t mag = c & 7u;
+  uint32_t bits = mag >= 2u ? ((((mag >> 1) + 126u) << 23) | ((mag & 1u) << 22))
+                            : (mag ? 0x3f000000u : 0u);
+  return u2f(bits | ((c & 8u) << 28));
+}
+
+// 8 e2m1 nibbles (even element in the low nibble) times an fp32 block scale
+// -> 8 bf16. e2m1 (2 significant bits) times e4m3 (4) fits bf16 exactly.
+__device__ __forceinline__ bf16x8 e2m1x8_scaled_to_bf16(uint32_t nib, float s) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float v0 = e2m1_to_f32((nib >> (8 * i)) & 0xfu) * s;
+    float v1 = e2m1_to_f32((nib >> (8 * i + 4)) & 0xfu) * s;
+    r[i] = pack_hi16(v0, v1);
+  }
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Element offset of the hi plane of afrag(row, k); the lo plane is +512.
+__device__ __forceinline__ size_t afrag_off(int row, int k, int KT) {
+  int mt = row >> 4, t = k >> 5;
+  int lane = (row & 15) + 16 * ((k & 31) >> 3);
+  return ((size_t)(mt * KT + t) * 2) * 512 + lane * 8 + (k & 7);
+}
+
+// Stores 8 consecutive fp32 values X[row][k0..k0+8) (k0 % 8 == 0) as hi/lo.
+__device__ __forceinline__ void store_afrag8(uint16_t* af, int KT, int row, int k0, const float* v) {
+  u32x4 hi, lo;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t h0 = bf16_rne(v[2 * i]), h1 = bf16_rne(v[2 * i + 1]);
+    uint32_t l0 = bf16_rne(v[2 * i] - bf16_to_f32(h0));
+    uint32_t l1 = bf16_rne(v[2 * i + 1] - bf16_to_f32(h1));
+    hi[i] = h0 | (h1 << 16);
+    lo[i] = l0 | (l1 << 16);
+  }
+  size_t off = afrag_off(row, k0, KT);
+  *reinterpret_cast<u32x4*>(af + off) = hi;
+  *reinterpret_cast<u32x4*>(af + off + 512) = lo;
+}
+
+// Stores 8 consecutive bf16 values (exact; lo plane zero).
+__device__ __forceinline__ void store_afrag8_bf16(uint16_t* af, int KT, int row, int k0, u32x4 bits) {
+  size_t off = afrag_off(row, k0, KT);
+  *reinterpret_cast<u32x4*>(af + off) = bits;
+  *reinterpret_cast<u32x4*>(af + off + 512) = u32x4{0u, 0u, 0u, 0u};
+}
+
+__device__ __forceinline__ float silu(float u) { return u / (1.0f + expf(-u)); }
+
+// Order-preserving map of an fp32 to uint32 (NaN handled by the caller).
+__device__ __forceinline__ uint32_t f32_order(float x) {
+  uint32_t u = f2u(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+// Argmax key: larger logit wins, then the lower index. 0 = no finite logit.
+__device__ __forceinline__ unsigned long long argmax_key(float x, uint32_t idx) {
+  if (!(x == x) || x == __builtin_inff() || x == -__builtin_inff()) return 0ull;
+  return ((unsigned long long)f32_order(x) << 32) | (0xffffffffu - idx);
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_xor(T v, int mask) { return __shfl_xor(v, mask, 64); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+// Sum over a workgroup of `nwaves` waves; every thread gets the result.
+template <int NWAVES>
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < NWAVES; ++i) t += red[i];
+  return t;
+}
+
+}  // namespace kd

@@ -1,0 +1,910 @@
+// HIP kernels of one Kolibri-1 block-drafter round for gfx950.
+//
+// The round (model card "Kolibri-1 block drafter", section Architecture):
+//   tap fuse -> row build (anchor row through fc; rows 1-3 = mask + fused
+//   state + predecessor term) -> 4 layers [spine (layers 2-4) -> RMSNorm ->
+//   QKV -> RoPE -> block-causal cross-attention over the last window rows ->
+//   O + residual -> RMSNorm -> SwiGLU FFN + residual] -> RMSNorm -> NVFP4 head
+//   restricted to the draft vocabulary -> argmax.
+//
+// Projections run on the matrix cores (v_mfma_f32_16x16x32_bf16): weights are
+// decoded exactly from e4m3 to bf16 in registers, activations enter as a
+// bf16 hi/lo pair, and the fp32 block scale of each 64 inputs is applied to the
+// partial sum of that block. Split-K partial sums are reduced in a fixed order
+// by the consumer kernel, so results are deterministic.
+#include "kd_device.h"
+#include "kd_runtime.h"
+
+namespace kd {
+
+// ---------------------------------------------------------------------------
+// Block-FP8 projection: part[split][r][n] = sum over the split's inputs of
+// X[r][k] * W[n_off*16 + n][k].
+// ---------------------------------------------------------------------------
+struct GemmK {
+  const uint16_t* af;
+  int R, KT;
+  const uint8_t* w;
+  const float* s;
+  int KB;        // 64-input blocks per weight row
+  int N;         // output columns of this launch (multiple of 64)
+  int n_off;     // first 16-row weight tile
+  float* part;
+  int splits, kbs;
+};
+
+__global__ __launch_bounds__(256) void k_gemm(GemmK g) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ngroups = g.N >> 6;
+  int u = blockIdx.x;
+  const int ng = u % ngroups;
+  u /= ngroups;
+  const int sp = u % g.splits;
+  const int mt = u / g.splits;
+  const int nt = ng * 4 + wave;
+  const int ntw = nt + g.n_off;
+  const int b0 = sp * g.kbs;
+  const int row = mt * 16 + (lane & 15);
+  const bool rv = row < g.R;
+  const uint8_t* wp = g.w + ((size_t)ntw * g.KB + b0) * 1024 + lane * 16;
+  const float* spp = g.s + ((size_t)ntw * g.KB + b0) * 16 + (lane & 15);
+  const uint16_t* ap = g.af + ((size_t)mt * g.KT + 2 * b0) * 1024 + lane * 8;
+  const bf16x8 zero = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int i = 0; i < g.kbs; ++i) {
+    const u32x4 wv = *reinterpret_cast<const u32x4*>(wp + (size_t)i * 1024);
+    const float sc = spp[i * 16];
+    bf16x8 ah0 = zero, al0 = zero, ah1 = zero, al1 = zero;
+    if (rv) {
+      const uint16_t* a = ap + (size_t)i * 2048;
+      ah0 = *reinterpret_cast<const bf16x8*>(a);
+      al0 = *reinterpret_cast<const bf16x8*>(a + 512);
+      ah1 = *reinterpret_cast<const bf16x8*>(a + 1024);
+      al1 = *reinterpret_cast<const bf16x8*>(a + 1536);
+    }
+    const bf16x8 w0 = e4m3x8_to_bf16(wv.x, wv.y);
+    const bf16x8 w1 = e4m3x8_to_bf16(wv.z, wv.w);
+    f32x4 t = {0.f, 0.f, 0.f, 0.f};
+    t = mfma_bf16(ah0, w0, t);
+    t = mfma_bf16(al0, w0, t);
+    t = mfma_bf16(ah1, w1, t);
+    t = mfma_bf16(al1, w1, t);
+    acc += sc * t;
+  }
+  float* out = g.part + (size_t)sp * g.R * g.N + nt * 16 + (lane & 15);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int r = mt * 16 + 4 * (lane >> 4) + e;
+    if (r < g.R) out[(size_t)r * g.N] = acc[e];
+  }
+}
+
+static int splits_for(int KB, int want) {
+  int s = want < 1 ? 1 : (want > KB ? KB : want);
+  while (KB % s) --s;
+  return s;
+}
+
+int gemm_splits(int K, int N, int R) {
+  const int KB = K / 64;
+  int base;
+  if (N <= 256) base = KB / 4;           // rank-256 adapters: thin matrices, split deep
+  else if (KB <= 4) base = 1;            // K = 256 (adapter U)
+  else if (KB >= 96) base = KB / 8;      // fuse (120), down (96)
+  else if (KB >= 80) base = KB / 8;      // fc (80)
+  else base = KB / 4;                    // K = 2560
+  const int mt = mtiles(R);
+  return splits_for(KB, mt == 1 ? base : base / mt);
+}
+
+void launch_gemm(hipStream_t st, const uint16_t* af, int R, const Fp8Mat& W, int n_off_tiles,
+                 int N, float* part, int splits) {
+  GemmK g;
+  g.af = af;
+  g.R = R;
+  g.KT = W.K / 32;
+  g.w = W.w;
+  g.s = W.s;
+  g.KB = W.K / 64;
+  g.N = N;
+  g.n_off = n_off_tiles;
+  g.part = part;
+  g.splits = splits;
+  g.kbs = g.KB / splits;
+  const int blocks = mtiles(R) * splits * (N / 64);
+  k_gemm<<<blocks, 256, 0, st>>>(g);
+}
+
+// ---------------------------------------------------------------------------
+// Round prologue: tapped states -> afrag, argmax keys cleared, RoPE table for
+// block positions len + j (angles in double: positions reach the thousands).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_prep(uint16_t* af_in, const uint16_t* taps,
+                                              unsigned long long* keys, float* rope,
+                                              const int32_t* lens, float theta) {
+  const int b = blockIdx.x;
+  constexpr int K = NTAP * H, KT = K / 32;
+  for (int g = threadIdx.x; g < K / 8; g += blockDim.x) {
+    u32x4 bits = *reinterpret_cast<const u32x4*>(taps + (size_t)b * K + g * 8);
+    store_afrag8_bf16(af_in, KT, b, g * 8, bits);
+  }
+  if (threadIdx.x < BLK) keys[b * BLK + threadIdx.x] = 0ull;
+  const int j = threadIdx.x >> 6, fi = threadIdx.x & 63;
+  const double pos = (double)lens[b] + j;
+  const double ang = pos * pow((double)theta, -(double)fi / (DH / 2));
+  rope[((b * BLK + j) * (DH / 2) + fi) * 2 + 0] = (float)cos(ang);
+  rope[((b * BLK + j) * (DH / 2) + fi) * 2 + 1] = (float)sin(ang);
+}
+
+void launch_prep(hipStream_t st, const Work& w, const DevWeights& d, int B, const uint16_t* taps,
+                 const int32_t* lens, float theta) {
+  (void)d;
+  k_prep<<<B, 256, 0, st>>>(w.af_in, taps, w.keys, w.rope, lens, theta);
+}
+
+// f = sum of fuse partials; afrag of [f ; E[anchor]] (fc input) and of
+// [f ; E[pred_j]] for j = 0..2 (input of [A_p | B_p]).
+__global__ __launch_bounds__(320) void k_post_fuse(const float* part, int splits, int B, float* f,
+                                                   uint16_t* af_fc, uint16_t* af_ab,
+                                                   const uint16_t* table, const int32_t* anchor,
+                                                   const int32_t* pred) {
+  const int b = blockIdx.x, c0 = threadIdx.x * 8;
+  constexpr int KT = 2 * H / 32;
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float* p = part + ((size_t)s * B + b) * H + c0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] += p[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[(size_t)b * H + c0 + i] = v[i];
+  store_afrag8(af_fc, KT, b, c0, v);
+  const u32x4 ea = *reinterpret_cast<const u32x4*>(table + (size_t)anchor[b] * H + c0);
+  store_afrag8_bf16(af_fc, KT, b, H + c0, ea);
+  for (int j = 0; j < BLK - 1; ++j) {
+    store_afrag8(af_ab, KT, b * 3 + j, c0, v);
+    const u32x4 ep = *reinterpret_cast<const u32x4*>(table + (size_t)pred[b * 3 + j] * H + c0);
+    store_afrag8_bf16(af_ab, KT, b * 3 + j, H + c0, ep);
+  }
+}
+
+void launch_post_fuse(hipStream_t st, const Work& w, const DevWeights& d, int B, int splits,
+                      const int32_t* anchor, const int32_t* pred) {
+  k_post_fuse<<<B, 320, 0, st>>>(w.part, splits, B, w.f, w.af_fc, w.af_ab, d.table, anchor, pred);
+}
+
+// afrag of silu(sum of partials) for a rank-256 hidden vector.
+__global__ __launch_bounds__(32) void k_silu_rank(const float* part, int splits, int rows,
+                                                  uint16_t* af) {
+  const int r = blockIdx.x, c0 = threadIdx.x * 8;
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float* p = part + ((size_t)s * rows + r) * RK + c0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] += p[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = silu(v[i]);
+  store_afrag8(af, RK / 32, r, c0, v);
+}
+
+void launch_silu_rank(hipStream_t st, const float* part, int splits, int rows, uint16_t* af) {
+  k_silu_rank<<<rows, 32, 0, st>>>(part, splits, rows, af);
+}
+
+// Writes RMSNorm(x_j; gain) of the 4 rows of stream b to afrag (320 threads,
+// 8 columns each; the rows are in v[4][8]).
+__device__ __forceinline__ void norm4_store(float (&v)[4][8], int b, const float* gain, float eps,
+                                            uint16_t* af, float* red) {
+  const int c0 = threadIdx.x * 8;
+  float inv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss += v[j][i] * v[j][i];
+    ss = block_sum<5>(ss, red + 8 * j);
+    inv[j] = 1.0f / sqrtf(ss / H + eps);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = gain[c0 + i] * v[j][i] * inv[j];
+    store_afrag8(af, H / 32, b * 4 + j, c0, o);
+  }
+}
+
+// Block rows: x0 = fc partials; x_j = mask + f + U_p partials (j = 1..3);
+// then the first layer's attention RMSNorm into afrag.
+__global__ __launch_bounds__(320) void k_rowbuild(const float* part_fc, int splits_fc,
+                                                  const float* part_u, int splits_u, int B,
+                                                  const float* f, const float* mask, float* x,
+                                                  const float* gain, float eps, uint16_t* af) {
+  __shared__ float red[64];
+  const int b = blockIdx.x, c0 = threadIdx.x * 8;
+  float v[4][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[0][i] = 0.f;
+  for (int s = 0; s < splits_fc; ++s) {
+    const float* p = part_fc + ((size_t)s * B + b) * H + c0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[0][i] += p[i];
+  }
+  for (int j = 1; j < 4; ++j) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[j][i] = 0.f;
+    for (int s = 0; s < splits_u; ++s) {
+      const float* p = part_u + ((size_t)s * 3 * B + b * 3 + j - 1) * H + c0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[j][i] += p[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[j][i] = (mask[c0 + i] + f[(size_t)b * H + c0 + i]) + v[j][i];
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[(size_t)(b * 4 + j) * H + c0 + i] = v[j][i];
+  norm4_store(v, b, gain, eps, af, red);
+}
+
+void launch_rowbuild(hipStream_t st, const Work& w, const DevWeights& d, int B, int splits_fc,
+                     int splits_u, const float* gain, float eps) {
+  const size_t half = w.part_elems / 2;
+  k_rowbuild<<<B, 320, 0, st>>>(w.part, splits_fc, w.part + half, splits_u, B, w.f, d.mask, w.x,
+                                gain, eps, w.af_x);
+}
+
+// Spine add (rows 1..3 of each stream) and the layer's attention RMSNorm.
+__global__ __launch_bounds__(320) void k_spine_add_norm(const float* part, int splits, int B,
+                                                        float* x, const float* gain, float eps,
+                                                        uint16_t* af) {
+  __shared__ float red[64];
+  const int b = blockIdx.x, c0 = threadIdx.x * 8;
+  float v[4][8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float* xr = x + (size_t)(b * 4 + j) * H + c0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[j][i] = xr[i];
+    if (j > 0) {
+      float add[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) add[i] = 0.f;
+      for (int s = 0; s < splits; ++s) {
+        const float* p = part + ((size_t)s * 3 * B + b * 3 + j - 1) * H + c0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) add[i] += p[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        v[j][i] += add[i];
+        xr[i] = v[j][i];
+      }
+    }
+  }
+  norm4_store(v, b, gain, eps, af, red);
+}
+
+void launch_spine_add_norm(hipStream_t st, const Work& w, int B, int splits, const float* gain,
+                           float eps) {
+  k_spine_add_norm<<<B, 320, 0, st>>>(w.part, splits, B, w.x, gain, eps, w.af_x);
+}
+
+// q|k|v partials -> q, k (RoPE, rotate-half) and v for every block row.
+__global__ __launch_bounds__(256) void k_qkv_post(const float* part, int splits, int R,
+                                                  const float* rope, float* q, float* kb,
+                                                  float* vb) {
+  const int r = blockIdx.x, b = r >> 2, j = r & 3;
+  for (int p = threadIdx.x; p < NH * DH / 2; p += blockDim.x) {
+    const int h = p >> 6, fi = p & 63;
+    const int c0 = h * DH + fi, c1 = c0 + DH / 2;
+    float qa = 0.f, qb = 0.f, ka = 0.f, kb2 = 0.f, va = 0.f, vb2 = 0.f;
+    for (int s = 0; s < splits; ++s) {
+      const float* pr = part + ((size_t)s * R + r) * QKV;
+      qa += pr[c0];
+      qb += pr[c1];
+      ka += pr[H + c0];
+      kb2 += pr[H + c1];
+      va += pr[2 * H + c0];
+      vb2 += pr[2 * H + c1];
+    }
+    const float cs = rope[((b * BLK + j) * (DH / 2) + fi) * 2];
+    const float sn = rope[((b * BLK + j) * (DH / 2) + fi) * 2 + 1];
+    float* qr = q + (size_t)r * H;
+    float* kr = kb + (size_t)r * H;
+    float* vr = vb + (size_t)r * H;
+    qr[c0] = qa * cs - qb * sn;
+    qr[c1] = qa * sn + qb * cs;
+    kr[c0] = ka * cs - kb2 * sn;
+    kr[c1] = ka * sn + kb2 * cs;
+    vr[c0] = va;
+    vr[c1] = vb2;
+  }
+}
+
+void launch_qkv_post(hipStream_t st, const Work& w, int B, int splits) {
+  k_qkv_post<<<B * BLK, 256, 0, st>>>(w.part, splits, B * BLK, w.rope, w.q, w.kb, w.vb);
+}
+
+// ---------------------------------------------------------------------------
+// Cross-attention over the context window, split over chunks of ATT_CH keys.
+// Each workgroup (stream b, head h, chunk c) produces for the 4 block rows the
+// running max m (log2 units), the sum l of 2^(s - m) and o = sum 2^(s - m) v.
+// ---------------------------------------------------------------------------
+struct AttnK {
+  const float* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t ss, sh, sl;
+  int cap, window, nch;
+  const int32_t* lens;
+  float* pm;
+  float* pl;
+  float* po;
+};
+
+__device__ __forceinline__ void bf16x8_to_f32(u32x4 w, float* o) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = u2f(w[i] << 16);
+    o[2 * i + 1] = u2f(w[i] & 0xffff0000u);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_attn_split(AttnK a) {
+  __shared__ float s_o[4][BLK][DH];
+  __shared__ float s_m[4][BLK], s_l[4][BLK];
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int len = a.lens[b];
+  const int n = min(len, a.window);
+  if (c * ATT_CH >= n) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, d0 = (lane & 15) * 8;
+  const float qs = 0.08838834764831845f * 1.4426950408889634f;  // 1/sqrt(128) * log2(e)
+  float q[BLK][8];
+#pragma unroll
+  for (int j = 0; j < BLK; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[j][e] = a.q[(size_t)(b * BLK + j) * H + h * DH + d0 + e] * qs;
+  const uint16_t* kbase = a.k + b * a.ss + h * a.sh + d0;
+  const uint16_t* vbase = a.v + b * a.ss + h * a.sh + d0;
+  const int base = c * ATT_CH + wave * 32;
+  const int first = len - n;
+  float sc[BLK][8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int idx = base + 4 * s + g;
+    const bool valid = idx < n;
+    float dot[BLK] = {0.f, 0.f, 0.f, 0.f};
+    if (valid) {
+      const int slot = (first + idx) % a.cap;
+      float kf[8];
+      bf16x8_to_f32(*reinterpret_cast<const u32x4*>(kbase + slot * a.sl), kf);
+#pragma unroll
+      for (int j = 0; j < BLK; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dot[j] += q[j][e] * kf[e];
+    }
+#pragma unroll
+    for (int j = 0; j < BLK; ++j) {
+#pragma unroll
+      for (int m = 8; m >= 1; m >>= 1) dot[j] += __shfl_xor(dot[j], m, 64);
+      sc[j][s] = valid ? dot[j] : -__builtin_inff();
+    }
+  }
+  float mx[BLK], l[BLK], o[BLK][8];
+#pragma unroll
+  for (int j = 0; j < BLK; ++j) {
+    float m = sc[j][0];
+#pragma unroll
+    for (int s = 1; s < 8; ++s) m = fmaxf(m, sc[j][s]);
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    mx[j] = m;
+    l[j] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
+  }
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int idx = base + 4 * s + g;
+    if (idx < n) {
+      const int slot = (first + idx) % a.cap;
+      float vf[8];
+      bf16x8_to_f32(*reinterpret_cast<const u32x4*>(vbase + slot * a.sl), vf);
+#pragma unroll
+      for (int j = 0; j < BLK; ++j) {
+        const float p = exp2f(sc[j][s] - mx[j]);
+        l[j] += p;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[j][e] += p * vf[e];
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < BLK; ++j) {
+    l[j] += __shfl_xor(l[j], 16, 64);
+    l[j] += __shfl_xor(l[j], 32, 64);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      o[j][e] += __shfl_xor(o[j][e], 16, 64);
+      o[j][e] += __shfl_xor(o[j][e], 32, 64);
+    }
+  }
+  if (g == 0) {
+#pragma unroll
+    for (int j = 0; j < BLK; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_o[wave][j][d0 + e] = o[j][e];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < BLK; ++j) {
+      s_m[wave][j] = mx[j];
+      s_l[wave][j] = l[j];
+    }
+  }
+  __syncthreads();
+  const size_t pb = ((size_t)(b * NH + h) * a.nch + c) * BLK;
+  for (int t = threadIdx.x; t < BLK * DH; t += blockDim.x) {
+    const int j = t / DH, d = t % DH;
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][j]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      if (s_m[w][j] != -__builtin_inff()) {
+        const float f = exp2f(s_m[w][j] - M);
+        L += s_l[w][j] * f;
+        O += s_o[w][j][d] * f;
+      }
+    }
+    a.po[(pb + j) * DH + d] = O;
+    if (d == 0) {
+      a.pm[pb + j] = M;
+      a.pl[pb + j] = L;
+    }
+  }
+}
+
+// Merge of the chunk partials with the block's own keys (row j sees block rows
+// 0..j), normalisation, and afrag of the attention output.
+__global__ __launch_bounds__(128) void k_attn_combine(const float* q, const float* kb,
+                                                      const float* vb, const float* pm,
+                                                      const float* pl, const float* po, int nch,
+                                                      const int32_t* lens, int window,
+                                                      uint16_t* af_o) {
+  __shared__ float red[2][10];
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = min(lens[b], window);
+  const int nc = (n + ATT_CH - 1) / ATT_CH;
+  const float qs = 0.08838834764831845f * 1.4426950408889634f;
+  float qv[BLK], kv[BLK], vv[BLK];
+#pragma unroll
+  for (int j = 0; j < BLK; ++j) {
+    const size_t off = (size_t)(b * BLK + j) * H + h * DH + d;
+    qv[j] = q[off];
+    kv[j] = kb[off];
+    vv[j] = vb[off];
+  }
+  float sb[10];
+  int t = 0;
+#pragma unroll
+  for (int j = 0; j < BLK; ++j)
+#pragma unroll
+    for (int i = 0; i <= j; ++i) sb[t++] = qv[j] * kv[i];
+#pragma unroll
+  for (int t2 = 0; t2 < 10; ++t2) {
+    float v = wave_sum(sb[t2]);
+    if (lane == 0) red[wave][t2] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int t2 = 0; t2 < 10; ++t2) sb[t2] = (red[0][t2] + red[1][t2]) * qs;
+  t = 0;
+#pragma unroll
+  for (int j = 0; j < BLK; ++j) {
+    float M = -__builtin_inff();
+    for (int c = 0; c < nc; ++c) M = fmaxf(M, pm[((size_t)(b * NH + h) * nch + c) * BLK + j]);
+#pragma unroll
+    for (int i = 0; i <= j; ++i) M = fmaxf(M, sb[t + i]);
+    float L = 0.f, O = 0.f;
+    for (int c = 0; c < nc; ++c) {
+      const size_t pb = ((size_t)(b * NH + h) * nch + c) * BLK + j;
+      const float f = exp2f(pm[pb] - M);
+      L += pl[pb] * f;
+      O += po[pb * DH + d] * f;
+    }
+#pragma unroll
+    for (int i = 0; i <= j; ++i) {
+      const float f = exp2f(sb[t + i] - M);
+      L += f;
+      O += f * vv[i];
+    }
+    t += j + 1;
+    const float out = O / L;
+    const uint32_t hi = bf16_rne(out);
+    const uint32_t lo = bf16_rne(out - bf16_to_f32(hi));
+    const size_t off = afrag_off(b * BLK + j, h * DH + d, H / 32);
+    af_o[off] = (uint16_t)hi;
+    af_o[off + 512] = (uint16_t)lo;
+  }
+}
+
+void launch_attention(hipStream_t st, const Work& w, int B, const KV& kv, int layer,
+                      const int32_t* lens, int window) {
+  AttnK a;
+  a.q = w.q;
+  a.k = kv.k[layer];
+  a.v = kv.v[layer];
+  a.ss = kv.ss;
+  a.sh = kv.sh;
+  a.sl = kv.sl;
+  a.cap = kv.cap;
+  a.window = window;
+  a.nch = w.att_nch;
+  a.lens = lens;
+  a.pm = w.att_m;
+  a.pl = w.att_l;
+  a.po = w.att_o;
+  k_attn_split<<<dim3(w.att_nch, NH, B), 256, 0, st>>>(a);
+  k_attn_combine<<<dim3(NH, B), 128, 0, st>>>(w.q, w.kb, w.vb, w.att_m, w.att_l, w.att_o,
+                                              w.att_nch, lens, window, w.af_o);
+}
+
+// x += sum of partials; afrag of RMSNorm(x; gain). spine_rows: write row
+// 4b+j (j < 3) as row 3b+j (the spine's input rows), else every row.
+__global__ __launch_bounds__(320) void k_resid_norm(float* x, const float* part, int splits, int R,
+                                                    const float* gain, float eps, uint16_t* af,
+                                                    int spine_rows) {
+  __shared__ float red[8];
+  const int r = blockIdx.x, c0 = threadIdx.x * 8;
+  float* xr = x + (size_t)r * H + c0;
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float* p = part + ((size_t)s * R + r) * H + c0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] += p[i];
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[i] = xr[i] + v[i];
+    xr[i] = v[i];
+    ss += v[i] * v[i];
+  }
+  ss = block_sum<5>(ss, red);
+  const float inv = 1.0f / sqrtf(ss / H + eps);
+  int orow = r;
+  if (spine_rows) {
+    if ((r & 3) == 3) return;
+    orow = (r >> 2) * 3 + (r & 3);
+  }
+  float o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = gain[c0 + i] * v[i] * inv;
+  store_afrag8(af, H / 32, orow, c0, o);
+}
+
+void launch_resid_norm(hipStream_t st, const Work& w, int R, int splits, const float* gain,
+                       float eps, uint16_t* af_out, int spine_rows) {
+  k_resid_norm<<<R, 320, 0, st>>>(w.x, w.part, splits, R, gain, eps, af_out, spine_rows);
+}
+
+// h = silu(gate) * up from the gate|up partials -> afrag.
+__global__ __launch_bounds__(256) void k_swiglu(const float* part, int splits, int R,
+                                                uint16_t* af) {
+  const int r = blockIdx.x;
+  for (int gidx = threadIdx.x; gidx < FF / 8; gidx += blockDim.x) {
+    const int c0 = gidx * 8;
+    float gt[8], up[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) gt[i] = up[i] = 0.f;
+    for (int s = 0; s < splits; ++s) {
+      const float* p = part + ((size_t)s * R + r) * GU + c0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        gt[i] += p[i];
+        up[i] += p[FF + i];
+      }
+    }
+    float hv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) hv[i] = silu(gt[i]) * up[i];
+    store_afrag8(af, FF / 32, r, c0, hv);
+  }
+}
+
+void launch_swiglu(hipStream_t st, const Work& w, int R, int splits) {
+  k_swiglu<<<R, 256, 0, st>>>(w.part, splits, R, w.af_h);
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4 head over the draft vocabulary with a fused per-row argmax.
+// logits[r][v] = g * sum_k z[r][k] * e2m1(q) * e4m3(s); the argmax key
+// (order-preserving logit bits, then the complement of the index) is reduced
+// across lanes and merged with a 64-bit atomicMax, which is independent of
+// scheduling: ties go to the lowest draft index.
+// ---------------------------------------------------------------------------
+constexpr int HEAD_NV = 4;  // vocab tiles per wave
+
+struct HeadK {
+  const uint16_t* af;
+  int R;
+  const uint8_t* hq;
+  const uint8_t* hs;
+  float g;
+  int VD, VT;
+  float* logits;
+  unsigned long long* keys;
+};
+
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m) {
+  uint32_t lo = __shfl_xor((uint32_t)v, m, 64);
+  uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+__global__ __launch_bounds__(256) void k_head(HeadK a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int vt0 = (blockIdx.x * 4 + wave) * HEAD_NV;
+  if (vt0 >= a.VT) return;
+  constexpr int KT = H / 32, KG = H / 128;
+  const bf16x8 zero = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+  const int MT = mtiles(a.R);
+  for (int mt = 0; mt < MT; ++mt) {
+    f32x4 acc[HEAD_NV];
+#pragma unroll
+    for (int v = 0; v < HEAD_NV; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bool rv = mt * 16 + (lane & 15) < a.R;
+    for (int kg = 0; kg < KG; ++kg) {
+      u32x4 qv[HEAD_NV];
+      uint32_t sv[HEAD_NV];
+#pragma unroll
+      for (int v = 0; v < HEAD_NV; ++v) {
+        const int vt = vt0 + v;
+        if (vt < a.VT) {
+          const size_t idx = ((size_t)vt * KG + kg) * 64 + lane;
+          qv[v] = *reinterpret_cast<const u32x4*>(a.hq + idx * 16);
+          sv[v] = *reinterpret_cast<const uint32_t*>(a.hs + idx * 4);
+        } else {
+          qv[v] = u32x4{0u, 0u, 0u, 0u};
+          sv[v] = 0u;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = kg * 4 + i;
+        bf16x8 ah = zero, al = zero;
+        if (rv) {
+          const uint16_t* ap = a.af + ((size_t)(mt * KT + t) * 2) * 512 + lane * 8;
+          ah = *reinterpret_cast<const bf16x8*>(ap);
+          al = *reinterpret_cast<const bf16x8*>(ap + 512);
+        }
+#pragma unroll
+        for (int v = 0; v < HEAD_NV; ++v) {
+          const bf16x8 wb = e2m1x8_scaled_to_bf16(qv[v][i], e4m3_to_f32((sv[v] >> (8 * i)) & 0xffu));
+          acc[v] = mfma_bf16(ah, wb, acc[v]);
+          acc[v] = mfma_bf16(al, wb, acc[v]);
+        }
+      }
+    }
+    unsigned long long best[4] = {0ull, 0ull, 0ull, 0ull};
+#pragma unroll
+    for (int v = 0; v < HEAD_NV; ++v) {
+      const int voc = (vt0 + v) * 16 + (lane & 15);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = mt * 16 + 4 * (lane >> 4) + e;
+        const float val = acc[v][e] * a.g;
+        if (r < a.R && voc < a.VD) {
+          if (a.logits) a.logits[(size_t)r * a.VD + voc] = val;
+          const unsigned long long key = argmax_key(val, (uint32_t)voc);
+          best[e] = key > best[e] ? key : best[e];
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+#pragma unroll
+      for (int m = 8; m >= 1; m >>= 1) {
+        const unsigned long long o = shfl_xor_u64(best[e], m);
+        best[e] = o > best[e] ? o : best[e];
+      }
+    }
+    if ((lane & 15) == 0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = mt * 16 + 4 * (lane >> 4) + e;
+        if (r < a.R && best[e]) atomicMax(&a.keys[r], best[e]);
+      }
+    }
+  }
+}
+
+void launch_head(hipStream_t st, const Work& w, const DevWeights& d, int R, float* logits) {
+  HeadK a;
+  a.af = w.af_x;
+  a.R = R;
+  a.hq = d.hq;
+  a.hs = d.hs;
+  a.g = d.hg;
+  a.VD = d.VD;
+  a.VT = d.VT;
+  a.logits = logits;
+  a.keys = w.keys;
+  const int waves = (d.VT + HEAD_NV - 1) / HEAD_NV;
+  k_head<<<(waves + 3) / 4, 256, 0, st>>>(a);
+}
+
+__global__ void k_finalize(const unsigned long long* keys, const int32_t* vocab, int R,
+                           int32_t* out) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= R) return;
+  const unsigned long long k = keys[r];
+  out[r] = k ? vocab[0xffffffffu - (uint32_t)(k & 0xffffffffu)] : -1;
+}
+
+void launch_finalize(hipStream_t st, const Work& w, const DevWeights& d, int R, int32_t* out_ids) {
+  k_finalize<<<(R + 255) / 256, 256, 0, st>>>(w.keys, d.vocab, R, out_ids);
+}
+
+// ---------------------------------------------------------------------------
+// Context ingest: new rows -> fuse -> fc -> per layer RMSNorm -> K, V -> RoPE(K)
+// -> bf16 into the ring at slot (len + i) % capacity; then len += n.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_ingest_prep(uint16_t* af_in, const uint16_t* taps) {
+  const int r = blockIdx.x;
+  constexpr int K = NTAP * H, KT = K / 32;
+  for (int g = threadIdx.x; g < K / 8; g += blockDim.x) {
+    u32x4 bits = *reinterpret_cast<const u32x4*>(taps + (size_t)r * K + g * 8);
+    store_afrag8_bf16(af_in, KT, r, g * 8, bits);
+  }
+}
+
+void launch_ingest_prep(hipStream_t st, const Work& w, int rows, const uint16_t* taps) {
+  k_ingest_prep<<<rows, 256, 0, st>>>(w.af_in, taps);
+}
+
+__global__ __launch_bounds__(320) void k_ingest_post_fuse(const float* part, int splits, int rows,
+                                                          uint16_t* af_fc, const uint16_t* table,
+                                                          const int32_t* next_ids) {
+  const int r = blockIdx.x, c0 = threadIdx.x * 8;
+  constexpr int KT = 2 * H / 32;
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float* p = part + ((size_t)s * rows + r) * H + c0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] += p[i];
+  }
+  store_afrag8(af_fc, KT, r, c0, v);
+  const u32x4 e = *reinterpret_cast<const u32x4*>(table + (size_t)next_ids[r] * H + c0);
+  store_afrag8_bf16(af_fc, KT, r, H + c0, e);
+}
+
+void launch_ingest_post_fuse(hipStream_t st, const Work& w, const DevWeights& d, int rows,
+                             int splits, const int32_t* next_ids) {
+  k_ingest_post_fuse<<<rows, 320, 0, st>>>(w.part, splits, rows, w.af_fc, d.table, next_ids);
+}
+
+__global__ __launch_bounds__(320) void k_ingest_c(const float* part, int splits, int rows,
+                                                  float* c) {
+  const int r = blockIdx.x, c0 = threadIdx.x * 8;
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float* p = part + ((size_t)s * rows + r) * H + c0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] += p[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[(size_t)r * H + c0 + i] = v[i];
+}
+
+void launch_ingest_c(hipStream_t st, const Work& w, int rows, int splits) {
+  k_ingest_c<<<rows, 320, 0, st>>>(w.part, splits, rows, w.c);
+}
+
+__global__ __launch_bounds__(320) void k_norm_rows(const float* x, const float* gain, float eps,
+                                                   uint16_t* af) {
+  __shared__ float red[8];
+  const int r = blockIdx.x, c0 = threadIdx.x * 8;
+  float v[8], ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[i] = x[(size_t)r * H + c0 + i];
+    ss += v[i] * v[i];
+  }
+  ss = block_sum<5>(ss, red);
+  const float inv = 1.0f / sqrtf(ss / H + eps);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = gain[c0 + i] * v[i] * inv;
+  store_afrag8(af, H / 32, r, c0, v);
+}
+
+void launch_norm_rows(hipStream_t st, const float* x, int rows, const float* gain, float eps,
+                      uint16_t* af) {
+  k_norm_rows<<<rows, 320, 0, st>>>(x, gain, eps, af);
+}
+
+// k|v partials (N = 2H) -> RoPE(k) at position len + i -> bf16 (nearest even)
+// into the ring.
+__global__ __launch_bounds__(256) void k_ingest_store(const float* part, int splits, int rows,
+                                                      int n_new, uint16_t* kc, uint16_t* vc,
+                                                      int64_t ss, int64_t sh, int64_t sl, int cap,
+                                                      const int32_t* lens, float theta) {
+  const int r = blockIdx.x, b = r / n_new, i = r % n_new;
+  const long pos = (long)lens[b] + i;
+  const int slot = (int)(pos % cap);
+  for (int p = threadIdx.x; p < NH * DH / 2; p += blockDim.x) {
+    const int h = p >> 6, fi = p & 63;
+    const int c0 = h * DH + fi, c1 = c0 + DH / 2;
+    float ka = 0.f, kb2 = 0.f, va = 0.f, vb2 = 0.f;
+    for (int s = 0; s < splits; ++s) {
+      const float* pr = part + ((size_t)s * rows + r) * (2 * H);
+      ka += pr[c0];
+      kb2 += pr[c1];
+      va += pr[H + c0];
+      vb2 += pr[H + c1];
+    }
+    const double ang = (double)pos * pow((double)theta, -(double)fi / (DH / 2));
+    const float cs = (float)cos(ang), sn = (float)sin(ang);
+    const size_t base = (size_t)b * ss + (size_t)h * sh + (size_t)slot * sl;
+    kc[base + fi] = (uint16_t)bf16_rne(ka * cs - kb2 * sn);
+    kc[base + fi + DH / 2] = (uint16_t)bf16_rne(ka * sn + kb2 * cs);
+    vc[base + fi] = (uint16_t)bf16_rne(va);
+    vc[base + fi + DH / 2] = (uint16_t)bf16_rne(vb2);
+  }
+}
+
+void launch_ingest_store(hipStream_t st, const Work& w, int B, int n_new, int splits, const KV& kv,
+                         int layer, const int32_t* lens, float theta) {
+  k_ingest_store<<<B * n_new, 256, 0, st>>>(w.part, splits, B * n_new, n_new,
+                                            const_cast<uint16_t*>(kv.k[layer]),
+                                            const_cast<uint16_t*>(kv.v[layer]), kv.ss, kv.sh,
+                                            kv.sl, kv.cap, lens, theta);
+}
+
+__global__ void k_bump_lens(int32_t* lens, int B, int n) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < B) lens[b] += n;
+}
+
+void launch_bump_lens(hipStream_t st, int32_t* lens, int B, int n) {
+  k_bump_lens<<<(B + 255) / 256, 256, 0, st>>>(lens, B, n);
+}
+
+// ---------------------------------------------------------------------------
+// Codec probes: the exact decoders the projection and head kernels use.
+// ---------------------------------------------------------------------------
+__global__ void k_probe_e4m3(uint16_t* out) {
+  const uint32_t c = threadIdx.x;
+  const bf16x8 v = e4m3x8_to_bf16(c, 0u);
+  out[c] = (uint16_t)(__builtin_bit_cast(u32x4, v).x & 0xffffu);
+}
+
+__global__ void k_probe_nvfp4(uint16_t* out) {
+  const uint32_t idx = blockIdx.x * blockDim.x + threadIdx.x;
+  const uint32_t s = idx >> 4, c = idx & 15u;
+  const bf16x8 v = e2m1x8_scaled_to_bf16(c, e4m3_to_f32(s));
+  out[idx] = (uint16_t)(__builtin_bit_cast(u32x4, v).x & 0xffffu);
+}
+
+void launch_probe_e4m3(hipStream_t st, uint16_t* out) { k_probe_e4m3<<<1, 256, 0, st>>>(out); }
+void launch_probe_nvfp4(hipStream_t st, uint16_t* out) { k_probe_nvfp4<<<16, 256, 0, st>>>(out); }
+
+}  // namespace kd

@@ -1,0 +1,116 @@
+// Host-side view of libkdraft's device state and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kd {
+
+// A repacked block-FP8 matrix on the device (layout in kd_device.h).
+struct Fp8Mat {
+  const uint8_t* w = nullptr;
+  const float* s = nullptr;
+  int N = 0, K = 0;
+};
+
+struct DevLayer {
+  Fp8Mat qkv, wo, gu, down, sa, su;
+  const float* attn_norm = nullptr;
+  const float* ffn_norm = nullptr;
+  const float* spine_norm = nullptr;
+};
+
+struct DevWeights {
+  Fp8Mat fuse, fc, pred_ab, pred_u;   // pred_ab = [A_p | B_p] along K
+  const float* mask = nullptr;
+  DevLayer layer[4];
+  const float* final_norm = nullptr;
+  const uint8_t* hq = nullptr;        // repacked NVFP4 codes
+  const uint8_t* hs = nullptr;        // repacked e4m3 block scales
+  float hg = 1.f;
+  int VD = 0, VT = 0;                 // draft vocab rows, 16-row tiles
+  const int32_t* vocab = nullptr;
+  const uint16_t* table = nullptr;    // borrowed bf16 [full_vocab][H]
+};
+
+// Context K/V description passed to kernels.
+struct KV {
+  const uint16_t* k[4];
+  const uint16_t* v[4];
+  int64_t ss, sh, sl;
+  int cap;
+};
+
+// Workspace (allocated once per context for max_streams).
+struct Work {
+  int Bmax = 0, Rmax = 0, Imax = 0;   // streams, block rows, ingest rows
+  float* f = nullptr;                 // [max(Bmax, Imax)][H] fused taps
+  float* x = nullptr;                 // [Rmax][H] residual stream
+  float* c = nullptr;                 // [Imax][H] ingest rows after fc
+  float* part = nullptr;              // split-K partial sums
+  size_t part_elems = 0;
+  uint16_t* af_in = nullptr;          // afrag [max(Bmax, Imax)][NTAP*H]
+  uint16_t* af_fc = nullptr;          // afrag [max(Bmax, Imax)][2H]
+  uint16_t* af_ab = nullptr;          // afrag [3 Bmax][2H]
+  uint16_t* af_rank = nullptr;        // afrag [3 Bmax][RK]
+  uint16_t* af_x = nullptr;           // afrag [max(Rmax, Imax)][H]
+  uint16_t* af_sp = nullptr;          // afrag [3 Bmax][H]
+  uint16_t* af_h = nullptr;           // afrag [Rmax][FF]
+  uint16_t* af_o = nullptr;           // afrag [Rmax][H]
+  float* q = nullptr;                 // [Rmax][H] post-RoPE queries
+  float* kb = nullptr;                // [Rmax][H] block keys (post-RoPE)
+  float* vb = nullptr;                // [Rmax][H] block values
+  float* rope = nullptr;              // [Bmax][BLK][DH/2][2] cos, sin
+  float* att_m = nullptr;             // [Bmax][NH][nch][BLK]
+  float* att_l = nullptr;             // [Bmax][NH][nch][BLK]
+  float* att_o = nullptr;             // [Bmax][NH][nch][BLK][DH]
+  int att_nch = 0;                    // chunks per (stream, head) = ceil(window / ATT_CH)
+  unsigned long long* keys = nullptr; // [Rmax] argmax keys
+};
+
+// Row tiles of 16 for R rows.
+__host__ __device__ inline int mtiles(int R) { return (R + 15) / 16; }
+// Elements of an afrag buffer for R rows and K inputs.
+inline size_t afrag_elems(int R, int K) { return (size_t)mtiles(R) * (K / 32) * 1024; }
+
+// Split-K policy for a projection with K/64 blocks over R rows: fixed per
+// matrix while R <= 16 (one row tile), so a stream's result does not depend on
+// the batch around it; fewer splits as row tiles multiply.
+int gemm_splits(int K, int N, int R);
+
+// ---- launchers (kd_kernels.hip) ----
+void launch_gemm(hipStream_t st, const uint16_t* af, int R, const Fp8Mat& W, int n_off_tiles,
+                 int N, float* part, int splits);
+void launch_prep(hipStream_t st, const Work& w, const DevWeights& d, int B, const uint16_t* taps,
+                 const int32_t* lens, float theta);
+void launch_post_fuse(hipStream_t st, const Work& w, const DevWeights& d, int B, int splits,
+                      const int32_t* anchor, const int32_t* pred);
+void launch_silu_rank(hipStream_t st, const float* part, int splits, int rows, uint16_t* af);
+void launch_rowbuild(hipStream_t st, const Work& w, const DevWeights& d, int B, int splits_fc,
+                     int splits_u, const float* gain, float eps);
+void launch_spine_add_norm(hipStream_t st, const Work& w, int B, int splits, const float* gain,
+                           float eps);
+void launch_qkv_post(hipStream_t st, const Work& w, int B, int splits);
+void launch_attention(hipStream_t st, const Work& w, int B, const KV& kv, int layer,
+                      const int32_t* lens, int window);
+void launch_resid_norm(hipStream_t st, const Work& w, int R, int splits, const float* gain,
+                       float eps, uint16_t* af_out, int spine_rows);
+void launch_swiglu(hipStream_t st, const Work& w, int R, int splits);
+void launch_head(hipStream_t st, const Work& w, const DevWeights& d, int R, float* logits);
+void launch_finalize(hipStream_t st, const Work& w, const DevWeights& d, int R, int32_t* out_ids);
+// ingest
+void launch_ingest_prep(hipStream_t st, const Work& w, int rows, const uint16_t* taps);
+void launch_ingest_post_fuse(hipStream_t st, const Work& w, const DevWeights& d, int rows,
+                             int splits, const int32_t* next_ids);
+void launch_ingest_c(hipStream_t st, const Work& w, int rows, int splits);
+void launch_norm_rows(hipStream_t st, const float* x, int rows, const float* gain, float eps,
+                      uint16_t* af);
+void launch_ingest_store(hipStream_t st, const Work& w, int B, int n_new, int splits, const KV& kv,
+                         int layer, const int32_t* lens, float theta);
+void launch_bump_lens(hipStream_t st, int32_t* lens, int B, int n);
+// probes
+void launch_probe_e4m3(hipStream_t st, uint16_t* out);
+void launch_probe_nvfp4(hipStream_t st, uint16_t* out);
+
+}  // namespace kd

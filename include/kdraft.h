@@ -1,0 +1,180 @@
+/*
+ * libkdraft: one batched round of the Kolibri-1 block drafter on one MI355X
+ * (gfx950), as a C ABI.
+ *
+ * What a round computes is fixed by the model card "Kolibri-1 block drafter",
+ * section "Architecture":
+ *   Input     - the target's normed outputs of layers 44, 47, 49 are
+ *               concatenated and fused 3x2560 -> 2560; context rows are
+ *               [fused state ; embedding of the next token] -> 5120 -> 2560.
+ *   Position 1 - block row 0 is the anchor's own row in that context-row form.
+ *   Positions 2-4 - rows 1..3 read the learned mask row plus the anchor's
+ *               fused state, plus the rank-256 predecessor term
+ *               U silu(A h + B embed(token before)).
+ *   Spine     - before layers 2-4, row j reads row j-1 through
+ *               RMSNorm -> A -> silu -> U (rank 256); row 0 is untouched.
+ *   Body      - 4 layers: hidden 2560, 20 heads x 128, SwiGLU 6144, RoPE
+ *               theta 10,000; each layer cross-attends to the last 2,048
+ *               context rows and is causal inside the block.
+ *   Output    - RMSNorm, then the LM head restricted to the draft vocabulary.
+ * and the Serving paragraph: every stream is drafted in one batched pass; the
+ * body is block-FP8 (e4m3, one fp32 scale per row and 64 inputs) and the
+ * 60k-row head slice is NVFP4 (e2m1, one e4m3 scale per 16 inputs, one fp32
+ * tensor scale). The draft for a row is the argmax of its restricted logits.
+ *
+ * Conventions (all entry points):
+ *  - Device pointers are HIP device addresses the caller owns (for example
+ *    torch tensors). Host pointers are only read during the call.
+ *  - Calls enqueue work on the context's HIP stream and return; argument and
+ *    state errors are reported synchronously and enqueue nothing. A fault on
+ *    the device surfaces as KD_ERR_HIP on a later call.
+ *  - A context is not thread-safe. kd_round / kd_ingest never allocate.
+ *  - Ids and lengths on the device are not range-checked: ids must lie in
+ *    [0, full_vocab), lengths must be >= 0.
+ */
+#ifndef KDRAFT_H
+#define KDRAFT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct kd_ctx kd_ctx;
+
+typedef enum {
+  KD_OK = 0,
+  KD_ERR_ARG = -1,         /* a NULL or out-of-range argument */
+  KD_ERR_STATE = -2,       /* e.g. kd_round before kd_load_weights */
+  KD_ERR_OOM = -3,         /* device allocation failed (create / load only) */
+  KD_ERR_HIP = -4,         /* a HIP runtime call failed */
+  KD_ERR_UNSUPPORTED = -5  /* a shape or format this build does not implement */
+} kd_status;
+
+enum { KD_QUANT_FP8_BLOCK64 = 1, KD_QUANT_NVFP4 = 2 };
+enum { KD_MAX_INGEST = 8 };  /* rows per stream per kd_ingest call */
+
+/* Model shape and limits. The kernels are built for the model card's shape;
+ * kd_create returns KD_ERR_UNSUPPORTED for any other hidden, heads, head_dim,
+ * ffn, layers, block, rank or taps. draft_vocab, full_vocab and window are
+ * free (window >= 1). */
+typedef struct {
+  int hidden;        /* 2560 */
+  int heads;         /* 20 */
+  int head_dim;      /* 128 */
+  int ffn;           /* 6144 */
+  int layers;        /* 4 */
+  int block;         /* 4 rows drafted per stream per round */
+  int rank;          /* 256: predecessor and spine adapters */
+  int taps;          /* 3 tapped target layers (44, 47, 49) */
+  int window;        /* 2048: context rows attended, the last min(len, window) */
+  int draft_vocab;   /* 60614 */
+  int full_vocab;    /* 131072: rows of the embedding/head table */
+  int max_streams;   /* largest `streams` any call will pass */
+  float rope_theta;  /* 10000 */
+  float rms_eps;     /* 1e-6 */
+  int body_quant;    /* KD_QUANT_FP8_BLOCK64 */
+  int head_quant;    /* KD_QUANT_NVFP4 */
+} kd_config;
+
+/* Fills *cfg with the model card's shape, max_streams = 256. */
+void kd_default_config(kd_config* cfg);
+
+/* A block-FP8 matrix W[rows][cols] on the host: q = e4m3 codes, row-major
+ * [rows][cols]; s = fp32 scales [rows][cols/64]; W = e4m3(q) * s[r][c/64]. */
+typedef struct {
+  const uint8_t* q;
+  const float* s;
+} kd_fp8_matrix;
+
+typedef struct {
+  kd_fp8_matrix wq, wk, wv, wo;  /* [hidden][hidden] */
+  kd_fp8_matrix w_gate, w_up;    /* [ffn][hidden] */
+  kd_fp8_matrix w_down;          /* [hidden][ffn] */
+  const float* attn_norm;        /* [hidden] RMSNorm gains */
+  const float* ffn_norm;         /* [hidden] */
+  /* Spine applied before this layer (layers 1..3); ignored for layer 0. */
+  const float* spine_norm;       /* [hidden] */
+  kd_fp8_matrix spine_a;         /* [rank][hidden] */
+  kd_fp8_matrix spine_u;         /* [hidden][rank] */
+} kd_layer_weights;
+
+/* Host copies of the weights (copied and repacked by kd_load_weights), except
+ * the embedding table, which is borrowed: it is the target's frozen bf16
+ * table, a device pointer that must outlive the context. */
+typedef struct {
+  kd_fp8_matrix fuse;            /* [hidden][taps*hidden] */
+  kd_fp8_matrix fc;              /* [hidden][2*hidden]: input [fused ; embedding] */
+  kd_fp8_matrix pred_a;          /* [rank][hidden] applied to the fused state */
+  kd_fp8_matrix pred_b;          /* [rank][hidden] applied to embed(predecessor) */
+  kd_fp8_matrix pred_u;          /* [hidden][rank] */
+  const float* mask_row;         /* [hidden] */
+  kd_layer_weights layer[4];
+  const float* final_norm;       /* [hidden] */
+  const uint8_t* head_q4;        /* [draft_vocab][hidden/2] e2m1 codes, even column in the low nibble */
+  const uint8_t* head_s4;        /* [draft_vocab][hidden/16] e4m3 block scales */
+  float head_g;                  /* fp32 tensor scale */
+  const int32_t* draft_vocab;    /* [draft_vocab] target-vocabulary id of each head row */
+  const void* embed_table;       /* DEVICE, bf16 [full_vocab][hidden], borrowed */
+} kd_weights;
+
+/* The context K/V cache (device, bf16), one K and one V tensor per layer.
+ * Element (stream b, head h, slot s, dim d) of layer l lives at
+ *   k[l] + b*stride_stream + h*stride_head + s*stride_slot + d   (elements),
+ * head_dim contiguous. K is stored after RoPE. A context of len tokens keeps
+ * position p at slot p % capacity; a round attends positions
+ * [len - n, len) with n = min(len, window), so capacity >= window. */
+typedef struct {
+  void* k[4];
+  void* v[4];
+  int64_t stride_stream, stride_head, stride_slot;
+  int capacity;
+} kd_kv;
+
+/* Creates a context whose work goes to hip_stream (a hipStream_t; NULL is the
+ * null stream). Allocates the workspace for cfg->max_streams. */
+kd_status kd_create(const kd_config* cfg, void* hip_stream, kd_ctx** out);
+
+/* Copies, validates and repacks the weights into device memory (synchronous).
+ * May be called again to replace them. */
+kd_status kd_load_weights(kd_ctx* ctx, const kd_weights* w);
+
+/* One round for `streams` streams (1 <= streams <= max_streams).
+ *   tapped_states [streams][taps][hidden] bf16 (order: layers 44, 47, 49)
+ *   anchor_ids    [streams]     int32, target-vocabulary ids (row 0's token)
+ *   pred_ids      [streams][3]  int32, pred_ids[b][j-1] is the token before
+ *                               the one block row j drafts (j = 1..3)
+ *   ctx_kv        the K/V cache (struct on the host, tensors on the device)
+ *   ctx_lens      [streams] int32, tokens seen; block row j is at position len + j
+ *   out_ids       [streams][4] int32: target-vocabulary id of each row's
+ *                 argmax (lowest draft index on ties; -1 if no logit is finite)
+ *   out_logits    [streams][4][draft_vocab] fp32 in draft-vocabulary order, or NULL
+ * All arrays are device pointers except ctx_kv itself. */
+kd_status kd_round(kd_ctx* ctx, int streams, const void* tapped_states,
+                   const int32_t* anchor_ids, const int32_t* pred_ids,
+                   const kd_kv* ctx_kv, const int32_t* ctx_lens,
+                   int32_t* out_ids, float* out_logits);
+
+/* Appends n_new context rows per stream (1 <= n_new <= KD_MAX_INGEST): row i
+ * of stream b is [fuse(taps[b][i]) ; embed(next_ids[b][i])] -> fc, projected
+ * through each layer's attention RMSNorm and W_k / W_v, K rotated at position
+ * len + i, both rounded to bf16 and written at slot (len + i) % capacity;
+ * then ctx_lens[b] += n_new on the device.
+ *   taps     [streams][n_new][taps][hidden] bf16 (device)
+ *   next_ids [streams][n_new] int32 (device) */
+kd_status kd_ingest(kd_ctx* ctx, int streams, int n_new, const void* taps,
+                    const int32_t* next_ids, const kd_kv* ctx_kv, int32_t* ctx_lens);
+
+/* Moves the context to another HIP stream. */
+kd_status kd_set_stream(kd_ctx* ctx, void* hip_stream);
+
+void kd_destroy(kd_ctx* ctx);
+const char* kd_status_string(kd_status s);
+/* Last error message of this context ("" if none); valid until the next call. */
+const char* kd_last_error(const kd_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDRAFT_H */

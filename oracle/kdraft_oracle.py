@@ -85,10 +85,11 @@ def round_bf16(x) -> np.ndarray:
 
 
 def block_fp8(q, s) -> np.ndarray:
-    """W[o][i] = e4m3(q[o][i]) * s[o][i // 64] (one scale per row per 64 inputs)."""
-    q = np.asarray(q)
+    """W[o][i] = e4m3(q[o][i]) * s[o][i // 64] (one scale per row per 64 inputs).
+    The codes are decoded through the table of all 256 exact values."""
+    q = np.asarray(q, dtype=np.uint8)
     s = np.asarray(s, dtype=np.float64)
-    return decode_e4m3(q) * np.repeat(s, 64, axis=1)
+    return decode_e4m3(np.arange(256))[q] * np.repeat(s, 64, axis=1)
 
 
 def nvfp4(q4, s4, g) -> np.ndarray:
@@ -99,7 +100,8 @@ def nvfp4(q4, s4, g) -> np.ndarray:
     codes = np.empty((rows, q4.shape[1] * 2), dtype=np.uint8)
     codes[:, 0::2] = q4 & 0xF
     codes[:, 1::2] = q4 >> 4
-    return decode_e2m1(codes) * np.repeat(decode_e4m3(s4), 16, axis=1) * float(np.float32(g))
+    scales = decode_e4m3(np.arange(256))[np.asarray(s4, dtype=np.uint8)]
+    return decode_e2m1(np.arange(16))[codes] * np.repeat(scales, 16, axis=1) * float(np.float32(g))
 
 
 # ----------------------------------------------------------------------------
@@ -272,7 +274,7 @@ def oracle_round(M: OracleModel, inp: dict, block: int | None = None,
     return logits, ids
 
 
-def oracle_ingest(M: OracleModel, inp: dict):
+def oracle_ingest(M: OracleModel, inp: dict, return_exact: bool = False):
     """Append new context rows (model card, "Architecture", Input: context rows
     are [fused state ; embedding of the next token] -> 5120->2560; Body: the
     cached K/V each layer attends to).
@@ -280,7 +282,8 @@ def oracle_ingest(M: OracleModel, inp: dict):
     Every layer projects the same row c through its attention RMSNorm and
     W_k / W_v; K gets RoPE at its absolute position; both are rounded to bf16
     and stored at slot pos % capacity; len grows by the number of rows.
-    Returns a new input dict (K/V copies and lengths updated).
+    Returns a new input dict (K/V copies and lengths updated); with
+    return_exact also the unrounded fp64 K and V per layer ([B][n][heads][d]).
     """
     d = M.dims
     B = int(inp["streams"])
@@ -295,10 +298,12 @@ def oracle_ingest(M: OracleModel, inp: dict):
     f = taps.reshape(B, n_new, d.taps * H) @ M.fuse.T
     c = np.concatenate([f, M.embed(nxt)], axis=-1) @ M.fc.T           # [B][n][H]
     pos = lens[:, None] + np.arange(n_new)[None, :]
+    exact = []
     for l, L in enumerate(M.layers):
         a = rmsnorm(c, L["attn_norm"], d.rms_eps)
         k = rope((a @ L["wk"].T).reshape(B, n_new, NH, Dh), pos[:, :, None], d.rope_theta)
         v = (a @ L["wv"].T).reshape(B, n_new, NH, Dh)
+        exact.append((k, v))
         kb, vb = round_bf16(k), round_bf16(v)
         for b in range(B):
             for i in range(n_new):
@@ -306,4 +311,4 @@ def oracle_ingest(M: OracleModel, inp: dict):
                 out["k"][l][b][:, slot, :] = kb[b, i]
                 out["v"][l][b][:, slot, :] = vb[b, i]
     out["lens"] = (lens + n_new).astype(np.int32)
-    return out
+    return (out, exact) if return_exact else out

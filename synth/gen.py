@@ -219,7 +219,8 @@ def _rms_normal(shape, device, *parts):
 
 
 def make_inputs(cfg: dict, dims: Dims = FULL, device="cpu", base: int | None = None,
-                poison: bool = False, vocab: torch.Tensor | None = None, streams=None):
+                poison: bool = False, vocab: torch.Tensor | None = None, streams=None,
+                lens_override=None):
     """Round inputs for one workload.
 
     Each stream's tensors are seeded by (base, name, stream), so stream b's
@@ -231,10 +232,13 @@ def make_inputs(cfg: dict, dims: Dims = FULL, device="cpu", base: int | None = N
       k, v   per layer bf16 [B][heads][capacity][head_dim]: N(0,1) at visible
              slots; NaN elsewhere when poison=True (out-of-window reads show up)
       ingest (when cfg["ingest"] > 0): taps [B][n][3][H] and next ids [B][n]
+    lens_override: explicit per-stream lengths instead of the config's law.
     """
     if base is None:
         base = 100 + CONFIGS.index(cfg) if cfg in CONFIGS else 100
     B = cfg["streams"] if streams is None else streams
+    if lens_override is not None:
+        B = len(lens_override)
     if vocab is None:
         perm = torch.randperm(dims.full_vocab, generator=_gen("cpu", 0, "vocab"))
         vocab = torch.sort(perm[: dims.draft_vocab]).values.to(torch.int32)
@@ -252,7 +256,9 @@ def make_inputs(cfg: dict, dims: Dims = FULL, device="cpu", base: int | None = N
         taps.append(_rms_normal((dims.taps, H), device, base, "taps", b).to(torch.bfloat16))
         anchor.append(ids((1,), "anchor", b))
         pred.append(ids((dims.block - 1,), "pred", b))
-        if mode[0] == "const":
+        if lens_override is not None:
+            lens.append(int(lens_override[b]))
+        elif mode[0] == "const":
             lens.append(int(mode[1]))
         else:
             g = _gen("cpu", base, "len", b)

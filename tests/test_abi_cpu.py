@@ -1,0 +1,70 @@
+"""The C-ABI library loads on a host without a GPU and exports every entry
+point its headers declare; host-only argument checks answer without touching
+the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_draft_model_amd import kdraft
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for h in ("kdraft.h", "kdraft_debug.h"):
+        src = open(os.path.join(ROOT, "include", h)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names |= set(re.findall(r"\b(kd_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kdraft.LIB_PATH):
+        pytest.fail("libkdraft.so is not built (python -m block_draft_model_amd.build)")
+    return kdraft.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 13
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert missing == []
+    assert set(names) == set(kdraft.EXPORTS)
+
+
+def test_status_strings(lib):
+    for s in (0, -1, -2, -3, -4, -5):
+        assert kdraft.status_string(s) not in ("", "unknown status")
+    assert kdraft.status_string(-99) == "unknown status"
+
+
+def test_default_config_is_the_model_card_shape(lib):
+    c = kdraft.default_config()
+    assert (c.hidden, c.heads, c.head_dim, c.ffn, c.layers, c.block, c.rank, c.taps) == \
+        (2560, 20, 128, 6144, 4, 4, 256, 3)
+    assert (c.window, c.draft_vocab, c.full_vocab) == (2048, 60614, 131072)
+    assert abs(c.rope_theta - 10000.0) < 1e-3 and abs(c.rms_eps - 1e-6) < 1e-12
+
+
+def test_host_side_argument_errors(lib):
+    h = ctypes.c_void_p()
+    assert lib.kd_create(None, None, ctypes.byref(h)) == kdraft.KD_ERR_ARG
+    assert lib.kd_create(ctypes.byref(kdraft.default_config()), None, None) == kdraft.KD_ERR_ARG
+    for field, val in (("hidden", 4096), ("heads", 32), ("layers", 5), ("rank", 128)):
+        cfg = kdraft.default_config(**{field: val})
+        assert lib.kd_create(ctypes.byref(cfg), None, ctypes.byref(h)) == kdraft.KD_ERR_UNSUPPORTED
+    cfg = kdraft.default_config(head_quant=99)
+    assert lib.kd_create(ctypes.byref(cfg), None, ctypes.byref(h)) == kdraft.KD_ERR_UNSUPPORTED
+    cfg = kdraft.default_config(window=0)
+    assert lib.kd_create(ctypes.byref(cfg), None, ctypes.byref(h)) == kdraft.KD_ERR_ARG
+    cfg = kdraft.default_config(max_streams=1 << 30)
+    assert lib.kd_create(ctypes.byref(cfg), None, ctypes.byref(h)) == kdraft.KD_ERR_OOM
+    assert lib.kd_round(None, 1, None, None, None, None, None, None, None) == kdraft.KD_ERR_ARG
+    assert lib.kd_ingest(None, 1, 1, None, None, None, None) == kdraft.KD_ERR_ARG
+    assert lib.kd_load_weights(None, None) == kdraft.KD_ERR_ARG
+    assert lib.kd_last_error(None) == b""
+    lib.kd_destroy(None)

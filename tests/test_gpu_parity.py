@@ -1,0 +1,220 @@
+"""GPU parity of libkdraft against the fp64 oracle, through the C ABI.
+
+Every context row outside a stream's window holds NaN (bf16), so a read
+outside the window shows up as a non-finite logit. Workloads: the five seeded
+synthetic configurations (B = 1, 4, 16 ragged, 64 with ingest, 256 ragged; the
+larger two checked on sampled streams) and edge cases of the context length.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from block_draft_model_amd import kdraft
+from gpu_common import Harness, compare, log, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+C = synth.CONFIGS
+
+
+@pytest.fixture(scope="module")
+def hA():
+    require_gpu()
+    return Harness("A")
+
+
+@pytest.fixture(scope="module")
+def hB():
+    require_gpu()
+    return Harness("B", max_streams=16)
+
+
+@pytest.fixture(scope="module")
+def hC():
+    require_gpu()
+    return Harness("C", max_streams=8)
+
+
+def _hip():
+    lib = ctypes.CDLL("libamdhip64.so")
+    lib.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+    lib.hipMemcpy.restype = ctypes.c_int
+    return lib
+
+
+def device_floats(ptr, n):
+    out = np.empty(n, dtype=np.float32)
+    assert _hip().hipMemcpy(out.ctypes.data, ptr, n * 4, 2) == 0   # device -> host
+    return out
+
+
+def test_probe_e4m3_decoder_is_exact():
+    require_gpu()
+    out = torch.zeros(256, dtype=torch.int16, device="cuda")
+    kdraft.probe_decode_e4m3(out)
+    got = out.cpu().numpy().view(np.uint16)
+    exact = oracle.decode_e4m3(np.arange(256))
+    fin = np.isfinite(exact)
+    assert np.array_equal(got[fin], oracle.round_bf16(exact[fin]))   # exact in bf16
+    assert np.all(np.isnan(oracle.decode_bf16(got[~fin])))
+
+
+def test_probe_nvfp4_decoder_is_exact():
+    require_gpu()
+    out = torch.zeros(4096, dtype=torch.int16, device="cuda")
+    kdraft.probe_decode_nvfp4(out)
+    got = out.cpu().numpy().view(np.uint16).reshape(256, 16)
+    exact = oracle.decode_e4m3(np.arange(256))[:, None] * oracle.decode_e2m1(np.arange(16))[None, :]
+    fin = np.isfinite(exact)
+    assert np.array_equal(got[fin], oracle.round_bf16(exact[fin]))
+
+
+def test_layer_by_layer_b1(hA):
+    """Bisection aid: hidden states after 0..4 layers against the oracle."""
+    inp = hA.inputs(C[0])
+    inp_np = synth.to_numpy_inputs(inp)
+    M = hA.oracle
+    full_layers = M.layers
+    try:
+        for n in range(0, 5):
+            hA.drafter.debug_set_layers(n)
+            lg, ids = hA.run(inp)
+            hid, fus = hA.drafter.debug_buffers()
+            x_gpu = device_floats(hid, 4 * 2560).reshape(1, 4, 2560)
+            M.layers = full_layers[:n]
+            ref, rid, x_ref = oracle.oracle_round(M, inp_np, return_hidden=True)
+            relx = np.linalg.norm(x_gpu - x_ref, axis=-1) / np.linalg.norm(x_ref, axis=-1)
+            log(f"layers={n} hidden rel err per row {relx.ravel()}")
+            if n == 0:
+                f_gpu = device_floats(fus, 2560)
+                f_ref = oracle.decode_bf16(inp_np["taps"]).reshape(1, -1) @ M.fuse.T
+                log("fused state rel err", np.linalg.norm(f_gpu - f_ref) / np.linalg.norm(f_ref))
+            assert relx.max() < 1e-3
+            compare(lg, ids, ref, rid, M.vocab, f"layers={n}")
+    finally:
+        M.layers = full_layers
+        hA.drafter.debug_set_layers(-1)
+
+
+@pytest.mark.parametrize("ci", [0, 1])
+def test_round_parity_small_batches(hA, ci):
+    inp = hA.inputs(C[ci])
+    lg, ids = hA.run(inp)
+    ref, rid = oracle.oracle_round(hA.oracle, synth.to_numpy_inputs(inp))
+    compare(lg, ids, ref, rid, hA.oracle.vocab, C[ci]["name"])
+
+
+def test_round_parity_adapters_and_gains_active(hC):
+    cfg = dict(name="C-B5", streams=5, lens=("uniform", 0, 3000), model="C", ingest=0)
+    inp = hC.inputs(cfg, base=7)
+    lg, ids = hC.run(inp)
+    ref, rid = oracle.oracle_round(hC.oracle, synth.to_numpy_inputs(inp))
+    compare(lg, ids, ref, rid, hC.oracle.vocab, "model C, B=5")
+
+
+def test_round_parity_b16_ragged(hB):
+    inp = hB.inputs(C[2])
+    lens = inp["lens"].cpu().numpy()
+    log("B16 lens", lens.tolist())
+    lg, ids = hB.run(inp)
+    ref, rid = oracle.oracle_round(hB.oracle, synth.to_numpy_inputs(inp))
+    compare(lg, ids, ref, rid, hB.oracle.vocab, C[2]["name"])
+
+
+def test_context_length_edges(hC):
+    # empty context, a single row, chunk boundaries, the full window, and
+    # contexts past the ring's capacity (positions wrap, RoPE keeps counting)
+    lens = [0, 1, 127, 128, 129, 2047, 2048, 6000]
+    cfg = dict(name="edges", streams=len(lens), lens=("const", 0), model="C", ingest=0)
+    inp = hC.inputs(cfg, base=11, lens_override=lens)
+    lg, ids = hC.run(inp)
+    ref, rid = oracle.oracle_round(hC.oracle, synth.to_numpy_inputs(inp))
+    compare(lg, ids, ref, rid, hC.oracle.vocab, "length edges")
+
+
+def test_ingest_then_round_b64(hA):
+    cfg = C[3]
+    inp = hA.inputs(cfg)
+    sample = [0, 21, 63]
+    before = synth.to_numpy_inputs(inp, streams=sample)
+    hA.ingest(inp)
+    assert np.array_equal(inp["lens"].cpu().numpy(), np.full(64, 2048))
+    after_gpu = synth.to_numpy_inputs(inp, streams=sample)
+    after_ref, exact = oracle.oracle_ingest(hA.oracle, before, return_exact=True)
+    for l in range(4):
+        for key, ex in (("k", exact[l][0]), ("v", exact[l][1])):
+            g = oracle.decode_bf16(after_gpu[key][l][:, :, 2043:2048])   # [s][h][n][d]
+            e = ex.transpose(0, 2, 1, 3)                                  # [s][h][n][d]
+            # fp32 arithmetic then bf16 rounding: within one bf16 ulp of the
+            # exact value, plus an fp32-level error relative to the size of the
+            # head vector (values that cancel to near zero carry that error)
+            ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(e), 1e-30))) - 7)
+            scale = np.sqrt(np.mean(e * e, axis=-1, keepdims=True))
+            rel = np.abs(g - e) / np.maximum(np.abs(e), 1e-30)
+            off = np.abs(g - e) > ulp + 2.0 ** -14 * scale
+            log(f"ingest layer {l} {key}: max rel err {rel.max():.3e}, "
+                f"beyond one ulp {int(off.sum())}/{off.size}, "
+                f"codes differing from oracle {(after_gpu[key][l][:, :, 2043:2048] != after_ref[key][l][:, :, 2043:2048]).mean():.2e}")
+            assert not off.any(), (l, key)
+    lg, ids = hA.run(inp)
+    ref, rid = oracle.oracle_round(hA.oracle, after_ref)
+    compare(lg[sample], ids[sample], ref, rid, hA.oracle.vocab, "B64 after ingest (sampled)")
+
+
+def test_round_parity_b256_sampled(hA):
+    inp = hA.inputs(C[4])
+    lg, ids = hA.run(inp)
+    sample = [0, 1, 77, 128, 200, 255]
+    ref, rid = oracle.oracle_round(hA.oracle, synth.to_numpy_inputs(inp, streams=sample))
+    compare(lg[sample], ids[sample], ref, rid, hA.oracle.vocab, "B256 (sampled)")
+    assert np.all(ids >= 0) and np.all(np.isin(ids, hA.oracle.vocab))
+
+
+def test_deterministic_and_logits_optional(hC):
+    cfg = dict(name="det", streams=3, lens=("uniform", 100, 2500), model="C", ingest=0)
+    inp = hC.inputs(cfg, base=13)
+    a, ia = hC.run(inp)
+    b, ib = hC.run(inp)
+    assert np.array_equal(a, b) and np.array_equal(ia, ib)
+    _, ic = hC.run(inp, logits=False)
+    assert np.array_equal(ia, ic)
+
+
+def test_stream_alone_equals_stream_in_batch(hC):
+    cfg = dict(name="inv", streams=4, lens=("uniform", 10, 2048), model="C", ingest=0)
+    inp = hC.inputs(cfg, base=17)
+    batch, ib = hC.run(inp)
+    for b in range(4):
+        one = {k: (v[b:b + 1] if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+        one["k"] = [t[b:b + 1] for t in inp["k"]]
+        one["v"] = [t[b:b + 1] for t in inp["v"]]
+        one["streams"] = 1
+        alone, ia = hC.run(one)
+        assert np.array_equal(alone[0], batch[b]) and np.array_equal(ia[0], ib[b])
+
+
+def test_gpu_argument_errors(hC):
+    B = 2
+    cfg = dict(name="err", streams=B, lens=("const", 5), model="C", ingest=0)
+    inp = hC.inputs(cfg, base=19)
+    kv = kdraft.kv_struct(inp["k"], inp["v"])
+    ids = torch.empty(B, 4, dtype=torch.int32, device="cuda")
+    with pytest.raises(kdraft.KDraftError) as e:
+        hC.drafter.round(9, inp["taps"], inp["anchor"], inp["pred"], kv, inp["lens"], ids)
+    assert e.value.status == kdraft.KD_ERR_ARG
+    with pytest.raises(kdraft.KDraftError) as e:
+        hC.drafter.round(B, None, inp["anchor"], inp["pred"], kv, inp["lens"], ids)
+    assert e.value.status == kdraft.KD_ERR_ARG
+    small = kdraft.kv_struct([t[:, :, :1024] for t in inp["k"]], [t[:, :, :1024] for t in inp["v"]])
+    with pytest.raises(kdraft.KDraftError) as e:
+        hC.drafter.round(B, inp["taps"], inp["anchor"], inp["pred"], small, inp["lens"], ids)
+    assert e.value.status == kdraft.KD_ERR_ARG
+    fresh = kdraft.Drafter(max_streams=2)
+    with pytest.raises(kdraft.KDraftError) as e:
+        fresh.round(B, inp["taps"], inp["anchor"], inp["pred"], kv, inp["lens"], ids)
+    assert e.value.status == kdraft.KD_ERR_STATE
+    fresh.close()
