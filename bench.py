@@ -1,0 +1,153 @@
+"""Throughput of one batched Kolibri-1 block-drafter round on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config I] [--no-cpu-baseline]
+
+A step is one kd_round over every stream of the workload (tap fuse, row build,
+4 layers with spine and cross-attention, restricted NVFP4 head, argmax) with
+every input already resident in HBM. The default workload is the 4-stream
+configuration: 4 streams, 2048 context rows each, FP8 body, NVFP4 head.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "drafter rounds/s & draft tokens/s at B streams; % of HBM roofline"
+HBM_PEAK_GBS = 8000.0
+
+
+def algorithmic_bytes(dims, lens, streams):
+    """Bytes a round must move: weights once (block-FP8 body with scales, NVFP4
+    head with block and tensor scales, fp32 vectors), 40,960 B of bf16 K/V per
+    visible context row per stream (4 layers x K,V x 20 heads x 128 x 2 B), and
+    per stream its tapped states, 4 embedding rows, ids, length and outputs."""
+    import synth
+    mb = synth.model_bytes(dims)
+    kv_row = dims.layers * 2 * dims.heads * dims.head_dim * 2
+    vis = sum(min(int(l), dims.window) for l in lens)
+    per_stream = (dims.taps * dims.hidden * 2 + dims.block * dims.hidden * 2
+                  + 4 * (1 + (dims.block - 1) + 1 + dims.block))
+    total = mb["body"] + mb["head"] + mb["vectors"] + kv_row * vis + per_stream * streams
+    return dict(total=total, body=mb["body"], head=mb["head"], kv=kv_row * vis)
+
+
+def cpu_baseline(model, inp, max_seconds=20.0, max_rounds=8):
+    """The oracle, as it stands, on this host: rounds of the same workload
+    until about max_seconds have passed. Weight decoding to fp64 is timed as a
+    separate one-off load step."""
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    t0 = time.perf_counter()
+    M = oracle.OracleModel(synth.to_numpy_model(model))
+    load_s = time.perf_counter() - t0
+    inp_np = synth.to_numpy_inputs(inp)
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < max_rounds and (time.perf_counter() - t_start) < max_seconds:
+        t1 = time.perf_counter()
+        oracle.oracle_round(M, inp_np)
+        times.append(time.perf_counter() - t1)
+    per_round = sum(times) / len(times)
+    cpu = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": 1.0 / per_round, "unit": "rounds/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(times)} full rounds of the same workload in fp64 NumPy "
+                      f"({per_round:.2f} s/round); weight decode to fp64 {load_s:.1f} s "
+                      f"as a separate load step; host CPU: {cpu}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(the round shards by stream with no collectives; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    from block_draft_model_amd import kdraft
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU available", file=sys.stderr)
+        sys.exit(1)
+    cfg = synth.CONFIGS[args.config]
+    dims = synth.FULL
+    model = synth.make_model(dims, cfg["model"], device="cuda")
+    inp = synth.make_inputs(cfg, dims, device="cuda", vocab=model["vocab"])
+    B = inp["streams"]
+    stream = torch.cuda.current_stream()
+    drafter = kdraft.Drafter(max_streams=B, stream=stream)
+    drafter.load_weights(model)
+    kv = kdraft.kv_struct(inp["k"], inp["v"])
+    ids = torch.empty(B, 4, dtype=torch.int32, device="cuda")
+    lens_host = inp["lens"].cpu().tolist()
+
+    def step():
+        drafter.round(B, inp["taps"], inp["anchor"], inp["pred"], kv, inp["lens"], ids, None)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end) / args.steps
+
+    ab = algorithmic_bytes(dims, lens_host, B)
+    rounds_s = 1000.0 / ms
+    achieved = ab["total"] / (ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "kd_round (whole round)", "bytes_per_launch": ab["total"]}
+    out = {"metric": METRIC, "value": round(rounds_s, 2), "unit": "rounds/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+           "data": "synthetic",
+           "config": {"workload": f"{cfg['name']}: {B} streams x 1 round, draft block 4, "
+                                  f"context rows per stream {sorted(set(min(l, 2048) for l in lens_host))}, "
+                                  f"block-FP8 body, NVFP4 head (60,614 rows)",
+                      "streams": B, "draft_tokens_per_round": 4 * B},
+           "draft_tokens_per_s": round(4 * B * rounds_s, 1),
+           "bytes_per_round": ab, "hbm_roofline_frac": round(achieved / HBM_PEAK_GBS, 4),
+           "wall_s": round(wall, 3), "roofline": roofline}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(model, inp)
+    print(json.dumps(out), flush=True)
+    drafter.close()
+
+
+if __name__ == "__main__":
+    main()
