@@ -11,6 +11,7 @@
 #include "../../include/kdraft_debug.h"
 #include "kd_device.h"
 #include "kd_runtime.h"
+#include "kd_small.h"
 
 struct kd_ctx {
   kd_config cfg{};
@@ -23,7 +24,17 @@ struct kd_ctx {
   bool loaded = false;
   int debug_layers = -1;
   int last_streams = 0;
+  int last_path = 0;
   std::string err;
+  // small-batch path (<= 4 streams)
+  char* small_mem = nullptr;
+  kd::SmallBufs small{};
+  int G = 0;                 // workgroups of the small path (one per CU, <= 256)
+  bool mega_ok = false;      // persistent cooperative kernel available
+  int path = 0;              // 0 auto, 1 general, 2 small per-phase, 3 small persistent
+  kd::SmallArgs* args_dev = nullptr;   // device copy of the small-path arguments
+  kd::SmallArgs* args_host = nullptr;  // pinned host copy last uploaded
+  bool args_valid = false;
 };
 
 namespace {
@@ -151,6 +162,21 @@ bool concat_cols(HostMat& m, const kd_fp8_matrix& a, const kd_fp8_matrix& b, int
            cb / 64 * sizeof(float));
   }
   return true;
+}
+
+// Reorders rows: row p of the result is row nat(p) of m.
+void permute_rows(HostMat& m, int (*nat)(int)) {
+  HostMat o;
+  o.N = m.N;
+  o.K = m.K;
+  o.q.resize(m.q.size());
+  o.s.resize(m.s.size());
+  for (int p = 0; p < m.N; ++p) {
+    const int r = nat(p);
+    memcpy(&o.q[(size_t)p * m.K], &m.q[(size_t)r * m.K], m.K);
+    memcpy(&o.s[(size_t)p * m.K / 64], &m.s[(size_t)r * m.K / 64], m.K / 64 * sizeof(float));
+  }
+  m = std::move(o);
 }
 
 kd_status upload_mat(kd_ctx* c, const HostMat& m, kd::Fp8Mat* out) {
@@ -293,11 +319,31 @@ kd_status kd_create(const kd_config* cfg, void* hip_stream, kd_ctx** out) {
             dev_alloc(c->work_allocs, &w.att_o,
                       (size_t)w.Bmax * kd::NH * w.att_nch * kd::BLK * kd::DH) &&
             dev_alloc(c->work_allocs, &w.keys, (size_t)w.Rmax);
+  if (ok) {
+    ok = dev_alloc(c->work_allocs, &c->small_mem, kd::small_bytes(w.att_nch)) &&
+         dev_alloc(c->work_allocs, &c->args_dev, 1) &&
+         hipHostMalloc((void**)&c->args_host, sizeof(kd::SmallArgs), hipHostMallocDefault) ==
+             hipSuccess;
+    if (ok) {
+      kd::small_carve(c->small_mem, w.att_nch, &c->small);
+      ok = hipMemset(c->small.bar, 0, 19 * 32 * sizeof(unsigned)) == hipSuccess &&
+           hipDeviceSynchronize() == hipSuccess;
+    }
+  }
   if (!ok) {
     free_all(c->work_allocs);
+    if (c->args_host) (void)hipHostFree(c->args_host);
     delete c;
     return KD_ERR_OOM;
   }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, c->device) == hipSuccess) {
+    c->G = std::min(prop.multiProcessorCount, kd::MAX_G);
+    c->mega_ok = prop.cooperativeLaunch && kd::small_mega_occupancy() >= 1;
+  } else {
+    c->G = 128;
+  }
+  (void)hipGetLastError();
   *out = c;
   return KD_OK;
 }
@@ -313,6 +359,7 @@ void kd_destroy(kd_ctx* ctx) {
   (void)hipStreamSynchronize(ctx->stream);
   free_all(ctx->work_allocs);
   free_all(ctx->weight_allocs);
+  if (ctx->args_host) (void)hipHostFree(ctx->args_host);
   delete ctx;
 }
 
@@ -367,6 +414,8 @@ kd_status kd_load_weights(kd_ctx* c, const kd_weights* wt) {
     if (!append_rows(gu, L.w_gate, F, H) || !append_rows(gu, L.w_up, F, H))
       return fail(c, KD_ERR_ARG, "bad gate/up matrix");
     if (!append_rows(dn, L.w_down, H, F)) return fail(c, KD_ERR_ARG, "bad down matrix");
+    permute_rows(qkv, kd::qkv_natural);
+    permute_rows(gu, kd::gu_natural);
     if ((st = upload_mat(c, qkv, &D.qkv)) != KD_OK || (st = upload_mat(c, wo, &D.wo)) != KD_OK ||
         (st = upload_mat(c, gu, &D.gu)) != KD_OK || (st = upload_mat(c, dn, &D.down)) != KD_OK)
       return st;
@@ -418,6 +467,7 @@ kd_status kd_load_weights(kd_ctx* c, const kd_weights* wt) {
   d.VT = VT;
   d.vocab = dv;
   d.table = static_cast<const uint16_t*>(wt->embed_table);
+  c->args_valid = false;
   c->loaded = true;
   c->err.clear();
   return KD_OK;
@@ -440,6 +490,55 @@ kd_status kd_round(kd_ctx* c, int B, const void* taps, const int32_t* anchor, co
   const hipStream_t st = c->stream;
   const float eps = c->cfg.rms_eps;
   const int R = kd::BLK * B, B3 = 3 * B;
+  int path = c->path;
+  if (path == 0) path = B <= kd::SB_MAX ? (c->mega_ok ? 3 : 2) : 1;
+  if (path == 3 && !c->mega_ok) path = 2;
+  if (path != 1 && B > kd::SB_MAX) path = 1;
+  c->last_path = path;
+  if (path != 1) {
+    (void)hipGetLastError();
+    kd::SmallArgs a;
+    memset(&a, 0, sizeof a);
+    a.B = B;
+    a.R = R;
+    a.nl = c->debug_layers < 0 ? kd::NL : c->debug_layers;
+    a.window = c->cfg.window;
+    a.nch = w.att_nch;
+    a.eps = eps;
+    a.theta = c->cfg.rope_theta;
+    a.taps = static_cast<const uint16_t*>(taps);
+    a.anchor = anchor;
+    a.pred = pred;
+    a.lens = lens;
+    a.kv = k;
+    a.out_ids = out_ids;
+    a.out_logits = out_logits;
+    a.d = d;
+    a.s = c->small;
+    // upload the argument block only when it changed (a serving loop that
+    // reuses its buffers uploads it once)
+    if (!c->args_valid || memcmp(c->args_host, &a, sizeof a) != 0) {
+      hipError_t e = hipStreamSynchronize(st);   // the pinned copy may still be in flight
+      if (e == hipSuccess) {
+        memcpy(c->args_host, &a, sizeof a);
+        e = hipMemcpyAsync(c->args_dev, c->args_host, sizeof a, hipMemcpyHostToDevice, st);
+      }
+      if (e != hipSuccess) return hip_fail(c, e, "argument upload");
+      c->args_valid = true;
+    }
+    const int np = kd::small_phase_count(a.nl);
+    if (path == 3) {
+      const hipError_t e = kd::launch_small_mega(st, c->args_dev, c->G);
+      if (e != hipSuccess) return hip_fail(c, e, "persistent round launch");
+    } else {
+      for (int i = 0; i < np; ++i)
+        kd::launch_small_phase(st, c->args_dev, c->G, kd::small_phase_id(a.nl, i));
+    }
+    c->last_streams = B;
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(c, e, "kd_round launch");
+    return KD_OK;
+  }
   float* partA = w.part;
   float* partB = w.part + w.part_elems / 2;
   const int nl = c->debug_layers < 0 ? kd::NL : c->debug_layers;
@@ -554,9 +653,25 @@ kd_status kd_debug_set_layers(kd_ctx* c, int n) {
 
 kd_status kd_debug_buffers(kd_ctx* c, const float** hidden, const float** fused) {
   if (!c || !hidden || !fused) return KD_ERR_ARG;
-  *hidden = c->w.x;
-  *fused = c->w.f;
+  if (c->last_path == 2 || c->last_path == 3) {
+    const int nl = c->debug_layers < 0 ? kd::NL : c->debug_layers;
+    *hidden = c->small.x[nl == 0 ? 0 : kd::xs_d(nl - 1)];
+    *fused = c->small.f;
+  } else {
+    *hidden = c->w.x;
+    *fused = c->w.f;
+  }
   return KD_OK;
 }
+
+kd_status kd_debug_set_path(kd_ctx* c, int path) {
+  if (!c) return KD_ERR_ARG;
+  if (path < 0 || path > 3) return fail(c, KD_ERR_ARG, "path must be 0..3");
+  if (path == 3 && !c->mega_ok) return fail(c, KD_ERR_UNSUPPORTED, "no cooperative launch");
+  c->path = path;
+  return KD_OK;
+}
+
+int kd_debug_last_path(const kd_ctx* c) { return c ? c->last_path : 0; }
 
 }  // extern "C"

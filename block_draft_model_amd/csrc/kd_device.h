@@ -102,6 +102,15 @@ __device__ __forceinline__ bf16x8 e2m1x8_scaled_to_bf16(uint32_t nib, float s) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// 8 bf16 (packed in 4 dwords) -> 8 fp32.
+__device__ __forceinline__ void bf16x8_to_f32(u32x4 w, float* o) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = u2f(w[i] << 16);
+    o[2 * i + 1] = u2f(w[i] & 0xffff0000u);
+  }
+}
+
 __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -170,6 +179,38 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 #pragma unroll
   for (int i = 0; i < NWAVES; ++i) t += red[i];
   return t;
+}
+
+// ---------------------------------------------------------------------------
+// Output-row order of the repacked q|k|v and gate|up matrices.
+//
+// q|k|v: a 16-row tile holds 8 dims of one head and their rotate-half
+// partners (d and d + 64), so a tile's epilogue can apply RoPE. Tile t of
+// section s (0 q, 1 k, 2 v): head t/8 within the section, dims 8*(t%8) + i
+// (rows 0..7) and 64 + 8*(t%8) + i (rows 8..15).
+// gate|up: tile t holds gate rows 8t..8t+7 then up rows 8t..8t+7, so a tile's
+// epilogue can form silu(gate) * up.
+// ---------------------------------------------------------------------------
+__host__ __device__ inline int qkv_natural(int pos) {
+  const int t = pos >> 4, n = pos & 15;
+  const int s = t / (H / 16), tt = t % (H / 16);
+  const int hh = tt >> 3, pg = tt & 7;
+  const int d = n < 8 ? 8 * pg + n : 64 + 8 * pg + (n - 8);
+  return s * H + hh * DH + d;
+}
+__host__ __device__ inline int qkv_position(int nat) {
+  const int s = nat / H, c = nat % H;
+  const int hh = c / DH, d = c % DH;
+  const int pg = (d & 63) >> 3, n = (d & 7) + (d >= 64 ? 8 : 0);
+  return 16 * (s * (H / 16) + hh * 8 + pg) + n;
+}
+__host__ __device__ inline int gu_natural(int pos) {  // gate rows 0..FF-1, up rows FF..2FF-1
+  const int t = pos >> 4, n = pos & 15;
+  return n < 8 ? 8 * t + n : FF + 8 * t + (n - 8);
+}
+__host__ __device__ inline int gu_position(int nat) {
+  const int up = nat >= FF, g = up ? nat - FF : nat;
+  return 16 * (g >> 3) + (g & 7) + (up ? 8 : 0);
 }
 
 }  // namespace kd

@@ -306,14 +306,17 @@ __global__ __launch_bounds__(256) void k_qkv_post(const float* part, int splits,
     const int h = p >> 6, fi = p & 63;
     const int c0 = h * DH + fi, c1 = c0 + DH / 2;
     float qa = 0.f, qb = 0.f, ka = 0.f, kb2 = 0.f, va = 0.f, vb2 = 0.f;
+    const int pq0 = qkv_position(c0), pq1 = qkv_position(c1);
+    const int pk0 = qkv_position(H + c0), pk1 = qkv_position(H + c1);
+    const int pv0 = qkv_position(2 * H + c0), pv1 = qkv_position(2 * H + c1);
     for (int s = 0; s < splits; ++s) {
       const float* pr = part + ((size_t)s * R + r) * QKV;
-      qa += pr[c0];
-      qb += pr[c1];
-      ka += pr[H + c0];
-      kb2 += pr[H + c1];
-      va += pr[2 * H + c0];
-      vb2 += pr[2 * H + c1];
+      qa += pr[pq0];
+      qb += pr[pq1];
+      ka += pr[pk0];
+      kb2 += pr[pk1];
+      va += pr[pv0];
+      vb2 += pr[pv1];
     }
     const float cs = rope[((b * BLK + j) * (DH / 2) + fi) * 2];
     const float sn = rope[((b * BLK + j) * (DH / 2) + fi) * 2 + 1];
@@ -349,14 +352,6 @@ struct AttnK {
   float* pl;
   float* po;
 };
-
-__device__ __forceinline__ void bf16x8_to_f32(u32x4 w, float* o) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    o[2 * i] = u2f(w[i] << 16);
-    o[2 * i + 1] = u2f(w[i] & 0xffff0000u);
-  }
-}
 
 __global__ __launch_bounds__(256) void k_attn_split(AttnK a) {
   __shared__ float s_o[4][BLK][DH];
@@ -611,12 +606,13 @@ __global__ __launch_bounds__(256) void k_swiglu(const float* part, int splits, i
     float gt[8], up[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) gt[i] = up[i] = 0.f;
+    // columns c0..c0+7 of gate and of up sit in one 16-row tile (gu_position)
     for (int s = 0; s < splits; ++s) {
-      const float* p = part + ((size_t)s * R + r) * GU + c0;
+      const float* p = part + ((size_t)s * R + r) * GU + gu_position(c0);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         gt[i] += p[i];
-        up[i] += p[FF + i];
+        up[i] += p[8 + i];
       }
     }
     float hv[8];
@@ -854,12 +850,15 @@ __global__ __launch_bounds__(256) void k_ingest_store(const float* part, int spl
     const int h = p >> 6, fi = p & 63;
     const int c0 = h * DH + fi, c1 = c0 + DH / 2;
     float ka = 0.f, kb2 = 0.f, va = 0.f, vb2 = 0.f;
+    // this launch covers q|k|v positions H..3H-1 (the k and v sections)
+    const int pk0 = qkv_position(H + c0) - H, pk1 = qkv_position(H + c1) - H;
+    const int pv0 = qkv_position(2 * H + c0) - H, pv1 = qkv_position(2 * H + c1) - H;
     for (int s = 0; s < splits; ++s) {
       const float* pr = part + ((size_t)s * rows + r) * (2 * H);
-      ka += pr[c0];
-      kb2 += pr[c1];
-      va += pr[H + c0];
-      vb2 += pr[H + c1];
+      ka += pr[pk0];
+      kb2 += pr[pk1];
+      va += pr[pv0];
+      vb2 += pr[pv1];
     }
     const double ang = (double)pos * pow((double)theta, -(double)fi / (DH / 2));
     const float cs = (float)cos(ang), sn = (float)sin(ang);

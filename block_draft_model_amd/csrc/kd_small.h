@@ -1,0 +1,71 @@
+// The small-batch round (up to 4 streams = 16 block rows): workgroup-level
+// phases that run either one launch per phase or all inside one persistent
+// cooperative kernel separated by grid barriers.
+#pragma once
+
+#include "kd_runtime.h"
+
+namespace kd {
+
+constexpr int SB_MAX = 4;      // streams
+constexpr int SR_MAX = 16;     // block rows (one matrix-core row tile)
+constexpr int NXS = 12;        // residual-stream stages written in one round
+constexpr int HT = H / 16;     // 160 column tiles of a hidden vector
+constexpr int SMALL_WG = 512;  // 8 waves per workgroup
+constexpr int HEAD_NT = 4;     // vocab tiles per head unit
+constexpr int MAX_G = 256;     // workgroups (one per CU); barrier tree is 16 x 16
+
+// Stage index of the residual stream: the layer input, after O, after down.
+__host__ __device__ inline int xs_in(int l) { return l == 0 ? 0 : 3 * l; }
+__host__ __device__ inline int xs_o(int l) { return 3 * l + 1; }
+__host__ __device__ inline int xs_d(int l) { return 3 * l + 2; }
+
+// Buffers written at most once per round (so no cache ever holds a stale
+// copy within a launch); every buffer starts on a 256-byte boundary and no two
+// phases write into the same 128-byte line.
+struct SmallBufs {
+  float* f;                  // [SB][H]   fused tap state
+  float* fce;                // [SB][H]   fc (embedding half) . E[anchor]
+  float* pb;                 // [3SB][RK] B_p . E[pred]
+  float* sp;                 // [3SB][RK] silu(A_p f + B_p E[pred])
+  float* rope;               // [SR][64][2] cos, sin at the block positions
+  float* x[NXS];             // [SR][H]   residual stream stages
+  float* ssq[NXS];           // [SR][HT]  sum of squares of each 16-column tile
+  float* ss[NL];             // [3SB][RK] spine hidden (layers 1..3)
+  float* q[NL];              // [SR][H]   post-RoPE, natural head-major layout
+  float* k[NL];
+  float* v[NL];
+  float* am[NL];             // [SB][NH][nch][4] chunk max (log2 units)
+  float* al[NL];             // [SB][NH][nch][4] chunk sum of 2^(s - max)
+  float* ao[NL];             // [SB][NH][nch][4][DH]
+  float* o[NL];              // [SR][H]   merged attention output
+  float* h[NL];              // [SR][FF]  silu(gate) * up
+  unsigned long long* cand;  // [MAX_G][SR] per-workgroup argmax candidates
+  unsigned* bar;             // barrier: 16 group lines, top, generation, error (32 u32 each)
+};
+
+struct SmallArgs {
+  int B, R, nl, window, nch;
+  float eps, theta;
+  const uint16_t* taps;
+  const int32_t* anchor;
+  const int32_t* pred;
+  const int32_t* lens;
+  KV kv;
+  int32_t* out_ids;
+  float* out_logits;
+  DevWeights d;
+  SmallBufs s;
+};
+
+// Bytes of the small-path buffers for a window (nch = ceil(window / 128)).
+size_t small_bytes(int nch);
+void small_carve(char* base, int nch, SmallBufs* s);
+__host__ __device__ int small_phase_count(int nl);
+__host__ __device__ int small_phase_id(int nl, int i);
+// dev_args: a device copy of the SmallArgs.
+void launch_small_phase(hipStream_t st, const SmallArgs* dev_args, int G, int phase);
+hipError_t launch_small_mega(hipStream_t st, const SmallArgs* dev_args, int G);
+int small_mega_occupancy();
+
+}  // namespace kd

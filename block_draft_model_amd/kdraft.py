@@ -53,7 +53,7 @@ class KdKV(ctypes.Structure):
 EXPORTS = ["kd_default_config", "kd_create", "kd_load_weights", "kd_round", "kd_ingest",
            "kd_set_stream", "kd_destroy", "kd_status_string", "kd_last_error",
            "kd_probe_decode_e4m3", "kd_probe_decode_nvfp4", "kd_debug_set_layers",
-           "kd_debug_buffers"]
+           "kd_debug_buffers", "kd_debug_set_path", "kd_debug_last_path"]
 
 _lib = None
 
@@ -100,6 +100,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kd_debug_set_layers.restype = c_int
     lib.kd_debug_buffers.argtypes = [c_void_p, P(c_void_p), P(c_void_p)]
     lib.kd_debug_buffers.restype = c_int
+    lib.kd_debug_set_path.argtypes = [c_void_p, c_int]
+    lib.kd_debug_set_path.restype = c_int
+    lib.kd_debug_last_path.argtypes = [c_void_p]
+    lib.kd_debug_last_path.restype = c_int
     _lib = lib
     return lib
 
@@ -223,6 +227,14 @@ class Drafter:
 
     def debug_set_layers(self, n: int):
         self._check(self.lib.kd_debug_set_layers(self.ctx, int(n)), "kd_debug_set_layers")
+
+    def debug_set_path(self, path: int):
+        """0 automatic, 1 general multi-kernel, 2 small-batch phases as launches,
+        3 small-batch persistent kernel (paths 2, 3 only for <= 4 streams)."""
+        self._check(self.lib.kd_debug_set_path(self.ctx, int(path)), "kd_debug_set_path")
+
+    def last_path(self) -> int:
+        return int(self.lib.kd_debug_last_path(self.ctx))
 
     def debug_buffers(self):
         hid, fus = c_void_p(), c_void_p()

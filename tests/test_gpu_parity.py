@@ -73,12 +73,17 @@ def test_probe_nvfp4_decoder_is_exact():
     assert np.array_equal(got[fin], oracle.round_bf16(exact[fin]))
 
 
-def test_layer_by_layer_b1(hA):
+PATHS = [1, 2, 3]   # general multi-kernel, small-batch phases, small-batch persistent
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_layer_by_layer_b1(hA, path):
     """Bisection aid: hidden states after 0..4 layers against the oracle."""
     inp = hA.inputs(C[0])
     inp_np = synth.to_numpy_inputs(inp)
     M = hA.oracle
     full_layers = M.layers
+    hA.drafter.debug_set_path(path)
     try:
         for n in range(0, 5):
             hA.drafter.debug_set_layers(n)
@@ -94,18 +99,70 @@ def test_layer_by_layer_b1(hA):
                 f_ref = oracle.decode_bf16(inp_np["taps"]).reshape(1, -1) @ M.fuse.T
                 log("fused state rel err", np.linalg.norm(f_gpu - f_ref) / np.linalg.norm(f_ref))
             assert relx.max() < 1e-3
-            compare(lg, ids, ref, rid, M.vocab, f"layers={n}")
+            assert hA.drafter.last_path() == path
+            compare(lg, ids, ref, rid, M.vocab, f"path {path} layers={n}")
     finally:
         M.layers = full_layers
         hA.drafter.debug_set_layers(-1)
+        hA.drafter.debug_set_path(0)
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("ci", [0, 1])
-def test_round_parity_small_batches(hA, ci):
+def test_round_parity_small_batches(hA, ci, path):
     inp = hA.inputs(C[ci])
-    lg, ids = hA.run(inp)
+    hA.drafter.debug_set_path(path)
+    try:
+        lg, ids = hA.run(inp)
+        assert hA.drafter.last_path() == path
+    finally:
+        hA.drafter.debug_set_path(0)
     ref, rid = oracle.oracle_round(hA.oracle, synth.to_numpy_inputs(inp))
-    compare(lg, ids, ref, rid, hA.oracle.vocab, C[ci]["name"])
+    compare(lg, ids, ref, rid, hA.oracle.vocab, f"{C[ci]['name']} path {path}")
+
+
+@pytest.mark.parametrize("path", [2, 3])
+def test_small_path_adapters_gains_and_edges(hC, path):
+    """Active spine and predecessor adapters, random gains, and context
+    lengths 0, 1, a chunk boundary + 1 and past the ring, on the <= 4-stream path."""
+    lens = [0, 1, 129, 6000]
+    cfg = dict(name="small-edges", streams=4, lens=("const", 0), model="C", ingest=0)
+    inp = hC.inputs(cfg, base=23, lens_override=lens)
+    hC.drafter.debug_set_path(path)
+    try:
+        lg, ids = hC.run(inp)
+        assert hC.drafter.last_path() == path
+    finally:
+        hC.drafter.debug_set_path(0)
+    ref, rid = oracle.oracle_round(hC.oracle, synth.to_numpy_inputs(inp))
+    compare(lg, ids, ref, rid, hC.oracle.vocab, f"model C small path {path}")
+
+
+def test_small_paths_agree_bitwise_and_are_deterministic(hC):
+    cfg = dict(name="agree", streams=3, lens=("uniform", 1, 3000), model="C", ingest=0)
+    inp = hC.inputs(cfg, base=29)
+    outs = []
+    for path in (2, 3, 3, 2):
+        hC.drafter.debug_set_path(path)
+        outs.append(hC.run(inp))
+    hC.drafter.debug_set_path(0)
+    for lg, ids in outs[1:]:
+        assert np.array_equal(lg, outs[0][0]) and np.array_equal(ids, outs[0][1])
+
+
+def test_small_path_stream_alone_equals_stream_in_batch(hC):
+    cfg = dict(name="inv-small", streams=4, lens=("uniform", 10, 2048), model="C", ingest=0)
+    inp = hC.inputs(cfg, base=31)
+    hC.drafter.debug_set_path(0)
+    batch, ib = hC.run(inp)
+    assert hC.drafter.last_path() in (2, 3)
+    for b in range(4):
+        one = {k: (v[b:b + 1] if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+        one["k"] = [t[b:b + 1] for t in inp["k"]]
+        one["v"] = [t[b:b + 1] for t in inp["v"]]
+        one["streams"] = 1
+        alone, ia = hC.run(one)
+        assert np.array_equal(alone[0], batch[b]) and np.array_equal(ia[0], ib[b])
 
 
 def test_round_parity_adapters_and_gains_active(hC):
@@ -174,19 +231,23 @@ def test_round_parity_b256_sampled(hA):
     assert np.all(ids >= 0) and np.all(np.isin(ids, hA.oracle.vocab))
 
 
-def test_deterministic_and_logits_optional(hC):
+@pytest.mark.parametrize("path", PATHS)
+def test_deterministic_and_logits_optional(hC, path):
     cfg = dict(name="det", streams=3, lens=("uniform", 100, 2500), model="C", ingest=0)
     inp = hC.inputs(cfg, base=13)
+    hC.drafter.debug_set_path(path)
     a, ia = hC.run(inp)
     b, ib = hC.run(inp)
     assert np.array_equal(a, b) and np.array_equal(ia, ib)
     _, ic = hC.run(inp, logits=False)
+    hC.drafter.debug_set_path(0)
     assert np.array_equal(ia, ic)
 
 
 def test_stream_alone_equals_stream_in_batch(hC):
     cfg = dict(name="inv", streams=4, lens=("uniform", 10, 2048), model="C", ingest=0)
     inp = hC.inputs(cfg, base=17)
+    hC.drafter.debug_set_path(1)
     batch, ib = hC.run(inp)
     for b in range(4):
         one = {k: (v[b:b + 1] if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
@@ -195,6 +256,7 @@ def test_stream_alone_equals_stream_in_batch(hC):
         one["streams"] = 1
         alone, ia = hC.run(one)
         assert np.array_equal(alone[0], batch[b]) and np.array_equal(ia[0], ib[b])
+    hC.drafter.debug_set_path(0)
 
 
 def test_gpu_argument_errors(hC):
