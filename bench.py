@@ -83,6 +83,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--path", type=int, default=0,
+                    help="0 automatic; 1 general multi-kernel; 2 small-batch phases as "
+                         "separate launches; 3 small-batch persistent kernel")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -106,6 +109,7 @@ def main():
     stream = torch.cuda.current_stream()
     drafter = kdraft.Drafter(max_streams=B, stream=stream)
     drafter.load_weights(model)
+    drafter.debug_set_path(args.path)
     kv = kdraft.kv_struct(inp["k"], inp["v"])
     ids = torch.empty(B, 4, dtype=torch.int32, device="cuda")
     lens_host = inp["lens"].cpu().tolist()
@@ -126,6 +130,7 @@ def main():
     wall = time.perf_counter() - t0
     ms = start.elapsed_time(end) / args.steps
 
+    path = drafter.last_path()
     ab = algorithmic_bytes(dims, lens_host, B)
     rounds_s = 1000.0 / ms
     achieved = ab["total"] / (ms * 1e-3) / 1e9
@@ -139,7 +144,9 @@ def main():
            "config": {"workload": f"{cfg['name']}: {B} streams x 1 round, draft block 4, "
                                   f"context rows per stream {sorted(set(min(l, 2048) for l in lens_host))}, "
                                   f"block-FP8 body, NVFP4 head (60,614 rows)",
-                      "streams": B, "draft_tokens_per_round": 4 * B},
+                      "streams": B, "draft_tokens_per_round": 4 * B,
+                      "path": {1: "general multi-kernel", 2: "small-batch phases, one launch each",
+                               3: "small-batch persistent kernel"}[path]},
            "draft_tokens_per_s": round(4 * B * rounds_s, 1),
            "bytes_per_round": ab, "hbm_roofline_frac": round(achieved / HBM_PEAK_GBS, 4),
            "wall_s": round(wall, 3), "roofline": roofline}

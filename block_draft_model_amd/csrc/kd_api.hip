@@ -30,11 +30,14 @@ struct kd_ctx {
   char* small_mem = nullptr;
   kd::SmallBufs small{};
   int G = 0;                 // workgroups of the small path (one per CU, <= 256)
+  bool small_ok = false;     // the window fits the small path's attention phase
   bool mega_ok = false;      // persistent cooperative kernel available
   int path = 0;              // 0 auto, 1 general, 2 small per-phase, 3 small persistent
   kd::SmallArgs* args_dev = nullptr;   // device copy of the small-path arguments
   kd::SmallArgs* args_host = nullptr;  // pinned host copy last uploaded
   bool args_valid = false;
+  unsigned long long* trace = nullptr;  // caller's device buffer for stage timestamps
+  int trace_phases = 0;
 };
 
 namespace {
@@ -319,14 +322,22 @@ kd_status kd_create(const kd_config* cfg, void* hip_stream, kd_ctx** out) {
             dev_alloc(c->work_allocs, &w.att_o,
                       (size_t)w.Bmax * kd::NH * w.att_nch * kd::BLK * kd::DH) &&
             dev_alloc(c->work_allocs, &w.keys, (size_t)w.Rmax);
-  if (ok) {
+  hipDeviceProp_t prop;
+  const bool have_prop = hipGetDeviceProperties(&prop, c->device) == hipSuccess;
+  c->G = have_prop ? std::min(prop.multiProcessorCount, kd::MAX_G) : 128;
+  // the small-batch attention phase completes at most ATT_UNITS_MAX chunks per
+  // workgroup; longer windows run every round on the general path
+  c->small_ok = (long long)kd::SB_MAX * kd::NH * w.att_nch <= (long long)kd::ATT_UNITS_MAX * c->G;
+  if (ok && c->small_ok) {
     ok = dev_alloc(c->work_allocs, &c->small_mem, kd::small_bytes(w.att_nch)) &&
          dev_alloc(c->work_allocs, &c->args_dev, 1) &&
          hipHostMalloc((void**)&c->args_host, sizeof(kd::SmallArgs), hipHostMallocDefault) ==
              hipSuccess;
     if (ok) {
       kd::small_carve(c->small_mem, w.att_nch, &c->small);
-      ok = hipMemset(c->small.bar, 0, 19 * 32 * sizeof(unsigned)) == hipSuccess &&
+      ok = hipMemset(c->small.bar, 0, 20 * 32 * sizeof(unsigned)) == hipSuccess &&
+           hipMemset(c->small.att_cnt, 0, kd::NL * kd::SB_MAX * kd::NH * 32 * sizeof(unsigned)) ==
+               hipSuccess &&
            hipDeviceSynchronize() == hipSuccess;
     }
   }
@@ -336,13 +347,7 @@ kd_status kd_create(const kd_config* cfg, void* hip_stream, kd_ctx** out) {
     delete c;
     return KD_ERR_OOM;
   }
-  hipDeviceProp_t prop;
-  if (hipGetDeviceProperties(&prop, c->device) == hipSuccess) {
-    c->G = std::min(prop.multiProcessorCount, kd::MAX_G);
-    c->mega_ok = prop.cooperativeLaunch && kd::small_mega_occupancy() >= 1;
-  } else {
-    c->G = 128;
-  }
+  c->mega_ok = c->small_ok && have_prop && prop.cooperativeLaunch && kd::small_mega_occupancy() >= 1;
   (void)hipGetLastError();
   *out = c;
   return KD_OK;
@@ -491,7 +496,8 @@ kd_status kd_round(kd_ctx* c, int B, const void* taps, const int32_t* anchor, co
   const float eps = c->cfg.rms_eps;
   const int R = kd::BLK * B, B3 = 3 * B;
   int path = c->path;
-  if (path == 0) path = B <= kd::SB_MAX ? (c->mega_ok ? 3 : 2) : 1;
+  if (path == 0) path = B <= kd::SB_MAX && c->small_ok ? (c->mega_ok ? 3 : 2) : 1;
+  if (!c->small_ok) path = 1;
   if (path == 3 && !c->mega_ok) path = 2;
   if (path != 1 && B > kd::SB_MAX) path = 1;
   c->last_path = path;
@@ -515,6 +521,8 @@ kd_status kd_round(kd_ctx* c, int B, const void* taps, const int32_t* anchor, co
     a.out_logits = out_logits;
     a.d = d;
     a.s = c->small;
+    a.trace = c->trace;
+    a.trace_phases = c->trace_phases;
     // upload the argument block only when it changed (a serving loop that
     // reuses its buffers uploads it once)
     if (!c->args_valid || memcmp(c->args_host, &a, sizeof a) != 0) {
@@ -532,7 +540,7 @@ kd_status kd_round(kd_ctx* c, int B, const void* taps, const int32_t* anchor, co
       if (e != hipSuccess) return hip_fail(c, e, "persistent round launch");
     } else {
       for (int i = 0; i < np; ++i)
-        kd::launch_small_phase(st, c->args_dev, c->G, kd::small_phase_id(a.nl, i));
+        kd::launch_small_phase(st, c->args_dev, c->G, kd::small_phase_id(a.nl, i), i);
     }
     c->last_streams = B;
     const hipError_t e = hipGetLastError();
@@ -667,11 +675,22 @@ kd_status kd_debug_buffers(kd_ctx* c, const float** hidden, const float** fused)
 kd_status kd_debug_set_path(kd_ctx* c, int path) {
   if (!c) return KD_ERR_ARG;
   if (path < 0 || path > 3) return fail(c, KD_ERR_ARG, "path must be 0..3");
+  if (path >= 2 && !c->small_ok)
+    return fail(c, KD_ERR_UNSUPPORTED, "the window is too long for the small-batch path");
   if (path == 3 && !c->mega_ok) return fail(c, KD_ERR_UNSUPPORTED, "no cooperative launch");
   c->path = path;
   return KD_OK;
 }
 
 int kd_debug_last_path(const kd_ctx* c) { return c ? c->last_path : 0; }
+
+kd_status kd_debug_set_trace(kd_ctx* c, unsigned long long* buf, int phases, int* workgroups) {
+  if (!c) return KD_ERR_ARG;
+  if (buf && phases < 1) return fail(c, KD_ERR_ARG, "trace needs at least one phase row");
+  c->trace = buf;
+  c->trace_phases = buf ? phases : 0;
+  if (workgroups) *workgroups = c->G;
+  return KD_OK;
+}
 
 }  // extern "C"

@@ -7,40 +7,61 @@
 
 namespace kd {
 
+// Device code reads the structures below through global-address-space
+// pointers (a load through a generic pointer compiles to a flat access, which
+// also occupies the LDS wait counter); host code sees ordinary pointers. Both
+// views share one layout.
+#if defined(__HIP_DEVICE_COMPILE__)
+#define KD_GLOBAL __attribute__((address_space(1)))
+#else
+#define KD_GLOBAL
+#endif
+template <class T> using HostPtr = T*;
+template <class T> using GlobalPtr = KD_GLOBAL T*;
+
 // A repacked block-FP8 matrix on the device (layout in kd_device.h).
-struct Fp8Mat {
-  const uint8_t* w = nullptr;
-  const float* s = nullptr;
+template <template <class> class P>
+struct Fp8MatT {
+  P<const uint8_t> w = nullptr;
+  P<const float> s = nullptr;
   int N = 0, K = 0;
 };
 
-struct DevLayer {
-  Fp8Mat qkv, wo, gu, down, sa, su;
-  const float* attn_norm = nullptr;
-  const float* ffn_norm = nullptr;
-  const float* spine_norm = nullptr;
+template <template <class> class P>
+struct DevLayerT {
+  Fp8MatT<P> qkv, wo, gu, down, sa, su;
+  P<const float> attn_norm = nullptr;
+  P<const float> ffn_norm = nullptr;
+  P<const float> spine_norm = nullptr;
 };
 
-struct DevWeights {
-  Fp8Mat fuse, fc, pred_ab, pred_u;   // pred_ab = [A_p | B_p] along K
-  const float* mask = nullptr;
-  DevLayer layer[4];
-  const float* final_norm = nullptr;
-  const uint8_t* hq = nullptr;        // repacked NVFP4 codes
-  const uint8_t* hs = nullptr;        // repacked e4m3 block scales
+template <template <class> class P>
+struct DevWeightsT {
+  Fp8MatT<P> fuse, fc, pred_ab, pred_u;   // pred_ab = [A_p | B_p] along K
+  P<const float> mask = nullptr;
+  DevLayerT<P> layer[4];
+  P<const float> final_norm = nullptr;
+  P<const uint8_t> hq = nullptr;          // repacked NVFP4 codes
+  P<const uint8_t> hs = nullptr;          // repacked e4m3 block scales
   float hg = 1.f;
-  int VD = 0, VT = 0;                 // draft vocab rows, 16-row tiles
-  const int32_t* vocab = nullptr;
-  const uint16_t* table = nullptr;    // borrowed bf16 [full_vocab][H]
+  int VD = 0, VT = 0;                     // draft vocab rows, 16-row tiles
+  P<const int32_t> vocab = nullptr;
+  P<const uint16_t> table = nullptr;      // borrowed bf16 [full_vocab][H]
 };
 
 // Context K/V description passed to kernels.
-struct KV {
-  const uint16_t* k[4];
-  const uint16_t* v[4];
+template <template <class> class P>
+struct KVT {
+  P<const uint16_t> k[4];
+  P<const uint16_t> v[4];
   int64_t ss, sh, sl;
   int cap;
 };
+
+using Fp8Mat = Fp8MatT<HostPtr>;
+using DevLayer = DevLayerT<HostPtr>;
+using DevWeights = DevWeightsT<HostPtr>;
+using KV = KVT<HostPtr>;
 
 // Workspace (allocated once per context for max_streams).
 struct Work {

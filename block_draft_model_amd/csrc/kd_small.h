@@ -12,8 +12,9 @@ constexpr int SR_MAX = 16;     // block rows (one matrix-core row tile)
 constexpr int NXS = 12;        // residual-stream stages written in one round
 constexpr int HT = H / 16;     // 160 column tiles of a hidden vector
 constexpr int SMALL_WG = 512;  // 8 waves per workgroup
-constexpr int HEAD_NT = 4;     // vocab tiles per head unit
+constexpr int HEAD_NT = 2;     // vocab tiles per head unit
 constexpr int MAX_G = 256;     // workgroups (one per CU); barrier tree is 16 x 16
+constexpr int ATT_UNITS_MAX = 64;  // attention chunks one workgroup completes per layer
 
 // Stage index of the residual stream: the layer input, after O, after down.
 __host__ __device__ inline int xs_in(int l) { return l == 0 ? 0 : 3 * l; }
@@ -23,40 +24,51 @@ __host__ __device__ inline int xs_d(int l) { return 3 * l + 2; }
 // Buffers written at most once per round (so no cache ever holds a stale
 // copy within a launch); every buffer starts on a 256-byte boundary and no two
 // phases write into the same 128-byte line.
-struct SmallBufs {
-  float* f;                  // [SB][H]   fused tap state
-  float* fce;                // [SB][H]   fc (embedding half) . E[anchor]
-  float* pb;                 // [3SB][RK] B_p . E[pred]
-  float* sp;                 // [3SB][RK] silu(A_p f + B_p E[pred])
-  float* rope;               // [SR][64][2] cos, sin at the block positions
-  float* x[NXS];             // [SR][H]   residual stream stages
-  float* ssq[NXS];           // [SR][HT]  sum of squares of each 16-column tile
-  float* ss[NL];             // [3SB][RK] spine hidden (layers 1..3)
-  float* q[NL];              // [SR][H]   post-RoPE, natural head-major layout
-  float* k[NL];
-  float* v[NL];
-  float* am[NL];             // [SB][NH][nch][4] chunk max (log2 units)
-  float* al[NL];             // [SB][NH][nch][4] chunk sum of 2^(s - max)
-  float* ao[NL];             // [SB][NH][nch][4][DH]
-  float* o[NL];              // [SR][H]   merged attention output
-  float* h[NL];              // [SR][FF]  silu(gate) * up
-  unsigned long long* cand;  // [MAX_G][SR] per-workgroup argmax candidates
-  unsigned* bar;             // barrier: 16 group lines, top, generation, error (32 u32 each)
+template <template <class> class P>
+struct SmallBufsT {
+  P<float> f;                  // [SB][H]   fused tap state
+  P<float> fce;                // [SB][H]   fc (embedding half) . E[anchor]
+  P<float> pb;                 // [3SB][RK] B_p . E[pred]
+  P<float> sp;                 // [3SB][RK] silu(A_p f + B_p E[pred])
+  P<float> rope;               // [SR][64][2] cos, sin at the block positions
+  P<float> x[NXS];             // [SR][H]   residual stream stages
+  P<float> xg[NXS];            // [SR][H]   the stage times the RMSNorm gain of its consumer
+  P<float> ssq[NXS];           // [SR][HT]  sum of squares of each 16-column tile
+  P<float> ss[NL];             // [3SB][RK] spine hidden (layers 1..3)
+  P<float> q[NL];              // [SR][H]   post-RoPE, natural head-major layout
+  P<float> k[NL];
+  P<float> v[NL];
+  P<float> am[NL];             // [SB][NH][nch][4] chunk max (log2 units)
+  P<float> al[NL];             // [SB][NH][nch][4] chunk sum of 2^(s - max)
+  P<float> ao[NL];             // [SB][NH][nch][4][DH]
+  P<float> o[NL];              // [SR][H]   merged attention output
+  P<float> h[NL];              // [SR][FF]  silu(gate) * up
+  P<unsigned long long> cand;  // [MAX_G][SR] per-workgroup argmax candidates
+  P<unsigned> bar;             // barrier: 16 group lines, top, generation, error,
+                               // head counter (32 u32 each)
+  P<unsigned> att_cnt;         // [NL][SB][NH] chunk counters, one 128-byte line each
 };
 
-struct SmallArgs {
+template <template <class> class P>
+struct SmallArgsT {
   int B, R, nl, window, nch;
   float eps, theta;
-  const uint16_t* taps;
-  const int32_t* anchor;
-  const int32_t* pred;
-  const int32_t* lens;
-  KV kv;
-  int32_t* out_ids;
-  float* out_logits;
-  DevWeights d;
-  SmallBufs s;
+  P<const uint16_t> taps;
+  P<const int32_t> anchor;
+  P<const int32_t> pred;
+  P<const int32_t> lens;
+  KVT<P> kv;
+  P<int32_t> out_ids;
+  P<float> out_logits;
+  DevWeightsT<P> d;
+  SmallBufsT<P> s;
+  // Optional stage timestamps (100 MHz wall clock), [phase slot][G][8]; null = off.
+  P<unsigned long long> trace;
+  int trace_phases;
 };
+
+using SmallBufs = SmallBufsT<HostPtr>;
+using SmallArgs = SmallArgsT<HostPtr>;
 
 // Bytes of the small-path buffers for a window (nch = ceil(window / 128)).
 size_t small_bytes(int nch);
@@ -64,7 +76,7 @@ void small_carve(char* base, int nch, SmallBufs* s);
 __host__ __device__ int small_phase_count(int nl);
 __host__ __device__ int small_phase_id(int nl, int i);
 // dev_args: a device copy of the SmallArgs.
-void launch_small_phase(hipStream_t st, const SmallArgs* dev_args, int G, int phase);
+void launch_small_phase(hipStream_t st, const SmallArgs* dev_args, int G, int phase, int slot);
 hipError_t launch_small_mega(hipStream_t st, const SmallArgs* dev_args, int G);
 int small_mega_occupancy();
 

@@ -9,52 +9,98 @@
 //     SA   (l >= 1) ss = silu(A_s (g_s * x_{j-1}) / rms(x_{j-1}))
 //     SU   (l >= 1) x_j += U_s ss   (rows 1..3; row 0 copied)
 //     QKV  q,k,v = W_qkv (g_a * x) / rms(x), RoPE on q and k
-//     ATTN partial softmax over 128 context keys per (stream, head, chunk)
-//     MERGE chunks + the block's own keys (causal) -> o
+//     ATTN partial softmax over 128 context keys per (stream, head, chunk);
+//          the last chunk of a (stream, head) to finish merges all chunks with
+//          the block's own keys (causal) -> o
 //     O    x += W_o o
 //     GU   h = silu(W_g (g_f * x) / rms(x)) * (W_u (g_f * x) / rms(x))
 //     DOWN x += W_down h
-//   HEAD  logits = Head (g_o * x) / rms(x) * g_tensor -> per-workgroup argmax
-//   FINAL per-row argmax over workgroups -> target id
+//   HEAD  logits = Head (g_o * x) / rms(x) * g_tensor -> per-workgroup argmax;
+//         the last workgroup to finish reduces the candidates -> target ids
 //
 // A workgroup (8 waves) owns whole output tiles: its waves split the inputs,
 // an LDS reduction sums them in a fixed order, and the epilogue applies the
 // elementwise steps, so every phase writes final values once. RMSNorm is
-// deferred: the projection runs on g * x and the epilogue scales by 1/rms(x),
+// deferred: the projection runs on g * x (each producer of x also writes the
+// gained copy its matrix consumer needs) and the epilogue scales by 1/rms(x),
 // with rms from per-tile sums of squares written by the producer of x.
 //
 // In the persistent kernel, phases are separated by a two-level counter
 // barrier without cache-wide fences. That is safe because every buffer a phase
 // reads from another workgroup is written at most once per launch, with
-// write-through stores, and is not read before the barrier that follows the
-// write (L1/L2 are clean for these lines at kernel start). Each workgroup
-// issues the weight loads of its first unit of a phase before waiting at the
-// barrier, so weight streaming overlaps the synchronisation.
+// write-through stores, and is read only after the barrier (or counter) that
+// follows the write; L1/L2 hold no copy of those lines at kernel start. A
+// workgroup arrives at the barrier, issues the weight loads of its first unit
+// of the next phase, and only then waits, so weight streaming overlaps the
+// synchronisation.
 #include "kd_device.h"
 #include "kd_small.h"
 
 namespace kd {
+
+#define KD_CONST __attribute__((address_space(4)))
+#define KD_LDS __attribute__((address_space(3)))
+// The argument block as device code reads it: constant address space (scalar
+// loads), global-address-space pointers inside.
+typedef const SmallArgsT<GlobalPtr> KD_CONST Args;
+typedef const SmallBufsT<GlobalPtr> KD_CONST Bufs;
+typedef const Fp8MatT<GlobalPtr> KD_CONST Mat;
+typedef KD_LDS float* lds_f;
+typedef const KD_LDS float* lds_cf;
+template <class T> using gptr = KD_GLOBAL T*;
+static_assert(sizeof(SmallArgsT<GlobalPtr>) == sizeof(SmallArgs), "one layout for both views");
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 enum Phase {
   PH_PRE0 = 0, PH_PRE1 = 1, PH_PRE2 = 2,
-  PH_SA = 0, PH_SU = 1, PH_QKV = 2, PH_ATTN = 3, PH_MERGE = 4, PH_O = 5, PH_GU = 6, PH_DOWN = 7,
-  PH_HEAD = 3 + 8 * NL, PH_FINAL = 4 + 8 * NL
+  PH_SA = 0, PH_SU = 1, PH_QKV = 2, PH_ATTN = 3, PH_O = 5, PH_GU = 6, PH_DOWN = 7,
+  PH_HEAD = 3 + 8 * NL
 };
 
 // ---------------------------------------------------------------------------
 // Small helpers
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void st_wt(float* p, float v) {
+// The argument block's address is uniform, but a called (not inlined) phase
+// receives it in vector registers; re-establish it as a scalar so that the
+// fields are fetched with scalar loads.
+template <class T>
+__device__ __forceinline__ const T KD_CONST& uni(const T KD_CONST& a) {
+  const unsigned long long p = reinterpret_cast<unsigned long long>(&a);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)p);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(p >> 32));
+  return *reinterpret_cast<const T KD_CONST*>(((unsigned long long)hi << 32) | lo);
+}
+template <class T>
+__device__ __forceinline__ KD_GLOBAL T* uni(KD_GLOBAL T* q) {
+  const unsigned long long p = reinterpret_cast<unsigned long long>(q);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)p);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(p >> 32));
+  return reinterpret_cast<KD_GLOBAL T*>(((unsigned long long)hi << 32) | lo);
+}
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ void st_wt(gptr<float> p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void st_wt64(unsigned long long* p, unsigned long long v) {
+__device__ __forceinline__ void st_wt64(gptr<unsigned long long> p, unsigned long long v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ unsigned ld_rlx(unsigned* p) {
+__device__ __forceinline__ unsigned ld_rlx(gptr<unsigned> p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned add_rlx(gptr<unsigned> p, unsigned v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations, not for its outstanding global loads or stores.
+__device__ __forceinline__ void lds_sync() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left alone
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // e4m3 pairs -> bf16 pairs with unit scale (exact on gfx950).
@@ -109,40 +155,62 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64s(unsigned long long v
 // ---------------------------------------------------------------------------
 // Grid barrier: two-level counters (groups of 16 workgroups), monotonic so
 // nothing is ever reset, a generation word, and a wall-clock bound: after
-// 0.2 s the workgroup sets the error word and goes on, so every wave still
-// reaches the end of the kernel.
+// 0.2 s a workgroup sets the error word and goes on, so every wave still
+// reaches the end of the kernel. Split into arrive and wait so a workgroup can
+// issue loads of data it does not depend on in between.
 // ---------------------------------------------------------------------------
 struct SyncState {
-  unsigned epoch;  // barriers passed in this launch
   unsigned base;   // generation word at kernel start
+  int slot;        // phase index within the launch; phase i > 0 passes barrier i
 };
 
-__device__ void grid_sync(const SmallArgs& a, SyncState& sy) {
-  ++sy.epoch;
-  const unsigned target = sy.base + sy.epoch;
+// Stage timestamps for tracing: slot 0 barrier arrival, 1 barrier passed,
+// 2 unit inputs issued, 3 compute done, 4 epilogue done, 7 phase exit.
+__device__ __forceinline__ void trace_mark(Args& a, const SyncState sy, int k) {
+  if (a.trace && threadIdx.x == 0 && sy.slot < a.trace_phases)
+    a.trace[((size_t)sy.slot * gridDim.x + blockIdx.x) * 8 + k] = wall_clock64();
+}
+
+__device__ void grid_arrive(Args& a, SyncState sy) {
+  // every wave's global stores of the previous phase are acknowledged before
+  // thread 0 publishes the arrival
+  __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0)
   __syncthreads();
   if (threadIdx.x == 0) {
-    unsigned* bar = a.s.bar;
+    auto bar = a.s.bar;
     const unsigned G = gridDim.x, grp = blockIdx.x >> 4, ngrp = (G + 15) >> 4;
     const unsigned gsize = min(16u, G - grp * 16);
-    const unsigned v = __hip_atomic_fetch_add(&bar[grp * 32], 1u, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
+    trace_mark(a, sy, 0);
+    const unsigned v = add_rlx(&bar[grp * 32], 1u);
     if ((v + 1) % gsize == 0) {
-      const unsigned w = __hip_atomic_fetch_add(&bar[16 * 32], 1u, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned w = add_rlx(&bar[16 * 32], 1u);
       if ((w + 1) % ngrp == 0)
-        __hip_atomic_store(&bar[17 * 32], target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&bar[17 * 32], sy.base + (unsigned)sy.slot, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
+  }
+}
+
+__device__ void grid_wait(Args& a, SyncState sy) {
+  if (threadIdx.x == 0) {
+    auto bar = a.s.bar;
+    const unsigned target = sy.base + (unsigned)sy.slot;
     const unsigned long long t0 = wall_clock64();
     while ((int)(ld_rlx(&bar[17 * 32]) - target) < 0) {
-      if (wall_clock64() - t0 > 20000000ull) {      // 0.2 s at the 100 MHz wall clock
+      if (wall_clock64() - t0 > 20000000ull) {  // 0.2 s at the 100 MHz wall clock
         __hip_atomic_store(&bar[18 * 32], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
       __builtin_amdgcn_s_sleep(1);
     }
+    trace_mark(a, sy, 1);
   }
-  __syncthreads();
+  lds_sync();
+}
+
+__device__ __forceinline__ void grid_sync(Args& a, SyncState sy) {
+  grid_arrive(a, sy);
+  grid_wait(a, sy);
 }
 
 // ---------------------------------------------------------------------------
@@ -156,7 +224,7 @@ struct WRegs {
 };
 
 template <int NT, int KBS, int AW>
-__device__ __forceinline__ void load_w(WRegs<NT, KBS>& r, const Fp8Mat& W, int tile0, int ntv,
+__device__ __forceinline__ void load_w(WRegs<NT, KBS>& r, Mat& W, int tile0, int ntv,
                                        int kb0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int KB = W.K >> 6;
@@ -168,22 +236,20 @@ __device__ __forceinline__ void load_w(WRegs<NT, KBS>& r, const Fp8Mat& W, int t
       r.s[i][j] = 0.f;
       if (wave < AW && i < ntv) {
         const size_t blk = (size_t)(tile0 + i) * KB + kb0 + wave * KBS + j;
-        r.w[i][j] = *reinterpret_cast<const u32x4*>(W.w + blk * 1024 + lane * 16);
+        r.w[i][j] = *reinterpret_cast<gptr<const u32x4>>(W.w + blk * 1024 + lane * 16);
         r.s[i][j] = W.s[blk * 16 + (lane & 15)];
       }
     }
 }
 
-// Activation rows for the A operand.
+// Activation rows of the A operand (bf16 rows are exact: the lo plane is 0).
 struct ASrc {
-  const void* base;
+  gptr<const void> base;
   int ld;               // elements per row
   int mode;             // 0: row r; 1: row r/3; 2: row 4(r/3) + r%3; 3: row ids[r]
-  const int32_t* ids;
-  const float* gain;    // per-column gain, or null
+  gptr<const int32_t> ids;
   int kb_off;           // weight block of column 0
   int R;
-  int bf16;             // 1: bf16 rows (exact, lo = 0); 0: fp32 rows
 };
 
 __device__ __forceinline__ size_t a_row(const ASrc& A, int r) {
@@ -195,60 +261,85 @@ __device__ __forceinline__ size_t a_row(const ASrc& A, int r) {
   }
 }
 
-__device__ __forceinline__ void load_a(const ASrc& A, int kb, bf16x8& h0, bf16x8& l0, bf16x8& h1,
-                                       bf16x8& l1) {
+// Issues the loads of one 64-input block of the lane's row (no conversion).
+template <bool ABF>
+__device__ __forceinline__ void a_issue(const ASrc& A, int kb, u32x4 (&raw)[4]) {
   const int lane = threadIdx.x & 63, r = lane & 15;
-  const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-  h0 = l0 = h1 = l1 = z;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) raw[i] = u32x4{0u, 0u, 0u, 0u};
   if (r >= A.R) return;
   const int c0 = (kb - A.kb_off) * 64 + 8 * (lane >> 4);
   const size_t row = a_row(A, r);
-  if (A.bf16) {
-    const uint16_t* p = static_cast<const uint16_t*>(A.base) + row * A.ld + c0;
-    h0 = *reinterpret_cast<const bf16x8*>(p);
-    h1 = *reinterpret_cast<const bf16x8*>(p + 32);
-    return;
+  if (ABF) {
+    auto p = static_cast<gptr<const uint16_t>>(A.base) + row * A.ld + c0;
+    raw[0] = *reinterpret_cast<gptr<const u32x4>>(p);
+    raw[1] = *reinterpret_cast<gptr<const u32x4>>(p + 32);
+  } else {
+    auto p = static_cast<gptr<const float>>(A.base) + row * A.ld + c0;
+    raw[0] = *reinterpret_cast<gptr<const u32x4>>(p);
+    raw[1] = *reinterpret_cast<gptr<const u32x4>>(p + 4);
+    raw[2] = *reinterpret_cast<gptr<const u32x4>>(p + 32);
+    raw[3] = *reinterpret_cast<gptr<const u32x4>>(p + 36);
   }
-  const float* p = static_cast<const float*>(A.base) + row * A.ld + c0;
-  float v0[8], v1[8];
-  *reinterpret_cast<f32x4*>(v0) = *reinterpret_cast<const f32x4*>(p);
-  *reinterpret_cast<f32x4*>(v0 + 4) = *reinterpret_cast<const f32x4*>(p + 4);
-  *reinterpret_cast<f32x4*>(v1) = *reinterpret_cast<const f32x4*>(p + 32);
-  *reinterpret_cast<f32x4*>(v1 + 4) = *reinterpret_cast<const f32x4*>(p + 36);
-  if (A.gain) {
+}
+
+template <bool ABF>
+__device__ __forceinline__ void a_convert(const u32x4 (&raw)[4], bf16x8& h0, bf16x8& l0,
+                                          bf16x8& h1, bf16x8& l1) {
+  if (ABF) {
+    const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    h0 = __builtin_bit_cast(bf16x8, raw[0]);
+    h1 = __builtin_bit_cast(bf16x8, raw[1]);
+    l0 = l1 = z;
+  } else {
+    float v0[8], v1[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      v0[i] *= A.gain[c0 + i];
-      v1[i] *= A.gain[c0 + 32 + i];
+    for (int i = 0; i < 4; ++i) {
+      v0[i] = u2f(raw[0][i]);
+      v0[4 + i] = u2f(raw[1][i]);
+      v1[i] = u2f(raw[2][i]);
+      v1[4 + i] = u2f(raw[3][i]);
     }
+    split_bf16(v0, h0, l0);
+    split_bf16(v1, h1, l1);
   }
-  split_bf16(v0, h0, l0);
-  split_bf16(v1, h1, l1);
 }
 
 // Partial products of each wave into LDS: red[((wave*NT + i)*4 + e)*64 + lane].
-template <int NT, int KBS, int AW>
+// The A loads of up to C blocks are in flight together.
+template <int NT, int KBS, int AW, bool ABF>
 __device__ __forceinline__ void gemm_compute(const WRegs<NT, KBS>& r, const ASrc& A, int kb0,
-                                             float* red) {
+                                             lds_f red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int C = ABF ? (KBS < 8 ? KBS : 8) : (NT >= 3 ? 3 : (KBS <= 6 ? KBS : 4));
   f32x4 acc[NT];
 #pragma unroll
   for (int i = 0; i < NT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (wave < AW) {
 #pragma unroll
-    for (int j = 0; j < KBS; ++j) {
-      bf16x8 h0, l0, h1, l1;
-      load_a(A, kb0 + wave * KBS + j, h0, l0, h1, l1);
+    for (int c0 = 0; c0 < KBS; c0 += C) {
+      u32x4 raw[C][4];
 #pragma unroll
-      for (int i = 0; i < NT; ++i) {
-        const bf16x8 w0 = e4m3x8_bf16(r.w[i][j].x, r.w[i][j].y);
-        const bf16x8 w1 = e4m3x8_bf16(r.w[i][j].z, r.w[i][j].w);
-        f32x4 t = {0.f, 0.f, 0.f, 0.f};
-        t = mfma_bf16(h0, w0, t);
-        t = mfma_bf16(l0, w0, t);
-        t = mfma_bf16(h1, w1, t);
-        t = mfma_bf16(l1, w1, t);
-        acc[i] += r.s[i][j] * t;
+      for (int j = 0; j < C; ++j)
+        if (c0 + j < KBS) a_issue<ABF>(A, kb0 + wave * KBS + c0 + j, raw[j]);
+#pragma unroll
+      for (int j = 0; j < C; ++j) {
+        if (c0 + j < KBS) {
+          bf16x8 h0, l0, h1, l1;
+          a_convert<ABF>(raw[j], h0, l0, h1, l1);
+#pragma unroll
+          for (int i = 0; i < NT; ++i) {
+            const u32x4 wv = r.w[i][c0 + j];
+            const bf16x8 w0 = e4m3x8_bf16(wv.x, wv.y);
+            const bf16x8 w1 = e4m3x8_bf16(wv.z, wv.w);
+            f32x4 t = {0.f, 0.f, 0.f, 0.f};
+            t = mfma_bf16(h0, w0, t);
+            t = mfma_bf16(l0, w0, t);
+            t = mfma_bf16(h1, w1, t);
+            t = mfma_bf16(l1, w1, t);
+            acc[i] += r.s[i][c0 + j] * t;
+          }
+        }
       }
     }
   }
@@ -256,14 +347,14 @@ __device__ __forceinline__ void gemm_compute(const WRegs<NT, KBS>& r, const ASrc
   for (int i = 0; i < NT; ++i)
 #pragma unroll
     for (int e = 0; e < 4; ++e) red[((wave * NT + i) * 4 + e) * 64 + lane] = acc[i][e];
-  __syncthreads();
+  lds_sync();
 }
 
 // Sums the 8 waves' partials in a fixed order and calls f(i, m, n, v) for
 // output row m and column n of tile i. Within a wave the 64 items cover 4 rows
 // x 16 columns of one tile, so f may use shuffles across columns (xor 1..8).
 template <int NT, class F>
-__device__ __forceinline__ void gemm_epilogue(const float* red, F&& f) {
+__device__ __forceinline__ void gemm_epilogue(lds_cf red, F&& f) {
   for (int it = threadIdx.x; it < NT * 256; it += SMALL_WG) {
     const int i = it >> 8, m = (it >> 4) & 15, n = it & 15;
     const int L = 16 * (m >> 2) + n, e = m & 3;
@@ -272,25 +363,38 @@ __device__ __forceinline__ void gemm_epilogue(const float* red, F&& f) {
     for (int w = 0; w < 8; ++w) v += red[((w * NT + i) * 4 + e) * 64 + L];
     f(i, m, n, v);
   }
-  __syncthreads();
+  lds_sync();
 }
 
 // 1/rms of up to 16 rows of a residual stage from its per-tile sums of
-// squares, into LDS inv[16]; `map` gives the stage row of row r.
-template <class Map>
-__device__ __forceinline__ void inv_rms_rows(const float* ssq, int nrows, Map map, float eps,
-                                             float* inv) {
-  const int t = threadIdx.x, r = t >> 5, l32 = t & 31;
-  float sum = 0.f;
-  if (r < nrows) {
-    const float* p = ssq + (size_t)map(r) * HT;
-    for (int k = l32; k < HT; k += 32) sum += p[k];
-  }
+// squares. issue() loads, finish() reduces into LDS inv[16].
+struct RmsRows {
+  gptr<const float> ssq;
+  int nrows, mode;      // mode 0: row r; 2: row 4(r/3) + r%3
+  float eps;
+  lds_f inv;
+  float v[5];
+  __device__ __forceinline__ void issue() {
+    const int r = threadIdx.x >> 5, l32 = threadIdx.x & 31;
 #pragma unroll
-  for (int m = 16; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 64);
-  if (r < nrows && l32 == 0) inv[r] = 1.0f / sqrtf(sum / H + eps);
-  __syncthreads();
-}
+    for (int k = 0; k < 5; ++k) v[k] = 0.f;
+    if (ssq && r < nrows) {
+      const int row = mode == 2 ? 4 * (r / 3) + r % 3 : r;
+      auto p = ssq + (size_t)row * HT + l32;
+#pragma unroll
+      for (int k = 0; k < 5; ++k) v[k] = p[32 * k];
+    }
+  }
+  __device__ __forceinline__ void finish() {
+    if (!ssq) return;
+    const int r = threadIdx.x >> 5, l32 = threadIdx.x & 31;
+    float sum = v[0] + v[1] + v[2] + v[3] + v[4];
+#pragma unroll
+    for (int m = 16; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 64);
+    if (r < nrows && l32 == 0) inv[r] = 1.0f / sqrtf(sum / H + eps);
+    lds_sync();
+  }
+};
 
 // Sum of squares of this tile's 16 columns for the item's row (all lanes).
 __device__ __forceinline__ float tile_ssq(float x) {
@@ -300,32 +404,57 @@ __device__ __forceinline__ float tile_ssq(float x) {
   return s;
 }
 
-// One projection unit: prefetch weights, wait at the barrier if this is the
-// workgroup's first unit of the phase, then compute, reduce and run `epi`.
-template <int NT, int KBS, int AW, class Prep, class Epi>
-__device__ __forceinline__ void gemm_unit(const SmallArgs& a, SyncState& epoch, bool sync,
-                                          const Fp8Mat& W, int tile0, int ntv, int kb0,
-                                          const ASrc& A, float* red, Prep&& prep, Epi&& epi) {
+// One projection unit: if this is the workgroup's first unit of the phase,
+// arrive at the barrier, issue the weight loads, then wait; compute; reduce;
+// run `epi`.
+template <int NT, int KBS, int AW, bool ABF, class Epi>
+__device__ __forceinline__ void gemm_unit(Args& a, SyncState sy, bool sync,
+                                          Mat& W, int tile0, int ntv, int kb0,
+                                          const ASrc& A, lds_f red, RmsRows rms, Epi&& epi) {
+  if (sync) grid_arrive(a, sy);
   WRegs<NT, KBS> r;
   load_w<NT, KBS, AW>(r, W, tile0, ntv, kb0);
-  if (sync) grid_sync(a, epoch);
-  prep();
-  gemm_compute<NT, KBS, AW>(r, A, kb0, red);
+  if (sync) grid_wait(a, sy);
+  trace_mark(a, sy, 2);
+  rms.issue();
+  gemm_compute<NT, KBS, AW, ABF>(r, A, kb0, red);
+  rms.finish();
+  trace_mark(a, sy, 3);
   gemm_epilogue<NT>(red, epi);
+  trace_mark(a, sy, 4);
 }
 
-struct NoPrep {
-  __device__ void operator()() const {}
-};
+__device__ __forceinline__ RmsRows no_rms() { return RmsRows{nullptr, 0, 0, 0.f, nullptr, {}}; }
+
+// Stores one element of a residual stage: raw x, gained copy and (once per
+// tile row) the tile's sum of squares.
+__device__ __forceinline__ void put_x(Bufs& s, int stage, gptr<const float> gain, int row,
+                                      int col, int tile, int n, float x, bool ok) {
+  const float q = tile_ssq(x);
+  if (ok) {
+    st_wt(&s.x[stage][row * H + col], x);
+    st_wt(&s.xg[stage][row * H + col], x * gain[col]);
+    if (n == 0) st_wt(&s.ssq[stage][row * HT + tile], q);
+  }
+}
+
+// Gain of the matrix consumer of a residual stage.
+__device__ __forceinline__ gptr<const float> gain_in(Args& a, int l) {
+  return l < a.nl ? a.d.layer[l].attn_norm : a.d.final_norm;
+}
+__device__ __forceinline__ gptr<const float> gain_after_down(Args& a, int l) {
+  return l + 1 < a.nl ? a.d.layer[l + 1].spine_norm : a.d.final_norm;
+}
 
 // ---------------------------------------------------------------------------
 // Phases. `sync` is true when the phase must wait at a grid barrier first
-// (persistent kernel); every workgroup then calls grid_sync exactly once.
+// (persistent kernel); every workgroup then passes exactly one barrier.
 // ---------------------------------------------------------------------------
-__device__ __attribute__((noinline)) void ph_pre0(const SmallArgs& a, float* red, SyncState& epoch) {
+__device__ __attribute__((noinline, not_tail_called)) void ph_pre0(Args& a_, lds_f red, SyncState sy) {
+  Args& a = uni(a_);
   const int G = gridDim.x, wg = blockIdx.x;
-  const SmallBufs& s = a.s;
-  const DevWeights& d = a.d;
+  auto& s = a.s;
+  auto& d = a.d;
   const int B = a.B, R = a.R;
   // RoPE table for every block row: positions len + j, angles in fp64.
   if (wg == G - 1) {
@@ -340,160 +469,165 @@ __device__ __attribute__((noinline)) void ph_pre0(const SmallArgs& a, float* red
   const int n_fuse = HT, n_fce = HT, n_pb = RK / 16;
   for (int u = wg; u < n_fuse + n_fce + n_pb; u += G) {
     if (u < n_fuse) {
-      const ASrc A{a.taps, NTAP * H, 0, nullptr, nullptr, 0, B, 1};
-      gemm_unit<1, 15, 8>(a, epoch, false, d.fuse, u, 1, 0, A, red, NoPrep{},
-                          [&](int, int m, int n, float v) {
-                            if (m < B) st_wt(&s.f[m * H + u * 16 + n], v);
-                          });
+      const ASrc A{a.taps, NTAP * H, 0, nullptr, 0, B};
+      gemm_unit<1, 15, 8, true>(a, sy, false, d.fuse, u, 1, 0, A, red, no_rms(),
+                                [&](int, int m, int n, float v) {
+                                  if (m < B) st_wt(&s.f[m * H + u * 16 + n], v);
+                                });
     } else if (u < n_fuse + n_fce) {
       const int t = u - n_fuse;
-      const ASrc A{d.table, H, 3, a.anchor, nullptr, 40, B, 1};
-      gemm_unit<1, 5, 8>(a, epoch, false, d.fc, t, 1, 40, A, red, NoPrep{},
-                         [&](int, int m, int n, float v) {
-                           if (m < B) st_wt(&s.fce[m * H + t * 16 + n], v);
-                         });
+      const ASrc A{d.table, H, 3, a.anchor, 40, B};
+      gemm_unit<1, 5, 8, true>(a, sy, false, d.fc, t, 1, 40, A, red, no_rms(),
+                               [&](int, int m, int n, float v) {
+                                 if (m < B) st_wt(&s.fce[m * H + t * 16 + n], v);
+                               });
     } else {
       const int t = u - n_fuse - n_fce;
-      const ASrc A{d.table, H, 3, a.pred, nullptr, 40, 3 * B, 1};
-      gemm_unit<1, 5, 8>(a, epoch, false, d.pred_ab, t, 1, 40, A, red, NoPrep{},
-                         [&](int, int m, int n, float v) {
-                           if (m < 3 * B) st_wt(&s.pb[m * RK + t * 16 + n], v);
-                         });
+      const ASrc A{d.table, H, 3, a.pred, 40, 3 * B};
+      gemm_unit<1, 5, 8, true>(a, sy, false, d.pred_ab, t, 1, 40, A, red, no_rms(),
+                               [&](int, int m, int n, float v) {
+                                 if (m < 3 * B) st_wt(&s.pb[m * RK + t * 16 + n], v);
+                               });
     }
   }
 }
 
-__device__ __attribute__((noinline)) void ph_pre1(const SmallArgs& a, float* red, SyncState& epoch, bool sync) {
+__device__ __attribute__((noinline, not_tail_called)) void ph_pre1(Args& a_, lds_f red, SyncState sy,
+                                                  bool sync) {
+  Args& a = uni(a_);
   const int G = gridDim.x, wg = blockIdx.x;
-  const SmallBufs& s = a.s;
-  const DevWeights& d = a.d;
+  auto& s = a.s;
+  auto& d = a.d;
   const int B = a.B;
+  auto gain = gain_in(a, 0);
   bool first = sync;
   for (int u = wg; u < HT + RK / 16; u += G) {
     if (u < HT) {
-      const ASrc A{s.f, H, 0, nullptr, nullptr, 0, B, 0};
-      gemm_unit<1, 5, 8>(a, epoch, first, d.fc, u, 1, 0, A, red, NoPrep{},
-                         [&](int, int m, int n, float v) {
-                           const int col = u * 16 + n;
-                           const float x = v + (m < B ? s.fce[m * H + col] : 0.f);
-                           const float q = tile_ssq(x);
-                           if (m < B) {
-                             st_wt(&s.x[0][(4 * m) * H + col], x);
-                             if (n == 0) st_wt(&s.ssq[0][(4 * m) * HT + u], q);
-                           }
-                         });
+      const ASrc A{s.f, H, 0, nullptr, 0, B};
+      gemm_unit<1, 5, 8, false>(a, sy, first, d.fc, u, 1, 0, A, red, no_rms(),
+                                [&](int, int m, int n, float v) {
+                                  const int col = u * 16 + n;
+                                  const float x = v + (m < B ? s.fce[m * H + col] : 0.f);
+                                  put_x(s, 0, gain, 4 * m, col, u, n, x, m < B);
+                                });
     } else {
       const int t = u - HT;
-      const ASrc A{s.f, H, 1, nullptr, nullptr, 0, 3 * B, 0};
-      gemm_unit<1, 5, 8>(a, epoch, first, d.pred_ab, t, 1, 0, A, red, NoPrep{},
-                         [&](int, int m, int n, float v) {
-                           if (m < 3 * B) {
-                             const int c = t * 16 + n;
-                             st_wt(&s.sp[m * RK + c], silu(v + s.pb[m * RK + c]));
-                           }
-                         });
+      const ASrc A{s.f, H, 1, nullptr, 0, 3 * B};
+      gemm_unit<1, 5, 8, false>(a, sy, first, d.pred_ab, t, 1, 0, A, red, no_rms(),
+                                [&](int, int m, int n, float v) {
+                                  if (m < 3 * B) {
+                                    const int c = t * 16 + n;
+                                    st_wt(&s.sp[m * RK + c], silu(v + s.pb[m * RK + c]));
+                                  }
+                                });
     }
     first = false;
   }
-  if (first) grid_sync(a, epoch);
+  if (first) grid_sync(a, sy);
 }
 
-__device__ __attribute__((noinline)) void ph_pre2(const SmallArgs& a, float* red, SyncState& epoch, bool sync) {
+__device__ __attribute__((noinline, not_tail_called)) void ph_pre2(Args& a_, lds_f red, SyncState sy,
+                                                  bool sync) {
+  Args& a = uni(a_);
   const int G = gridDim.x, wg = blockIdx.x;
-  const SmallBufs& s = a.s;
-  const DevWeights& d = a.d;
+  auto& s = a.s;
+  auto& d = a.d;
   const int B = a.B;
+  auto gain = gain_in(a, 0);
   bool first = sync;
   for (int u = wg; u < HT; u += G) {
-    const ASrc A{s.sp, RK, 0, nullptr, nullptr, 0, 3 * B, 0};
-    gemm_unit<1, 1, 4>(a, epoch, first, d.pred_u, u, 1, 0, A, red, NoPrep{},
-                       [&](int, int m, int n, float v) {
-                         const int col = u * 16 + n;
-                         const int row = 4 * (m / 3) + m % 3 + 1;
-                         const float x =
-                             m < 3 * B ? d.mask[col] + s.f[(m / 3) * H + col] + v : 0.f;
-                         const float q = tile_ssq(x);
-                         if (m < 3 * B) {
-                           st_wt(&s.x[0][row * H + col], x);
-                           if (n == 0) st_wt(&s.ssq[0][row * HT + u], q);
-                         }
-                       });
+    const ASrc A{s.sp, RK, 0, nullptr, 0, 3 * B};
+    gemm_unit<1, 1, 4, false>(a, sy, first, d.pred_u, u, 1, 0, A, red, no_rms(),
+                              [&](int, int m, int n, float v) {
+                                const int col = u * 16 + n;
+                                const bool ok = m < 3 * B;
+                                const float x = ok ? d.mask[col] + s.f[(m / 3) * H + col] + v : 0.f;
+                                put_x(s, 0, gain, 4 * (m / 3) + m % 3 + 1, col, u, n, x, ok);
+                              });
     first = false;
   }
-  if (first) grid_sync(a, epoch);
+  if (first) grid_sync(a, sy);
 }
 
 // Spine A: ss = silu(A_s (g_s * x_{j-1}) / rms(x_{j-1})) for rows j = 1..3.
-__device__ __attribute__((noinline)) void ph_sa(const SmallArgs& a, int l, float* red, SyncState& epoch, bool sync) {
+__device__ __attribute__((noinline, not_tail_called)) void ph_sa(Args& a_, int l_, lds_f red,
+                                                SyncState sy, bool sync) {
+  const auto l = uni(l_);
+  Args& a = uni(a_);
   const int G = gridDim.x, wg = blockIdx.x;
-  const SmallBufs& s = a.s;
-  const DevLayer& L = a.d.layer[l];
+  auto& s = a.s;
+  auto& L = a.d.layer[l];
   const int B = a.B, src = xs_d(l - 1);
-  float* inv = red + 8192;
+  lds_f inv = red + 8192;
   bool first = sync;
   for (int u = wg; u < RK / 16; u += G) {
-    const ASrc A{s.x[src], H, 2, nullptr, L.spine_norm, 0, 3 * B, 0};
-    gemm_unit<1, 5, 8>(
-        a, epoch, first, L.sa, u, 1, 0, A, red,
-        [&] { inv_rms_rows(s.ssq[src], 3 * B, [](int r) { return 4 * (r / 3) + r % 3; }, a.eps, inv); },
-        [&](int, int m, int n, float v) {
-          if (m < 3 * B) st_wt(&s.ss[l][m * RK + u * 16 + n], silu(v * inv[m]));
-        });
+    const ASrc A{s.xg[src], H, 2, nullptr, 0, 3 * B};
+    gemm_unit<1, 5, 8, false>(a, sy, first, L.sa, u, 1, 0, A, red,
+                              RmsRows{s.ssq[src], 3 * B, 2, a.eps, inv, {}},
+                              [&](int, int m, int n, float v) {
+                                if (m < 3 * B) st_wt(&s.ss[l][m * RK + u * 16 + n], silu(v * inv[m]));
+                              });
     first = false;
   }
-  if (first) grid_sync(a, epoch);
+  if (first) grid_sync(a, sy);
 }
 
-// Spine U: x_j (j = 1..3) = x_{j} + U_s ss; row 0 copied into the new stage.
-__device__ __attribute__((noinline)) void ph_su(const SmallArgs& a, int l, float* red, SyncState& epoch, bool sync) {
+// Spine U: x_j (j = 1..3) += U_s ss; row 0 copied into the new stage.
+__device__ __attribute__((noinline, not_tail_called)) void ph_su(Args& a_, int l_, lds_f red,
+                                                SyncState sy, bool sync) {
+  const auto l = uni(l_);
+  Args& a = uni(a_);
   const int G = gridDim.x, wg = blockIdx.x;
-  const SmallBufs& s = a.s;
-  const DevLayer& L = a.d.layer[l];
+  auto& s = a.s;
+  auto& L = a.d.layer[l];
   const int B = a.B, src = xs_d(l - 1), dst = xs_in(l);
+  auto gain = gain_in(a, l);
   bool first = sync;
   for (int u = wg; u < HT; u += G) {
-    const ASrc A{s.ss[l], RK, 0, nullptr, nullptr, 0, 3 * B, 0};
-    gemm_unit<1, 1, 4>(a, epoch, first, L.su, u, 1, 0, A, red, NoPrep{},
-                       [&](int, int m, int n, float v) {
-                         const int col = u * 16 + n;
-                         const int row = 4 * (m / 3) + m % 3 + 1;
-                         const float x = m < 3 * B ? s.x[src][row * H + col] + v : 0.f;
-                         const float q = tile_ssq(x);
-                         if (m < 3 * B) {
-                           st_wt(&s.x[dst][row * H + col], x);
-                           if (n == 0) st_wt(&s.ssq[dst][row * HT + u], q);
-                         }
-                       });
+    const ASrc A{s.ss[l], RK, 0, nullptr, 0, 3 * B};
+    gemm_unit<1, 1, 4, false>(a, sy, first, L.su, u, 1, 0, A, red, no_rms(),
+                              [&](int, int m, int n, float v) {
+                                const int col = u * 16 + n;
+                                const int row = 4 * (m / 3) + m % 3 + 1;
+                                const bool ok = m < 3 * B;
+                                const float x = ok ? s.x[src][row * H + col] + v : 0.f;
+                                put_x(s, dst, gain, row, col, u, n, x, ok);
+                              });
     // row 0 of every stream is untouched by the spine
     for (int t = threadIdx.x; t < B * 17; t += SMALL_WG) {
-      const int b = t / 17, c = t % 17, row = 4 * b;
-      if (c < 16)
-        st_wt(&s.x[dst][row * H + u * 16 + c], s.x[src][row * H + u * 16 + c]);
-      else
+      const int b = t / 17, c = t % 17, row = 4 * b, col = u * 16 + c;
+      if (c < 16) {
+        const float x = s.x[src][row * H + col];
+        st_wt(&s.x[dst][row * H + col], x);
+        st_wt(&s.xg[dst][row * H + col], x * gain[col]);
+      } else {
         st_wt(&s.ssq[dst][row * HT + u], s.ssq[src][row * HT + u]);
+      }
     }
     first = false;
   }
-  if (first) grid_sync(a, epoch);
+  if (first) grid_sync(a, sy);
 }
 
 // q|k|v = W (g_a * x) / rms(x); RoPE on q and k inside each paired tile.
-__device__ __attribute__((noinline)) void ph_qkv(const SmallArgs& a, int l, float* red, SyncState& epoch, bool sync) {
+__device__ __attribute__((noinline, not_tail_called)) void ph_qkv(Args& a_, int l_, lds_f red,
+                                                 SyncState sy, bool sync) {
+  const auto l = uni(l_);
+  Args& a = uni(a_);
   const int G = gridDim.x, wg = blockIdx.x;
-  const SmallBufs& s = a.s;
-  const DevLayer& L = a.d.layer[l];
+  auto& s = a.s;
+  auto& L = a.d.layer[l];
   const int R = a.R, src = xs_in(l);
-  float* inv = red + 8192;
+  lds_f inv = red + 8192;
   constexpr int NT = 2, NTILE = QKV / 16, NU = NTILE / NT;
   bool first = sync;
   for (int u = wg; u < NU; u += G) {
-    const ASrc A{s.x[src], H, 0, nullptr, L.attn_norm, 0, R, 0};
-    gemm_unit<NT, 5, 8>(
-        a, epoch, first, L.qkv, u * NT, NT, 0, A, red,
-        [&] { inv_rms_rows(s.ssq[src], R, [](int r) { return r; }, a.eps, inv); },
+    const ASrc A{s.xg[src], H, 0, nullptr, 0, R};
+    gemm_unit<NT, 5, 8, false>(
+        a, sy, first, L.qkv, u * NT, NT, 0, A, red, RmsRows{s.ssq[src], R, 0, a.eps, inv, {}},
         [&](int i, int m, int n, float v) {
           const int t = u * NT + i, sec = t / HT;
-          const int nat = qkv_natural(t * 16 + n) - sec * H;      // column within q, k or v
+          const int nat = qkv_natural(t * 16 + n) - sec * H;  // column within q, k or v
           const float val = m < R ? v * inv[m] : 0.f;
           const float partner = __shfl_xor(val, 8, 64);
           float out = val;
@@ -504,104 +638,296 @@ __device__ __attribute__((noinline)) void ph_qkv(const SmallArgs& a, int l, floa
             out = n < 8 ? val * cs - partner * sn : partner * sn + val * cs;
           }
           if (m < R) {
-            float* dstp = sec == 0 ? s.q[l] : (sec == 1 ? s.k[l] : s.v[l]);
+            gptr<float> dstp = sec == 0 ? s.q[l] : (sec == 1 ? s.k[l] : s.v[l]);
             st_wt(&dstp[m * H + nat], out);
           }
         });
     first = false;
   }
-  if (first) grid_sync(a, epoch);
+  if (first) grid_sync(a, sy);
+}
+
+// Cross-lane steps inside a wavefront without LDS traffic. row16_sum: sum
+// over the 16 lanes of each row by DPP (quad swaps, then the half-row and row
+// mirrors; every lane ends with the same bits). rows_sum_to_row3: per lane
+// position, the sum over the 4 rows, valid in row 3 only; it uses the first
+// result of the gfx950 row-swap permutes (which moves row 0 to row 1, row 2 to
+// row 3, and then the lower half to the upper half). rows_max4 / rows_sum4:
+// combine a value that is uniform within each row across the 4 rows, in every
+// lane, through scalar lane reads.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF,
+                                                            0xF, true));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp<0x141>(x);  // row_half_mirror
+  x += dpp<0x140>(x);  // row_mirror
+  return x;
+}
+__device__ __forceinline__ float rows_sum_to_row3(float x) {
+  const unsigned xb = __builtin_bit_cast(unsigned, x);
+  const float s = x + __builtin_bit_cast(float, __builtin_amdgcn_permlane16_swap(xb, xb, false, false)[0]);
+  const unsigned sb = __builtin_bit_cast(unsigned, s);
+  return s + __builtin_bit_cast(float, __builtin_amdgcn_permlane32_swap(sb, sb, false, false)[0]);
+}
+__device__ __forceinline__ float lane_read(float x, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+__device__ __forceinline__ float rows_max4(float x) {
+  return fmaxf(fmaxf(lane_read(x, 0), lane_read(x, 16)), fmaxf(lane_read(x, 32), lane_read(x, 48)));
+}
+__device__ __forceinline__ float rows_sum4(float x) {
+  return (lane_read(x, 0) + lane_read(x, 16)) + (lane_read(x, 32) + lane_read(x, 48));
+}
+
+// Context rows of each stream of the round, read once per phase; kept as
+// separate scalars (an indexed array would live in scratch memory).
+__device__ __forceinline__ int pick4(int b, int x0, int x1, int x2, int x3) {
+  return b == 0 ? x0 : (b == 1 ? x1 : (b == 2 ? x2 : x3));
+}
+struct StreamLens {
+  int n0, n1, n2, n3;      // visible context rows min(len, window)
+  int f0, f1, f2, f3;      // position of the first visible row
+  int o1, o2, o3, total;   // first attention unit of streams 1..3; all units
+  __device__ __forceinline__ void load(Args& a) {
+    const int B = a.B, W = a.window;
+    const int l0 = __builtin_amdgcn_readfirstlane(a.lens[0]);
+    const int l1 = B > 1 ? __builtin_amdgcn_readfirstlane(a.lens[1]) : 0;
+    const int l2 = B > 2 ? __builtin_amdgcn_readfirstlane(a.lens[2]) : 0;
+    const int l3 = B > 3 ? __builtin_amdgcn_readfirstlane(a.lens[3]) : 0;
+    n0 = min(l0, W); n1 = min(l1, W); n2 = min(l2, W); n3 = min(l3, W);
+    f0 = l0 - n0; f1 = l1 - n1; f2 = l2 - n2; f3 = l3 - n3;
+    o1 = NH * ((n0 + ATT_CH - 1) / ATT_CH);
+    o2 = o1 + NH * ((n1 + ATT_CH - 1) / ATT_CH);
+    o3 = o2 + NH * ((n2 + ATT_CH - 1) / ATT_CH);
+    total = o3 + NH * ((n3 + ATT_CH - 1) / ATT_CH);
+  }
+  __device__ __forceinline__ int vis(int b) const { return pick4(b, n0, n1, n2, n3); }
+  __device__ __forceinline__ int first(int b) const { return pick4(b, f0, f1, f2, f3); }
+  // Unit u -> stream b, chunk c, head h (stream-major, then chunk, then head,
+  // so the chunks of one (stream, head) lie NH units apart). A stream with no
+  // units shares its offset with the next one, which then wins.
+  __device__ __forceinline__ void unit(int u, int& b, int& c, int& h) const {
+    b = u >= o3 ? 3 : (u >= o2 ? 2 : (u >= o1 ? 1 : 0));
+    const int loc = u - pick4(b, 0, o1, o2, o3);
+    c = loc / NH;
+    h = loc - c * NH;
+  }
+};
+
+// Merge of the chunk partials of one (stream, head) with the block's own keys
+// (row j sees block rows 0..j); thread (j, d). Called by the workgroup whose
+// chunk completed the (stream, head), after the completion counter says so.
+__device__ __attribute__((noinline, not_tail_called)) void attn_merge(Args& a_, int l_, int b_, int h_, int n_,
+                                                     lds_f red) {
+  const auto l = uni(l_);
+  const auto b = uni(b_);
+  const auto h = uni(h_);
+  const auto n = uni(n_);
+  Args& a = uni(a_);
+  auto& s = a.s;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nch = a.nch;
+  const float qs = 0.08838834764831845f * 1.4426950408889634f;  // 1/sqrt(128) * log2(e)
+  const int nc = (n + ATT_CH - 1) / ATT_CH;
+  const int j = threadIdx.x >> 7, dd = threadIdx.x & 127;
+  constexpr int MAXC = 16;
+  float pm[MAXC], pl[MAXC], po[MAXC];
+  const size_t base = (size_t)(b * NH + h) * nch;
+  auto am = s.am[l] + base * 4 + j;
+  auto al = s.al[l] + base * 4 + j;
+  auto ao = s.ao[l] + (base * 4 + j) * DH + dd;
+  // every load issued together: chunks past the last one re-read it and are
+  // masked afterwards
+  const int clast = max(nc - 1, 0);
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    const int cc = min(c, clast);
+    pm[c] = am[cc * 4];
+    pl[c] = al[cc * 4];
+    po[c] = ao[(size_t)cc * 4 * DH];
+  }
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c)
+    if (c >= nc) {
+      pm[c] = -__builtin_inff();
+      pl[c] = 0.f;
+      po[c] = 0.f;
+    }
+  for (int c = MAXC; c < nc; ++c) {  // windows beyond 2048 rows: fold the rest in
+    const float m1 = am[c * 4];
+    const float mn = fmaxf(pm[0], m1);
+    const float f0 = exp2f(pm[0] - mn), f1 = exp2f(m1 - mn);
+    pl[0] = pl[0] * f0 + al[c * 4] * f1;
+    po[0] = po[0] * f0 + ao[(size_t)c * 4 * DH] * f1;
+    pm[0] = mn;
+  }
+  float vv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) vv[i] = s.v[l][(b * 4 + i) * H + h * DH + dd];
+  {
+    // block scores s[j][i] = q_j . k_i: wave w covers row w/2, dims 64*(w%2)..
+    const int jw = wave >> 1, dw = 64 * (wave & 1) + lane;
+    const float qv = s.q[l][(b * 4 + jw) * H + h * DH + dw];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = wave_sum(qv * s.k[l][(b * 4 + i) * H + h * DH + dw]);
+      if (lane == 0) red[wave * 4 + i] = p;
+    }
+  }
+  lds_sync();
+  float sb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sb[i] = (red[(2 * j) * 4 + i] + red[(2 * j + 1) * 4 + i]) * qs;
+  float M = -__builtin_inff();
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) M = fmaxf(M, pm[c]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (i <= j) M = fmaxf(M, sb[i]);
+  float Ls = 0.f, O = 0.f;
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    if (pm[c] != -__builtin_inff()) {
+      const float f = exp2f(pm[c] - M);
+      Ls += pl[c] * f;
+      O += po[c] * f;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (i <= j) {
+      const float f = exp2f(sb[i] - M);
+      Ls += f;
+      O += f * vv[i];
+    }
+  st_wt(&s.o[l][(b * 4 + j) * H + h * DH + dd], O / Ls);
+  lds_sync();
 }
 
 // Attention over one chunk of 128 context keys for one (stream, head):
-// wave w takes keys 16w..16w+15 (4 keys per step, 16 lanes x 8 dims per key).
-__device__ __attribute__((noinline)) void ph_attn(const SmallArgs& a, int l, float* red, SyncState& epoch, bool sync) {
+// wave w takes keys 16w..16w+15 (4 keys per step: row g of the wave holds key
+// 4 step + g, 16 lanes x 8 dims per key).
+// The next unit's keys, values and queries are loaded while one is computed.
+// A (stream, head) is complete when all its chunks have stored their partials;
+// completion counters are taken once, after the workgroup's last unit, and the
+// workgroup that completes a (stream, head) merges it.
+__device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int l_, lds_f red, SyncState sy,
+                                                  bool sync) {
+  const auto l = uni(l_);
+  Args& a = uni(a_);
   const int G = gridDim.x, wg = blockIdx.x;
-  const SmallBufs& s = a.s;
+  auto& s = a.s;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, d0 = (lane & 15) * 8;
-  const int nch = a.nch, nunits = a.B * NH * nch;
-  const float qs = 0.08838834764831845f * 1.4426950408889634f;  // 1/sqrt(128) * log2(e)
-  float* s_o = red;                   // [8][4][128]
-  float* s_m = red + 8 * 4 * DH;      // [8][4]
-  float* s_l = s_m + 32;              // [8][4]
-  bool first = sync;
-  for (int u = wg; u < nunits; u += G) {
-    const int b = u / (NH * nch), h = (u / nch) % NH, c = u % nch;
-    const int len = a.lens[b];
-    const int n = min(len, a.window), first_pos = len - n;
-    const bool active = c * ATT_CH < n;
-    u32x4 kr[4], vr[4];
-    const uint16_t* kbase = a.kv.k[l] + b * a.kv.ss + h * a.kv.sh + d0;
-    const uint16_t* vbase = a.kv.v[l] + b * a.kv.ss + h * a.kv.sh + d0;
+  const int nch = a.nch;
+  const float qs = 0.08838834764831845f * 1.4426950408889634f;
+  lds_f s_o = red;                    // [8][4][128]
+  lds_f s_m = red + 8 * 4 * DH;       // [8][4]
+  lds_f s_l = s_m + 32;               // [8][4]
+  lds_f s_q = s_l + 32;               // [4][128] queries of the unit, scaled
+  KD_LDS unsigned* s_list = reinterpret_cast<KD_LDS unsigned*>(s_q + 4 * DH);  // [1 + ATT_UNITS_MAX]
+
+  if (sync) grid_arrive(a, sy);
+  StreamLens sl;
+  sl.load(a);
+  const int nunits = sl.total;
+  auto load_unit = [&](int u, u32x4 (&kr)[4], u32x4 (&vr)[4], float& qr) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st) kr[st] = vr[st] = u32x4{0u, 0u, 0u, 0u};
+    qr = 0.f;
+    if (u >= nunits) return;
+    int b, c, h;
+    sl.unit(u, b, c, h);
+    const int n = sl.vis(b), fp = sl.first(b);
+    auto kbase = a.kv.k[l] + b * a.kv.ss + h * a.kv.sh + d0;
+    auto vbase = a.kv.v[l] + b * a.kv.ss + h * a.kv.sh + d0;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const int idx = c * ATT_CH + wave * 16 + st * 4 + g;
-      kr[st] = vr[st] = u32x4{0u, 0u, 0u, 0u};
-      if (active && idx < n) {
-        const int slot = (first_pos + idx) % a.kv.cap;
-        kr[st] = *reinterpret_cast<const u32x4*>(kbase + (size_t)slot * a.kv.sl);
-        vr[st] = *reinterpret_cast<const u32x4*>(vbase + (size_t)slot * a.kv.sl);
+      if (idx < n) {
+        const int slot = (fp + idx) % a.kv.cap;
+        kr[st] = *reinterpret_cast<gptr<const u32x4>>(kbase + (size_t)slot * a.kv.sl);
+        vr[st] = *reinterpret_cast<gptr<const u32x4>>(vbase + (size_t)slot * a.kv.sl);
       }
     }
-    if (first) grid_sync(a, epoch);
-    first = false;
-    if (!active) continue;
+    qr = s.q[l][(b * 4 + (threadIdx.x >> 7)) * H + h * DH + (threadIdx.x & 127)];
+  };
+
+  u32x4 kr[4], vr[4];
+  float qr;
+  if (sync) grid_wait(a, sy);
+  // queries come from the previous phase: load only after the barrier
+  load_unit(wg, kr, vr, qr);
+  trace_mark(a, sy, 2);
+  for (int u = wg; u < nunits; u += G) {
+    u32x4 kn[4], vn[4];
+    float qn;
+    load_unit(u + G, kn, vn, qn);
+    int b, c, h;
+    sl.unit(u, b, c, h);
+    const int n = sl.vis(b);
+    s_q[threadIdx.x] = qr * qs;
+    lds_sync();
     float q[4][8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 q0 = *reinterpret_cast<const KD_LDS f32x4*>(s_q + j * DH + d0);
+      const f32x4 q1 = *reinterpret_cast<const KD_LDS f32x4*>(s_q + j * DH + d0 + 4);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) q[j][e] = s.q[l][(b * 4 + j) * H + h * DH + d0 + e] * qs;
+      for (int e = 0; e < 4; ++e) {
+        q[j][e] = q0[e];
+        q[j][4 + e] = q1[e];
+      }
+    }
     float sc[4][4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const int idx = c * ATT_CH + wave * 16 + st * 4 + g;
       float kf[8];
       bf16x8_to_f32(kr[st], kf);
-      float dot[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        dot[j] = 0.f;
+        float dot = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dot[j] += q[j][e] * kf[e];
-#pragma unroll
-        for (int m = 8; m >= 1; m >>= 1) dot[j] += __shfl_xor(dot[j], m, 64);
-        sc[j][st] = idx < n ? dot[j] : -__builtin_inff();
+        for (int e = 0; e < 8; ++e) dot += q[j][e] * kf[e];
+        dot = row16_sum(dot);
+        sc[j][st] = idx < n ? dot : -__builtin_inff();
       }
     }
+    float vf[4][8];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) bf16x8_to_f32(vr[st], vf[st]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       float mx = fmaxf(fmaxf(sc[j][0], sc[j][1]), fmaxf(sc[j][2], sc[j][3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = rows_max4(mx);
       float lsum = 0.f, o[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = 0.f;
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         const float p = sc[j][st] == -__builtin_inff() ? 0.f : exp2f(sc[j][st] - mx);
-        float vf[8];
-        bf16x8_to_f32(vr[st], vf);
         lsum += p;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] += p * vf[e];
+        for (int e = 0; e < 8; ++e) o[e] += p * vf[st][e];
       }
-      lsum += __shfl_xor(lsum, 16, 64);
-      lsum += __shfl_xor(lsum, 32, 64);
+      lsum = rows_sum4(lsum);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        o[e] += __shfl_xor(o[e], 16, 64);
-        o[e] += __shfl_xor(o[e], 32, 64);
+      for (int e = 0; e < 8; ++e) o[e] = rows_sum_to_row3(o[e]);
+      if (g == 3) {
+        *reinterpret_cast<KD_LDS f32x4*>(s_o + (wave * 4 + j) * DH + d0) = f32x4{o[0], o[1], o[2], o[3]};
+        *reinterpret_cast<KD_LDS f32x4*>(s_o + (wave * 4 + j) * DH + d0 + 4) = f32x4{o[4], o[5], o[6], o[7]};
       }
-      if (g == 0)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s_o[(wave * 4 + j) * DH + d0 + e] = o[e];
       if (lane == 0) {
         s_m[wave * 4 + j] = mx;
         s_l[wave * 4 + j] = lsum;
       }
     }
-    __syncthreads();
+    lds_sync();
     {
       const int j = threadIdx.x >> 7, dd = threadIdx.x & 127;
       float M = -__builtin_inff();
@@ -624,104 +950,101 @@ __device__ __attribute__((noinline)) void ph_attn(const SmallArgs& a, int l, flo
         st_wt(&s.al[l][pb], Ls);
       }
     }
-    __syncthreads();
-  }
-  if (first) grid_sync(a, epoch);
-}
-
-// Merge of the chunk partials with the block's own keys (row j sees block
-// rows 0..j) for one (stream, head); thread (j, d).
-__device__ __attribute__((noinline)) void ph_merge(const SmallArgs& a, int l, float* red, SyncState& epoch, bool sync) {
-  const int G = gridDim.x, wg = blockIdx.x;
-  const SmallBufs& s = a.s;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nch = a.nch;
-  const float qs = 0.08838834764831845f * 1.4426950408889634f;
-  bool first = sync;
-  for (int u = wg; u < a.B * NH; u += G) {
-    if (first) grid_sync(a, epoch);
-    first = false;
-    const int b = u / NH, h = u % NH;
-    const int n = min(a.lens[b], a.window), nc = (n + ATT_CH - 1) / ATT_CH;
-    // block scores s[j][i] = q_j . k_i: wave w covers row j = w/2, dims 64*(w%2)..
-    {
-      const int j = wave >> 1, dd = 64 * (wave & 1) + lane;
-      const float qv = s.q[l][(b * 4 + j) * H + h * DH + dd];
+    if (u == wg) trace_mark(a, sy, 3);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = wave_sum(qv * s.k[l][(b * 4 + i) * H + h * DH + dd]);
-        if (lane == 0) red[wave * 4 + i] = p;
+    for (int st = 0; st < 4; ++st) {
+      kr[st] = kn[st];
+      vr[st] = vn[st];
+    }
+    qr = qn;
+  }
+  // completion counters: one per (stream, head) and layer; thread k takes this
+  // workgroup's k-th unit once every partial store of the workgroup is done
+  __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0): stores acknowledged
+  __syncthreads();
+  if (threadIdx.x == 0) s_list[0] = 0u;
+  lds_sync();
+  {
+    const int u = wg + threadIdx.x * G;
+    if (threadIdx.x < ATT_UNITS_MAX && u < nunits) {
+      int b, c, h;
+      sl.unit(u, b, c, h);
+      const int nc = (sl.vis(b) + ATT_CH - 1) / ATT_CH;
+      auto cnt = &s.att_cnt[((l * SB_MAX + b) * NH + h) * 32];
+      const unsigned v = add_rlx(cnt, 1u);
+      if (v == (unsigned)(nc - 1)) {
+        __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned k = __hip_atomic_fetch_add(&s_list[0], 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_WORKGROUP);
+        s_list[1 + k] = (unsigned)(b * NH + h);
       }
     }
-    __syncthreads();
-    const int j = threadIdx.x >> 7, dd = threadIdx.x & 127;
-    float sb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sb[i] = (red[(2 * j) * 4 + i] + red[(2 * j + 1) * 4 + i]) * qs;
-    float M = -__builtin_inff();
-    for (int c = 0; c < nc; ++c) M = fmaxf(M, s.am[l][((size_t)(b * NH + h) * nch + c) * 4 + j]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (i <= j) M = fmaxf(M, sb[i]);
-    float Ls = 0.f, O = 0.f;
-    for (int c = 0; c < nc; ++c) {
-      const size_t pb = ((size_t)(b * NH + h) * nch + c) * 4 + j;
-      const float f = exp2f(s.am[l][pb] - M);
-      Ls += s.al[l][pb] * f;
-      O += s.ao[l][pb * DH + dd] * f;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (i <= j) {
-        const float f = exp2f(sb[i] - M);
-        Ls += f;
-        O += f * s.v[l][(b * 4 + i) * H + h * DH + dd];
-      }
-    st_wt(&s.o[l][(b * 4 + j) * H + h * DH + dd], O / Ls);
-    __syncthreads();
   }
-  if (first) grid_sync(a, epoch);
+  lds_sync();
+  const unsigned nm = s_list[0];
+  trace_mark(a, sy, 5);
+  for (unsigned k = 0; k < nm; ++k) {
+    const unsigned bh = s_list[1 + k];
+    const int b = bh / NH, h = bh % NH;
+    attn_merge(a, l, b, h, sl.vis(b), red);
+  }
+  // streams with an empty context: the block attends to itself only
+  for (int t = wg; t < a.B * NH; t += G) {
+    const int b = t / NH, h = t % NH;
+    if (sl.vis(b) == 0) attn_merge(a, l, b, h, 0, red);
+  }
+  trace_mark(a, sy, 6);
+  trace_mark(a, sy, 4);
 }
 
-// x_{out} = x_{in} + W v for a 2560-wide output, with per-tile sums of squares.
+// x_{out} = x_{in} + W v for a 2560-wide output, with the gained copy and
+// per-tile sums of squares.
 template <int KBS>
-__device__ __attribute__((noinline)) void ph_resid(const SmallArgs& a, const Fp8Mat& W, const float* srcA, int ldA,
-                         int xin, int xout, float* red, SyncState& epoch, bool sync) {
+__device__ __attribute__((noinline, not_tail_called)) void ph_resid(Args& a_, Mat& W_,
+                                                   gptr<const float> srcA_, int ldA_, int xin_, int xout_,
+                                                   gptr<const float> gain_, lds_f red, SyncState sy,
+                                                   bool sync) {
+  const auto srcA = uni(srcA_);
+  const auto ldA = uni(ldA_);
+  const auto xin = uni(xin_);
+  const auto xout = uni(xout_);
+  const auto gain = uni(gain_);
+  Mat& W = uni(W_);
+  Args& a = uni(a_);
   const int G = gridDim.x, wg = blockIdx.x;
-  const SmallBufs& s = a.s;
+  auto& s = a.s;
   const int R = a.R;
   bool first = sync;
   for (int u = wg; u < HT; u += G) {
-    const ASrc A{srcA, ldA, 0, nullptr, nullptr, 0, R, 0};
-    gemm_unit<1, KBS, 8>(a, epoch, first, W, u, 1, 0, A, red, NoPrep{},
-                         [&](int, int m, int n, float v) {
-                           const int col = u * 16 + n;
-                           const float x = m < R ? s.x[xin][m * H + col] + v : 0.f;
-                           const float q = tile_ssq(x);
-                           if (m < R) {
-                             st_wt(&s.x[xout][m * H + col], x);
-                             if (n == 0) st_wt(&s.ssq[xout][m * HT + u], q);
-                           }
-                         });
+    const ASrc A{srcA, ldA, 0, nullptr, 0, R};
+    gemm_unit<1, KBS, 8, false>(a, sy, first, W, u, 1, 0, A, red, no_rms(),
+                                [&](int, int m, int n, float v) {
+                                  const int col = u * 16 + n;
+                                  const bool ok = m < R;
+                                  const float x = ok ? s.x[xin][m * H + col] + v : 0.f;
+                                  put_x(s, xout, gain, m, col, u, n, x, ok);
+                                });
     first = false;
   }
-  if (first) grid_sync(a, epoch);
+  if (first) grid_sync(a, sy);
 }
 
 // h = silu(gate / rms) * (up / rms) with gate, up = W (g_f * x).
-__device__ __attribute__((noinline)) void ph_gu(const SmallArgs& a, int l, float* red, SyncState& epoch, bool sync) {
+__device__ __attribute__((noinline, not_tail_called)) void ph_gu(Args& a_, int l_, lds_f red,
+                                                SyncState sy, bool sync) {
+  const auto l = uni(l_);
+  Args& a = uni(a_);
   const int G = gridDim.x, wg = blockIdx.x;
-  const SmallBufs& s = a.s;
-  const DevLayer& L = a.d.layer[l];
+  auto& s = a.s;
+  auto& L = a.d.layer[l];
   const int R = a.R, src = xs_o(l);
-  float* inv = red + 8192;
+  lds_f inv = red + 8192;
   constexpr int NT = 3, NU = GU / 16 / NT;
   bool first = sync;
   for (int u = wg; u < NU; u += G) {
-    const ASrc A{s.x[src], H, 0, nullptr, L.ffn_norm, 0, R, 0};
-    gemm_unit<NT, 5, 8>(
-        a, epoch, first, L.gu, u * NT, NT, 0, A, red,
-        [&] { inv_rms_rows(s.ssq[src], R, [](int r) { return r; }, a.eps, inv); },
+    const ASrc A{s.xg[src], H, 0, nullptr, 0, R};
+    gemm_unit<NT, 5, 8, false>(
+        a, sy, first, L.gu, u * NT, NT, 0, A, red, RmsRows{s.ssq[src], R, 0, a.eps, inv, {}},
         [&](int i, int m, int n, float v) {
           const int t = u * NT + i;
           const float val = m < R ? v * inv[m] : 0.f;
@@ -730,24 +1053,28 @@ __device__ __attribute__((noinline)) void ph_gu(const SmallArgs& a, int l, float
         });
     first = false;
   }
-  if (first) grid_sync(a, epoch);
+  if (first) grid_sync(a, sy);
 }
 
 // NVFP4 head over 16-row vocab tiles (HEAD_NT per unit): wave w takes the
-// 128-input groups kg0(w)..kg1(w); per-workgroup argmax candidates per row.
-__device__ __attribute__((noinline)) void ph_head(const SmallArgs& a, float* red, SyncState& epoch, bool sync) {
+// 128-input groups kg0(w)..kg1(w); the next unit's codes are loaded while one
+// is computed. Argmax candidates per row are kept per workgroup; the last
+// workgroup to finish reduces them to the output ids.
+__device__ __attribute__((noinline, not_tail_called)) void ph_head(Args& a_, lds_f red, SyncState sy,
+                                                  bool sync) {
+  Args& a = uni(a_);
   const int G = gridDim.x, wg = blockIdx.x;
-  const SmallBufs& s = a.s;
-  const DevWeights& d = a.d;
+  auto& s = a.s;
+  auto& d = a.d;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int R = a.R, VT = d.VT, VD = d.VD;
   constexpr int KG = H / 128;
   const int kg0 = (KG * wave) >> 3, kg1 = (KG * (wave + 1)) >> 3, ng = kg1 - kg0;  // 2 or 3
   const int src = a.nl == 0 ? 0 : xs_d(a.nl - 1);
   const int nunits = (VT + HEAD_NT - 1) / HEAD_NT;
-  float* inv = red + 8192;
-  unsigned long long* best = reinterpret_cast<unsigned long long*>(red + 8192 + 32);  // [16]
-  if (threadIdx.x < SR_MAX) best[threadIdx.x] = 0ull;
+  lds_f inv = red + 8192;
+  KD_LDS unsigned long long* best = reinterpret_cast<KD_LDS unsigned long long*>(red + 8192 + 32);  // [16]
+  KD_LDS unsigned* s_flag = reinterpret_cast<KD_LDS unsigned*>(red + 8192 + 64);
 
   auto load_unit = [&](int u, u32x4 (&q)[HEAD_NT][3], uint32_t (&sv)[HEAD_NT][3]) {
 #pragma unroll
@@ -757,39 +1084,59 @@ __device__ __attribute__((noinline)) void ph_head(const SmallArgs& a, float* red
         q[i][gg] = u32x4{0u, 0u, 0u, 0u};
         sv[i][gg] = 0u;
         const int vt = u * HEAD_NT + i;
-        if (vt < VT && gg < ng) {
+        if (u < nunits && vt < VT && gg < ng) {
           const size_t idx = ((size_t)vt * KG + kg0 + gg) * 64 + lane;
-          q[i][gg] = *reinterpret_cast<const u32x4*>(d.hq + idx * 16);
-          sv[i][gg] = *reinterpret_cast<const uint32_t*>(d.hs + idx * 4);
+          q[i][gg] = *reinterpret_cast<gptr<const u32x4>>(d.hq + idx * 16);
+          sv[i][gg] = *reinterpret_cast<gptr<const uint32_t>>(d.hs + idx * 4);
         }
       }
   };
 
+  if (sync) grid_arrive(a, sy);
   u32x4 q[HEAD_NT][3];
   uint32_t sv[HEAD_NT][3];
-  if (wg < nunits) load_unit(wg, q, sv);
-  if (sync) grid_sync(a, epoch);
-  inv_rms_rows(s.ssq[src], R, [](int r) { return r; }, a.eps, inv);
+  load_unit(wg, q, sv);
+  if (sync) grid_wait(a, sy);
+  trace_mark(a, sy, 2);
+  if (threadIdx.x < SR_MAX) best[threadIdx.x] = 0ull;
+  RmsRows rms{s.ssq[src], R, 0, a.eps, inv, {}};
+  rms.issue();
   // A operand (g_o * x, hi/lo f16) for this wave's inputs, kept for all units
   f16x8 ah[3][4], al[3][4];
   {
     const int r = lane & 15;
+    f32x4 raw[3][4][2];
+#pragma unroll
+    for (int gg = 0; gg < 3; ++gg)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        raw[gg][t][0] = raw[gg][t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int c0 = (kg0 + gg) * 128 + t * 32 + 8 * (lane >> 4);
+        if (r < R && gg < ng) {
+          auto p = s.xg[src] + r * H + c0;
+          raw[gg][t][0] = *reinterpret_cast<gptr<const f32x4>>(p);
+          raw[gg][t][1] = *reinterpret_cast<gptr<const f32x4>>(p + 4);
+        }
+      }
 #pragma unroll
     for (int gg = 0; gg < 3; ++gg)
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         float v[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = 0.f;
-        const int c0 = (kg0 + gg) * 128 + t * 32 + 8 * (lane >> 4);
-        if (r < R && gg < ng)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = s.x[src][r * H + c0 + e] * d.final_norm[c0 + e];
+        for (int e = 0; e < 4; ++e) {
+          v[e] = raw[gg][t][0][e];
+          v[4 + e] = raw[gg][t][1][e];
+        }
         split_f16(v, ah[gg][t], al[gg][t]);
       }
   }
+  rms.finish();
+  trace_mark(a, sy, 3);
   for (int u = wg; u < nunits; u += G) {
-    if (u != wg) load_unit(u, q, sv);
+    u32x4 qn[HEAD_NT][3];
+    uint32_t svn[HEAD_NT][3];
+    load_unit(u + G, qn, svn);
     f32x4 acc[HEAD_NT];
 #pragma unroll
     for (int i = 0; i < HEAD_NT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -810,7 +1157,7 @@ __device__ __attribute__((noinline)) void ph_head(const SmallArgs& a, float* red
     for (int i = 0; i < HEAD_NT; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) red[((wave * HEAD_NT + i) * 4 + e) * 64 + lane] = acc[i][e];
-    __syncthreads();
+    lds_sync();
     gemm_epilogue<HEAD_NT>(red, [&](int i, int m, int n, float v) {
       const int voc = (u * HEAD_NT + i) * 16 + n;
       const bool ok = m < R && voc < VD;
@@ -819,54 +1166,72 @@ __device__ __attribute__((noinline)) void ph_head(const SmallArgs& a, float* red
       unsigned long long key = ok ? argmax_key(logit, (uint32_t)voc) : 0ull;
 #pragma unroll
       for (int mm = 1; mm <= 8; mm <<= 1) key = u64_max(key, shfl_xor_u64s(key, mm));
-      if (n == 0 && key) atomicMax(&best[m], key);
+      if (n == 0 && key)
+        __hip_atomic_fetch_max(&best[m], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     });
+#pragma unroll
+    for (int i = 0; i < HEAD_NT; ++i)
+#pragma unroll
+      for (int gg = 0; gg < 3; ++gg) {
+        q[i][gg] = qn[i][gg];
+        sv[i][gg] = svn[i][gg];
+      }
+    if (u == wg) trace_mark(a, sy, 5);
   }
-  __syncthreads();
+  lds_sync();
   if (threadIdx.x < SR_MAX) st_wt64(&s.cand[wg * SR_MAX + threadIdx.x], best[threadIdx.x]);
-}
-
-__device__ __attribute__((noinline)) void ph_final(const SmallArgs& a, SyncState& epoch, bool sync) {
-  if (sync) grid_sync(a, epoch);
-  if (blockIdx.x != 0) return;
-  const int G = gridDim.x, t = threadIdx.x, r = t >> 5, l32 = t & 31;
+  trace_mark(a, sy, 4);
+  // the last workgroup to finish reduces every workgroup's candidates
+  __builtin_amdgcn_s_waitcnt(0);  // the candidate stores are acknowledged
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    auto cnt = &s.bar[19 * 32];
+    const unsigned v = add_rlx(cnt, 1u);
+    const bool last = v == (unsigned)(G - 1);
+    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = last ? 1u : 0u;
+  }
+  lds_sync();
+  if (!*s_flag) return;
+  const int t = threadIdx.x, r = t >> 5, l32 = t & 31;
   unsigned long long k = 0ull;
-  if (r < a.R)
-    for (int g = l32; g < G; g += 32) k = u64_max(k, a.s.cand[g * SR_MAX + r]);
+  if (r < R)
+    for (int gi = l32; gi < G; gi += 32) k = u64_max(k, s.cand[gi * SR_MAX + r]);
 #pragma unroll
   for (int m = 16; m >= 1; m >>= 1) k = u64_max(k, shfl_xor_u64s(k, m));
-  const bool failed = ld_rlx(&a.s.bar[18 * 32]) != 0u;
-  if (r < a.R && l32 == 0)
-    a.out_ids[r] = failed ? -2 : (k ? a.d.vocab[0xffffffffu - (uint32_t)(k & 0xffffffffu)] : -1);
+  const bool failed = ld_rlx(&s.bar[18 * 32]) != 0u;
+  if (r < R && l32 == 0)
+    a.out_ids[r] = failed ? -2 : (k ? d.vocab[0xffffffffu - (uint32_t)(k & 0xffffffffu)] : -1);
 }
 
 // ---------------------------------------------------------------------------
 // Phase dispatch
 // ---------------------------------------------------------------------------
-__device__ void run_phase(const SmallArgs& a, int p, float* red, SyncState& epoch, bool sync) {
-  if (p == PH_PRE0) return ph_pre0(a, red, epoch);
-  if (p == PH_PRE1) return ph_pre1(a, red, epoch, sync);
-  if (p == PH_PRE2) return ph_pre2(a, red, epoch, sync);
-  if (p == PH_HEAD) return ph_head(a, red, epoch, sync);
-  if (p == PH_FINAL) return ph_final(a, epoch, sync);
+__device__ void run_phase(Args& a, int p, lds_f red, SyncState sy, bool sync) {
+  if (p == PH_PRE0) return ph_pre0(a, red, sy);
+  if (p == PH_PRE1) return ph_pre1(a, red, sy, sync);
+  if (p == PH_PRE2) return ph_pre2(a, red, sy, sync);
+  if (p == PH_HEAD) return ph_head(a, red, sy, sync);
   const int l = (p - 3) >> 3, k = (p - 3) & 7;
-  const SmallBufs& s = a.s;
-  const DevLayer& L = a.d.layer[l];
+  auto& s = a.s;
+  auto& L = a.d.layer[l];
   switch (k) {
-    case PH_SA: return ph_sa(a, l, red, epoch, sync);
-    case PH_SU: return ph_su(a, l, red, epoch, sync);
-    case PH_QKV: return ph_qkv(a, l, red, epoch, sync);
-    case PH_ATTN: return ph_attn(a, l, red, epoch, sync);
-    case PH_MERGE: return ph_merge(a, l, red, epoch, sync);
-    case PH_O: return ph_resid<5>(a, L.wo, s.o[l], H, xs_in(l), xs_o(l), red, epoch, sync);
-    case PH_GU: return ph_gu(a, l, red, epoch, sync);
-    case PH_DOWN: return ph_resid<12>(a, L.down, s.h[l], FF, xs_o(l), xs_d(l), red, epoch, sync);
+    case PH_SA: return ph_sa(a, l, red, sy, sync);
+    case PH_SU: return ph_su(a, l, red, sy, sync);
+    case PH_QKV: return ph_qkv(a, l, red, sy, sync);
+    case PH_ATTN: return ph_attn(a, l, red, sy, sync);
+    case PH_O:
+      return ph_resid<5>(a, L.wo, s.o[l], H, xs_in(l), xs_o(l), L.ffn_norm, red, sy, sync);
+    case PH_GU: return ph_gu(a, l, red, sy, sync);
+    case PH_DOWN:
+      return ph_resid<12>(a, L.down, s.h[l], FF, xs_o(l), xs_d(l), gain_after_down(a, l), red,
+                          sy, sync);
   }
 }
 
 __host__ __device__ int small_phase_count(int nl) {
-  int n = 3 + 2;
-  for (int l = 0; l < nl; ++l) n += l == 0 ? 6 : 8;
+  int n = 3 + 1;
+  for (int l = 0; l < nl; ++l) n += l == 0 ? 5 : 7;
   return n;
 }
 
@@ -874,37 +1239,47 @@ __host__ __device__ int small_phase_id(int nl, int i) {
   if (i < 3) return i;
   i -= 3;
   for (int l = 0; l < nl; ++l) {
-    const int nk = l == 0 ? 6 : 8;
-    if (i < nk) return 3 + 8 * l + (l == 0 ? i + 2 : i);
+    // SA, SU (layers >= 1), QKV, ATTN, O, GU, DOWN
+    const int nk = l == 0 ? 5 : 7;
+    if (i < nk) {
+      const int k = l == 0 ? i + 2 : i;
+      return 3 + 8 * l + (k >= 4 ? k + 1 : k);
+    }
     i -= nk;
   }
-  return i == 0 ? PH_HEAD : PH_FINAL;
+  return PH_HEAD;
 }
 
-constexpr int RED_FLOATS = 8192 + 32 + 32;   // partial sums, inv rms, argmax candidates
+constexpr int RED_FLOATS = 8192 + 32 + 32 + 32;   // partials, inv rms, argmax candidates, flag
 
 // The argument block lives in device memory (read through scalar loads), so
 // no per-lane copy of it is made when it is passed down to the phases.
-__global__ __launch_bounds__(SMALL_WG) void k_small_phase(const SmallArgs* __restrict__ ap, int p) {
+__global__ __launch_bounds__(SMALL_WG) void k_small_phase(const SmallArgs* __restrict__ ap, int p,
+                                                         int slot) {
   __shared__ __attribute__((aligned(16))) float red[RED_FLOATS];
-  SyncState sy{0u, 0u};
-  run_phase(*ap, p, red, sy, false);
+  const SyncState sy{0u, slot};
+  Args& a = *(Args*)ap;
+  run_phase(a, p, (lds_f)red, sy, false);
+  trace_mark(a, sy, 7);
 }
 
 __global__ __launch_bounds__(SMALL_WG) void k_small_mega(const SmallArgs* __restrict__ ap) {
   __shared__ __attribute__((aligned(16))) float red[RED_FLOATS];
   __shared__ unsigned base;
-  const SmallArgs& a = *ap;
+  Args& a = *(Args*)ap;
   // the previous launch has finished, so the generation word is stable here
   if (threadIdx.x == 0) base = ld_rlx(&a.s.bar[17 * 32]);
   __syncthreads();
-  SyncState sy{0u, base};
   const int np = small_phase_count(a.nl);
-  for (int i = 0; i < np; ++i) run_phase(a, small_phase_id(a.nl, i), red, sy, i > 0);
+  for (int i = 0; i < np; ++i) {
+    const SyncState sy{base, i};
+    run_phase(a, small_phase_id(a.nl, i), (lds_f)red, sy, i > 0);
+    trace_mark(a, sy, 7);
+  }
 }
 
-void launch_small_phase(hipStream_t st, const SmallArgs* dev_args, int G, int phase) {
-  k_small_phase<<<G, SMALL_WG, 0, st>>>(dev_args, phase);
+void launch_small_phase(hipStream_t st, const SmallArgs* dev_args, int G, int phase, int slot) {
+  k_small_phase<<<G, SMALL_WG, 0, st>>>(dev_args, phase, slot);
 }
 
 hipError_t launch_small_mega(hipStream_t st, const SmallArgs* dev_args, int G) {
@@ -943,6 +1318,7 @@ static size_t small_layout(char* base, int nch, SmallBufs* s) {
   carve(base, off, (size_t)SR_MAX * (DH / 2) * 2 * F, (void**)&o->rope);
   for (int i = 0; i < NXS; ++i) {
     carve(base, off, (size_t)SR_MAX * H * F, (void**)&o->x[i]);
+    carve(base, off, (size_t)SR_MAX * H * F, (void**)&o->xg[i]);
     carve(base, off, (size_t)SR_MAX * HT * F, (void**)&o->ssq[i]);
   }
   for (int l = 0; l < NL; ++l) {
@@ -957,7 +1333,8 @@ static size_t small_layout(char* base, int nch, SmallBufs* s) {
     carve(base, off, (size_t)SR_MAX * FF * F, (void**)&o->h[l]);
   }
   carve(base, off, (size_t)MAX_G * SR_MAX * sizeof(unsigned long long), (void**)&o->cand);
-  carve(base, off, (size_t)19 * 32 * sizeof(unsigned), (void**)&o->bar);
+  carve(base, off, (size_t)20 * 32 * sizeof(unsigned), (void**)&o->bar);
+  carve(base, off, (size_t)NL * SB_MAX * NH * 32 * sizeof(unsigned), (void**)&o->att_cnt);
   return (off + 255) & ~(size_t)255;
 }
 

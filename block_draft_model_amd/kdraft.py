@@ -53,7 +53,8 @@ class KdKV(ctypes.Structure):
 EXPORTS = ["kd_default_config", "kd_create", "kd_load_weights", "kd_round", "kd_ingest",
            "kd_set_stream", "kd_destroy", "kd_status_string", "kd_last_error",
            "kd_probe_decode_e4m3", "kd_probe_decode_nvfp4", "kd_debug_set_layers",
-           "kd_debug_buffers", "kd_debug_set_path", "kd_debug_last_path"]
+           "kd_debug_buffers", "kd_debug_set_path", "kd_debug_last_path",
+           "kd_debug_set_trace"]
 
 _lib = None
 
@@ -104,6 +105,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kd_debug_set_path.restype = c_int
     lib.kd_debug_last_path.argtypes = [c_void_p]
     lib.kd_debug_last_path.restype = c_int
+    lib.kd_debug_set_trace.argtypes = [c_void_p, c_void_p, c_int, P(c_int)]
+    lib.kd_debug_set_trace.restype = c_int
     _lib = lib
     return lib
 
@@ -232,6 +235,14 @@ class Drafter:
         """0 automatic, 1 general multi-kernel, 2 small-batch phases as launches,
         3 small-batch persistent kernel (paths 2, 3 only for <= 4 streams)."""
         self._check(self.lib.kd_debug_set_path(self.ctx, int(path)), "kd_debug_set_path")
+
+    def debug_set_trace(self, buf, phases: int) -> int:
+        """Stage timestamps of later rounds into buf (device uint64 [phases][G][8]);
+        None turns tracing off. Returns G, the workgroup count."""
+        g = c_int(0)
+        self._check(self.lib.kd_debug_set_trace(self.ctx, _ptr(buf), int(phases), ctypes.byref(g)),
+                    "kd_debug_set_trace")
+        return g.value
 
     def last_path(self) -> int:
         return int(self.lib.kd_debug_last_path(self.ctx))

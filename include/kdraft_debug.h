@@ -42,6 +42,13 @@ kd_status kd_debug_set_path(kd_ctx* ctx, int path);
 /* The path the last round ran on (1, 2 or 3; 0 before any round). */
 int kd_debug_last_path(const kd_ctx* ctx);
 
+/* Stage tracing of the small-batch paths: later rounds write 100 MHz
+ * wall-clock stamps into buf (device, [phases][workgroups][8] uint64, caller
+ * owned; slots: 0 phase entry or barrier arrival, 1 barrier passed, 2 unit
+ * inputs issued, 3 compute done, 4 epilogue done, 7 phase exit). buf = NULL
+ * turns tracing off. *workgroups (if not NULL) receives the workgroup count. */
+kd_status kd_debug_set_trace(kd_ctx* ctx, unsigned long long* buf, int phases, int* workgroups);
+
 #ifdef __cplusplus
 }
 #endif
