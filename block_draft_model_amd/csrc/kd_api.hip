@@ -31,6 +31,7 @@ struct kd_ctx {
   kd::SmallBufs small{};
   int G = 0;                 // workgroups of the small path (one per CU, <= 256)
   bool small_ok = false;     // the window fits the small path's attention phase
+  unsigned epoch = 0;        // grid barriers completed by persistent launches so far
   bool mega_ok = false;      // persistent cooperative kernel available
   int path = 0;              // 0 auto, 1 general, 2 small per-phase, 3 small persistent
   kd::SmallArgs* args_dev = nullptr;   // device copy of the small-path arguments
@@ -536,8 +537,9 @@ kd_status kd_round(kd_ctx* c, int B, const void* taps, const int32_t* anchor, co
     }
     const int np = kd::small_phase_count(a.nl);
     if (path == 3) {
-      const hipError_t e = kd::launch_small_mega(st, c->args_dev, c->G);
+      const hipError_t e = kd::launch_small_mega(st, c->args_dev, c->G, c->epoch);
       if (e != hipSuccess) return hip_fail(c, e, "persistent round launch");
+      c->epoch += (unsigned)(kd::small_phase_count(a.nl) - 1);
     } else {
       for (int i = 0; i < np; ++i)
         kd::launch_small_phase(st, c->args_dev, c->G, kd::small_phase_id(a.nl, i), i);

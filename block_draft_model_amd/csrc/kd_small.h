@@ -44,8 +44,8 @@ struct SmallBufsT {
   P<float> o[NL];              // [SR][H]   merged attention output
   P<float> h[NL];              // [SR][FF]  silu(gate) * up
   P<unsigned long long> cand;  // [MAX_G][SR] per-workgroup argmax candidates
-  P<unsigned> bar;             // barrier: 16 group lines, top, generation, error,
-                               // head counter (32 u32 each)
+  P<unsigned> bar;             // control words, 32 u32 apart: [0..15] arrival counters of
+                               // the 16-workgroup groups, [18] error, [19] head counter
   P<unsigned> att_cnt;         // [NL][SB][NH] chunk counters, one 128-byte line each
 };
 
@@ -77,7 +77,9 @@ __host__ __device__ int small_phase_count(int nl);
 __host__ __device__ int small_phase_id(int nl, int i);
 // dev_args: a device copy of the SmallArgs.
 void launch_small_phase(hipStream_t st, const SmallArgs* dev_args, int G, int phase, int slot);
-hipError_t launch_small_mega(hipStream_t st, const SmallArgs* dev_args, int G);
+// epoch0: grid barriers completed by earlier persistent launches on these
+// buffers (each launch completes small_phase_count(nl) - 1).
+hipError_t launch_small_mega(hipStream_t st, const SmallArgs* dev_args, int G, unsigned epoch0);
 int small_mega_occupancy();
 
 }  // namespace kd

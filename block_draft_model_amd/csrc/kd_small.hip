@@ -160,51 +160,68 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64s(unsigned long long v
 // issue loads of data it does not depend on in between.
 // ---------------------------------------------------------------------------
 struct SyncState {
-  unsigned base;   // generation word at kernel start
-  int slot;        // phase index within the launch; phase i > 0 passes barrier i
+  unsigned epoch0;  // barriers completed by earlier launches (from the host)
+  int slot;         // phase index within the launch; phase i > 0 passes barrier i
 };
 
 // Stage timestamps for tracing: slot 0 barrier arrival, 1 barrier passed,
 // 2 unit inputs issued, 3 compute done, 4 epilogue done, 7 phase exit.
-__device__ __forceinline__ void trace_mark(Args& a, const SyncState sy, int k) {
-  if (a.trace && threadIdx.x == 0 && sy.slot < a.trace_phases)
+__device__ __forceinline__ void trace_mark(Args& a, const SyncState sy, int k, int who = 0) {
+  if (a.trace && threadIdx.x == who && sy.slot < a.trace_phases)
     a.trace[((size_t)sy.slot * gridDim.x + blockIdx.x) * 8 + k] = wall_clock64();
+}
+
+// Wave POLL_WAVE publishes the arrival and polls. A wave's vector loads
+// complete in issue order, so a poll issued behind a weight prefetch would see
+// the barrier only after the whole prefetch has landed; the polling wave
+// therefore issues its own loads of the next phase only after the barrier,
+// while the other waves prefetch before it.
+constexpr int POLL_WAVE = SMALL_WG / 64 - 1;
+constexpr int POLL_LANE0 = POLL_WAVE * 64;
+
+__device__ __forceinline__ bool is_poll_wave() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == POLL_WAVE;
 }
 
 __device__ void grid_arrive(Args& a, SyncState sy) {
   // every wave's global stores of the previous phase are acknowledged before
-  // thread 0 publishes the arrival
+  // the arrival is published: one atomic add on the group's counter whose
+  // result is not waited for
   __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0)
   __syncthreads();
-  if (threadIdx.x == 0) {
-    auto bar = a.s.bar;
-    const unsigned G = gridDim.x, grp = blockIdx.x >> 4, ngrp = (G + 15) >> 4;
-    const unsigned gsize = min(16u, G - grp * 16);
-    trace_mark(a, sy, 0);
-    const unsigned v = add_rlx(&bar[grp * 32], 1u);
-    if ((v + 1) % gsize == 0) {
-      const unsigned w = add_rlx(&bar[16 * 32], 1u);
-      if ((w + 1) % ngrp == 0)
-        __hip_atomic_store(&bar[17 * 32], sy.base + (unsigned)sy.slot, __ATOMIC_RELAXED,
+  if (threadIdx.x == POLL_LANE0) {
+    trace_mark(a, sy, 0, POLL_LANE0);
+    __hip_atomic_fetch_add(&a.s.bar[(blockIdx.x >> 4) * 32], 1u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
-    }
   }
 }
 
-__device__ void grid_wait(Args& a, SyncState sy) {
-  if (threadIdx.x == 0) {
-    auto bar = a.s.bar;
-    const unsigned target = sy.base + (unsigned)sy.slot;
-    const unsigned long long t0 = wall_clock64();
-    while ((int)(ld_rlx(&bar[17 * 32]) - target) < 0) {
-      if (wall_clock64() - t0 > 20000000ull) {  // 0.2 s at the 100 MHz wall clock
-        __hip_atomic_store(&bar[18 * 32], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
+// Called by the whole polling wave, before it issues any load of the phase:
+// lane g < 16 watches group g's counter until it holds the group's size times
+// the number of barriers completed so far (every counter starts at zero and
+// grows by its group's size per barrier; 32-bit wrap-around is harmless).
+__device__ void grid_poll(Args& a, SyncState sy) {
+  const int lane = threadIdx.x & 63, G = gridDim.x, ngrp = (G + 15) >> 4;
+  const int g = min(lane, ngrp - 1);
+  const unsigned gsize = min(16, G - g * 16);
+  const unsigned target = gsize * (sy.epoch0 + (unsigned)sy.slot);
+  auto cnt = &a.s.bar[g * 32];
+  const unsigned long long t0 = wall_clock64();
+  while (true) {
+    const bool ok = (int)(ld_rlx(cnt) - target) >= 0;
+    if (__all(ok)) break;
+    if (wall_clock64() - t0 > 20000000ull) {  // 0.2 s at the 100 MHz wall clock
+      if (lane == 0) __hip_atomic_store(&a.s.bar[18 * 32], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
     }
-    trace_mark(a, sy, 1);
+    __builtin_amdgcn_s_sleep(1);
   }
+  trace_mark(a, sy, 1, POLL_LANE0);
+}
+
+// Arrival and wait with no prefetch in between.
+__device__ __forceinline__ void grid_wait(Args& a, SyncState sy) {
+  if (is_poll_wave()) grid_poll(a, sy);
   lds_sync();
 }
 
@@ -223,22 +240,23 @@ struct WRegs {
   float s[NT][KBS];
 };
 
+// Loads are unconditional (indices clamped into range): a load inside a
+// conditional block with a fallback value makes the compiler wait for it at the
+// join, which would serialise the prefetch. Waves past AW load wave AW-1's
+// blocks and ignore them; tiles past ntv repeat the last valid tile, whose
+// results the epilogue discards.
 template <int NT, int KBS, int AW>
 __device__ __forceinline__ void load_w(WRegs<NT, KBS>& r, Mat& W, int tile0, int ntv,
                                        int kb0) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = min((int)(threadIdx.x >> 6), AW - 1);
   const int KB = W.K >> 6;
 #pragma unroll
   for (int i = 0; i < NT; ++i)
 #pragma unroll
     for (int j = 0; j < KBS; ++j) {
-      r.w[i][j] = u32x4{0u, 0u, 0u, 0u};
-      r.s[i][j] = 0.f;
-      if (wave < AW && i < ntv) {
-        const size_t blk = (size_t)(tile0 + i) * KB + kb0 + wave * KBS + j;
-        r.w[i][j] = *reinterpret_cast<gptr<const u32x4>>(W.w + blk * 1024 + lane * 16);
-        r.s[i][j] = W.s[blk * 16 + (lane & 15)];
-      }
+      const size_t blk = (size_t)(tile0 + min(i, ntv - 1)) * KB + kb0 + wave * KBS + j;
+      r.w[i][j] = *reinterpret_cast<gptr<const u32x4>>(W.w + blk * 1024 + lane * 16);
+      r.s[i][j] = W.s[blk * 16 + (lane & 15)];
     }
 }
 
@@ -264,10 +282,8 @@ __device__ __forceinline__ size_t a_row(const ASrc& A, int r) {
 // Issues the loads of one 64-input block of the lane's row (no conversion).
 template <bool ABF>
 __device__ __forceinline__ void a_issue(const ASrc& A, int kb, u32x4 (&raw)[4]) {
-  const int lane = threadIdx.x & 63, r = lane & 15;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) raw[i] = u32x4{0u, 0u, 0u, 0u};
-  if (r >= A.R) return;
+  // rows past R repeat row R-1; they only feed output rows that are discarded
+  const int lane = threadIdx.x & 63, r = min(lane & 15, A.R - 1);
   const int c0 = (kb - A.kb_off) * 64 + 8 * (lane >> 4);
   const size_t row = a_row(A, r);
   if (ABF) {
@@ -375,15 +391,12 @@ struct RmsRows {
   lds_f inv;
   float v[5];
   __device__ __forceinline__ void issue() {
-    const int r = threadIdx.x >> 5, l32 = threadIdx.x & 31;
+    if (!ssq) return;  // v stays unset and unused
+    const int r = min((int)(threadIdx.x >> 5), nrows - 1), l32 = threadIdx.x & 31;
+    const int row = mode == 2 ? 4 * (r / 3) + r % 3 : r;
+    auto p = ssq + (size_t)row * HT + l32;
 #pragma unroll
-    for (int k = 0; k < 5; ++k) v[k] = 0.f;
-    if (ssq && r < nrows) {
-      const int row = mode == 2 ? 4 * (r / 3) + r % 3 : r;
-      auto p = ssq + (size_t)row * HT + l32;
-#pragma unroll
-      for (int k = 0; k < 5; ++k) v[k] = p[32 * k];
-    }
+    for (int k = 0; k < 5; ++k) v[k] = p[32 * k];
   }
   __device__ __forceinline__ void finish() {
     if (!ssq) return;
@@ -411,10 +424,13 @@ template <int NT, int KBS, int AW, bool ABF, class Epi>
 __device__ __forceinline__ void gemm_unit(Args& a, SyncState sy, bool sync,
                                           Mat& W, int tile0, int ntv, int kb0,
                                           const ASrc& A, lds_f red, RmsRows rms, Epi&& epi) {
-  if (sync) grid_arrive(a, sy);
+  if (sync) {
+    grid_arrive(a, sy);
+    if (is_poll_wave()) grid_poll(a, sy);
+  }
   WRegs<NT, KBS> r;
   load_w<NT, KBS, AW>(r, W, tile0, ntv, kb0);
-  if (sync) grid_wait(a, sy);
+  if (sync) lds_sync();
   trace_mark(a, sy, 2);
   rms.issue();
   gemm_compute<NT, KBS, AW, ABF>(r, A, kb0, red);
@@ -694,10 +710,14 @@ struct StreamLens {
   int o1, o2, o3, total;   // first attention unit of streams 1..3; all units
   __device__ __forceinline__ void load(Args& a) {
     const int B = a.B, W = a.window;
-    const int l0 = __builtin_amdgcn_readfirstlane(a.lens[0]);
-    const int l1 = B > 1 ? __builtin_amdgcn_readfirstlane(a.lens[1]) : 0;
-    const int l2 = B > 2 ? __builtin_amdgcn_readfirstlane(a.lens[2]) : 0;
-    const int l3 = B > 3 ? __builtin_amdgcn_readfirstlane(a.lens[3]) : 0;
+    // lane b < B reads stream b's length (one load), then every lane takes
+    // the four values from lanes 0..3
+    const int lane = threadIdx.x & 63;
+    const int mine = a.lens[min(lane, B - 1)];
+    const int l0 = __builtin_amdgcn_readlane(mine, 0);
+    const int l1 = B > 1 ? __builtin_amdgcn_readlane(mine, 1) : 0;
+    const int l2 = B > 2 ? __builtin_amdgcn_readlane(mine, 2) : 0;
+    const int l3 = B > 3 ? __builtin_amdgcn_readlane(mine, 3) : 0;
     n0 = min(l0, W); n1 = min(l1, W); n2 = min(l2, W); n3 = min(l3, W);
     f0 = l0 - n0; f1 = l1 - n1; f2 = l2 - n2; f3 = l3 - n3;
     o1 = NH * ((n0 + ATT_CH - 1) / ATT_CH);
@@ -734,6 +754,16 @@ __device__ __attribute__((noinline, not_tail_called)) void attn_merge(Args& a_, 
   const float qs = 0.08838834764831845f * 1.4426950408889634f;  // 1/sqrt(128) * log2(e)
   const int nc = (n + ATT_CH - 1) / ATT_CH;
   const int j = threadIdx.x >> 7, dd = threadIdx.x & 127;
+  // block queries, keys and values first, then every chunk partial: the loads
+  // go out together
+  const int jw = wave >> 1, dw = 64 * (wave & 1) + lane;
+  const float qv = s.q[l][(b * 4 + jw) * H + h * DH + dw];
+  float kb4[4], vv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    kb4[i] = s.k[l][(b * 4 + i) * H + h * DH + dw];
+    vv[i] = s.v[l][(b * 4 + i) * H + h * DH + dd];
+  }
   constexpr int MAXC = 16;
   float pm[MAXC], pl[MAXC], po[MAXC];
   const size_t base = (size_t)(b * NH + h) * nch;
@@ -765,18 +795,11 @@ __device__ __attribute__((noinline, not_tail_called)) void attn_merge(Args& a_, 
     po[0] = po[0] * f0 + ao[(size_t)c * 4 * DH] * f1;
     pm[0] = mn;
   }
-  float vv[4];
+  // block scores s[j][i] = q_j . k_i: wave w covers row w/2, dims 64*(w%2)..
 #pragma unroll
-  for (int i = 0; i < 4; ++i) vv[i] = s.v[l][(b * 4 + i) * H + h * DH + dd];
-  {
-    // block scores s[j][i] = q_j . k_i: wave w covers row w/2, dims 64*(w%2)..
-    const int jw = wave >> 1, dw = 64 * (wave & 1) + lane;
-    const float qv = s.q[l][(b * 4 + jw) * H + h * DH + dw];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p = wave_sum(qv * s.k[l][(b * 4 + i) * H + h * DH + dw]);
-      if (lane == 0) red[wave * 4 + i] = p;
-    }
+  for (int i = 0; i < 4; ++i) {
+    const float p = wave_sum(qv * kb4[i]);
+    if (lane == 0) red[wave * 4 + i] = p;
   }
   lds_sync();
   float sb[4];
@@ -808,9 +831,14 @@ __device__ __attribute__((noinline, not_tail_called)) void attn_merge(Args& a_, 
   lds_sync();
 }
 
-// Attention over one chunk of 128 context keys for one (stream, head):
-// wave w takes keys 16w..16w+15 (4 keys per step: row g of the wave holds key
-// 4 step + g, 16 lanes x 8 dims per key).
+// Attention over one chunk of 128 context keys for one (stream, head). Wave w
+// takes keys 16w..16w+15:
+//   scores  S^T[key][j] = K Q^T on the matrix cores (16x16x32 bf16): K rows as
+//           the A operand (lane: key lane%16, dims 32kb + 8(lane/16)), the
+//           queries split into bf16 hi + lo as B (column j < 4 of 4 block rows);
+//   softmax per row j over the wave's 16 keys, probabilities to LDS;
+//   P V     on the vector units, lane l owning dims 2l, 2l+1, probabilities
+//           read back as LDS broadcasts -- no cross-lane sums for the output.
 // The next unit's keys, values and queries are loaded while one is computed.
 // A (stream, head) is complete when all its chunks have stored their partials;
 // completion counters are taken once, after the workgroup's last unit, and the
@@ -822,111 +850,152 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
   const int G = gridDim.x, wg = blockIdx.x;
   auto& s = a.s;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane >> 4, d0 = (lane & 15) * 8;
+  const int lr = lane & 15, lg = lane >> 4;
   const int nch = a.nch;
   const float qs = 0.08838834764831845f * 1.4426950408889634f;
-  lds_f s_o = red;                    // [8][4][128]
+  lds_f s_o = red;                    // [8][4][128] per-wave outputs
   lds_f s_m = red + 8 * 4 * DH;       // [8][4]
   lds_f s_l = s_m + 32;               // [8][4]
   lds_f s_q = s_l + 32;               // [4][128] queries of the unit, scaled
-  KD_LDS unsigned* s_list = reinterpret_cast<KD_LDS unsigned*>(s_q + 4 * DH);  // [1 + ATT_UNITS_MAX]
+  lds_f s_p = s_q + 4 * DH;           // [8][4][16] probabilities
+  KD_LDS unsigned* s_list = reinterpret_cast<KD_LDS unsigned*>(s_p + 8 * 4 * 16);  // [1 + ATT_UNITS_MAX]
 
-  if (sync) grid_arrive(a, sy);
   StreamLens sl;
-  sl.load(a);
+  sl.load(a);  // an input: read before the arrival
   const int nunits = sl.total;
-  auto load_unit = [&](int u, u32x4 (&kr)[4], u32x4 (&vr)[4], float& qr) {
-#pragma unroll
-    for (int st = 0; st < 4; ++st) kr[st] = vr[st] = u32x4{0u, 0u, 0u, 0u};
-    qr = 0.f;
-    if (u >= nunits) return;
+  auto kb_l = a.kv.k[l], vb_l = a.kv.v[l];
+  const long long kv_ss = a.kv.ss, kv_sh = a.kv.sh, kv_sl = a.kv.sl;
+  const int kv_cap = a.kv.cap;
+  auto q_l = s.q[l];
+  // Issues the key/value loads of unit u (u < nunits): keys past the visible
+  // rows are clamped to the last one and masked out of the scores. Keys and
+  // values are inputs, so the first unit's are loaded before the barrier; the
+  // queries come from the previous phase.
+  auto load_kv = [&](int u, u32x4 (&kr)[4], uint32_t (&vr)[16]) {
     int b, c, h;
     sl.unit(u, b, c, h);
     const int n = sl.vis(b), fp = sl.first(b);
-    auto kbase = a.kv.k[l] + b * a.kv.ss + h * a.kv.sh + d0;
-    auto vbase = a.kv.v[l] + b * a.kv.ss + h * a.kv.sh + d0;
+    auto kbase = kb_l + b * kv_ss + h * kv_sh;
+    auto vbase = vb_l + b * kv_ss + h * kv_sh;
+    // slot of the chunk's first key; visible keys are less than cap past it
+    const int s0 = (fp + c * ATT_CH) % kv_cap;
+    const int last = n - 1 - c * ATT_CH;
+    auto slot_of = [&](int off) {
+      int sl_ = s0 + min(off, last);
+      return sl_ - (sl_ >= kv_cap ? kv_cap : 0);
+    };
+    {
+      const size_t row = (size_t)slot_of(wave * 16 + lr) * kv_sl;
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int idx = c * ATT_CH + wave * 16 + st * 4 + g;
-      if (idx < n) {
-        const int slot = (fp + idx) % a.kv.cap;
-        kr[st] = *reinterpret_cast<gptr<const u32x4>>(kbase + (size_t)slot * a.kv.sl);
-        vr[st] = *reinterpret_cast<gptr<const u32x4>>(vbase + (size_t)slot * a.kv.sl);
-      }
+      for (int kb = 0; kb < 4; ++kb)
+        kr[kb] = *reinterpret_cast<gptr<const u32x4>>(kbase + row + 32 * kb + 8 * lg);
     }
-    qr = s.q[l][(b * 4 + (threadIdx.x >> 7)) * H + h * DH + (threadIdx.x & 127)];
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk)
+      vr[kk] = *reinterpret_cast<gptr<const uint32_t>>(vbase + (size_t)slot_of(wave * 16 + kk) * kv_sl +
+                                                       2 * lane);
+  };
+  auto load_q = [&](int u, float& qr) {
+    int b, c, h;
+    sl.unit(u, b, c, h);
+    qr = q_l[(b * 4 + (threadIdx.x >> 7)) * H + h * DH + (threadIdx.x & 127)];
   };
 
-  u32x4 kr[4], vr[4];
+  u32x4 kr[4];
+  uint32_t vr[16];
   float qr;
-  if (sync) grid_wait(a, sy);
-  // queries come from the previous phase: load only after the barrier
-  load_unit(wg, kr, vr, qr);
+  if (sync) {
+    grid_arrive(a, sy);
+    if (is_poll_wave()) grid_poll(a, sy);
+  }
+  if (wg < nunits) load_kv(wg, kr, vr);
+  if (sync) lds_sync();
+  if (wg < nunits) load_q(wg, qr);
   trace_mark(a, sy, 2);
   for (int u = wg; u < nunits; u += G) {
-    u32x4 kn[4], vn[4];
+    u32x4 kn[4];
+    uint32_t vn[16];
     float qn;
-    load_unit(u + G, kn, vn, qn);
+    if (u + G < nunits) {
+      load_kv(u + G, kn, vn);
+      load_q(u + G, qn);
+    }
     int b, c, h;
     sl.unit(u, b, c, h);
     const int n = sl.vis(b);
     s_q[threadIdx.x] = qr * qs;
     lds_sync();
-    float q[4][8];
+    // B operand: Q^T split into bf16 hi + lo; columns j >= 4 are zero
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4 q0 = *reinterpret_cast<const KD_LDS f32x4*>(s_q + j * DH + d0);
-      const f32x4 q1 = *reinterpret_cast<const KD_LDS f32x4*>(s_q + j * DH + d0 + 4);
+    for (int kb = 0; kb < 4; ++kb) {
+      float qv[8];
+      const int jq = min(lr, 3);
+      const f32x4 q0 = *reinterpret_cast<const KD_LDS f32x4*>(s_q + jq * DH + 32 * kb + 8 * lg);
+      const f32x4 q1 = *reinterpret_cast<const KD_LDS f32x4*>(s_q + jq * DH + 32 * kb + 8 * lg + 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        q[j][e] = q0[e];
-        q[j][4 + e] = q1[e];
+        qv[e] = lr < 4 ? q0[e] : 0.f;
+        qv[4 + e] = lr < 4 ? q1[e] : 0.f;
+      }
+      bf16x8 qh, ql;
+      split_bf16(qv, qh, ql);
+      const bf16x8 kk = __builtin_bit_cast(bf16x8, kr[kb]);
+      acc = mfma_bf16(kk, qh, acc);
+      acc = mfma_bf16(kk, ql, acc);
+    }
+    // lane holds S^T[key 4 lg + e][j = lr]; softmax over the wave's 16 keys
+    float sc[4], mx = -__builtin_inff();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int key = c * ATT_CH + wave * 16 + 4 * lg + e;
+      sc[e] = key < n ? acc[e] : -__builtin_inff();
+      mx = fmaxf(mx, sc[e]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    float pe[4], ls = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      pe[e] = sc[e] == -__builtin_inff() ? 0.f : exp2f(sc[e] - mx);
+      ls += pe[e];
+    }
+    ls += __shfl_xor(ls, 16, 64);
+    ls += __shfl_xor(ls, 32, 64);
+    if (lr < 4) {
+      *reinterpret_cast<KD_LDS f32x4*>(s_p + (wave * 4 + lr) * 16 + 4 * lg) =
+          f32x4{pe[0], pe[1], pe[2], pe[3]};
+      if (lg == 0) {
+        s_m[wave * 4 + lr] = mx;
+        s_l[wave * 4 + lr] = ls;
       }
     }
-    float sc[4][4];
+    // P V: this wave's own probabilities (LDS operations of a wave complete in
+    // order; the signal fence keeps the compiler from moving the reads up)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    float o[4][2];
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int idx = c * ATT_CH + wave * 16 + st * 4 + g;
-      float kf[8];
-      bf16x8_to_f32(kr[st], kf);
+    for (int j = 0; j < 4; ++j) o[j][0] = o[j][1] = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float dot = 0.f;
+    for (int kg = 0; kg < 4; ++kg) {
+      f32x4 pj[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dot += q[j][e] * kf[e];
-        dot = row16_sum(dot);
-        sc[j][st] = idx < n ? dot : -__builtin_inff();
+      for (int j = 0; j < 4; ++j)
+        pj[j] = *reinterpret_cast<const KD_LDS f32x4*>(s_p + (wave * 4 + j) * 16 + 4 * kg);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t vv = vr[4 * kg + t];
+        const float v0 = u2f(vv << 16), v1 = u2f(vv & 0xffff0000u);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          o[j][0] += pj[j][t] * v0;
+          o[j][1] += pj[j][t] * v1;
+        }
       }
     }
-    float vf[4][8];
 #pragma unroll
-    for (int st = 0; st < 4; ++st) bf16x8_to_f32(vr[st], vf[st]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float mx = fmaxf(fmaxf(sc[j][0], sc[j][1]), fmaxf(sc[j][2], sc[j][3]));
-      mx = rows_max4(mx);
-      float lsum = 0.f, o[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = 0.f;
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const float p = sc[j][st] == -__builtin_inff() ? 0.f : exp2f(sc[j][st] - mx);
-        lsum += p;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] += p * vf[st][e];
-      }
-      lsum = rows_sum4(lsum);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = rows_sum_to_row3(o[e]);
-      if (g == 3) {
-        *reinterpret_cast<KD_LDS f32x4*>(s_o + (wave * 4 + j) * DH + d0) = f32x4{o[0], o[1], o[2], o[3]};
-        *reinterpret_cast<KD_LDS f32x4*>(s_o + (wave * 4 + j) * DH + d0 + 4) = f32x4{o[4], o[5], o[6], o[7]};
-      }
-      if (lane == 0) {
-        s_m[wave * 4 + j] = mx;
-        s_l[wave * 4 + j] = lsum;
-      }
-    }
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<KD_LDS f32x2*>(s_o + (wave * 4 + j) * DH + 2 * lane) = f32x2{o[j][0], o[j][1]};
     lds_sync();
     {
       const int j = threadIdx.x >> 7, dd = threadIdx.x & 127;
@@ -952,10 +1021,9 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
     }
     if (u == wg) trace_mark(a, sy, 3);
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      kr[st] = kn[st];
-      vr[st] = vn[st];
-    }
+    for (int kb = 0; kb < 4; ++kb) kr[kb] = kn[kb];
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) vr[kk] = vn[kk];
     qr = qn;
   }
   // completion counters: one per (stream, head) and layer; thread k takes this
@@ -1076,27 +1144,29 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_head(Args& a_, lds
   KD_LDS unsigned long long* best = reinterpret_cast<KD_LDS unsigned long long*>(red + 8192 + 32);  // [16]
   KD_LDS unsigned* s_flag = reinterpret_cast<KD_LDS unsigned*>(red + 8192 + 64);
 
+  // unit u < nunits: tiles past the last repeat it (their columns are past
+  // the vocabulary and masked); a wave with 2 input groups repeats its last
+  // group in slot 2 and skips it
   auto load_unit = [&](int u, u32x4 (&q)[HEAD_NT][3], uint32_t (&sv)[HEAD_NT][3]) {
 #pragma unroll
     for (int i = 0; i < HEAD_NT; ++i)
 #pragma unroll
       for (int gg = 0; gg < 3; ++gg) {
-        q[i][gg] = u32x4{0u, 0u, 0u, 0u};
-        sv[i][gg] = 0u;
-        const int vt = u * HEAD_NT + i;
-        if (u < nunits && vt < VT && gg < ng) {
-          const size_t idx = ((size_t)vt * KG + kg0 + gg) * 64 + lane;
-          q[i][gg] = *reinterpret_cast<gptr<const u32x4>>(d.hq + idx * 16);
-          sv[i][gg] = *reinterpret_cast<gptr<const uint32_t>>(d.hs + idx * 4);
-        }
+        const int vt = min(u * HEAD_NT + i, VT - 1);
+        const size_t idx = ((size_t)vt * KG + kg0 + min(gg, ng - 1)) * 64 + lane;
+        q[i][gg] = *reinterpret_cast<gptr<const u32x4>>(d.hq + idx * 16);
+        sv[i][gg] = *reinterpret_cast<gptr<const uint32_t>>(d.hs + idx * 4);
       }
   };
 
-  if (sync) grid_arrive(a, sy);
+  if (sync) {
+    grid_arrive(a, sy);
+    if (is_poll_wave()) grid_poll(a, sy);
+  }
   u32x4 q[HEAD_NT][3];
   uint32_t sv[HEAD_NT][3];
-  load_unit(wg, q, sv);
-  if (sync) grid_wait(a, sy);
+  if (wg < nunits) load_unit(wg, q, sv);
+  if (sync) lds_sync();
   trace_mark(a, sy, 2);
   if (threadIdx.x < SR_MAX) best[threadIdx.x] = 0ull;
   RmsRows rms{s.ssq[src], R, 0, a.eps, inv, {}};
@@ -1104,19 +1174,18 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_head(Args& a_, lds
   // A operand (g_o * x, hi/lo f16) for this wave's inputs, kept for all units
   f16x8 ah[3][4], al[3][4];
   {
-    const int r = lane & 15;
+    // rows past R repeat row R-1 (their logits are discarded); slot 2 of a
+    // wave with 2 input groups repeats group 1 and is skipped
+    const int r = min(lane & 15, R - 1);
     f32x4 raw[3][4][2];
 #pragma unroll
     for (int gg = 0; gg < 3; ++gg)
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        raw[gg][t][0] = raw[gg][t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int c0 = (kg0 + gg) * 128 + t * 32 + 8 * (lane >> 4);
-        if (r < R && gg < ng) {
-          auto p = s.xg[src] + r * H + c0;
-          raw[gg][t][0] = *reinterpret_cast<gptr<const f32x4>>(p);
-          raw[gg][t][1] = *reinterpret_cast<gptr<const f32x4>>(p + 4);
-        }
+        const int c0 = (kg0 + min(gg, ng - 1)) * 128 + t * 32 + 8 * (lane >> 4);
+        auto p = s.xg[src] + r * H + c0;
+        raw[gg][t][0] = *reinterpret_cast<gptr<const f32x4>>(p);
+        raw[gg][t][1] = *reinterpret_cast<gptr<const f32x4>>(p + 4);
       }
 #pragma unroll
     for (int gg = 0; gg < 3; ++gg)
@@ -1136,7 +1205,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_head(Args& a_, lds
   for (int u = wg; u < nunits; u += G) {
     u32x4 qn[HEAD_NT][3];
     uint32_t svn[HEAD_NT][3];
-    load_unit(u + G, qn, svn);
+    if (u + G < nunits) load_unit(u + G, qn, svn);
     f32x4 acc[HEAD_NT];
 #pragma unroll
     for (int i = 0; i < HEAD_NT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1263,16 +1332,13 @@ __global__ __launch_bounds__(SMALL_WG) void k_small_phase(const SmallArgs* __res
   trace_mark(a, sy, 7);
 }
 
-__global__ __launch_bounds__(SMALL_WG) void k_small_mega(const SmallArgs* __restrict__ ap) {
+__global__ __launch_bounds__(SMALL_WG) void k_small_mega(const SmallArgs* __restrict__ ap,
+                                                        unsigned epoch0) {
   __shared__ __attribute__((aligned(16))) float red[RED_FLOATS];
-  __shared__ unsigned base;
   Args& a = *(Args*)ap;
-  // the previous launch has finished, so the generation word is stable here
-  if (threadIdx.x == 0) base = ld_rlx(&a.s.bar[17 * 32]);
-  __syncthreads();
   const int np = small_phase_count(a.nl);
   for (int i = 0; i < np; ++i) {
-    const SyncState sy{base, i};
+    const SyncState sy{epoch0, i};
     run_phase(a, small_phase_id(a.nl, i), (lds_f)red, sy, i > 0);
     trace_mark(a, sy, 7);
   }
@@ -1282,9 +1348,9 @@ void launch_small_phase(hipStream_t st, const SmallArgs* dev_args, int G, int ph
   k_small_phase<<<G, SMALL_WG, 0, st>>>(dev_args, phase, slot);
 }
 
-hipError_t launch_small_mega(hipStream_t st, const SmallArgs* dev_args, int G) {
+hipError_t launch_small_mega(hipStream_t st, const SmallArgs* dev_args, int G, unsigned epoch0) {
   const SmallArgs* p = dev_args;
-  void* args[] = {&p};
+  void* args[] = {&p, &epoch0};
   return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_small_mega), dim3(G),
                                     dim3(SMALL_WG), args, 0, st);
 }
