@@ -22,6 +22,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "drafter rounds/s & draft tokens/s at B streams; % of HBM roofline"
 HBM_PEAK_GBS = 8000.0
+# the kernel that runs the whole round, per path (path 3: one launch per round)
+KERNEL_NAME = {3: "kd::k_small_mega"}
 
 
 def algorithmic_bytes(dims, lens, streams):
@@ -37,6 +39,34 @@ def algorithmic_bytes(dims, lens, streams):
                   + 4 * (1 + (dims.block - 1) + 1 + dims.block))
     total = mb["body"] + mb["head"] + mb["vectors"] + kv_row * vis + per_stream * streams
     return dict(total=total, body=mb["body"], head=mb["head"], kv=kv_row * vis)
+
+
+def kernel_source_hash():
+    """sha256 over the HIP sources, first 12 hex digits: identifies the kernels
+    a counter measurement was taken on."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "block_draft_model_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:12]
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch from the rocprofv3 counter summary, if it was taken
+    on the kernels as they are now (same source hash), else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+    try:
+        lines = open(path).read().splitlines()
+    except OSError:
+        return None
+    sha = kernel_source_hash()
+    for line in lines:
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) == 9 and cells[0] == workload and cells[1] == kernel and cells[2] == sha:
+            return int(cells[7].replace(",", ""))
+    return None
 
 
 def cpu_baseline(model, inp, max_seconds=20.0, max_rounds=8):
@@ -83,6 +113,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB 5 times and "
+                         "exit: the calibration kernel for HBM byte counters")
     ap.add_argument("--path", type=int, default=0,
                     help="0 automatic; 1 general multi-kernel; 2 small-batch phases as "
                          "separate launches; 3 small-batch persistent kernel")
@@ -101,6 +134,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU available", file=sys.stderr)
         sys.exit(1)
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src_t = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst_t = torch.empty_like(src_t)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst_t.copy_(src_t)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
+        return
     cfg = synth.CONFIGS[args.config]
     dims = synth.FULL
     model = synth.make_model(dims, cfg["model"], device="cuda")
@@ -135,8 +178,10 @@ def main():
     rounds_s = 1000.0 / ms
     achieved = ab["total"] / (ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "kd_round (whole round)", "bytes_per_launch": ab["total"]}
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(cfg["name"], KERNEL_NAME.get(path, "")),
+                "kernel": KERNEL_NAME.get(path, "several kernels per round"),
+                "bytes_per_launch": ab["total"]}
     out = {"metric": METRIC, "value": round(rounds_s, 2), "unit": "rounds/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
