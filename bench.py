@@ -23,7 +23,7 @@ sys.path.insert(0, ROOT)
 METRIC = "drafter rounds/s & draft tokens/s at B streams; % of HBM roofline"
 HBM_PEAK_GBS = 8000.0
 # the kernel that runs the whole round, per path (path 3: one launch per round)
-KERNEL_NAME = {3: "kd::k_small_mega"}
+KERNEL_NAME = {3: "kd::k_small_mega", 4: "kd::k_stream"}
 
 
 def algorithmic_bytes(dims, lens, streams):
@@ -191,7 +191,7 @@ def main():
                                   f"block-FP8 body, NVFP4 head (60,614 rows)",
                       "streams": B, "draft_tokens_per_round": 4 * B,
                       "path": {1: "general multi-kernel", 2: "small-batch phases, one launch each",
-                               3: "small-batch persistent kernel"}[path]},
+                               3: "small-batch persistent kernel", 4: "streamed persistent kernel"}[path]},
            "draft_tokens_per_s": round(4 * B * rounds_s, 1),
            "bytes_per_round": ab, "hbm_roofline_frac": round(achieved / HBM_PEAK_GBS, 4),
            "wall_s": round(wall, 3), "roofline": roofline}

@@ -33,7 +33,10 @@ struct kd_ctx {
   bool small_ok = false;     // the window fits the small path's attention phase
   unsigned epoch = 0;        // grid barriers completed by persistent launches so far
   bool mega_ok = false;      // persistent cooperative kernel available
-  int path = 0;              // 0 auto, 1 general, 2 small per-phase, 3 small persistent
+  bool stream_ok = false;    // streamed persistent kernel available
+  int nch_stream = 0;        // attention chunks of the window on the streamed path
+  int path = 0;              // 0 auto, 1 general, 2 small per-phase, 3 small persistent,
+                             // 4 streamed persistent
   kd::SmallArgs* args_dev = nullptr;   // device copy of the small-path arguments
   kd::SmallArgs* args_host = nullptr;  // pinned host copy last uploaded
   bool args_valid = false;
@@ -189,7 +192,10 @@ kd_status upload_mat(kd_ctx* c, const HostMat& m, kd::Fp8Mat* out) {
   repack_fp8(m.q.data(), m.s.data(), m.N, m.K, wq.data(), ws.data());
   uint8_t* dw;
   float* ds;
-  if (!dev_alloc(c->weight_allocs, &dw, wq.size()) || !dev_alloc(c->weight_allocs, &ds, ws.size()))
+  // scales get 1 KB of slack: the streamed round copies them in whole 1 KB
+  // chunks, the last of which may run past the matrix
+  if (!dev_alloc(c->weight_allocs, &dw, wq.size()) ||
+      !dev_alloc(c->weight_allocs, &ds, ws.size() + 256))
     return fail(c, KD_ERR_OOM, "weight allocation failed");
   hipError_t e = hipMemcpy(dw, wq.data(), wq.size(), hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(ds, ws.data(), ws.size() * sizeof(float), hipMemcpyHostToDevice);
@@ -330,12 +336,16 @@ kd_status kd_create(const kd_config* cfg, void* hip_stream, kd_ctx** out) {
   // workgroup; longer windows run every round on the general path
   c->small_ok = (long long)kd::SB_MAX * kd::NH * w.att_nch <= (long long)kd::ATT_UNITS_MAX * c->G;
   if (ok && c->small_ok) {
-    ok = dev_alloc(c->work_allocs, &c->small_mem, kd::small_bytes(w.att_nch)) &&
+    // chunk partials of one (stream, head) must not share a 128-byte line with
+    // another's (different workgroups merge them): whole groups of 8 chunks
+    c->nch_stream = ((cfg->window + kd::stream_chunk_keys() - 1) / kd::stream_chunk_keys() + 7) / 8 * 8;
+    ok = dev_alloc(c->work_allocs, &c->small_mem,
+                   kd::small_bytes(std::max(w.att_nch, c->nch_stream))) &&
          dev_alloc(c->work_allocs, &c->args_dev, 1) &&
          hipHostMalloc((void**)&c->args_host, sizeof(kd::SmallArgs), hipHostMallocDefault) ==
              hipSuccess;
     if (ok) {
-      kd::small_carve(c->small_mem, w.att_nch, &c->small);
+      kd::small_carve(c->small_mem, std::max(w.att_nch, c->nch_stream), &c->small);
       ok = hipMemset(c->small.bar, 0, 20 * 32 * sizeof(unsigned)) == hipSuccess &&
            hipMemset(c->small.att_cnt, 0, kd::NL * kd::SB_MAX * kd::NH * 32 * sizeof(unsigned)) ==
                hipSuccess &&
@@ -349,6 +359,7 @@ kd_status kd_create(const kd_config* cfg, void* hip_stream, kd_ctx** out) {
     return KD_ERR_OOM;
   }
   c->mega_ok = c->small_ok && have_prop && prop.cooperativeLaunch && kd::small_mega_occupancy() >= 1;
+  c->stream_ok = c->small_ok && have_prop && prop.cooperativeLaunch && kd::stream_occupancy() >= 1;
   (void)hipGetLastError();
   *out = c;
   return KD_OK;
@@ -500,6 +511,7 @@ kd_status kd_round(kd_ctx* c, int B, const void* taps, const int32_t* anchor, co
   if (path == 0) path = B <= kd::SB_MAX && c->small_ok ? (c->mega_ok ? 3 : 2) : 1;
   if (!c->small_ok) path = 1;
   if (path == 3 && !c->mega_ok) path = 2;
+  if (path == 4 && !c->stream_ok) path = c->mega_ok ? 3 : 2;
   if (path != 1 && B > kd::SB_MAX) path = 1;
   c->last_path = path;
   if (path != 1) {
@@ -510,7 +522,7 @@ kd_status kd_round(kd_ctx* c, int B, const void* taps, const int32_t* anchor, co
     a.R = R;
     a.nl = c->debug_layers < 0 ? kd::NL : c->debug_layers;
     a.window = c->cfg.window;
-    a.nch = w.att_nch;
+    a.nch = path == 4 ? c->nch_stream : w.att_nch;
     a.eps = eps;
     a.theta = c->cfg.rope_theta;
     a.taps = static_cast<const uint16_t*>(taps);
@@ -536,7 +548,11 @@ kd_status kd_round(kd_ctx* c, int B, const void* taps, const int32_t* anchor, co
       c->args_valid = true;
     }
     const int np = kd::small_phase_count(a.nl);
-    if (path == 3) {
+    if (path == 4) {
+      const hipError_t e = kd::launch_stream(st, c->args_dev, c->G, c->epoch);
+      if (e != hipSuccess) return hip_fail(c, e, "streamed round launch");
+      c->epoch += (unsigned)(kd::small_phase_count(a.nl) - 1);
+    } else if (path == 3) {
       const hipError_t e = kd::launch_small_mega(st, c->args_dev, c->G, c->epoch);
       if (e != hipSuccess) return hip_fail(c, e, "persistent round launch");
       c->epoch += (unsigned)(kd::small_phase_count(a.nl) - 1);
@@ -663,7 +679,7 @@ kd_status kd_debug_set_layers(kd_ctx* c, int n) {
 
 kd_status kd_debug_buffers(kd_ctx* c, const float** hidden, const float** fused) {
   if (!c || !hidden || !fused) return KD_ERR_ARG;
-  if (c->last_path == 2 || c->last_path == 3) {
+  if (c->last_path >= 2) {
     const int nl = c->debug_layers < 0 ? kd::NL : c->debug_layers;
     *hidden = c->small.x[nl == 0 ? 0 : kd::xs_d(nl - 1)];
     *fused = c->small.f;
@@ -676,10 +692,12 @@ kd_status kd_debug_buffers(kd_ctx* c, const float** hidden, const float** fused)
 
 kd_status kd_debug_set_path(kd_ctx* c, int path) {
   if (!c) return KD_ERR_ARG;
-  if (path < 0 || path > 3) return fail(c, KD_ERR_ARG, "path must be 0..3");
+  if (path < 0 || path > 4) return fail(c, KD_ERR_ARG, "path must be 0..4");
   if (path >= 2 && !c->small_ok)
     return fail(c, KD_ERR_UNSUPPORTED, "the window is too long for the small-batch path");
   if (path == 3 && !c->mega_ok) return fail(c, KD_ERR_UNSUPPORTED, "no cooperative launch");
+  if (path == 4 && !c->stream_ok)
+    return fail(c, KD_ERR_UNSUPPORTED, "the streamed round kernel cannot be made resident");
   c->path = path;
   return KD_OK;
 }

@@ -82,4 +82,11 @@ void launch_small_phase(hipStream_t st, const SmallArgs* dev_args, int G, int ph
 hipError_t launch_small_mega(hipStream_t st, const SmallArgs* dev_args, int G, unsigned epoch0);
 int small_mega_occupancy();
 
+// The streamed persistent round (kd_stream.hip): same arguments and buffers;
+// SmallArgs::nch must be the number of stream_chunk_keys()-key chunks of the
+// window. epoch0 as for launch_small_mega (the same barrier count per launch).
+hipError_t launch_stream(hipStream_t st, const SmallArgs* dev_args, int G, unsigned epoch0);
+int stream_occupancy();
+int stream_chunk_keys();
+
 }  // namespace kd

@@ -73,7 +73,7 @@ def test_probe_nvfp4_decoder_is_exact():
     assert np.array_equal(got[fin], oracle.round_bf16(exact[fin]))
 
 
-PATHS = [1, 2, 3]   # general multi-kernel, small-batch phases, small-batch persistent
+PATHS = [1, 2, 3, 4]   # general multi-kernel, small-batch phases, small-batch persistent, streamed
 
 
 @pytest.mark.parametrize("path", PATHS)
@@ -121,7 +121,7 @@ def test_round_parity_small_batches(hA, ci, path):
     compare(lg, ids, ref, rid, hA.oracle.vocab, f"{C[ci]['name']} path {path}")
 
 
-@pytest.mark.parametrize("path", [2, 3])
+@pytest.mark.parametrize("path", [2, 3, 4])
 def test_small_path_adapters_gains_and_edges(hC, path):
     """Active spine and predecessor adapters, random gains, and context
     lengths 0, 1, a chunk boundary + 1 and past the ring, on the <= 4-stream path."""
