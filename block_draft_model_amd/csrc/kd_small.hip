@@ -858,7 +858,6 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
   lds_f s_l = s_m + 32;               // [8][4]
   lds_f s_q = s_l + 32;               // [4][128] queries of the unit, scaled
   lds_f s_p = s_q + 4 * DH;           // [8][4][16] probabilities
-  KD_LDS unsigned* s_list = reinterpret_cast<KD_LDS unsigned*>(s_p + 8 * 4 * 16);  // [1 + ATT_UNITS_MAX]
 
   StreamLens sl;
   sl.load(a);  // an input: read before the arrival
@@ -1026,40 +1025,43 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
     for (int kk = 0; kk < 16; ++kk) vr[kk] = vn[kk];
     qr = qn;
   }
-  // completion counters: one per (stream, head) and layer; thread k takes this
-  // workgroup's k-th unit once every partial store of the workgroup is done
+  // completion counters: one per (stream, head) and layer; thread k counts
+  // this workgroup's k-th unit once every partial store of the workgroup is done
   __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0): stores acknowledged
   __syncthreads();
-  if (threadIdx.x == 0) s_list[0] = 0u;
-  lds_sync();
   {
     const int u = wg + threadIdx.x * G;
     if (threadIdx.x < ATT_UNITS_MAX && u < nunits) {
       int b, c, h;
       sl.unit(u, b, c, h);
-      const int nc = (sl.vis(b) + ATT_CH - 1) / ATT_CH;
-      auto cnt = &s.att_cnt[((l * SB_MAX + b) * NH + h) * 32];
-      const unsigned v = add_rlx(cnt, 1u);
-      if (v == (unsigned)(nc - 1)) {
-        __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const unsigned k = __hip_atomic_fetch_add(&s_list[0], 1u, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_WORKGROUP);
-        s_list[1 + k] = (unsigned)(b * NH + h);
-      }
+      (void)add_rlx(&s.att_cnt[((l * SB_MAX + b) * NH + h) * 32], 1u);
     }
   }
-  lds_sync();
-  const unsigned nm = s_list[0];
   trace_mark(a, sy, 5);
-  for (unsigned k = 0; k < nm; ++k) {
-    const unsigned bh = s_list[1 + k];
-    const int b = bh / NH, h = bh % NH;
-    attn_merge(a, l, b, h, sl.vis(b), red);
-  }
-  // streams with an empty context: the block attends to itself only
-  for (int t = wg; t < a.B * NH; t += G) {
-    const int b = t / NH, h = t % NH;
-    if (sl.vis(b) == 0) attn_merge(a, l, b, h, 0, red);
+  // Merges: (stream, head) i is merged by workgroup i * G / (B * NH) -- one
+  // per workgroup, all in parallel -- once its counter shows every chunk
+  // stored. The merging workgroup resets the counter for the next round.
+  // Streams with an empty context attend to the block only.
+  const int nbh = a.B * NH;
+  for (int i = (wg * nbh + G - 1) / G; i < nbh && (i * G) / nbh == wg; ++i) {
+    const int b = i / NH, h = i % NH, n = sl.vis(b);
+    if (n > 0) {
+      if (threadIdx.x == 0) {
+        auto cnt = &s.att_cnt[((l * SB_MAX + b) * NH + h) * 32];
+        const unsigned need = (unsigned)((n + ATT_CH - 1) / ATT_CH);
+        const unsigned long long t0 = wall_clock64();
+        for (unsigned it = 1; ld_rlx(cnt) < need; ++it) {
+          if ((it & 63) == 0 && wall_clock64() - t0 > 20000000ull) {  // 0.2 s
+            __hip_atomic_store(&s.bar[18 * 32], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+        }
+        __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      lds_sync();
+    }
+    attn_merge(a, l, b, h, n, red);
   }
   trace_mark(a, sy, 6);
   trace_mark(a, sy, 4);
