@@ -22,8 +22,11 @@ sys.path.insert(0, ROOT)
 
 METRIC = "drafter rounds/s & draft tokens/s at B streams; % of HBM roofline"
 HBM_PEAK_GBS = 8000.0
-# the kernel that runs the whole round, per path (path 3: one launch per round)
-KERNEL_NAME = {3: "kd::k_small_mega", 4: "kd::k_stream"}
+# the kernel of each small-batch path: path 2 launches k_small_phase once per
+# phase (30 launches per 4-layer round), paths 3 and 4 run the whole round in
+# one launch
+KERNEL_NAME = {2: "kd::k_small_phase", 3: "kd::k_small_mega", 4: "kd::k_stream"}
+LAUNCHES_PER_ROUND = {2: 30, 3: 1, 4: 1}
 
 
 def algorithmic_bytes(dims, lens, streams):
@@ -54,8 +57,9 @@ def kernel_source_hash():
 
 
 def measured_traffic(workload, kernel):
-    """HBM bytes per launch from the rocprofv3 counter summary, if it was taken
-    on the kernels as they are now (same source hash), else None."""
+    """HBM bytes per round moved by the round's launches of `kernel`, from the
+    rocprofv3 counter summary, if it was taken on the kernels as they are now
+    (same source hash), else None."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
     try:
         lines = open(path).read().splitlines()
@@ -118,7 +122,8 @@ def main():
                          "exit: the calibration kernel for HBM byte counters")
     ap.add_argument("--path", type=int, default=0,
                     help="0 automatic; 1 general multi-kernel; 2 small-batch phases as "
-                         "separate launches; 3 small-batch persistent kernel")
+                         "separate launches; 3 small-batch persistent kernel; 4 streamed persistent "
+                         "kernel (experimental)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -176,12 +181,20 @@ def main():
     path = drafter.last_path()
     ab = algorithmic_bytes(dims, lens_host, B)
     rounds_s = 1000.0 / ms
-    achieved = ab["total"] / (ms * 1e-3) / 1e9
+    # roofline of the round's kernel: algorithmic bytes per launch over the
+    # average launch duration (the HIP-event time of the timed rounds on the
+    # stream the kernels run on, divided by the launches of a round)
+    launches = LAUNCHES_PER_ROUND.get(path, 1)
+    per_launch = ab["total"] / launches
+    launch_us = ms * 1e3 / launches
+    achieved = per_launch / (launch_us * 1e-6) / 1e9
+    traffic_round = measured_traffic(cfg["name"], KERNEL_NAME.get(path, ""))
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(cfg["name"], KERNEL_NAME.get(path, "")),
+                "traffic": None if traffic_round is None else round(traffic_round / launches),
                 "kernel": KERNEL_NAME.get(path, "several kernels per round"),
-                "bytes_per_launch": ab["total"]}
+                "launches_per_round": launches, "bytes_per_launch": round(per_launch),
+                "avg_launch_us": round(launch_us, 3)}
     out = {"metric": METRIC, "value": round(rounds_s, 2), "unit": "rounds/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",

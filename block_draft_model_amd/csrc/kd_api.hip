@@ -38,6 +38,12 @@ struct kd_ctx {
   int path = 0;              // 0 auto, 1 general, 2 small per-phase, 3 small persistent,
                              // 4 streamed persistent
   kd::SmallArgs* args_dev = nullptr;   // device copy of the small-path arguments
+  // The per-phase launches of path 2 as one graph: the kernels read their
+  // arguments from args_dev, so the graph depends only on the layer count and
+  // the grid; it is captured on a private stream and launched on the caller's.
+  hipStream_t cap_stream = nullptr;
+  hipGraphExec_t phase_graph = nullptr;
+  int phase_graph_nl = -1;
   kd::SmallArgs* args_host = nullptr;  // pinned host copy last uploaded
   bool args_valid = false;
   unsigned long long* trace = nullptr;  // caller's device buffer for stage timestamps
@@ -374,6 +380,8 @@ kd_status kd_set_stream(kd_ctx* ctx, void* hip_stream) {
 void kd_destroy(kd_ctx* ctx) {
   if (!ctx) return;
   (void)hipStreamSynchronize(ctx->stream);
+  if (ctx->phase_graph) (void)hipGraphExecDestroy(ctx->phase_graph);
+  if (ctx->cap_stream) (void)hipStreamDestroy(ctx->cap_stream);
   free_all(ctx->work_allocs);
   free_all(ctx->weight_allocs);
   if (ctx->args_host) (void)hipHostFree(ctx->args_host);
@@ -508,7 +516,9 @@ kd_status kd_round(kd_ctx* c, int B, const void* taps, const int32_t* anchor, co
   const float eps = c->cfg.rms_eps;
   const int R = kd::BLK * B, B3 = 3 * B;
   int path = c->path;
-  if (path == 0) path = B <= kd::SB_MAX && c->small_ok ? (c->mega_ok ? 3 : 2) : 1;
+  // automatic: the per-phase launches (path 2) are the fastest measured small-
+  // batch form on MI355X; the persistent forms (3, 4) are kept selectable
+  if (path == 0) path = B <= kd::SB_MAX && c->small_ok ? 2 : 1;
   if (!c->small_ok) path = 1;
   if (path == 3 && !c->mega_ok) path = 2;
   if (path == 4 && !c->stream_ok) path = c->mega_ok ? 3 : 2;
@@ -557,8 +567,27 @@ kd_status kd_round(kd_ctx* c, int B, const void* taps, const int32_t* anchor, co
       if (e != hipSuccess) return hip_fail(c, e, "persistent round launch");
       c->epoch += (unsigned)(kd::small_phase_count(a.nl) - 1);
     } else {
-      for (int i = 0; i < np; ++i)
-        kd::launch_small_phase(st, c->args_dev, c->G, kd::small_phase_id(a.nl, i), i);
+      if (!c->phase_graph || c->phase_graph_nl != a.nl) {
+        hipError_t e = hipSuccess;
+        if (c->phase_graph) {
+          (void)hipGraphExecDestroy(c->phase_graph);
+          c->phase_graph = nullptr;
+        }
+        if (!c->cap_stream) e = hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking);
+        hipGraph_t g = nullptr;
+        if (e == hipSuccess) e = hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal);
+        if (e == hipSuccess) {
+          for (int i = 0; i < np; ++i)
+            kd::launch_small_phase(c->cap_stream, c->args_dev, c->G, kd::small_phase_id(a.nl, i), i);
+          e = hipStreamEndCapture(c->cap_stream, &g);
+        }
+        if (e == hipSuccess) e = hipGraphInstantiate(&c->phase_graph, g, nullptr, nullptr, 0);
+        if (g) (void)hipGraphDestroy(g);
+        if (e != hipSuccess) return hip_fail(c, e, "phase graph capture");
+        c->phase_graph_nl = a.nl;
+      }
+      const hipError_t e = hipGraphLaunch(c->phase_graph, st);
+      if (e != hipSuccess) return hip_fail(c, e, "phase graph launch");
     }
     c->last_streams = B;
     const hipError_t e = hipGetLastError();

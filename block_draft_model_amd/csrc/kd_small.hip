@@ -900,24 +900,27 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
     qr = q_l[(b * 4 + (threadIdx.x >> 7)) * H + h * DH + (threadIdx.x & 127)];
   };
 
-  u32x4 kr[4];
-  uint32_t vr[16];
-  float qr;
+  // keys and values of two units ahead are in flight while one is computed
+  u32x4 kr[4], k2[4];
+  uint32_t vr[16], v2[16];
+  float qr, q2;
   if (sync) {
     grid_arrive(a, sy);
     if (is_poll_wave()) grid_poll(a, sy);
   }
   if (wg < nunits) load_kv(wg, kr, vr);
+  if (wg + G < nunits) load_kv(wg + G, k2, v2);
   if (sync) lds_sync();
   if (wg < nunits) load_q(wg, qr);
+  if (wg + G < nunits) load_q(wg + G, q2);
   trace_mark(a, sy, 2);
   for (int u = wg; u < nunits; u += G) {
     u32x4 kn[4];
     uint32_t vn[16];
     float qn;
-    if (u + G < nunits) {
-      load_kv(u + G, kn, vn);
-      load_q(u + G, qn);
+    if (u + 2 * G < nunits) {
+      load_kv(u + 2 * G, kn, vn);
+      load_q(u + 2 * G, qn);
     }
     int b, c, h;
     sl.unit(u, b, c, h);
@@ -1020,10 +1023,17 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
     }
     if (u == wg) trace_mark(a, sy, 3);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) kr[kb] = kn[kb];
+    for (int kb = 0; kb < 4; ++kb) {
+      kr[kb] = k2[kb];
+      k2[kb] = kn[kb];
+    }
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) vr[kk] = vn[kk];
-    qr = qn;
+    for (int kk = 0; kk < 16; ++kk) {
+      vr[kk] = v2[kk];
+      v2[kk] = vn[kk];
+    }
+    qr = q2;
+    q2 = qn;
   }
   // completion counters: one per (stream, head) and layer; thread k counts
   // this workgroup's k-th unit once every partial store of the workgroup is done
