@@ -338,9 +338,8 @@ kd_status kd_create(const kd_config* cfg, void* hip_stream, kd_ctx** out) {
   hipDeviceProp_t prop;
   const bool have_prop = hipGetDeviceProperties(&prop, c->device) == hipSuccess;
   c->G = have_prop ? std::min(prop.multiProcessorCount, kd::MAX_G) : 128;
-  // the small-batch attention phase completes at most ATT_UNITS_MAX chunks per
-  // workgroup; longer windows run every round on the general path
-  c->small_ok = (long long)kd::SB_MAX * kd::NH * w.att_nch <= (long long)kd::ATT_UNITS_MAX * c->G;
+  // the small-batch paths serve any window; they need their buffers below
+  c->small_ok = true;
   if (ok && c->small_ok) {
     // chunk partials of one (stream, head) must not share a 128-byte line with
     // another's (different workgroups merge them): whole groups of 8 chunks
@@ -532,7 +531,9 @@ kd_status kd_round(kd_ctx* c, int B, const void* taps, const int32_t* anchor, co
     a.R = R;
     a.nl = c->debug_layers < 0 ? kd::NL : c->debug_layers;
     a.window = c->cfg.window;
-    a.nch = path == 4 ? c->nch_stream : w.att_nch;
+    // partial slots per (stream, head), padded to whole 128-byte lines of the
+    // per-chunk max and sum (8 chunks): different pairs never share a line
+    a.nch = path == 4 ? c->nch_stream : (w.att_nch + 7) / 8 * 8;
     a.eps = eps;
     a.theta = c->cfg.rope_theta;
     a.taps = static_cast<const uint16_t*>(taps);

@@ -14,7 +14,6 @@ constexpr int HT = H / 16;     // 160 column tiles of a hidden vector
 constexpr int SMALL_WG = 512;  // 8 waves per workgroup
 constexpr int HEAD_NT = 2;     // vocab tiles per head unit
 constexpr int MAX_G = 256;     // workgroups (one per CU); barrier tree is 16 x 16
-constexpr int ATT_UNITS_MAX = 64;  // attention chunks one workgroup completes per layer
 
 // Stage index of the residual stream: the layer input, after O, after down.
 __host__ __device__ inline int xs_in(int l) { return l == 0 ? 0 : 3 * l; }

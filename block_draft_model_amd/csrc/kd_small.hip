@@ -707,6 +707,7 @@ __device__ __forceinline__ int pick4(int b, int x0, int x1, int x2, int x3) {
 struct StreamLens {
   int n0, n1, n2, n3;      // visible context rows min(len, window)
   int f0, f1, f2, f3;      // position of the first visible row
+  int c0, c1, c2, c3;      // chunks of ATT_CH rows per (stream, head)
   int o1, o2, o3, total;   // first attention unit of streams 1..3; all units
   __device__ __forceinline__ void load(Args& a) {
     const int B = a.B, W = a.window;
@@ -720,42 +721,75 @@ struct StreamLens {
     const int l3 = B > 3 ? __builtin_amdgcn_readlane(mine, 3) : 0;
     n0 = min(l0, W); n1 = min(l1, W); n2 = min(l2, W); n3 = min(l3, W);
     f0 = l0 - n0; f1 = l1 - n1; f2 = l2 - n2; f3 = l3 - n3;
-    o1 = NH * ((n0 + ATT_CH - 1) / ATT_CH);
-    o2 = o1 + NH * ((n1 + ATT_CH - 1) / ATT_CH);
-    o3 = o2 + NH * ((n2 + ATT_CH - 1) / ATT_CH);
-    total = o3 + NH * ((n3 + ATT_CH - 1) / ATT_CH);
+    c0 = (n0 + ATT_CH - 1) / ATT_CH;
+    c1 = (n1 + ATT_CH - 1) / ATT_CH;
+    c2 = (n2 + ATT_CH - 1) / ATT_CH;
+    c3 = (n3 + ATT_CH - 1) / ATT_CH;
+    o1 = NH * c0;
+    o2 = o1 + NH * c1;
+    o3 = o2 + NH * c2;
+    total = o3 + NH * c3;
   }
   __device__ __forceinline__ int vis(int b) const { return pick4(b, n0, n1, n2, n3); }
   __device__ __forceinline__ int first(int b) const { return pick4(b, f0, f1, f2, f3); }
-  // Unit u -> stream b, chunk c, head h (stream-major, then chunk, then head,
-  // so the chunks of one (stream, head) lie NH units apart). A stream with no
-  // units shares its offset with the next one, which then wins.
+  __device__ __forceinline__ int chunks(int b) const { return pick4(b, c0, c1, c2, c3); }
+  // Unit u -> stream b, chunk c, head h (stream-major, then head, then chunk,
+  // so the chunks of one (stream, head) are consecutive units). A stream with
+  // no units shares its offset with the next one, which then wins.
   __device__ __forceinline__ void unit(int u, int& b, int& c, int& h) const {
     b = u >= o3 ? 3 : (u >= o2 ? 2 : (u >= o1 ? 1 : 0));
-    const int loc = u - pick4(b, 0, o1, o2, o3);
-    c = loc / NH;
-    h = loc - c * NH;
+    const int loc = u - pick4(b, 0, o1, o2, o3), nc = chunks(b);
+    h = loc / nc;
+    c = loc - h * nc;
+  }
+  __device__ __forceinline__ int first_unit(int b, int h) const {
+    return pick4(b, 0, o1, o2, o3) + h * chunks(b);
+  }
+  // Workgroup w of G takes the units [start(w), start(w + 1)); owner(u) is
+  // the workgroup whose range holds unit u.
+  __device__ __forceinline__ int start(int w, int G) const { return (w * total) / G; }
+  __device__ __forceinline__ int owner(int u, int G) const { return ((u + 1) * G - 1) / total; }
+  // Segments the ranges cut the units [u0, u0 + nc) into: with at least as
+  // many units as workgroups every range is non-empty; with fewer, a range
+  // holds at most one unit.
+  __device__ __forceinline__ int segments(int u0, int nc, int G) const {
+    return total < G ? nc : owner(u0 + nc - 1, G) - owner(u0, G) + 1;
   }
 };
 
-// Merge of the chunk partials of one (stream, head) with the block's own keys
-// (row j sees block rows 0..j); thread (j, d). Called by the workgroup whose
-// chunk completed the (stream, head), after the completion counter says so.
+// Merge of the partials of one (stream, head) with the block's own keys (row
+// j sees block rows 0..j); thread (j, d). The partials are those of the
+// segments of its chunks that the workgroups' ranges cut out, each stored at
+// the slot of its first chunk; u0 is the pair's first unit and U all units.
 __device__ __attribute__((noinline, not_tail_called)) void attn_merge(Args& a_, int l_, int b_, int h_, int n_,
-                                                     lds_f red) {
+                                                     int u0_, int U_, lds_f red) {
   const auto l = uni(l_);
   const auto b = uni(b_);
   const auto h = uni(h_);
   const auto n = uni(n_);
+  const auto u0 = uni(u0_);
+  const auto U = uni(U_);
   Args& a = uni(a_);
   auto& s = a.s;
+  const int G = gridDim.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nch = a.nch;
   const float qs = 0.08838834764831845f * 1.4426950408889634f;  // 1/sqrt(128) * log2(e)
   const int nc = (n + ATT_CH - 1) / ATT_CH;
+  // segments: with at least as many units as workgroups every range is
+  // non-empty, and the pair's segments are those of workgroups owner(u0) ..
+  // owner(u0 + nc - 1), segment k starting at chunk max(start(w0 + k), u0) - u0;
+  // with fewer, a range holds at most one unit and every chunk is a segment
+  const bool one_each = U < G;
+  int w0 = 0, nseg = 0;
+  if (nc > 0) {
+    w0 = ((u0 + 1) * G - 1) / U;
+    nseg = one_each ? nc : ((u0 + nc) * G - 1) / U - w0 + 1;
+  }
+  auto seg_chunk = [&](int k) { return one_each ? k : max(((w0 + k) * U) / G, u0) - u0; };
   const int j = threadIdx.x >> 7, dd = threadIdx.x & 127;
-  // block queries, keys and values first, then every chunk partial: the loads
-  // go out together
+  // block queries, keys and values first, then every segment partial: the
+  // loads go out together
   const int jw = wave >> 1, dw = 64 * (wave & 1) + lane;
   const float qv = s.q[l][(b * 4 + jw) * H + h * DH + dw];
   float kb4[4], vv[4];
@@ -764,35 +798,36 @@ __device__ __attribute__((noinline, not_tail_called)) void attn_merge(Args& a_, 
     kb4[i] = s.k[l][(b * 4 + i) * H + h * DH + dw];
     vv[i] = s.v[l][(b * 4 + i) * H + h * DH + dd];
   }
-  constexpr int MAXC = 16;
-  float pm[MAXC], pl[MAXC], po[MAXC];
+  constexpr int MAXS = 16;
+  float pm[MAXS], pl[MAXS], po[MAXS];
   const size_t base = (size_t)(b * NH + h) * nch;
   auto am = s.am[l] + base * 4 + j;
   auto al = s.al[l] + base * 4 + j;
   auto ao = s.ao[l] + (base * 4 + j) * DH + dd;
-  // every load issued together: chunks past the last one re-read it and are
-  // masked afterwards
-  const int clast = max(nc - 1, 0);
+  // segments past the last one re-read it and are masked afterwards
+  const int klast = max(nseg - 1, 0);
 #pragma unroll
-  for (int c = 0; c < MAXC; ++c) {
-    const int cc = min(c, clast);
-    pm[c] = am[cc * 4];
-    pl[c] = al[cc * 4];
-    po[c] = ao[(size_t)cc * 4 * DH];
+  for (int k = 0; k < MAXS; ++k) {
+    const int cc = seg_chunk(min(k, klast));
+    pm[k] = am[cc * 4];
+    pl[k] = al[cc * 4];
+    po[k] = ao[(size_t)cc * 4 * DH];
   }
 #pragma unroll
-  for (int c = 0; c < MAXC; ++c)
-    if (c >= nc) {
-      pm[c] = -__builtin_inff();
-      pl[c] = 0.f;
-      po[c] = 0.f;
+  for (int k = 0; k < MAXS; ++k)
+    if (k >= nseg) {
+      pm[k] = -__builtin_inff();
+      pl[k] = 0.f;
+      po[k] = 0.f;
     }
-  for (int c = MAXC; c < nc; ++c) {  // windows beyond 2048 rows: fold the rest in
-    const float m1 = am[c * 4];
+  for (int k = MAXS; k < nseg; ++k) {  // more segments than registers: fold the rest in
+    const int cc = seg_chunk(k);
+    const float m1 = am[cc * 4];
+    if (m1 == -__builtin_inff()) continue;
     const float mn = fmaxf(pm[0], m1);
-    const float f0 = exp2f(pm[0] - mn), f1 = exp2f(m1 - mn);
-    pl[0] = pl[0] * f0 + al[c * 4] * f1;
-    po[0] = po[0] * f0 + ao[(size_t)c * 4 * DH] * f1;
+    const float f0 = pm[0] == -__builtin_inff() ? 0.f : exp2f(pm[0] - mn), f1 = exp2f(m1 - mn);
+    pl[0] = pl[0] * f0 + al[cc * 4] * f1;
+    po[0] = po[0] * f0 + ao[(size_t)cc * 4 * DH] * f1;
     pm[0] = mn;
   }
   // block scores s[j][i] = q_j . k_i: wave w covers row w/2, dims 64*(w%2)..
@@ -807,17 +842,17 @@ __device__ __attribute__((noinline, not_tail_called)) void attn_merge(Args& a_, 
   for (int i = 0; i < 4; ++i) sb[i] = (red[(2 * j) * 4 + i] + red[(2 * j + 1) * 4 + i]) * qs;
   float M = -__builtin_inff();
 #pragma unroll
-  for (int c = 0; c < MAXC; ++c) M = fmaxf(M, pm[c]);
+  for (int k = 0; k < MAXS; ++k) M = fmaxf(M, pm[k]);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     if (i <= j) M = fmaxf(M, sb[i]);
   float Ls = 0.f, O = 0.f;
 #pragma unroll
-  for (int c = 0; c < MAXC; ++c) {
-    if (pm[c] != -__builtin_inff()) {
-      const float f = exp2f(pm[c] - M);
-      Ls += pl[c] * f;
-      O += po[c] * f;
+  for (int k = 0; k < MAXS; ++k) {
+    if (pm[k] != -__builtin_inff()) {
+      const float f = exp2f(pm[k] - M);
+      Ls += pl[k] * f;
+      O += po[k] * f;
     }
   }
 #pragma unroll
@@ -831,46 +866,175 @@ __device__ __attribute__((noinline, not_tail_called)) void attn_merge(Args& a_, 
   lds_sync();
 }
 
-// Attention over one chunk of 128 context keys for one (stream, head). Wave w
-// takes keys 16w..16w+15:
+// LDS of the attention phase. Keys, values and queries arrive by global-to-LDS
+// copies into a two-slot ring (slot = parity of the workgroup's unit count):
+// per slot, 8 blocks of 1 KB per wave for its 16 keys (4 key blocks, 4 value
+// blocks; a copy puts lane l's 16 bytes at l * 16, and the same lane reads
+// them back), then 2 blocks of queries ([4][128] fp32, copied by wave 0).
+// The ring is also the reduction area of every other phase.
+constexpr int ATT_WAVE_BLOCKS = 8;
+constexpr int ATT_SLOT_BLOCKS = 8 * ATT_WAVE_BLOCKS + 2;
+constexpr unsigned ATT_SLOT_BYTES = ATT_SLOT_BLOCKS * 1024u;
+__shared__ __attribute__((aligned(16))) u32x4 g_att_ring[2][ATT_SLOT_BLOCKS][64];
+// per-wave outputs [8][4][128], softmax max and sum [8][4] each, probabilities [8][4][16]
+constexpr int ATT_SMALL = 8 * 4 * DH + 32 + 32 + 8 * 4 * 16;
+__shared__ __attribute__((aligned(16))) float g_att_small[ATT_SMALL];
+
+// Waits until at most N vector memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void att_wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+__device__ __forceinline__ void att_wait_vm(int n) {
+  if (n >= 10) att_wait_vm<10>();
+  else if (n >= 8) att_wait_vm<8>();
+  else if (n >= 2) att_wait_vm<2>();
+  else att_wait_vm<0>();
+}
+
+// Reads the lane's 4 key and 4 value blocks (at kva, 1 KB apart) and waits
+// for the reads. The copies that filled them must have landed.
+__device__ __forceinline__ void att_read_kv(unsigned kva, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %8 offset:1024\n\t"
+      "ds_read_b128 %2, %8 offset:2048\n\t"
+      "ds_read_b128 %3, %8 offset:3072\n\t"
+      "ds_read_b128 %4, %8 offset:4096\n\t"
+      "ds_read_b128 %5, %8 offset:5120\n\t"
+      "ds_read_b128 %6, %8 offset:6144\n\t"
+      "ds_read_b128 %7, %8 offset:7168\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(kr[0]), "=&v"(kr[1]), "=&v"(kr[2]), "=&v"(kr[3]), "=&v"(vr[0]), "=&v"(vr[1]),
+        "=&v"(vr[2]), "=&v"(vr[3])
+      : "v"(kva)
+      : "memory");
+}
+// Reads 8 x 16 B of one query row (at qa: dims 32 kb + 8 (lane / 16) .. + 8
+// for kb = 0..3) and waits for the reads.
+__device__ __forceinline__ void att_read_q(unsigned qa, u32x4 (&qv)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %8 offset:16\n\t"
+      "ds_read_b128 %2, %8 offset:128\n\t"
+      "ds_read_b128 %3, %8 offset:144\n\t"
+      "ds_read_b128 %4, %8 offset:256\n\t"
+      "ds_read_b128 %5, %8 offset:272\n\t"
+      "ds_read_b128 %6, %8 offset:384\n\t"
+      "ds_read_b128 %7, %8 offset:400\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(qv[0]), "=&v"(qv[1]), "=&v"(qv[2]), "=&v"(qv[3]), "=&v"(qv[4]), "=&v"(qv[5]),
+        "=&v"(qv[6]), "=&v"(qv[7])
+      : "v"(qa)
+      : "memory");
+}
+
+// LDS reads of the attention phase that the compiler must not see: it would
+// make every LDS read wait for all global-to-LDS copies in flight. Each reads
+// and waits for its own results.
+// Four 16-byte reads at addr + 64 i.
+__device__ __forceinline__ void att_read_p(unsigned addr, f32x4 (&r)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:64\n\t"
+      "ds_read_b128 %2, %4 offset:128\n\t"
+      "ds_read_b128 %3, %4 offset:192\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(addr)
+      : "memory");
+}
+// Writes a wave's max at ma and its sum at ma + 128 (kept from the compiler,
+// which would make the writes wait for the global-to-LDS copies in flight).
+__device__ __forceinline__ void att_write_ml(unsigned ma, float m, float l) {
+  asm volatile("ds_write_b32 %0, %1\n\tds_write_b32 %0, %2 offset:128" : : "v"(ma), "v"(m), "v"(l) : "memory");
+}
+// Eight waves' max (at ma + 16 w), sum (at ma + 128 + 16 w) and output (at
+// oa + 2048 w).
+__device__ __forceinline__ void att_read_mlo(unsigned ma, unsigned oa, float (&m)[8], float (&ls)[8],
+                                             float (&o)[8]) {
+  asm volatile(
+      "ds_read_b32 %0, %24\n\t"
+      "ds_read_b32 %1, %24 offset:16\n\t"
+      "ds_read_b32 %2, %24 offset:32\n\t"
+      "ds_read_b32 %3, %24 offset:48\n\t"
+      "ds_read_b32 %4, %24 offset:64\n\t"
+      "ds_read_b32 %5, %24 offset:80\n\t"
+      "ds_read_b32 %6, %24 offset:96\n\t"
+      "ds_read_b32 %7, %24 offset:112\n\t"
+      "ds_read_b32 %8, %24 offset:128\n\t"
+      "ds_read_b32 %9, %24 offset:144\n\t"
+      "ds_read_b32 %10, %24 offset:160\n\t"
+      "ds_read_b32 %11, %24 offset:176\n\t"
+      "ds_read_b32 %12, %24 offset:192\n\t"
+      "ds_read_b32 %13, %24 offset:208\n\t"
+      "ds_read_b32 %14, %24 offset:224\n\t"
+      "ds_read_b32 %15, %24 offset:240\n\t"
+      "ds_read_b32 %16, %25\n\t"
+      "ds_read_b32 %17, %25 offset:2048\n\t"
+      "ds_read_b32 %18, %25 offset:4096\n\t"
+      "ds_read_b32 %19, %25 offset:6144\n\t"
+      "ds_read_b32 %20, %25 offset:8192\n\t"
+      "ds_read_b32 %21, %25 offset:10240\n\t"
+      "ds_read_b32 %22, %25 offset:12288\n\t"
+      "ds_read_b32 %23, %25 offset:14336\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(m[0]), "=&v"(m[1]), "=&v"(m[2]), "=&v"(m[3]), "=&v"(m[4]), "=&v"(m[5]), "=&v"(m[6]),
+        "=&v"(m[7]), "=&v"(ls[0]), "=&v"(ls[1]), "=&v"(ls[2]), "=&v"(ls[3]), "=&v"(ls[4]),
+        "=&v"(ls[5]), "=&v"(ls[6]), "=&v"(ls[7]), "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]),
+        "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+      : "v"(ma), "v"(oa)
+      : "memory");
+}
+
+// Attention over the round's units: a unit is one chunk of ATT_CH = 128
+// context keys of one (stream, head), and workgroup w takes the contiguous
+// unit range [start(w), start(w + 1)) in (stream, head, chunk) order, so that
+// its consecutive units are chunks of one (stream, head) pair. Wave v takes
+// keys 16v .. 16v+15 of every unit and keeps an online softmax over them:
 //   scores  S^T[key][j] = K Q^T on the matrix cores (16x16x32 bf16): K rows as
 //           the A operand (lane: key lane%16, dims 32kb + 8(lane/16)), the
 //           queries split into bf16 hi + lo as B (column j < 4 of 4 block rows);
-//   softmax per row j over the wave's 16 keys, probabilities to LDS;
-//   P V     on the vector units, lane l owning dims 2l, 2l+1, probabilities
-//           read back as LDS broadcasts -- no cross-lane sums for the output.
-// The next unit's keys, values and queries are loaded while one is computed.
-// A (stream, head) is complete when all its chunks have stored their partials;
-// completion counters are taken once, after the workgroup's last unit, and the
-// workgroup that completes a (stream, head) merges it.
-__device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int l_, lds_f red, SyncState sy,
+//   softmax running max and sum per row j, the output rescaled when the max
+//           grows;
+//   P V     on the vector units from 16-byte value rows (8 dims of 4 keys per
+//           lane), probabilities passed through the wave's own LDS area.
+// Keys, values and queries are copied into LDS one unit ahead (global-to-LDS
+// copies hold no registers; the waits on them are explicit). Where a pair's
+// chunks end, or the range does, the 8 waves' states are merged into one
+// partial per segment, stored at the slot of the segment's first chunk; the
+// pair's counter then counts the segment, and a designated workgroup per
+// (stream, head) merges its segments with the block's own keys.
+__device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int l_, SyncState sy,
                                                   bool sync) {
   const auto l = uni(l_);
   Args& a = uni(a_);
   const int G = gridDim.x, wg = blockIdx.x;
   auto& s = a.s;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wave_s = uni(wave);
   const int lr = lane & 15, lg = lane >> 4;
   const int nch = a.nch;
   const float qs = 0.08838834764831845f * 1.4426950408889634f;
-  lds_f s_o = red;                    // [8][4][128] per-wave outputs
-  lds_f s_m = red + 8 * 4 * DH;       // [8][4]
-  lds_f s_l = s_m + 32;               // [8][4]
-  lds_f s_q = s_l + 32;               // [4][128] queries of the unit, scaled
-  lds_f s_p = s_q + 4 * DH;           // [8][4][16] probabilities
+  lds_f s_o = (lds_f)g_att_small;      // [8][4][128] per-wave outputs
+  lds_f s_m = s_o + 8 * 4 * DH;        // [8][4]
+  lds_f s_l = s_m + 32;                // [8][4]
+  lds_f s_p = s_l + 32;                // [8][4][16] probabilities
 
   StreamLens sl;
   sl.load(a);  // an input: read before the arrival
-  const int nunits = sl.total;
+  const int U = sl.total;
+  const int ub = U > 0 ? sl.start(wg, G) : 0, ue = U > 0 ? sl.start(wg + 1, G) : 0;
   auto kb_l = a.kv.k[l], vb_l = a.kv.v[l];
   const long long kv_ss = a.kv.ss, kv_sh = a.kv.sh, kv_sl = a.kv.sl;
   const int kv_cap = a.kv.cap;
   auto q_l = s.q[l];
-  // Issues the key/value loads of unit u (u < nunits): keys past the visible
-  // rows are clamped to the last one and masked out of the scores. Keys and
-  // values are inputs, so the first unit's are loaded before the barrier; the
-  // queries come from the previous phase.
-  auto load_kv = [&](int u, u32x4 (&kr)[4], uint32_t (&vr)[16]) {
+  // Copies the keys and values of unit u into ring slot `slot`: keys past the
+  // visible rows are clamped to the last one and masked out of the scores.
+  // Keys and values are inputs, so the first units' copies go out before the
+  // barrier; the queries come from the previous phase.
+  auto copy_kv = [&](int u, int slot) {
     int b, c, h;
     sl.unit(u, b, c, h);
     const int n = sl.vis(b), fp = sl.first(b);
@@ -883,70 +1047,111 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
       int sl_ = s0 + min(off, last);
       return sl_ - (sl_ >= kv_cap ? kv_cap : 0);
     };
-    {
-      const size_t row = (size_t)slot_of(wave * 16 + lr) * kv_sl;
+    KD_LDS u32x4* dst = (KD_LDS u32x4*)&g_att_ring[slot][wave_s * ATT_WAVE_BLOCKS][0];
+    const size_t krow = (size_t)slot_of(wave * 16 + lr) * kv_sl;
+    // key block kb: lane (key lr, group lg) brings dims 32 kb + 8 lg .. + 8
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        kr[kb] = *reinterpret_cast<gptr<const u32x4>>(kbase + row + 32 * kb + 8 * lg);
-    }
+    for (int kb = 0; kb < 4; ++kb)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(kbase + krow + 32 * kb + 8 * lg),
+                                       (KD_LDS void*)(dst + kb * 64), 16, 0, 0);
+    // value block t: lane (group g = lg, c = lr) brings key 4g + t, dims 8c .. + 8
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk)
-      vr[kk] = *reinterpret_cast<gptr<const uint32_t>>(vbase + (size_t)slot_of(wave * 16 + kk) * kv_sl +
-                                                       2 * lane);
+    for (int t = 0; t < 4; ++t)
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<const void*>(vbase + (size_t)slot_of(wave * 16 + 4 * lg + t) * kv_sl + 8 * lr),
+          (KD_LDS void*)(dst + (4 + t) * 64), 16, 0, 0);
   };
-  auto load_q = [&](int u, float& qr) {
+  // wave 0 copies the unit's 4 query rows (2 x 1 KB) into the slot
+  auto copy_q = [&](int u, int slot) {
+    if (wave_s != 0) return;
     int b, c, h;
     sl.unit(u, b, c, h);
-    qr = q_l[(b * 4 + (threadIdx.x >> 7)) * H + h * DH + (threadIdx.x & 127)];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int e = i * 256 + lane * 4, j = e >> 7, d = e & 127;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(q_l + (b * 4 + j) * H + h * DH + d),
+                                       (KD_LDS void*)(KD_LDS u32x4*)&g_att_ring[slot][8 * ATT_WAVE_BLOCKS + i][0], 16, 0,
+                                       0);
+    }
   };
+  const unsigned ring0 = (unsigned)(uintptr_t)&g_att_ring[0][0][0];
 
-  // keys and values of two units ahead are in flight while one is computed
-  u32x4 kr[4], k2[4];
-  uint32_t vr[16], v2[16];
-  float qr, q2;
   if (sync) {
     grid_arrive(a, sy);
     if (is_poll_wave()) grid_poll(a, sy);
   }
-  if (wg < nunits) load_kv(wg, kr, vr);
-  if (wg + G < nunits) load_kv(wg + G, k2, v2);
-  if (sync) lds_sync();
-  if (wg < nunits) load_q(wg, qr);
-  if (wg + G < nunits) load_q(wg + G, q2);
+  if (ub < ue) {
+    copy_kv(ub, 0);
+    if (!sync) copy_q(ub, 0);
+  }
+  if (ub + 1 < ue) {
+    copy_kv(ub + 1, 1);
+    if (!sync) copy_q(ub + 1, 1);
+  }
+  if (sync) {
+    lds_sync();
+    if (ub < ue) copy_q(ub, 0);
+    if (ub + 1 < ue) copy_q(ub + 1, 1);
+  }
   trace_mark(a, sy, 2);
-  for (int u = wg; u < nunits; u += G) {
-    u32x4 kn[4];
-    uint32_t vn[16];
-    float qn;
-    if (u + 2 * G < nunits) {
-      load_kv(u + 2 * G, kn, vn);
-      load_q(u + 2 * G, qn);
-    }
+
+  // the wave's running state for the current segment: scaled queries as the
+  // B operand, max and sum of row lr (lanes lr < 4), output of rows 0..3 for
+  // the lane's dims 8 (lane % 16) .. + 8 over its key group lane / 16
+  bf16x8 qh[4], ql[4];
+  float m_run = -__builtin_inff(), l_run = 0.f;
+  float o[4][8];
+  int seg_c0 = 0;
+  int slot = 0;
+  for (int u = ub; u < ue; ++u, slot ^= 1) {
     int b, c, h;
     sl.unit(u, b, c, h);
-    const int n = sl.vis(b);
-    s_q[threadIdx.x] = qr * qs;
-    lds_sync();
-    // B operand: Q^T split into bf16 hi + lo; columns j >= 4 are zero
+    const int n = sl.vis(b), nc = sl.chunks(b);
+    const bool seg_start = u == ub || c == 0;
+    const bool seg_end = u + 1 == ue || c == nc - 1;
+    // copies per unit: 8 per wave, 10 for wave 0 (its query blocks); in the
+    // persistent kernel wave 0's first two query copies follow both key/value
+    // sets, so its first unit waits for the second unit's queries only
+    const bool next = u + 1 < ue;
+    const int nwait = !next ? 0 : (wave_s != 0 ? 8 : (sync && u == ub ? 2 : 10));
+    att_wait_vm(uni(nwait));
+    if (seg_start) {
+      // wave 0's query copy has landed for every wave; the previous
+      // segment's readers of the shared LDS areas are done
+      lds_sync();
+      u32x4 qw[8];
+      att_read_q(ring0 + slot * ATT_SLOT_BYTES + 8 * ATT_WAVE_BLOCKS * 1024 + min(lr, 3) * 512 + lg * 32,
+                 qw);
+      // no wave copies the next queries into this slot before all have read them
+      lds_sync();
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        float qv[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qv[e] = lr < 4 ? u2f(qw[2 * kb][e]) * qs : 0.f;
+          qv[4 + e] = lr < 4 ? u2f(qw[2 * kb + 1][e]) * qs : 0.f;
+        }
+        split_bf16(qv, qh[kb], ql[kb]);
+      }
+      m_run = -__builtin_inff();
+      l_run = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
+      seg_c0 = c;
+    }
+    u32x4 kr[4], vr[4];
+    att_read_kv(ring0 + slot * ATT_SLOT_BYTES + wave * ATT_WAVE_BLOCKS * 1024 + lane * 16, kr, vr);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      float qv[8];
-      const int jq = min(lr, 3);
-      const f32x4 q0 = *reinterpret_cast<const KD_LDS f32x4*>(s_q + jq * DH + 32 * kb + 8 * lg);
-      const f32x4 q1 = *reinterpret_cast<const KD_LDS f32x4*>(s_q + jq * DH + 32 * kb + 8 * lg + 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qv[e] = lr < 4 ? q0[e] : 0.f;
-        qv[4 + e] = lr < 4 ? q1[e] : 0.f;
-      }
-      bf16x8 qh, ql;
-      split_bf16(qv, qh, ql);
       const bf16x8 kk = __builtin_bit_cast(bf16x8, kr[kb]);
-      acc = mfma_bf16(kk, qh, acc);
-      acc = mfma_bf16(kk, ql, acc);
+      acc = mfma_bf16(kk, qh[kb], acc);
+      acc = mfma_bf16(kk, ql[kb], acc);
     }
-    // lane holds S^T[key 4 lg + e][j = lr]; softmax over the wave's 16 keys
+    // lane holds S^T[key 4 lg + e][j = lr] of the wave's 16 keys
     float sc[4], mx = -__builtin_inff();
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -956,109 +1161,130 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    // rescale of the state so far (0 while it is empty)
+    const float alpha = m_run == -__builtin_inff() ? 0.f : exp2f(m_run - m_new);
     float pe[4], ls = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      pe[e] = sc[e] == -__builtin_inff() ? 0.f : exp2f(sc[e] - mx);
+      pe[e] = sc[e] == -__builtin_inff() ? 0.f : exp2f(sc[e] - m_new);
       ls += pe[e];
     }
     ls += __shfl_xor(ls, 16, 64);
     ls += __shfl_xor(ls, 32, 64);
-    if (lr < 4) {
+    l_run = l_run * alpha + ls;
+    m_run = m_new;
+    if (lr < 4)
       *reinterpret_cast<KD_LDS f32x4*>(s_p + (wave * 4 + lr) * 16 + 4 * lg) =
           f32x4{pe[0], pe[1], pe[2], pe[3]};
-      if (lg == 0) {
-        s_m[wave * 4 + lr] = mx;
-        s_l[wave * 4 + lr] = ls;
-      }
-    }
-    // P V: this wave's own probabilities (LDS operations of a wave complete in
-    // order; the signal fence keeps the compiler from moving the reads up)
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    float o[4][2];
+    // the rescale factor of row j lives in lane j
+    float aj[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o[j][0] = o[j][1] = 0.f;
-#pragma unroll
-    for (int kg = 0; kg < 4; ++kg) {
-      f32x4 pj[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        pj[j] = *reinterpret_cast<const KD_LDS f32x4*>(s_p + (wave * 4 + j) * 16 + 4 * kg);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const uint32_t vv = vr[4 * kg + t];
-        const float v0 = u2f(vv << 16), v1 = u2f(vv & 0xffff0000u);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          o[j][0] += pj[j][t] * v0;
-          o[j][1] += pj[j][t] * v1;
-        }
-      }
-    }
+    for (int j = 0; j < 4; ++j) aj[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), j));
+    // P V: lane (g, c) = (lane / 16, lane % 16) adds its keys 4g..4g+3 for
+    // dims 8c..8c+7 and all 4 rows (the wave's own probabilities: LDS
+    // operations of a wave complete in order)
+    f32x4 pj[4];  // pj[j] = probabilities of row j, keys 4g .. 4g+3
+    att_read_p((unsigned)(uintptr_t)(s_p + wave * 64 + 4 * lg), pj);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<KD_LDS f32x2*>(s_o + (wave * 4 + j) * DH + 2 * lane) = f32x2{o[j][0], o[j][1]};
-    lds_sync();
-    {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[j][e] *= aj[j];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float vf[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        vf[2 * i] = u2f(vr[t][i] << 16);
+        vf[2 * i + 1] = u2f(vr[t][i] & 0xffff0000u);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[j][e] += pj[j][t] * vf[e];
+    }
+    // the slot is free again: copy the unit after next into it
+    if (u + 2 < ue) {
+      copy_kv(u + 2, slot);
+      copy_q(u + 2, slot);
+    }
+    if (u == ub) trace_mark(a, sy, 3);
+    if (seg_end) {
+      // sum the 4 key groups: groups g and g^2 exchange, g < 2 keeping rows
+      // 0, 1 and g >= 2 rows 2, 3; then g and g^1, odd groups keeping the
+      // second of their rows -- group g ends with row g
+      const bool upper = lg >= 2, odd = lg & 1;
+      float r1[2][8];
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float keep = upper ? o[2 + jj][e] : o[jj][e];
+          const float send = upper ? o[jj][e] : o[2 + jj][e];
+          r1[jj][e] = keep + __shfl_xor(send, 32, 64);
+        }
+      f32x4 r2a, r2b;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float keep = odd ? r1[1][e] : r1[0][e];
+        const float send = odd ? r1[0][e] : r1[1][e];
+        const float v = keep + __shfl_xor(send, 16, 64);
+        if (e < 4) r2a[e] = v; else r2b[e - 4] = v;
+      }
+      *reinterpret_cast<KD_LDS f32x4*>(s_o + (wave * 4 + lg) * DH + 8 * lr) = r2a;
+      *reinterpret_cast<KD_LDS f32x4*>(s_o + (wave * 4 + lg) * DH + 8 * lr + 4) = r2b;
+      if (lr < 4 && lg == 0) att_write_ml((unsigned)(uintptr_t)(s_m + wave * 4 + lr), m_run, l_run);
+      lds_sync();
+      // thread (j, d): merge of the 8 waves, stored as the segment's partial
       const int j = threadIdx.x >> 7, dd = threadIdx.x & 127;
+      float mw[8], lw[8], ow[8];
+      att_read_mlo((unsigned)(uintptr_t)(s_m + j), (unsigned)(uintptr_t)(s_o + j * DH + dd), mw, lw, ow);
       float M = -__builtin_inff();
 #pragma unroll
-      for (int w = 0; w < 8; ++w) M = fmaxf(M, s_m[w * 4 + j]);
+      for (int w = 0; w < 8; ++w) M = fmaxf(M, mw[w]);
       float Ls = 0.f, O = 0.f;
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
-        const float mw = s_m[w * 4 + j];
-        if (mw != -__builtin_inff()) {
-          const float f = exp2f(mw - M);
-          Ls += s_l[w * 4 + j] * f;
-          O += s_o[(w * 4 + j) * DH + dd] * f;
+        if (mw[w] != -__builtin_inff()) {
+          const float f = exp2f(mw[w] - M);
+          Ls += lw[w] * f;
+          O += ow[w] * f;
         }
       }
-      const size_t pb = ((size_t)(b * NH + h) * nch + c) * 4 + j;
+      const size_t pb = ((size_t)(b * NH + h) * nch + seg_c0) * 4 + j;
       st_wt(&s.ao[l][pb * DH + dd], O);
       if (dd == 0) {
         st_wt(&s.am[l][pb], M);
         st_wt(&s.al[l][pb], Ls);
       }
+      // the next segment starts with a barrier before the LDS areas are reused
     }
-    if (u == wg) trace_mark(a, sy, 3);
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      kr[kb] = k2[kb];
-      k2[kb] = kn[kb];
-    }
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      vr[kk] = v2[kk];
-      v2[kk] = vn[kk];
-    }
-    qr = q2;
-    q2 = qn;
   }
-  // completion counters: one per (stream, head) and layer; thread k counts
-  // this workgroup's k-th unit once every partial store of the workgroup is done
+  // completion counters: one per (stream, head) and layer, counting the
+  // segments; taken once every partial store of the workgroup is done
   __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0): stores acknowledged
   __syncthreads();
-  {
-    const int u = wg + threadIdx.x * G;
-    if (threadIdx.x < ATT_UNITS_MAX && u < nunits) {
+  if (threadIdx.x == 0) {
+    for (int u = ub; u < ue;) {
       int b, c, h;
       sl.unit(u, b, c, h);
       (void)add_rlx(&s.att_cnt[((l * SB_MAX + b) * NH + h) * 32], 1u);
+      u += sl.chunks(b) - c;
     }
   }
   trace_mark(a, sy, 5);
   // Merges: (stream, head) i is merged by workgroup i * G / (B * NH) -- one
-  // per workgroup, all in parallel -- once its counter shows every chunk
+  // per workgroup, all in parallel -- once its counter shows every segment
   // stored. The merging workgroup resets the counter for the next round.
   // Streams with an empty context attend to the block only.
   const int nbh = a.B * NH;
   for (int i = (wg * nbh + G - 1) / G; i < nbh && (i * G) / nbh == wg; ++i) {
     const int b = i / NH, h = i % NH, n = sl.vis(b);
+    const int u0 = n > 0 ? sl.first_unit(b, h) : 0;
     if (n > 0) {
       if (threadIdx.x == 0) {
         auto cnt = &s.att_cnt[((l * SB_MAX + b) * NH + h) * 32];
-        const unsigned need = (unsigned)((n + ATT_CH - 1) / ATT_CH);
+        const unsigned need = (unsigned)sl.segments(u0, sl.chunks(b), G);
         const unsigned long long t0 = wall_clock64();
         for (unsigned it = 1; ld_rlx(cnt) < need; ++it) {
           if ((it & 63) == 0 && wall_clock64() - t0 > 20000000ull) {  // 0.2 s
@@ -1071,7 +1297,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
       }
       lds_sync();
     }
-    attn_merge(a, l, b, h, n, red);
+    attn_merge(a, l, b, h, n, u0, U, (lds_f)g_att_small);
   }
   trace_mark(a, sy, 6);
   trace_mark(a, sy, 4);
@@ -1300,7 +1526,7 @@ __device__ void run_phase(Args& a, int p, lds_f red, SyncState sy, bool sync) {
     case PH_SA: return ph_sa(a, l, red, sy, sync);
     case PH_SU: return ph_su(a, l, red, sy, sync);
     case PH_QKV: return ph_qkv(a, l, red, sy, sync);
-    case PH_ATTN: return ph_attn(a, l, red, sy, sync);
+    case PH_ATTN: return ph_attn(a, l, sy, sync);
     case PH_O:
       return ph_resid<5>(a, L.wo, s.o[l], H, xs_in(l), xs_o(l), L.ffn_norm, red, sy, sync);
     case PH_GU: return ph_gu(a, l, red, sy, sync);
@@ -1332,26 +1558,32 @@ __host__ __device__ int small_phase_id(int nl, int i) {
 }
 
 constexpr int RED_FLOATS = 8192 + 32 + 32 + 32;   // partials, inv rms, argmax candidates, flag
+static_assert(sizeof(g_att_ring) >= RED_FLOATS * sizeof(float), "reduction area");
+
+// The reduction area of the phases other than attention (which has its own).
+__device__ __forceinline__ lds_f red_area() { return (lds_f)&g_att_ring[0][0][0]; }
 
 // The argument block lives in device memory (read through scalar loads), so
 // no per-lane copy of it is made when it is passed down to the phases.
 __global__ __launch_bounds__(SMALL_WG) void k_small_phase(const SmallArgs* __restrict__ ap, int p,
                                                          int slot) {
-  __shared__ __attribute__((aligned(16))) float red[RED_FLOATS];
+  const unsigned long long t_entry = wall_clock64();
   const SyncState sy{0u, slot};
   Args& a = *(Args*)ap;
-  run_phase(a, p, (lds_f)red, sy, false);
+  run_phase(a, p, red_area(), sy, false);
+  // stage 0 (the barrier arrival of the persistent kernel) holds the entry time
+  if (a.trace && threadIdx.x == 0 && slot < a.trace_phases)
+    a.trace[((size_t)slot * gridDim.x + blockIdx.x) * 8] = t_entry;
   trace_mark(a, sy, 7);
 }
 
 __global__ __launch_bounds__(SMALL_WG) void k_small_mega(const SmallArgs* __restrict__ ap,
                                                         unsigned epoch0) {
-  __shared__ __attribute__((aligned(16))) float red[RED_FLOATS];
   Args& a = *(Args*)ap;
   const int np = small_phase_count(a.nl);
   for (int i = 0; i < np; ++i) {
     const SyncState sy{epoch0, i};
-    run_phase(a, small_phase_id(a.nl, i), (lds_f)red, sy, i > 0);
+    run_phase(a, small_phase_id(a.nl, i), red_area(), sy, i > 0);
     trace_mark(a, sy, 7);
   }
 }

@@ -138,6 +138,24 @@ def test_small_path_adapters_gains_and_edges(hC, path):
     compare(lg, ids, ref, rid, hC.oracle.vocab, f"model C small path {path}")
 
 
+@pytest.mark.parametrize("path", [2, 3])
+@pytest.mark.parametrize("lens", [[700], [1, 300], [0, 0, 5, 128], [0, 0]])
+def test_small_path_fewer_chunks_than_workgroups(hC, path, lens):
+    """Short contexts: fewer 128-row chunks in the round than workgroups, so
+    some workgroups get no attention work and every chunk is its own segment
+    (and no context at all: block-only attention)."""
+    cfg = dict(name="short", streams=len(lens), lens=("const", 0), model="C", ingest=0)
+    inp = hC.inputs(cfg, base=37, lens_override=lens)
+    hC.drafter.debug_set_path(path)
+    try:
+        lg, ids = hC.run(inp)
+        assert hC.drafter.last_path() == path
+    finally:
+        hC.drafter.debug_set_path(0)
+    ref, rid = oracle.oracle_round(hC.oracle, synth.to_numpy_inputs(inp))
+    compare(lg, ids, ref, rid, hC.oracle.vocab, f"short contexts {lens} path {path}")
+
+
 def test_small_paths_agree_bitwise_and_are_deterministic(hC):
     cfg = dict(name="agree", streams=3, lens=("uniform", 1, 3000), model="C", ingest=0)
     inp = hC.inputs(cfg, base=29)
@@ -151,6 +169,11 @@ def test_small_paths_agree_bitwise_and_are_deterministic(hC):
 
 
 def test_small_path_stream_alone_equals_stream_in_batch(hC):
+    # The small-batch attention cuts each (stream, head)'s chunks where the
+    # workgroups' shares of the whole batch's work end, so a stream's softmax
+    # partials are summed in a batch-dependent order: alone and in a batch
+    # agree to fp32 reassociation, and the ids wherever the top two logits are
+    # not within that noise.
     cfg = dict(name="inv-small", streams=4, lens=("uniform", 10, 2048), model="C", ingest=0)
     inp = hC.inputs(cfg, base=31)
     hC.drafter.debug_set_path(0)
@@ -162,7 +185,10 @@ def test_small_path_stream_alone_equals_stream_in_batch(hC):
         one["v"] = [t[b:b + 1] for t in inp["v"]]
         one["streams"] = 1
         alone, ia = hC.run(one)
-        assert np.array_equal(alone[0], batch[b]) and np.array_equal(ia[0], ib[b])
+        np.testing.assert_allclose(alone[0], batch[b], rtol=1e-4, atol=1e-4)
+        top2 = np.sort(batch[b], axis=1)[:, -2:]
+        clear = (top2[:, 1] - top2[:, 0]) > 1e-3
+        assert np.array_equal(ia[0][clear], ib[b][clear])
 
 
 def test_round_parity_adapters_and_gains_active(hC):
