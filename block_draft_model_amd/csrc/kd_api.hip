@@ -338,8 +338,9 @@ kd_status kd_create(const kd_config* cfg, void* hip_stream, kd_ctx** out) {
   hipDeviceProp_t prop;
   const bool have_prop = hipGetDeviceProperties(&prop, c->device) == hipSuccess;
   c->G = have_prop ? std::min(prop.multiProcessorCount, kd::MAX_G) : 128;
-  // the small-batch paths serve any window; they need their buffers below
-  c->small_ok = true;
+  // the small-batch paths serve any window; their attention merges one
+  // (stream, head) per workgroup, so the grid must cover every pair
+  c->small_ok = c->G >= kd::SB_MAX * kd::NH;
   if (ok && c->small_ok) {
     // chunk partials of one (stream, head) must not share a 128-byte line with
     // another's (different workgroups merge them): whole groups of 8 chunks
@@ -354,6 +355,7 @@ kd_status kd_create(const kd_config* cfg, void* hip_stream, kd_ctx** out) {
       ok = hipMemset(c->small.bar, 0, 20 * 32 * sizeof(unsigned)) == hipSuccess &&
            hipMemset(c->small.att_cnt, 0, kd::NL * kd::SB_MAX * kd::NH * 32 * sizeof(unsigned)) ==
                hipSuccess &&
+           hipMemset(c->small.down_cnt, 0, kd::NL * (kd::HT / 2) * 32 * sizeof(unsigned)) == hipSuccess &&
            hipDeviceSynchronize() == hipSuccess;
     }
   }

@@ -14,6 +14,7 @@ constexpr int HT = H / 16;     // 160 column tiles of a hidden vector
 constexpr int SMALL_WG = 512;  // 8 waves per workgroup
 constexpr int HEAD_NT = 2;     // vocab tiles per head unit
 constexpr int MAX_G = 256;     // workgroups (one per CU); barrier tree is 16 x 16
+constexpr int DOWN_KS = 3;     // the down projection's inputs split in thirds across workgroups
 
 // Stage index of the residual stream: the layer input, after O, after down.
 __host__ __device__ inline int xs_in(int l) { return l == 0 ? 0 : 3 * l; }
@@ -46,6 +47,8 @@ struct SmallBufsT {
   P<unsigned> bar;             // control words, 32 u32 apart: [0..15] arrival counters of
                                // the 16-workgroup groups, [18] error, [19] head counter
   P<unsigned> att_cnt;         // [NL][SB][NH] chunk counters, one 128-byte line each
+  P<float> dpart[NL];          // [DOWN_KS][SR][H] down projection partials over thirds of FF
+  P<unsigned> down_cnt;        // [NL][HT / 2] counters of the partials, one 128-byte line each
 };
 
 template <template <class> class P>

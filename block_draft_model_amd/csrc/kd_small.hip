@@ -757,12 +757,60 @@ struct StreamLens {
   }
 };
 
-// Merge of the partials of one (stream, head) with the block's own keys (row
-// j sees block rows 0..j); thread (j, d). The partials are those of the
-// segments of its chunks that the workgroups' ranges cut out, each stored at
-// the slot of its first chunk; u0 is the pair's first unit and U all units.
+// The block's own part of the attention of one (stream, head) for thread
+// (j, d): scores s[j][i] = q_j . k_i of block rows i <= j (log2 units, -inf
+// for i > j) and the values v_i[d]. It needs no context: the workgroup that
+// merges the pair loads the block rows (BlockRows::load) before its own
+// chunks and finishes the part (attn_block) after them.
+struct BlockPart {
+  float s0, s1, s2, s3;
+  float v0, v1, v2, v3;
+};
+struct BlockRows {
+  float q, k0, k1, k2, k3;     // wave w: query row w/2 and the 4 key rows, dim 64 (w%2) + lane
+  float v0, v1, v2, v3;        // thread (j, d): the 4 value rows at dim d
+  __device__ __forceinline__ void load(Args& a, int l, int b, int h) {
+    auto& s = a.s;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int dd = threadIdx.x & 127;
+    const int jw = wave >> 1, dw = 64 * (wave & 1) + lane;
+    const size_t hb = (size_t)b * 4 * H + h * DH;
+    q = s.q[l][hb + jw * H + dw];
+    k0 = s.k[l][hb + 0 * H + dw];
+    k1 = s.k[l][hb + 1 * H + dw];
+    k2 = s.k[l][hb + 2 * H + dw];
+    k3 = s.k[l][hb + 3 * H + dw];
+    v0 = s.v[l][hb + 0 * H + dd];
+    v1 = s.v[l][hb + 1 * H + dd];
+    v2 = s.v[l][hb + 2 * H + dd];
+    v3 = s.v[l][hb + 3 * H + dd];
+  }
+};
+__device__ __attribute__((noinline, not_tail_called)) BlockPart attn_block(BlockRows br, lds_f red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float qs = 0.08838834764831845f * 1.4426950408889634f;  // 1/sqrt(128) * log2(e)
+  const int j = threadIdx.x >> 7;
+  const float kb4[4] = {br.k0, br.k1, br.k2, br.k3};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float p = wave_sum(br.q * kb4[i]);
+    if (lane == 0) red[wave * 4 + i] = p;
+  }
+  lds_sync();
+  float sb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    sb[i] = i <= j ? (red[(2 * j) * 4 + i] + red[(2 * j + 1) * 4 + i]) * qs : -__builtin_inff();
+  lds_sync();
+  return BlockPart{sb[0], sb[1], sb[2], sb[3], br.v0, br.v1, br.v2, br.v3};
+}
+
+// Merge of the partials of one (stream, head) with the block's part; thread
+// (j, d). The partials are those of the segments of its chunks that the
+// workgroups' ranges cut out, each stored at the slot of its first chunk; u0
+// is the pair's first unit and U all units.
 __device__ __attribute__((noinline, not_tail_called)) void attn_merge(Args& a_, int l_, int b_, int h_, int n_,
-                                                     int u0_, int U_, lds_f red) {
+                                                     int u0_, int U_, BlockPart bp) {
   const auto l = uni(l_);
   const auto b = uni(b_);
   const auto h = uni(h_);
@@ -772,9 +820,7 @@ __device__ __attribute__((noinline, not_tail_called)) void attn_merge(Args& a_, 
   Args& a = uni(a_);
   auto& s = a.s;
   const int G = gridDim.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nch = a.nch;
-  const float qs = 0.08838834764831845f * 1.4426950408889634f;  // 1/sqrt(128) * log2(e)
   const int nc = (n + ATT_CH - 1) / ATT_CH;
   // segments: with at least as many units as workgroups every range is
   // non-empty, and the pair's segments are those of workgroups owner(u0) ..
@@ -788,23 +834,14 @@ __device__ __attribute__((noinline, not_tail_called)) void attn_merge(Args& a_, 
   }
   auto seg_chunk = [&](int k) { return one_each ? k : max(((w0 + k) * U) / G, u0) - u0; };
   const int j = threadIdx.x >> 7, dd = threadIdx.x & 127;
-  // block queries, keys and values first, then every segment partial: the
-  // loads go out together
-  const int jw = wave >> 1, dw = 64 * (wave & 1) + lane;
-  const float qv = s.q[l][(b * 4 + jw) * H + h * DH + dw];
-  float kb4[4], vv[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    kb4[i] = s.k[l][(b * 4 + i) * H + h * DH + dw];
-    vv[i] = s.v[l][(b * 4 + i) * H + h * DH + dd];
-  }
   constexpr int MAXS = 16;
   float pm[MAXS], pl[MAXS], po[MAXS];
   const size_t base = (size_t)(b * NH + h) * nch;
   auto am = s.am[l] + base * 4 + j;
   auto al = s.al[l] + base * 4 + j;
   auto ao = s.ao[l] + (base * 4 + j) * DH + dd;
-  // segments past the last one re-read it and are masked afterwards
+  // every load issued together: segments past the last one re-read it and
+  // are masked afterwards
   const int klast = max(nseg - 1, 0);
 #pragma unroll
   for (int k = 0; k < MAXS; ++k) {
@@ -830,22 +867,12 @@ __device__ __attribute__((noinline, not_tail_called)) void attn_merge(Args& a_, 
     po[0] = po[0] * f0 + ao[(size_t)cc * 4 * DH] * f1;
     pm[0] = mn;
   }
-  // block scores s[j][i] = q_j . k_i: wave w covers row w/2, dims 64*(w%2)..
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float p = wave_sum(qv * kb4[i]);
-    if (lane == 0) red[wave * 4 + i] = p;
-  }
-  lds_sync();
-  float sb[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) sb[i] = (red[(2 * j) * 4 + i] + red[(2 * j + 1) * 4 + i]) * qs;
+  const float sb[4] = {bp.s0, bp.s1, bp.s2, bp.s3}, vv[4] = {bp.v0, bp.v1, bp.v2, bp.v3};
   float M = -__builtin_inff();
 #pragma unroll
   for (int k = 0; k < MAXS; ++k) M = fmaxf(M, pm[k]);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    if (i <= j) M = fmaxf(M, sb[i]);
+  for (int i = 0; i < 4; ++i) M = fmaxf(M, sb[i]);
   float Ls = 0.f, O = 0.f;
 #pragma unroll
   for (int k = 0; k < MAXS; ++k) {
@@ -863,7 +890,6 @@ __device__ __attribute__((noinline, not_tail_called)) void attn_merge(Args& a_, 
       O += f * vv[i];
     }
   st_wt(&s.o[l][(b * 4 + j) * H + h * DH + dd], O / Ls);
-  lds_sync();
 }
 
 // LDS of the attention phase. Keys, values and queries arrive by global-to-LDS
@@ -1076,6 +1102,17 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
   };
   const unsigned ring0 = (unsigned)(uintptr_t)&g_att_ring[0][0][0];
 
+  // the (stream, head) this workgroup merges, if any: (stream, head) i is
+  // merged by workgroup i * G / (B * NH), at most one per workgroup while
+  // B * NH <= G
+  const int nbh = a.B * NH;
+  const int mi = (wg * nbh + G - 1) / G;
+  const bool merges = mi < nbh && (mi * G) / nbh == wg;
+  // the block rows of that pair are loaded before the copies (once the
+  // previous phase has written them) and used after the workgroup's chunks
+  BlockRows br{};
+  if (merges && !sync) br.load(a, l, mi / NH, mi % NH);
+
   if (sync) {
     grid_arrive(a, sy);
     if (is_poll_wave()) grid_poll(a, sy);
@@ -1090,6 +1127,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
   }
   if (sync) {
     lds_sync();
+    if (merges) br.load(a, l, mi / NH, mi % NH);
     if (ub < ue) copy_q(ub, 0);
     if (ub + 1 < ue) copy_q(ub + 1, 1);
   }
@@ -1273,14 +1311,14 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
     }
   }
   trace_mark(a, sy, 5);
-  // Merges: (stream, head) i is merged by workgroup i * G / (B * NH) -- one
-  // per workgroup, all in parallel -- once its counter shows every segment
-  // stored. The merging workgroup resets the counter for the next round.
-  // Streams with an empty context attend to the block only.
-  const int nbh = a.B * NH;
-  for (int i = (wg * nbh + G - 1) / G; i < nbh && (i * G) / nbh == wg; ++i) {
-    const int b = i / NH, h = i % NH, n = sl.vis(b);
+  // Merge: one (stream, head) per workgroup, all in parallel, once its
+  // counter shows every segment stored. The merging workgroup resets the
+  // counter for the next round. Streams with an empty context attend to the
+  // block only.
+  if (merges) {
+    const int b = mi / NH, h = mi % NH, n = sl.vis(b);
     const int u0 = n > 0 ? sl.first_unit(b, h) : 0;
+    const BlockPart bp = attn_block(br, (lds_f)g_att_small);
     if (n > 0) {
       if (threadIdx.x == 0) {
         auto cnt = &s.att_cnt[((l * SB_MAX + b) * NH + h) * 32];
@@ -1297,7 +1335,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
       }
       lds_sync();
     }
-    attn_merge(a, l, b, h, n, u0, U, (lds_f)g_att_small);
+    attn_merge(a, l, b, h, n, u0, U, bp);
   }
   trace_mark(a, sy, 6);
   trace_mark(a, sy, 4);
@@ -1331,6 +1369,68 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_resid(Args& a_, Ma
                                   put_x(s, xout, gain, m, col, u, n, x, ok);
                                 });
     first = false;
+  }
+  if (first) grid_sync(a, sy);
+}
+
+// x_{out} = x_{in} + W_down h, with the 6144 inputs split in DOWN_KS thirds
+// across workgroups: unit u covers the tile pair u / DOWN_KS (32 output
+// columns) over third u % DOWN_KS, so that 240 units spread over the grid and
+// each loads a third of the activations. Every unit stores its partial; the
+// last of a pair's units to finish (counter) adds the thirds in a fixed order
+// and runs the residual epilogue.
+__device__ __attribute__((noinline, not_tail_called)) void ph_down(Args& a_, int l_, lds_f red, SyncState sy,
+                                                  bool sync) {
+  const auto l = uni(l_);
+  Args& a = uni(a_);
+  const int G = gridDim.x, wg = blockIdx.x;
+  auto& s = a.s;
+  auto& L = a.d.layer[l];
+  const int R = a.R;
+  const int xin = xs_o(l), xout = xs_d(l);
+  const auto gain = gain_after_down(a, l);
+  constexpr int NT = 2, KBS = FF / 64 / DOWN_KS / 8;
+  static_assert(KBS * 8 * DOWN_KS * 64 == FF, "down split");
+  constexpr int NU = HT / NT * DOWN_KS;
+  auto part = s.dpart[l];
+  KD_LDS unsigned* s_last = reinterpret_cast<KD_LDS unsigned*>(red + 8192 + 64);
+  bool first = sync;
+  for (int u = wg; u < NU; u += G) {
+    const int tp = u / DOWN_KS, p = u - tp * DOWN_KS;
+    const ASrc A{s.h[l], FF, 0, nullptr, 0, R};
+    // thread (i, m, n) = (tid / 256, (tid / 16) % 16, tid % 16) holds one
+    // output of the pair after the epilogue's reduction over the 8 waves
+    float mine = 0.f;
+    gemm_unit<NT, KBS, 8, false>(a, sy, first, L.down, tp * NT, NT, p * KBS * 8, A, red, no_rms(),
+                                 [&](int i, int m, int n, float v) {
+                                   mine = v;
+                                   if (m < R) st_wt(&part[((size_t)p * SR_MAX + m) * H + (tp * NT + i) * 16 + n], v);
+                                 });
+    first = false;
+    __builtin_amdgcn_s_waitcnt(0);  // the partial stores are acknowledged
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      auto cnt = &s.down_cnt[(l * (HT / 2) + tp) * 32];
+      const bool last = add_rlx(cnt, 1u) == (unsigned)(DOWN_KS - 1);
+      if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *s_last = last ? 1u : 0u;
+    }
+    lds_sync();
+    if (*s_last) {
+      const int it = threadIdx.x, i = it >> 8, m = (it >> 4) & 15, n = it & 15;
+      const int tile = tp * NT + i, col = tile * 16 + n;
+      const bool ok = m < R;
+      float pv[DOWN_KS];
+#pragma unroll
+      for (int q = 0; q < DOWN_KS; ++q)
+        pv[q] = q == p ? mine : (ok ? part[((size_t)q * SR_MAX + m) * H + col] : 0.f);
+      float v = pv[0];
+#pragma unroll
+      for (int q = 1; q < DOWN_KS; ++q) v += pv[q];
+      const float x = ok ? s.x[xin][m * H + col] + v : 0.f;
+      put_x(s, xout, gain, m, col, tile, n, x, ok);
+    }
+    lds_sync();
   }
   if (first) grid_sync(a, sy);
 }
@@ -1375,7 +1475,8 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_head(Args& a_, lds
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int R = a.R, VT = d.VT, VD = d.VD;
   constexpr int KG = H / 128;
-  const int kg0 = (KG * wave) >> 3, kg1 = (KG * (wave + 1)) >> 3, ng = kg1 - kg0;  // 2 or 3
+  const int wave_s = uni(wave);
+  const int kg0 = (KG * wave_s) >> 3, kg1 = (KG * (wave_s + 1)) >> 3, ng = kg1 - kg0;  // 2 or 3
   const int src = a.nl == 0 ? 0 : xs_d(a.nl - 1);
   const int nunits = (VT + HEAD_NT - 1) / HEAD_NT;
   lds_f inv = red + 8192;
@@ -1385,65 +1486,70 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_head(Args& a_, lds
   // unit u < nunits: tiles past the last repeat it (their columns are past
   // the vocabulary and masked); a wave with 2 input groups repeats its last
   // group in slot 2 and skips it
+  // (block addresses are wave-uniform, so they stay in scalar registers and
+  // only the lane offset is a vector one)
   auto load_unit = [&](int u, u32x4 (&q)[HEAD_NT][3], uint32_t (&sv)[HEAD_NT][3]) {
 #pragma unroll
     for (int i = 0; i < HEAD_NT; ++i)
 #pragma unroll
       for (int gg = 0; gg < 3; ++gg) {
         const int vt = min(u * HEAD_NT + i, VT - 1);
-        const size_t idx = ((size_t)vt * KG + kg0 + min(gg, ng - 1)) * 64 + lane;
-        q[i][gg] = *reinterpret_cast<gptr<const u32x4>>(d.hq + idx * 16);
-        sv[i][gg] = *reinterpret_cast<gptr<const uint32_t>>(d.hs + idx * 4);
+        const size_t blk = (size_t)vt * KG + kg0 + min(gg, ng - 1);
+        q[i][gg] = *(uni(reinterpret_cast<gptr<const u32x4>>(d.hq + blk * 1024)) + lane);
+        sv[i][gg] = *(uni(reinterpret_cast<gptr<const uint32_t>>(d.hs + blk * 256)) + lane);
       }
   };
 
   if (sync) {
     grid_arrive(a, sy);
     if (is_poll_wave()) grid_poll(a, sy);
+    lds_sync();
   }
-  u32x4 q[HEAD_NT][3];
-  uint32_t sv[HEAD_NT][3];
-  if (wg < nunits) load_unit(wg, q, sv);
-  if (sync) lds_sync();
   trace_mark(a, sy, 2);
   if (threadIdx.x < SR_MAX) best[threadIdx.x] = 0ull;
   RmsRows rms{s.ssq[src], R, 0, a.eps, inv, {}};
+  // the activations (written by the previous phase) are loaded before the
+  // first unit's codes, so that they land first (a wave's loads complete in
+  // issue order)
   rms.issue();
+  const int ar = min(lane & 15, R - 1);
+  f32x4 raw[3][4][2];
+#pragma unroll
+  for (int gg = 0; gg < 3; ++gg)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      // rows past R repeat row R-1 (their logits are discarded); slot 2 of a
+      // wave with 2 input groups repeats group 1 and is skipped
+      const int c0 = (kg0 + min(gg, ng - 1)) * 128 + t * 32 + 8 * (lane >> 4);
+      auto p = s.xg[src] + ar * H + c0;
+      raw[gg][t][0] = *reinterpret_cast<gptr<const f32x4>>(p);
+      raw[gg][t][1] = *reinterpret_cast<gptr<const f32x4>>(p + 4);
+    }
+  // two register sets of codes and scales alternate (an unrolled pair of
+  // units, so that no copy between them makes the compiler wait for loads in
+  // flight); units past the last repeat it and are skipped
+  u32x4 qa[HEAD_NT][3], qb[HEAD_NT][3];
+  uint32_t sa[HEAD_NT][3], sb[HEAD_NT][3];
+  const int ulast = max(nunits - 1, 0);
+  load_unit(min(wg, ulast), qa, sa);
   // A operand (g_o * x, hi/lo f16) for this wave's inputs, kept for all units
   f16x8 ah[3][4], al[3][4];
-  {
-    // rows past R repeat row R-1 (their logits are discarded); slot 2 of a
-    // wave with 2 input groups repeats group 1 and is skipped
-    const int r = min(lane & 15, R - 1);
-    f32x4 raw[3][4][2];
 #pragma unroll
-    for (int gg = 0; gg < 3; ++gg)
+  for (int gg = 0; gg < 3; ++gg)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int c0 = (kg0 + min(gg, ng - 1)) * 128 + t * 32 + 8 * (lane >> 4);
-        auto p = s.xg[src] + r * H + c0;
-        raw[gg][t][0] = *reinterpret_cast<gptr<const f32x4>>(p);
-        raw[gg][t][1] = *reinterpret_cast<gptr<const f32x4>>(p + 4);
+    for (int t = 0; t < 4; ++t) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = raw[gg][t][0][e];
+        v[4 + e] = raw[gg][t][1][e];
       }
-#pragma unroll
-    for (int gg = 0; gg < 3; ++gg)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[e] = raw[gg][t][0][e];
-          v[4 + e] = raw[gg][t][1][e];
-        }
-        split_f16(v, ah[gg][t], al[gg][t]);
-      }
-  }
+      split_f16(v, ah[gg][t], al[gg][t]);
+    }
   rms.finish();
   trace_mark(a, sy, 3);
-  for (int u = wg; u < nunits; u += G) {
-    u32x4 qn[HEAD_NT][3];
-    uint32_t svn[HEAD_NT][3];
-    if (u + G < nunits) load_unit(u + G, qn, svn);
+  auto unit_body = [&](int u, const u32x4 (&q)[HEAD_NT][3], const uint32_t (&sv)[HEAD_NT][3])
+                       __attribute__((always_inline)) {
     f32x4 acc[HEAD_NT];
 #pragma unroll
     for (int i = 0; i < HEAD_NT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1476,14 +1582,14 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_head(Args& a_, lds
       if (n == 0 && key)
         __hip_atomic_fetch_max(&best[m], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     });
-#pragma unroll
-    for (int i = 0; i < HEAD_NT; ++i)
-#pragma unroll
-      for (int gg = 0; gg < 3; ++gg) {
-        q[i][gg] = qn[i][gg];
-        sv[i][gg] = svn[i][gg];
-      }
     if (u == wg) trace_mark(a, sy, 5);
+  };
+  for (int u = wg; u < nunits; u += 2 * G) {
+    load_unit(min(u + G, ulast), qb, sb);
+    unit_body(u, qa, sa);
+    if (u + G >= nunits) break;
+    load_unit(min(u + 2 * G, ulast), qa, sa);
+    unit_body(u + G, qb, sb);
   }
   lds_sync();
   if (threadIdx.x < SR_MAX) st_wt64(&s.cand[wg * SR_MAX + threadIdx.x], best[threadIdx.x]);
@@ -1530,9 +1636,7 @@ __device__ void run_phase(Args& a, int p, lds_f red, SyncState sy, bool sync) {
     case PH_O:
       return ph_resid<5>(a, L.wo, s.o[l], H, xs_in(l), xs_o(l), L.ffn_norm, red, sy, sync);
     case PH_GU: return ph_gu(a, l, red, sy, sync);
-    case PH_DOWN:
-      return ph_resid<12>(a, L.down, s.h[l], FF, xs_o(l), xs_d(l), gain_after_down(a, l), red,
-                          sy, sync);
+    case PH_DOWN: return ph_down(a, l, red, sy, sync);
   }
 }
 
@@ -1645,6 +1749,8 @@ static size_t small_layout(char* base, int nch, SmallBufs* s) {
   carve(base, off, (size_t)MAX_G * SR_MAX * sizeof(unsigned long long), (void**)&o->cand);
   carve(base, off, (size_t)20 * 32 * sizeof(unsigned), (void**)&o->bar);
   carve(base, off, (size_t)NL * SB_MAX * NH * 32 * sizeof(unsigned), (void**)&o->att_cnt);
+  for (int l = 0; l < NL; ++l) carve(base, off, (size_t)DOWN_KS * SR_MAX * H * F, (void**)&o->dpart[l]);
+  carve(base, off, (size_t)NL * (HT / 2) * 32 * sizeof(unsigned), (void**)&o->down_cnt);
   return (off + 255) & ~(size_t)255;
 }
 
