@@ -29,6 +29,9 @@ def command(out: str = LIB) -> list[str]:
     return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
             # packed fp32 ops stay off: hipcc would otherwise form v_pk_* fp32 ops
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # the first kernel arguments arrive in scalar registers (the kernel
+            # keeps a loading prologue for dispatchers that do not preload)
+            "-mllvm", "-amdgpu-kernarg-preload-count=4",
             "-Wall", "-Wno-unused-function",
             "-I", os.path.join(ROOT, "include"), *SOURCES, "-o", out]
 

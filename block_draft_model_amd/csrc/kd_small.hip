@@ -482,8 +482,16 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_pre0(Args& a_, lds
       st_wt(&s.rope[t * 2 + 1], (float)sin(ang));
     }
   }
-  const int n_fuse = HT, n_fce = HT, n_pb = RK / 16;
-  for (int u = wg; u < n_fuse + n_fce + n_pb; u += G) {
+  // units: the fuse tiles (120 input blocks each), then the fc and
+  // predecessor tiles (40 each). With enough workgroups every fuse tile gets
+  // its own and the other workgroups share the light tiles; otherwise they
+  // are dealt in turn.
+  const int n_fuse = HT, n_fce = HT, n_pb = RK / 16, n_all = n_fuse + n_fce + n_pb;
+  const bool split = G > n_fuse;
+  const int u_first = split ? (wg < n_fuse ? wg : n_fuse + (wg - n_fuse)) : wg;
+  const int u_end = split && wg < n_fuse ? wg + 1 : n_all;
+  const int u_step = split ? G - n_fuse : G;
+  for (int u = u_first; u < u_end; u += u_step) {
     if (u < n_fuse) {
       const ASrc A{a.taps, NTAP * H, 0, nullptr, 0, B};
       gemm_unit<1, 15, 8, true>(a, sy, false, d.fuse, u, 1, 0, A, red, no_rms(),
