@@ -230,6 +230,70 @@ __device__ __forceinline__ void grid_sync(Args& a, SyncState sy) {
   grid_wait(a, sy);
 }
 
+// LDS of the attention phase. Keys, values and queries arrive by global-to-LDS
+// copies into a two-slot ring (slot = parity of the workgroup's unit count):
+// per slot, 8 blocks of 1 KB per wave for its 16 keys (4 key blocks, 4 value
+// blocks; a copy puts lane l's 16 bytes at l * 16, and the same lane reads
+// them back), then 2 blocks of queries ([4][128] fp32, copied by wave 0).
+// The ring is also the reduction area of every other phase.
+constexpr int ATT_WAVE_BLOCKS = 8;
+constexpr int ATT_SLOT_BLOCKS = 8 * ATT_WAVE_BLOCKS + 2;
+constexpr unsigned ATT_SLOT_BYTES = ATT_SLOT_BLOCKS * 1024u;
+__shared__ __attribute__((aligned(16))) u32x4 g_att_ring[2][ATT_SLOT_BLOCKS][64];
+// per-wave outputs [8][4][128], softmax max and sum [8][4] each, probabilities [8][4][16]
+constexpr int ATT_SMALL = 8 * 4 * DH + 32 + 32 + 8 * 4 * 16;
+__shared__ __attribute__((aligned(16))) float g_att_small[ATT_SMALL];
+
+// Waits until at most N vector memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void att_wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+__device__ __forceinline__ void att_wait_vm(int n) {
+  if (n >= 10) att_wait_vm<10>();
+  else if (n >= 8) att_wait_vm<8>();
+  else if (n >= 2) att_wait_vm<2>();
+  else att_wait_vm<0>();
+}
+
+// ---------------------------------------------------------------------------
+// Cache warming by idle workgroups
+// ---------------------------------------------------------------------------
+// Unit u of a phase with at most G units runs on workgroup u, which the
+// dispatcher places on XCD u % 8 (workgroups are dealt to the 8 XCDs in turn).
+// Workgroups idle in the current phase read the data of units of a later
+// phase on the XCD that will run them, so that those loads find the lines in
+// that XCD's L2 or the memory-side cache. The reads are global-to-LDS copies
+// of one dword per 128-byte line into a scratch area of LDS: they hold no
+// registers and nothing waits for them until the end.
+__device__ __forceinline__ void touch(gptr<const uint8_t> p, size_t bytes) {
+  KD_LDS void* dump = (KD_LDS void*)(KD_LDS float*)g_att_small;
+  for (size_t off = (size_t)threadIdx.x * 128; off < bytes; off += (size_t)SMALL_WG * 128)
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(p + off), dump, 4, 0, 0);
+}
+// The weights and scales of tiles [t0, t0 + ntile), input blocks [kb0, kb0 + nkb).
+__device__ __forceinline__ void touch_tiles(Mat& W, int t0, int ntile, int kb0, int nkb) {
+  const int KB = W.K >> 6;
+  for (int t = t0; t < t0 + ntile; ++t) {
+    touch(W.w + ((size_t)t * KB + kb0) * 1024, (size_t)nkb * 1024);
+    touch(reinterpret_cast<gptr<const uint8_t>>(W.s + ((size_t)t * KB + kb0) * 16), (size_t)nkb * 64);
+  }
+}
+// Idle workgroups [i0, G): workgroup w on XCD x = w % 8 takes the units
+// u = x (mod 8) of the later phase in turn with the other idle workgroups of
+// that XCD; touch_unit(u) reads what unit u will load.
+template <class F>
+__device__ __forceinline__ void warm(int i0, int nunits, F&& touch_unit) {
+  const int w = blockIdx.x, G = gridDim.x;
+  if (w < i0) return;
+  const int x = w & 7, f = i0 + ((x - i0) & 7);
+  const int k = (w - f) >> 3, nk = (G - f + 7) >> 3;
+  for (int u = x + 8 * k; u < nunits; u += 8 * nk) touch_unit(u);
+}
+// Every copy has landed (before the workgroup ends, while its LDS is still its own).
+__device__ __forceinline__ void warm_done() { att_wait_vm<0>(); }
+
 // ---------------------------------------------------------------------------
 // Projection units: NT consecutive 16-row weight tiles; wave w (< AW) takes
 // the 64-input blocks kb0 + w*KBS .. + KBS.
@@ -594,6 +658,13 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_sa(Args& a_, int l
     first = false;
   }
   if (first) grid_sync(a, sy);
+  // the workgroups without a tile warm the next two phases' weights: the
+  // spine U (one tile per unit) and q|k|v (two); not in the persistent kernel
+  if (!sync) {
+    warm(RK / 16, HT, [&](int u) { touch_tiles(L.su, u, 1, 0, RK / 64); });
+    warm(RK / 16, QKV / 16 / 2, [&](int u) { touch_tiles(L.qkv, 2 * u, 2, 0, H / 64); });
+    warm_done();
+  }
 }
 
 // Spine U: x_j (j = 1..3) += U_s ss; row 0 copied into the new stage.
@@ -900,33 +971,6 @@ __device__ __attribute__((noinline, not_tail_called)) void attn_merge(Args& a_, 
   st_wt(&s.o[l][(b * 4 + j) * H + h * DH + dd], O / Ls);
 }
 
-// LDS of the attention phase. Keys, values and queries arrive by global-to-LDS
-// copies into a two-slot ring (slot = parity of the workgroup's unit count):
-// per slot, 8 blocks of 1 KB per wave for its 16 keys (4 key blocks, 4 value
-// blocks; a copy puts lane l's 16 bytes at l * 16, and the same lane reads
-// them back), then 2 blocks of queries ([4][128] fp32, copied by wave 0).
-// The ring is also the reduction area of every other phase.
-constexpr int ATT_WAVE_BLOCKS = 8;
-constexpr int ATT_SLOT_BLOCKS = 8 * ATT_WAVE_BLOCKS + 2;
-constexpr unsigned ATT_SLOT_BYTES = ATT_SLOT_BLOCKS * 1024u;
-__shared__ __attribute__((aligned(16))) u32x4 g_att_ring[2][ATT_SLOT_BLOCKS][64];
-// per-wave outputs [8][4][128], softmax max and sum [8][4] each, probabilities [8][4][16]
-constexpr int ATT_SMALL = 8 * 4 * DH + 32 + 32 + 8 * 4 * 16;
-__shared__ __attribute__((aligned(16))) float g_att_small[ATT_SMALL];
-
-// Waits until at most N vector memory operations of this wave are in flight.
-template <int N>
-__device__ __forceinline__ void att_wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-__device__ __forceinline__ void att_wait_vm(int n) {
-  if (n >= 10) att_wait_vm<10>();
-  else if (n >= 8) att_wait_vm<8>();
-  else if (n >= 2) att_wait_vm<2>();
-  else att_wait_vm<0>();
-}
-
 // Reads the lane's 4 key and 4 value blocks (at kva, 1 KB apart) and waits
 // for the reads. The copies that filled them must have landed.
 __device__ __forceinline__ void att_read_kv(unsigned kva, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
@@ -1111,11 +1155,10 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
   const unsigned ring0 = (unsigned)(uintptr_t)&g_att_ring[0][0][0];
 
   // the (stream, head) this workgroup merges, if any: (stream, head) i is
-  // merged by workgroup i * G / (B * NH), at most one per workgroup while
-  // B * NH <= G
+  // merged by workgroup i (B * NH <= G)
   const int nbh = a.B * NH;
-  const int mi = (wg * nbh + G - 1) / G;
-  const bool merges = mi < nbh && (mi * G) / nbh == wg;
+  const int mi = wg;
+  const bool merges = wg < nbh;
   // the block rows of that pair are loaded before the copies (once the
   // previous phase has written them) and used after the workgroup's chunks
   BlockRows br{};
@@ -1319,6 +1362,14 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
     }
   }
   trace_mark(a, sy, 5);
+  // The other workgroups warm the next phases' weights on the XCDs that will
+  // read them: the output projection (one tile per unit) and gate|up (three).
+  if (!merges && !sync) {
+    auto& L = a.d.layer[l];
+    warm(nbh, HT, [&](int u) { touch_tiles(L.wo, u, 1, 0, H / 64); });
+    warm(nbh, GU / 16 / 3, [&](int u) { touch_tiles(L.gu, 3 * u, 3, 0, H / 64); });
+    warm_done();
+  }
   // Merge: one (stream, head) per workgroup, all in parallel, once its
   // counter shows every segment stored. The merging workgroup resets the
   // counter for the next round. Streams with an empty context attend to the
@@ -1349,36 +1400,42 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
   trace_mark(a, sy, 4);
 }
 
-// x_{out} = x_{in} + W v for a 2560-wide output, with the gained copy and
-// per-tile sums of squares.
-template <int KBS>
-__device__ __attribute__((noinline, not_tail_called)) void ph_resid(Args& a_, Mat& W_,
-                                                   gptr<const float> srcA_, int ldA_, int xin_, int xout_,
-                                                   gptr<const float> gain_, lds_f red, SyncState sy,
-                                                   bool sync) {
-  const auto srcA = uni(srcA_);
-  const auto ldA = uni(ldA_);
-  const auto xin = uni(xin_);
-  const auto xout = uni(xout_);
-  const auto gain = uni(gain_);
-  Mat& W = uni(W_);
+// Output projection: x_{out} = x_{in} + W_o o, with the gained copy and
+// per-tile sums of squares; one 16-column tile per unit. The workgroups
+// without a tile warm the weights of the down projection two phases on.
+__device__ __attribute__((noinline, not_tail_called)) void ph_o(Args& a_, int l_, lds_f red, SyncState sy,
+                                               bool sync) {
+  const auto l = uni(l_);
   Args& a = uni(a_);
   const int G = gridDim.x, wg = blockIdx.x;
   auto& s = a.s;
-  const int R = a.R;
+  auto& L = a.d.layer[l];
+  const int R = a.R, xin = xs_in(l), xout = xs_o(l);
+  const auto gain = L.ffn_norm;
   bool first = sync;
   for (int u = wg; u < HT; u += G) {
-    const ASrc A{srcA, ldA, 0, nullptr, 0, R};
-    gemm_unit<1, KBS, 8, false>(a, sy, first, W, u, 1, 0, A, red, no_rms(),
-                                [&](int, int m, int n, float v) {
-                                  const int col = u * 16 + n;
-                                  const bool ok = m < R;
-                                  const float x = ok ? s.x[xin][m * H + col] + v : 0.f;
-                                  put_x(s, xout, gain, m, col, u, n, x, ok);
-                                });
+    const ASrc A{s.o[l], H, 0, nullptr, 0, R};
+    gemm_unit<1, 5, 8, false>(a, sy, first, L.wo, u, 1, 0, A, red, no_rms(),
+                              [&](int, int m, int n, float v) {
+                                const int col = u * 16 + n;
+                                const bool ok = m < R;
+                                const float x = ok ? s.x[xin][m * H + col] + v : 0.f;
+                                put_x(s, xout, gain, m, col, u, n, x, ok);
+                              });
     first = false;
   }
   if (first) grid_sync(a, sy);
+  // down units u: tile pair u / DOWN_KS, input third u % DOWN_KS (not in
+  // the persistent kernel, where an idle workgroup's late arrival would hold
+  // up the next barrier)
+  if (!sync) {
+    constexpr int DKB = FF / 64 / DOWN_KS;
+    warm(HT, HT / 2 * DOWN_KS, [&](int u) {
+      const int tp = u / DOWN_KS, p = u - tp * DOWN_KS;
+      touch_tiles(L.down, 2 * tp, 2, p * DKB, DKB);
+    });
+    warm_done();
+  }
 }
 
 // x_{out} = x_{in} + W_down h, with the 6144 inputs split in DOWN_KS thirds
@@ -1634,15 +1691,12 @@ __device__ void run_phase(Args& a, int p, lds_f red, SyncState sy, bool sync) {
   if (p == PH_PRE2) return ph_pre2(a, red, sy, sync);
   if (p == PH_HEAD) return ph_head(a, red, sy, sync);
   const int l = (p - 3) >> 3, k = (p - 3) & 7;
-  auto& s = a.s;
-  auto& L = a.d.layer[l];
   switch (k) {
     case PH_SA: return ph_sa(a, l, red, sy, sync);
     case PH_SU: return ph_su(a, l, red, sy, sync);
     case PH_QKV: return ph_qkv(a, l, red, sy, sync);
     case PH_ATTN: return ph_attn(a, l, sy, sync);
-    case PH_O:
-      return ph_resid<5>(a, L.wo, s.o[l], H, xs_in(l), xs_o(l), L.ffn_norm, red, sy, sync);
+    case PH_O: return ph_o(a, l, red, sy, sync);
     case PH_GU: return ph_gu(a, l, red, sy, sync);
     case PH_DOWN: return ph_down(a, l, red, sy, sync);
   }
