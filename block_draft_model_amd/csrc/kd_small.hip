@@ -293,6 +293,13 @@ __device__ __forceinline__ void warm(int i0, int nunits, F&& touch_unit) {
 }
 // Every copy has landed (before the workgroup ends, while its LDS is still its own).
 __device__ __forceinline__ void warm_done() { att_wait_vm<0>(); }
+// q|k|v units [u0, u1) of layer l (two tiles each), by idle workgroups [i0, G).
+__device__ __forceinline__ void warm_qkv(Args& a, int l, int i0, int u0, int u1) {
+  Mat& W = a.d.layer[l].qkv;
+  warm(i0, u1, [&](int u) {
+    if (u >= u0) touch_tiles(W, 2 * u, 2, 0, H / 64);
+  });
+}
 
 // ---------------------------------------------------------------------------
 // Projection units: NT consecutive 16-row weight tiles; wave w (< AW) takes
@@ -612,6 +619,11 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_pre1(Args& a_, lds
     first = false;
   }
   if (first) grid_sync(a, sy);
+  // idle workgroups warm the first half of layer 0's q|k|v (per-phase path)
+  if (!sync) {
+    warm_qkv(a, 0, HT + RK / 16, 0, QKV / 32 / 2);
+    warm_done();
+  }
 }
 
 __device__ __attribute__((noinline, not_tail_called)) void ph_pre2(Args& a_, lds_f red, SyncState sy,
@@ -635,6 +647,11 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_pre2(Args& a_, lds
     first = false;
   }
   if (first) grid_sync(a, sy);
+  // idle workgroups warm the second half of layer 0's q|k|v (per-phase path)
+  if (!sync && a.nl > 0) {
+    warm_qkv(a, 0, HT, QKV / 32 / 2, QKV / 32);
+    warm_done();
+  }
 }
 
 // Spine A: ss = silu(A_s (g_s * x_{j-1}) / rms(x_{j-1})) for rows j = 1..3.
@@ -658,11 +675,12 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_sa(Args& a_, int l
     first = false;
   }
   if (first) grid_sync(a, sy);
-  // the workgroups without a tile warm the next two phases' weights: the
-  // spine U (one tile per unit) and q|k|v (two); not in the persistent kernel
+  // the workgroups without a tile warm the next phases' weights: the spine U
+  // (one tile per unit) and the first half of q|k|v (two); not in the
+  // persistent kernel
   if (!sync) {
     warm(RK / 16, HT, [&](int u) { touch_tiles(L.su, u, 1, 0, RK / 64); });
-    warm(RK / 16, QKV / 16 / 2, [&](int u) { touch_tiles(L.qkv, 2 * u, 2, 0, H / 64); });
+    warm_qkv(a, l, RK / 16, 0, QKV / 32 / 2);
     warm_done();
   }
 }
@@ -702,6 +720,11 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_su(Args& a_, int l
     first = false;
   }
   if (first) grid_sync(a, sy);
+  // idle workgroups warm the second half of q|k|v (per-phase path)
+  if (!sync) {
+    warm_qkv(a, l, HT, QKV / 32 / 2, QKV / 32);
+    warm_done();
+  }
 }
 
 // q|k|v = W (g_a * x) / rms(x); RoPE on q and k inside each paired tile.
