@@ -250,9 +250,13 @@ __device__ __forceinline__ void att_wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
+// (n is wave-uniform; values the attention loop uses: 0, 2, 5, 8, 10, 11, 13)
 __device__ __forceinline__ void att_wait_vm(int n) {
-  if (n >= 10) att_wait_vm<10>();
+  if (n >= 13) att_wait_vm<13>();
+  else if (n >= 11) att_wait_vm<11>();
+  else if (n >= 10) att_wait_vm<10>();
   else if (n >= 8) att_wait_vm<8>();
+  else if (n >= 5) att_wait_vm<5>();
   else if (n >= 2) att_wait_vm<2>();
   else att_wait_vm<0>();
 }
@@ -1051,6 +1055,11 @@ __device__ __forceinline__ void att_read_p(unsigned addr, f32x4 (&r)[4]) {
 __device__ __forceinline__ void att_write_ml(unsigned ma, float m, float l) {
   asm volatile("ds_write_b32 %0, %1\n\tds_write_b32 %0, %2 offset:128" : : "v"(ma), "v"(m), "v"(l) : "memory");
 }
+// A write-through store that is exactly one vector memory instruction, so the
+// attention loop can count it in its waits.
+__device__ __forceinline__ void att_store(gptr<float> p, float v) {
+  asm volatile("global_store_dword %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
+}
 // Eight waves' max (at ma + 16 w), sum (at ma + 128 + 16 w) and output (at
 // oa + 2048 w).
 __device__ __forceinline__ void att_read_mlo(unsigned ma, unsigned oa, float (&m)[8], float (&ls)[8],
@@ -1215,18 +1224,24 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
   float o[4][8];
   int seg_c0 = 0;
   int slot = 0;
+  int stores = 0;  // store instructions the previous unit issued after its copies
   for (int u = ub; u < ue; ++u, slot ^= 1) {
     int b, c, h;
     sl.unit(u, b, c, h);
     const int n = sl.vis(b), nc = sl.chunks(b);
     const bool seg_start = u == ub || c == 0;
     const bool seg_end = u + 1 == ue || c == nc - 1;
-    // copies per unit: 8 per wave, 10 for wave 0 (its query blocks); in the
-    // persistent kernel wave 0's first two query copies follow both key/value
-    // sets, so its first unit waits for the second unit's queries only
+    // Vector memory operations issued after this unit's copies, which its
+    // wait lets stay in flight: the next unit's copies (8 per wave, 10 for
+    // wave 0 with its query blocks; in the persistent kernel wave 0's first
+    // two query copies follow both key/value sets, so its first unit allows
+    // only the second unit's queries), then the previous unit's partial
+    // stores, issued after those copies. Counting fewer than were issued
+    // would only make the wait stricter.
     const bool next = u + 1 < ue;
-    const int nwait = !next ? 0 : (wave_s != 0 ? 8 : (sync && u == ub ? 2 : 10));
+    const int nwait = !next ? 0 : (wave_s != 0 ? 8 : (sync && u == ub ? 2 : 10)) + stores;
     att_wait_vm(uni(nwait));
+    stores = 0;
     if (seg_start) {
       // wave 0's query copy has landed for every wave; the previous
       // segment's readers of the shared LDS areas are done
@@ -1256,6 +1271,14 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
     }
     u32x4 kr[4], vr[4];
     att_read_kv(ring0 + slot * ATT_SLOT_BYTES + wave * ATT_WAVE_BLOCKS * 1024 + lane * 16, kr, vr);
+    if (u == ub) trace_mark(a, sy, 3);
+    // the unit's keys and values are in registers and every wave has read
+    // its queries: the slot is free, so the unit after next is copied into
+    // it before this one is computed
+    if (u + 2 < ue) {
+      copy_kv(u + 2, slot);
+      copy_q(u + 2, slot);
+    }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -1315,12 +1338,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[j][e] += pj[j][t] * vf[e];
     }
-    // the slot is free again: copy the unit after next into it
-    if (u + 2 < ue) {
-      copy_kv(u + 2, slot);
-      copy_q(u + 2, slot);
-    }
-    if (u == ub) trace_mark(a, sy, 3);
+
     if (seg_end) {
       // sum the 4 key groups: groups g and g^2 exchange, g < 2 keeping rows
       // 0, 1 and g >= 2 rows 2, 3; then g and g^1, odd groups keeping the
@@ -1363,12 +1381,15 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
           O += ow[w] * f;
         }
       }
+      // three store instructions per wave: the output by every lane, the max
+      // and sum of row j by lane 0 (waves 2j and 2j + 1 store the same values)
       const size_t pb = ((size_t)(b * NH + h) * nch + seg_c0) * 4 + j;
-      st_wt(&s.ao[l][pb * DH + dd], O);
-      if (dd == 0) {
-        st_wt(&s.am[l][pb], M);
-        st_wt(&s.al[l][pb], Ls);
+      att_store(s.ao[l] + pb * DH + dd, O);
+      if (lane == 0) {
+        att_store(s.am[l] + pb, M);
+        att_store(s.al[l] + pb, Ls);
       }
+      stores = 3;
       // the next segment starts with a barrier before the LDS areas are reused
     }
   }
