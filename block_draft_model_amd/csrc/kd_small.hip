@@ -9,12 +9,13 @@
 //     SA   (l >= 1) ss = silu(A_s (g_s * x_{j-1}) / rms(x_{j-1}))
 //     SU   (l >= 1) x_j += U_s ss   (rows 1..3; row 0 copied)
 //     QKV  q,k,v = W_qkv (g_a * x) / rms(x), RoPE on q and k
-//     ATTN partial softmax over 128 context keys per (stream, head, chunk);
-//          the last chunk of a (stream, head) to finish merges all chunks with
+//     ATTN online softmax over each workgroup's contiguous range of 128-key
+//          chunks, one partial per (stream, head) segment of the range; a
+//          designated workgroup per (stream, head) merges the segments with
 //          the block's own keys (causal) -> o
 //     O    x += W_o o
 //     GU   h = silu(W_g (g_f * x) / rms(x)) * (W_u (g_f * x) / rms(x))
-//     DOWN x += W_down h
+//     DOWN x += W_down h   (inputs split in thirds across workgroups)
 //   HEAD  logits = Head (g_o * x) / rms(x) * g_tensor -> per-workgroup argmax;
 //         the last workgroup to finish reduces the candidates -> target ids
 //
@@ -24,6 +25,10 @@
 // deferred: the projection runs on g * x (each producer of x also writes the
 // gained copy its matrix consumer needs) and the epilogue scales by 1/rms(x),
 // with rms from per-tile sums of squares written by the producer of x.
+//
+// Per-phase launches (the default): phase p's unit u runs on workgroup u.
+// Workgroups with no unit in a phase read ahead the weights of a later phase
+// for the workgroups on their XCD (cache warming).
 //
 // In the persistent kernel, phases are separated by a two-level counter
 // barrier without cache-wide fences. That is safe because every buffer a phase
