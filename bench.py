@@ -45,14 +45,19 @@ def algorithmic_bytes(dims, lens, streams):
 
 
 def kernel_source_hash():
-    """sha256 over the HIP sources, first 12 hex digits: identifies the kernels
-    a counter measurement was taken on."""
+    """sha256 over the HIP sources with comments and blank space removed, first
+    12 hex digits: identifies the kernels a counter measurement was taken on
+    (an edit of comments alone keeps it)."""
     import glob
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(ROOT, "block_draft_model_amd", "csrc", "*"))):
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:12]
 
 
