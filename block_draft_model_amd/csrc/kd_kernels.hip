@@ -87,6 +87,7 @@ static int splits_for(int KB, int want) {
 }
 
 int gemm_splits(int K, int N, int R) {
+  if (gemm_mm_fits(R, N)) return gemm_mm_splits(K, N, R);
   const int KB = K / 64;
   int base;
   if (N <= 256) base = KB / 4;           // rank-256 adapters: thin matrices, split deep
@@ -100,6 +101,7 @@ int gemm_splits(int K, int N, int R) {
 
 void launch_gemm(hipStream_t st, const uint16_t* af, int R, const Fp8Mat& W, int n_off_tiles,
                  int N, float* part, int splits) {
+  if (gemm_mm_fits(R, N)) return launch_gemm_mm(st, af, R, W, n_off_tiles, N, part, splits);
   GemmK g;
   g.af = af;
   g.R = R;
@@ -730,6 +732,7 @@ __global__ __launch_bounds__(256) void k_head(HeadK a) {
 }
 
 void launch_head(hipStream_t st, const Work& w, const DevWeights& d, int R, float* logits) {
+  if (head_mm_fits(R)) return launch_head_mm(st, w.af_x, R, d, logits, w.keys);
   HeadK a;
   a.af = w.af_x;
   a.R = R;

@@ -130,6 +130,14 @@ void launch_norm_rows(hipStream_t st, const float* x, int rows, const float* gai
 void launch_ingest_store(hipStream_t st, const Work& w, int B, int n_new, int splits, const KV& kv,
                          int layer, const int32_t* lens, float theta);
 void launch_bump_lens(hipStream_t st, int32_t* lens, int B, int n);
+// many block rows (kd_mm.hip): matrix-core tiles of 64 rows x 256 columns
+bool gemm_mm_fits(int R, int N);
+int gemm_mm_splits(int K, int N, int R);
+void launch_gemm_mm(hipStream_t st, const uint16_t* af, int R, const Fp8Mat& W, int n_off_tiles,
+                    int N, float* part, int splits);
+bool head_mm_fits(int R);
+void launch_head_mm(hipStream_t st, const uint16_t* af, int R, const DevWeights& d, float* logits,
+                    unsigned long long* keys);
 // probes
 void launch_probe_e4m3(hipStream_t st, uint16_t* out);
 void launch_probe_nvfp4(hipStream_t st, uint16_t* out);
