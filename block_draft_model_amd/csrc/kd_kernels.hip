@@ -339,119 +339,221 @@ void launch_qkv_post(hipStream_t st, const Work& w, int B, int splits) {
 }
 
 // ---------------------------------------------------------------------------
-// Cross-attention over the context window, split over chunks of ATT_CH keys.
-// Each workgroup (stream b, head h, chunk c) produces for the 4 block rows the
-// running max m (log2 units), the sum l of 2^(s - m) and o = sum 2^(s - m) v.
+// Cross-attention over the context window (model card, Architecture, Body:
+// every block row attends to the last window rows of its stream's cached K/V
+// and causally to the block). A workgroup takes one segment of one (stream,
+// head): S segments split the window's 16-key blocks evenly. Wave w takes the
+// segment's blocks w, w + 4, ..., with the next block's keys and values in
+// flight while one is computed:
+//   scores  S^T[key][j] = K Q^T on the matrix cores (16x16x32 bf16): keys as
+//           the A operand (lane: key lane%16, dims 32kb + 8(lane/16)), the
+//           queries (pre-scaled by log2(e)/sqrt(128)) split into bf16 hi + lo
+//           as the B operand (column j < 4 of the 4 block rows);
+//   softmax running max and sum per row j (log2 units), the output rescaled
+//           when the max grows;
+//   P V     on the vector units: lane (g, c) adds keys 4g..4g+3 of the block
+//           for dims 8c..8c+7 of all 4 rows.
+// The 4 waves' states are merged in LDS. With one segment the workgroup also
+// adds the block's own keys (row j sees block rows 0..j), normalises, and
+// writes the output rows; otherwise it stores the segment's max m, sum l and
+// unnormalised output o for k_attn_combine.
 // ---------------------------------------------------------------------------
 struct AttnK {
   const float* q;
+  const float* kb;
+  const float* vb;
   const uint16_t* k;
   const uint16_t* v;
   int64_t ss, sh, sl;
-  int cap, window, nch;
+  int cap, window, nch, S;
   const int32_t* lens;
   float* pm;
   float* pl;
   float* po;
+  uint16_t* af_o;
 };
+
+// The block's own keys for rows j = 0..3 of one (stream, head), merged into
+// (M, L, O) of thread item (j, d); returns the normalised output.
+__device__ __forceinline__ float attn_block_merge(const float* sblk, const float* vb, size_t vrow0,
+                                                  int j, int d, float M, float L, float O) {
+  float Mn = M;
+#pragma unroll
+  for (int i = 0; i < BLK; ++i)
+    if (i <= j) Mn = fmaxf(Mn, sblk[j * BLK + i]);
+  const float f = M == -__builtin_inff() ? 0.f : exp2f(M - Mn);
+  L *= f;
+  O *= f;
+#pragma unroll
+  for (int i = 0; i < BLK; ++i)
+    if (i <= j) {
+      const float p = exp2f(sblk[j * BLK + i] - Mn);
+      L += p;
+      O += p * vb[vrow0 + (size_t)i * H + d];
+    }
+  return O / L;
+}
 
 __global__ __launch_bounds__(256) void k_attn_split(AttnK a) {
   __shared__ float s_o[4][BLK][DH];
   __shared__ float s_m[4][BLK], s_l[4][BLK];
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  __shared__ float s_blk[BLK * BLK];
+  const int seg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
   const int len = a.lens[b];
   const int n = min(len, a.window);
-  if (c * ATT_CH >= n) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane >> 4, d0 = (lane & 15) * 8;
+  const int nblk = (n + 15) >> 4;
+  const int blk0 = (int)(((long long)seg * nblk) / a.S), blk1 = (int)(((long long)(seg + 1) * nblk) / a.S);
   const float qs = 0.08838834764831845f * 1.4426950408889634f;  // 1/sqrt(128) * log2(e)
-  float q[BLK][8];
+  const size_t qrow0 = (size_t)(b * BLK) * H + h * DH;
+
+  float m_run = -__builtin_inff(), l_run = 0.f;
+  float o[BLK][8];
 #pragma unroll
   for (int j = 0; j < BLK; ++j)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) q[j][e] = a.q[(size_t)(b * BLK + j) * H + h * DH + d0 + e] * qs;
-  const uint16_t* kbase = a.k + b * a.ss + h * a.sh + d0;
-  const uint16_t* vbase = a.v + b * a.ss + h * a.sh + d0;
-  const int base = c * ATT_CH + wave * 32;
-  const int first = len - n;
-  float sc[BLK][8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const int idx = base + 4 * s + g;
-    const bool valid = idx < n;
-    float dot[BLK] = {0.f, 0.f, 0.f, 0.f};
-    if (valid) {
-      const int slot = (first + idx) % a.cap;
-      float kf[8];
-      bf16x8_to_f32(*reinterpret_cast<const u32x4*>(kbase + slot * a.sl), kf);
-#pragma unroll
-      for (int j = 0; j < BLK; ++j)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dot[j] += q[j][e] * kf[e];
-    }
-#pragma unroll
-    for (int j = 0; j < BLK; ++j) {
-#pragma unroll
-      for (int m = 8; m >= 1; m >>= 1) dot[j] += __shfl_xor(dot[j], m, 64);
-      sc[j][s] = valid ? dot[j] : -__builtin_inff();
-    }
-  }
-  float mx[BLK], l[BLK], o[BLK][8];
-#pragma unroll
-  for (int j = 0; j < BLK; ++j) {
-    float m = sc[j][0];
-#pragma unroll
-    for (int s = 1; s < 8; ++s) m = fmaxf(m, sc[j][s]);
-    m = fmaxf(m, __shfl_xor(m, 16, 64));
-    m = fmaxf(m, __shfl_xor(m, 32, 64));
-    mx[j] = m;
-    l[j] = 0.f;
-#pragma unroll
     for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
-  }
+
+  if (blk0 < blk1) {
+    // queries as the B operand: lane (lr, lg) holds q_lr[32kb + 8lg .. + 8] (rows >= 4 zero)
+    bf16x8 qh[4], ql[4];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const int idx = base + 4 * s + g;
-    if (idx < n) {
-      const int slot = (first + idx) % a.cap;
-      float vf[8];
-      bf16x8_to_f32(*reinterpret_cast<const u32x4*>(vbase + slot * a.sl), vf);
+    for (int kb = 0; kb < 4; ++kb) {
+      float qv[8];
+      if (lr < BLK) {
+        const float* qp = a.q + qrow0 + (size_t)lr * H + 32 * kb + 8 * lg;
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(qp);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(qp + 4);
 #pragma unroll
-      for (int j = 0; j < BLK; ++j) {
-        const float p = exp2f(sc[j][s] - mx[j]);
-        l[j] += p;
+        for (int e = 0; e < 4; ++e) {
+          qv[e] = x0[e] * qs;
+          qv[4 + e] = x1[e] * qs;
+        }
+      } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[j][e] += p * vf[e];
+        for (int e = 0; e < 8; ++e) qv[e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const __bf16 hh = (__bf16)qv[e];
+        qh[kb][e] = hh;
+        ql[kb][e] = (__bf16)(qv[e] - (float)hh);
       }
     }
-  }
+    const uint16_t* kbase = a.k + b * a.ss + h * a.sh;
+    const uint16_t* vbase = a.v + b * a.ss + h * a.sh;
+    const int f0 = (len - n) % a.cap;
+    auto slot_of = [&](int key) {
+      const int s_ = f0 + min(key, n - 1);
+      return s_ - (s_ >= a.cap ? a.cap : 0);
+    };
+    // keys past n are clamped to the last visible key and masked in the scores
+    auto load_blk = [&](int bi, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
+      const uint16_t* kp = kbase + (size_t)slot_of(16 * bi + lr) * a.sl + 8 * lg;
 #pragma unroll
-  for (int j = 0; j < BLK; ++j) {
-    l[j] += __shfl_xor(l[j], 16, 64);
-    l[j] += __shfl_xor(l[j], 32, 64);
+      for (int kb = 0; kb < 4; ++kb) kr[kb] = *reinterpret_cast<const u32x4*>(kp + 32 * kb);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        vr[t] = *reinterpret_cast<const u32x4*>(vbase + (size_t)slot_of(16 * bi + 4 * lg + t) * a.sl + 8 * lr);
+    };
+    auto process = [&](int bi, const u32x4 (&kr)[4], const u32x4 (&vr)[4]) __attribute__((always_inline)) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const bf16x8 kk = __builtin_bit_cast(bf16x8, kr[kb]);
+        acc = mfma_bf16(kk, qh[kb], acc);
+        acc = mfma_bf16(kk, ql[kb], acc);
+      }
+      // lane (lr, lg): acc[e] = S^T[key 4lg + e][row lr]
+      float sc[4], mx = -__builtin_inff();
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sc[e] = 16 * bi + 4 * lg + e < n ? acc[e] : -__builtin_inff();
+        mx = fmaxf(mx, sc[e]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_run == -__builtin_inff() ? 0.f : exp2f(m_run - m_new);
+      float pe[4], ls = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pe[e] = sc[e] == -__builtin_inff() ? 0.f : exp2f(sc[e] - m_new);
+        ls += pe[e];
+      }
+      ls += __shfl_xor(ls, 16, 64);
+      ls += __shfl_xor(ls, 32, 64);
+      l_run = l_run * alpha + ls;
+      m_run = m_new;
+      // lane (g = lg, c = lr) gathers P[j][4g + t] from lane (j, g)
+#pragma unroll
+      for (int j = 0; j < BLK; ++j) {
+        const float aj = __shfl(alpha, j, 64);
+        float pj[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) pj[t] = __shfl(pe[t], (lg << 4) | j, 64);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[j][e] *= aj;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          float vf[8];
+          bf16x8_to_f32(vr[t], vf);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[j][e] += pj[t] * vf[e];
+        }
+      }
+    };
+    // blocks of this wave: blk0 + wave + 4i; two register sets alternate so the
+    // next block's loads are in flight while one is computed
+    const int last = blk1 - 1;
+    int bi = blk0 + wave;
+    u32x4 kA[4], vA[4], kB[4], vB[4];
+    load_blk(min(bi, last), kA, vA);
+    for (; bi <= last; bi += 8) {
+      load_blk(min(bi + 4, last), kB, vB);
+      process(bi, kA, vA);
+      if (bi + 4 > last) break;
+      load_blk(min(bi + 8, last), kA, vA);
+      process(bi + 4, kB, vB);
+    }
+  }
+  // sum the 4 key groups of the wave: lanes lg = 0 end with o[j][8 lr + e]
+#pragma unroll
+  for (int j = 0; j < BLK; ++j)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       o[j][e] += __shfl_xor(o[j][e], 16, 64);
       o[j][e] += __shfl_xor(o[j][e], 32, 64);
     }
-  }
-  if (g == 0) {
-#pragma unroll
-    for (int j = 0; j < BLK; ++j)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s_o[wave][j][d0 + e] = o[j][e];
-  }
-  if (lane == 0) {
+  if (lg == 0) {
 #pragma unroll
     for (int j = 0; j < BLK; ++j) {
-      s_m[wave][j] = mx[j];
-      s_l[wave][j] = l[j];
+      *reinterpret_cast<f32x4*>(&s_o[wave][j][8 * lr]) = f32x4{o[j][0], o[j][1], o[j][2], o[j][3]};
+      *reinterpret_cast<f32x4*>(&s_o[wave][j][8 * lr + 4]) = f32x4{o[j][4], o[j][5], o[j][6], o[j][7]};
+    }
+  }
+  // row lr's max and sum live in every lane with lane % 16 == lr
+  if (lane < BLK) {
+    s_m[wave][lane] = m_run;
+    s_l[wave][lane] = l_run;
+  }
+  // the block's own scores s[j][i] (i <= j): wave j, lane l covers dims 2l, 2l+1
+  if (a.S == 1) {
+    const int j = wave;
+    const float q0 = a.q[qrow0 + (size_t)j * H + 2 * lane], q1 = a.q[qrow0 + (size_t)j * H + 2 * lane + 1];
+#pragma unroll
+    for (int i = 0; i < BLK; ++i) {
+      if (i > j) break;
+      const float* kp = a.kb + qrow0 + (size_t)i * H + 2 * lane;
+      const float p = wave_sum(q0 * kp[0] + q1 * kp[1]);
+      if (lane == 0) s_blk[j * BLK + i] = p * qs;
     }
   }
   __syncthreads();
-  const size_t pb = ((size_t)(b * NH + h) * a.nch + c) * BLK;
-  for (int t = threadIdx.x; t < BLK * DH; t += blockDim.x) {
-    const int j = t / DH, d = t % DH;
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int j = (threadIdx.x >> 7) + 2 * it, d = threadIdx.x & 127;
     float M = -__builtin_inff();
 #pragma unroll
     for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][j]);
@@ -464,10 +566,20 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnK a) {
         O += s_o[w][j][d] * f;
       }
     }
-    a.po[(pb + j) * DH + d] = O;
-    if (d == 0) {
-      a.pm[pb + j] = M;
-      a.pl[pb + j] = L;
+    if (a.S == 1) {
+      const float out = attn_block_merge(s_blk, a.vb, qrow0, j, d, M, L, O);
+      const uint32_t hi = bf16_rne(out);
+      const uint32_t lo = bf16_rne(out - bf16_to_f32(hi));
+      const size_t off = afrag_off(b * BLK + j, h * DH + d, H / 32);
+      a.af_o[off] = (uint16_t)hi;
+      a.af_o[off + 512] = (uint16_t)lo;
+    } else {
+      const size_t pb = ((size_t)(b * NH + h) * a.nch + seg) * BLK + j;
+      a.po[pb * DH + d] = O;
+      if (d == 0) {
+        a.pm[pb] = M;
+        a.pl[pb] = L;
+      }
     }
   }
 }
@@ -478,12 +590,13 @@ __global__ __launch_bounds__(128) void k_attn_combine(const float* q, const floa
                                                       const float* vb, const float* pm,
                                                       const float* pl, const float* po, int nch,
                                                       const int32_t* lens, int window,
-                                                      uint16_t* af_o) {
+                                                      int nseg, uint16_t* af_o) {
   __shared__ float red[2][10];
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = min(lens[b], window);
-  const int nc = (n + ATT_CH - 1) / ATT_CH;
+  // the segment partials (an empty segment stored m = -inf, l = 0, o = 0)
+  const int nc = n > 0 ? nseg : 0;
   const float qs = 0.08838834764831845f * 1.4426950408889634f;
   float qv[BLK], kv[BLK], vv[BLK];
 #pragma unroll
@@ -517,6 +630,7 @@ __global__ __launch_bounds__(128) void k_attn_combine(const float* q, const floa
     float L = 0.f, O = 0.f;
     for (int c = 0; c < nc; ++c) {
       const size_t pb = ((size_t)(b * NH + h) * nch + c) * BLK + j;
+      if (pm[pb] == -__builtin_inff()) continue;
       const float f = exp2f(pm[pb] - M);
       L += pl[pb] * f;
       O += po[pb * DH + d] * f;
@@ -541,6 +655,8 @@ void launch_attention(hipStream_t st, const Work& w, int B, const KV& kv, int la
                       const int32_t* lens, int window) {
   AttnK a;
   a.q = w.q;
+  a.kb = w.kb;
+  a.vb = w.vb;
   a.k = kv.k[layer];
   a.v = kv.v[layer];
   a.ss = kv.ss;
@@ -549,13 +665,22 @@ void launch_attention(hipStream_t st, const Work& w, int B, const KV& kv, int la
   a.cap = kv.cap;
   a.window = window;
   a.nch = w.att_nch;
+  // segments per (stream, head): enough workgroups to fill the chip (about
+  // 1024), at most 8 and at most the partial slots per (stream, head)
+  const int pairs = B * NH;
+  int S = (1024 + pairs - 1) / pairs;
+  S = S < 1 ? 1 : (S > 8 ? 8 : S);
+  if (S > w.att_nch) S = w.att_nch;
+  a.S = S;
   a.lens = lens;
   a.pm = w.att_m;
   a.pl = w.att_l;
   a.po = w.att_o;
-  k_attn_split<<<dim3(w.att_nch, NH, B), 256, 0, st>>>(a);
-  k_attn_combine<<<dim3(NH, B), 128, 0, st>>>(w.q, w.kb, w.vb, w.att_m, w.att_l, w.att_o,
-                                              w.att_nch, lens, window, w.af_o);
+  a.af_o = w.af_o;
+  k_attn_split<<<dim3(S, NH, B), 256, 0, st>>>(a);
+  if (S > 1)
+    k_attn_combine<<<dim3(NH, B), 128, 0, st>>>(w.q, w.kb, w.vb, w.att_m, w.att_l, w.att_o,
+                                                w.att_nch, lens, window, S, w.af_o);
 }
 
 // x += sum of partials; afrag of RMSNorm(x; gain). spine_rows: write row
