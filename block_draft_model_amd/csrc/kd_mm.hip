@@ -26,9 +26,13 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int MM_RT = 4;                          // 16-row tiles per workgroup
-constexpr int MM_CT = 4;                          // 16-column tiles per wave
 constexpr int MM_WAVES = 4;
-constexpr int MM_COLS = 16 * MM_CT * MM_WAVES;    // output columns per workgroup
+// 4 column tiles per wave (256 columns per workgroup) once the
+// rows make the work matrix-core bound; 1 (64 columns) for fewer rows, where
+// the weights stream from HBM and narrower tiles give more workgroups with
+// fewer split-K partial sums.
+constexpr int MM_SMALL_R = 128;
+__host__ __device__ inline int mm_ct(int R) { return R > MM_SMALL_R ? 4 : 1; }
 
 // Workgroup -> (row block, column block, split). Column unit c = (column
 // block, split) runs on XCD c % 8; its row blocks are consecutive slots there.
@@ -90,15 +94,17 @@ struct GemmMM {
   const uint8_t* w;     // repacked codes [N/16][KB][64][16]
   const float* s;       // scales [N/16][KB][16]
   int KB;
-  int N, n_off;         // output columns (multiple of MM_COLS), first weight tile
+  int N, n_off;         // output columns (a multiple of the workgroup's), first weight tile
   float* part;
   int splits, kbs;
 };
 
+template <int CT>
 __global__ __launch_bounds__(256) void k_gemm_mm(GemmMM g) {
+  constexpr int COLS = 16 * CT * MM_WAVES;
   // [buffer][row tile][hi t, lo t, hi t+1, lo t+1][lane]
   __shared__ __attribute__((aligned(16))) u32x4 sa[2][MM_RT * 4][64];
-  const int RB = (g.R + 63) / 64, CB = g.N / MM_COLS;
+  const int RB = (g.R + 63) / 64, CB = g.N / COLS;
   const MmMap m = mm_map(RB, CB, g.splits);
   if (!m.ok) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -108,23 +114,23 @@ __global__ __launch_bounds__(256) void k_gemm_mm(GemmMM g) {
   // and its output rows are past R and discarded)
   const int mt_ld = min(m.rb * MM_RT + wave, MT - 1);
   const uint16_t* ap = g.af + ((size_t)mt_ld * g.KT + 2 * b0) * 1024 + lane * 8;
-  const int nt0 = g.n_off + m.cb * (MM_COLS / 16) + wave * MM_CT;
+  const int nt0 = g.n_off + m.cb * (COLS / 16) + wave * CT;
   const uint8_t* wp = g.w + ((size_t)nt0 * g.KB + b0) * 1024 + lane * 16;
   const float* spp = g.s + ((size_t)nt0 * g.KB + b0) * 16 + (lane & 15);
   const size_t wt_stride = (size_t)g.KB * 1024, st_stride = (size_t)g.KB * 16;
 
-  f32x4 acc[MM_RT][MM_CT];
+  f32x4 acc[MM_RT][CT];
 #pragma unroll
   for (int r = 0; r < MM_RT; ++r)
 #pragma unroll
-    for (int c = 0; c < MM_CT; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < CT; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 ar[4], wr[MM_CT];
-  float sr[MM_CT];
+  u32x4 ar[4], wr[CT];
+  float sr[CT];
 #pragma unroll
   for (int j = 0; j < 4; ++j) ar[j] = *reinterpret_cast<const u32x4*>(ap + j * 512);
 #pragma unroll
-  for (int c = 0; c < MM_CT; ++c) {
+  for (int c = 0; c < CT; ++c) {
     wr[c] = *reinterpret_cast<const u32x4*>(wp + c * wt_stride);
     sr[c] = spp[c * st_stride];
   }
@@ -136,19 +142,19 @@ __global__ __launch_bounds__(256) void k_gemm_mm(GemmMM g) {
     // next step's loads (the last step re-loads itself; unconditional loads
     // keep the compiler from waiting for them at a join)
     const int in = min(i + 1, nb - 1);
-    u32x4 an[4], wn[MM_CT];
-    float sn[MM_CT];
+    u32x4 an[4], wn[CT];
+    float sn[CT];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       an[j] = *reinterpret_cast<const u32x4*>(ap + (size_t)in * 2048 + j * 512);
 #pragma unroll
-    for (int c = 0; c < MM_CT; ++c) {
+    for (int c = 0; c < CT; ++c) {
       wn[c] = *reinterpret_cast<const u32x4*>(wp + c * wt_stride + (size_t)in * 1024);
       sn[c] = spp[c * st_stride + (size_t)in * 16];
     }
-    bf16x8 w0[MM_CT], w1[MM_CT];
+    bf16x8 w0[CT], w1[CT];
 #pragma unroll
-    for (int c = 0; c < MM_CT; ++c) {
+    for (int c = 0; c < CT; ++c) {
       w0[c] = mm_e4m3x8(wr[c].x, wr[c].y);
       w1[c] = mm_e4m3x8(wr[c].z, wr[c].w);
     }
@@ -160,7 +166,7 @@ __global__ __launch_bounds__(256) void k_gemm_mm(GemmMM g) {
       const bf16x8 ah1 = __builtin_bit_cast(bf16x8, sa[buf][r * 4 + 2][lane]);
       const bf16x8 al1 = __builtin_bit_cast(bf16x8, sa[buf][r * 4 + 3][lane]);
 #pragma unroll
-      for (int c = 0; c < MM_CT; ++c) {
+      for (int c = 0; c < CT; ++c) {
         f32x4 t = {0.f, 0.f, 0.f, 0.f};
         t = mfma_bf16(ah0, w0[c], t);
         t = mfma_bf16(al0, w0[c], t);
@@ -174,7 +180,7 @@ __global__ __launch_bounds__(256) void k_gemm_mm(GemmMM g) {
       for (int j = 0; j < 4; ++j) sa[buf ^ 1][wave * 4 + j][lane] = an[j];
     }
 #pragma unroll
-    for (int c = 0; c < MM_CT; ++c) {
+    for (int c = 0; c < CT; ++c) {
       wr[c] = wn[c];
       sr[c] = sn[c];
     }
@@ -185,8 +191,8 @@ __global__ __launch_bounds__(256) void k_gemm_mm(GemmMM g) {
 #pragma unroll
   for (int r = 0; r < MM_RT; ++r)
 #pragma unroll
-    for (int c = 0; c < MM_CT; ++c) {
-      const int col = (m.cb * (MM_COLS / 16) + wave * MM_CT + c) * 16 + (lane & 15);
+    for (int c = 0; c < CT; ++c) {
+      const int col = (m.cb * (COLS / 16) + wave * CT + c) * 16 + (lane & 15);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = (m.rb * MM_RT + r) * 16 + 4 * (lane >> 4) + e;
@@ -197,7 +203,7 @@ __global__ __launch_bounds__(256) void k_gemm_mm(GemmMM g) {
 
 int gemm_mm_splits(int K, int N, int R) {
   const int KB = K / 64;
-  const int wgs = ((R + 63) / 64) * (N / MM_COLS);
+  const int wgs = ((R + 63) / 64) * (N / (64 * mm_ct(R)));
   int want = (512 + wgs - 1) / wgs;          // about two workgroups per CU
   want = std::min(want, std::max(KB / 4, 1));  // at least 4 blocks per split
   int s = std::max(want, 1);
@@ -205,7 +211,7 @@ int gemm_mm_splits(int K, int N, int R) {
   return s;
 }
 
-bool gemm_mm_fits(int R, int N) { return R > 32 && N % MM_COLS == 0; }
+bool gemm_mm_fits(int R, int N) { return R > 32 && N % (64 * mm_ct(R)) == 0; }
 
 void launch_gemm_mm(hipStream_t st, const uint16_t* af, int R, const Fp8Mat& W, int n_off_tiles,
                     int N, float* part, int splits) {
@@ -221,7 +227,10 @@ void launch_gemm_mm(hipStream_t st, const uint16_t* af, int R, const Fp8Mat& W, 
   g.part = part;
   g.splits = splits;
   g.kbs = g.KB / splits;
-  k_gemm_mm<<<mm_grid(R, N / MM_COLS, splits), 256, 0, st>>>(g);
+  if (mm_ct(R) == 4)
+    k_gemm_mm<4><<<mm_grid(R, N / 256, splits), 256, 0, st>>>(g);
+  else
+    k_gemm_mm<1><<<mm_grid(R, N / 64, splits), 256, 0, st>>>(g);
 }
 
 // ---------------------------------------------------------------------------
@@ -245,12 +254,13 @@ struct HeadMM {
   unsigned long long* keys;
 };
 
+template <int CT>
 __global__ __launch_bounds__(256) void k_head_mm(HeadMM a) {
   // [buffer][row tile][hi/lo of k tiles 0..3][lane] f16
   __shared__ __attribute__((aligned(16))) u32x4 sa[2][MM_RT * 8][64];
   __shared__ unsigned long long best_s[MM_RT * 16];
   constexpr int KT = H / 32, KG = H / 128;
-  const int RB = (a.R + 63) / 64, CB = (a.VT + 15) / 16;
+  const int RB = (a.R + 63) / 64, CB = (a.VT + 4 * CT - 1) / (4 * CT);
   const MmMap m = mm_map(RB, CB, 1);
   if (!m.ok) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -259,11 +269,11 @@ __global__ __launch_bounds__(256) void k_head_mm(HeadMM a) {
   const int mt_ld = min(m.rb * MM_RT + wave, MT - 1);
   const uint16_t* ap = a.af + (size_t)mt_ld * KT * 1024 + lane * 8;
   // vocab tiles of this wave (tiles past the last repeat it and are masked)
-  const int vt0 = m.cb * 16 + wave * MM_CT;
-  const uint8_t* qp[MM_CT];
-  const uint8_t* sp[MM_CT];
+  const int vt0 = (m.cb * MM_WAVES + wave) * CT;
+  const uint8_t* qp[CT];
+  const uint8_t* sp[CT];
 #pragma unroll
-  for (int c = 0; c < MM_CT; ++c) {
+  for (int c = 0; c < CT; ++c) {
     const int vt = min(vt0 + c, a.VT - 1);
     qp[c] = a.hq + (size_t)vt * KG * 1024 + lane * 16;
     sp[c] = a.hs + (size_t)vt * KG * 256 + lane * 4;
@@ -289,18 +299,18 @@ __global__ __launch_bounds__(256) void k_head_mm(HeadMM a) {
     }
   };
 
-  f32x4 acc[MM_RT][MM_CT];
+  f32x4 acc[MM_RT][CT];
 #pragma unroll
   for (int r = 0; r < MM_RT; ++r)
 #pragma unroll
-    for (int c = 0; c < MM_CT; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < CT; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 ar[8], qr[MM_CT];
-  uint32_t sr[MM_CT];
+  u32x4 ar[8], qr[CT];
+  uint32_t sr[CT];
 #pragma unroll
   for (int j = 0; j < 8; ++j) ar[j] = *reinterpret_cast<const u32x4*>(ap + j * 512);
 #pragma unroll
-  for (int c = 0; c < MM_CT; ++c) {
+  for (int c = 0; c < CT; ++c) {
     qr[c] = *reinterpret_cast<const u32x4*>(qp[c]);
     sr[c] = *reinterpret_cast<const uint32_t*>(sp[c]);
   }
@@ -309,28 +319,28 @@ __global__ __launch_bounds__(256) void k_head_mm(HeadMM a) {
 
   for (int kg = 0; kg < KG; ++kg) {
     const int kn = min(kg + 1, KG - 1);
-    u32x4 an[8], qn[MM_CT];
-    uint32_t sn[MM_CT];
+    u32x4 an[8], qn[CT];
+    uint32_t sn[CT];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       an[j] = *reinterpret_cast<const u32x4*>(ap + (size_t)kn * 4096 + j * 512);
 #pragma unroll
-    for (int c = 0; c < MM_CT; ++c) {
+    for (int c = 0; c < CT; ++c) {
       qn[c] = *reinterpret_cast<const u32x4*>(qp[c] + (size_t)kn * 1024);
       sn[c] = *reinterpret_cast<const uint32_t*>(sp[c] + (size_t)kn * 256);
     }
     const int buf = kg & 1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      f16x8 w[MM_CT];
+      f16x8 w[CT];
 #pragma unroll
-      for (int c = 0; c < MM_CT; ++c) w[c] = mm_nvfp4x8(qr[c][i], (sr[c] >> (8 * i)) & 0xffu);
+      for (int c = 0; c < CT; ++c) w[c] = mm_nvfp4x8(qr[c][i], (sr[c] >> (8 * i)) & 0xffu);
 #pragma unroll
       for (int r = 0; r < MM_RT; ++r) {
         const f16x8 ah = __builtin_bit_cast(f16x8, sa[buf][r * 8 + 2 * i][lane]);
         const f16x8 al = __builtin_bit_cast(f16x8, sa[buf][r * 8 + 2 * i + 1][lane]);
 #pragma unroll
-        for (int c = 0; c < MM_CT; ++c) {
+        for (int c = 0; c < CT; ++c) {
           acc[r][c] = mfma_f16(ah, w[c], acc[r][c]);
           acc[r][c] = mfma_f16(al, w[c], acc[r][c]);
         }
@@ -338,7 +348,7 @@ __global__ __launch_bounds__(256) void k_head_mm(HeadMM a) {
     }
     if (kg + 1 < KG) stage(an, buf ^ 1);
 #pragma unroll
-    for (int c = 0; c < MM_CT; ++c) {
+    for (int c = 0; c < CT; ++c) {
       qr[c] = qn[c];
       sr[c] = sn[c];
     }
@@ -351,7 +361,7 @@ __global__ __launch_bounds__(256) void k_head_mm(HeadMM a) {
   for (int r = 0; r < MM_RT; ++r) {
     unsigned long long best[4] = {0ull, 0ull, 0ull, 0ull};
 #pragma unroll
-    for (int c = 0; c < MM_CT; ++c) {
+    for (int c = 0; c < CT; ++c) {
       const int voc = (vt0 + c) * 16 + (lane & 15);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -400,7 +410,9 @@ void launch_head_mm(hipStream_t st, const uint16_t* af, int R, const DevWeights&
   a.VT = d.VT;
   a.logits = logits;
   a.keys = keys;
-  k_head_mm<<<mm_grid(R, (d.VT + 15) / 16, 1), 256, 0, st>>>(a);
+  // 256 vocabulary rows per workgroup at every row count (narrower tiles
+  // measured slower at 64 rows)
+  k_head_mm<4><<<mm_grid(R, (d.VT + 15) / 16, 1), 256, 0, st>>>(a);
 }
 
 }  // namespace kd
