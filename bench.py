@@ -23,10 +23,10 @@ sys.path.insert(0, ROOT)
 METRIC = "drafter rounds/s & draft tokens/s at B streams; % of HBM roofline"
 HBM_PEAK_GBS = 8000.0
 # the kernel of each small-batch path: path 2 launches k_small_phase once per
-# phase (30 launches per 4-layer round), paths 3 and 4 run the whole round in
+# phase (30 launches per 4-layer round), path 3 runs the whole round in
 # one launch
-KERNEL_NAME = {2: "kd::k_small_phase", 3: "kd::k_small_mega", 4: "kd::k_stream"}
-LAUNCHES_PER_ROUND = {2: 30, 3: 1, 4: 1}
+KERNEL_NAME = {2: "kd::k_small_phase", 3: "kd::k_small_mega"}
+LAUNCHES_PER_ROUND = {2: 30, 3: 1}
 
 
 def algorithmic_bytes(dims, lens, streams):
@@ -127,8 +127,7 @@ def main():
                          "exit: the calibration kernel for HBM byte counters")
     ap.add_argument("--path", type=int, default=0,
                     help="0 automatic; 1 general multi-kernel; 2 small-batch phases as "
-                         "separate launches; 3 small-batch persistent kernel; 4 streamed persistent "
-                         "kernel (experimental)")
+                         "separate launches; 3 small-batch persistent kernel")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -209,7 +208,7 @@ def main():
                                   f"block-FP8 body, NVFP4 head (60,614 rows)",
                       "streams": B, "draft_tokens_per_round": 4 * B,
                       "path": {1: "general multi-kernel", 2: "small-batch phases, one launch each",
-                               3: "small-batch persistent kernel", 4: "streamed persistent kernel"}[path]},
+                               3: "small-batch persistent kernel"}[path]},
            "draft_tokens_per_s": round(4 * B * rounds_s, 1),
            "bytes_per_round": ab, "hbm_roofline_frac": round(achieved / HBM_PEAK_GBS, 4),
            "wall_s": round(wall, 3), "roofline": roofline}

@@ -33,8 +33,6 @@ struct kd_ctx {
   bool small_ok = false;     // the window fits the small path's attention phase
   unsigned epoch = 0;        // grid barriers completed by persistent launches so far
   bool mega_ok = false;      // persistent cooperative kernel available
-  bool stream_ok = false;    // streamed persistent kernel available
-  int nch_stream = 0;        // attention chunks of the window on the streamed path
   int path = 0;              // 0 auto, 1 general, 2 small per-phase, 3 small persistent,
                              // 4 streamed persistent
   kd::SmallArgs* args_dev = nullptr;   // device copy of the small-path arguments
@@ -342,16 +340,12 @@ kd_status kd_create(const kd_config* cfg, void* hip_stream, kd_ctx** out) {
   // (stream, head) per workgroup, so the grid must cover every pair
   c->small_ok = c->G >= kd::SB_MAX * kd::NH;
   if (ok && c->small_ok) {
-    // chunk partials of one (stream, head) must not share a 128-byte line with
-    // another's (different workgroups merge them): whole groups of 8 chunks
-    c->nch_stream = ((cfg->window + kd::stream_chunk_keys() - 1) / kd::stream_chunk_keys() + 7) / 8 * 8;
-    ok = dev_alloc(c->work_allocs, &c->small_mem,
-                   kd::small_bytes(std::max(w.att_nch, c->nch_stream))) &&
+    ok = dev_alloc(c->work_allocs, &c->small_mem, kd::small_bytes(w.att_nch)) &&
          dev_alloc(c->work_allocs, &c->args_dev, 1) &&
          hipHostMalloc((void**)&c->args_host, sizeof(kd::SmallArgs), hipHostMallocDefault) ==
              hipSuccess;
     if (ok) {
-      kd::small_carve(c->small_mem, std::max(w.att_nch, c->nch_stream), &c->small);
+      kd::small_carve(c->small_mem, w.att_nch, &c->small);
       ok = hipMemset(c->small.bar, 0, 20 * 32 * sizeof(unsigned)) == hipSuccess &&
            hipMemset(c->small.att_cnt, 0, kd::NL * kd::SB_MAX * kd::NH * 32 * sizeof(unsigned)) ==
                hipSuccess &&
@@ -366,7 +360,6 @@ kd_status kd_create(const kd_config* cfg, void* hip_stream, kd_ctx** out) {
     return KD_ERR_OOM;
   }
   c->mega_ok = c->small_ok && have_prop && prop.cooperativeLaunch && kd::small_mega_occupancy() >= 1;
-  c->stream_ok = c->small_ok && have_prop && prop.cooperativeLaunch && kd::stream_occupancy() >= 1;
   (void)hipGetLastError();
   *out = c;
   return KD_OK;
@@ -522,7 +515,6 @@ kd_status kd_round(kd_ctx* c, int B, const void* taps, const int32_t* anchor, co
   if (path == 0) path = B <= kd::SB_MAX && c->small_ok ? 2 : 1;
   if (!c->small_ok) path = 1;
   if (path == 3 && !c->mega_ok) path = 2;
-  if (path == 4 && !c->stream_ok) path = c->mega_ok ? 3 : 2;
   if (path != 1 && B > kd::SB_MAX) path = 1;
   c->last_path = path;
   if (path != 1) {
@@ -535,7 +527,7 @@ kd_status kd_round(kd_ctx* c, int B, const void* taps, const int32_t* anchor, co
     a.window = c->cfg.window;
     // partial slots per (stream, head), padded to whole 128-byte lines of the
     // per-chunk max and sum (8 chunks): different pairs never share a line
-    a.nch = path == 4 ? c->nch_stream : (w.att_nch + 7) / 8 * 8;
+    a.nch = (w.att_nch + 7) / 8 * 8;
     a.eps = eps;
     a.theta = c->cfg.rope_theta;
     a.taps = static_cast<const uint16_t*>(taps);
@@ -561,11 +553,7 @@ kd_status kd_round(kd_ctx* c, int B, const void* taps, const int32_t* anchor, co
       c->args_valid = true;
     }
     const int np = kd::small_phase_count(a.nl);
-    if (path == 4) {
-      const hipError_t e = kd::launch_stream(st, c->args_dev, c->G, c->epoch);
-      if (e != hipSuccess) return hip_fail(c, e, "streamed round launch");
-      c->epoch += (unsigned)(kd::small_phase_count(a.nl) - 1);
-    } else if (path == 3) {
+    if (path == 3) {
       const hipError_t e = kd::launch_small_mega(st, c->args_dev, c->G, c->epoch);
       if (e != hipSuccess) return hip_fail(c, e, "persistent round launch");
       c->epoch += (unsigned)(kd::small_phase_count(a.nl) - 1);
@@ -724,12 +712,10 @@ kd_status kd_debug_buffers(kd_ctx* c, const float** hidden, const float** fused)
 
 kd_status kd_debug_set_path(kd_ctx* c, int path) {
   if (!c) return KD_ERR_ARG;
-  if (path < 0 || path > 4) return fail(c, KD_ERR_ARG, "path must be 0..4");
+  if (path < 0 || path > 3) return fail(c, KD_ERR_ARG, "path must be 0..3");
   if (path >= 2 && !c->small_ok)
     return fail(c, KD_ERR_UNSUPPORTED, "the window is too long for the small-batch path");
   if (path == 3 && !c->mega_ok) return fail(c, KD_ERR_UNSUPPORTED, "no cooperative launch");
-  if (path == 4 && !c->stream_ok)
-    return fail(c, KD_ERR_UNSUPPORTED, "the streamed round kernel cannot be made resident");
   c->path = path;
   return KD_OK;
 }

@@ -23,26 +23,29 @@ __host__ __device__ inline int xs_d(int l) { return 3 * l + 2; }
 
 // Buffers written at most once per round (so no cache ever holds a stale
 // copy within a launch); every buffer starts on a 256-byte boundary and no two
-// phases write into the same 128-byte line.
+// phases write into the same 128-byte line. Activations that only enter the
+// matrix cores are stored as f16 bits (fh, sp, xg, ss, o, h); the residual
+// stream, its sums of squares and the attention inputs stay fp32.
 template <template <class> class P>
 struct SmallBufsT {
   P<float> f;                  // [SB][H]   fused tap state
+  P<uint16_t> fh;              // [SB][H]   the same, f16 (matrix input)
   P<float> fce;                // [SB][H]   fc (embedding half) . E[anchor]
   P<float> pb;                 // [3SB][RK] B_p . E[pred]
-  P<float> sp;                 // [3SB][RK] silu(A_p f + B_p E[pred])
+  P<uint16_t> sp;              // [3SB][RK] silu(A_p f + B_p E[pred]), f16
   P<float> rope;               // [SR][64][2] cos, sin at the block positions
   P<float> x[NXS];             // [SR][H]   residual stream stages
-  P<float> xg[NXS];            // [SR][H]   the stage times the RMSNorm gain of its consumer
+  P<uint16_t> xg[NXS];         // [SR][H]   the stage times the RMSNorm gain of its consumer, f16
   P<float> ssq[NXS];           // [SR][HT]  sum of squares of each 16-column tile
-  P<float> ss[NL];             // [3SB][RK] spine hidden (layers 1..3)
+  P<uint16_t> ss[NL];          // [3SB][RK] spine hidden (layers 1..3), f16
   P<float> q[NL];              // [SR][H]   post-RoPE, natural head-major layout
   P<float> k[NL];
   P<float> v[NL];
   P<float> am[NL];             // [SB][NH][nch][4] chunk max (log2 units)
   P<float> al[NL];             // [SB][NH][nch][4] chunk sum of 2^(s - max)
   P<float> ao[NL];             // [SB][NH][nch][4][DH]
-  P<float> o[NL];              // [SR][H]   merged attention output
-  P<float> h[NL];              // [SR][FF]  silu(gate) * up
+  P<uint16_t> o[NL];           // [SR][H]   merged attention output, f16
+  P<uint16_t> h[NL];           // [SR][FF]  silu(gate) * up, f16
   P<unsigned long long> cand;  // [MAX_G][SR] per-workgroup argmax candidates
   P<unsigned> bar;             // control words, 32 u32 apart: [0..15] arrival counters of
                                // the 16-workgroup groups, [18] error, [19] head counter
@@ -84,11 +87,5 @@ void launch_small_phase(hipStream_t st, const SmallArgs* dev_args, int G, int ph
 hipError_t launch_small_mega(hipStream_t st, const SmallArgs* dev_args, int G, unsigned epoch0);
 int small_mega_occupancy();
 
-// The streamed persistent round (kd_stream.hip): same arguments and buffers;
-// SmallArgs::nch must be the number of stream_chunk_keys()-key chunks of the
-// window. epoch0 as for launch_small_mega (the same barrier count per launch).
-hipError_t launch_stream(hipStream_t st, const SmallArgs* dev_args, int G, unsigned epoch0);
-int stream_occupancy();
-int stream_chunk_keys();
 
 }  // namespace kd

@@ -89,6 +89,11 @@ __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlan
 __device__ __forceinline__ void st_wt(gptr<float> p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// f16 bits of v (round to nearest even), written through like st_wt.
+__device__ __forceinline__ void st_wt_h(gptr<uint16_t> p, float v) {
+  __hip_atomic_store(p, __builtin_bit_cast(uint16_t, (_Float16)v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ void st_wt64(gptr<unsigned long long> p, unsigned long long v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -118,6 +123,16 @@ __device__ __forceinline__ bf16x8 e4m3x8_bf16(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// e4m3 pairs -> f16 pairs with unit scale (exact: e4m3 values lie within
+// f16's normal range and carry at most 4 significant bits).
+__device__ __forceinline__ f16x8 e4m3x8_f16(uint32_t lo, uint32_t hi) {
+  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
+  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
+  const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
+  const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
+  return f16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
 // 8 e2m1 codes (even element in the low nibble) times an e4m3 block scale,
 // exactly in f16: e2m1 decoded with unit scale, then one packed f16 multiply
 // per pair (<= 6 significant bits, within f16's normal range).
@@ -137,14 +152,6 @@ __device__ __forceinline__ void split_bf16(const float* v, bf16x8& hi, bf16x8& l
     const __bf16 h = (__bf16)v[i];
     hi[i] = h;
     lo[i] = (__bf16)(v[i] - (float)h);
-  }
-}
-__device__ __forceinline__ void split_f16(const float* v, f16x8& hi, f16x8& lo) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const _Float16 h = (_Float16)v[i];
-    hi[i] = h;
-    lo[i] = (_Float16)(v[i] - (float)h);
   }
 }
 
@@ -340,7 +347,9 @@ __device__ __forceinline__ void load_w(WRegs<NT, KBS>& r, Mat& W, int tile0, int
     }
 }
 
-// Activation rows of the A operand (bf16 rows are exact: the lo plane is 0).
+// Activation rows of the A operand: bf16 (the tapped states and embedding
+// rows, taken exactly on the bf16 matrix cores) or f16 (activations the round
+// produces, on the f16 matrix cores).
 struct ASrc {
   gptr<const void> base;
   int ld;               // elements per row
@@ -359,80 +368,53 @@ __device__ __forceinline__ size_t a_row(const ASrc& A, int r) {
   }
 }
 
-// Issues the loads of one 64-input block of the lane's row (no conversion).
-template <bool ABF>
-__device__ __forceinline__ void a_issue(const ASrc& A, int kb, u32x4 (&raw)[4]) {
+// Issues the loads of one 64-input block of the lane's row: 8 values at
+// inputs 8 (lane / 16) .. + 8 of each of the block's two 32-input halves.
+__device__ __forceinline__ void a_issue(const ASrc& A, int kb, u32x4 (&raw)[2]) {
   // rows past R repeat row R-1; they only feed output rows that are discarded
   const int lane = threadIdx.x & 63, r = min(lane & 15, A.R - 1);
   const int c0 = (kb - A.kb_off) * 64 + 8 * (lane >> 4);
   const size_t row = a_row(A, r);
-  if (ABF) {
-    auto p = static_cast<gptr<const uint16_t>>(A.base) + row * A.ld + c0;
-    raw[0] = *reinterpret_cast<gptr<const u32x4>>(p);
-    raw[1] = *reinterpret_cast<gptr<const u32x4>>(p + 32);
-  } else {
-    auto p = static_cast<gptr<const float>>(A.base) + row * A.ld + c0;
-    raw[0] = *reinterpret_cast<gptr<const u32x4>>(p);
-    raw[1] = *reinterpret_cast<gptr<const u32x4>>(p + 4);
-    raw[2] = *reinterpret_cast<gptr<const u32x4>>(p + 32);
-    raw[3] = *reinterpret_cast<gptr<const u32x4>>(p + 36);
-  }
-}
-
-template <bool ABF>
-__device__ __forceinline__ void a_convert(const u32x4 (&raw)[4], bf16x8& h0, bf16x8& l0,
-                                          bf16x8& h1, bf16x8& l1) {
-  if (ABF) {
-    const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-    h0 = __builtin_bit_cast(bf16x8, raw[0]);
-    h1 = __builtin_bit_cast(bf16x8, raw[1]);
-    l0 = l1 = z;
-  } else {
-    float v0[8], v1[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v0[i] = u2f(raw[0][i]);
-      v0[4 + i] = u2f(raw[1][i]);
-      v1[i] = u2f(raw[2][i]);
-      v1[4 + i] = u2f(raw[3][i]);
-    }
-    split_bf16(v0, h0, l0);
-    split_bf16(v1, h1, l1);
-  }
+  auto p = static_cast<gptr<const uint16_t>>(A.base) + row * A.ld + c0;
+  raw[0] = *reinterpret_cast<gptr<const u32x4>>(p);
+  raw[1] = *reinterpret_cast<gptr<const u32x4>>(p + 32);
 }
 
 // Partial products of each wave into LDS: red[((wave*NT + i)*4 + e)*64 + lane].
-// The A loads of up to C blocks are in flight together.
+// The A loads of up to C blocks are in flight together. ABF: bf16 activations
+// (weights decoded to bf16), else f16 (weights decoded to f16); both decodes
+// are exact.
 template <int NT, int KBS, int AW, bool ABF>
 __device__ __forceinline__ void gemm_compute(const WRegs<NT, KBS>& r, const ASrc& A, int kb0,
                                              lds_f red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  constexpr int C = ABF ? (KBS < 8 ? KBS : 8) : (NT >= 3 ? 3 : (KBS <= 6 ? KBS : 4));
+  constexpr int C = KBS < 8 ? KBS : 8;
   f32x4 acc[NT];
 #pragma unroll
   for (int i = 0; i < NT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (wave < AW) {
 #pragma unroll
     for (int c0 = 0; c0 < KBS; c0 += C) {
-      u32x4 raw[C][4];
+      u32x4 raw[C][2];
 #pragma unroll
       for (int j = 0; j < C; ++j)
-        if (c0 + j < KBS) a_issue<ABF>(A, kb0 + wave * KBS + c0 + j, raw[j]);
+        if (c0 + j < KBS) a_issue(A, kb0 + wave * KBS + c0 + j, raw[j]);
 #pragma unroll
       for (int j = 0; j < C; ++j) {
         if (c0 + j < KBS) {
-          bf16x8 h0, l0, h1, l1;
-          a_convert<ABF>(raw[j], h0, l0, h1, l1);
 #pragma unroll
           for (int i = 0; i < NT; ++i) {
             const u32x4 wv = r.w[i][c0 + j];
-            const bf16x8 w0 = e4m3x8_bf16(wv.x, wv.y);
-            const bf16x8 w1 = e4m3x8_bf16(wv.z, wv.w);
             f32x4 t = {0.f, 0.f, 0.f, 0.f};
-            t = mfma_bf16(h0, w0, t);
-            t = mfma_bf16(l0, w0, t);
-            t = mfma_bf16(h1, w1, t);
-            t = mfma_bf16(l1, w1, t);
+            if (ABF) {
+              t = mfma_bf16(__builtin_bit_cast(bf16x8, raw[j][0]), e4m3x8_bf16(wv.x, wv.y), t);
+              t = mfma_bf16(__builtin_bit_cast(bf16x8, raw[j][1]), e4m3x8_bf16(wv.z, wv.w), t);
+            } else {
+              t = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, raw[j][0]),
+                                                         e4m3x8_f16(wv.x, wv.y), t, 0, 0, 0);
+              t = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, raw[j][1]),
+                                                         e4m3x8_f16(wv.z, wv.w), t, 0, 0, 0);
+            }
             acc[i] += r.s[i][c0 + j] * t;
           }
         }
@@ -529,7 +511,7 @@ __device__ __forceinline__ void put_x(Bufs& s, int stage, gptr<const float> gain
   const float q = tile_ssq(x);
   if (ok) {
     st_wt(&s.x[stage][row * H + col], x);
-    st_wt(&s.xg[stage][row * H + col], x * gain[col]);
+    st_wt_h(&s.xg[stage][row * H + col], x * gain[col]);
     if (n == 0) st_wt(&s.ssq[stage][row * HT + tile], q);
   }
 }
@@ -576,7 +558,10 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_pre0(Args& a_, lds
       const ASrc A{a.taps, NTAP * H, 0, nullptr, 0, B};
       gemm_unit<1, 15, 8, true>(a, sy, false, d.fuse, u, 1, 0, A, red, no_rms(),
                                 [&](int, int m, int n, float v) {
-                                  if (m < B) st_wt(&s.f[m * H + u * 16 + n], v);
+                                  if (m < B) {
+                                    st_wt(&s.f[m * H + u * 16 + n], v);
+                                    st_wt_h(&s.fh[m * H + u * 16 + n], v);
+                                  }
                                 });
     } else if (u < n_fuse + n_fce) {
       const int t = u - n_fuse;
@@ -607,7 +592,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_pre1(Args& a_, lds
   bool first = sync;
   for (int u = wg; u < HT + RK / 16; u += G) {
     if (u < HT) {
-      const ASrc A{s.f, H, 0, nullptr, 0, B};
+      const ASrc A{s.fh, H, 0, nullptr, 0, B};
       gemm_unit<1, 5, 8, false>(a, sy, first, d.fc, u, 1, 0, A, red, no_rms(),
                                 [&](int, int m, int n, float v) {
                                   const int col = u * 16 + n;
@@ -616,12 +601,12 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_pre1(Args& a_, lds
                                 });
     } else {
       const int t = u - HT;
-      const ASrc A{s.f, H, 1, nullptr, 0, 3 * B};
+      const ASrc A{s.fh, H, 1, nullptr, 0, 3 * B};
       gemm_unit<1, 5, 8, false>(a, sy, first, d.pred_ab, t, 1, 0, A, red, no_rms(),
                                 [&](int, int m, int n, float v) {
                                   if (m < 3 * B) {
                                     const int c = t * 16 + n;
-                                    st_wt(&s.sp[m * RK + c], silu(v + s.pb[m * RK + c]));
+                                    st_wt_h(&s.sp[m * RK + c], silu(v + s.pb[m * RK + c]));
                                   }
                                 });
     }
@@ -679,7 +664,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_sa(Args& a_, int l
     gemm_unit<1, 5, 8, false>(a, sy, first, L.sa, u, 1, 0, A, red,
                               RmsRows{s.ssq[src], 3 * B, 2, a.eps, inv, {}},
                               [&](int, int m, int n, float v) {
-                                if (m < 3 * B) st_wt(&s.ss[l][m * RK + u * 16 + n], silu(v * inv[m]));
+                                if (m < 3 * B) st_wt_h(&s.ss[l][m * RK + u * 16 + n], silu(v * inv[m]));
                               });
     first = false;
   }
@@ -721,7 +706,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_su(Args& a_, int l
       if (c < 16) {
         const float x = s.x[src][row * H + col];
         st_wt(&s.x[dst][row * H + col], x);
-        st_wt(&s.xg[dst][row * H + col], x * gain[col]);
+        st_wt_h(&s.xg[dst][row * H + col], x * gain[col]);
       } else {
         st_wt(&s.ssq[dst][row * HT + u], s.ssq[src][row * HT + u]);
       }
@@ -1000,7 +985,7 @@ __device__ __attribute__((noinline, not_tail_called)) void attn_merge(Args& a_, 
       Ls += f;
       O += f * vv[i];
     }
-  st_wt(&s.o[l][(b * 4 + j) * H + h * DH + dd], O / Ls);
+  st_wt_h(&s.o[l][(b * 4 + j) * H + h * DH + dd], O / Ls);
 }
 
 // Reads the lane's 4 key and 4 value blocks (at kva, 1 KB apart) and waits
@@ -1569,7 +1554,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_gu(Args& a_, int l
           const int t = u * NT + i;
           const float val = m < R ? v * inv[m] : 0.f;
           const float up = __shfl_xor(val, 8, 64);
-          if (m < R && n < 8) st_wt(&s.h[l][m * FF + 8 * t + n], silu(val) * up);
+          if (m < R && n < 8) st_wt_h(&s.h[l][m * FF + 8 * t + n], silu(val) * up);
         });
     first = false;
   }
@@ -1627,7 +1612,8 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_head(Args& a_, lds
   // issue order)
   rms.issue();
   const int ar = min(lane & 15, R - 1);
-  f32x4 raw[3][4][2];
+  // A operand (g_o * x in f16) for this wave's inputs, kept for all units
+  f16x8 ah[3][4];
 #pragma unroll
   for (int gg = 0; gg < 3; ++gg)
 #pragma unroll
@@ -1635,9 +1621,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_head(Args& a_, lds
       // rows past R repeat row R-1 (their logits are discarded); slot 2 of a
       // wave with 2 input groups repeats group 1 and is skipped
       const int c0 = (kg0 + min(gg, ng - 1)) * 128 + t * 32 + 8 * (lane >> 4);
-      auto p = s.xg[src] + ar * H + c0;
-      raw[gg][t][0] = *reinterpret_cast<gptr<const f32x4>>(p);
-      raw[gg][t][1] = *reinterpret_cast<gptr<const f32x4>>(p + 4);
+      ah[gg][t] = *reinterpret_cast<gptr<const f16x8>>(s.xg[src] + ar * H + c0);
     }
   // two register sets of codes and scales alternate (an unrolled pair of
   // units, so that no copy between them makes the compiler wait for loads in
@@ -1646,20 +1630,6 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_head(Args& a_, lds
   uint32_t sa[HEAD_NT][3], sb[HEAD_NT][3];
   const int ulast = max(nunits - 1, 0);
   load_unit(min(wg, ulast), qa, sa);
-  // A operand (g_o * x, hi/lo f16) for this wave's inputs, kept for all units
-  f16x8 ah[3][4], al[3][4];
-#pragma unroll
-  for (int gg = 0; gg < 3; ++gg)
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      float v[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[e] = raw[gg][t][0][e];
-        v[4 + e] = raw[gg][t][1][e];
-      }
-      split_f16(v, ah[gg][t], al[gg][t]);
-    }
   rms.finish();
   trace_mark(a, sy, 3);
   auto unit_body = [&](int u, const u32x4 (&q)[HEAD_NT][3], const uint32_t (&sv)[HEAD_NT][3])
@@ -1676,7 +1646,6 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_head(Args& a_, lds
           for (int i = 0; i < HEAD_NT; ++i) {
             const f16x8 w = nvfp4x8_f16(q[i][gg][t], sv[i][gg] >> (8 * t));
             acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[gg][t], w, acc[i], 0, 0, 0);
-            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[gg][t], w, acc[i], 0, 0, 0);
           }
       }
     }
@@ -1836,26 +1805,28 @@ static size_t small_layout(char* base, int nch, SmallBufs* s) {
   SmallBufs* o = s ? s : &tmp;
   size_t off = 0;
   const size_t F = sizeof(float);
+  const size_t F2 = sizeof(uint16_t);
   carve(base, off, (size_t)SB_MAX * H * F, (void**)&o->f);
+  carve(base, off, (size_t)SB_MAX * H * F2, (void**)&o->fh);
   carve(base, off, (size_t)SB_MAX * H * F, (void**)&o->fce);
   carve(base, off, (size_t)3 * SB_MAX * RK * F, (void**)&o->pb);
-  carve(base, off, (size_t)3 * SB_MAX * RK * F, (void**)&o->sp);
+  carve(base, off, (size_t)3 * SB_MAX * RK * F2, (void**)&o->sp);
   carve(base, off, (size_t)SR_MAX * (DH / 2) * 2 * F, (void**)&o->rope);
   for (int i = 0; i < NXS; ++i) {
     carve(base, off, (size_t)SR_MAX * H * F, (void**)&o->x[i]);
-    carve(base, off, (size_t)SR_MAX * H * F, (void**)&o->xg[i]);
+    carve(base, off, (size_t)SR_MAX * H * F2, (void**)&o->xg[i]);
     carve(base, off, (size_t)SR_MAX * HT * F, (void**)&o->ssq[i]);
   }
   for (int l = 0; l < NL; ++l) {
-    carve(base, off, (size_t)3 * SB_MAX * RK * F, (void**)&o->ss[l]);
+    carve(base, off, (size_t)3 * SB_MAX * RK * F2, (void**)&o->ss[l]);
     carve(base, off, (size_t)SR_MAX * H * F, (void**)&o->q[l]);
     carve(base, off, (size_t)SR_MAX * H * F, (void**)&o->k[l]);
     carve(base, off, (size_t)SR_MAX * H * F, (void**)&o->v[l]);
     carve(base, off, (size_t)SB_MAX * NH * nch * 4 * F, (void**)&o->am[l]);
     carve(base, off, (size_t)SB_MAX * NH * nch * 4 * F, (void**)&o->al[l]);
     carve(base, off, (size_t)SB_MAX * NH * nch * 4 * DH * F, (void**)&o->ao[l]);
-    carve(base, off, (size_t)SR_MAX * H * F, (void**)&o->o[l]);
-    carve(base, off, (size_t)SR_MAX * FF * F, (void**)&o->h[l]);
+    carve(base, off, (size_t)SR_MAX * H * F2, (void**)&o->o[l]);
+    carve(base, off, (size_t)SR_MAX * FF * F2, (void**)&o->h[l]);
   }
   carve(base, off, (size_t)MAX_G * SR_MAX * sizeof(unsigned long long), (void**)&o->cand);
   carve(base, off, (size_t)20 * 32 * sizeof(unsigned), (void**)&o->bar);

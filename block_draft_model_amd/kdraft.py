@@ -233,8 +233,7 @@ class Drafter:
 
     def debug_set_path(self, path: int):
         """0 automatic, 1 general multi-kernel, 2 small-batch phases as launches,
-        3 small-batch persistent kernel, 4 streamed persistent kernel (paths 2-4
-        only for <= 4 streams)."""
+        3 small-batch persistent kernel (paths 2-3 only for <= 4 streams)."""
         self._check(self.lib.kd_debug_set_path(self.ctx, int(path)), "kd_debug_set_path")
 
     def debug_set_trace(self, buf, phases: int) -> int:

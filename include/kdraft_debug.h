@@ -30,13 +30,13 @@ kd_status kd_debug_set_layers(kd_ctx* ctx, int n);
  * [streams][hidden]. */
 kd_status kd_debug_buffers(kd_ctx* ctx, const float** hidden, const float** fused);
 
-/* Chooses how later rounds run: 0 automatic (the persistent kernel for up to
- * 4 streams when cooperative launch is available, else one launch per phase;
- * the general multi-kernel path above 4 streams), 1 the general path,
- * 2 the small-batch phases as separate launches, 3 the small-batch persistent
- * kernel. Paths 2 and 3 apply only to rounds of at most 4 streams; larger
- * rounds use path 1. KD_ERR_UNSUPPORTED if 3 is asked for without
- * cooperative launch. */
+/* Chooses how later rounds run: 0 automatic (the small-batch phases as
+ * separate launches for up to 4 streams, the general multi-kernel path above
+ * 4 streams), 1 the general path, 2 the small-batch phases as separate
+ * launches, 3 the small-batch persistent kernel. Paths 2 and 3 apply only to
+ * rounds of at most 4 streams; larger rounds use path 1. KD_ERR_ARG for a
+ * path outside 0..3; KD_ERR_UNSUPPORTED if 3 is asked for without cooperative
+ * launch. */
 kd_status kd_debug_set_path(kd_ctx* ctx, int path);
 
 /* The path the last round ran on (1, 2 or 3; 0 before any round). */

@@ -14,7 +14,7 @@ import torch
 import oracle
 import synth
 from block_draft_model_amd import kdraft
-from gpu_common import Harness, compare, log, require_gpu
+from gpu_common import GAP_MIN, Harness, compare, log, require_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -73,7 +73,7 @@ def test_probe_nvfp4_decoder_is_exact():
     assert np.array_equal(got[fin], oracle.round_bf16(exact[fin]))
 
 
-PATHS = [1, 2, 3, 4]   # general multi-kernel, small-batch phases, small-batch persistent, streamed
+PATHS = [1, 2, 3]   # general multi-kernel, small-batch phases, small-batch persistent
 
 
 @pytest.mark.parametrize("path", PATHS)
@@ -121,7 +121,7 @@ def test_round_parity_small_batches(hA, ci, path):
     compare(lg, ids, ref, rid, hA.oracle.vocab, f"{C[ci]['name']} path {path}")
 
 
-@pytest.mark.parametrize("path", [2, 3, 4])
+@pytest.mark.parametrize("path", [2, 3])
 def test_small_path_adapters_gains_and_edges(hC, path):
     """Active spine and predecessor adapters, random gains, and context
     lengths 0, 1, a chunk boundary + 1 and past the ring, on the <= 4-stream path."""
@@ -171,9 +171,12 @@ def test_small_paths_agree_bitwise_and_are_deterministic(hC):
 def test_small_path_stream_alone_equals_stream_in_batch(hC):
     # The small-batch attention cuts each (stream, head)'s chunks where the
     # workgroups' shares of the whole batch's work end, so a stream's softmax
-    # partials are summed in a batch-dependent order: alone and in a batch
-    # agree to fp32 reassociation, and the ids wherever the top two logits are
-    # not within that noise.
+    # partials are summed in a batch-dependent order. A reassociated fp32 sum
+    # can round to the neighbouring f16 value where it becomes the next
+    # matrix input, so alone and in a batch agree to the f16-activation error
+    # (each within ~5e-4 relative L2 of the oracle, so within 2e-3 of each
+    # other), and the ids wherever the top two logits are more than the
+    # acceptance gap apart.
     cfg = dict(name="inv-small", streams=4, lens=("uniform", 10, 2048), model="C", ingest=0)
     inp = hC.inputs(cfg, base=31)
     hC.drafter.debug_set_path(0)
@@ -185,9 +188,11 @@ def test_small_path_stream_alone_equals_stream_in_batch(hC):
         one["v"] = [t[b:b + 1] for t in inp["v"]]
         one["streams"] = 1
         alone, ia = hC.run(one)
-        np.testing.assert_allclose(alone[0], batch[b], rtol=1e-4, atol=1e-4)
+        rel = np.linalg.norm(alone[0] - batch[b], axis=1) / np.linalg.norm(batch[b], axis=1)
+        log(f"stream {b} alone vs in batch: max rel L2 {rel.max():.2e}")
+        assert rel.max() <= 2e-3
         top2 = np.sort(batch[b], axis=1)[:, -2:]
-        clear = (top2[:, 1] - top2[:, 0]) > 1e-3
+        clear = (top2[:, 1] - top2[:, 0]) > GAP_MIN
         assert np.array_equal(ia[0][clear], ib[b][clear])
 
 
