@@ -684,6 +684,12 @@ kd_status kd_probe_decode_e4m3(uint16_t* out) {
   return hipDeviceSynchronize() == hipSuccess ? KD_OK : KD_ERR_HIP;
 }
 
+kd_status kd_probe_decode_e4m3_f16(uint16_t* out) {
+  if (!out) return KD_ERR_ARG;
+  kd::launch_probe_e4m3_f16(nullptr, out);
+  return hipDeviceSynchronize() == hipSuccess ? KD_OK : KD_ERR_HIP;
+}
+
 kd_status kd_probe_decode_nvfp4(uint16_t* out) {
   if (!out) return KD_ERR_ARG;
   kd::launch_probe_nvfp4(nullptr, out);

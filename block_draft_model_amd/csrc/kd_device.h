@@ -3,13 +3,13 @@
 // Data layouts shared by the kernels:
 //
 //  * Activation fragments ("afrag"): an activation matrix X[R][K] (fp32 in
-//    value) is stored as two bf16 planes, hi = bf16(x) and lo = bf16(x - hi),
-//    arranged as the A operand of v_mfma_f32_16x16x32_bf16. For row tile mt
-//    (16 rows) and k tile t (32 inputs) the plane holds 64 lanes x 8 bf16;
-//    lane l, element e is X[16*mt + l%16][32*t + 8*(l/16) + e]. Element offset
-//    of (mt, t): ((mt*KT + t)*2 + plane) * 512 with KT = K/32. hi + lo carries
-//    ~16 significant bits, so each product with an exact bf16 weight keeps
-//    fp32-level accuracy at twice the (cheap) matrix-core work.
+//    value) is stored in f16 (round to nearest even), arranged as the A
+//    operand of v_mfma_f32_16x16x32_f16. For row tile mt (16 rows) and k tile
+//    t (32 inputs) the fragment holds 64 lanes x 8 f16; lane l, element e is
+//    X[16*mt + l%16][32*t + 8*(l/16) + e]. Element offset of (mt, t):
+//    (mt*KT + t) * 512 with KT = K/32. f16 keeps 11 significant bits; the
+//    weights it multiplies are decoded exactly into f16 and the products are
+//    summed in fp32.
 //
 //  * Block-FP8 weights W[N][K] are repacked once at load to the B operand of
 //    the same instruction: [N/16][K/64][64 lanes][16 bytes]. Lane l's 16 bytes
@@ -61,45 +61,42 @@ __device__ __forceinline__ uint32_t pack_hi16(float e0, float e1) {
   return __builtin_amdgcn_perm(f2u(e1), f2u(e0), 0x07060302u);
 }
 
-// 8 e4m3 codes (little-endian in two dwords) -> 8 exact bf16 values.
-// v_cvt_pk_f32_fp8 decodes OCP e4m3 on gfx950; every e4m3 value has at most
-// 4 significant bits, so the bf16 truncation below is exact.
-__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
-  f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
-  f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
-  f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
-  f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// 8 e4m3 codes (little-endian in two dwords) -> 8 exact bf16 values
+// (gfx950's scaled conversion with a unit scale).
+__device__ __forceinline__ bf16x8 e4m3x8_bf16(uint32_t lo, uint32_t hi) {
   u32x4 r;
-  r.x = pack_hi16(a.x, a.y);
-  r.y = pack_hi16(b.x, b.y);
-  r.z = pack_hi16(c.x, c.y);
-  r.w = pack_hi16(d.x, d.y);
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
+  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
+  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
   return __builtin_bit_cast(bf16x8, r);
 }
 
-__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
-  return __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
+// 8 e4m3 codes -> 8 exact f16 values: every e4m3 value (at most 4
+// significant bits, magnitudes 2^-9 .. 448) is an f16 normal or zero.
+__device__ __forceinline__ f16x8 e4m3x8_f16(uint32_t lo, uint32_t hi) {
+  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
+  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
+  const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
+  const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
+  return f16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
-// e2m1 nibble -> fp32, exact: magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6.
-__device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
-  uint32_t mag = c & 7u;
-  uint32_t bits = mag >= 2u ? ((((mag >> 1) + 126u) << 23) | ((mag & 1u) << 22))
-                            : (mag ? 0x3f000000u : 0u);
-  return u2f(bits | ((c & 8u) << 28));
-}
-
-// 8 e2m1 nibbles (even element in the low nibble) times an fp32 block scale
-// -> 8 bf16. e2m1 (2 significant bits) times e4m3 (4) fits bf16 exactly.
-__device__ __forceinline__ bf16x8 e2m1x8_scaled_to_bf16(uint32_t nib, float s) {
-  u32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float v0 = e2m1_to_f32((nib >> (8 * i)) & 0xfu) * s;
-    float v1 = e2m1_to_f32((nib >> (8 * i + 4)) & 0xfu) * s;
-    r[i] = pack_hi16(v0, v1);
-  }
-  return __builtin_bit_cast(bf16x8, r);
+// 8 e2m1 codes (even element in the low nibble) times their e4m3 block scale,
+// exactly in f16: e2m1 decoded with a unit scale, then one packed f16
+// multiply per pair (the product has at most 6 significant bits and lies
+// within f16's normal range).
+__device__ __forceinline__ f16x8 nvfp4x8_f16(uint32_t nib, uint32_t scode) {
+  const f16x2 s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scode, 1.0f, false);
+  const f16x2 sc = {s2.x, s2.x};
+  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(nib, 1.0f, 0) * sc;
+  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(nib, 1.0f, 1) * sc;
+  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(nib, 1.0f, 2) * sc;
+  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(nib, 1.0f, 3) * sc;
+  return f16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
 // 8 bf16 (packed in 4 dwords) -> 8 fp32.
@@ -114,35 +111,30 @@ __device__ __forceinline__ void bf16x8_to_f32(u32x4 w, float* o) {
 __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
 
-// Element offset of the hi plane of afrag(row, k); the lo plane is +512.
+// Element offset of afrag(row, k).
 __device__ __forceinline__ size_t afrag_off(int row, int k, int KT) {
   int mt = row >> 4, t = k >> 5;
   int lane = (row & 15) + 16 * ((k & 31) >> 3);
-  return ((size_t)(mt * KT + t) * 2) * 512 + lane * 8 + (k & 7);
+  return (size_t)(mt * KT + t) * 512 + lane * 8 + (k & 7);
 }
 
-// Stores 8 consecutive fp32 values X[row][k0..k0+8) (k0 % 8 == 0) as hi/lo.
+// Stores 8 consecutive fp32 values X[row][k0..k0+8) (k0 % 8 == 0) as f16.
 __device__ __forceinline__ void store_afrag8(uint16_t* af, int KT, int row, int k0, const float* v) {
-  u32x4 hi, lo;
+  f16x8 h;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t h0 = bf16_rne(v[2 * i]), h1 = bf16_rne(v[2 * i + 1]);
-    uint32_t l0 = bf16_rne(v[2 * i] - bf16_to_f32(h0));
-    uint32_t l1 = bf16_rne(v[2 * i + 1] - bf16_to_f32(h1));
-    hi[i] = h0 | (h1 << 16);
-    lo[i] = l0 | (l1 << 16);
-  }
-  size_t off = afrag_off(row, k0, KT);
-  *reinterpret_cast<u32x4*>(af + off) = hi;
-  *reinterpret_cast<u32x4*>(af + off + 512) = lo;
+  for (int i = 0; i < 8; ++i) h[i] = (_Float16)v[i];
+  *reinterpret_cast<f16x8*>(af + afrag_off(row, k0, KT)) = h;
 }
 
-// Stores 8 consecutive bf16 values (exact; lo plane zero).
+// Stores 8 consecutive bf16 values (given as bits) as f16.
 __device__ __forceinline__ void store_afrag8_bf16(uint16_t* af, int KT, int row, int k0, u32x4 bits) {
-  size_t off = afrag_off(row, k0, KT);
-  *reinterpret_cast<u32x4*>(af + off) = bits;
-  *reinterpret_cast<u32x4*>(af + off + 512) = u32x4{0u, 0u, 0u, 0u};
+  float v[8];
+  bf16x8_to_f32(bits, v);
+  store_afrag8(af, KT, row, k0, v);
 }
 
 __device__ __forceinline__ float silu(float u) { return u / (1.0f + expf(-u)); }

@@ -7,10 +7,10 @@
 //   O + residual -> RMSNorm -> SwiGLU FFN + residual] -> RMSNorm -> NVFP4 head
 //   restricted to the draft vocabulary -> argmax.
 //
-// Projections run on the matrix cores (v_mfma_f32_16x16x32_bf16): weights are
-// decoded exactly from e4m3 to bf16 in registers, activations enter as a
-// bf16 hi/lo pair, and the fp32 block scale of each 64 inputs is applied to the
-// partial sum of that block. Split-K partial sums are reduced in a fixed order
+// Projections run on the matrix cores (v_mfma_f32_16x16x32_f16): weights are
+// decoded exactly from e4m3 to f16 in registers, activations enter as f16,
+// and the fp32 block scale of each 64 inputs is applied to the partial sum of
+// that block. Split-K partial sums are reduced in a fixed order
 // by the consumer kernel, so results are deterministic.
 #include "kd_device.h"
 #include "kd_runtime.h"
@@ -48,28 +48,22 @@ __global__ __launch_bounds__(256) void k_gemm(GemmK g) {
   const bool rv = row < g.R;
   const uint8_t* wp = g.w + ((size_t)ntw * g.KB + b0) * 1024 + lane * 16;
   const float* spp = g.s + ((size_t)ntw * g.KB + b0) * 16 + (lane & 15);
-  const uint16_t* ap = g.af + ((size_t)mt * g.KT + 2 * b0) * 1024 + lane * 8;
-  const bf16x8 zero = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+  const uint16_t* ap = g.af + ((size_t)mt * g.KT + 2 * b0) * 512 + lane * 8;
+  const f16x8 zero = __builtin_bit_cast(f16x8, u32x4{0u, 0u, 0u, 0u});
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
   for (int i = 0; i < g.kbs; ++i) {
     const u32x4 wv = *reinterpret_cast<const u32x4*>(wp + (size_t)i * 1024);
     const float sc = spp[i * 16];
-    bf16x8 ah0 = zero, al0 = zero, ah1 = zero, al1 = zero;
+    f16x8 a0 = zero, a1 = zero;
     if (rv) {
-      const uint16_t* a = ap + (size_t)i * 2048;
-      ah0 = *reinterpret_cast<const bf16x8*>(a);
-      al0 = *reinterpret_cast<const bf16x8*>(a + 512);
-      ah1 = *reinterpret_cast<const bf16x8*>(a + 1024);
-      al1 = *reinterpret_cast<const bf16x8*>(a + 1536);
+      const uint16_t* a = ap + (size_t)i * 1024;
+      a0 = *reinterpret_cast<const f16x8*>(a);
+      a1 = *reinterpret_cast<const f16x8*>(a + 512);
     }
-    const bf16x8 w0 = e4m3x8_to_bf16(wv.x, wv.y);
-    const bf16x8 w1 = e4m3x8_to_bf16(wv.z, wv.w);
     f32x4 t = {0.f, 0.f, 0.f, 0.f};
-    t = mfma_bf16(ah0, w0, t);
-    t = mfma_bf16(al0, w0, t);
-    t = mfma_bf16(ah1, w1, t);
-    t = mfma_bf16(al1, w1, t);
+    t = mfma_f16(a0, e4m3x8_f16(wv.x, wv.y), t);
+    t = mfma_f16(a1, e4m3x8_f16(wv.z, wv.w), t);
     acc += sc * t;
   }
   float* out = g.part + (size_t)sp * g.R * g.N + nt * 16 + (lane & 15);
@@ -568,11 +562,7 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnK a) {
     }
     if (a.S == 1) {
       const float out = attn_block_merge(s_blk, a.vb, qrow0, j, d, M, L, O);
-      const uint32_t hi = bf16_rne(out);
-      const uint32_t lo = bf16_rne(out - bf16_to_f32(hi));
-      const size_t off = afrag_off(b * BLK + j, h * DH + d, H / 32);
-      a.af_o[off] = (uint16_t)hi;
-      a.af_o[off + 512] = (uint16_t)lo;
+      a.af_o[afrag_off(b * BLK + j, h * DH + d, H / 32)] = __builtin_bit_cast(uint16_t, (_Float16)out);
     } else {
       const size_t pb = ((size_t)(b * NH + h) * a.nch + seg) * BLK + j;
       a.po[pb * DH + d] = O;
@@ -643,11 +633,7 @@ __global__ __launch_bounds__(128) void k_attn_combine(const float* q, const floa
     }
     t += j + 1;
     const float out = O / L;
-    const uint32_t hi = bf16_rne(out);
-    const uint32_t lo = bf16_rne(out - bf16_to_f32(hi));
-    const size_t off = afrag_off(b * BLK + j, h * DH + d, H / 32);
-    af_o[off] = (uint16_t)hi;
-    af_o[off + 512] = (uint16_t)lo;
+    af_o[afrag_off(b * BLK + j, h * DH + d, H / 32)] = __builtin_bit_cast(uint16_t, (_Float16)out);
   }
 }
 
@@ -784,7 +770,7 @@ __global__ __launch_bounds__(256) void k_head(HeadK a) {
   const int vt0 = (blockIdx.x * 4 + wave) * HEAD_NV;
   if (vt0 >= a.VT) return;
   constexpr int KT = H / 32, KG = H / 128;
-  const bf16x8 zero = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+  const f16x8 zero = __builtin_bit_cast(f16x8, u32x4{0u, 0u, 0u, 0u});
   const int MT = mtiles(a.R);
   for (int mt = 0; mt < MT; ++mt) {
     f32x4 acc[HEAD_NV];
@@ -809,18 +795,11 @@ __global__ __launch_bounds__(256) void k_head(HeadK a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = kg * 4 + i;
-        bf16x8 ah = zero, al = zero;
-        if (rv) {
-          const uint16_t* ap = a.af + ((size_t)(mt * KT + t) * 2) * 512 + lane * 8;
-          ah = *reinterpret_cast<const bf16x8*>(ap);
-          al = *reinterpret_cast<const bf16x8*>(ap + 512);
-        }
+        f16x8 av = zero;
+        if (rv) av = *reinterpret_cast<const f16x8*>(a.af + (size_t)(mt * KT + t) * 512 + lane * 8);
 #pragma unroll
-        for (int v = 0; v < HEAD_NV; ++v) {
-          const bf16x8 wb = e2m1x8_scaled_to_bf16(qv[v][i], e4m3_to_f32((sv[v] >> (8 * i)) & 0xffu));
-          acc[v] = mfma_bf16(ah, wb, acc[v]);
-          acc[v] = mfma_bf16(al, wb, acc[v]);
-        }
+        for (int v = 0; v < HEAD_NV; ++v)
+          acc[v] = mfma_f16(av, nvfp4x8_f16(qv[v][i], (sv[v] >> (8 * i)) & 0xffu), acc[v]);
       }
     }
     unsigned long long best[4] = {0ull, 0ull, 0ull, 0ull};
@@ -1020,18 +999,25 @@ void launch_bump_lens(hipStream_t st, int32_t* lens, int B, int n) {
 // ---------------------------------------------------------------------------
 __global__ void k_probe_e4m3(uint16_t* out) {
   const uint32_t c = threadIdx.x;
-  const bf16x8 v = e4m3x8_to_bf16(c, 0u);
+  const bf16x8 v = e4m3x8_bf16(c, 0u);
+  out[c] = (uint16_t)(__builtin_bit_cast(u32x4, v).x & 0xffffu);
+}
+
+__global__ void k_probe_e4m3_f16(uint16_t* out) {
+  const uint32_t c = threadIdx.x;
+  const f16x8 v = e4m3x8_f16(c, 0u);
   out[c] = (uint16_t)(__builtin_bit_cast(u32x4, v).x & 0xffffu);
 }
 
 __global__ void k_probe_nvfp4(uint16_t* out) {
   const uint32_t idx = blockIdx.x * blockDim.x + threadIdx.x;
   const uint32_t s = idx >> 4, c = idx & 15u;
-  const bf16x8 v = e2m1x8_scaled_to_bf16(c, e4m3_to_f32(s));
+  const f16x8 v = nvfp4x8_f16(c, s);
   out[idx] = (uint16_t)(__builtin_bit_cast(u32x4, v).x & 0xffffu);
 }
 
 void launch_probe_e4m3(hipStream_t st, uint16_t* out) { k_probe_e4m3<<<1, 256, 0, st>>>(out); }
+void launch_probe_e4m3_f16(hipStream_t st, uint16_t* out) { k_probe_e4m3_f16<<<1, 256, 0, st>>>(out); }
 void launch_probe_nvfp4(hipStream_t st, uint16_t* out) { k_probe_nvfp4<<<16, 256, 0, st>>>(out); }
 
 }  // namespace kd

@@ -6,9 +6,9 @@
 //
 // A workgroup owns 64 rows (four 16-row tiles) and 256 output columns; wave w
 // computes columns 64w .. 64w+63 for all 64 rows. Per step, the activation
-// rows of the step's inputs are loaded once per workgroup (each wave stages
-// one row tile) and written to LDS; the weights are read by the wave that uses
-// them and decoded in registers. Steps are double-buffered: the next step's
+// rows of the step's inputs (f16 fragments) are loaded once per workgroup
+// (each wave stages one row tile) and written to LDS; the weights are read by
+// the wave that uses them and decoded exactly to f16 in registers. Steps are double-buffered: the next step's
 // loads are in flight while the current step runs on the matrix cores.
 //
 // Workgroups are laid out per XCD: workgroup i runs on XCD i % 8 (the
@@ -21,9 +21,6 @@
 #include "kd_runtime.h"
 
 namespace kd {
-
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int MM_RT = 4;                          // 16-row tiles per workgroup
 constexpr int MM_WAVES = 4;
@@ -56,32 +53,6 @@ static int mm_grid(int R, int CB, int S) {
   return 8 * RB * ((units + 7) / 8);
 }
 
-__device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
-// 8 e4m3 codes -> 8 exact bf16 values (unit scale).
-__device__ __forceinline__ bf16x8 mm_e4m3x8(uint32_t lo, uint32_t hi) {
-  u32x4 r;
-  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
-  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
-  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
-  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
-  return __builtin_bit_cast(bf16x8, r);
-}
-
-// 8 e2m1 codes (even element in the low nibble) times their e4m3 block scale,
-// exactly in f16 (a product of <= 6 significant bits within f16's range).
-__device__ __forceinline__ f16x8 mm_nvfp4x8(uint32_t nib, uint32_t scode) {
-  const f16x2 s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scode, 1.0f, false);
-  const f16x2 sc = {s2.x, s2.x};
-  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(nib, 1.0f, 0) * sc;
-  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(nib, 1.0f, 1) * sc;
-  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(nib, 1.0f, 2) * sc;
-  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(nib, 1.0f, 3) * sc;
-  return f16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
-}
-
 // ---------------------------------------------------------------------------
 // Block-FP8 projection: part[split][r][n] = sum over the split's inputs of
 // X[r][k] * W[n_off*16 + n][k]; one step is one 64-input block (the block's
@@ -89,7 +60,7 @@ __device__ __forceinline__ f16x8 mm_nvfp4x8(uint32_t nib, uint32_t scode) {
 // 64 inputs).
 // ---------------------------------------------------------------------------
 struct GemmMM {
-  const uint16_t* af;   // afrag of X: [mtiles(R)][KT][2][512] bf16 hi/lo
+  const uint16_t* af;   // afrag of X: [mtiles(R)][KT][512] f16
   int R, KT;
   const uint8_t* w;     // repacked codes [N/16][KB][64][16]
   const float* s;       // scales [N/16][KB][16]
@@ -102,8 +73,8 @@ struct GemmMM {
 template <int CT>
 __global__ __launch_bounds__(256) void k_gemm_mm(GemmMM g) {
   constexpr int COLS = 16 * CT * MM_WAVES;
-  // [buffer][row tile][hi t, lo t, hi t+1, lo t+1][lane]
-  __shared__ __attribute__((aligned(16))) u32x4 sa[2][MM_RT * 4][64];
+  // [buffer][row tile][k tile t, t+1][lane]
+  __shared__ __attribute__((aligned(16))) u32x4 sa[2][MM_RT * 2][64];
   const int RB = (g.R + 63) / 64, CB = g.N / COLS;
   const MmMap m = mm_map(RB, CB, g.splits);
   if (!m.ok) return;
@@ -113,7 +84,7 @@ __global__ __launch_bounds__(256) void k_gemm_mm(GemmMM g) {
   // wave w stages row tile rb*4 + w (clamped: a tile past the last repeats it,
   // and its output rows are past R and discarded)
   const int mt_ld = min(m.rb * MM_RT + wave, MT - 1);
-  const uint16_t* ap = g.af + ((size_t)mt_ld * g.KT + 2 * b0) * 1024 + lane * 8;
+  const uint16_t* ap = g.af + ((size_t)mt_ld * g.KT + 2 * b0) * 512 + lane * 8;
   const int nt0 = g.n_off + m.cb * (COLS / 16) + wave * CT;
   const uint8_t* wp = g.w + ((size_t)nt0 * g.KB + b0) * 1024 + lane * 16;
   const float* spp = g.s + ((size_t)nt0 * g.KB + b0) * 16 + (lane & 15);
@@ -125,59 +96,55 @@ __global__ __launch_bounds__(256) void k_gemm_mm(GemmMM g) {
 #pragma unroll
     for (int c = 0; c < CT; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 ar[4], wr[CT];
+  u32x4 ar[2], wr[CT];
   float sr[CT];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) ar[j] = *reinterpret_cast<const u32x4*>(ap + j * 512);
+  for (int j = 0; j < 2; ++j) ar[j] = *reinterpret_cast<const u32x4*>(ap + j * 512);
 #pragma unroll
   for (int c = 0; c < CT; ++c) {
     wr[c] = *reinterpret_cast<const u32x4*>(wp + c * wt_stride);
     sr[c] = spp[c * st_stride];
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) sa[0][wave * 4 + j][lane] = ar[j];
+  for (int j = 0; j < 2; ++j) sa[0][wave * 2 + j][lane] = ar[j];
   __syncthreads();
 
   for (int i = 0; i < nb; ++i) {
     // next step's loads (the last step re-loads itself; unconditional loads
     // keep the compiler from waiting for them at a join)
     const int in = min(i + 1, nb - 1);
-    u32x4 an[4], wn[CT];
+    u32x4 an[2], wn[CT];
     float sn[CT];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      an[j] = *reinterpret_cast<const u32x4*>(ap + (size_t)in * 2048 + j * 512);
+    for (int j = 0; j < 2; ++j)
+      an[j] = *reinterpret_cast<const u32x4*>(ap + (size_t)in * 1024 + j * 512);
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
       wn[c] = *reinterpret_cast<const u32x4*>(wp + c * wt_stride + (size_t)in * 1024);
       sn[c] = spp[c * st_stride + (size_t)in * 16];
     }
-    bf16x8 w0[CT], w1[CT];
+    f16x8 w0[CT], w1[CT];
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
-      w0[c] = mm_e4m3x8(wr[c].x, wr[c].y);
-      w1[c] = mm_e4m3x8(wr[c].z, wr[c].w);
+      w0[c] = e4m3x8_f16(wr[c].x, wr[c].y);
+      w1[c] = e4m3x8_f16(wr[c].z, wr[c].w);
     }
     const int buf = i & 1;
 #pragma unroll
     for (int r = 0; r < MM_RT; ++r) {
-      const bf16x8 ah0 = __builtin_bit_cast(bf16x8, sa[buf][r * 4 + 0][lane]);
-      const bf16x8 al0 = __builtin_bit_cast(bf16x8, sa[buf][r * 4 + 1][lane]);
-      const bf16x8 ah1 = __builtin_bit_cast(bf16x8, sa[buf][r * 4 + 2][lane]);
-      const bf16x8 al1 = __builtin_bit_cast(bf16x8, sa[buf][r * 4 + 3][lane]);
+      const f16x8 a0 = __builtin_bit_cast(f16x8, sa[buf][r * 2 + 0][lane]);
+      const f16x8 a1 = __builtin_bit_cast(f16x8, sa[buf][r * 2 + 1][lane]);
 #pragma unroll
       for (int c = 0; c < CT; ++c) {
         f32x4 t = {0.f, 0.f, 0.f, 0.f};
-        t = mfma_bf16(ah0, w0[c], t);
-        t = mfma_bf16(al0, w0[c], t);
-        t = mfma_bf16(ah1, w1[c], t);
-        t = mfma_bf16(al1, w1[c], t);
+        t = mfma_f16(a0, w0[c], t);
+        t = mfma_f16(a1, w1[c], t);
         acc[r][c] += sr[c] * t;
       }
     }
     if (i + 1 < nb) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sa[buf ^ 1][wave * 4 + j][lane] = an[j];
+      for (int j = 0; j < 2; ++j) sa[buf ^ 1][wave * 2 + j][lane] = an[j];
     }
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
@@ -236,15 +203,15 @@ void launch_gemm_mm(hipStream_t st, const uint16_t* af, int R, const Fp8Mat& W, 
 // ---------------------------------------------------------------------------
 // NVFP4 head over the draft vocabulary with a fused per-row argmax:
 // logits[r][v] = g * sum_k z[r][k] * e2m1(q) * e4m3(s). One step is one
-// 128-input group (the repacked code layout's unit). The activations arrive as
-// bf16 hi/lo and are re-split into f16 hi/lo when staged, so that the exact
-// f16 head values run on the f16 matrix cores. Each row's best (logit, index)
+// 128-input group (the repacked code layout's unit). The f16 activations
+// multiply the exactly decoded f16 head values on the f16 matrix cores. Each
+// row's best (logit, index)
 // key over the workgroup's 256 vocabulary rows is merged with a 64-bit
 // atomicMax: the result does not depend on scheduling, and ties go to the
 // lowest draft index.
 // ---------------------------------------------------------------------------
 struct HeadMM {
-  const uint16_t* af;   // afrag of z = RMSNorm(x; g_final): [mtiles(R)][H/32][2][512]
+  const uint16_t* af;   // afrag of z = RMSNorm(x; g_final): [mtiles(R)][H/32][512] f16
   int R;
   const uint8_t* hq;    // [VT][H/128][64][16] e2m1 codes
   const uint8_t* hs;    // [VT][H/128][64][4] e4m3 scale codes
@@ -256,8 +223,8 @@ struct HeadMM {
 
 template <int CT>
 __global__ __launch_bounds__(256) void k_head_mm(HeadMM a) {
-  // [buffer][row tile][hi/lo of k tiles 0..3][lane] f16
-  __shared__ __attribute__((aligned(16))) u32x4 sa[2][MM_RT * 8][64];
+  // [buffer][row tile][k tiles 0..3][lane] f16
+  __shared__ __attribute__((aligned(16))) u32x4 sa[2][MM_RT * 4][64];
   __shared__ unsigned long long best_s[MM_RT * 16];
   constexpr int KT = H / 32, KG = H / 128;
   const int RB = (a.R + 63) / 64, CB = (a.VT + 4 * CT - 1) / (4 * CT);
@@ -267,7 +234,7 @@ __global__ __launch_bounds__(256) void k_head_mm(HeadMM a) {
   const int MT = mtiles(a.R);
   if (threadIdx.x < MM_RT * 16) best_s[threadIdx.x] = 0ull;
   const int mt_ld = min(m.rb * MM_RT + wave, MT - 1);
-  const uint16_t* ap = a.af + (size_t)mt_ld * KT * 1024 + lane * 8;
+  const uint16_t* ap = a.af + (size_t)mt_ld * KT * 512 + lane * 8;
   // vocab tiles of this wave (tiles past the last repeat it and are masked)
   const int vt0 = (m.cb * MM_WAVES + wave) * CT;
   const uint8_t* qp[CT];
@@ -279,51 +246,32 @@ __global__ __launch_bounds__(256) void k_head_mm(HeadMM a) {
     sp[c] = a.hs + (size_t)vt * KG * 256 + lane * 4;
   }
 
-  // bf16 hi/lo of 8 elements -> f16 hi/lo (the pair's fp32 sum re-split)
-  auto stage = [&](const u32x4 (&raw)[8], int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v[8], lo[8];
-      bf16x8_to_f32(raw[2 * i], v);
-      bf16x8_to_f32(raw[2 * i + 1], lo);
-      f16x8 h, l;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = v[e] + lo[e];
-        const _Float16 hh = (_Float16)x;
-        h[e] = hh;
-        l[e] = (_Float16)(x - (float)hh);
-      }
-      sa[buf][wave * 8 + 2 * i][lane] = __builtin_bit_cast(u32x4, h);
-      sa[buf][wave * 8 + 2 * i + 1][lane] = __builtin_bit_cast(u32x4, l);
-    }
-  };
-
   f32x4 acc[MM_RT][CT];
 #pragma unroll
   for (int r = 0; r < MM_RT; ++r)
 #pragma unroll
     for (int c = 0; c < CT; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 ar[8], qr[CT];
+  u32x4 ar[4], qr[CT];
   uint32_t sr[CT];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) ar[j] = *reinterpret_cast<const u32x4*>(ap + j * 512);
+  for (int j = 0; j < 4; ++j) ar[j] = *reinterpret_cast<const u32x4*>(ap + j * 512);
 #pragma unroll
   for (int c = 0; c < CT; ++c) {
     qr[c] = *reinterpret_cast<const u32x4*>(qp[c]);
     sr[c] = *reinterpret_cast<const uint32_t*>(sp[c]);
   }
-  stage(ar, 0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sa[0][wave * 4 + j][lane] = ar[j];
   __syncthreads();
 
   for (int kg = 0; kg < KG; ++kg) {
     const int kn = min(kg + 1, KG - 1);
-    u32x4 an[8], qn[CT];
+    u32x4 an[4], qn[CT];
     uint32_t sn[CT];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      an[j] = *reinterpret_cast<const u32x4*>(ap + (size_t)kn * 4096 + j * 512);
+    for (int j = 0; j < 4; ++j)
+      an[j] = *reinterpret_cast<const u32x4*>(ap + (size_t)kn * 2048 + j * 512);
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
       qn[c] = *reinterpret_cast<const u32x4*>(qp[c] + (size_t)kn * 1024);
@@ -334,19 +282,18 @@ __global__ __launch_bounds__(256) void k_head_mm(HeadMM a) {
     for (int i = 0; i < 4; ++i) {
       f16x8 w[CT];
 #pragma unroll
-      for (int c = 0; c < CT; ++c) w[c] = mm_nvfp4x8(qr[c][i], (sr[c] >> (8 * i)) & 0xffu);
+      for (int c = 0; c < CT; ++c) w[c] = nvfp4x8_f16(qr[c][i], (sr[c] >> (8 * i)) & 0xffu);
 #pragma unroll
       for (int r = 0; r < MM_RT; ++r) {
-        const f16x8 ah = __builtin_bit_cast(f16x8, sa[buf][r * 8 + 2 * i][lane]);
-        const f16x8 al = __builtin_bit_cast(f16x8, sa[buf][r * 8 + 2 * i + 1][lane]);
+        const f16x8 av = __builtin_bit_cast(f16x8, sa[buf][r * 4 + i][lane]);
 #pragma unroll
-        for (int c = 0; c < CT; ++c) {
-          acc[r][c] = mfma_f16(ah, w[c], acc[r][c]);
-          acc[r][c] = mfma_f16(al, w[c], acc[r][c]);
-        }
+        for (int c = 0; c < CT; ++c) acc[r][c] = mfma_f16(av, w[c], acc[r][c]);
       }
     }
-    if (kg + 1 < KG) stage(an, buf ^ 1);
+    if (kg + 1 < KG) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sa[buf ^ 1][wave * 4 + j][lane] = an[j];
+    }
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
       qr[c] = qn[c];

@@ -71,7 +71,7 @@ struct Work {
   float* c = nullptr;                 // [Imax][H] ingest rows after fc
   float* part = nullptr;              // split-K partial sums
   size_t part_elems = 0;
-  uint16_t* af_in = nullptr;          // afrag [max(Bmax, Imax)][NTAP*H]
+  uint16_t* af_in = nullptr;          // afrag (f16) [max(Bmax, Imax)][NTAP*H]
   uint16_t* af_fc = nullptr;          // afrag [max(Bmax, Imax)][2H]
   uint16_t* af_ab = nullptr;          // afrag [3 Bmax][2H]
   uint16_t* af_rank = nullptr;        // afrag [3 Bmax][RK]
@@ -93,7 +93,7 @@ struct Work {
 // Row tiles of 16 for R rows.
 __host__ __device__ inline int mtiles(int R) { return (R + 15) / 16; }
 // Elements of an afrag buffer for R rows and K inputs.
-inline size_t afrag_elems(int R, int K) { return (size_t)mtiles(R) * (K / 32) * 1024; }
+inline size_t afrag_elems(int R, int K) { return (size_t)mtiles(R) * (K / 32) * 512; }
 
 // Split-K policy for a projection with K/64 blocks over R rows: fixed per
 // matrix while R <= 16 (one row tile), so a stream's result does not depend on
@@ -141,5 +141,6 @@ void launch_head_mm(hipStream_t st, const uint16_t* af, int R, const DevWeights&
 // probes
 void launch_probe_e4m3(hipStream_t st, uint16_t* out);
 void launch_probe_nvfp4(hipStream_t st, uint16_t* out);
+void launch_probe_e4m3_f16(hipStream_t st, uint16_t* out);
 
 }  // namespace kd

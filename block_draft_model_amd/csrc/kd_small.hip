@@ -55,9 +55,6 @@ typedef const KD_LDS float* lds_cf;
 template <class T> using gptr = KD_GLOBAL T*;
 static_assert(sizeof(SmallArgsT<GlobalPtr>) == sizeof(SmallArgs), "one layout for both views");
 
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
 enum Phase {
   PH_PRE0 = 0, PH_PRE1 = 1, PH_PRE2 = 2,
   PH_SA = 0, PH_SU = 1, PH_QKV = 2, PH_ATTN = 3, PH_O = 5, PH_GU = 6, PH_DOWN = 7,
@@ -111,39 +108,6 @@ __device__ __forceinline__ void lds_sync() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left alone
   __builtin_amdgcn_s_barrier();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-// e4m3 pairs -> bf16 pairs with unit scale (exact on gfx950).
-__device__ __forceinline__ bf16x8 e4m3x8_bf16(uint32_t lo, uint32_t hi) {
-  u32x4 r;
-  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
-  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
-  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
-  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
-  return __builtin_bit_cast(bf16x8, r);
-}
-
-// e4m3 pairs -> f16 pairs with unit scale (exact: e4m3 values lie within
-// f16's normal range and carry at most 4 significant bits).
-__device__ __forceinline__ f16x8 e4m3x8_f16(uint32_t lo, uint32_t hi) {
-  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
-  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
-  const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
-  const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
-  return f16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
-}
-
-// 8 e2m1 codes (even element in the low nibble) times an e4m3 block scale,
-// exactly in f16: e2m1 decoded with unit scale, then one packed f16 multiply
-// per pair (<= 6 significant bits, within f16's normal range).
-__device__ __forceinline__ f16x8 nvfp4x8_f16(uint32_t nib, uint32_t scode) {
-  const f16x2 s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scode, 1.0f, false);
-  const f16x2 sc = {s2.x, s2.x};
-  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(nib, 1.0f, 0) * sc;
-  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(nib, 1.0f, 1) * sc;
-  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(nib, 1.0f, 2) * sc;
-  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(nib, 1.0f, 3) * sc;
-  return f16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
 __device__ __forceinline__ void split_bf16(const float* v, bf16x8& hi, bf16x8& lo) {

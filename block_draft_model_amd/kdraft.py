@@ -52,7 +52,7 @@ class KdKV(ctypes.Structure):
 
 EXPORTS = ["kd_default_config", "kd_create", "kd_load_weights", "kd_round", "kd_ingest",
            "kd_set_stream", "kd_destroy", "kd_status_string", "kd_last_error",
-           "kd_probe_decode_e4m3", "kd_probe_decode_nvfp4", "kd_debug_set_layers",
+           "kd_probe_decode_e4m3", "kd_probe_decode_e4m3_f16", "kd_probe_decode_nvfp4", "kd_debug_set_layers",
            "kd_debug_buffers", "kd_debug_set_path", "kd_debug_last_path",
            "kd_debug_set_trace"]
 
@@ -95,6 +95,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kd_last_error.restype = ctypes.c_char_p
     lib.kd_probe_decode_e4m3.argtypes = [c_void_p]
     lib.kd_probe_decode_e4m3.restype = c_int
+    lib.kd_probe_decode_e4m3_f16.argtypes = [c_void_p]
+    lib.kd_probe_decode_e4m3_f16.restype = c_int
     lib.kd_probe_decode_nvfp4.argtypes = [c_void_p]
     lib.kd_probe_decode_nvfp4.restype = c_int
     lib.kd_debug_set_layers.argtypes = [c_void_p, c_int]
@@ -269,6 +271,12 @@ def probe_decode_e4m3(out) -> None:
     st = load_library().kd_probe_decode_e4m3(_ptr(out))
     if st != KD_OK:
         raise KDraftError(st, "kd_probe_decode_e4m3")
+
+
+def probe_decode_e4m3_f16(out) -> None:
+    st = load_library().kd_probe_decode_e4m3_f16(_ptr(out))
+    if st != KD_OK:
+        raise KDraftError(st, "kd_probe_decode_e4m3_f16")
 
 
 def probe_decode_nvfp4(out) -> None:

@@ -11,15 +11,22 @@
 extern "C" {
 #endif
 
-/* Decodes every e4m3 code (0..255) with the body kernels' weight decoder
- * (block-FP8 values as they enter the matrix cores) and writes the bf16 bit
+/* Decodes every e4m3 code (0..255) with the bf16 weight decoder (block-FP8
+ * values as they meet bf16 activations on the matrix cores: the small-batch
+ * path's tapped-state and embedding projections) and writes the bf16 bit
  * patterns to out_bf16[256] (device). Blocks until done. */
 kd_status kd_probe_decode_e4m3(uint16_t* out_bf16);
 
-/* Decodes every (e4m3 scale code s, e2m1 code c) pair with the head kernel's
- * decoder, e2m1(c) * e4m3(s) as bf16, into out_bf16[s*16 + c] (device,
+/* Decodes every e4m3 code (0..255) with the f16 weight decoder (block-FP8
+ * values as they meet f16 activations on the matrix cores: every other
+ * projection) and writes the f16 bit patterns to out_f16[256] (device).
+ * Blocks until done. */
+kd_status kd_probe_decode_e4m3_f16(uint16_t* out_f16);
+
+/* Decodes every (e4m3 scale code s, e2m1 code c) pair with the head kernels'
+ * decoder, e2m1(c) * e4m3(s) as f16, into out_f16[s*16 + c] (device,
  * 4096 entries). Blocks until done. */
-kd_status kd_probe_decode_nvfp4(uint16_t* out_bf16);
+kd_status kd_probe_decode_nvfp4(uint16_t* out_f16);
 
 /* Runs only the first n body layers in later rounds (n in [0, layers]);
  * n < 0 restores the full depth. For bisecting parity failures. */

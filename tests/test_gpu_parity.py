@@ -63,14 +63,25 @@ def test_probe_e4m3_decoder_is_exact():
     assert np.all(np.isnan(oracle.decode_bf16(got[~fin])))
 
 
+def test_probe_e4m3_f16_decoder_is_exact():
+    require_gpu()
+    out = torch.zeros(256, dtype=torch.int16, device="cuda")
+    kdraft.probe_decode_e4m3_f16(out)
+    got = out.cpu().numpy().view(np.float16).astype(np.float64)
+    exact = oracle.decode_e4m3(np.arange(256))
+    fin = np.isfinite(exact)
+    assert np.array_equal(got[fin], exact[fin])                  # every finite code exactly
+    assert np.all(np.isnan(got[~fin]))
+
+
 def test_probe_nvfp4_decoder_is_exact():
     require_gpu()
     out = torch.zeros(4096, dtype=torch.int16, device="cuda")
     kdraft.probe_decode_nvfp4(out)
-    got = out.cpu().numpy().view(np.uint16).reshape(256, 16)
+    got = out.cpu().numpy().view(np.float16).astype(np.float64).reshape(256, 16)
     exact = oracle.decode_e4m3(np.arange(256))[:, None] * oracle.decode_e2m1(np.arange(16))[None, :]
     fin = np.isfinite(exact)
-    assert np.array_equal(got[fin], oracle.round_bf16(exact[fin]))
+    assert np.array_equal(got[fin], exact[fin])                  # e2m1 x e4m3 exactly in f16
 
 
 PATHS = [1, 2, 3]   # general multi-kernel, small-batch phases, small-batch persistent
@@ -237,15 +248,19 @@ def test_ingest_then_round_b64(hA):
         for key, ex in (("k", exact[l][0]), ("v", exact[l][1])):
             g = oracle.decode_bf16(after_gpu[key][l][:, :, 2043:2048])   # [s][h][n][d]
             e = ex.transpose(0, 2, 1, 3)                                  # [s][h][n][d]
-            # fp32 arithmetic then bf16 rounding: within one bf16 ulp of the
-            # exact value, plus an fp32-level error relative to the size of the
-            # head vector (values that cancel to near zero carry that error)
+            # the normalised row enters the K/V projections as f16 (11
+            # significant bits): each value carries an error of about 2^-12 of
+            # its head vector's RMS (std over 2560 rounded inputs), which can
+            # move it past a bf16 rounding boundary. Bound: one bf16 ulp of the
+            # exact value plus 2^-8 of the head vector's RMS (over 10 std of
+            # that error; a wrong input or weight gives errors of order the RMS)
             ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(e), 1e-30))) - 7)
             scale = np.sqrt(np.mean(e * e, axis=-1, keepdims=True))
             rel = np.abs(g - e) / np.maximum(np.abs(e), 1e-30)
-            off = np.abs(g - e) > ulp + 2.0 ** -14 * scale
+            err = np.abs(g - e) / scale
+            off = np.abs(g - e) > ulp + 2.0 ** -8 * scale
             log(f"ingest layer {l} {key}: max rel err {rel.max():.3e}, "
-                f"beyond one ulp {int(off.sum())}/{off.size}, "
+                f"max err / head RMS {err.max():.2e}, beyond the bound {int(off.sum())}/{off.size}, "
                 f"codes differing from oracle {(after_gpu[key][l][:, :, 2043:2048] != after_ref[key][l][:, :, 2043:2048]).mean():.2e}")
             assert not off.any(), (l, key)
     lg, ids = hA.run(inp)
