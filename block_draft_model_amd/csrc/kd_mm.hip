@@ -70,8 +70,8 @@ struct GemmMM {
   int splits, kbs;
 };
 
-template <int CT>
-__global__ __launch_bounds__(256) void k_gemm_mm(GemmMM g) {
+template <int CT, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_mm(GemmMM g) {
   constexpr int COLS = 16 * CT * MM_WAVES;
   // [buffer][row tile][k tile t, t+1][lane]
   __shared__ __attribute__((aligned(16))) u32x4 sa[2][MM_RT * 2][64];
@@ -96,62 +96,66 @@ __global__ __launch_bounds__(256) void k_gemm_mm(GemmMM g) {
 #pragma unroll
     for (int c = 0; c < CT; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 ar[2], wr[CT];
-  float sr[CT];
+  // A register ring of D steps: slot d holds the activation fragments (bound
+  // for LDS) and the weights of the steps s with s % D == d. Step s's weights
+  // are decoded, the slot is refilled with step s + D, and step s runs on the
+  // matrix cores while D - 1 later steps are in flight. Loads past the last
+  // step re-load it (unconditional loads keep the compiler from waiting for
+  // them at a join).
+  u32x4 ar[D][2], wr[D][CT];
+  float sr[D][CT];
+  auto load = [&](int st, int d) __attribute__((always_inline)) {
+    const size_t sc = (size_t)min(st, nb - 1);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) ar[j] = *reinterpret_cast<const u32x4*>(ap + j * 512);
+    for (int j = 0; j < 2; ++j) ar[d][j] = *reinterpret_cast<const u32x4*>(ap + sc * 1024 + j * 512);
 #pragma unroll
-  for (int c = 0; c < CT; ++c) {
-    wr[c] = *reinterpret_cast<const u32x4*>(wp + c * wt_stride);
-    sr[c] = spp[c * st_stride];
-  }
+    for (int c = 0; c < CT; ++c) {
+      wr[d][c] = *reinterpret_cast<const u32x4*>(wp + c * wt_stride + sc * 1024);
+      sr[d][c] = spp[c * st_stride + sc * 16];
+    }
+  };
 #pragma unroll
-  for (int j = 0; j < 2; ++j) sa[0][wave * 2 + j][lane] = ar[j];
+  for (int d = 0; d < D; ++d) load(d, d);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) sa[0][wave * 2 + j][lane] = ar[0][j];
   __syncthreads();
 
-  for (int i = 0; i < nb; ++i) {
-    // next step's loads (the last step re-loads itself; unconditional loads
-    // keep the compiler from waiting for them at a join)
-    const int in = min(i + 1, nb - 1);
-    u32x4 an[2], wn[CT];
-    float sn[CT];
+  for (int i0 = 0; i0 < nb; i0 += D) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      an[j] = *reinterpret_cast<const u32x4*>(ap + (size_t)in * 1024 + j * 512);
+    for (int d = 0; d < D; ++d) {
+      const int i = i0 + d;
+      if (i < nb) {
+        f16x8 w0[CT], w1[CT];
+        float sc[CT];
 #pragma unroll
-    for (int c = 0; c < CT; ++c) {
-      wn[c] = *reinterpret_cast<const u32x4*>(wp + c * wt_stride + (size_t)in * 1024);
-      sn[c] = spp[c * st_stride + (size_t)in * 16];
-    }
-    f16x8 w0[CT], w1[CT];
+        for (int c = 0; c < CT; ++c) {
+          w0[c] = e4m3x8_f16(wr[d][c].x, wr[d][c].y);
+          w1[c] = e4m3x8_f16(wr[d][c].z, wr[d][c].w);
+          sc[c] = sr[d][c];
+        }
+        // the slot's activations went to LDS a step ago: refill it
+        load(i + D, d);
+        const int buf = i & 1;
 #pragma unroll
-    for (int c = 0; c < CT; ++c) {
-      w0[c] = e4m3x8_f16(wr[c].x, wr[c].y);
-      w1[c] = e4m3x8_f16(wr[c].z, wr[c].w);
-    }
-    const int buf = i & 1;
+        for (int r = 0; r < MM_RT; ++r) {
+          const f16x8 a0 = __builtin_bit_cast(f16x8, sa[buf][r * 2 + 0][lane]);
+          const f16x8 a1 = __builtin_bit_cast(f16x8, sa[buf][r * 2 + 1][lane]);
 #pragma unroll
-    for (int r = 0; r < MM_RT; ++r) {
-      const f16x8 a0 = __builtin_bit_cast(f16x8, sa[buf][r * 2 + 0][lane]);
-      const f16x8 a1 = __builtin_bit_cast(f16x8, sa[buf][r * 2 + 1][lane]);
+          for (int c = 0; c < CT; ++c) {
+            f32x4 t = {0.f, 0.f, 0.f, 0.f};
+            t = mfma_f16(a0, w0[c], t);
+            t = mfma_f16(a1, w1[c], t);
+            acc[r][c] += sc[c] * t;
+          }
+        }
+        if (i + 1 < nb) {
+          const int dn = d + 1 == D ? 0 : d + 1;
 #pragma unroll
-      for (int c = 0; c < CT; ++c) {
-        f32x4 t = {0.f, 0.f, 0.f, 0.f};
-        t = mfma_f16(a0, w0[c], t);
-        t = mfma_f16(a1, w1[c], t);
-        acc[r][c] += sr[c] * t;
+          for (int j = 0; j < 2; ++j) sa[buf ^ 1][wave * 2 + j][lane] = ar[dn][j];
+        }
+        __syncthreads();
       }
     }
-    if (i + 1 < nb) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) sa[buf ^ 1][wave * 2 + j][lane] = an[j];
-    }
-#pragma unroll
-    for (int c = 0; c < CT; ++c) {
-      wr[c] = wn[c];
-      sr[c] = sn[c];
-    }
-    __syncthreads();
   }
 
   float* out = g.part + (size_t)m.sp * g.R * g.N;
@@ -195,9 +199,9 @@ void launch_gemm_mm(hipStream_t st, const uint16_t* af, int R, const Fp8Mat& W, 
   g.splits = splits;
   g.kbs = g.KB / splits;
   if (mm_ct(R) == 4)
-    k_gemm_mm<4><<<mm_grid(R, N / 256, splits), 256, 0, st>>>(g);
+    k_gemm_mm<4, 2><<<mm_grid(R, N / 256, splits), 256, 0, st>>>(g);
   else
-    k_gemm_mm<1><<<mm_grid(R, N / 64, splits), 256, 0, st>>>(g);
+    k_gemm_mm<1, 4><<<mm_grid(R, N / 64, splits), 256, 0, st>>>(g);
 }
 
 // ---------------------------------------------------------------------------
