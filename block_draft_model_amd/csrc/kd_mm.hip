@@ -225,8 +225,8 @@ struct HeadMM {
   unsigned long long* keys;
 };
 
-template <int CT>
-__global__ __launch_bounds__(256) void k_head_mm(HeadMM a) {
+template <int CT, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_head_mm(HeadMM a) {
   // [buffer][row tile][k tiles 0..3][lane] f16
   __shared__ __attribute__((aligned(16))) u32x4 sa[2][MM_RT * 4][64];
   __shared__ unsigned long long best_s[MM_RT * 16];
@@ -256,54 +256,59 @@ __global__ __launch_bounds__(256) void k_head_mm(HeadMM a) {
 #pragma unroll
     for (int c = 0; c < CT; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 ar[4], qr[CT];
-  uint32_t sr[CT];
+  // register ring of D steps (128-input groups), as in k_gemm_mm
+  u32x4 ar[D][4], qr[D][CT];
+  uint32_t sr[D][CT];
+  auto load = [&](int st, int d) __attribute__((always_inline)) {
+    const size_t kc = (size_t)min(st, KG - 1);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) ar[j] = *reinterpret_cast<const u32x4*>(ap + j * 512);
+    for (int j = 0; j < 4; ++j) ar[d][j] = *reinterpret_cast<const u32x4*>(ap + kc * 2048 + j * 512);
 #pragma unroll
-  for (int c = 0; c < CT; ++c) {
-    qr[c] = *reinterpret_cast<const u32x4*>(qp[c]);
-    sr[c] = *reinterpret_cast<const uint32_t*>(sp[c]);
-  }
+    for (int c = 0; c < CT; ++c) {
+      qr[d][c] = *reinterpret_cast<const u32x4*>(qp[c] + kc * 1024);
+      sr[d][c] = *reinterpret_cast<const uint32_t*>(sp[c] + kc * 256);
+    }
+  };
 #pragma unroll
-  for (int j = 0; j < 4; ++j) sa[0][wave * 4 + j][lane] = ar[j];
+  for (int d = 0; d < D; ++d) load(d, d);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sa[0][wave * 4 + j][lane] = ar[0][j];
   __syncthreads();
 
-  for (int kg = 0; kg < KG; ++kg) {
-    const int kn = min(kg + 1, KG - 1);
-    u32x4 an[4], qn[CT];
-    uint32_t sn[CT];
+  for (int k0 = 0; k0 < KG; k0 += D) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      an[j] = *reinterpret_cast<const u32x4*>(ap + (size_t)kn * 2048 + j * 512);
+    for (int d = 0; d < D; ++d) {
+      const int kg = k0 + d;
+      if (kg < KG) {
+        u32x4 q[CT];
+        uint32_t sv[CT];
 #pragma unroll
-    for (int c = 0; c < CT; ++c) {
-      qn[c] = *reinterpret_cast<const u32x4*>(qp[c] + (size_t)kn * 1024);
-      sn[c] = *reinterpret_cast<const uint32_t*>(sp[c] + (size_t)kn * 256);
-    }
-    const int buf = kg & 1;
+        for (int c = 0; c < CT; ++c) {
+          q[c] = qr[d][c];
+          sv[c] = sr[d][c];
+        }
+        load(kg + D, d);
+        const int buf = kg & 1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f16x8 w[CT];
+        for (int i = 0; i < 4; ++i) {
+          f16x8 w[CT];
 #pragma unroll
-      for (int c = 0; c < CT; ++c) w[c] = nvfp4x8_f16(qr[c][i], (sr[c] >> (8 * i)) & 0xffu);
+          for (int c = 0; c < CT; ++c) w[c] = nvfp4x8_f16(q[c][i], (sv[c] >> (8 * i)) & 0xffu);
 #pragma unroll
-      for (int r = 0; r < MM_RT; ++r) {
-        const f16x8 av = __builtin_bit_cast(f16x8, sa[buf][r * 4 + i][lane]);
+          for (int r = 0; r < MM_RT; ++r) {
+            const f16x8 av = __builtin_bit_cast(f16x8, sa[buf][r * 4 + i][lane]);
 #pragma unroll
-        for (int c = 0; c < CT; ++c) acc[r][c] = mfma_f16(av, w[c], acc[r][c]);
+            for (int c = 0; c < CT; ++c) acc[r][c] = mfma_f16(av, w[c], acc[r][c]);
+          }
+        }
+        if (kg + 1 < KG) {
+          const int dn = d + 1 == D ? 0 : d + 1;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sa[buf ^ 1][wave * 4 + j][lane] = ar[dn][j];
+        }
+        __syncthreads();
       }
     }
-    if (kg + 1 < KG) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sa[buf ^ 1][wave * 4 + j][lane] = an[j];
-    }
-#pragma unroll
-    for (int c = 0; c < CT; ++c) {
-      qr[c] = qn[c];
-      sr[c] = sn[c];
-    }
-    __syncthreads();
   }
 
   // logits, per-row best over this wave's 64 vocabulary rows, then over the
@@ -363,7 +368,7 @@ void launch_head_mm(hipStream_t st, const uint16_t* af, int R, const DevWeights&
   a.keys = keys;
   // 256 vocabulary rows per workgroup at every row count (narrower tiles
   // measured slower at 64 rows)
-  k_head_mm<4><<<mm_grid(R, (d.VT + 15) / 16, 1), 256, 0, st>>>(a);
+  k_head_mm<4, 3><<<mm_grid(R, (d.VT + 15) / 16, 1), 256, 0, st>>>(a);
 }
 
 }  // namespace kd
