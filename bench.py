@@ -3,8 +3,9 @@
     python bench.py [--steps K] [--warmup W] [--config I] [--no-cpu-baseline]
 
 A step is one kd_round over every stream of the workload (tap fuse, row build,
-4 layers with spine and cross-attention, restricted NVFP4 head, argmax) with
-every input already resident in HBM. The default workload is the 4-stream
+4 layers with spine and cross-attention, restricted NVFP4 head, argmax), for
+the ingesting workload preceded by the kd_ingest of each stream's new context
+rows, with every input already resident in HBM. The default workload is the 4-stream
 configuration: 4 streams, 2048 context rows each, FP8 body, NVFP4 head.
 Prints one JSON line.
 """
@@ -29,30 +30,39 @@ KERNEL_NAME = {2: "kd::k_small_phase", 3: "kd::k_small_mega"}
 LAUNCHES_PER_ROUND = {2: 30, 3: 1}
 
 
-def algorithmic_bytes(dims, lens, streams):
-    """Bytes a round must move: weights once (block-FP8 body with scales, NVFP4
+def algorithmic_bytes(dims, lens, streams, ingest=0):
+    """Bytes a step must move: weights once (block-FP8 body with scales, NVFP4
     head with block and tensor scales, fp32 vectors), 40,960 B of bf16 K/V per
     visible context row per stream (4 layers x K,V x 20 heads x 128 x 2 B), and
-    per stream its tapped states, 4 embedding rows, ids, length and outputs."""
+    per stream its tapped states, 4 embedding rows, ids, length and outputs.
+    With `ingest` new context rows per stream ahead of the round: their tapped
+    states, next-token ids and embedding rows, and the 40,960 B of K/V each
+    writes (the weights they use are the round's, counted once); `lens` are the
+    lengths the round sees."""
     import synth
     mb = synth.model_bytes(dims)
     kv_row = dims.layers * 2 * dims.heads * dims.head_dim * 2
     vis = sum(min(int(l), dims.window) for l in lens)
     per_stream = (dims.taps * dims.hidden * 2 + dims.block * dims.hidden * 2
                   + 4 * (1 + (dims.block - 1) + 1 + dims.block))
-    total = mb["body"] + mb["head"] + mb["vectors"] + kv_row * vis + per_stream * streams
-    return dict(total=total, body=mb["body"], head=mb["head"], kv=kv_row * vis)
+    ingest_bytes = streams * ingest * (dims.taps * dims.hidden * 2 + 4 + dims.hidden * 2 + kv_row)
+    total = mb["body"] + mb["head"] + mb["vectors"] + kv_row * vis + per_stream * streams + ingest_bytes
+    return dict(total=total, body=mb["body"], head=mb["head"], kv=kv_row * vis, ingest=ingest_bytes)
+
+
+# the sources the small-batch round kernels are compiled from
+SMALL_SOURCES = ("kd_device.h", "kd_runtime.h", "kd_small.h", "kd_small.hip")
 
 
 def kernel_source_hash():
-    """sha256 over the HIP sources with comments and blank space removed, first
-    12 hex digits: identifies the kernels a counter measurement was taken on
-    (an edit of comments alone keeps it)."""
-    import glob
+    """sha256 over the sources of the small-batch round kernels with comments
+    and blank space removed, first 12 hex digits: identifies the kernels a
+    counter measurement was taken on (an edit of comments alone, or of the
+    general path's sources, keeps it)."""
     import hashlib
     import re
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "block_draft_model_amd", "csrc", "*"))):
+    for f in [os.path.join(ROOT, "block_draft_model_amd", "csrc", n) for n in SMALL_SOURCES]:
         with open(f, encoding="utf-8") as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -164,9 +174,14 @@ def main():
     drafter.debug_set_path(args.path)
     kv = kdraft.kv_struct(inp["k"], inp["v"])
     ids = torch.empty(B, 4, dtype=torch.int32, device="cuda")
-    lens_host = inp["lens"].cpu().tolist()
+    n_ingest = cfg.get("ingest", 0)
+    # the lengths the timed rounds see (an ingesting step appends its rows
+    # first; the window keeps the visible rows at min(len, 2048) as they grow)
+    lens_host = [l + n_ingest for l in inp["lens"].cpu().tolist()]
 
     def step():
+        if n_ingest:
+            drafter.ingest(B, n_ingest, inp["ingest_taps"], inp["ingest_ids"], kv, inp["lens"])
         drafter.round(B, inp["taps"], inp["anchor"], inp["pred"], kv, inp["lens"], ids, None)
 
     for _ in range(args.warmup):
@@ -183,7 +198,7 @@ def main():
     ms = start.elapsed_time(end) / args.steps
 
     path = drafter.last_path()
-    ab = algorithmic_bytes(dims, lens_host, B)
+    ab = algorithmic_bytes(dims, lens_host, B, n_ingest)
     rounds_s = 1000.0 / ms
     # roofline of the round's kernel: algorithmic bytes per launch over the
     # average launch duration (the HIP-event time of the timed rounds on the
@@ -203,7 +218,9 @@ def main():
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
            "data": "synthetic",
-           "config": {"workload": f"{cfg['name']}: {B} streams x 1 round, draft block 4, "
+           "config": {"workload": f"{cfg['name']}: {B} streams x 1 round"
+                                  + (f" after ingesting {n_ingest} context rows per stream" if n_ingest else "")
+                                  + ", draft block 4, "
                                   f"context rows per stream {sorted(set(min(l, 2048) for l in lens_host))}, "
                                   f"block-FP8 body, NVFP4 head (60,614 rows)",
                       "streams": B, "draft_tokens_per_round": 4 * B,
