@@ -216,7 +216,10 @@ def main():
                 "avg_launch_us": round(launch_us, 3)}
     out = {"metric": METRIC, "value": round(rounds_s, 2), "unit": "rounds/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           # matrix products take f16 inputs (FP8 / NVFP4 weights decoded exactly) and
+           # accumulate in fp32; norms, softmax and the residual stream are fp32
+           "dtype": "f16",
            "data": "synthetic",
            "config": {"workload": f"{cfg['name']}: {B} streams x 1 round"
                                   + (f" after ingesting {n_ingest} context rows per stream" if n_ingest else "")
