@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #include "../../include/kdraft.h"
@@ -33,8 +34,7 @@ struct kd_ctx {
   bool small_ok = false;     // the window fits the small path's attention phase
   unsigned epoch = 0;        // grid barriers completed by persistent launches so far
   bool mega_ok = false;      // persistent cooperative kernel available
-  int path = 0;              // 0 auto, 1 general, 2 small per-phase, 3 small persistent,
-                             // 4 streamed persistent
+  int path = 0;              // 0 auto, 1 general, 2 small per-phase, 3 small persistent
   kd::SmallArgs* args_dev = nullptr;   // device copy of the small-path arguments
   // The per-phase launches of path 2 as one graph: the kernels read their
   // arguments from args_dev, so the graph depends only on the layer count and
@@ -46,6 +46,15 @@ struct kd_ctx {
   bool args_valid = false;
   unsigned long long* trace = nullptr;  // caller's device buffer for stage timestamps
   int trace_phases = 0;
+  // The general path's launches of a round (and of an ingest) as graphs: their
+  // kernel arguments hold the caller's pointers, so each graph is kept with the
+  // arguments it was captured for and captured again when they change (a
+  // serving loop that reuses its buffers captures once).
+  struct CachedGraph {
+    hipGraphExec_t exec = nullptr;
+    std::vector<unsigned char> key;
+  };
+  CachedGraph round_graph, ingest_graph;
 };
 
 namespace {
@@ -57,6 +66,58 @@ kd_status fail(kd_ctx* c, kd_status s, const std::string& msg) {
 
 kd_status hip_fail(kd_ctx* c, hipError_t e, const char* what) {
   return fail(c, KD_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+void drop_graph(kd_ctx::CachedGraph& g) {
+  if (g.exec) (void)hipGraphExecDestroy(g.exec);
+  g.exec = nullptr;
+  g.key.clear();
+}
+
+// Appends the bytes of v (a scalar or pointer: no padding) to a graph key.
+template <class T>
+void key_add(std::vector<unsigned char>& key, const T& v) {
+  static_assert(std::is_scalar<T>::value, "key fields are scalars");
+  const unsigned char* p = reinterpret_cast<const unsigned char*>(&v);
+  key.insert(key.end(), p, p + sizeof(T));
+}
+void key_add_kv(std::vector<unsigned char>& key, const kd::KV& k) {
+  for (int l = 0; l < 4; ++l) {
+    key_add(key, k.k[l]);
+    key_add(key, k.v[l]);
+  }
+  key_add(key, k.ss);
+  key_add(key, k.sh);
+  key_add(key, k.sl);
+  key_add(key, k.cap);
+}
+
+// Launches `enqueue`'s kernels on st as a graph: captured on the private
+// stream when key differs from the cached graph's, else replayed.
+template <class F>
+kd_status launch_cached(kd_ctx* c, kd_ctx::CachedGraph& g, std::vector<unsigned char>&& key,
+                        hipStream_t st, F&& enqueue, const char* what) {
+  if (!g.exec || g.key != key) {
+    drop_graph(g);
+    hipError_t e = hipSuccess;
+    if (!c->cap_stream) e = hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking);
+    hipGraph_t graph = nullptr;
+    if (e == hipSuccess) e = hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal);
+    if (e == hipSuccess) {
+      enqueue(c->cap_stream);
+      e = hipStreamEndCapture(c->cap_stream, &graph);
+    }
+    if (e == hipSuccess) e = hipGraphInstantiate(&g.exec, graph, nullptr, nullptr, 0);
+    if (graph) (void)hipGraphDestroy(graph);
+    if (e != hipSuccess) {
+      g.exec = nullptr;
+      return hip_fail(c, e, what);
+    }
+    g.key = std::move(key);
+  }
+  const hipError_t e = hipGraphLaunch(g.exec, st);
+  if (e != hipSuccess) return hip_fail(c, e, what);
+  return KD_OK;
 }
 
 template <typename T>
@@ -375,6 +436,8 @@ void kd_destroy(kd_ctx* ctx) {
   if (!ctx) return;
   (void)hipStreamSynchronize(ctx->stream);
   if (ctx->phase_graph) (void)hipGraphExecDestroy(ctx->phase_graph);
+  drop_graph(ctx->round_graph);
+  drop_graph(ctx->ingest_graph);
   if (ctx->cap_stream) (void)hipStreamDestroy(ctx->cap_stream);
   free_all(ctx->work_allocs);
   free_all(ctx->weight_allocs);
@@ -487,6 +550,8 @@ kd_status kd_load_weights(kd_ctx* c, const kd_weights* wt) {
   d.vocab = dv;
   d.table = static_cast<const uint16_t*>(wt->embed_table);
   c->args_valid = false;
+  drop_graph(c->round_graph);
+  drop_graph(c->ingest_graph);
   c->loaded = true;
   c->err.clear();
   return KD_OK;
@@ -511,7 +576,7 @@ kd_status kd_round(kd_ctx* c, int B, const void* taps, const int32_t* anchor, co
   const int R = kd::BLK * B, B3 = 3 * B;
   int path = c->path;
   // automatic: the per-phase launches (path 2) are the fastest measured small-
-  // batch form on MI355X; the persistent forms (3, 4) are kept selectable
+  // batch form on MI355X; the persistent form (3) is kept selectable
   if (path == 0) path = B <= kd::SB_MAX && c->small_ok ? 2 : 1;
   if (!c->small_ok) path = 1;
   if (path == 3 && !c->mega_ok) path = 2;
@@ -589,50 +654,64 @@ kd_status kd_round(kd_ctx* c, int B, const void* taps, const int32_t* anchor, co
   float* partB = w.part + w.part_elems / 2;
   const int nl = c->debug_layers < 0 ? kd::NL : c->debug_layers;
   (void)hipGetLastError();
+  auto enqueue = [&](hipStream_t st) {
 
-  kd::launch_prep(st, w, d, B, static_cast<const uint16_t*>(taps), lens, c->cfg.rope_theta);
-  const int s_fuse = kd::gemm_splits(d.fuse.K, d.fuse.N, B);
-  kd::launch_gemm(st, w.af_in, B, d.fuse, 0, d.fuse.N, partA, s_fuse);
-  kd::launch_post_fuse(st, w, d, B, s_fuse, anchor, pred);
-  const int s_fc = kd::gemm_splits(d.fc.K, d.fc.N, B);
-  kd::launch_gemm(st, w.af_fc, B, d.fc, 0, d.fc.N, partA, s_fc);
-  const int s_ab = kd::gemm_splits(d.pred_ab.K, d.pred_ab.N, B3);
-  kd::launch_gemm(st, w.af_ab, B3, d.pred_ab, 0, d.pred_ab.N, partB, s_ab);
-  kd::launch_silu_rank(st, partB, s_ab, B3, w.af_rank);
-  const int s_u = kd::gemm_splits(d.pred_u.K, d.pred_u.N, B3);
-  kd::launch_gemm(st, w.af_rank, B3, d.pred_u, 0, d.pred_u.N, partB, s_u);
-  kd::launch_rowbuild(st, w, d, B, s_fc, s_u, d.layer[0].attn_norm, eps);
+    kd::launch_prep(st, w, d, B, static_cast<const uint16_t*>(taps), lens, c->cfg.rope_theta);
+    const int s_fuse = kd::gemm_splits(d.fuse.K, d.fuse.N, B);
+    kd::launch_gemm(st, w.af_in, B, d.fuse, 0, d.fuse.N, partA, s_fuse);
+    kd::launch_post_fuse(st, w, d, B, s_fuse, anchor, pred);
+    const int s_fc = kd::gemm_splits(d.fc.K, d.fc.N, B);
+    kd::launch_gemm(st, w.af_fc, B, d.fc, 0, d.fc.N, partA, s_fc);
+    const int s_ab = kd::gemm_splits(d.pred_ab.K, d.pred_ab.N, B3);
+    kd::launch_gemm(st, w.af_ab, B3, d.pred_ab, 0, d.pred_ab.N, partB, s_ab);
+    kd::launch_silu_rank(st, partB, s_ab, B3, w.af_rank);
+    const int s_u = kd::gemm_splits(d.pred_u.K, d.pred_u.N, B3);
+    kd::launch_gemm(st, w.af_rank, B3, d.pred_u, 0, d.pred_u.N, partB, s_u);
+    kd::launch_rowbuild(st, w, d, B, s_fc, s_u, d.layer[0].attn_norm, eps);
 
-  for (int l = 0; l < nl; ++l) {
-    const kd::DevLayer& L = d.layer[l];
-    if (l >= 1) {
-      const int s_sa = kd::gemm_splits(L.sa.K, L.sa.N, B3);
-      kd::launch_gemm(st, w.af_sp, B3, L.sa, 0, L.sa.N, partA, s_sa);
-      kd::launch_silu_rank(st, partA, s_sa, B3, w.af_rank);
-      const int s_su = kd::gemm_splits(L.su.K, L.su.N, B3);
-      kd::launch_gemm(st, w.af_rank, B3, L.su, 0, L.su.N, partA, s_su);
-      kd::launch_spine_add_norm(st, w, B, s_su, L.attn_norm, eps);
+    for (int l = 0; l < nl; ++l) {
+      const kd::DevLayer& L = d.layer[l];
+      if (l >= 1) {
+        const int s_sa = kd::gemm_splits(L.sa.K, L.sa.N, B3);
+        kd::launch_gemm(st, w.af_sp, B3, L.sa, 0, L.sa.N, partA, s_sa);
+        kd::launch_silu_rank(st, partA, s_sa, B3, w.af_rank);
+        const int s_su = kd::gemm_splits(L.su.K, L.su.N, B3);
+        kd::launch_gemm(st, w.af_rank, B3, L.su, 0, L.su.N, partA, s_su);
+        kd::launch_spine_add_norm(st, w, B, s_su, L.attn_norm, eps);
+      }
+      const int s_qkv = kd::gemm_splits(L.qkv.K, L.qkv.N, R);
+      kd::launch_gemm(st, w.af_x, R, L.qkv, 0, L.qkv.N, partA, s_qkv);
+      kd::launch_qkv_post(st, w, B, s_qkv);
+      kd::launch_attention(st, w, B, k, l, lens, c->cfg.window);
+      const int s_o = kd::gemm_splits(L.wo.K, L.wo.N, R);
+      kd::launch_gemm(st, w.af_o, R, L.wo, 0, L.wo.N, partA, s_o);
+      kd::launch_resid_norm(st, w, R, s_o, L.ffn_norm, eps, w.af_x, 0);
+      const int s_gu = kd::gemm_splits(L.gu.K, L.gu.N, R);
+      kd::launch_gemm(st, w.af_x, R, L.gu, 0, L.gu.N, partA, s_gu);
+      kd::launch_swiglu(st, w, R, s_gu);
+      const int s_d = kd::gemm_splits(L.down.K, L.down.N, R);
+      kd::launch_gemm(st, w.af_h, R, L.down, 0, L.down.N, partA, s_d);
+      if (l + 1 < nl)
+        kd::launch_resid_norm(st, w, R, s_d, d.layer[l + 1].spine_norm, eps, w.af_sp, 1);
+      else
+        kd::launch_resid_norm(st, w, R, s_d, d.final_norm, eps, w.af_x, 0);
     }
-    const int s_qkv = kd::gemm_splits(L.qkv.K, L.qkv.N, R);
-    kd::launch_gemm(st, w.af_x, R, L.qkv, 0, L.qkv.N, partA, s_qkv);
-    kd::launch_qkv_post(st, w, B, s_qkv);
-    kd::launch_attention(st, w, B, k, l, lens, c->cfg.window);
-    const int s_o = kd::gemm_splits(L.wo.K, L.wo.N, R);
-    kd::launch_gemm(st, w.af_o, R, L.wo, 0, L.wo.N, partA, s_o);
-    kd::launch_resid_norm(st, w, R, s_o, L.ffn_norm, eps, w.af_x, 0);
-    const int s_gu = kd::gemm_splits(L.gu.K, L.gu.N, R);
-    kd::launch_gemm(st, w.af_x, R, L.gu, 0, L.gu.N, partA, s_gu);
-    kd::launch_swiglu(st, w, R, s_gu);
-    const int s_d = kd::gemm_splits(L.down.K, L.down.N, R);
-    kd::launch_gemm(st, w.af_h, R, L.down, 0, L.down.N, partA, s_d);
-    if (l + 1 < nl)
-      kd::launch_resid_norm(st, w, R, s_d, d.layer[l + 1].spine_norm, eps, w.af_sp, 1);
-    else
-      kd::launch_resid_norm(st, w, R, s_d, d.final_norm, eps, w.af_x, 0);
-  }
-  if (nl == 0) kd::launch_norm_rows(st, w.x, R, d.final_norm, eps, w.af_x);
-  kd::launch_head(st, w, d, R, out_logits);
-  kd::launch_finalize(st, w, d, R, out_ids);
+    if (nl == 0) kd::launch_norm_rows(st, w.x, R, d.final_norm, eps, w.af_x);
+    kd::launch_head(st, w, d, R, out_logits);
+    kd::launch_finalize(st, w, d, R, out_ids);
+  };
+  std::vector<unsigned char> key;
+  key_add(key, B);
+  key_add(key, nl);
+  key_add(key, taps);
+  key_add(key, anchor);
+  key_add(key, pred);
+  key_add_kv(key, k);
+  key_add(key, lens);
+  key_add(key, out_ids);
+  key_add(key, out_logits);
+  s = launch_cached(c, c->round_graph, std::move(key), st, enqueue, "general round graph");
+  if (s != KD_OK) return s;
   c->last_streams = B;
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(c, e, "kd_round launch");
@@ -656,21 +735,32 @@ kd_status kd_ingest(kd_ctx* c, int B, int n_new, const void* taps, const int32_t
   const hipStream_t st = c->stream;
   const int rows = B * n_new;
   (void)hipGetLastError();
-  kd::launch_ingest_prep(st, w, rows, static_cast<const uint16_t*>(taps));
-  const int s_fuse = kd::gemm_splits(d.fuse.K, d.fuse.N, rows);
-  kd::launch_gemm(st, w.af_in, rows, d.fuse, 0, d.fuse.N, w.part, s_fuse);
-  kd::launch_ingest_post_fuse(st, w, d, rows, s_fuse, next_ids);
-  const int s_fc = kd::gemm_splits(d.fc.K, d.fc.N, rows);
-  kd::launch_gemm(st, w.af_fc, rows, d.fc, 0, d.fc.N, w.part, s_fc);
-  kd::launch_ingest_c(st, w, rows, s_fc);
-  for (int l = 0; l < kd::NL; ++l) {
-    const kd::DevLayer& L = d.layer[l];
-    kd::launch_norm_rows(st, w.c, rows, L.attn_norm, c->cfg.rms_eps, w.af_x);
-    const int s_kv = kd::gemm_splits(L.qkv.K, 2 * kd::H, rows);
-    kd::launch_gemm(st, w.af_x, rows, L.qkv, kd::H / 16, 2 * kd::H, w.part, s_kv);
-    kd::launch_ingest_store(st, w, B, n_new, s_kv, k, l, lens, c->cfg.rope_theta);
-  }
-  kd::launch_bump_lens(st, lens, B, n_new);
+  auto enqueue = [&](hipStream_t st) {
+    kd::launch_ingest_prep(st, w, rows, static_cast<const uint16_t*>(taps));
+    const int s_fuse = kd::gemm_splits(d.fuse.K, d.fuse.N, rows);
+    kd::launch_gemm(st, w.af_in, rows, d.fuse, 0, d.fuse.N, w.part, s_fuse);
+    kd::launch_ingest_post_fuse(st, w, d, rows, s_fuse, next_ids);
+    const int s_fc = kd::gemm_splits(d.fc.K, d.fc.N, rows);
+    kd::launch_gemm(st, w.af_fc, rows, d.fc, 0, d.fc.N, w.part, s_fc);
+    kd::launch_ingest_c(st, w, rows, s_fc);
+    for (int l = 0; l < kd::NL; ++l) {
+      const kd::DevLayer& L = d.layer[l];
+      kd::launch_norm_rows(st, w.c, rows, L.attn_norm, c->cfg.rms_eps, w.af_x);
+      const int s_kv = kd::gemm_splits(L.qkv.K, 2 * kd::H, rows);
+      kd::launch_gemm(st, w.af_x, rows, L.qkv, kd::H / 16, 2 * kd::H, w.part, s_kv);
+      kd::launch_ingest_store(st, w, B, n_new, s_kv, k, l, lens, c->cfg.rope_theta);
+    }
+    kd::launch_bump_lens(st, lens, B, n_new);
+  };
+  std::vector<unsigned char> key;
+  key_add(key, B);
+  key_add(key, n_new);
+  key_add(key, taps);
+  key_add(key, next_ids);
+  key_add_kv(key, k);
+  key_add(key, lens);
+  s = launch_cached(c, c->ingest_graph, std::move(key), st, enqueue, "ingest graph");
+  if (s != KD_OK) return s;
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(c, e, "kd_ingest launch");
   return KD_OK;
