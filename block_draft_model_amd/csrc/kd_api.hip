@@ -35,15 +35,19 @@ struct kd_ctx {
   unsigned epoch = 0;        // grid barriers completed by persistent launches so far
   bool mega_ok = false;      // persistent cooperative kernel available
   int path = 0;              // 0 auto, 1 general, 2 small per-phase, 3 small persistent
-  kd::SmallArgs* args_dev = nullptr;   // device copy of the small-path arguments
-  // The per-phase launches of path 2 as one graph: the kernels read their
-  // arguments from args_dev, so the graph depends only on the layer count and
-  // the grid; it is captured on a private stream and launched on the caller's.
+  // Device copies of the small-path arguments: slot 0 for a call's first
+  // round, slot 1 for the later rounds of kd_round_depth (predecessors from
+  // the previous round's ids).
+  kd::SmallArgs* args_dev[2] = {nullptr, nullptr};
+  // The per-phase launches of path 2 as one graph per slot: the kernels read
+  // their arguments from args_dev[slot], so a graph depends only on the layer
+  // count and the grid; it is captured on a private stream and launched on the
+  // caller's.
   hipStream_t cap_stream = nullptr;
-  hipGraphExec_t phase_graph = nullptr;
-  int phase_graph_nl = -1;
-  kd::SmallArgs* args_host = nullptr;  // pinned host copy last uploaded
-  bool args_valid = false;
+  hipGraphExec_t phase_graph[2] = {nullptr, nullptr};
+  int phase_graph_nl[2] = {-1, -1};
+  kd::SmallArgs* args_host[2] = {nullptr, nullptr};  // pinned host copies last uploaded
+  bool args_valid[2] = {false, false};
   unsigned long long* trace = nullptr;  // caller's device buffer for stage timestamps
   int trace_phases = 0;
   // The general path's launches of a round (and of an ingest) as graphs: their
@@ -402,8 +406,10 @@ kd_status kd_create(const kd_config* cfg, void* hip_stream, kd_ctx** out) {
   c->small_ok = c->G >= kd::SB_MAX * kd::NH;
   if (ok && c->small_ok) {
     ok = dev_alloc(c->work_allocs, &c->small_mem, kd::small_bytes(w.att_nch)) &&
-         dev_alloc(c->work_allocs, &c->args_dev, 1) &&
-         hipHostMalloc((void**)&c->args_host, sizeof(kd::SmallArgs), hipHostMallocDefault) ==
+         dev_alloc(c->work_allocs, &c->args_dev[0], 1) && dev_alloc(c->work_allocs, &c->args_dev[1], 1) &&
+         hipHostMalloc((void**)&c->args_host[0], sizeof(kd::SmallArgs), hipHostMallocDefault) ==
+             hipSuccess &&
+         hipHostMalloc((void**)&c->args_host[1], sizeof(kd::SmallArgs), hipHostMallocDefault) ==
              hipSuccess;
     if (ok) {
       kd::small_carve(c->small_mem, w.att_nch, &c->small);
@@ -416,7 +422,8 @@ kd_status kd_create(const kd_config* cfg, void* hip_stream, kd_ctx** out) {
   }
   if (!ok) {
     free_all(c->work_allocs);
-    if (c->args_host) (void)hipHostFree(c->args_host);
+    for (int i = 0; i < 2; ++i)
+      if (c->args_host[i]) (void)hipHostFree(c->args_host[i]);
     delete c;
     return KD_ERR_OOM;
   }
@@ -435,13 +442,15 @@ kd_status kd_set_stream(kd_ctx* ctx, void* hip_stream) {
 void kd_destroy(kd_ctx* ctx) {
   if (!ctx) return;
   (void)hipStreamSynchronize(ctx->stream);
-  if (ctx->phase_graph) (void)hipGraphExecDestroy(ctx->phase_graph);
+  for (int i = 0; i < 2; ++i)
+    if (ctx->phase_graph[i]) (void)hipGraphExecDestroy(ctx->phase_graph[i]);
   drop_graph(ctx->round_graph);
   drop_graph(ctx->ingest_graph);
   if (ctx->cap_stream) (void)hipStreamDestroy(ctx->cap_stream);
   free_all(ctx->work_allocs);
   free_all(ctx->weight_allocs);
-  if (ctx->args_host) (void)hipHostFree(ctx->args_host);
+  for (int i = 0; i < 2; ++i)
+    if (ctx->args_host[i]) (void)hipHostFree(ctx->args_host[i]);
   delete ctx;
 }
 
@@ -549,7 +558,7 @@ kd_status kd_load_weights(kd_ctx* c, const kd_weights* wt) {
   d.VT = VT;
   d.vocab = dv;
   d.table = static_cast<const uint16_t*>(wt->embed_table);
-  c->args_valid = false;
+  c->args_valid[0] = c->args_valid[1] = false;
   drop_graph(c->round_graph);
   drop_graph(c->ingest_graph);
   c->loaded = true;
@@ -557,9 +566,11 @@ kd_status kd_load_weights(kd_ctx* c, const kd_weights* wt) {
   return KD_OK;
 }
 
-kd_status kd_round(kd_ctx* c, int B, const void* taps, const int32_t* anchor, const int32_t* pred,
-                   const kd_kv* kv, const int32_t* lens, int32_t* out_ids, float* out_logits) {
-  if (!c) return KD_ERR_ARG;
+// `depth` rounds; round r > 0 reads its predecessor ids from out_ids (the
+// previous round's drafts, 4 per stream).
+static kd_status round_impl(kd_ctx* c, int depth, int B, const void* taps, const int32_t* anchor,
+                            const int32_t* pred, const kd_kv* kv, const int32_t* lens,
+                            int32_t* out_ids, float* out_logits) {
   if (!c->loaded) return fail(c, KD_ERR_STATE, "kd_round before kd_load_weights");
   if (B < 1 || B > c->cfg.max_streams) return fail(c, KD_ERR_ARG, "streams out of range");
   if (!taps || !anchor || !pred || !lens || !out_ids)
@@ -584,66 +595,70 @@ kd_status kd_round(kd_ctx* c, int B, const void* taps, const int32_t* anchor, co
   c->last_path = path;
   if (path != 1) {
     (void)hipGetLastError();
-    kd::SmallArgs a;
-    memset(&a, 0, sizeof a);
-    a.B = B;
-    a.R = R;
-    a.nl = c->debug_layers < 0 ? kd::NL : c->debug_layers;
-    a.window = c->cfg.window;
-    // partial slots per (stream, head), padded to whole 128-byte lines of the
-    // per-chunk max and sum (8 chunks): different pairs never share a line
-    a.nch = (w.att_nch + 7) / 8 * 8;
-    a.eps = eps;
-    a.theta = c->cfg.rope_theta;
-    a.taps = static_cast<const uint16_t*>(taps);
-    a.anchor = anchor;
-    a.pred = pred;
-    a.lens = lens;
-    a.kv = k;
-    a.out_ids = out_ids;
-    a.out_logits = out_logits;
-    a.d = d;
-    a.s = c->small;
-    a.trace = c->trace;
-    a.trace_phases = c->trace_phases;
-    // upload the argument block only when it changed (a serving loop that
-    // reuses its buffers uploads it once)
-    if (!c->args_valid || memcmp(c->args_host, &a, sizeof a) != 0) {
-      hipError_t e = hipStreamSynchronize(st);   // the pinned copy may still be in flight
-      if (e == hipSuccess) {
-        memcpy(c->args_host, &a, sizeof a);
-        e = hipMemcpyAsync(c->args_dev, c->args_host, sizeof a, hipMemcpyHostToDevice, st);
-      }
-      if (e != hipSuccess) return hip_fail(c, e, "argument upload");
-      c->args_valid = true;
-    }
-    const int np = kd::small_phase_count(a.nl);
-    if (path == 3) {
-      const hipError_t e = kd::launch_small_mega(st, c->args_dev, c->G, c->epoch);
-      if (e != hipSuccess) return hip_fail(c, e, "persistent round launch");
-      c->epoch += (unsigned)(kd::small_phase_count(a.nl) - 1);
-    } else {
-      if (!c->phase_graph || c->phase_graph_nl != a.nl) {
-        hipError_t e = hipSuccess;
-        if (c->phase_graph) {
-          (void)hipGraphExecDestroy(c->phase_graph);
-          c->phase_graph = nullptr;
-        }
-        if (!c->cap_stream) e = hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking);
-        hipGraph_t g = nullptr;
-        if (e == hipSuccess) e = hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal);
+    for (int r = 0; r < depth; ++r) {
+      const int slot = r == 0 ? 0 : 1;
+      kd::SmallArgs a;
+      memset(&a, 0, sizeof a);
+      a.B = B;
+      a.R = R;
+      a.nl = c->debug_layers < 0 ? kd::NL : c->debug_layers;
+      a.window = c->cfg.window;
+      // partial slots per (stream, head), padded to whole 128-byte lines of the
+      // per-chunk max and sum (8 chunks): different pairs never share a line
+      a.nch = (w.att_nch + 7) / 8 * 8;
+      a.eps = eps;
+      a.theta = c->cfg.rope_theta;
+      a.taps = static_cast<const uint16_t*>(taps);
+      a.anchor = anchor;
+      a.pred = r == 0 ? pred : out_ids;
+      a.pred_stride = r == 0 ? kd::BLK - 1 : kd::BLK;
+      a.lens = lens;
+      a.kv = k;
+      a.out_ids = out_ids;
+      a.out_logits = r + 1 == depth ? out_logits : nullptr;
+      a.d = d;
+      a.s = c->small;
+      a.trace = c->trace;
+      a.trace_phases = c->trace_phases;
+      // upload the argument block only when it changed (a serving loop that
+      // reuses its buffers uploads it once)
+      if (!c->args_valid[slot] || memcmp(c->args_host[slot], &a, sizeof a) != 0) {
+        hipError_t e = hipStreamSynchronize(st);   // the pinned copy may still be in flight
         if (e == hipSuccess) {
-          for (int i = 0; i < np; ++i)
-            kd::launch_small_phase(c->cap_stream, c->args_dev, c->G, kd::small_phase_id(a.nl, i), i);
-          e = hipStreamEndCapture(c->cap_stream, &g);
+          memcpy(c->args_host[slot], &a, sizeof a);
+          e = hipMemcpyAsync(c->args_dev[slot], c->args_host[slot], sizeof a, hipMemcpyHostToDevice, st);
         }
-        if (e == hipSuccess) e = hipGraphInstantiate(&c->phase_graph, g, nullptr, nullptr, 0);
-        if (g) (void)hipGraphDestroy(g);
-        if (e != hipSuccess) return hip_fail(c, e, "phase graph capture");
-        c->phase_graph_nl = a.nl;
+        if (e != hipSuccess) return hip_fail(c, e, "argument upload");
+        c->args_valid[slot] = true;
       }
-      const hipError_t e = hipGraphLaunch(c->phase_graph, st);
-      if (e != hipSuccess) return hip_fail(c, e, "phase graph launch");
+      const int np = kd::small_phase_count(a.nl);
+      if (path == 3) {
+        const hipError_t e = kd::launch_small_mega(st, c->args_dev[slot], c->G, c->epoch);
+        if (e != hipSuccess) return hip_fail(c, e, "persistent round launch");
+        c->epoch += (unsigned)(np - 1);
+      } else {
+        if (!c->phase_graph[slot] || c->phase_graph_nl[slot] != a.nl) {
+          hipError_t e = hipSuccess;
+          if (c->phase_graph[slot]) {
+            (void)hipGraphExecDestroy(c->phase_graph[slot]);
+            c->phase_graph[slot] = nullptr;
+          }
+          if (!c->cap_stream) e = hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking);
+          hipGraph_t g = nullptr;
+          if (e == hipSuccess) e = hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal);
+          if (e == hipSuccess) {
+            for (int i = 0; i < np; ++i)
+              kd::launch_small_phase(c->cap_stream, c->args_dev[slot], c->G, kd::small_phase_id(a.nl, i), i);
+            e = hipStreamEndCapture(c->cap_stream, &g);
+          }
+          if (e == hipSuccess) e = hipGraphInstantiate(&c->phase_graph[slot], g, nullptr, nullptr, 0);
+          if (g) (void)hipGraphDestroy(g);
+          if (e != hipSuccess) return hip_fail(c, e, "phase graph capture");
+          c->phase_graph_nl[slot] = a.nl;
+        }
+        const hipError_t e = hipGraphLaunch(c->phase_graph[slot], st);
+        if (e != hipSuccess) return hip_fail(c, e, "phase graph launch");
+      }
     }
     c->last_streams = B;
     const hipError_t e = hipGetLastError();
@@ -655,52 +670,56 @@ kd_status kd_round(kd_ctx* c, int B, const void* taps, const int32_t* anchor, co
   const int nl = c->debug_layers < 0 ? kd::NL : c->debug_layers;
   (void)hipGetLastError();
   auto enqueue = [&](hipStream_t st) {
+    for (int r = 0; r < depth; ++r) {
+      const int32_t* pred_r = r == 0 ? pred : out_ids;
+      const int pred_stride = r == 0 ? kd::BLK - 1 : kd::BLK;
+      kd::launch_prep(st, w, d, B, static_cast<const uint16_t*>(taps), lens, c->cfg.rope_theta);
+      const int s_fuse = kd::gemm_splits(d.fuse.K, d.fuse.N, B);
+      kd::launch_gemm(st, w.af_in, B, d.fuse, 0, d.fuse.N, partA, s_fuse);
+      kd::launch_post_fuse(st, w, d, B, s_fuse, anchor, pred_r, pred_stride);
+      const int s_fc = kd::gemm_splits(d.fc.K, d.fc.N, B);
+      kd::launch_gemm(st, w.af_fc, B, d.fc, 0, d.fc.N, partA, s_fc);
+      const int s_ab = kd::gemm_splits(d.pred_ab.K, d.pred_ab.N, B3);
+      kd::launch_gemm(st, w.af_ab, B3, d.pred_ab, 0, d.pred_ab.N, partB, s_ab);
+      kd::launch_silu_rank(st, partB, s_ab, B3, w.af_rank);
+      const int s_u = kd::gemm_splits(d.pred_u.K, d.pred_u.N, B3);
+      kd::launch_gemm(st, w.af_rank, B3, d.pred_u, 0, d.pred_u.N, partB, s_u);
+      kd::launch_rowbuild(st, w, d, B, s_fc, s_u, d.layer[0].attn_norm, eps);
 
-    kd::launch_prep(st, w, d, B, static_cast<const uint16_t*>(taps), lens, c->cfg.rope_theta);
-    const int s_fuse = kd::gemm_splits(d.fuse.K, d.fuse.N, B);
-    kd::launch_gemm(st, w.af_in, B, d.fuse, 0, d.fuse.N, partA, s_fuse);
-    kd::launch_post_fuse(st, w, d, B, s_fuse, anchor, pred);
-    const int s_fc = kd::gemm_splits(d.fc.K, d.fc.N, B);
-    kd::launch_gemm(st, w.af_fc, B, d.fc, 0, d.fc.N, partA, s_fc);
-    const int s_ab = kd::gemm_splits(d.pred_ab.K, d.pred_ab.N, B3);
-    kd::launch_gemm(st, w.af_ab, B3, d.pred_ab, 0, d.pred_ab.N, partB, s_ab);
-    kd::launch_silu_rank(st, partB, s_ab, B3, w.af_rank);
-    const int s_u = kd::gemm_splits(d.pred_u.K, d.pred_u.N, B3);
-    kd::launch_gemm(st, w.af_rank, B3, d.pred_u, 0, d.pred_u.N, partB, s_u);
-    kd::launch_rowbuild(st, w, d, B, s_fc, s_u, d.layer[0].attn_norm, eps);
-
-    for (int l = 0; l < nl; ++l) {
-      const kd::DevLayer& L = d.layer[l];
-      if (l >= 1) {
-        const int s_sa = kd::gemm_splits(L.sa.K, L.sa.N, B3);
-        kd::launch_gemm(st, w.af_sp, B3, L.sa, 0, L.sa.N, partA, s_sa);
-        kd::launch_silu_rank(st, partA, s_sa, B3, w.af_rank);
-        const int s_su = kd::gemm_splits(L.su.K, L.su.N, B3);
-        kd::launch_gemm(st, w.af_rank, B3, L.su, 0, L.su.N, partA, s_su);
-        kd::launch_spine_add_norm(st, w, B, s_su, L.attn_norm, eps);
+      for (int l = 0; l < nl; ++l) {
+        const kd::DevLayer& L = d.layer[l];
+        if (l >= 1) {
+          const int s_sa = kd::gemm_splits(L.sa.K, L.sa.N, B3);
+          kd::launch_gemm(st, w.af_sp, B3, L.sa, 0, L.sa.N, partA, s_sa);
+          kd::launch_silu_rank(st, partA, s_sa, B3, w.af_rank);
+          const int s_su = kd::gemm_splits(L.su.K, L.su.N, B3);
+          kd::launch_gemm(st, w.af_rank, B3, L.su, 0, L.su.N, partA, s_su);
+          kd::launch_spine_add_norm(st, w, B, s_su, L.attn_norm, eps);
+        }
+        const int s_qkv = kd::gemm_splits(L.qkv.K, L.qkv.N, R);
+        kd::launch_gemm(st, w.af_x, R, L.qkv, 0, L.qkv.N, partA, s_qkv);
+        kd::launch_qkv_post(st, w, B, s_qkv);
+        kd::launch_attention(st, w, B, k, l, lens, c->cfg.window);
+        const int s_o = kd::gemm_splits(L.wo.K, L.wo.N, R);
+        kd::launch_gemm(st, w.af_o, R, L.wo, 0, L.wo.N, partA, s_o);
+        kd::launch_resid_norm(st, w, R, s_o, L.ffn_norm, eps, w.af_x, 0);
+        const int s_gu = kd::gemm_splits(L.gu.K, L.gu.N, R);
+        kd::launch_gemm(st, w.af_x, R, L.gu, 0, L.gu.N, partA, s_gu);
+        kd::launch_swiglu(st, w, R, s_gu);
+        const int s_d = kd::gemm_splits(L.down.K, L.down.N, R);
+        kd::launch_gemm(st, w.af_h, R, L.down, 0, L.down.N, partA, s_d);
+        if (l + 1 < nl)
+          kd::launch_resid_norm(st, w, R, s_d, d.layer[l + 1].spine_norm, eps, w.af_sp, 1);
+        else
+          kd::launch_resid_norm(st, w, R, s_d, d.final_norm, eps, w.af_x, 0);
       }
-      const int s_qkv = kd::gemm_splits(L.qkv.K, L.qkv.N, R);
-      kd::launch_gemm(st, w.af_x, R, L.qkv, 0, L.qkv.N, partA, s_qkv);
-      kd::launch_qkv_post(st, w, B, s_qkv);
-      kd::launch_attention(st, w, B, k, l, lens, c->cfg.window);
-      const int s_o = kd::gemm_splits(L.wo.K, L.wo.N, R);
-      kd::launch_gemm(st, w.af_o, R, L.wo, 0, L.wo.N, partA, s_o);
-      kd::launch_resid_norm(st, w, R, s_o, L.ffn_norm, eps, w.af_x, 0);
-      const int s_gu = kd::gemm_splits(L.gu.K, L.gu.N, R);
-      kd::launch_gemm(st, w.af_x, R, L.gu, 0, L.gu.N, partA, s_gu);
-      kd::launch_swiglu(st, w, R, s_gu);
-      const int s_d = kd::gemm_splits(L.down.K, L.down.N, R);
-      kd::launch_gemm(st, w.af_h, R, L.down, 0, L.down.N, partA, s_d);
-      if (l + 1 < nl)
-        kd::launch_resid_norm(st, w, R, s_d, d.layer[l + 1].spine_norm, eps, w.af_sp, 1);
-      else
-        kd::launch_resid_norm(st, w, R, s_d, d.final_norm, eps, w.af_x, 0);
+      if (nl == 0) kd::launch_norm_rows(st, w.x, R, d.final_norm, eps, w.af_x);
+      kd::launch_head(st, w, d, R, r + 1 == depth ? out_logits : nullptr);
+      kd::launch_finalize(st, w, d, R, out_ids);
     }
-    if (nl == 0) kd::launch_norm_rows(st, w.x, R, d.final_norm, eps, w.af_x);
-    kd::launch_head(st, w, d, R, out_logits);
-    kd::launch_finalize(st, w, d, R, out_ids);
   };
   std::vector<unsigned char> key;
+  key_add(key, depth);
   key_add(key, B);
   key_add(key, nl);
   key_add(key, taps);
@@ -716,6 +735,20 @@ kd_status kd_round(kd_ctx* c, int B, const void* taps, const int32_t* anchor, co
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(c, e, "kd_round launch");
   return KD_OK;
+}
+
+kd_status kd_round(kd_ctx* c, int B, const void* taps, const int32_t* anchor, const int32_t* pred,
+                   const kd_kv* kv, const int32_t* lens, int32_t* out_ids, float* out_logits) {
+  if (!c) return KD_ERR_ARG;
+  return round_impl(c, 1, B, taps, anchor, pred, kv, lens, out_ids, out_logits);
+}
+
+kd_status kd_round_depth(kd_ctx* c, int depth, int B, const void* taps, const int32_t* anchor,
+                         const int32_t* pred, const kd_kv* kv, const int32_t* lens,
+                         int32_t* out_ids, float* out_logits) {
+  if (!c) return KD_ERR_ARG;
+  if (depth < 1 || depth > KD_MAX_DEPTH) return fail(c, KD_ERR_ARG, "depth out of range");
+  return round_impl(c, depth, B, taps, anchor, pred, kv, lens, out_ids, out_logits);
 }
 
 kd_status kd_ingest(kd_ctx* c, int B, int n_new, const void* taps, const int32_t* next_ids,

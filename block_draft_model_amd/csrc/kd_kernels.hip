@@ -144,7 +144,7 @@ void launch_prep(hipStream_t st, const Work& w, const DevWeights& d, int B, cons
 __global__ __launch_bounds__(320) void k_post_fuse(const float* part, int splits, int B, float* f,
                                                    uint16_t* af_fc, uint16_t* af_ab,
                                                    const uint16_t* table, const int32_t* anchor,
-                                                   const int32_t* pred) {
+                                                   const int32_t* pred, int pred_stride) {
   const int b = blockIdx.x, c0 = threadIdx.x * 8;
   constexpr int KT = 2 * H / 32;
   float v[8];
@@ -162,14 +162,15 @@ __global__ __launch_bounds__(320) void k_post_fuse(const float* part, int splits
   store_afrag8_bf16(af_fc, KT, b, H + c0, ea);
   for (int j = 0; j < BLK - 1; ++j) {
     store_afrag8(af_ab, KT, b * 3 + j, c0, v);
-    const u32x4 ep = *reinterpret_cast<const u32x4*>(table + (size_t)pred[b * 3 + j] * H + c0);
+    const u32x4 ep = *reinterpret_cast<const u32x4*>(table + (size_t)pred[b * pred_stride + j] * H + c0);
     store_afrag8_bf16(af_ab, KT, b * 3 + j, H + c0, ep);
   }
 }
 
 void launch_post_fuse(hipStream_t st, const Work& w, const DevWeights& d, int B, int splits,
-                      const int32_t* anchor, const int32_t* pred) {
-  k_post_fuse<<<B, 320, 0, st>>>(w.part, splits, B, w.f, w.af_fc, w.af_ab, d.table, anchor, pred);
+                      const int32_t* anchor, const int32_t* pred, int pred_stride) {
+  k_post_fuse<<<B, 320, 0, st>>>(w.part, splits, B, w.f, w.af_fc, w.af_ab, d.table, anchor, pred,
+                                 pred_stride);
 }
 
 // afrag of silu(sum of partials) for a rank-256 hidden vector.

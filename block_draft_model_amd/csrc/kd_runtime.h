@@ -105,8 +105,9 @@ void launch_gemm(hipStream_t st, const uint16_t* af, int R, const Fp8Mat& W, int
                  int N, float* part, int splits);
 void launch_prep(hipStream_t st, const Work& w, const DevWeights& d, int B, const uint16_t* taps,
                  const int32_t* lens, float theta);
+// pred_stride: ids per stream in pred (3, or 4 for a previous round's out_ids)
 void launch_post_fuse(hipStream_t st, const Work& w, const DevWeights& d, int B, int splits,
-                      const int32_t* anchor, const int32_t* pred);
+                      const int32_t* anchor, const int32_t* pred, int pred_stride);
 void launch_silu_rank(hipStream_t st, const float* part, int splits, int rows, uint16_t* af);
 void launch_rowbuild(hipStream_t st, const Work& w, const DevWeights& d, int B, int splits_fc,
                      int splits_u, const float* gain, float eps);

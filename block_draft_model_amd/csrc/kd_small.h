@@ -61,6 +61,7 @@ struct SmallArgsT {
   P<const uint16_t> taps;
   P<const int32_t> anchor;
   P<const int32_t> pred;
+  int pred_stride;              // ids per stream in pred: 3 (caller's), 4 (previous round's out_ids)
   P<const int32_t> lens;
   KVT<P> kv;
   P<int32_t> out_ids;

@@ -317,7 +317,8 @@ __device__ __forceinline__ void load_w(WRegs<NT, KBS>& r, Mat& W, int tile0, int
 struct ASrc {
   gptr<const void> base;
   int ld;               // elements per row
-  int mode;             // 0: row r; 1: row r/3; 2: row 4(r/3) + r%3; 3: row ids[r]
+  int mode;             // 0: row r; 1: row r/3; 2: row 4(r/3) + r%3; 3: row ids[r];
+                        // 4: row ids[4(r/3) + r%3]
   gptr<const int32_t> ids;
   int kb_off;           // weight block of column 0
   int R;
@@ -328,6 +329,7 @@ __device__ __forceinline__ size_t a_row(const ASrc& A, int r) {
     case 1: return (size_t)(r / 3);
     case 2: return (size_t)(4 * (r / 3) + r % 3);
     case 3: return (size_t)A.ids[r];
+    case 4: return (size_t)A.ids[4 * (r / 3) + r % 3];
     default: return (size_t)r;
   }
 }
@@ -536,7 +538,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_pre0(Args& a_, lds
                                });
     } else {
       const int t = u - n_fuse - n_fce;
-      const ASrc A{d.table, H, 3, a.pred, 40, 3 * B};
+      const ASrc A{d.table, H, a.pred_stride == 4 ? 4 : 3, a.pred, 40, 3 * B};
       gemm_unit<1, 5, 8, true>(a, sy, false, d.pred_ab, t, 1, 40, A, red, no_rms(),
                                [&](int, int m, int n, float v) {
                                  if (m < 3 * B) st_wt(&s.pb[m * RK + t * 16 + n], v);

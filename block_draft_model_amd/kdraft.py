@@ -50,7 +50,8 @@ class KdKV(ctypes.Structure):
                 ("stride_head", c_int64), ("stride_slot", c_int64), ("capacity", c_int)]
 
 
-EXPORTS = ["kd_default_config", "kd_create", "kd_load_weights", "kd_round", "kd_ingest",
+EXPORTS = ["kd_default_config", "kd_create", "kd_load_weights", "kd_round", "kd_round_depth",
+           "kd_ingest",
            "kd_set_stream", "kd_destroy", "kd_status_string", "kd_last_error",
            "kd_probe_decode_e4m3", "kd_probe_decode_e4m3_f16", "kd_probe_decode_nvfp4", "kd_debug_set_layers",
            "kd_debug_buffers", "kd_debug_set_path", "kd_debug_last_path",
@@ -83,6 +84,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kd_round.argtypes = [c_void_p, c_int, c_void_p, c_void_p, c_void_p, P(KdKV), c_void_p,
                              c_void_p, c_void_p]
     lib.kd_round.restype = c_int
+    lib.kd_round_depth.argtypes = [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, P(KdKV),
+                                   c_void_p, c_void_p, c_void_p]
+    lib.kd_round_depth.restype = c_int
     lib.kd_ingest.argtypes = [c_void_p, c_int, c_int, c_void_p, c_void_p, P(KdKV), c_void_p]
     lib.kd_ingest.restype = c_int
     lib.kd_set_stream.argtypes = [c_void_p, c_void_p]
@@ -166,7 +170,7 @@ def _host(t):
 
 
 class Drafter:
-    """Owns one kd_ctx. Methods mirror kd_load_weights / kd_round / kd_ingest."""
+    """Owns one kd_ctx. Methods mirror kd_load_weights / kd_round / kd_round_depth / kd_ingest."""
 
     def __init__(self, max_streams: int = 256, stream=None, **cfg_over):
         self.lib = load_library()
@@ -225,6 +229,13 @@ class Drafter:
         self._check(self.lib.kd_round(self.ctx, int(streams), _ptr(taps), _ptr(anchor), _ptr(pred),
                                       ctypes.byref(kv), _ptr(lens), _ptr(out_ids), _ptr(out_logits)),
                     "kd_round")
+
+    def round_depth(self, depth, streams, taps, anchor, pred, kv: KdKV, lens, out_ids,
+                    out_logits=None):
+        self._check(self.lib.kd_round_depth(self.ctx, int(depth), int(streams), _ptr(taps),
+                                            _ptr(anchor), _ptr(pred), ctypes.byref(kv), _ptr(lens),
+                                            _ptr(out_ids), _ptr(out_logits)),
+                    "kd_round_depth")
 
     def ingest(self, streams, n_new, taps, next_ids, kv: KdKV, lens):
         self._check(self.lib.kd_ingest(self.ctx, int(streams), int(n_new), _ptr(taps), _ptr(next_ids),

@@ -54,6 +54,7 @@ typedef enum {
 
 enum { KD_QUANT_FP8_BLOCK64 = 1, KD_QUANT_NVFP4 = 2 };
 enum { KD_MAX_INGEST = 8 };  /* rows per stream per kd_ingest call */
+enum { KD_MAX_DEPTH = 8 };   /* rounds per kd_round_depth call */
 
 /* Model shape and limits. The kernels are built for the model card's shape;
  * kd_create returns KD_ERR_UNSUPPORTED for any other hidden, heads, head_dim,
@@ -155,6 +156,20 @@ kd_status kd_round(kd_ctx* ctx, int streams, const void* tapped_states,
                    const int32_t* anchor_ids, const int32_t* pred_ids,
                    const kd_kv* ctx_kv, const int32_t* ctx_lens,
                    int32_t* out_ids, float* out_logits);
+
+/* `depth` rounds in a row before the target verifies (model card,
+ * Architecture: Serving runs several drafter rounds in a row, and at serving
+ * the predecessor token a row reads is the drafter's own previous draft;
+ * section Files: the serving default is depth 2). Round 1 is kd_round with
+ * the caller's pred_ids; every later round is the same round with
+ * pred_ids[b][j-1] = the previous round's out_ids[b][j-1], taken on the
+ * device. out_ids and out_logits receive the last round's results (earlier
+ * rounds write out_ids and no logits). depth = 1 is kd_round. Arguments as
+ * for kd_round; KD_ERR_ARG for depth < 1 or depth > KD_MAX_DEPTH. */
+kd_status kd_round_depth(kd_ctx* ctx, int depth, int streams, const void* tapped_states,
+                         const int32_t* anchor_ids, const int32_t* pred_ids,
+                         const kd_kv* ctx_kv, const int32_t* ctx_lens,
+                         int32_t* out_ids, float* out_logits);
 
 /* Appends n_new context rows per stream (1 <= n_new <= KD_MAX_INGEST): row i
  * of stream b is [fuse(taps[b][i]) ; embed(next_ids[b][i])] -> fc, projected

@@ -6,8 +6,9 @@ TEST INFRASTRUCTURE ONLY. Only the tests, ``__graft_entry__.smoke()`` and the
 """
 from .kdraft_oracle import (decode_e4m3, decode_e2m1, decode_bf16, round_bf16,
                             block_fp8, nvfp4, rmsnorm, silu, rope, attention,
-                            OracleModel, oracle_round, oracle_ingest, top2_gap)
+                            OracleModel, oracle_round, oracle_round_depth, oracle_ingest,
+                            top2_gap)
 
 __all__ = ["decode_e4m3", "decode_e2m1", "decode_bf16", "round_bf16", "block_fp8", "nvfp4",
            "rmsnorm", "silu", "rope", "attention", "OracleModel", "oracle_round",
-           "oracle_ingest", "top2_gap"]
+           "oracle_round_depth", "oracle_ingest", "top2_gap"]

@@ -274,6 +274,19 @@ def oracle_round(M: OracleModel, inp: dict, block: int | None = None,
     return logits, ids
 
 
+def oracle_round_depth(M: OracleModel, inp: dict, depth: int):
+    """`depth` rounds in a row (model card, "Architecture", Serving: several
+    drafter rounds run before the target verifies; Predecessor head: at serving
+    the token before a row is the drafter's own previous draft). Round 1 takes
+    the given predecessor ids; round r+1 takes pred[b][j-1] = round r's draft
+    of block row j-1. Returns the last round's (logits, ids)."""
+    cur = dict(inp)
+    for r in range(depth):
+        logits, ids = oracle_round(M, cur)
+        cur = dict(cur, pred=np.asarray(ids)[:, : M.dims.block - 1].copy())
+    return logits, ids
+
+
 def oracle_ingest(M: OracleModel, inp: dict, return_exact: bool = False):
     """Append new context rows (model card, "Architecture", Input: context rows
     are [fused state ; embedding of the next token] -> 5120->2560; Body: the

@@ -305,6 +305,73 @@ def test_stream_alone_equals_stream_in_batch(hC):
     hC.drafter.debug_set_path(0)
 
 
+def _run_depth(h, inp, depth):
+    B = inp["streams"]
+    kv = kdraft.kv_struct(inp["k"], inp["v"])
+    ids = torch.full((B, 4), -7, dtype=torch.int32, device="cuda")
+    lg = torch.full((B, 4, synth.FULL.draft_vocab), float("nan"), device="cuda")
+    h.drafter.round_depth(depth, B, inp["taps"], inp["anchor"], inp["pred"], kv, inp["lens"], ids, lg)
+    torch.cuda.synchronize()
+    return lg.cpu().numpy().astype(np.float64), ids.cpu().numpy()
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_depth_two_rounds(hC, path):
+    """Two rounds in a row: the second takes the first's drafts as its
+    predecessor ids on the device. It equals a round called with those drafts
+    as pred_ids, and both rounds meet the acceptance rule against the oracle
+    (round 2's reference takes the GPU's round-1 drafts, which may differ from
+    the oracle's only where its top two logits are within the gap)."""
+    cfg = dict(name="depth", streams=3, lens=("uniform", 50, 2500), model="C", ingest=0)
+    inp = hC.inputs(cfg, base=37)
+    hC.drafter.debug_set_path(path)
+    try:
+        lg1, ids1 = hC.run(inp)
+        lg2, ids2 = _run_depth(hC, inp, 2)
+        assert hC.drafter.last_path() == path
+        alt = dict(inp)
+        alt["pred"] = torch.from_numpy(np.ascontiguousarray(ids1[:, :3])).to("cuda")
+        lga, idsa = hC.run(alt)
+        lgd1, idsd1 = _run_depth(hC, inp, 1)
+    finally:
+        hC.drafter.debug_set_path(0)
+    assert np.array_equal(lgd1, lg1) and np.array_equal(idsd1, ids1)   # depth 1 is kd_round
+    assert np.array_equal(lg2, lga) and np.array_equal(ids2, idsa)
+    assert np.array_equal(lg2[:, 0], lg1[:, 0])                      # row 0 reads no predecessor
+    assert not np.array_equal(ids1[:, :3], inp["pred"].cpu().numpy())  # the predecessors changed
+    assert not np.allclose(lg2[:, 1:], lg1[:, 1:], rtol=1e-3, atol=1e-3)  # and moved rows 1..3
+    ref1, rid1 = oracle.oracle_round(hC.oracle, synth.to_numpy_inputs(inp))
+    compare(lg1, ids1, ref1, rid1, hC.oracle.vocab, f"depth round 1 path {path}")
+    ref2, rid2 = oracle.oracle_round(hC.oracle, synth.to_numpy_inputs(alt))
+    compare(lg2, ids2, ref2, rid2, hC.oracle.vocab, f"depth round 2 path {path}")
+
+
+def test_depth_general_path_batch(hB):
+    # more than 4 streams: the general path chains the rounds inside one graph
+    cfg = dict(name="depth-gen", streams=6, lens=("uniform", 200, 2048), model="B", ingest=0)
+    inp = hB.inputs(cfg, base=41)
+    lg1, ids1 = hB.run(inp)
+    lg3, ids3 = _run_depth(hB, inp, 3)
+    alt = dict(inp)
+    alt["pred"] = torch.from_numpy(np.ascontiguousarray(ids1[:, :3])).to("cuda")
+    lg2, ids2 = hB.run(alt)
+    alt2 = dict(inp)
+    alt2["pred"] = torch.from_numpy(np.ascontiguousarray(ids2[:, :3])).to("cuda")
+    lga, idsa = hB.run(alt2)
+    assert np.array_equal(lg3, lga) and np.array_equal(ids3, idsa)
+    ref, rid = oracle.oracle_round(hB.oracle, synth.to_numpy_inputs(alt2))
+    compare(lg3, ids3, ref, rid, hB.oracle.vocab, "depth 3, 6 streams")
+
+
+def test_depth_argument_errors(hC):
+    cfg = dict(name="derr", streams=2, lens=("const", 5), model="C", ingest=0)
+    inp = hC.inputs(cfg, base=43)
+    for depth in (0, 9):
+        with pytest.raises(kdraft.KDraftError) as e:
+            _run_depth(hC, inp, depth)
+        assert e.value.status == kdraft.KD_ERR_ARG
+
+
 def test_gpu_argument_errors(hC):
     B = 2
     cfg = dict(name="err", streams=B, lens=("const", 5), model="C", ingest=0)

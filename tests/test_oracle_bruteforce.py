@@ -204,3 +204,32 @@ def test_ingest_matches_brute_force(setup):
     logits, _ = oracle.oracle_round(M, after)
     want = np.array(brute.round_one(inp["taps"][0], inp["anchor"][0], inp["pred"][0], 33, kc, vc))
     assert np.allclose(logits[0], want, rtol=1e-6, atol=1e-8)
+
+
+def test_depth_two_matches_brute_force(setup):
+    """Two rounds in a row (model card, Architecture, Serving; Predecessor
+    head: at serving a row's predecessor is the drafter's own previous draft):
+    the brute-force round run again with its own first-round drafts as
+    predecessors."""
+    mnp, M, brute = setup
+    length = 20
+    cfg = dict(name="bfd", streams=1, lens=("const", length), model="C", ingest=0)
+    inp = synth.to_numpy_inputs(synth.make_inputs(cfg, D, vocab=torch.from_numpy(mnp["vocab"]),
+                                                  poison=True))
+    logits, ids = oracle.oracle_round_depth(M, inp, 2)
+    kc, vc = [k[0] for k in inp["k"]], [v[0] for v in inp["v"]]
+    first = brute.round_one(inp["taps"][0], inp["anchor"][0], inp["pred"][0], length, kc, vc)
+    # each row's draft: the vocabulary entry at its first maximum
+    drafts = []
+    for row in first:
+        best = 0
+        for i in range(1, len(row)):
+            if row[i] > row[best]:
+                best = i
+        drafts.append(int(mnp["vocab"][best]))
+    second = np.array(brute.round_one(inp["taps"][0], inp["anchor"][0], drafts[:3], length, kc, vc))
+    assert np.allclose(logits[0], second, rtol=1e-10, atol=1e-12)
+    # row 0 never reads a predecessor: the same in both rounds
+    assert np.allclose(logits[0][0], np.array(first[0]), rtol=1e-10, atol=1e-12)
+    # the predecessors did change (else the test would not see the chaining)
+    assert list(drafts[:3]) != [int(t) for t in inp["pred"][0]]

@@ -191,3 +191,22 @@ def test_ingest_then_round_is_finite_and_moves_lengths(models):
         assert not np.any(np.isnan(oracle.decode_bf16(after["k"][l])))
     logits, _ = oracle.oracle_round(M, after)
     assert np.all(np.isfinite(logits))
+
+
+def test_depth_one_is_one_round_and_row0_ignores_depth(models, inputs):
+    M = models["B"][1]
+    one, ids1 = oracle.oracle_round(M, inputs)
+    d1, i1 = oracle.oracle_round_depth(M, inputs, 1)
+    assert np.array_equal(one, d1) and np.array_equal(ids1, i1)
+    d2, _ = oracle.oracle_round_depth(M, inputs, 2)
+    # row 0 never reads a predecessor (Position 1 bullet): identical at any depth
+    assert np.array_equal(d2[:, 0], one[:, 0])
+    assert not np.allclose(d2[:, 1:], one[:, 1:])
+
+
+def test_depth_with_zero_predecessor_head_is_one_round(models, inputs):
+    # model A's predecessor U is zero: predecessors cannot change any row
+    M = models["A"][1]
+    one, ids1 = oracle.oracle_round(M, inputs)
+    d3, i3 = oracle.oracle_round_depth(M, inputs, 3)
+    assert np.array_equal(one, d3) and np.array_equal(ids1, i3)
