@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libkdraft.so")
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("kd_kernels.hip", "kd_mm.hip", "kd_small.hip", "kd_api.hip")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("kd_kernels.hip", "kd_mm.hip", "kd_copy.hip", "kd_small.hip", "kd_api.hip")]
 HEADERS = [os.path.join(HERE, "csrc", f) for f in ("kd_device.h", "kd_runtime.h", "kd_small.h")] + [
     os.path.join(ROOT, "include", f) for f in ("kdraft.h", "kdraft_debug.h")]
 ARCH = "gfx950"

@@ -397,7 +397,8 @@ kd_status kd_create(const kd_config* cfg, void* hip_stream, kd_ctx** out) {
             dev_alloc(c->work_allocs, &w.att_l, (size_t)w.Bmax * kd::NH * w.att_nch * kd::BLK) &&
             dev_alloc(c->work_allocs, &w.att_o,
                       (size_t)w.Bmax * kd::NH * w.att_nch * kd::BLK * kd::DH) &&
-            dev_alloc(c->work_allocs, &w.keys, (size_t)w.Rmax);
+            dev_alloc(c->work_allocs, &w.keys, (size_t)w.Rmax) &&
+            dev_alloc(c->work_allocs, &w.copy_keys, (size_t)2 * w.Bmax);
   hipDeviceProp_t prop;
   const bool have_prop = hipGetDeviceProperties(&prop, c->device) == hipSuccess;
   c->G = have_prop ? std::min(prop.multiProcessorCount, kd::MAX_G) : 128;
@@ -797,6 +798,59 @@ kd_status kd_ingest(kd_ctx* c, int B, int n_new, const void* taps, const int32_t
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(c, e, "kd_ingest launch");
   return KD_OK;
+}
+
+kd_status kd_copy_draft(kd_ctx* c, int B, const int32_t* tokens, long long stride,
+                        const int32_t* lens, const int32_t* corpus, long long corpus_len, int K,
+                        int32_t* out_ids, int32_t* out_info) {
+  if (!c) return KD_ERR_ARG;
+  if (B < 1 || B > c->cfg.max_streams) return fail(c, KD_ERR_ARG, "streams out of range");
+  if (K < 1 || K > KD_MAX_COPY) return fail(c, KD_ERR_ARG, "K out of range");
+  if (stride < 0 || stride >= (1ll << 31) || corpus_len < 0 || corpus_len >= (1ll << 31))
+    return fail(c, KD_ERR_ARG, "history stride or corpus length out of range");
+  if ((stride > 0 && !tokens) || !lens || !out_ids || !out_info || (corpus_len > 0 && !corpus))
+    return fail(c, KD_ERR_ARG, "NULL device pointer");
+  (void)hipGetLastError();
+  kd::launch_copy_draft(c->stream, B, tokens, stride, lens, corpus_len > 0 ? corpus : nullptr,
+                        corpus_len, K, c->w.copy_keys, out_ids, out_info);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(c, e, "kd_copy_draft launch");
+  return KD_OK;
+}
+
+void kd_copy_guard_init(kd_copy_guard* g, int window, float min_accept, int pause) {
+  if (!g) return;
+  memset(g, 0, sizeof *g);
+  g->window = window < 1 ? 1 : (window > KD_GUARD_MAX_WINDOW ? KD_GUARD_MAX_WINDOW : window);
+  g->min_accept = min_accept;
+  g->pause = pause < 0 ? 0 : pause;
+}
+
+int kd_copy_guard_armed(const kd_copy_guard* g) { return g && g->paused_left == 0 ? 1 : 0; }
+
+void kd_copy_guard_record(kd_copy_guard* g, int proposed, int accepted) {
+  if (!g) return;
+  g->proposed[g->next] = proposed;
+  g->accepted[g->next] = accepted;
+  g->next = (g->next + 1) % g->window;
+  if (g->count < g->window) ++g->count;
+  if (g->count == g->window) {
+    long long p = 0, a = 0;
+    for (int i = 0; i < g->window; ++i) {
+      p += g->proposed[i];
+      a += g->accepted[i];
+    }
+    if (p > 0 && (double)a < (double)g->min_accept * (double)p) {
+      g->paused_left = g->pause;
+      g->count = 0;
+      g->next = 0;
+    }
+  }
+}
+
+void kd_copy_guard_advance(kd_copy_guard* g, int tokens) {
+  if (!g || tokens <= 0) return;
+  g->paused_left = g->paused_left > tokens ? g->paused_left - tokens : 0;
 }
 
 // ---- debug / probes ----

@@ -88,6 +88,7 @@ struct Work {
   float* att_o = nullptr;             // [Bmax][NH][nch][BLK][DH]
   int att_nch = 0;                    // chunks per (stream, head) = ceil(window / ATT_CH)
   unsigned long long* keys = nullptr; // [Rmax] argmax keys
+  unsigned long long* copy_keys = nullptr;  // [2 Bmax] copy-draft (match, position) keys
 };
 
 // Row tiles of 16 for R rows.
@@ -139,6 +140,10 @@ void launch_gemm_mm(hipStream_t st, const uint16_t* af, int R, const Fp8Mat& W, 
 bool head_mm_fits(int R);
 void launch_head_mm(hipStream_t st, const uint16_t* af, int R, const DevWeights& d, float* logits,
                     unsigned long long* keys);
+// copy drafts (kd_copy.hip); keys: [2 B] workspace
+void launch_copy_draft(hipStream_t st, int B, const int32_t* tokens, long long stride,
+                       const int32_t* lens, const int32_t* corpus, long long n, int K,
+                       unsigned long long* keys, int32_t* out_ids, int32_t* out_info);
 // probes
 void launch_probe_e4m3(hipStream_t st, uint16_t* out);
 void launch_probe_nvfp4(hipStream_t st, uint16_t* out);

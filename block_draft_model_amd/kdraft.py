@@ -51,11 +51,22 @@ class KdKV(ctypes.Structure):
 
 
 EXPORTS = ["kd_default_config", "kd_create", "kd_load_weights", "kd_round", "kd_round_depth",
-           "kd_ingest",
+           "kd_ingest", "kd_copy_draft", "kd_copy_guard_init", "kd_copy_guard_armed",
+           "kd_copy_guard_record", "kd_copy_guard_advance",
            "kd_set_stream", "kd_destroy", "kd_status_string", "kd_last_error",
            "kd_probe_decode_e4m3", "kd_probe_decode_e4m3_f16", "kd_probe_decode_nvfp4", "kd_debug_set_layers",
            "kd_debug_buffers", "kd_debug_set_path", "kd_debug_last_path",
            "kd_debug_set_trace"]
+
+KD_MAX_COPY = 48
+KD_GUARD_MAX_WINDOW = 64
+
+
+class KdCopyGuard(ctypes.Structure):
+    _fields_ = [("window", c_int), ("pause", c_int), ("paused_left", c_int), ("count", c_int),
+                ("next", c_int), ("min_accept", c_float),
+                ("proposed", c_int * KD_GUARD_MAX_WINDOW), ("accepted", c_int * KD_GUARD_MAX_WINDOW)]
+
 
 _lib = None
 
@@ -87,6 +98,17 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kd_round_depth.argtypes = [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, P(KdKV),
                                    c_void_p, c_void_p, c_void_p]
     lib.kd_round_depth.restype = c_int
+    lib.kd_copy_draft.argtypes = [c_void_p, c_int, c_void_p, ctypes.c_longlong, c_void_p, c_void_p,
+                                  ctypes.c_longlong, c_int, c_void_p, c_void_p]
+    lib.kd_copy_draft.restype = c_int
+    lib.kd_copy_guard_init.argtypes = [P(KdCopyGuard), c_int, c_float, c_int]
+    lib.kd_copy_guard_init.restype = None
+    lib.kd_copy_guard_armed.argtypes = [P(KdCopyGuard)]
+    lib.kd_copy_guard_armed.restype = c_int
+    lib.kd_copy_guard_record.argtypes = [P(KdCopyGuard), c_int, c_int]
+    lib.kd_copy_guard_record.restype = None
+    lib.kd_copy_guard_advance.argtypes = [P(KdCopyGuard), c_int]
+    lib.kd_copy_guard_advance.restype = None
     lib.kd_ingest.argtypes = [c_void_p, c_int, c_int, c_void_p, c_void_p, P(KdKV), c_void_p]
     lib.kd_ingest.restype = c_int
     lib.kd_set_stream.argtypes = [c_void_p, c_void_p]
@@ -237,6 +259,11 @@ class Drafter:
                                             _ptr(out_ids), _ptr(out_logits)),
                     "kd_round_depth")
 
+    def copy_draft(self, streams, tokens, stride, lens, corpus, corpus_len, K, out_ids, out_info):
+        self._check(self.lib.kd_copy_draft(self.ctx, int(streams), _ptr(tokens), int(stride),
+                                           _ptr(lens), _ptr(corpus), int(corpus_len), int(K),
+                                           _ptr(out_ids), _ptr(out_info)), "kd_copy_draft")
+
     def ingest(self, streams, n_new, taps, next_ids, kv: KdKV, lens):
         self._check(self.lib.kd_ingest(self.ctx, int(streams), int(n_new), _ptr(taps), _ptr(next_ids),
                                        ctypes.byref(kv), _ptr(lens)), "kd_ingest")
@@ -294,3 +321,21 @@ def probe_decode_nvfp4(out) -> None:
     st = load_library().kd_probe_decode_nvfp4(_ptr(out))
     if st != KD_OK:
         raise KDraftError(st, "kd_probe_decode_nvfp4")
+
+
+class CopyGuard:
+    """kd_copy_guard: the copy source's acceptance pause guard (host only)."""
+
+    def __init__(self, window=24, min_accept=0.5, pause=256):
+        self.lib = load_library()
+        self.g = KdCopyGuard()
+        self.lib.kd_copy_guard_init(ctypes.byref(self.g), int(window), float(min_accept), int(pause))
+
+    def armed(self) -> bool:
+        return bool(self.lib.kd_copy_guard_armed(ctypes.byref(self.g)))
+
+    def record(self, proposed, accepted):
+        self.lib.kd_copy_guard_record(ctypes.byref(self.g), int(proposed), int(accepted))
+
+    def advance(self, tokens):
+        self.lib.kd_copy_guard_advance(ctypes.byref(self.g), int(tokens))

@@ -55,6 +55,8 @@ typedef enum {
 enum { KD_QUANT_FP8_BLOCK64 = 1, KD_QUANT_NVFP4 = 2 };
 enum { KD_MAX_INGEST = 8 };  /* rows per stream per kd_ingest call */
 enum { KD_MAX_DEPTH = 8 };   /* rounds per kd_round_depth call */
+enum { KD_MAX_COPY = 48 };   /* tokens per copy-draft proposal */
+enum { KD_GUARD_MAX_WINDOW = 64 };  /* proposals the pause guard can track */
 
 /* Model shape and limits. The kernels are built for the model card's shape;
  * kd_create returns KD_ERR_UNSUPPORTED for any other hidden, heads, head_dim,
@@ -180,6 +182,49 @@ kd_status kd_round_depth(kd_ctx* ctx, int depth, int streams, const void* tapped
  *   next_ids [streams][n_new] int32 (device) */
 kd_status kd_ingest(kd_ctx* ctx, int streams, int n_new, const void* taps,
                     const int32_t* next_ids, const kd_kv* ctx_kv, int32_t* ctx_lens);
+
+/* Copy drafts (model card, section Use: copy drafts from the context are
+ * tried before the learned block; the frozen-corpus drafting article: the
+ * continuation after the longest suffix of the context, suffix length 8 down
+ * to 3, most recent occurrence, a span of up to K tokens that never crosses a
+ * -1 separator). Per stream, the sources are its own history and an optional
+ * corpus; at each suffix length the history is tried before the corpus. An
+ * occurrence must be followed by a token (in the corpus, not a separator).
+ *   tokens     [streams][stride] int32 (device): each stream's history, oldest
+ *              first; token ids >= 0
+ *   lens       [streams] int32 (device): tokens in each history; values
+ *              outside [0, stride] are clamped into it
+ *   corpus     [corpus_len] int32 (device) or NULL: frozen ids, -1 between spans
+ *   K          proposal length limit, 1..KD_MAX_COPY
+ *   out_ids    [streams][K] int32 (device): the proposed span, -1 past its end
+ *   out_info   [streams][3] int32 (device): tokens proposed (0 = no match),
+ *              matched suffix length (0 or 3..8), source (0 none, 1 history,
+ *              2 corpus)
+ * stride and corpus_len must be below 2^31. Asynchronous on the context's
+ * stream; uses the context's workspace (calls on one context must not
+ * overlap). */
+kd_status kd_copy_draft(kd_ctx* ctx, int streams, const int32_t* tokens, long long stride,
+                        const int32_t* lens, const int32_t* corpus, long long corpus_len, int K,
+                        int32_t* out_ids, int32_t* out_info);
+
+/* The copy source's pause guard (frozen-corpus drafting article: when fewer
+ * than min_accept of the tokens proposed over the last `window` proposals were
+ * accepted, the source pauses for `pause` decoded tokens, then re-arms with an
+ * empty window; its defaults are 24, 0.5 and 256). Host-only state, one per
+ * stream; the caller records each proposal's outcome and the tokens decoded. */
+typedef struct {
+  int window, pause, paused_left, count, next;
+  float min_accept;
+  int proposed[KD_GUARD_MAX_WINDOW], accepted[KD_GUARD_MAX_WINDOW];
+} kd_copy_guard;
+/* window is clamped into [1, KD_GUARD_MAX_WINDOW], pause to >= 0. */
+void kd_copy_guard_init(kd_copy_guard* g, int window, float min_accept, int pause);
+/* 1 while the source may propose, 0 while paused. */
+int kd_copy_guard_armed(const kd_copy_guard* g);
+/* One proposal of `proposed` tokens of which `accepted` were kept. */
+void kd_copy_guard_record(kd_copy_guard* g, int proposed, int accepted);
+/* `tokens` tokens were decoded (with or without proposals). */
+void kd_copy_guard_advance(kd_copy_guard* g, int tokens);
 
 /* Moves the context to another HIP stream. */
 kd_status kd_set_stream(kd_ctx* ctx, void* hip_stream);

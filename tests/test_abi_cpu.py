@@ -68,3 +68,28 @@ def test_host_side_argument_errors(lib):
     assert lib.kd_load_weights(None, None) == kdraft.KD_ERR_ARG
     assert lib.kd_last_error(None) == b""
     lib.kd_destroy(None)
+
+
+def test_copy_guard_follows_the_reference(lib):
+    """The host-side pause guard against the reference on random outcomes."""
+    import numpy as np
+    from oracle.copy_draft import PauseGuard
+    rng = np.random.default_rng(3)
+    for trial in range(20):
+        window = int(rng.integers(1, 30))
+        pause = int(rng.integers(0, 50))
+        ref, got = PauseGuard(window, 0.5, pause), kdraft.CopyGuard(window, 0.5, pause)
+        for step in range(400):
+            if ref.armed():
+                p = int(rng.integers(1, 9))
+                a = int(rng.integers(0, p + 1)) if rng.random() < 0.7 else 0
+                ref.record(p, a)
+                got.record(p, a)
+            adv = int(rng.integers(1, 5))
+            ref.advance(adv)
+            got.advance(adv)
+            assert ref.armed() == got.armed(), (trial, step)
+
+
+def test_copy_draft_argument_errors(lib):
+    assert lib.kd_copy_draft(None, 1, None, 0, None, None, 0, 8, None, None) == kdraft.KD_ERR_ARG
