@@ -84,6 +84,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise ImportError(f"libkdraft.so not found at {path}; run python -m block_draft_model_amd.build")
+    # torch carries its own HIP runtime; loading it first makes the library bind
+    # to that same runtime, so that torch's device memory and streams are valid
+    # in the library's calls (loaded the other way round, a process holds two
+    # HIP runtimes and the library's launches do not reach torch's device state)
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     P = ctypes.POINTER
     lib.kd_default_config.argtypes = [P(KdConfig)]
