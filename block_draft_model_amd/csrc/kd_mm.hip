@@ -28,7 +28,7 @@ constexpr int MM_WAVES = 4;
 // rows make the work matrix-core bound; 1 (64 columns) for fewer rows, where
 // the weights stream from HBM and narrower tiles give more workgroups with
 // fewer split-K partial sums.
-constexpr int MM_SMALL_R = 128;
+constexpr int MM_SMALL_R = 256;
 __host__ __device__ inline int mm_ct(int R) { return R > MM_SMALL_R ? 4 : 1; }
 
 // Workgroup -> (row block, column block, split). Column unit c = (column
