@@ -23,7 +23,8 @@ silent the plainest reading is taken and named in the function that uses it:
   0..j; scores are scaled by 1/sqrt(head_dim);
 * head rows are in draft-vocabulary order; ties go to the lowest draft index,
   NaN never wins, a row with no finite logit reports id -1;
-* ingested K/V are rounded to bf16 (nearest even) because the cache is bf16.
+* ingested K/V are rounded to bf16 (nearest even) because the cache is bf16;
+  a rotated 4-bit cache follows the readings listed in kv_int4.
 
 Every weight is decoded to its exact real value; activations are never
 quantised. Integer data (ids, lengths) follow the same indexing as the card.
@@ -33,6 +34,8 @@ from __future__ import annotations
 import math
 
 import numpy as np
+
+from . import kv_int4
 
 
 # ----------------------------------------------------------------------------
@@ -193,6 +196,9 @@ class OracleModel:
         self.head = nvfp4(m["head.q4"], m["head.s4"], m["head.g"])
         self.vocab = np.asarray(m["vocab"], dtype=np.int64)
         self.table_bits = m["table"]           # bf16 bits; rows decoded on use
+        # per-layer sign vectors of a rotated 4-bit cache (absent: bf16 only)
+        rs = m.get("kv_rot_signs")
+        self.kv_rot_signs = None if rs is None else np.asarray(rs, dtype=np.int64)
 
     def embed(self, ids) -> np.ndarray:
         return decode_bf16(self.table_bits[np.asarray(ids, dtype=np.int64)])
@@ -206,6 +212,19 @@ def _visible(length, dims):
     n = min(int(length), dims.window)
     pos = np.arange(int(length) - n, int(length))
     return pos, pos % dims.capacity
+
+
+def _context_kv(M: OracleModel, inp: dict, l: int, b: int, slots):
+    """The visible context keys and values of stream b, layer l, [heads][n][d].
+    A bf16 cache holds them directly. A rotated 4-bit cache (the INT4 KV
+    article, section Method) holds codes of R k and of v: the values are
+    decoded, and the keys turned back by R^T, which leaves every score q.k
+    as the rotated cache gives it, (R q).(R k)."""
+    if inp.get("kv_format") == "int4":
+        kr = kv_int4.decode_int4(inp["k"][l][b][:, slots, :], inp["k_so"][l][b][:, slots, :])
+        vc = kv_int4.decode_int4(inp["v"][l][b][:, slots, :], inp["v_so"][l][b][:, slots, :])
+        return kv_int4.unrotate_rows(kr, M.kv_rot_signs[l]), vc
+    return decode_bf16(inp["k"][l][b][:, slots, :]), decode_bf16(inp["v"][l][b][:, slots, :])
 
 
 def oracle_round(M: OracleModel, inp: dict, block: int | None = None,
@@ -256,8 +275,7 @@ def oracle_round(M: OracleModel, inp: dict, block: int | None = None,
         o = np.empty((B, R, NH, Dh))
         for b in range(B):
             _, slots = _visible(lens[b], d)
-            kc = decode_bf16(inp["k"][l][b][:, slots, :])
-            vc = decode_bf16(inp["v"][l][b][:, slots, :])
+            kc, vc = _context_kv(M, inp, l, b, slots)
             o[b] = attention(q[b], kc, vc, k[b], v[b])
         x = x + o.reshape(B, R, H) @ L["wo"].T
         c = rmsnorm(x, L["ffn_norm"], d.rms_eps)
@@ -295,8 +313,12 @@ def oracle_ingest(M: OracleModel, inp: dict, return_exact: bool = False):
     Every layer projects the same row c through its attention RMSNorm and
     W_k / W_v; K gets RoPE at its absolute position; both are rounded to bf16
     and stored at slot pos % capacity; len grows by the number of rows.
+    With a rotated 4-bit cache (kv_format "int4"; the INT4 KV article,
+    section Method) K is rotated by the layer's R after RoPE, and both K and V
+    are stored as codes with their fp16 scale and offset instead.
     Returns a new input dict (K/V copies and lengths updated); with
-    return_exact also the unrounded fp64 K and V per layer ([B][n][heads][d]).
+    return_exact also the unrounded fp64 K (rotated, for a 4-bit cache) and V
+    per layer ([B][n][heads][d]).
     """
     d = M.dims
     B = int(inp["streams"])
@@ -306,8 +328,12 @@ def oracle_ingest(M: OracleModel, inp: dict, return_exact: bool = False):
     nxt = np.asarray(inp["ingest_ids"]).reshape(B, n_new)
     lens = np.asarray(inp["lens"]).reshape(B).astype(np.int64)
     out = dict(inp)
+    int4 = inp.get("kv_format") == "int4"
     out["k"] = [k.copy() for k in inp["k"]]
     out["v"] = [v.copy() for v in inp["v"]]
+    if int4:
+        out["k_so"] = [t.copy() for t in inp["k_so"]]
+        out["v_so"] = [t.copy() for t in inp["v_so"]]
     f = taps.reshape(B, n_new, d.taps * H) @ M.fuse.T
     c = np.concatenate([f, M.embed(nxt)], axis=-1) @ M.fc.T           # [B][n][H]
     pos = lens[:, None] + np.arange(n_new)[None, :]
@@ -316,12 +342,22 @@ def oracle_ingest(M: OracleModel, inp: dict, return_exact: bool = False):
         a = rmsnorm(c, L["attn_norm"], d.rms_eps)
         k = rope((a @ L["wk"].T).reshape(B, n_new, NH, Dh), pos[:, :, None], d.rope_theta)
         v = (a @ L["wv"].T).reshape(B, n_new, NH, Dh)
+        if int4:
+            k = kv_int4.rotate_rows(k, M.kv_rot_signs[l])
+            (kq, kso), (vq, vso) = kv_int4.quantize_int4(k), kv_int4.quantize_int4(v)
+        else:
+            kb, vb = round_bf16(k), round_bf16(v)
         exact.append((k, v))
-        kb, vb = round_bf16(k), round_bf16(v)
         for b in range(B):
             for i in range(n_new):
                 slot = int(pos[b, i]) % d.capacity
-                out["k"][l][b][:, slot, :] = kb[b, i]
-                out["v"][l][b][:, slot, :] = vb[b, i]
+                if int4:
+                    out["k"][l][b][:, slot, :] = kq[b, i]
+                    out["v"][l][b][:, slot, :] = vq[b, i]
+                    out["k_so"][l][b][:, slot, :] = kso[b, i]
+                    out["v_so"][l][b][:, slot, :] = vso[b, i]
+                else:
+                    out["k"][l][b][:, slot, :] = kb[b, i]
+                    out["v"][l][b][:, slot, :] = vb[b, i]
     out["lens"] = (lens + n_new).astype(np.int32)
     return (out, exact) if return_exact else out

@@ -154,6 +154,8 @@ def make_model(dims: Dims = FULL, variant: str = "A", device="cpu", base: int = 
     All other matrices N(0, 0.02) -> block-FP8. The mask row is N(0, 0.02).
     The embedding/head table is N(0, 0.02) rounded to bf16; the head is the
     NVFP4 quantisation of its rows at the (sorted) draft vocabulary.
+    kv_rot_signs: int8 [layers][head_dim], each +1 or -1 with probability 1/2
+    (the random signs of a rotated 4-bit K/V cache).
     """
     assert variant in ("A", "B", "C")
     H, F, r, L = dims.hidden, dims.ffn, dims.rank, dims.layers
@@ -192,6 +194,9 @@ def make_model(dims: Dims = FULL, variant: str = "A", device="cpu", base: int = 
     m["vocab"] = vocab.to(device)
     q4, s4, g = quant_nvfp4(table[vocab.to(device).long()].float())
     m["head.q4"], m["head.s4"], m["head.g"] = q4, s4, g
+    # one random sign per head dimension and layer, for a rotated 4-bit cache
+    signs = torch.randint(0, 2, (L, dims.head_dim), generator=_gen("cpu", base, "kv_rot_signs"))
+    m["kv_rot_signs"] = (1 - 2 * signs).to(torch.int8).to(device)
     return m
 
 
@@ -220,7 +225,7 @@ def _rms_normal(shape, device, *parts):
 
 def make_inputs(cfg: dict, dims: Dims = FULL, device="cpu", base: int | None = None,
                 poison: bool = False, vocab: torch.Tensor | None = None, streams=None,
-                lens_override=None):
+                lens_override=None, kv: str = "bf16"):
     """Round inputs for one workload.
 
     Each stream's tensors are seeded by (base, name, stream), so stream b's
@@ -233,6 +238,10 @@ def make_inputs(cfg: dict, dims: Dims = FULL, device="cpu", base: int | None = N
              slots; NaN elsewhere when poison=True (out-of-window reads show up)
       ingest (when cfg["ingest"] > 0): taps [B][n][3][H] and next ids [B][n]
     lens_override: explicit per-stream lengths instead of the config's law.
+    kv="int4": the cache holds 4-bit codes instead (see _int4_cache); then
+      k, v are uint8 [B][heads][capacity][head_dim/2] and k_so, v_so are
+      fp16 bits uint16 [B][heads][capacity][2] (scale, offset); invisible
+      slots get NaN scale and offset when poison=True.
     """
     if base is None:
         base = 100 + CONFIGS.index(cfg) if cfg in CONFIGS else 100
@@ -268,22 +277,14 @@ def make_inputs(cfg: dict, dims: Dims = FULL, device="cpu", base: int | None = N
     inp["pred"] = torch.stack(pred).to(device)
     inp["lens"] = torch.tensor(lens, dtype=torch.int32, device=device)
 
-    nan = torch.tensor(float("nan"), dtype=torch.bfloat16, device=device)
-    ks, vs = [], []
-    for l in range(dims.layers):
-        for name, store in (("k", ks), ("v", vs)):
-            t = torch.empty((B, NH, C, D), dtype=torch.bfloat16, device=device)
-            for b in range(B):
-                x = _normal((NH, C, D), 1.0, device, base, f"{name}{l}", b).to(torch.bfloat16)
-                if poison:
-                    n = min(lens[b], dims.window)
-                    pos = torch.arange(lens[b] - n, lens[b])
-                    vis = torch.zeros(C, dtype=torch.bool)
-                    vis[pos % C] = True
-                    x[:, ~vis.to(device)] = nan
-                t[b] = x
-            store.append(t)
-    inp["k"], inp["v"] = ks, vs
+    if kv == "int4":
+        _int4_cache(inp, dims, B, lens, device, base, poison)
+        ks = vs = None
+    else:
+        assert kv == "bf16"
+        ks, vs = _bf16_cache(dims, B, lens, device, base, poison)
+    if ks is not None:
+        inp["k"], inp["v"] = ks, vs
 
     n_new = cfg.get("ingest", 0)
     if n_new:
@@ -292,6 +293,60 @@ def make_inputs(cfg: dict, dims: Dims = FULL, device="cpu", base: int | None = N
             for b in range(B)])
         inp["ingest_ids"] = torch.stack([ids((n_new,), "iids", b) for b in range(B)]).to(device)
     return inp
+
+
+def _visible_mask(dims, length, C):
+    n = min(length, dims.window)
+    pos = torch.arange(length - n, length)
+    vis = torch.zeros(C, dtype=torch.bool)
+    vis[pos % C] = True
+    return vis
+
+
+def _bf16_cache(dims, B, lens, device, base, poison):
+    NH, D, C = dims.heads, dims.head_dim, dims.capacity
+    nan = torch.tensor(float("nan"), dtype=torch.bfloat16, device=device)
+    ks, vs = [], []
+    for l in range(dims.layers):
+        for name, store in (("k", ks), ("v", vs)):
+            t = torch.empty((B, NH, C, D), dtype=torch.bfloat16, device=device)
+            for b in range(B):
+                x = _normal((NH, C, D), 1.0, device, base, f"{name}{l}", b).to(torch.bfloat16)
+                if poison:
+                    x[:, ~_visible_mask(dims, lens[b], C).to(device)] = nan
+                t[b] = x
+            store.append(t)
+    return ks, vs
+
+
+def _int4_cache(inp, dims, B, lens, device, base, poison):
+    """A 4-bit cache drawn directly in its stored form (no quantiser runs
+    here): per element a code round(7.5 + 2.5 z) clamped to 0..15 (z ~ N(0,1)),
+    two per byte with the even dimension in the low nibble; per (stream, head,
+    slot) an fp16 scale ~ U(0.25, 0.45) and an fp16 offset of
+    -7.5 * scale + N(0, 0.1), so scale * code + offset is roughly N(0, 0.8)."""
+    NH, D, C = dims.heads, dims.head_dim, dims.capacity
+    nan16 = 0x7E00
+    out = {"k": [], "v": [], "k_so": [], "v_so": []}
+    for l in range(dims.layers):
+        for name in ("k", "v"):
+            codes = torch.empty((B, NH, C, D // 2), dtype=torch.uint8)
+            so = torch.empty((B, NH, C, 2), dtype=torch.int16)
+            for b in range(B):
+                z = _normal((NH, C, D), 1.0, "cpu", base, f"{name}{l}q", b)
+                c = (7.5 + 2.5 * z).round().clamp(0, 15).to(torch.uint8)
+                codes[b] = c[..., 0::2] | (c[..., 1::2] << 4)
+                g = _gen("cpu", base, f"{name}{l}so", b)
+                sc = (0.25 + 0.2 * torch.rand((NH, C), generator=g)).to(torch.float16)
+                off = (-7.5 * sc.float() + 0.1 * torch.randn((NH, C), generator=g)).to(torch.float16)
+                pair = torch.stack([sc.view(torch.int16), off.view(torch.int16)], dim=-1)
+                if poison:
+                    pair[:, ~_visible_mask(dims, lens[b], C)] = nan16
+                so[b] = pair
+            out[name].append(codes.to(device))
+            out[name + "_so"].append(so.to(device))
+    inp.update(out)
+    inp["kv_format"] = "int4"
 
 
 # ----------------------------------------------------------------------------
@@ -319,5 +374,9 @@ def to_numpy_inputs(inp: dict, streams=None) -> dict:
             out[k] = _np(inp[k][sel])
     out["k"] = [_np(t[sel]) for t in inp["k"]]
     out["v"] = [_np(t[sel]) for t in inp["v"]]
+    if inp.get("kv_format") == "int4":
+        out["kv_format"] = "int4"
+        out["k_so"] = [_np(t[sel]).view(np.uint16) for t in inp["k_so"]]
+        out["v_so"] = [_np(t[sel]).view(np.uint16) for t in inp["v_so"]]
     out["streams"] = len(out["lens"])
     return out
