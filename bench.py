@@ -30,18 +30,23 @@ KERNEL_NAME = {2: "kd::k_small_phase", 3: "kd::k_small_mega"}
 LAUNCHES_PER_ROUND = {2: 30, 3: 1}
 
 
-def algorithmic_bytes(dims, lens, streams, ingest=0):
+def algorithmic_bytes(dims, lens, streams, ingest=0, kv="bf16"):
     """Bytes a step must move: weights once (block-FP8 body with scales, NVFP4
     head with block and tensor scales, fp32 vectors), 40,960 B of bf16 K/V per
-    visible context row per stream (4 layers x K,V x 20 heads x 128 x 2 B), and
-    per stream its tapped states, 4 embedding rows, ids, length and outputs.
+    visible context row per stream (4 layers x K,V x 20 heads x 128 x 2 B;
+    with the rotated 4-bit cache 10,880 B: 64 code bytes and a 4-byte fp16
+    scale and offset per layer, K/V, head), and per stream its tapped states,
+    4 embedding rows, ids, length and outputs.
     With `ingest` new context rows per stream ahead of the round: their tapped
     states, next-token ids and embedding rows, and the 40,960 B of K/V each
     writes (the weights they use are the round's, counted once); `lens` are the
     lengths the round sees."""
     import synth
     mb = synth.model_bytes(dims)
-    kv_row = dims.layers * 2 * dims.heads * dims.head_dim * 2
+    if kv == "int4":
+        kv_row = dims.layers * 2 * dims.heads * (dims.head_dim // 2 + 4)
+    else:
+        kv_row = dims.layers * 2 * dims.heads * dims.head_dim * 2
     vis = sum(min(int(l), dims.window) for l in lens)
     per_stream = (dims.taps * dims.hidden * 2 + dims.block * dims.hidden * 2
                   + 4 * (1 + (dims.block - 1) + 1 + dims.block))
@@ -135,6 +140,9 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB 5 times and "
                          "exit: the calibration kernel for HBM byte counters")
+    ap.add_argument("--kv", choices=("bf16", "int4"), default="bf16",
+                    help="context cache format: bf16, or rotated 4-bit codes with an fp16 "
+                         "scale and offset per row (read by the general path)")
     ap.add_argument("--path", type=int, default=0,
                     help="0 automatic; 1 general multi-kernel; 2 small-batch phases as "
                          "separate launches; 3 small-batch persistent kernel")
@@ -166,13 +174,16 @@ def main():
     cfg = synth.CONFIGS[args.config]
     dims = synth.FULL
     model = synth.make_model(dims, cfg["model"], device="cuda")
-    inp = synth.make_inputs(cfg, dims, device="cuda", vocab=model["vocab"])
+    inp = synth.make_inputs(cfg, dims, device="cuda", vocab=model["vocab"], kv=args.kv)
     B = inp["streams"]
     stream = torch.cuda.current_stream()
     drafter = kdraft.Drafter(max_streams=B, stream=stream)
     drafter.load_weights(model)
     drafter.debug_set_path(args.path)
-    kv = kdraft.kv_struct(inp["k"], inp["v"])
+    if args.kv == "int4":
+        kv = kdraft.kv_struct_int4(inp["k"], inp["v"], inp["k_so"], inp["v_so"])
+    else:
+        kv = kdraft.kv_struct(inp["k"], inp["v"])
     ids = torch.empty(B, 4, dtype=torch.int32, device="cuda")
     n_ingest = cfg.get("ingest", 0)
     # the lengths the timed rounds see (an ingesting step appends its rows
@@ -198,7 +209,7 @@ def main():
     ms = start.elapsed_time(end) / args.steps
 
     path = drafter.last_path()
-    ab = algorithmic_bytes(dims, lens_host, B, n_ingest)
+    ab = algorithmic_bytes(dims, lens_host, B, n_ingest, args.kv)
     rounds_s = 1000.0 / ms
     # roofline of the round's kernel: algorithmic bytes per launch over the
     # average launch duration (the HIP-event time of the timed rounds on the
@@ -225,8 +236,9 @@ def main():
                                   + (f" after ingesting {n_ingest} context rows per stream" if n_ingest else "")
                                   + ", draft block 4, "
                                   f"context rows per stream {sorted(set(min(l, 2048) for l in lens_host))}, "
-                                  f"block-FP8 body, NVFP4 head (60,614 rows)",
-                      "streams": B, "draft_tokens_per_round": 4 * B,
+                                  f"block-FP8 body, NVFP4 head (60,614 rows)"
+                                  + (", rotated 4-bit K/V cache" if args.kv == "int4" else ""),
+                      "streams": B, "draft_tokens_per_round": 4 * B, "kv_cache": args.kv,
                       "path": {1: "general multi-kernel", 2: "small-batch phases, one launch each",
                                3: "small-batch persistent kernel"}[path]},
            "draft_tokens_per_s": round(4 * B * rounds_s, 1),

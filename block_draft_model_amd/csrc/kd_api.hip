@@ -94,6 +94,11 @@ void key_add_kv(std::vector<unsigned char>& key, const kd::KV& k) {
   key_add(key, k.sh);
   key_add(key, k.sl);
   key_add(key, k.cap);
+  key_add(key, k.fmt);
+  for (int l = 0; l < 4; ++l) {
+    key_add(key, k.kso[l]);
+    key_add(key, k.vso[l]);
+  }
 }
 
 // Launches `enqueue`'s kernels on st as a graph: captured on the private
@@ -289,9 +294,12 @@ kd_status upload_vec(kd_ctx* c, const float* src, size_t n, const float** out) {
 
 kd::KV make_kv(const kd_kv* kv) {
   kd::KV k;
+  k.fmt = kv->format;
   for (int l = 0; l < 4; ++l) {
     k.k[l] = static_cast<const uint16_t*>(kv->k[l]);
     k.v[l] = static_cast<const uint16_t*>(kv->v[l]);
+    k.kso[l] = kv->format == KD_KV_INT4_ROT ? static_cast<const uint16_t*>(kv->k_so[l]) : nullptr;
+    k.vso[l] = kv->format == KD_KV_INT4_ROT ? static_cast<const uint16_t*>(kv->v_so[l]) : nullptr;
   }
   k.ss = kv->stride_stream;
   k.sh = kv->stride_head;
@@ -306,6 +314,21 @@ kd_status check_kv(kd_ctx* c, const kd_kv* kv) {
     if (!kv->k[l] || !kv->v[l]) return fail(c, KD_ERR_ARG, "NULL K/V tensor");
   if (kv->capacity < c->cfg.window)
     return fail(c, KD_ERR_ARG, "K/V capacity is smaller than the window");
+  if (kv->format == KD_KV_INT4_ROT) {
+    if (!c->d.kv_signs)
+      return fail(c, KD_ERR_ARG, "a 4-bit cache needs kv_rot_signs in the loaded weights");
+    for (int l = 0; l < 4; ++l) {
+      if (!kv->k_so[l] || !kv->v_so[l]) return fail(c, KD_ERR_ARG, "NULL K/V scale tensor");
+      if ((reinterpret_cast<uintptr_t>(kv->k[l]) | reinterpret_cast<uintptr_t>(kv->v[l])) & 15)
+        return fail(c, KD_ERR_ARG, "K/V code tensors must be 16-byte aligned");
+      if ((reinterpret_cast<uintptr_t>(kv->k_so[l]) | reinterpret_cast<uintptr_t>(kv->v_so[l])) & 3)
+        return fail(c, KD_ERR_ARG, "K/V scale tensors must be 4-byte aligned");
+    }
+    if (kv->stride_slot < 1 || kv->stride_head < 1 || kv->stride_stream < 1)
+      return fail(c, KD_ERR_ARG, "bad K/V strides");
+    return KD_OK;
+  }
+  if (kv->format != KD_KV_BF16) return fail(c, KD_ERR_ARG, "unknown K/V format");
   if (kv->stride_slot < kd::DH || kv->stride_head < 1 || kv->stride_stream < 1)
     return fail(c, KD_ERR_ARG, "bad K/V strides");
   for (int l = 0; l < 4; ++l)
@@ -524,6 +547,17 @@ kd_status kd_load_weights(kd_ctx* c, const kd_weights* wt) {
     }
   }
   if ((st = upload_vec(c, wt->final_norm, H, &d.final_norm)) != KD_OK) return st;
+  // signs of the rotated 4-bit cache, kept as +-1.0f
+  d.kv_signs = nullptr;
+  if (wt->kv_rot_signs) {
+    std::vector<float> sg((size_t)kd::NL * kd::DH);
+    for (size_t i = 0; i < sg.size(); ++i) {
+      const int8_t v = wt->kv_rot_signs[i];
+      if (v != 1 && v != -1) return fail(c, KD_ERR_ARG, "kv_rot_signs entries must be +1 or -1");
+      sg[i] = (float)v;
+    }
+    if ((st = upload_vec(c, sg.data(), sg.size(), &d.kv_signs)) != KD_OK) return st;
+  }
 
   // NVFP4 head, repacked to 16-row vocab tiles (layout in kd_device.h).
   const int VT = (VD + 15) / 16, KG = H / 128;
@@ -593,6 +627,7 @@ static kd_status round_impl(kd_ctx* c, int depth, int B, const void* taps, const
   if (!c->small_ok) path = 1;
   if (path == 3 && !c->mega_ok) path = 2;
   if (path != 1 && B > kd::SB_MAX) path = 1;
+  if (k.fmt == KD_KV_INT4_ROT) path = 1;   // the 4-bit cache is read by the general path
   c->last_path = path;
   if (path != 1) {
     (void)hipGetLastError();
@@ -700,7 +735,7 @@ static kd_status round_impl(kd_ctx* c, int depth, int B, const void* taps, const
         const int s_qkv = kd::gemm_splits(L.qkv.K, L.qkv.N, R);
         kd::launch_gemm(st, w.af_x, R, L.qkv, 0, L.qkv.N, partA, s_qkv);
         kd::launch_qkv_post(st, w, B, s_qkv);
-        kd::launch_attention(st, w, B, k, l, lens, c->cfg.window);
+        kd::launch_attention(st, w, d, B, k, l, lens, c->cfg.window);
         const int s_o = kd::gemm_splits(L.wo.K, L.wo.N, R);
         kd::launch_gemm(st, w.af_o, R, L.wo, 0, L.wo.N, partA, s_o);
         kd::launch_resid_norm(st, w, R, s_o, L.ffn_norm, eps, w.af_x, 0);
@@ -782,7 +817,7 @@ kd_status kd_ingest(kd_ctx* c, int B, int n_new, const void* taps, const int32_t
       kd::launch_norm_rows(st, w.c, rows, L.attn_norm, c->cfg.rms_eps, w.af_x);
       const int s_kv = kd::gemm_splits(L.qkv.K, 2 * kd::H, rows);
       kd::launch_gemm(st, w.af_x, rows, L.qkv, kd::H / 16, 2 * kd::H, w.part, s_kv);
-      kd::launch_ingest_store(st, w, B, n_new, s_kv, k, l, lens, c->cfg.rope_theta);
+      kd::launch_ingest_store(st, w, d, B, n_new, s_kv, k, l, lens, c->cfg.rope_theta);
     }
     kd::launch_bump_lens(st, lens, B, n_new);
   };

@@ -359,6 +359,9 @@ struct AttnK {
   const float* vb;
   const uint16_t* k;
   const uint16_t* v;
+  const uint16_t* kso;    // rotated 4-bit cache: (scale, offset) fp16 pairs
+  const uint16_t* vso;
+  const float* signs;     // rotated 4-bit cache: the layer's [DH] signs
   int64_t ss, sh, sl;
   int cap, window, nch, S;
   const int32_t* lens;
@@ -389,10 +392,82 @@ __device__ __forceinline__ float attn_block_merge(const float* sblk, const float
   return O / L;
 }
 
-__global__ __launch_bounds__(256) void k_attn_split(AttnK a) {
+// The end of a segment workgroup: the 4 key groups of each wave summed, the
+// 4 waves merged in LDS, then either the block's own keys added and the
+// output rows written (one segment) or the segment's (m, l, o) stored.
+// Thread (lr, lg) of wave w holds o[j][e] = unnormalised output of row j,
+// dims 8 lr + e, over its key group; m_run / l_run are row lr's (lr < 4).
+__device__ __forceinline__ void attn_finish(const AttnK& a, float (&o)[BLK][8], float m_run,
+                                            float l_run, int seg, int h, int b, size_t qrow0) {
   __shared__ float s_o[4][BLK][DH];
   __shared__ float s_m[4][BLK], s_l[4][BLK];
   __shared__ float s_blk[BLK * BLK];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const float qs = 0.08838834764831845f * 1.4426950408889634f;  // 1/sqrt(128) * log2(e)
+  // sum the 4 key groups of the wave: lanes lg = 0 end with o[j][8 lr + e]
+#pragma unroll
+  for (int j = 0; j < BLK; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      o[j][e] += __shfl_xor(o[j][e], 16, 64);
+      o[j][e] += __shfl_xor(o[j][e], 32, 64);
+    }
+  if (lg == 0) {
+#pragma unroll
+    for (int j = 0; j < BLK; ++j) {
+      *reinterpret_cast<f32x4*>(&s_o[wave][j][8 * lr]) = f32x4{o[j][0], o[j][1], o[j][2], o[j][3]};
+      *reinterpret_cast<f32x4*>(&s_o[wave][j][8 * lr + 4]) = f32x4{o[j][4], o[j][5], o[j][6], o[j][7]};
+    }
+  }
+  // row lr's max and sum live in every lane with lane % 16 == lr
+  if (lane < BLK) {
+    s_m[wave][lane] = m_run;
+    s_l[wave][lane] = l_run;
+  }
+  // the block's own scores s[j][i] (i <= j): wave j, lane l covers dims 2l, 2l+1
+  if (a.S == 1) {
+    const int j = wave;
+    const float q0 = a.q[qrow0 + (size_t)j * H + 2 * lane], q1 = a.q[qrow0 + (size_t)j * H + 2 * lane + 1];
+#pragma unroll
+    for (int i = 0; i < BLK; ++i) {
+      if (i > j) break;
+      const float* kp = a.kb + qrow0 + (size_t)i * H + 2 * lane;
+      const float p = wave_sum(q0 * kp[0] + q1 * kp[1]);
+      if (lane == 0) s_blk[j * BLK + i] = p * qs;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int j = (threadIdx.x >> 7) + 2 * it, d = threadIdx.x & 127;
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][j]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      if (s_m[w][j] != -__builtin_inff()) {
+        const float f = exp2f(s_m[w][j] - M);
+        L += s_l[w][j] * f;
+        O += s_o[w][j][d] * f;
+      }
+    }
+    if (a.S == 1) {
+      const float out = attn_block_merge(s_blk, a.vb, qrow0, j, d, M, L, O);
+      a.af_o[afrag_off(b * BLK + j, h * DH + d, H / 32)] = __builtin_bit_cast(uint16_t, (_Float16)out);
+    } else {
+      const size_t pb = ((size_t)(b * NH + h) * a.nch + seg) * BLK + j;
+      a.po[pb * DH + d] = O;
+      if (d == 0) {
+        a.pm[pb] = M;
+        a.pl[pb] = L;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_attn_split(AttnK a) {
   const int seg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -513,66 +588,211 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnK a) {
       process(bi + 4, kB, vB);
     }
   }
-  // sum the 4 key groups of the wave: lanes lg = 0 end with o[j][8 lr + e]
+  attn_finish(a, o, m_run, l_run, seg, h, b, qrow0);
+}
+
+
+// ---------------------------------------------------------------------------
+// Rotated 4-bit context cache (the article "Serving Kolibri-1 with a 4-bit KV
+// cache", section What we do): keys are cached as codes of R k with
+// R = H diag(s)/sqrt(128), values as codes of v, one fp16 (scale, offset) per
+// (stream, head, slot) row; the query is turned by the same R, so the scores
+// are those of the unrotated keys.
+// ---------------------------------------------------------------------------
+
+// In-wave Walsh-Hadamard transform of 128 values: lane l holds x[l] (y0) and
+// x[l + 64] (y1) and ends with (H x)[l], (H x)[l + 64], H[i][k] =
+// (-1)^popcount(i & k). One butterfly per index bit: (a, c) -> (a + c, a - c)
+// for the pair differing in that bit; bit 6 pairs the two registers, bits
+// 5..0 pair lanes.
+__device__ __forceinline__ void fwht128(float& y0, float& y1, int lane) {
+  const float a = y0, c = y1;
+  y0 = a + c;
+  y1 = a - c;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const float p0 = __shfl_xor(y0, m, 64), p1 = __shfl_xor(y1, m, 64);
+    const bool up = (lane & m) != 0;
+    y0 = up ? p0 - y0 : y0 + p0;
+    y1 = up ? p1 - y1 : y1 + p1;
+  }
+}
+
+// 8 4-bit codes (one dword, dim 2i in the low nibble of byte i) -> 8 exact
+// f16 values 0..15: each code is placed in the mantissa of 1024 (0x6400) and
+// 1024 subtracted again.
+__device__ __forceinline__ f16x8 nib8_f16(uint32_t w) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  const f16x2 k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+  const f16x2 p0 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(hi, lo, 0x0C040C00u) | 0x64006400u) - k1024;
+  const f16x2 p1 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(hi, lo, 0x0C050C01u) | 0x64006400u) - k1024;
+  const f16x2 p2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(hi, lo, 0x0C060C02u) | 0x64006400u) - k1024;
+  const f16x2 p3 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(hi, lo, 0x0C070C03u) | 0x64006400u) - k1024;
+  return f16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+// (scale, offset) fp16 pair in one dword -> two floats.
+__device__ __forceinline__ void so_unpack(uint32_t w, float& sc, float& of) {
+  sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+  of = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// The segment workgroup of k_attn_split for the rotated 4-bit cache. Per
+// 16-key block, lane (lr, lg):
+//   scores  K codes of key lr, dims 32 lg .. 32 lg + 31 (one 16-byte load),
+//           as the A operand of four 16x16x32 f16 MFMAs, MFMA kb pairing
+//           operand column 8 lg + e with dim 32 lg + 8 kb + e; the rotated
+//           queries (split into f16 hi + lo) use the same pairing. A key's
+//           score is scale * (q_rot . codes) + offset * sum(q_rot);
+//   P V     lane (g = lg, c = lr) adds keys 4g .. 4g + 3 for dims 8c .. 8c + 7
+//           with weights p * scale; sum over keys of p * offset is one number
+//           per row, carried beside the output and added to every dim.
+__global__ __launch_bounds__(256) void k_attn_split_q4(AttnK a) {
+  __shared__ float s_q[BLK][DH];
+  __shared__ float s_qsum[BLK];
+  const int seg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int len = a.lens[b];
+  const int n = min(len, a.window);
+  const int nblk = (n + 15) >> 4;
+  const int blk0 = (int)(((long long)seg * nblk) / a.S), blk1 = (int)(((long long)(seg + 1) * nblk) / a.S);
+  const float qs = 0.08838834764831845f * 1.4426950408889634f;  // 1/sqrt(128) * log2(e)
+  const size_t qrow0 = (size_t)(b * BLK) * H + h * DH;
+
+  float m_run = -__builtin_inff(), l_run = 0.f, w_run = 0.f;
+  float o[BLK][8];
 #pragma unroll
   for (int j = 0; j < BLK; ++j)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      o[j][e] += __shfl_xor(o[j][e], 16, 64);
-      o[j][e] += __shfl_xor(o[j][e], 32, 64);
+    for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
+
+  if (blk0 < blk1) {
+    // wave j turns block row j's query: R q = H (s * q) / sqrt(128), scaled
+    // like the scores (1/sqrt(128) * log2(e))
+    {
+      const float* qp = a.q + qrow0 + (size_t)wave * H;
+      float y0 = qp[lane] * a.signs[lane], y1 = qp[lane + 64] * a.signs[lane + 64];
+      fwht128(y0, y1, lane);
+      const float f = 0.08838834764831845f * qs;
+      y0 *= f;
+      y1 *= f;
+      s_q[wave][lane] = y0;
+      s_q[wave][lane + 64] = y1;
+      const float t = wave_sum(y0 + y1);
+      if (lane == 0) s_qsum[wave] = t;
     }
-  if (lg == 0) {
+    __syncthreads();
+    f16x8 qh[4], ql[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = lr < BLK ? s_q[lr][32 * lg + 8 * kb + e] : 0.f;
+        const _Float16 hh = (_Float16)v;
+        qh[kb][e] = hh;
+        ql[kb][e] = (_Float16)(v - (float)hh);
+      }
+    const float qsum = lr < BLK ? s_qsum[lr] : 0.f;
+
+    const size_t row0 = (size_t)(b * a.ss + h * a.sh);
+    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k) + row0 * 64;
+    const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v) + row0 * 64;
+    const uint32_t* ksb = reinterpret_cast<const uint32_t*>(a.kso) + row0;
+    const uint32_t* vsb = reinterpret_cast<const uint32_t*>(a.vso) + row0;
+    const int f0 = (len - n) % a.cap;
+    auto slot_of = [&](int key) {
+      const int s_ = f0 + min(key, n - 1);
+      return (size_t)(s_ - (s_ >= a.cap ? a.cap : 0)) * (size_t)a.sl;
+    };
+    // keys past n are clamped to the last visible key and masked in the scores
+    auto load_blk = [&](int bi, u32x4& kr, uint32_t (&vr)[4], uint32_t (&ks)[4], uint32_t (&vs)[4]) {
+      kr = *reinterpret_cast<const u32x4*>(kbase + slot_of(16 * bi + lr) * 64 + 16 * lg);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const size_t ro = slot_of(16 * bi + 4 * lg + t);
+        vr[t] = *reinterpret_cast<const uint32_t*>(vbase + ro * 64 + 4 * lr);
+        ks[t] = ksb[ro];
+        vs[t] = vsb[ro];
+      }
+    };
+    auto process = [&](int bi, const u32x4& kr, const uint32_t (&vr)[4], const uint32_t (&ks)[4],
+                       const uint32_t (&vs)[4]) __attribute__((always_inline)) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const f16x8 kk = nib8_f16(kr[kb]);
+        acc = mfma_f16(kk, qh[kb], acc);
+        acc = mfma_f16(kk, ql[kb], acc);
+      }
+      // lane (lr, lg): acc[e] = q_rot[lr] . codes[key 4lg + e]
+      float sc[4], mx = -__builtin_inff();
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float ksc, kof;
+        so_unpack(ks[e], ksc, kof);
+        sc[e] = 16 * bi + 4 * lg + e < n ? ksc * acc[e] + kof * qsum : -__builtin_inff();
+        mx = fmaxf(mx, sc[e]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_run == -__builtin_inff() ? 0.f : exp2f(m_run - m_new);
+      float pe[4], ls = 0.f, ws = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p = sc[e] == -__builtin_inff() ? 0.f : exp2f(sc[e] - m_new);
+        float vsc, vof;
+        so_unpack(vs[e], vsc, vof);
+        ls += p;
+        ws += p * vof;
+        pe[e] = p * vsc;
+      }
+      ls += __shfl_xor(ls, 16, 64);
+      ls += __shfl_xor(ls, 32, 64);
+      l_run = l_run * alpha + ls;
+      w_run = w_run * alpha + ws;
+      m_run = m_new;
+      // lane (g = lg, c = lr) gathers P[j][4g + t] * scale from lane (j, g)
+#pragma unroll
+      for (int j = 0; j < BLK; ++j) {
+        const float aj = __shfl(alpha, j, 64);
+        float pj[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) pj[t] = __shfl(pe[t], (lg << 4) | j, 64);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[j][e] *= aj;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            o[j][e] += pj[t] * (float)((vr[t] >> (4 * e)) & 0xFu);
+        }
+      }
+    };
+    // nibble e of a V dword is dim 8c + e: byte e/2, low nibble for even e,
+    // which is bits 4e .. 4e + 3 of the little-endian dword
+    const int last = blk1 - 1;
+    int bi = blk0 + wave;
+    u32x4 kA, kB;
+    uint32_t vA[4], vB[4], ksA[4], ksB[4], vsA[4], vsB[4];
+    load_blk(min(bi, last), kA, vA, ksA, vsA);
+    for (; bi <= last; bi += 8) {
+      load_blk(min(bi + 4, last), kB, vB, ksB, vsB);
+      process(bi, kA, vA, ksA, vsA);
+      if (bi + 4 > last) break;
+      load_blk(min(bi + 8, last), kA, vA, ksA, vsA);
+      process(bi + 4, kB, vB, ksB, vsB);
+    }
+    // the offsets' share: row j, key group g lives in lane (g, j)
 #pragma unroll
     for (int j = 0; j < BLK; ++j) {
-      *reinterpret_cast<f32x4*>(&s_o[wave][j][8 * lr]) = f32x4{o[j][0], o[j][1], o[j][2], o[j][3]};
-      *reinterpret_cast<f32x4*>(&s_o[wave][j][8 * lr + 4]) = f32x4{o[j][4], o[j][5], o[j][6], o[j][7]};
+      const float wj = __shfl(w_run, (lg << 4) | j, 64);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[j][e] += wj;
     }
   }
-  // row lr's max and sum live in every lane with lane % 16 == lr
-  if (lane < BLK) {
-    s_m[wave][lane] = m_run;
-    s_l[wave][lane] = l_run;
-  }
-  // the block's own scores s[j][i] (i <= j): wave j, lane l covers dims 2l, 2l+1
-  if (a.S == 1) {
-    const int j = wave;
-    const float q0 = a.q[qrow0 + (size_t)j * H + 2 * lane], q1 = a.q[qrow0 + (size_t)j * H + 2 * lane + 1];
-#pragma unroll
-    for (int i = 0; i < BLK; ++i) {
-      if (i > j) break;
-      const float* kp = a.kb + qrow0 + (size_t)i * H + 2 * lane;
-      const float p = wave_sum(q0 * kp[0] + q1 * kp[1]);
-      if (lane == 0) s_blk[j * BLK + i] = p * qs;
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int j = (threadIdx.x >> 7) + 2 * it, d = threadIdx.x & 127;
-    float M = -__builtin_inff();
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][j]);
-    float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      if (s_m[w][j] != -__builtin_inff()) {
-        const float f = exp2f(s_m[w][j] - M);
-        L += s_l[w][j] * f;
-        O += s_o[w][j][d] * f;
-      }
-    }
-    if (a.S == 1) {
-      const float out = attn_block_merge(s_blk, a.vb, qrow0, j, d, M, L, O);
-      a.af_o[afrag_off(b * BLK + j, h * DH + d, H / 32)] = __builtin_bit_cast(uint16_t, (_Float16)out);
-    } else {
-      const size_t pb = ((size_t)(b * NH + h) * a.nch + seg) * BLK + j;
-      a.po[pb * DH + d] = O;
-      if (d == 0) {
-        a.pm[pb] = M;
-        a.pl[pb] = L;
-      }
-    }
-  }
+  attn_finish(a, o, m_run, l_run, seg, h, b, qrow0);
 }
 
 // Merge of the chunk partials with the block's own keys (row j sees block rows
@@ -638,9 +858,12 @@ __global__ __launch_bounds__(128) void k_attn_combine(const float* q, const floa
   }
 }
 
-void launch_attention(hipStream_t st, const Work& w, int B, const KV& kv, int layer,
-                      const int32_t* lens, int window) {
+void launch_attention(hipStream_t st, const Work& w, const DevWeights& dw, int B, const KV& kv,
+                      int layer, const int32_t* lens, int window) {
   AttnK a;
+  a.kso = kv.kso[layer];
+  a.vso = kv.vso[layer];
+  a.signs = dw.kv_signs ? dw.kv_signs + layer * DH : nullptr;
   a.q = w.q;
   a.kb = w.kb;
   a.vb = w.vb;
@@ -664,7 +887,10 @@ void launch_attention(hipStream_t st, const Work& w, int B, const KV& kv, int la
   a.pl = w.att_l;
   a.po = w.att_o;
   a.af_o = w.af_o;
-  k_attn_split<<<dim3(S, NH, B), 256, 0, st>>>(a);
+  if (kv.fmt == 1)
+    k_attn_split_q4<<<dim3(S, NH, B), 256, 0, st>>>(a);
+  else
+    k_attn_split<<<dim3(S, NH, B), 256, 0, st>>>(a);
   if (S > 1)
     k_attn_combine<<<dim3(NH, B), 128, 0, st>>>(w.q, w.kb, w.vb, w.att_m, w.att_l, w.att_o,
                                                 w.att_nch, lens, window, S, w.af_o);
@@ -978,8 +1204,95 @@ __global__ __launch_bounds__(256) void k_ingest_store(const float* part, int spl
   }
 }
 
-void launch_ingest_store(hipStream_t st, const Work& w, int B, int n_new, int splits, const KV& kv,
-                         int layer, const int32_t* lens, float theta) {
+
+// The same rows for the rotated 4-bit cache (the article "Serving Kolibri-1
+// with a 4-bit KV cache", section What we do): wave w takes heads w, w + 4,
+// ...; lane l holds dims l and l + 64 (the RoPE pair). K after RoPE is turned
+// by R = H diag(s)/sqrt(128); K and V rows then get scale = fp16((max -
+// min)/15), offset = fp16(min) and codes clamp(rne((x - offset)/scale), 0,
+// 15) (0 for a zero scale).
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fminf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+// Codes the row held as (x0 at dim lane, x1 at dim lane + 64) and writes its
+// 64 code bytes and (scale, offset) pair.
+__device__ __forceinline__ void store_row_q4(float x0, float x1, int lane, uint8_t* codes,
+                                             uint32_t* so) {
+  const float mn = wave_min(fminf(x0, x1)), mx = wave_max(fmaxf(x0, x1));
+  const _Float16 sc_h = (_Float16)((mx - mn) / 15.0f), of_h = (_Float16)mn;
+  const float sc = (float)sc_h, of = (float)of_h;
+  auto code = [&](float x) -> uint32_t {
+    if (!(sc > 0.f)) return 0u;
+    const float c = __builtin_rintf((x - of) / sc);
+    return (uint32_t)fminf(fmaxf(c, 0.f), 15.f);
+  };
+  const uint32_t c0 = code(x0), c1 = code(x1);
+  // dims (2m, 2m + 1) meet in the even lane
+  const uint32_t n0 = __shfl_xor(c0, 1, 64), n1 = __shfl_xor(c1, 1, 64);
+  if ((lane & 1) == 0) {
+    codes[lane >> 1] = (uint8_t)(c0 | (n0 << 4));
+    codes[32 + (lane >> 1)] = (uint8_t)(c1 | (n1 << 4));
+  }
+  if (lane == 0)
+    *so = (uint32_t)__builtin_bit_cast(uint16_t, sc_h) | ((uint32_t)__builtin_bit_cast(uint16_t, of_h) << 16);
+}
+
+__global__ __launch_bounds__(256) void k_ingest_store_q4(const float* part, int splits, int rows,
+                                                         int n_new, uint8_t* kc, uint8_t* vc,
+                                                         uint32_t* kso, uint32_t* vso,
+                                                         int64_t ss, int64_t sh, int64_t sl,
+                                                         int cap, const int32_t* lens,
+                                                         float theta, const float* signs) {
+  const int r = blockIdx.x, b = r / n_new, i = r % n_new;
+  const long pos = (long)lens[b] + i;
+  const int slot = (int)(pos % cap);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int fi = lane;
+  const double ang = (double)pos * pow((double)theta, -(double)fi / (DH / 2));
+  const float cs = (float)cos(ang), sn = (float)sin(ang);
+  const float s0 = signs[fi], s1 = signs[fi + DH / 2];
+  for (int h = wave; h < NH; h += 4) {
+    const int c0 = h * DH + fi, c1 = c0 + DH / 2;
+    float ka = 0.f, kb2 = 0.f, va = 0.f, vb2 = 0.f;
+    const int pk0 = qkv_position(H + c0) - H, pk1 = qkv_position(H + c1) - H;
+    const int pv0 = qkv_position(2 * H + c0) - H, pv1 = qkv_position(2 * H + c1) - H;
+    for (int s = 0; s < splits; ++s) {
+      const float* pr = part + ((size_t)s * rows + r) * (2 * H);
+      ka += pr[pk0];
+      kb2 += pr[pk1];
+      va += pr[pv0];
+      vb2 += pr[pv1];
+    }
+    float y0 = (ka * cs - kb2 * sn) * s0, y1 = (ka * sn + kb2 * cs) * s1;
+    fwht128(y0, y1, lane);
+    y0 *= 0.08838834764831845f;
+    y1 *= 0.08838834764831845f;
+    const size_t row = (size_t)b * ss + (size_t)h * sh + (size_t)slot * sl;
+    store_row_q4(y0, y1, lane, kc + row * 64, kso + row);
+    store_row_q4(va, vb2, lane, vc + row * 64, vso + row);
+  }
+}
+
+void launch_ingest_store(hipStream_t st, const Work& w, const DevWeights& d, int B, int n_new,
+                         int splits, const KV& kv, int layer, const int32_t* lens, float theta) {
+  if (kv.fmt == 1) {
+    k_ingest_store_q4<<<B * n_new, 256, 0, st>>>(
+        w.part, splits, B * n_new, n_new,
+        reinterpret_cast<uint8_t*>(const_cast<uint16_t*>(kv.k[layer])),
+        reinterpret_cast<uint8_t*>(const_cast<uint16_t*>(kv.v[layer])),
+        reinterpret_cast<uint32_t*>(const_cast<uint16_t*>(kv.kso[layer])),
+        reinterpret_cast<uint32_t*>(const_cast<uint16_t*>(kv.vso[layer])), kv.ss, kv.sh, kv.sl,
+        kv.cap, lens, theta, d.kv_signs + layer * DH);
+    return;
+  }
   k_ingest_store<<<B * n_new, 256, 0, st>>>(w.part, splits, B * n_new, n_new,
                                             const_cast<uint16_t*>(kv.k[layer]),
                                             const_cast<uint16_t*>(kv.v[layer]), kv.ss, kv.sh,

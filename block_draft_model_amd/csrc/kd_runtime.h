@@ -47,15 +47,21 @@ struct DevWeightsT {
   int VD = 0, VT = 0;                     // draft vocab rows, 16-row tiles
   P<const int32_t> vocab = nullptr;
   P<const uint16_t> table = nullptr;      // borrowed bf16 [full_vocab][H]
+  P<const float> kv_signs = nullptr;      // [NL][DH] +-1 of the rotated 4-bit cache, or null
 };
 
-// Context K/V description passed to kernels.
+// Context K/V description passed to kernels. fmt 0: bf16 elements, strides
+// in elements. fmt 1: rotated 4-bit rows (64 code bytes at k + 64 i, an fp16
+// (scale, offset) pair at kso + 2 i, i = b ss + h sh + slot sl).
 template <template <class> class P>
 struct KVT {
   P<const uint16_t> k[4];
   P<const uint16_t> v[4];
   int64_t ss, sh, sl;
   int cap;
+  int fmt = 0;
+  P<const uint16_t> kso[4] = {};
+  P<const uint16_t> vso[4] = {};
 };
 
 using Fp8Mat = Fp8MatT<HostPtr>;
@@ -115,7 +121,7 @@ void launch_rowbuild(hipStream_t st, const Work& w, const DevWeights& d, int B, 
 void launch_spine_add_norm(hipStream_t st, const Work& w, int B, int splits, const float* gain,
                            float eps);
 void launch_qkv_post(hipStream_t st, const Work& w, int B, int splits);
-void launch_attention(hipStream_t st, const Work& w, int B, const KV& kv, int layer,
+void launch_attention(hipStream_t st, const Work& w, const DevWeights& d, int B, const KV& kv, int layer,
                       const int32_t* lens, int window);
 void launch_resid_norm(hipStream_t st, const Work& w, int R, int splits, const float* gain,
                        float eps, uint16_t* af_out, int spine_rows);
@@ -129,7 +135,7 @@ void launch_ingest_post_fuse(hipStream_t st, const Work& w, const DevWeights& d,
 void launch_ingest_c(hipStream_t st, const Work& w, int rows, int splits);
 void launch_norm_rows(hipStream_t st, const float* x, int rows, const float* gain, float eps,
                       uint16_t* af);
-void launch_ingest_store(hipStream_t st, const Work& w, int B, int n_new, int splits, const KV& kv,
+void launch_ingest_store(hipStream_t st, const Work& w, const DevWeights& d, int B, int n_new, int splits, const KV& kv,
                          int layer, const int32_t* lens, float theta);
 void launch_bump_lens(hipStream_t st, int32_t* lens, int B, int n);
 // many block rows (kd_mm.hip): matrix-core tiles of 64 rows x 256 columns

@@ -42,12 +42,16 @@ class KdWeights(ctypes.Structure):
     _fields_ = [(n, KdFp8Matrix) for n in ("fuse", "fc", "pred_a", "pred_b", "pred_u")] + [
         ("mask_row", c_void_p), ("layer", KdLayerWeights * 4), ("final_norm", c_void_p),
         ("head_q4", c_void_p), ("head_s4", c_void_p), ("head_g", c_float),
-        ("draft_vocab", c_void_p), ("embed_table", c_void_p)]
+        ("draft_vocab", c_void_p), ("embed_table", c_void_p), ("kv_rot_signs", c_void_p)]
+
+
+KD_KV_BF16, KD_KV_INT4_ROT = 0, 1
 
 
 class KdKV(ctypes.Structure):
     _fields_ = [("k", c_void_p * 4), ("v", c_void_p * 4), ("stride_stream", c_int64),
-                ("stride_head", c_int64), ("stride_slot", c_int64), ("capacity", c_int)]
+                ("stride_head", c_int64), ("stride_slot", c_int64), ("capacity", c_int),
+                ("format", c_int), ("k_so", c_void_p * 4), ("v_so", c_void_p * 4)]
 
 
 EXPORTS = ["kd_default_config", "kd_create", "kd_load_weights", "kd_round", "kd_round_depth",
@@ -186,6 +190,38 @@ def kv_struct(k_layers, v_layers) -> KdKV:
         kv.v[l] = v_layers[l].data_ptr()
     kv.stride_stream, kv.stride_head, kv.stride_slot = ref.stride(0), ref.stride(1), ref.stride(2)
     kv.capacity = ref.shape[2]
+    kv.format = KD_KV_BF16
+    return kv
+
+
+def kv_struct_int4(k_layers, v_layers, kso_layers, vso_layers) -> KdKV:
+    """Rotated 4-bit cache description from per-layer torch tensors: codes
+    uint8 [B][heads][capacity][head_dim/2] and (scale, offset) fp16 bits
+    [B][heads][capacity][2] (any 16-bit dtype). The library takes strides in
+    rows, so both tensors must index rows the same way."""
+    kv = KdKV()
+    ref, sref = k_layers[0], kso_layers[0]
+    for l in range(4):
+        for t in (k_layers[l], v_layers[l]):
+            if (t.shape != ref.shape or t.stride() != ref.stride() or t.element_size() != 1
+                    or t.shape[-1] != 64 or t.stride(-1) != 1):
+                raise ValueError("4-bit code tensors must share one [B][heads][capacity][64] byte layout")
+        for t in (kso_layers[l], vso_layers[l]):
+            if (t.shape != sref.shape or t.stride() != sref.stride() or t.element_size() != 2
+                    or t.shape[-1] != 2 or t.stride(-1) != 1):
+                raise ValueError("scale tensors must share one [B][heads][capacity][2] 16-bit layout")
+        kv.k[l], kv.v[l] = k_layers[l].data_ptr(), v_layers[l].data_ptr()
+        kv.k_so[l], kv.v_so[l] = kso_layers[l].data_ptr(), vso_layers[l].data_ptr()
+    if tuple(sref.shape[:3]) != tuple(ref.shape[:3]):
+        raise ValueError("codes and scales must cover the same rows")
+    rows = []
+    for i in range(3):
+        if ref.stride(i) % 64 or sref.stride(i) % 2 or ref.stride(i) // 64 != sref.stride(i) // 2:
+            raise ValueError("codes and scales must use the same row strides")
+        rows.append(ref.stride(i) // 64)
+    kv.stride_stream, kv.stride_head, kv.stride_slot = rows
+    kv.capacity = ref.shape[2]
+    kv.format = KD_KV_INT4_ROT
     return kv
 
 
@@ -248,6 +284,8 @@ class Drafter:
         w.head_q4, w.head_s4 = h(model["head.q4"]), h(model["head.s4"])
         w.head_g = float(model["head.g"])
         w.draft_vocab = h(model["vocab"])
+        if model.get("kv_rot_signs") is not None:
+            w.kv_rot_signs = h(model["kv_rot_signs"])
         table = model["table"]
         if not getattr(table, "is_cuda", False):
             raise ValueError("the embedding table must be a device tensor (it is borrowed)")

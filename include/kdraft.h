@@ -57,6 +57,8 @@ enum { KD_MAX_INGEST = 8 };  /* rows per stream per kd_ingest call */
 enum { KD_MAX_DEPTH = 8 };   /* rounds per kd_round_depth call */
 enum { KD_MAX_COPY = 48 };   /* tokens per copy-draft proposal */
 enum { KD_GUARD_MAX_WINDOW = 64 };  /* proposals the pause guard can track */
+/* Context K/V storage formats (kd_kv.format). */
+enum { KD_KV_BF16 = 0, KD_KV_INT4_ROT = 1 };
 
 /* Model shape and limits. The kernels are built for the model card's shape;
  * kd_create returns KD_ERR_UNSUPPORTED for any other hidden, heads, head_dim,
@@ -120,19 +122,43 @@ typedef struct {
   float head_g;                  /* fp32 tensor scale */
   const int32_t* draft_vocab;    /* [draft_vocab] target-vocabulary id of each head row */
   const void* embed_table;       /* DEVICE, bf16 [full_vocab][hidden], borrowed */
+  /* Sign vectors s of the rotated 4-bit cache, [layers][head_dim] int8, each
+   * +1 or -1 (see kd_kv), or NULL when no cache in that format is used. */
+  const int8_t* kv_rot_signs;
 } kd_weights;
 
-/* The context K/V cache (device, bf16), one K and one V tensor per layer.
- * Element (stream b, head h, slot s, dim d) of layer l lives at
- *   k[l] + b*stride_stream + h*stride_head + s*stride_slot + d   (elements),
- * head_dim contiguous. K is stored after RoPE. A context of len tokens keeps
- * position p at slot p % capacity; a round attends positions
- * [len - n, len) with n = min(len, window), so capacity >= window. */
+/* The context K/V cache (device), one K and one V tensor per layer. A
+ * context of len tokens keeps position p at slot p % capacity; a round attends
+ * positions [len - n, len) with n = min(len, window), so capacity >= window.
+ * K is stored after RoPE.
+ *
+ * format KD_KV_BF16: element (stream b, head h, slot s, dim d) of layer l is
+ *   the bf16 at k[l] + b*stride_stream + h*stride_head + s*stride_slot + d
+ *   (strides in elements, multiples of 8; head_dim contiguous). k_so/v_so
+ *   are ignored.
+ * format KD_KV_INT4_ROT (the article "Serving Kolibri-1 with a 4-bit KV
+ *   cache", section What we do): per layer a fixed R = H diag(s)/sqrt(128),
+ *   H the 128x128 Sylvester Hadamard matrix (H[i][j] = (-1)^popcount(i&j)) and
+ *   s the layer's kv_rot_signs; the cache holds R k for keys and v unrotated,
+ *   each (stream, head, slot) row as 128 4-bit codes plus an fp16 scale and
+ *   offset: value = scale * code + offset. Row index
+ *   i = b*stride_stream + h*stride_head + s*stride_slot (strides count rows);
+ *   its codes are the 64 bytes at k[l] + 64*i (dim 2m in the low nibble of
+ *   byte m, dim 2m+1 in the high nibble; 16-byte aligned tensors) and its
+ *   (scale, offset) pair the two fp16 at k_so[l] + 4*i (4-byte aligned); the
+ *   same for v / v_so. kd_ingest writes codes with scale = fp16((max-min)/15),
+ *   offset = fp16(min) over the row, code = clamp(round_half_even((x -
+ *   offset)/scale), 0, 15) (0 when the scale is 0). Rounds on this format
+ *   run the general (any batch) path and need kv_rot_signs loaded.
+ */
 typedef struct {
   void* k[4];
   void* v[4];
   int64_t stride_stream, stride_head, stride_slot;
   int capacity;
+  int format;        /* KD_KV_BF16 or KD_KV_INT4_ROT */
+  void* k_so[4];     /* KD_KV_INT4_ROT: (scale, offset) fp16 pairs of K, per row */
+  void* v_so[4];     /* KD_KV_INT4_ROT: the same for V */
 } kd_kv;
 
 /* Creates a context whose work goes to hip_stream (a hipStream_t; NULL is the
@@ -176,7 +202,8 @@ kd_status kd_round_depth(kd_ctx* ctx, int depth, int streams, const void* tapped
 /* Appends n_new context rows per stream (1 <= n_new <= KD_MAX_INGEST): row i
  * of stream b is [fuse(taps[b][i]) ; embed(next_ids[b][i])] -> fc, projected
  * through each layer's attention RMSNorm and W_k / W_v, K rotated at position
- * len + i, both rounded to bf16 and written at slot (len + i) % capacity;
+ * len + i, both rounded to bf16 (or, for KD_KV_INT4_ROT, K turned by R and
+ * both coded as described at kd_kv) and written at slot (len + i) % capacity;
  * then ctx_lens[b] += n_new on the device.
  *   taps     [streams][n_new][taps][hidden] bf16 (device)
  *   next_ids [streams][n_new] int32 (device) */

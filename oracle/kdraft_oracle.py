@@ -216,8 +216,8 @@ def _visible(length, dims):
 
 def _context_kv(M: OracleModel, inp: dict, l: int, b: int, slots):
     """The visible context keys and values of stream b, layer l, [heads][n][d].
-    A bf16 cache holds them directly. A rotated 4-bit cache (the INT4 KV
-    article, section Method) holds codes of R k and of v: the values are
+    A bf16 cache holds them directly. A rotated 4-bit cache (the 4-bit KV
+    cache article, section What we do) holds codes of R k and of v: the values are
     decoded, and the keys turned back by R^T, which leaves every score q.k
     as the rotated cache gives it, (R q).(R k)."""
     if inp.get("kv_format") == "int4":
@@ -313,8 +313,8 @@ def oracle_ingest(M: OracleModel, inp: dict, return_exact: bool = False):
     Every layer projects the same row c through its attention RMSNorm and
     W_k / W_v; K gets RoPE at its absolute position; both are rounded to bf16
     and stored at slot pos % capacity; len grows by the number of rows.
-    With a rotated 4-bit cache (kv_format "int4"; the INT4 KV article,
-    section Method) K is rotated by the layer's R after RoPE, and both K and V
+    With a rotated 4-bit cache (kv_format "int4"; the 4-bit KV cache
+    article, section What we do) K is rotated by the layer's R after RoPE, and both K and V
     are stored as codes with their fp16 scale and offset instead.
     Returns a new input dict (K/V copies and lengths updated); with
     return_exact also the unrounded fp64 K (rotated, for a 4-bit cache) and V

@@ -3,8 +3,8 @@
 TEST INFRASTRUCTURE ONLY: imported by the tests, by ``__graft_entry__.smoke()``
 and by the ``cpu_baseline`` leg of ``bench.py``; never by the library.
 
-Authority: the article "Serving Kolibri-1 with a rotated INT4 KV cache",
-section Method. Per attention layer a fixed matrix R = H diag(s) / sqrt(d)
+Authority: the article "Serving Kolibri-1 with a 4-bit KV cache", section
+What we do. Per attention layer a fixed matrix R = H diag(s) / sqrt(d)
 (H the d x d Hadamard matrix, s one random sign per column) rotates every key
 before it is cached and every query the same way, so q.k is unchanged
 (R is orthogonal). Keys and values are stored as 4-bit codes with one fp16

@@ -330,21 +330,22 @@ def _int4_cache(inp, dims, B, lens, device, base, poison):
     out = {"k": [], "v": [], "k_so": [], "v_so": []}
     for l in range(dims.layers):
         for name in ("k", "v"):
-            codes = torch.empty((B, NH, C, D // 2), dtype=torch.uint8)
-            so = torch.empty((B, NH, C, 2), dtype=torch.int16)
+            codes = torch.empty((B, NH, C, D // 2), dtype=torch.uint8, device=device)
+            so = torch.empty((B, NH, C, 2), dtype=torch.int16, device=device)
             for b in range(B):
-                z = _normal((NH, C, D), 1.0, "cpu", base, f"{name}{l}q", b)
+                z = _normal((NH, C, D), 1.0, device, base, f"{name}{l}q", b)
                 c = (7.5 + 2.5 * z).round().clamp(0, 15).to(torch.uint8)
                 codes[b] = c[..., 0::2] | (c[..., 1::2] << 4)
-                g = _gen("cpu", base, f"{name}{l}so", b)
-                sc = (0.25 + 0.2 * torch.rand((NH, C), generator=g)).to(torch.float16)
-                off = (-7.5 * sc.float() + 0.1 * torch.randn((NH, C), generator=g)).to(torch.float16)
+                g = _gen(device, base, f"{name}{l}so", b)
+                sc = (0.25 + 0.2 * torch.rand((NH, C), generator=g, device=device)).to(torch.float16)
+                off = (-7.5 * sc.float()
+                       + 0.1 * torch.randn((NH, C), generator=g, device=device)).to(torch.float16)
                 pair = torch.stack([sc.view(torch.int16), off.view(torch.int16)], dim=-1)
                 if poison:
-                    pair[:, ~_visible_mask(dims, lens[b], C)] = nan16
+                    pair[:, ~_visible_mask(dims, lens[b], C).to(device)] = nan16
                 so[b] = pair
-            out[name].append(codes.to(device))
-            out[name + "_so"].append(so.to(device))
+            out[name].append(codes)
+            out[name + "_so"].append(so)
     inp.update(out)
     inp["kv_format"] = "int4"
 

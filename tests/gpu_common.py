@@ -57,9 +57,15 @@ class Harness:
         kw.setdefault("poison", True)
         return synth.make_inputs(cfg, synth.FULL, device="cuda", vocab=self.model["vocab"], **kw)
 
+    @staticmethod
+    def kv(inp):
+        if inp.get("kv_format") == "int4":
+            return kdraft.kv_struct_int4(inp["k"], inp["v"], inp["k_so"], inp["v_so"])
+        return kdraft.kv_struct(inp["k"], inp["v"])
+
     def run(self, inp, logits=True):
         B = inp["streams"]
-        kv = kdraft.kv_struct(inp["k"], inp["v"])
+        kv = self.kv(inp)
         ids = torch.full((B, 4), -7, dtype=torch.int32, device="cuda")
         lg = torch.full((B, 4, synth.FULL.draft_vocab), float("nan"), device="cuda") if logits else None
         self.drafter.round(B, inp["taps"], inp["anchor"], inp["pred"], kv, inp["lens"], ids, lg)
@@ -68,7 +74,7 @@ class Harness:
 
     def ingest(self, inp):
         B = inp["streams"]
-        kv = kdraft.kv_struct(inp["k"], inp["v"])
+        kv = self.kv(inp)
         n = inp["ingest_ids"].shape[1]
         self.drafter.ingest(B, n, inp["ingest_taps"], inp["ingest_ids"], kv, inp["lens"])
         torch.cuda.synchronize()

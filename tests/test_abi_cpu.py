@@ -93,3 +93,37 @@ def test_copy_guard_follows_the_reference(lib):
 
 def test_copy_draft_argument_errors(lib):
     assert lib.kd_copy_draft(None, 1, None, 0, None, None, 0, 8, None, None) == kdraft.KD_ERR_ARG
+
+
+def test_ctypes_structs_match_the_c_header(tmp_path):
+    """The binding's ctypes structures have the header's sizes and field
+    offsets (compiled with the host C compiler from include/kdraft.h)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    checks = {
+        "kd_kv": (kdraft.KdKV, ["k", "v", "stride_stream", "capacity", "format", "k_so", "v_so"]),
+        "kd_weights": (kdraft.KdWeights, ["fuse", "mask_row", "layer", "final_norm", "head_g",
+                                          "embed_table", "kv_rot_signs"]),
+        "kd_config": (kdraft.KdConfig, ["hidden", "max_streams", "rope_theta", "head_quant"]),
+        "kd_copy_guard": (kdraft.KdCopyGuard, ["window", "min_accept", "proposed", "accepted"]),
+    }
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "kdraft.h"', "int main(void) {"]
+    for name, (_, fields) in checks.items():
+        lines.append(f'  printf("{name} sizeof %zu\\n", sizeof({name}));')
+        for f in fields:
+            lines.append(f'  printf("{name} {f} %zu\\n", offsetof({name}, {f}));')
+    lines.append("  return 0;\n}")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run([cc, "-I", inc, str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {tuple(l.split()[:2]): int(l.split()[2]) for l in out if l}
+    for name, (cls, fields) in checks.items():
+        assert got[(name, "sizeof")] == ctypes.sizeof(cls), name
+        for f in fields:
+            assert got[(name, f)] == getattr(cls, f).offset, (name, f)

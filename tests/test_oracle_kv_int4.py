@@ -1,7 +1,7 @@
 """Pins of the rotated 4-bit K/V cache in the oracle.
 
-The INT4 KV article ("Serving Kolibri-1 with a rotated INT4 KV cache",
-section Method) fixes R = H diag(s) / sqrt(d) with H the Hadamard matrix,
+The article "Serving Kolibri-1 with a 4-bit KV cache" (section What we do)
+fixes R = H diag(s) / sqrt(d) with H the Hadamard matrix,
 keys rotated before caching and queries by the same R (q.k unchanged), and
 4-bit codes with one fp16 scale and offset per token and head; values are not
 rotated. The pins below tie each step to something outside the oracle: the
