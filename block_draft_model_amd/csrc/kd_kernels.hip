@@ -397,14 +397,20 @@ __device__ __forceinline__ float attn_block_merge(const float* sblk, const float
 // output rows written (one segment) or the segment's (m, l, o) stored.
 // Thread (lr, lg) of wave w holds o[j][e] = unnormalised output of row j,
 // dims 8 lr + e, over its key group; m_run / l_run are row lr's (lr < 4).
-__device__ __forceinline__ void attn_finish(const AttnK& a, float (&o)[BLK][8], float m_run,
-                                            float l_run, int seg, int h, int b, size_t qrow0) {
-  __shared__ float s_o[4][BLK][DH];
-  __shared__ float s_m[4][BLK], s_l[4][BLK];
-  __shared__ float s_blk[BLK * BLK];
+struct AttnLds {
+  float o[4][BLK][DH];           // per wave: unnormalised output of each row
+  float m[4][BLK], l[4][BLK];    // per wave: running max and sum of each row
+  float blk[BLK * BLK];          // the block's own scores
+};
+
+__device__ __forceinline__ void attn_merge(const AttnK& a, AttnLds& s, float m_run, float l_run,
+                                           int seg, int h, int b, size_t qrow0);
+
+__device__ __forceinline__ void attn_finish(const AttnK& a, AttnLds& s, float (&o)[BLK][8],
+                                            float m_run, float l_run, int seg, int h, int b,
+                                            size_t qrow0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  const float qs = 0.08838834764831845f * 1.4426950408889634f;  // 1/sqrt(128) * log2(e)
   // sum the 4 key groups of the wave: lanes lg = 0 end with o[j][8 lr + e]
 #pragma unroll
   for (int j = 0; j < BLK; ++j)
@@ -416,14 +422,23 @@ __device__ __forceinline__ void attn_finish(const AttnK& a, float (&o)[BLK][8], 
   if (lg == 0) {
 #pragma unroll
     for (int j = 0; j < BLK; ++j) {
-      *reinterpret_cast<f32x4*>(&s_o[wave][j][8 * lr]) = f32x4{o[j][0], o[j][1], o[j][2], o[j][3]};
-      *reinterpret_cast<f32x4*>(&s_o[wave][j][8 * lr + 4]) = f32x4{o[j][4], o[j][5], o[j][6], o[j][7]};
+      *reinterpret_cast<f32x4*>(&s.o[wave][j][8 * lr]) = f32x4{o[j][0], o[j][1], o[j][2], o[j][3]};
+      *reinterpret_cast<f32x4*>(&s.o[wave][j][8 * lr + 4]) = f32x4{o[j][4], o[j][5], o[j][6], o[j][7]};
     }
   }
+  attn_merge(a, s, m_run, l_run, seg, h, b, qrow0);
+}
+
+// Wave w's s.o[w] must hold its rows' unnormalised outputs; m_run / l_run
+// are row lr's (lanes lr < 4). Merges the 4 waves and finishes the segment.
+__device__ __forceinline__ void attn_merge(const AttnK& a, AttnLds& s, float m_run, float l_run,
+                                           int seg, int h, int b, size_t qrow0) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float qs = 0.08838834764831845f * 1.4426950408889634f;  // 1/sqrt(128) * log2(e)
   // row lr's max and sum live in every lane with lane % 16 == lr
   if (lane < BLK) {
-    s_m[wave][lane] = m_run;
-    s_l[wave][lane] = l_run;
+    s.m[wave][lane] = m_run;
+    s.l[wave][lane] = l_run;
   }
   // the block's own scores s[j][i] (i <= j): wave j, lane l covers dims 2l, 2l+1
   if (a.S == 1) {
@@ -434,7 +449,7 @@ __device__ __forceinline__ void attn_finish(const AttnK& a, float (&o)[BLK][8], 
       if (i > j) break;
       const float* kp = a.kb + qrow0 + (size_t)i * H + 2 * lane;
       const float p = wave_sum(q0 * kp[0] + q1 * kp[1]);
-      if (lane == 0) s_blk[j * BLK + i] = p * qs;
+      if (lane == 0) s.blk[j * BLK + i] = p * qs;
     }
   }
   __syncthreads();
@@ -443,18 +458,18 @@ __device__ __forceinline__ void attn_finish(const AttnK& a, float (&o)[BLK][8], 
     const int j = (threadIdx.x >> 7) + 2 * it, d = threadIdx.x & 127;
     float M = -__builtin_inff();
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][j]);
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, s.m[w][j]);
     float L = 0.f, O = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      if (s_m[w][j] != -__builtin_inff()) {
-        const float f = exp2f(s_m[w][j] - M);
-        L += s_l[w][j] * f;
-        O += s_o[w][j][d] * f;
+      if (s.m[w][j] != -__builtin_inff()) {
+        const float f = exp2f(s.m[w][j] - M);
+        L += s.l[w][j] * f;
+        O += s.o[w][j][d] * f;
       }
     }
     if (a.S == 1) {
-      const float out = attn_block_merge(s_blk, a.vb, qrow0, j, d, M, L, O);
+      const float out = attn_block_merge(s.blk, a.vb, qrow0, j, d, M, L, O);
       a.af_o[afrag_off(b * BLK + j, h * DH + d, H / 32)] = __builtin_bit_cast(uint16_t, (_Float16)out);
     } else {
       const size_t pb = ((size_t)(b * NH + h) * a.nch + seg) * BLK + j;
@@ -468,6 +483,7 @@ __device__ __forceinline__ void attn_finish(const AttnK& a, float (&o)[BLK][8], 
 }
 
 __global__ __launch_bounds__(256) void k_attn_split(AttnK a) {
+  __shared__ AttnLds lds;
   const int seg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -588,7 +604,7 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnK a) {
       process(bi + 4, kB, vB);
     }
   }
-  attn_finish(a, o, m_run, l_run, seg, h, b, qrow0);
+  attn_finish(a, lds, o, m_run, l_run, seg, h, b, qrow0);
 }
 
 
@@ -644,10 +660,31 @@ __device__ __forceinline__ void so_unpack(uint32_t w, float& sc, float& of) {
 //           operand column 8 lg + e with dim 32 lg + 8 kb + e; the rotated
 //           queries (split into f16 hi + lo) use the same pairing. A key's
 //           score is scale * (q_rot . codes) + offset * sum(q_rot);
-//   P V     lane (g = lg, c = lr) adds keys 4g .. 4g + 3 for dims 8c .. 8c + 7
-//           with weights p * scale; sum over keys of p * offset is one number
-//           per row, carried beside the output and added to every dim.
+//   P V     on the matrix cores too, as O^T = V^T P'^T with P' = p * scale
+//           (16x16x16 f16, k = the block's 16 keys): the lane loads the V
+//           codes of keys 4 lg + e, dims 8 lr .. 8 lr + 7, and MFMA t (t =
+//           0..7) takes dim 8 i + t as its operand row i, so nibble t of the
+//           lane's 4 dwords is its A operand; its B operand, P'[lr][4 lg + e],
+//           is exactly what the lane's scores produced. MFMA t leaves
+//           O[lr][32 lg + 8 e + t] in element e of accumulator t. The sum over
+//           keys of p * offset is one number per row, carried beside the
+//           output and added to every dim.
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma_16x16x16_f16(f16x4 a, f16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+// Byte m of x0 and of x1 (each a code 0..15) -> f16x2 of the two codes.
+template <int M>
+__device__ __forceinline__ f16x2 byte_pair_f16(uint32_t x0, uint32_t x1) {
+  const f16x2 k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+  constexpr uint32_t sel = 0x0C000C00u | ((uint32_t)(4 + M) << 16) | (uint32_t)M;
+  return __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(x1, x0, sel) | 0x64006400u) - k1024;
+}
+
 __global__ __launch_bounds__(256) void k_attn_split_q4(AttnK a) {
+  __shared__ AttnLds lds;
   __shared__ float s_q[BLK][DH];
   __shared__ float s_qsum[BLK];
   const int seg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -661,11 +698,9 @@ __global__ __launch_bounds__(256) void k_attn_split_q4(AttnK a) {
   const size_t qrow0 = (size_t)(b * BLK) * H + h * DH;
 
   float m_run = -__builtin_inff(), l_run = 0.f, w_run = 0.f;
-  float o[BLK][8];
+  f32x4 oa[8];
 #pragma unroll
-  for (int j = 0; j < BLK; ++j)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
+  for (int t = 0; t < 8; ++t) oa[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (blk0 < blk1) {
     // wave j turns block row j's query: R q = H (s * q) / sqrt(128), scaled
@@ -738,7 +773,8 @@ __global__ __launch_bounds__(256) void k_attn_split_q4(AttnK a) {
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float m_new = fmaxf(m_run, mx);
       const float alpha = m_run == -__builtin_inff() ? 0.f : exp2f(m_run - m_new);
-      float pe[4], ls = 0.f, ws = 0.f;
+      f16x4 pb;
+      float ls = 0.f, ws = 0.f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float p = sc[e] == -__builtin_inff() ? 0.f : exp2f(sc[e] - m_new);
@@ -746,32 +782,39 @@ __global__ __launch_bounds__(256) void k_attn_split_q4(AttnK a) {
         so_unpack(vs[e], vsc, vof);
         ls += p;
         ws += p * vof;
-        pe[e] = p * vsc;
+        pb[e] = (_Float16)(p * vsc);
       }
       ls += __shfl_xor(ls, 16, 64);
       ls += __shfl_xor(ls, 32, 64);
       l_run = l_run * alpha + ls;
       w_run = w_run * alpha + ws;
       m_run = m_new;
-      // lane (g = lg, c = lr) gathers P[j][4g + t] * scale from lane (j, g)
+      // even nibbles (dims 8 lr + 2m) and odd nibbles (8 lr + 2m + 1) per key
+      uint32_t ev[4], od[4];
 #pragma unroll
-      for (int j = 0; j < BLK; ++j) {
-        const float aj = __shfl(alpha, j, 64);
-        float pj[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) pj[t] = __shfl(pe[t], (lg << 4) | j, 64);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[j][e] *= aj;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            o[j][e] += pj[t] * (float)((vr[t] >> (4 * e)) & 0xFu);
-        }
+      for (int e = 0; e < 4; ++e) {
+        ev[e] = vr[e] & 0x0F0F0F0Fu;
+        od[e] = (vr[e] >> 4) & 0x0F0F0F0Fu;
       }
+#define KD_PV_TILE(T, X, M)                                                    \
+  {                                                                            \
+    const f16x2 lo = byte_pair_f16<M>(X[0], X[1]);                             \
+    const f16x2 hi = byte_pair_f16<M>(X[2], X[3]);                             \
+    oa[T] *= alpha;                                                            \
+    oa[T] = mfma_16x16x16_f16(f16x4{lo.x, lo.y, hi.x, hi.y}, pb, oa[T]);       \
+  }
+      KD_PV_TILE(0, ev, 0)
+      KD_PV_TILE(1, od, 0)
+      KD_PV_TILE(2, ev, 1)
+      KD_PV_TILE(3, od, 1)
+      KD_PV_TILE(4, ev, 2)
+      KD_PV_TILE(5, od, 2)
+      KD_PV_TILE(6, ev, 3)
+      KD_PV_TILE(7, od, 3)
+#undef KD_PV_TILE
     };
-    // nibble e of a V dword is dim 8c + e: byte e/2, low nibble for even e,
-    // which is bits 4e .. 4e + 3 of the little-endian dword
+    // blocks of this wave: blk0 + wave + 4i; two register sets alternate so
+    // the next block's loads are in flight while one is computed
     const int last = blk1 - 1;
     int bi = blk0 + wave;
     u32x4 kA, kB;
@@ -784,15 +827,22 @@ __global__ __launch_bounds__(256) void k_attn_split_q4(AttnK a) {
       load_blk(min(bi + 8, last), kA, vA, ksA, vsA);
       process(bi + 4, kB, vB, ksB, vsB);
     }
-    // the offsets' share: row j, key group g lives in lane (g, j)
+  }
+  // the offsets' share of row lr, summed over the 4 key groups
+  w_run += __shfl_xor(w_run, 16, 64);
+  w_run += __shfl_xor(w_run, 32, 64);
+  // lane (lr < 4, lg) holds dims 32 lg + 8 e + t of row lr
+  if (lr < BLK) {
 #pragma unroll
-    for (int j = 0; j < BLK; ++j) {
-      const float wj = __shfl(w_run, (lg << 4) | j, 64);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[j][e] += wj;
+    for (int e = 0; e < 4; ++e) {
+      float* dst = &lds.o[wave][lr][32 * lg + 8 * e];
+      *reinterpret_cast<f32x4*>(dst) =
+          f32x4{oa[0][e] + w_run, oa[1][e] + w_run, oa[2][e] + w_run, oa[3][e] + w_run};
+      *reinterpret_cast<f32x4*>(dst + 4) =
+          f32x4{oa[4][e] + w_run, oa[5][e] + w_run, oa[6][e] + w_run, oa[7][e] + w_run};
     }
   }
-  attn_finish(a, o, m_run, l_run, seg, h, b, qrow0);
+  attn_merge(a, lds, m_run, l_run, seg, h, b, qrow0);
 }
 
 // Merge of the chunk partials with the block's own keys (row j sees block rows
