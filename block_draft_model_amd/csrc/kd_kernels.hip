@@ -634,18 +634,19 @@ __device__ __forceinline__ void fwht128(float& y0, float& y1, int lane) {
   }
 }
 
-// 8 4-bit codes (one dword, dim 2i in the low nibble of byte i) -> 8 exact
-// f16 values 0..15: each code is placed in the mantissa of 1024 (0x6400) and
-// 1024 subtracted again.
+// 8 4-bit codes (one dword, dim 2i in the low nibble of byte i) -> 8 f16
+// values code * 2^-24: each code becomes the mantissa of an f16 subnormal
+// (exact; the matrix cores take f16 subnormals as they are). Users scale
+// the products by 2^24.
 __device__ __forceinline__ f16x8 nib8_f16(uint32_t w) {
   const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-  const f16x2 k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
-  const f16x2 p0 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(hi, lo, 0x0C040C00u) | 0x64006400u) - k1024;
-  const f16x2 p1 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(hi, lo, 0x0C050C01u) | 0x64006400u) - k1024;
-  const f16x2 p2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(hi, lo, 0x0C060C02u) | 0x64006400u) - k1024;
-  const f16x2 p3 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(hi, lo, 0x0C070C03u) | 0x64006400u) - k1024;
+  const f16x2 p0 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(hi, lo, 0x0C040C00u));
+  const f16x2 p1 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(hi, lo, 0x0C050C01u));
+  const f16x2 p2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(hi, lo, 0x0C060C02u));
+  const f16x2 p3 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(hi, lo, 0x0C070C03u));
   return f16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
+constexpr float KD_2P24 = 16777216.0f;
 
 // (scale, offset) fp16 pair in one dword -> two floats.
 __device__ __forceinline__ void so_unpack(uint32_t w, float& sc, float& of) {
@@ -675,12 +676,12 @@ __device__ __forceinline__ f32x4 mfma_16x16x16_f16(f16x4 a, f16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 
-// Byte m of x0 and of x1 (each a code 0..15) -> f16x2 of the two codes.
+// Byte m of x0 and of x1 (each a code 0..15) -> f16x2 of the two codes
+// times 2^-24 (f16 subnormals, as in nib8_f16).
 template <int M>
 __device__ __forceinline__ f16x2 byte_pair_f16(uint32_t x0, uint32_t x1) {
-  const f16x2 k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
   constexpr uint32_t sel = 0x0C000C00u | ((uint32_t)(4 + M) << 16) | (uint32_t)M;
-  return __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(x1, x0, sel) | 0x64006400u) - k1024;
+  return __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(x1, x0, sel));
 }
 
 __global__ __launch_bounds__(256) void k_attn_split_q4(AttnK a) {
@@ -760,13 +761,13 @@ __global__ __launch_bounds__(256) void k_attn_split_q4(AttnK a) {
         acc = mfma_f16(kk, qh[kb], acc);
         acc = mfma_f16(kk, ql[kb], acc);
       }
-      // lane (lr, lg): acc[e] = q_rot[lr] . codes[key 4lg + e]
+      // lane (lr, lg): acc[e] = q_rot[lr] . codes[key 4lg + e] * 2^-24
       float sc[4], mx = -__builtin_inff();
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float ksc, kof;
         so_unpack(ks[e], ksc, kof);
-        sc[e] = 16 * bi + 4 * lg + e < n ? ksc * acc[e] + kof * qsum : -__builtin_inff();
+        sc[e] = 16 * bi + 4 * lg + e < n ? (ksc * KD_2P24) * acc[e] + kof * qsum : -__builtin_inff();
         mx = fmaxf(mx, sc[e]);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
@@ -831,15 +832,16 @@ __global__ __launch_bounds__(256) void k_attn_split_q4(AttnK a) {
   // the offsets' share of row lr, summed over the 4 key groups
   w_run += __shfl_xor(w_run, 16, 64);
   w_run += __shfl_xor(w_run, 32, 64);
-  // lane (lr < 4, lg) holds dims 32 lg + 8 e + t of row lr
+  // lane (lr < 4, lg) holds dims 32 lg + 8 e + t of row lr, times 2^-24
   if (lr < BLK) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
+      float v[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) v[t] = oa[t][e] * KD_2P24 + w_run;
       float* dst = &lds.o[wave][lr][32 * lg + 8 * e];
-      *reinterpret_cast<f32x4*>(dst) =
-          f32x4{oa[0][e] + w_run, oa[1][e] + w_run, oa[2][e] + w_run, oa[3][e] + w_run};
-      *reinterpret_cast<f32x4*>(dst + 4) =
-          f32x4{oa[4][e] + w_run, oa[5][e] + w_run, oa[6][e] + w_run, oa[7][e] + w_run};
+      *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{v[4], v[5], v[6], v[7]};
     }
   }
   attn_merge(a, lds, m_run, l_run, seg, h, b, qrow0);
