@@ -797,11 +797,16 @@ __global__ __launch_bounds__(256) void k_attn_split_q4(AttnK a) {
         ev[e] = vr[e] & 0x0F0F0F0Fu;
         od[e] = (vr[e] >> 4) & 0x0F0F0F0Fu;
       }
+      // the outputs are rescaled only when some row's maximum grew (after
+      // the first blocks, most blocks leave every maximum as it was)
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) oa[t] *= alpha;
+      }
 #define KD_PV_TILE(T, X, M)                                                    \
   {                                                                            \
     const f16x2 lo = byte_pair_f16<M>(X[0], X[1]);                             \
     const f16x2 hi = byte_pair_f16<M>(X[2], X[3]);                             \
-    oa[T] *= alpha;                                                            \
     oa[T] = mfma_16x16x16_f16(f16x4{lo.x, lo.y, hi.x, hi.y}, pb, oa[T]);       \
   }
       KD_PV_TILE(0, ev, 0)
