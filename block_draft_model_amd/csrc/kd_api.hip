@@ -326,6 +326,9 @@ kd_status check_kv(kd_ctx* c, const kd_kv* kv) {
     }
     if (kv->stride_slot < 1 || kv->stride_head < 1 || kv->stride_stream < 1)
       return fail(c, KD_ERR_ARG, "bad K/V strides");
+    // the attention addresses one (stream, head)'s slots with 32-bit offsets
+    if ((int64_t)(kv->capacity - 1) * kv->stride_slot * 64 + 64 > (int64_t)0xffffffffLL)
+      return fail(c, KD_ERR_ARG, "4-bit cache: one (stream, head) spans more than 4 GiB of codes");
     return KD_OK;
   }
   if (kv->format != KD_KV_BF16) return fail(c, KD_ERR_ARG, "unknown K/V format");

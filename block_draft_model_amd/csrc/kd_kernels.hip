@@ -731,25 +731,34 @@ __global__ __launch_bounds__(256) void k_attn_split_q4(AttnK a) {
       }
     const float qsum = lr < BLK ? s_qsum[lr] : 0.f;
 
+    // the rows of this (stream, head) through buffer resources: 32-bit
+    // offsets from a base held in scalar registers, and the hardware returns
+    // 0 for any offset past the span (the host checks the span fits 4 GiB)
     const size_t row0 = (size_t)(b * a.ss + h * a.sh);
-    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k) + row0 * 64;
-    const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v) + row0 * 64;
-    const uint32_t* ksb = reinterpret_cast<const uint32_t*>(a.kso) + row0;
-    const uint32_t* vsb = reinterpret_cast<const uint32_t*>(a.vso) + row0;
+    const uint32_t span = (uint32_t)((a.cap - 1) * a.sl + 1);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(reinterpret_cast<const uint8_t*>(a.k) + row0 * 64), (short)0, span * 64, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(reinterpret_cast<const uint8_t*>(a.v) + row0 * 64), (short)0, span * 64, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rks = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.kso + row0 * 2), (short)0, span * 4, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.vso + row0 * 2), (short)0, span * 4, 0x00020000);
+    const uint32_t sl = (uint32_t)a.sl;
     const int f0 = (len - n) % a.cap;
-    auto slot_of = [&](int key) {
+    auto row_of = [&](int key) {
       const int s_ = f0 + min(key, n - 1);
-      return (size_t)(s_ - (s_ >= a.cap ? a.cap : 0)) * (size_t)a.sl;
+      return (uint32_t)(s_ - (s_ >= a.cap ? a.cap : 0)) * sl;
     };
     // keys past n are clamped to the last visible key and masked in the scores
     auto load_blk = [&](int bi, u32x4& kr, uint32_t (&vr)[4], uint32_t (&ks)[4], uint32_t (&vs)[4]) {
-      kr = *reinterpret_cast<const u32x4*>(kbase + slot_of(16 * bi + lr) * 64 + 16 * lg);
+      kr = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, row_of(16 * bi + lr) * 64 + 16 * lg, 0, 0));
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const size_t ro = slot_of(16 * bi + 4 * lg + t);
-        vr[t] = *reinterpret_cast<const uint32_t*>(vbase + ro * 64 + 4 * lr);
-        ks[t] = ksb[ro];
-        vs[t] = vsb[ro];
+        const uint32_t ro = row_of(16 * bi + 4 * lg + t);
+        vr[t] = __builtin_amdgcn_raw_buffer_load_b32(rv, ro * 64 + 4 * lr, 0, 0);
+        ks[t] = __builtin_amdgcn_raw_buffer_load_b32(rks, ro * 4, 0, 0);
+        vs[t] = __builtin_amdgcn_raw_buffer_load_b32(rvs, ro * 4, 0, 0);
       }
     };
     auto process = [&](int bi, const u32x4& kr, const uint32_t (&vr)[4], const uint32_t (&ks)[4],
