@@ -134,3 +134,79 @@ def test_int4_argument_errors(hC):
     kv.v_so[1] = kv.v_so[1] + 2
     with pytest.raises(kdraft.KDraftError):
         hC.drafter.round(2, inp["taps"], inp["anchor"], inp["pred"], kv, inp["lens"], ids)
+
+
+def _slot_major(inp):
+    """The same cache stored slot-major ([B][capacity][heads][...] memory,
+    viewed as [B][heads][capacity][...]): the row strides become
+    (capacity * heads, 1, heads) instead of (heads * capacity, capacity, 1)."""
+    out = dict(inp)
+    for key in ("k", "v", "k_so", "v_so"):
+        out[key] = [t.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3) for t in inp[key]]
+    return out
+
+
+def test_int4_round_slot_major_layout(hC):
+    cfg = dict(name="int4 strides", streams=5, lens=("uniform", 1, 5000), model="C", ingest=0)
+    inp = hC.inputs(cfg, base=15, kv="int4")
+    alt = _slot_major(inp)
+    kv = Harness.kv(alt)
+    assert (kv.stride_stream, kv.stride_head, kv.stride_slot) == (2048 * 20, 1, 20)
+    a, ia = hC.run(inp)
+    b, ib = hC.run(alt)
+    # the same codes through other strides: the same round, bit for bit
+    assert np.array_equal(a, b) and np.array_equal(ia, ib)
+    ref, rid = oracle.oracle_round(hC.oracle, synth.to_numpy_inputs(alt))
+    compare(b, ib, ref, rid, hC.oracle.vocab, "int4 slot-major layout")
+
+
+def test_int4_depth_two_rounds(hC):
+    cfg = dict(name="int4 depth", streams=6, lens=("uniform", 30, 2500), model="C", ingest=0)
+    inp = hC.inputs(cfg, base=16, kv="int4")
+    B = inp["streams"]
+    kv = Harness.kv(inp)
+    ids = torch.full((B, 4), -7, dtype=torch.int32, device="cuda")
+    lg = torch.full((B, 4, synth.FULL.draft_vocab), float("nan"), device="cuda")
+    hC.drafter.round_depth(2, B, inp["taps"], inp["anchor"], inp["pred"], kv, inp["lens"], ids, lg)
+    torch.cuda.synchronize()
+    ref, rid = oracle.oracle_round_depth(hC.oracle, synth.to_numpy_inputs(inp), 2)
+    compare(lg.cpu().numpy().astype(np.float64), ids.cpu().numpy(), ref, rid, hC.oracle.vocab,
+            "int4 depth 2")
+
+
+def test_int4_ingest_wraps_the_ring(hC):
+    # new rows past the ring's end land at slots 0, 1, ...; an empty context
+    # and a long one (positions far past the capacity) as well
+    lens = [2046, 4095, 0, 9000]
+    cfg = dict(name="int4 ingest wrap", streams=4, lens=("const", 0), model="C", ingest=5)
+    inp = hC.inputs(cfg, base=17, lens_override=lens, kv="int4")
+    before = synth.to_numpy_inputs(inp)
+    hC.ingest(inp)
+    assert np.array_equal(inp["lens"].cpu().numpy(), np.array(lens) + 5)
+    after_gpu = synth.to_numpy_inputs(inp)
+    after_ref, exact = oracle.oracle_ingest(hC.oracle, before, return_exact=True)
+    for l in range(4):
+        for key, ex in (("k", exact[l][0]), ("v", exact[l][1])):
+            for b, L in enumerate(lens):
+                slots = [(L + i) % 2048 for i in range(5)]
+                x = ex[b].transpose(1, 0, 2)                             # [h][n][d]
+                y = kv_int4.decode_int4(after_gpu[key][l][b][:, slots], after_gpu[key + "_so"][l][b][:, slots])
+                sc = kv_int4.decode_f16(after_gpu[key + "_so"][l][b][:, slots, 0])[..., None]
+                rms = np.sqrt(np.mean(x * x, axis=-1, keepdims=True))
+                amax = np.abs(x).max(axis=-1, keepdims=True)
+                bound = 0.5 * sc + 2.0 ** -10 * amax + 2.0 ** -7 * rms
+                assert not (np.abs(y - x) > bound).any(), (l, key, b)
+    # the round on each side's own cache: the library's codes may differ by
+    # one step from the oracle's where the projection error crosses a
+    # rounding boundary (checked above). Over a full window those few steps
+    # move the logits by ~1e-3; the stream whose whole context is the 5 new
+    # rows sees each such step at full weight, so it is checked for valid
+    # output only.
+    lg, ids = hC.run(inp)
+    ref, rid = oracle.oracle_round(hC.oracle, after_ref)
+    rel = (np.linalg.norm(lg - ref, axis=-1) / np.linalg.norm(ref, axis=-1)).max(axis=-1)
+    log("int4 round after a wrapping ingest, max rel L2 per stream", rel.tolist())
+    full = [0, 1, 3]
+    compare(lg[full], ids[full], ref[full], rid[full], hC.oracle.vocab,
+            "int4 round after a wrapping ingest")
+    assert np.all(np.isfinite(lg[2])) and np.all(np.isin(ids[2], hC.oracle.vocab))
