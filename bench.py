@@ -30,19 +30,22 @@ KERNEL_NAME = {2: "kd::k_small_phase", 3: "kd::k_small_mega"}
 LAUNCHES_PER_ROUND = {2: 30, 3: 1}
 
 
-def algorithmic_bytes(dims, lens, streams, ingest=0, kv="bf16"):
+def algorithmic_bytes(dims, lens, streams, ingest=0, kv="bf16", head="nvfp4"):
     """Bytes a step must move: weights once (block-FP8 body with scales, NVFP4
     head with block and tensor scales, fp32 vectors), 40,960 B of bf16 K/V per
     visible context row per stream (4 layers x K,V x 20 heads x 128 x 2 B;
     with the rotated 4-bit cache 10,880 B: 64 code bytes and a 4-byte fp16
     scale and offset per layer, K/V, head), and per stream its tapped states,
-    4 embedding rows, ids, length and outputs.
+    4 embedding rows, ids, length and outputs. A bf16 head slice reads 2 B
+    per value instead of the NVFP4 head's codes and scales.
     With `ingest` new context rows per stream ahead of the round: their tapped
     states, next-token ids and embedding rows, and the 40,960 B of K/V each
     writes (the weights they use are the round's, counted once); `lens` are the
     lengths the round sees."""
     import synth
     mb = synth.model_bytes(dims)
+    if head == "bf16":
+        mb["head"] = dims.draft_vocab * dims.hidden * 2
     if kv == "int4":
         kv_row = dims.layers * 2 * dims.heads * (dims.head_dim // 2 + 4)
     else:
@@ -143,6 +146,8 @@ def main():
     ap.add_argument("--kv", choices=("bf16", "int4"), default="bf16",
                     help="context cache format: bf16, or rotated 4-bit codes with an fp16 "
                          "scale and offset per row (read by the general path)")
+    ap.add_argument("--head", choices=("nvfp4", "bf16"), default="nvfp4",
+                    help="head slice format: NVFP4, or bf16 (read by the general path)")
     ap.add_argument("--path", type=int, default=0,
                     help="0 automatic; 1 general multi-kernel; 2 small-batch phases as "
                          "separate launches; 3 small-batch persistent kernel")
@@ -173,11 +178,12 @@ def main():
         return
     cfg = synth.CONFIGS[args.config]
     dims = synth.FULL
-    model = synth.make_model(dims, cfg["model"], device="cuda")
+    model = synth.make_model(dims, cfg["model"], device="cuda", head=args.head)
     inp = synth.make_inputs(cfg, dims, device="cuda", vocab=model["vocab"], kv=args.kv)
     B = inp["streams"]
     stream = torch.cuda.current_stream()
-    drafter = kdraft.Drafter(max_streams=B, stream=stream)
+    drafter = kdraft.Drafter(max_streams=B, stream=stream,
+                             head_quant=kdraft.KD_QUANT_BF16 if args.head == "bf16" else kdraft.KD_QUANT_NVFP4)
     drafter.load_weights(model)
     drafter.debug_set_path(args.path)
     if args.kv == "int4":
@@ -209,7 +215,7 @@ def main():
     ms = start.elapsed_time(end) / args.steps
 
     path = drafter.last_path()
-    ab = algorithmic_bytes(dims, lens_host, B, n_ingest, args.kv)
+    ab = algorithmic_bytes(dims, lens_host, B, n_ingest, args.kv, args.head)
     rounds_s = 1000.0 / ms
     # roofline of the round's kernel: algorithmic bytes per launch over the
     # average launch duration (the HIP-event time of the timed rounds on the
@@ -236,9 +242,9 @@ def main():
                                   + (f" after ingesting {n_ingest} context rows per stream" if n_ingest else "")
                                   + ", draft block 4, "
                                   f"context rows per stream {sorted(set(min(l, 2048) for l in lens_host))}, "
-                                  f"block-FP8 body, NVFP4 head (60,614 rows)"
+                                  f"block-FP8 body, {'bf16' if args.head == 'bf16' else 'NVFP4'} head (60,614 rows)"
                                   + (", rotated 4-bit K/V cache" if args.kv == "int4" else ""),
-                      "streams": B, "draft_tokens_per_round": 4 * B, "kv_cache": args.kv,
+                      "streams": B, "draft_tokens_per_round": 4 * B, "kv_cache": args.kv, "head": args.head,
                       "path": {1: "general multi-kernel", 2: "small-batch phases, one launch each",
                                3: "small-batch persistent kernel"}[path]},
            "draft_tokens_per_s": round(4 * B * rounds_s, 1),

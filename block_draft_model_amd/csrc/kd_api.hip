@@ -385,7 +385,8 @@ kd_status kd_create(const kd_config* cfg, void* hip_stream, kd_ctx** out) {
   *out = nullptr;
   if (!cfg) return KD_ERR_ARG;
   if (!shape_is_supported(*cfg)) return KD_ERR_UNSUPPORTED;
-  if (cfg->body_quant != KD_QUANT_FP8_BLOCK64 || cfg->head_quant != KD_QUANT_NVFP4)
+  if (cfg->body_quant != KD_QUANT_FP8_BLOCK64 ||
+      (cfg->head_quant != KD_QUANT_NVFP4 && cfg->head_quant != KD_QUANT_BF16))
     return KD_ERR_UNSUPPORTED;
   if (cfg->window < 1 || cfg->draft_vocab < 1 || cfg->full_vocab < 1 || cfg->max_streams < 1 ||
       !(cfg->rms_eps >= 0.f) || !(cfg->rope_theta > 0.f))
@@ -486,10 +487,11 @@ kd_status kd_load_weights(kd_ctx* c, const kd_weights* wt) {
   if (!wt) return fail(c, KD_ERR_ARG, "weights is NULL");
   const int H = kd::H, F = kd::FF, r = kd::RK;
   const int VD = c->cfg.draft_vocab;
-  if (!wt->head_q4 || !wt->head_s4 || !wt->draft_vocab || !wt->embed_table || !wt->mask_row ||
-      !wt->final_norm)
+  const bool head_bf16 = c->cfg.head_quant == KD_QUANT_BF16;
+  if ((head_bf16 ? !wt->head_bf16 : (!wt->head_q4 || !wt->head_s4)) || !wt->draft_vocab ||
+      !wt->embed_table || !wt->mask_row || !wt->final_norm)
     return fail(c, KD_ERR_ARG, "NULL pointer in weights");
-  if (!std::isfinite(wt->head_g)) return fail(c, KD_ERR_ARG, "non-finite head scale");
+  if (!head_bf16 && !std::isfinite(wt->head_g)) return fail(c, KD_ERR_ARG, "non-finite head scale");
   for (int i = 0; i < VD; ++i)
     if (wt->draft_vocab[i] < 0 || wt->draft_vocab[i] >= c->cfg.full_vocab)
       return fail(c, KD_ERR_ARG, "draft vocabulary id out of range");
@@ -562,8 +564,43 @@ kd_status kd_load_weights(kd_ctx* c, const kd_weights* wt) {
     if ((st = upload_vec(c, sg.data(), sg.size(), &d.kv_signs)) != KD_OK) return st;
   }
 
+  const int VT = (VD + 15) / 16;
+  if (head_bf16) {
+    // bf16 head rows repacked to the B operand of the 16x16x32 bf16 matrix
+    // cores: [VT][H/32][64 lanes][8] (lane l: row 16 vt + l % 16, inputs
+    // 32 t + 8 (l / 16) .. + 8), rows past the vocabulary zero
+    const uint16_t* src = static_cast<const uint16_t*>(wt->head_bf16);
+    for (size_t i = 0; i < (size_t)VD * H; ++i)
+      if ((src[i] & 0x7f80) == 0x7f80) return fail(c, KD_ERR_ARG, "non-finite bf16 head value");
+    const int KT = H / 32;
+    std::vector<uint16_t> hb((size_t)VT * KT * 512, 0);
+    for (int vt = 0; vt < VT; ++vt)
+      for (int t = 0; t < KT; ++t)
+        for (int lane = 0; lane < 64; ++lane) {
+          const int row = 16 * vt + (lane & 15);
+          if (row >= VD) continue;
+          memcpy(&hb[((size_t)(vt * KT + t) * 64 + lane) * 8], src + (size_t)row * H + 32 * t + 8 * (lane >> 4),
+                 16);
+        }
+    uint16_t* dh;
+    int32_t* dv;
+    if (!dev_alloc(c->weight_allocs, &dh, hb.size()) || !dev_alloc(c->weight_allocs, &dv, (size_t)VD))
+      return fail(c, KD_ERR_OOM, "head allocation failed");
+    hipError_t e = hipMemcpy(dh, hb.data(), hb.size() * 2, hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+      e = hipMemcpy(dv, wt->draft_vocab, (size_t)VD * sizeof(int32_t), hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(c, e, "head upload");
+    d.head_fmt = 1;
+    d.hb = dh;
+    d.hq = nullptr;
+    d.hs = nullptr;
+    d.hg = 1.f;
+    d.VD = VD;
+    d.VT = VT;
+    d.vocab = dv;
+  } else {
   // NVFP4 head, repacked to 16-row vocab tiles (layout in kd_device.h).
-  const int VT = (VD + 15) / 16, KG = H / 128;
+  const int KG = H / 128;
   for (size_t i = 0; i < (size_t)VD * H / 16; ++i)
     if ((wt->head_s4[i] & 0x7f) == 0x7f) return fail(c, KD_ERR_ARG, "NaN head block scale");
   std::vector<uint8_t> hq((size_t)VT * KG * 64 * 16, 0), hs((size_t)VT * KG * 64 * 4, 0);
@@ -595,6 +632,9 @@ kd_status kd_load_weights(kd_ctx* c, const kd_weights* wt) {
   d.VD = VD;
   d.VT = VT;
   d.vocab = dv;
+  d.head_fmt = 0;
+  d.hb = nullptr;
+  }
   d.table = static_cast<const uint16_t*>(wt->embed_table);
   c->args_valid[0] = c->args_valid[1] = false;
   drop_graph(c->round_graph);
@@ -631,6 +671,7 @@ static kd_status round_impl(kd_ctx* c, int depth, int B, const void* taps, const
   if (path == 3 && !c->mega_ok) path = 2;
   if (path != 1 && B > kd::SB_MAX) path = 1;
   if (k.fmt == KD_KV_INT4_ROT) path = 1;   // the 4-bit cache is read by the general path
+  if (d.head_fmt == 1) path = 1;           // so is the bf16 head
   c->last_path = path;
   if (path != 1) {
     (void)hipGetLastError();

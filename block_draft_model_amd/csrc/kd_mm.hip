@@ -219,13 +219,18 @@ struct HeadMM {
   int R;
   const uint8_t* hq;    // [VT][H/128][64][16] e2m1 codes
   const uint8_t* hs;    // [VT][H/128][64][4] e4m3 scale codes
+  const uint16_t* hb;   // bf16 head instead: [VT][H/32][64][8]
   float g;
   int VD, VT;
   float* logits;        // [R][VD] or null
   unsigned long long* keys;
 };
 
-template <int CT, int D>
+// HQ = 0: NVFP4 head (e2m1 x e4m3 decoded exactly to f16, f16 matrix
+// cores). HQ = 1: bf16 head; each f16 activation is split exactly into two
+// bf16 terms (hi = its top 8 significant bits, lo = the rest, at most 3
+// bits) for the bf16 matrix cores.
+template <int CT, int D, int HQ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_head_mm(HeadMM a) {
   // [buffer][row tile][k tiles 0..3][lane] f16
   __shared__ __attribute__((aligned(16))) u32x4 sa[2][MM_RT * 4][64];
@@ -243,11 +248,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int vt0 = (m.cb * MM_WAVES + wave) * CT;
   const uint8_t* qp[CT];
   const uint8_t* sp[CT];
+  const uint16_t* bp[CT];
 #pragma unroll
   for (int c = 0; c < CT; ++c) {
     const int vt = min(vt0 + c, a.VT - 1);
-    qp[c] = a.hq + (size_t)vt * KG * 1024 + lane * 16;
-    sp[c] = a.hs + (size_t)vt * KG * 256 + lane * 4;
+    if constexpr (HQ == 0) {
+      qp[c] = a.hq + (size_t)vt * KG * 1024 + lane * 16;
+      sp[c] = a.hs + (size_t)vt * KG * 256 + lane * 4;
+    } else {
+      bp[c] = a.hb + (size_t)vt * KT * 512 + lane * 8;
+    }
   }
 
   f32x4 acc[MM_RT][CT];
@@ -257,7 +267,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     for (int c = 0; c < CT; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // register ring of D steps (128-input groups), as in k_gemm_mm
-  u32x4 ar[D][4], qr[D][CT];
+  u32x4 ar[D][4], qr[D][CT][HQ == 0 ? 1 : 4];
   uint32_t sr[D][CT];
   auto load = [&](int st, int d) __attribute__((always_inline)) {
     const size_t kc = (size_t)min(st, KG - 1);
@@ -265,8 +275,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     for (int j = 0; j < 4; ++j) ar[d][j] = *reinterpret_cast<const u32x4*>(ap + kc * 2048 + j * 512);
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
-      qr[d][c] = *reinterpret_cast<const u32x4*>(qp[c] + kc * 1024);
-      sr[d][c] = *reinterpret_cast<const uint32_t*>(sp[c] + kc * 256);
+      if constexpr (HQ == 0) {
+        qr[d][c][0] = *reinterpret_cast<const u32x4*>(qp[c] + kc * 1024);
+        sr[d][c] = *reinterpret_cast<const uint32_t*>(sp[c] + kc * 256);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qr[d][c][i] = *reinterpret_cast<const u32x4*>(bp[c] + (kc * 4 + i) * 512);
+      }
     }
   };
 #pragma unroll
@@ -280,25 +295,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     for (int d = 0; d < D; ++d) {
       const int kg = k0 + d;
       if (kg < KG) {
-        u32x4 q[CT];
+        u32x4 q[CT][HQ == 0 ? 1 : 4];
         uint32_t sv[CT];
 #pragma unroll
         for (int c = 0; c < CT; ++c) {
-          q[c] = qr[d][c];
+#pragma unroll
+          for (int i = 0; i < (HQ == 0 ? 1 : 4); ++i) q[c][i] = qr[d][c][i];
           sv[c] = sr[d][c];
         }
         load(kg + D, d);
         const int buf = kg & 1;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          f16x8 w[CT];
+          if constexpr (HQ == 0) {
+            f16x8 w[CT];
 #pragma unroll
-          for (int c = 0; c < CT; ++c) w[c] = nvfp4x8_f16(q[c][i], (sv[c] >> (8 * i)) & 0xffu);
+            for (int c = 0; c < CT; ++c) w[c] = nvfp4x8_f16(q[c][0][i], (sv[c] >> (8 * i)) & 0xffu);
 #pragma unroll
-          for (int r = 0; r < MM_RT; ++r) {
-            const f16x8 av = __builtin_bit_cast(f16x8, sa[buf][r * 4 + i][lane]);
+            for (int r = 0; r < MM_RT; ++r) {
+              const f16x8 av = __builtin_bit_cast(f16x8, sa[buf][r * 4 + i][lane]);
 #pragma unroll
-            for (int c = 0; c < CT; ++c) acc[r][c] = mfma_f16(av, w[c], acc[r][c]);
+              for (int c = 0; c < CT; ++c) acc[r][c] = mfma_f16(av, w[c], acc[r][c]);
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < MM_RT; ++r) {
+              const f16x8 av = __builtin_bit_cast(f16x8, sa[buf][r * 4 + i][lane]);
+              u32x4 hi, lo;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float v0 = (float)av[2 * e], v1 = (float)av[2 * e + 1];
+                const float h0 = u2f(f2u(v0) & 0xffff0000u), h1 = u2f(f2u(v1) & 0xffff0000u);
+                hi[e] = pack_hi16(h0, h1);
+                // v - h is exact and has at most 3 significant bits
+                lo[e] = pack_hi16(v0 - h0, v1 - h1);
+              }
+              const bf16x8 ah = __builtin_bit_cast(bf16x8, hi), al = __builtin_bit_cast(bf16x8, lo);
+#pragma unroll
+              for (int c = 0; c < CT; ++c) {
+                const bf16x8 w = __builtin_bit_cast(bf16x8, q[c][i]);
+                acc[r][c] = mfma_bf16(ah, w, acc[r][c]);
+                acc[r][c] = mfma_bf16(al, w, acc[r][c]);
+              }
+            }
           }
         }
         if (kg + 1 < KG) {
@@ -361,14 +400,21 @@ void launch_head_mm(hipStream_t st, const uint16_t* af, int R, const DevWeights&
   a.R = R;
   a.hq = d.hq;
   a.hs = d.hs;
+  a.hb = d.hb;
   a.g = d.hg;
   a.VD = d.VD;
   a.VT = d.VT;
   a.logits = logits;
   a.keys = keys;
+  if (d.head_fmt == 1) {
+    // bf16 head (4 times the NVFP4 bytes): 128 vocabulary rows per
+    // workgroup, two steps in flight, at every row count
+    k_head_mm<2, 2, 1><<<mm_grid(R, (d.VT + 7) / 8, 1), 256, 0, st>>>(a);
+    return;
+  }
   // 256 vocabulary rows per workgroup at every row count (narrower tiles
   // measured slower at 64 rows)
-  k_head_mm<4, 3><<<mm_grid(R, (d.VT + 15) / 16, 1), 256, 0, st>>>(a);
+  k_head_mm<4, 3, 0><<<mm_grid(R, (d.VT + 15) / 16, 1), 256, 0, st>>>(a);
 }
 
 }  // namespace kd

@@ -48,6 +48,8 @@ struct DevWeightsT {
   P<const int32_t> vocab = nullptr;
   P<const uint16_t> table = nullptr;      // borrowed bf16 [full_vocab][H]
   P<const float> kv_signs = nullptr;      // [NL][DH] +-1 of the rotated 4-bit cache, or null
+  int head_fmt = 0;                       // 0 NVFP4 (hq, hs, hg), 1 bf16 (hb)
+  P<const uint16_t> hb = nullptr;         // bf16 head [VT][H/32][64 lanes][8]
 };
 
 // Context K/V description passed to kernels. fmt 0: bf16 elements, strides

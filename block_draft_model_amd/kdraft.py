@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkdraft.so")
 
 KD_OK, KD_ERR_ARG, KD_ERR_STATE, KD_ERR_OOM, KD_ERR_HIP, KD_ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5
-KD_QUANT_FP8_BLOCK64, KD_QUANT_NVFP4 = 1, 2
+KD_QUANT_FP8_BLOCK64, KD_QUANT_NVFP4, KD_QUANT_BF16 = 1, 2, 3
 KD_MAX_INGEST = 8
 
 c_int, c_float, c_void_p, c_int64 = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int64
@@ -42,7 +42,8 @@ class KdWeights(ctypes.Structure):
     _fields_ = [(n, KdFp8Matrix) for n in ("fuse", "fc", "pred_a", "pred_b", "pred_u")] + [
         ("mask_row", c_void_p), ("layer", KdLayerWeights * 4), ("final_norm", c_void_p),
         ("head_q4", c_void_p), ("head_s4", c_void_p), ("head_g", c_float),
-        ("draft_vocab", c_void_p), ("embed_table", c_void_p), ("kv_rot_signs", c_void_p)]
+        ("draft_vocab", c_void_p), ("embed_table", c_void_p), ("kv_rot_signs", c_void_p),
+        ("head_bf16", c_void_p)]
 
 
 KD_KV_BF16, KD_KV_INT4_ROT = 0, 1
@@ -286,6 +287,10 @@ class Drafter:
         w.draft_vocab = h(model["vocab"])
         if model.get("kv_rot_signs") is not None:
             w.kv_rot_signs = h(model["kv_rot_signs"])
+        if model.get("head_bf16") is not None:
+            import torch
+            hb = model["head_bf16"]
+            w.head_bf16 = h(hb.view(torch.int16) if isinstance(hb, torch.Tensor) else hb)
         table = model["table"]
         if not getattr(table, "is_cuda", False):
             raise ValueError("the embedding table must be a device tensor (it is borrowed)")

@@ -52,7 +52,7 @@ typedef enum {
   KD_ERR_UNSUPPORTED = -5  /* a shape or format this build does not implement */
 } kd_status;
 
-enum { KD_QUANT_FP8_BLOCK64 = 1, KD_QUANT_NVFP4 = 2 };
+enum { KD_QUANT_FP8_BLOCK64 = 1, KD_QUANT_NVFP4 = 2, KD_QUANT_BF16 = 3 };
 enum { KD_MAX_INGEST = 8 };  /* rows per stream per kd_ingest call */
 enum { KD_MAX_DEPTH = 8 };   /* rounds per kd_round_depth call */
 enum { KD_MAX_COPY = 48 };   /* tokens per copy-draft proposal */
@@ -80,7 +80,9 @@ typedef struct {
   float rope_theta;  /* 10000 */
   float rms_eps;     /* 1e-6 */
   int body_quant;    /* KD_QUANT_FP8_BLOCK64 */
-  int head_quant;    /* KD_QUANT_NVFP4 */
+  int head_quant;    /* KD_QUANT_NVFP4, or KD_QUANT_BF16 (the card's Use section
+                        offers a bf16 head slice; rounds then run the general
+                        path at every batch size) */
 } kd_config;
 
 /* Fills *cfg with the model card's shape, max_streams = 256. */
@@ -125,6 +127,9 @@ typedef struct {
   /* Sign vectors s of the rotated 4-bit cache, [layers][head_dim] int8, each
    * +1 or -1 (see kd_kv), or NULL when no cache in that format is used. */
   const int8_t* kv_rot_signs;
+  /* head_quant = KD_QUANT_BF16: the head slice as bf16 [draft_vocab][hidden]
+   * (host; finite values), used instead of head_q4 / head_s4 / head_g. */
+  const void* head_bf16;
 } kd_weights;
 
 /* The context K/V cache (device), one K and one V tensor per layer. A

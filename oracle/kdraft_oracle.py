@@ -193,7 +193,12 @@ class OracleModel:
                 L["spine_a"], L["spine_u"] = W(sp + "a"), W(sp + "u")
             self.layers.append(L)
         self.final_norm = np.asarray(m["final_norm"], np.float64)
-        self.head = nvfp4(m["head.q4"], m["head.s4"], m["head.g"])
+        # the head slice: NVFP4 (the card's serving format) or, as its Use
+        # section allows, bf16
+        if m.get("head_format") == "bf16":
+            self.head = decode_bf16(m["head_bf16"])
+        else:
+            self.head = nvfp4(m["head.q4"], m["head.s4"], m["head.g"])
         self.vocab = np.asarray(m["vocab"], dtype=np.int64)
         self.table_bits = m["table"]           # bf16 bits; rows decoded on use
         # per-layer sign vectors of a rotated 4-bit cache (absent: bf16 only)

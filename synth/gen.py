@@ -144,7 +144,8 @@ def _fp8(model, name, rows, cols, device, base, zero=False):
     model[name + ".s"] = s
 
 
-def make_model(dims: Dims = FULL, variant: str = "A", device="cpu", base: int = 0):
+def make_model(dims: Dims = FULL, variant: str = "A", device="cpu", base: int = 0,
+               head: str = "nvfp4"):
     """Synthetic drafter weights.
 
     variant "A": predecessor and spine output projections U are zero (the
@@ -156,6 +157,8 @@ def make_model(dims: Dims = FULL, variant: str = "A", device="cpu", base: int = 
     NVFP4 quantisation of its rows at the (sorted) draft vocabulary.
     kv_rot_signs: int8 [layers][head_dim], each +1 or -1 with probability 1/2
     (the random signs of a rotated 4-bit K/V cache).
+    head="bf16": the head slice is also given unquantised, head_bf16 = the
+    table's bf16 rows at the draft vocabulary (head_format "bf16").
     """
     assert variant in ("A", "B", "C")
     H, F, r, L = dims.hidden, dims.ffn, dims.rank, dims.layers
@@ -197,6 +200,10 @@ def make_model(dims: Dims = FULL, variant: str = "A", device="cpu", base: int = 
     # one random sign per head dimension and layer, for a rotated 4-bit cache
     signs = torch.randint(0, 2, (L, dims.head_dim), generator=_gen("cpu", base, "kv_rot_signs"))
     m["kv_rot_signs"] = (1 - 2 * signs).to(torch.int8).to(device)
+    assert head in ("nvfp4", "bf16")
+    m["head_format"] = head
+    if head == "bf16":
+        m["head_bf16"] = table[vocab.to(device).long()].contiguous()
     return m
 
 

@@ -36,11 +36,13 @@ def require_gpu():
 class Harness:
     """A synthetic model on the GPU, loaded into one kd_ctx, plus its oracle."""
 
-    def __init__(self, variant: str, max_streams: int = 256, window: int = 2048):
+    def __init__(self, variant: str, max_streams: int = 256, window: int = 2048,
+                 head: str = "nvfp4"):
         t0 = time.time()
         self.variant = variant
-        self.model = synth.make_model(synth.FULL, variant, device="cuda")
-        self.drafter = kdraft.Drafter(max_streams=max_streams, window=window)
+        self.model = synth.make_model(synth.FULL, variant, device="cuda", head=head)
+        quant = {"nvfp4": kdraft.KD_QUANT_NVFP4, "bf16": kdraft.KD_QUANT_BF16}[head]
+        self.drafter = kdraft.Drafter(max_streams=max_streams, window=window, head_quant=quant)
         self.drafter.load_weights(self.model)
         self._oracle = None
         log(f"model {variant} ready in {time.time() - t0:.1f}s")

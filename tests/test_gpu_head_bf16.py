@@ -1,0 +1,99 @@
+"""GPU parity of the bf16 head slice (the model card "Kolibri-1 block
+drafter", section Use: the head slice can be bf16, FP8 or NVFP4; Serving: the
+NVFP4 head keeps the drafts at a quarter of the bf16 bytes).
+
+A bf16 head runs the general path at every batch size: the tiled head kernel
+reads the repacked bf16 rows and splits each f16 activation exactly into two
+bf16 terms for the bf16 matrix cores. Acceptance as for every round: relative
+L2 of the logits <= 1e-2 and ids equal wherever the oracle's top-1/top-2 gap
+exceeds 1e-2.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from block_draft_model_amd import kdraft
+from gpu_common import Harness, compare, log, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+C = synth.CONFIGS
+
+
+@pytest.fixture(scope="module")
+def hbC():
+    require_gpu()
+    return Harness("C", max_streams=256, head="bf16")
+
+
+def test_bf16_head_b4(hbC):
+    inp = hbC.inputs(C[1])
+    lg, ids = hbC.run(inp)
+    assert hbC.drafter.last_path() == 1
+    ref, rid = oracle.oracle_round(hbC.oracle, synth.to_numpy_inputs(inp))
+    compare(lg, ids, ref, rid, hbC.oracle.vocab, "bf16 head B4")
+
+
+def test_bf16_head_b1_and_edges(hbC):
+    lens = [0, 1, 129, 2048, 6000]
+    cfg = dict(name="bf16 head edges", streams=len(lens), lens=("const", 0), model="C", ingest=0)
+    inp = hbC.inputs(cfg, base=18, lens_override=lens)
+    lg, ids = hbC.run(inp)
+    ref, rid = oracle.oracle_round(hbC.oracle, synth.to_numpy_inputs(inp))
+    compare(lg, ids, ref, rid, hbC.oracle.vocab, "bf16 head edges")
+    one = hbC.inputs(C[0])
+    lg, ids = hbC.run(one)
+    ref, rid = oracle.oracle_round(hbC.oracle, synth.to_numpy_inputs(one))
+    compare(lg, ids, ref, rid, hbC.oracle.vocab, "bf16 head B1")
+
+
+def test_bf16_head_b16_ragged(hbC):
+    inp = hbC.inputs(C[2])
+    lg, ids = hbC.run(inp)
+    ref, rid = oracle.oracle_round(hbC.oracle, synth.to_numpy_inputs(inp))
+    compare(lg, ids, ref, rid, hbC.oracle.vocab, "bf16 head B16-ragged")
+
+
+def test_bf16_head_b256_sampled(hbC):
+    inp = hbC.inputs(C[4])
+    lg, ids = hbC.run(inp)
+    sample = [0, 5, 99, 200, 255]
+    ref, rid = oracle.oracle_round(hbC.oracle, synth.to_numpy_inputs(inp, streams=sample))
+    compare(lg[sample], ids[sample], ref, rid, hbC.oracle.vocab, "bf16 head B256 (sampled)")
+    assert np.all(np.isin(ids, hbC.oracle.vocab))
+
+
+def test_bf16_head_with_a_4bit_cache_and_depth(hbC):
+    cfg = dict(name="bf16 head int4", streams=6, lens=("uniform", 10, 3000), model="C", ingest=0)
+    inp = hbC.inputs(cfg, base=19, kv="int4")
+    B = inp["streams"]
+    ids = torch.full((B, 4), -7, dtype=torch.int32, device="cuda")
+    lg = torch.full((B, 4, synth.FULL.draft_vocab), float("nan"), device="cuda")
+    hbC.drafter.round_depth(2, B, inp["taps"], inp["anchor"], inp["pred"], Harness.kv(inp),
+                            inp["lens"], ids, lg)
+    torch.cuda.synchronize()
+    ref, rid = oracle.oracle_round_depth(hbC.oracle, synth.to_numpy_inputs(inp), 2)
+    compare(lg.cpu().numpy().astype(np.float64), ids.cpu().numpy(), ref, rid, hbC.oracle.vocab,
+            "bf16 head, 4-bit cache, depth 2")
+
+
+def test_bf16_head_weight_errors():
+    require_gpu()
+    m = synth.make_model(synth.FULL, "A", device="cuda", head="bf16")
+    d = kdraft.Drafter(max_streams=4, head_quant=kdraft.KD_QUANT_BF16)
+    bad = dict(m)
+    hb = m["head_bf16"].clone()
+    hb[7, 3] = float("inf")
+    bad["head_bf16"] = hb
+    with pytest.raises(kdraft.KDraftError):
+        d.load_weights(bad)
+    none = dict(m)
+    none["head_bf16"] = None
+    with pytest.raises(kdraft.KDraftError):
+        d.load_weights(none)
+    d.load_weights(m)
+    d.close()

@@ -210,3 +210,21 @@ def test_depth_with_zero_predecessor_head_is_one_round(models, inputs):
     one, ids1 = oracle.oracle_round(M, inputs)
     d3, i3 = oracle.oracle_round_depth(M, inputs, 3)
     assert np.array_equal(one, d3) and np.array_equal(ids1, i3)
+
+
+def test_bf16_head_is_the_full_head_gathered():
+    # the card's Use section allows a bf16 head slice: the LM head's rows at
+    # the draft vocabulary, unquantised
+    m = synth.make_model(D, "C", head="bf16")
+    mnp = synth.to_numpy_model(m)
+    M = oracle.OracleModel(mnp)
+    cfg = dict(name="h", streams=2, lens=("uniform", 1, 40), model="C", ingest=0)
+    inp = synth.to_numpy_inputs(synth.make_inputs(cfg, D, vocab=m["vocab"]))
+    logits, ids, x = oracle.oracle_round(M, inp, return_hidden=True)
+    full = oracle.decode_bf16(mnp["table"])                           # [full_vocab][H]
+    z = oracle.rmsnorm(x, M.final_norm, D.rms_eps)
+    assert np.allclose((z @ full.T)[..., mnp["vocab"]], logits, rtol=1e-12, atol=1e-12)
+    # the NVFP4 head of the same table drafts from nearby logits
+    Mq = oracle.OracleModel({k: v for k, v in mnp.items() if k != "head_format"})
+    lq, _ = oracle.oracle_round(Mq, inp)
+    assert 0 < np.abs(lq - logits).max() < 0.2 * np.abs(logits).max()
