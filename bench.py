@@ -46,6 +46,8 @@ def algorithmic_bytes(dims, lens, streams, ingest=0, kv="bf16", head="nvfp4"):
     mb = synth.model_bytes(dims)
     if head == "bf16":
         mb["head"] = dims.draft_vocab * dims.hidden * 2
+    elif head == "fp8":
+        mb["head"] = dims.draft_vocab * dims.hidden + dims.draft_vocab * dims.hidden // 64 * 4
     if kv == "int4":
         kv_row = dims.layers * 2 * dims.heads * (dims.head_dim // 2 + 4)
     else:
@@ -146,8 +148,8 @@ def main():
     ap.add_argument("--kv", choices=("bf16", "int4"), default="bf16",
                     help="context cache format: bf16, or rotated 4-bit codes with an fp16 "
                          "scale and offset per row (read by the general path)")
-    ap.add_argument("--head", choices=("nvfp4", "bf16"), default="nvfp4",
-                    help="head slice format: NVFP4, or bf16 (read by the general path)")
+    ap.add_argument("--head", choices=("nvfp4", "bf16", "fp8"), default="nvfp4",
+                    help="head slice format: NVFP4, or bf16 / block-FP8 (read by the general path)")
     ap.add_argument("--path", type=int, default=0,
                     help="0 automatic; 1 general multi-kernel; 2 small-batch phases as "
                          "separate launches; 3 small-batch persistent kernel")
@@ -183,7 +185,8 @@ def main():
     B = inp["streams"]
     stream = torch.cuda.current_stream()
     drafter = kdraft.Drafter(max_streams=B, stream=stream,
-                             head_quant=kdraft.KD_QUANT_BF16 if args.head == "bf16" else kdraft.KD_QUANT_NVFP4)
+                             head_quant={"nvfp4": kdraft.KD_QUANT_NVFP4, "bf16": kdraft.KD_QUANT_BF16,
+                                         "fp8": kdraft.KD_QUANT_FP8_BLOCK64}[args.head])
     drafter.load_weights(model)
     drafter.debug_set_path(args.path)
     if args.kv == "int4":
@@ -242,7 +245,7 @@ def main():
                                   + (f" after ingesting {n_ingest} context rows per stream" if n_ingest else "")
                                   + ", draft block 4, "
                                   f"context rows per stream {sorted(set(min(l, 2048) for l in lens_host))}, "
-                                  f"block-FP8 body, {'bf16' if args.head == 'bf16' else 'NVFP4'} head (60,614 rows)"
+                                  f"block-FP8 body, {dict(nvfp4='NVFP4', bf16='bf16', fp8='block-FP8')[args.head]} head (60,614 rows)"
                                   + (", rotated 4-bit K/V cache" if args.kv == "int4" else ""),
                       "streams": B, "draft_tokens_per_round": 4 * B, "kv_cache": args.kv, "head": args.head,
                       "path": {1: "general multi-kernel", 2: "small-batch phases, one launch each",

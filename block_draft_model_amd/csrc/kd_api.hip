@@ -386,7 +386,8 @@ kd_status kd_create(const kd_config* cfg, void* hip_stream, kd_ctx** out) {
   if (!cfg) return KD_ERR_ARG;
   if (!shape_is_supported(*cfg)) return KD_ERR_UNSUPPORTED;
   if (cfg->body_quant != KD_QUANT_FP8_BLOCK64 ||
-      (cfg->head_quant != KD_QUANT_NVFP4 && cfg->head_quant != KD_QUANT_BF16))
+      (cfg->head_quant != KD_QUANT_NVFP4 && cfg->head_quant != KD_QUANT_BF16 &&
+       cfg->head_quant != KD_QUANT_FP8_BLOCK64))
     return KD_ERR_UNSUPPORTED;
   if (cfg->window < 1 || cfg->draft_vocab < 1 || cfg->full_vocab < 1 || cfg->max_streams < 1 ||
       !(cfg->rms_eps >= 0.f) || !(cfg->rope_theta > 0.f))
@@ -488,10 +489,14 @@ kd_status kd_load_weights(kd_ctx* c, const kd_weights* wt) {
   const int H = kd::H, F = kd::FF, r = kd::RK;
   const int VD = c->cfg.draft_vocab;
   const bool head_bf16 = c->cfg.head_quant == KD_QUANT_BF16;
-  if ((head_bf16 ? !wt->head_bf16 : (!wt->head_q4 || !wt->head_s4)) || !wt->draft_vocab ||
+  const bool head_fp8 = c->cfg.head_quant == KD_QUANT_FP8_BLOCK64;
+  if ((head_bf16 ? !wt->head_bf16
+                 : head_fp8 ? (!wt->head_fp8.q || !wt->head_fp8.s) : (!wt->head_q4 || !wt->head_s4)) ||
+      !wt->draft_vocab ||
       !wt->embed_table || !wt->mask_row || !wt->final_norm)
     return fail(c, KD_ERR_ARG, "NULL pointer in weights");
-  if (!head_bf16 && !std::isfinite(wt->head_g)) return fail(c, KD_ERR_ARG, "non-finite head scale");
+  if (!head_bf16 && !head_fp8 && !std::isfinite(wt->head_g))
+    return fail(c, KD_ERR_ARG, "non-finite head scale");
   for (int i = 0; i < VD; ++i)
     if (wt->draft_vocab[i] < 0 || wt->draft_vocab[i] >= c->cfg.full_vocab)
       return fail(c, KD_ERR_ARG, "draft vocabulary id out of range");
@@ -565,7 +570,29 @@ kd_status kd_load_weights(kd_ctx* c, const kd_weights* wt) {
   }
 
   const int VT = (VD + 15) / 16;
-  if (head_bf16) {
+  d.hf8 = kd::Fp8Mat();
+  if (head_fp8) {
+    // block-FP8 head rows, zero rows (code 0, scale 1) up to whole 16-row
+    // tiles, repacked as a body matrix
+    HostMat m;
+    if (!append_rows(m, wt->head_fp8, VD, H)) return fail(c, KD_ERR_ARG, "bad FP8 head");
+    m.q.resize((size_t)VT * 16 * H, 0);
+    m.s.resize((size_t)VT * 16 * H / 64, 1.0f);
+    m.N = VT * 16;
+    if ((st = upload_mat(c, m, &d.hf8)) != KD_OK) return st;
+    int32_t* dv;
+    if (!dev_alloc(c->weight_allocs, &dv, (size_t)VD)) return fail(c, KD_ERR_OOM, "head allocation failed");
+    const hipError_t e = hipMemcpy(dv, wt->draft_vocab, (size_t)VD * sizeof(int32_t), hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(c, e, "head upload");
+    d.head_fmt = 2;
+    d.hb = nullptr;
+    d.hq = nullptr;
+    d.hs = nullptr;
+    d.hg = 1.f;
+    d.VD = VD;
+    d.VT = VT;
+    d.vocab = dv;
+  } else if (head_bf16) {
     // bf16 head rows repacked to the B operand of the 16x16x32 bf16 matrix
     // cores: [VT][H/32][64 lanes][8] (lane l: row 16 vt + l % 16, inputs
     // 32 t + 8 (l / 16) .. + 8), rows past the vocabulary zero
@@ -671,7 +698,7 @@ static kd_status round_impl(kd_ctx* c, int depth, int B, const void* taps, const
   if (path == 3 && !c->mega_ok) path = 2;
   if (path != 1 && B > kd::SB_MAX) path = 1;
   if (k.fmt == KD_KV_INT4_ROT) path = 1;   // the 4-bit cache is read by the general path
-  if (d.head_fmt == 1) path = 1;           // so is the bf16 head
+  if (d.head_fmt != 0) path = 1;           // so are the bf16 and FP8 heads
   c->last_path = path;
   if (path != 1) {
     (void)hipGetLastError();

@@ -1129,7 +1129,7 @@ __global__ __launch_bounds__(256) void k_head(HeadK a) {
 }
 
 void launch_head(hipStream_t st, const Work& w, const DevWeights& d, int R, float* logits) {
-  if (head_mm_fits(R) || d.head_fmt == 1) return launch_head_mm(st, w.af_x, R, d, logits, w.keys);
+  if (head_mm_fits(R) || d.head_fmt != 0) return launch_head_mm(st, w.af_x, R, d, logits, w.keys);
   HeadK a;
   a.af = w.af_x;
   a.R = R;

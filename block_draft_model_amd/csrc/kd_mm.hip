@@ -220,6 +220,8 @@ struct HeadMM {
   const uint8_t* hq;    // [VT][H/128][64][16] e2m1 codes
   const uint8_t* hs;    // [VT][H/128][64][4] e4m3 scale codes
   const uint16_t* hb;   // bf16 head instead: [VT][H/32][64][8]
+  const uint8_t* fw;    // or a block-FP8 head: codes [VT][H/64][64][16]
+  const float* fs;      //   and scales [VT][H/64][16]
   float g;
   int VD, VT;
   float* logits;        // [R][VD] or null
@@ -229,7 +231,8 @@ struct HeadMM {
 // HQ = 0: NVFP4 head (e2m1 x e4m3 decoded exactly to f16, f16 matrix
 // cores). HQ = 1: bf16 head; each f16 activation is split exactly into two
 // bf16 terms (hi = its top 8 significant bits, lo = the rest, at most 3
-// bits) for the bf16 matrix cores.
+// bits) for the bf16 matrix cores. HQ = 2: block-FP8 head, e4m3 decoded
+// exactly to f16, each 64-input block's product scaled by its row's scale.
 template <int CT, int D, int HQ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_head_mm(HeadMM a) {
   // [buffer][row tile][k tiles 0..3][lane] f16
@@ -249,14 +252,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const uint8_t* qp[CT];
   const uint8_t* sp[CT];
   const uint16_t* bp[CT];
+  const float* fsp[CT];
 #pragma unroll
   for (int c = 0; c < CT; ++c) {
     const int vt = min(vt0 + c, a.VT - 1);
     if constexpr (HQ == 0) {
       qp[c] = a.hq + (size_t)vt * KG * 1024 + lane * 16;
       sp[c] = a.hs + (size_t)vt * KG * 256 + lane * 4;
-    } else {
+    } else if constexpr (HQ == 1) {
       bp[c] = a.hb + (size_t)vt * KT * 512 + lane * 8;
+    } else {
+      qp[c] = a.fw + (size_t)vt * (H / 64) * 1024 + lane * 16;
+      fsp[c] = a.fs + (size_t)vt * (H / 64) * 16 + (lane & 15);
     }
   }
 
@@ -267,8 +274,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     for (int c = 0; c < CT; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // register ring of D steps (128-input groups), as in k_gemm_mm
-  u32x4 ar[D][4], qr[D][CT][HQ == 0 ? 1 : 4];
+  constexpr int NQ = HQ == 0 ? 1 : (HQ == 1 ? 4 : 2);
+  u32x4 ar[D][4], qr[D][CT][NQ];
   uint32_t sr[D][CT];
+  float fr[D][CT][2];
   auto load = [&](int st, int d) __attribute__((always_inline)) {
     const size_t kc = (size_t)min(st, KG - 1);
 #pragma unroll
@@ -278,9 +287,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       if constexpr (HQ == 0) {
         qr[d][c][0] = *reinterpret_cast<const u32x4*>(qp[c] + kc * 1024);
         sr[d][c] = *reinterpret_cast<const uint32_t*>(sp[c] + kc * 256);
-      } else {
+      } else if constexpr (HQ == 1) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) qr[d][c][i] = *reinterpret_cast<const u32x4*>(bp[c] + (kc * 4 + i) * 512);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          qr[d][c][j] = *reinterpret_cast<const u32x4*>(qp[c] + (kc * 2 + j) * 1024);
+          fr[d][c][j] = fsp[c][(kc * 2 + j) * 16];
+        }
       }
     }
   };
@@ -295,18 +310,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     for (int d = 0; d < D; ++d) {
       const int kg = k0 + d;
       if (kg < KG) {
-        u32x4 q[CT][HQ == 0 ? 1 : 4];
+        u32x4 q[CT][NQ];
         uint32_t sv[CT];
+        float fv[CT][2];
 #pragma unroll
         for (int c = 0; c < CT; ++c) {
 #pragma unroll
-          for (int i = 0; i < (HQ == 0 ? 1 : 4); ++i) q[c][i] = qr[d][c][i];
+          for (int i = 0; i < NQ; ++i) q[c][i] = qr[d][c][i];
           sv[c] = sr[d][c];
+          fv[c][0] = fr[d][c][0];
+          fv[c][1] = fr[d][c][1];
         }
         load(kg + D, d);
         const int buf = kg & 1;
+        if constexpr (HQ == 2) {
+          // two 64-input blocks per step, each scaled by its row's scale
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+          for (int j = 0; j < 2; ++j) {
+            f16x8 w0[CT], w1[CT];
+#pragma unroll
+            for (int c = 0; c < CT; ++c) {
+              w0[c] = e4m3x8_f16(q[c][j].x, q[c][j].y);
+              w1[c] = e4m3x8_f16(q[c][j].z, q[c][j].w);
+            }
+#pragma unroll
+            for (int r = 0; r < MM_RT; ++r) {
+              const f16x8 a0 = __builtin_bit_cast(f16x8, sa[buf][r * 4 + 2 * j][lane]);
+              const f16x8 a1 = __builtin_bit_cast(f16x8, sa[buf][r * 4 + 2 * j + 1][lane]);
+#pragma unroll
+              for (int c = 0; c < CT; ++c) {
+                f32x4 t = {0.f, 0.f, 0.f, 0.f};
+                t = mfma_f16(a0, w0[c], t);
+                t = mfma_f16(a1, w1[c], t);
+                acc[r][c] += fv[c][j] * t;
+              }
+            }
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < (HQ == 2 ? 0 : 4); ++i) {
           if constexpr (HQ == 0) {
             f16x8 w[CT];
 #pragma unroll
@@ -317,7 +359,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
               for (int c = 0; c < CT; ++c) acc[r][c] = mfma_f16(av, w[c], acc[r][c]);
             }
-          } else {
+          } else if constexpr (HQ == 1) {
 #pragma unroll
             for (int r = 0; r < MM_RT; ++r) {
               const f16x8 av = __builtin_bit_cast(f16x8, sa[buf][r * 4 + i][lane]);
@@ -401,11 +443,19 @@ void launch_head_mm(hipStream_t st, const uint16_t* af, int R, const DevWeights&
   a.hq = d.hq;
   a.hs = d.hs;
   a.hb = d.hb;
+  a.fw = d.hf8.w;
+  a.fs = d.hf8.s;
   a.g = d.hg;
   a.VD = d.VD;
   a.VT = d.VT;
   a.logits = logits;
   a.keys = keys;
+  if (d.head_fmt == 2) {
+    // block-FP8 head (2 times the NVFP4 bytes): 128 vocabulary rows per
+    // workgroup, two steps in flight, at every row count
+    k_head_mm<2, 2, 2><<<mm_grid(R, (d.VT + 7) / 8, 1), 256, 0, st>>>(a);
+    return;
+  }
   if (d.head_fmt == 1) {
     // bf16 head (4 times the NVFP4 bytes): 128 vocabulary rows per
     // workgroup, two steps in flight, at every row count

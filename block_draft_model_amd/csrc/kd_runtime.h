@@ -48,8 +48,9 @@ struct DevWeightsT {
   P<const int32_t> vocab = nullptr;
   P<const uint16_t> table = nullptr;      // borrowed bf16 [full_vocab][H]
   P<const float> kv_signs = nullptr;      // [NL][DH] +-1 of the rotated 4-bit cache, or null
-  int head_fmt = 0;                       // 0 NVFP4 (hq, hs, hg), 1 bf16 (hb)
+  int head_fmt = 0;                       // 0 NVFP4 (hq, hs, hg), 1 bf16 (hb), 2 FP8 (hf8)
   P<const uint16_t> hb = nullptr;         // bf16 head [VT][H/32][64 lanes][8]
+  Fp8MatT<P> hf8;                         // block-FP8 head, VT * 16 rows (zero-padded)
 };
 
 // Context K/V description passed to kernels. fmt 0: bf16 elements, strides

@@ -43,7 +43,7 @@ class KdWeights(ctypes.Structure):
         ("mask_row", c_void_p), ("layer", KdLayerWeights * 4), ("final_norm", c_void_p),
         ("head_q4", c_void_p), ("head_s4", c_void_p), ("head_g", c_float),
         ("draft_vocab", c_void_p), ("embed_table", c_void_p), ("kv_rot_signs", c_void_p),
-        ("head_bf16", c_void_p)]
+        ("head_bf16", c_void_p), ("head_fp8", KdFp8Matrix)]
 
 
 KD_KV_BF16, KD_KV_INT4_ROT = 0, 1
@@ -291,6 +291,8 @@ class Drafter:
             import torch
             hb = model["head_bf16"]
             w.head_bf16 = h(hb.view(torch.int16) if isinstance(hb, torch.Tensor) else hb)
+        if model.get("head_fp8.q") is not None:
+            w.head_fp8 = fp8("head_fp8")
         table = model["table"]
         if not getattr(table, "is_cuda", False):
             raise ValueError("the embedding table must be a device tensor (it is borrowed)")

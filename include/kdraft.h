@@ -80,8 +80,9 @@ typedef struct {
   float rope_theta;  /* 10000 */
   float rms_eps;     /* 1e-6 */
   int body_quant;    /* KD_QUANT_FP8_BLOCK64 */
-  int head_quant;    /* KD_QUANT_NVFP4, or KD_QUANT_BF16 (the card's Use section
-                        offers a bf16 head slice; rounds then run the general
+  int head_quant;    /* KD_QUANT_NVFP4, or KD_QUANT_BF16 / KD_QUANT_FP8_BLOCK64
+                        (the card's Use section offers bf16, FP8 and NVFP4
+                        head slices; the bf16 and FP8 heads run the general
                         path at every batch size) */
 } kd_config;
 
@@ -130,6 +131,9 @@ typedef struct {
   /* head_quant = KD_QUANT_BF16: the head slice as bf16 [draft_vocab][hidden]
    * (host; finite values), used instead of head_q4 / head_s4 / head_g. */
   const void* head_bf16;
+  /* head_quant = KD_QUANT_FP8_BLOCK64: the head slice in block-FP8,
+   * [draft_vocab][hidden], as the body matrices. */
+  kd_fp8_matrix head_fp8;
 } kd_weights;
 
 /* The context K/V cache (device), one K and one V tensor per layer. A

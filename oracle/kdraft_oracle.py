@@ -194,9 +194,11 @@ class OracleModel:
             self.layers.append(L)
         self.final_norm = np.asarray(m["final_norm"], np.float64)
         # the head slice: NVFP4 (the card's serving format) or, as its Use
-        # section allows, bf16
+        # section allows, bf16 or block-FP8
         if m.get("head_format") == "bf16":
             self.head = decode_bf16(m["head_bf16"])
+        elif m.get("head_format") == "fp8":
+            self.head = block_fp8(m["head_fp8.q"], m["head_fp8.s"])
         else:
             self.head = nvfp4(m["head.q4"], m["head.s4"], m["head.g"])
         self.vocab = np.asarray(m["vocab"], dtype=np.int64)

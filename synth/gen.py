@@ -158,7 +158,8 @@ def make_model(dims: Dims = FULL, variant: str = "A", device="cpu", base: int = 
     kv_rot_signs: int8 [layers][head_dim], each +1 or -1 with probability 1/2
     (the random signs of a rotated 4-bit K/V cache).
     head="bf16": the head slice is also given unquantised, head_bf16 = the
-    table's bf16 rows at the draft vocabulary (head_format "bf16").
+    table's bf16 rows at the draft vocabulary (head_format "bf16");
+    head="fp8": also as block-FP8 of those rows (head_fp8.q / .s).
     """
     assert variant in ("A", "B", "C")
     H, F, r, L = dims.hidden, dims.ffn, dims.rank, dims.layers
@@ -200,10 +201,12 @@ def make_model(dims: Dims = FULL, variant: str = "A", device="cpu", base: int = 
     # one random sign per head dimension and layer, for a rotated 4-bit cache
     signs = torch.randint(0, 2, (L, dims.head_dim), generator=_gen("cpu", base, "kv_rot_signs"))
     m["kv_rot_signs"] = (1 - 2 * signs).to(torch.int8).to(device)
-    assert head in ("nvfp4", "bf16")
+    assert head in ("nvfp4", "bf16", "fp8")
     m["head_format"] = head
     if head == "bf16":
         m["head_bf16"] = table[vocab.to(device).long()].contiguous()
+    if head == "fp8":
+        m["head_fp8.q"], m["head_fp8.s"] = quant_block_fp8(table[vocab.to(device).long()].float())
     return m
 
 

@@ -41,7 +41,8 @@ class Harness:
         t0 = time.time()
         self.variant = variant
         self.model = synth.make_model(synth.FULL, variant, device="cuda", head=head)
-        quant = {"nvfp4": kdraft.KD_QUANT_NVFP4, "bf16": kdraft.KD_QUANT_BF16}[head]
+        quant = {"nvfp4": kdraft.KD_QUANT_NVFP4, "bf16": kdraft.KD_QUANT_BF16,
+                 "fp8": kdraft.KD_QUANT_FP8_BLOCK64}[head]
         self.drafter = kdraft.Drafter(max_streams=max_streams, window=window, head_quant=quant)
         self.drafter.load_weights(self.model)
         self._oracle = None

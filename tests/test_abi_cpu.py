@@ -106,7 +106,7 @@ def test_ctypes_structs_match_the_c_header(tmp_path):
     checks = {
         "kd_kv": (kdraft.KdKV, ["k", "v", "stride_stream", "capacity", "format", "k_so", "v_so"]),
         "kd_weights": (kdraft.KdWeights, ["fuse", "mask_row", "layer", "final_norm", "head_g",
-                                          "embed_table", "kv_rot_signs", "head_bf16"]),
+                                          "embed_table", "kv_rot_signs", "head_bf16", "head_fp8"]),
         "kd_config": (kdraft.KdConfig, ["hidden", "max_streams", "rope_theta", "head_quant"]),
         "kd_copy_guard": (kdraft.KdCopyGuard, ["window", "min_accept", "proposed", "accepted"]),
     }

@@ -1,10 +1,12 @@
-"""GPU parity of the bf16 head slice (the model card "Kolibri-1 block
-drafter", section Use: the head slice can be bf16, FP8 or NVFP4; Serving: the
-NVFP4 head keeps the drafts at a quarter of the bf16 bytes).
+"""GPU parity of the bf16 and block-FP8 head slices (the model card
+"Kolibri-1 block drafter", section Use: the head slice can be bf16, FP8 or
+NVFP4; Serving: the NVFP4 head keeps the drafts at a quarter of the bf16
+bytes).
 
-A bf16 head runs the general path at every batch size: the tiled head kernel
-reads the repacked bf16 rows and splits each f16 activation exactly into two
-bf16 terms for the bf16 matrix cores. Acceptance as for every round: relative
+These heads run the general path at every batch size. For bf16 the tiled
+head kernel splits each f16 activation exactly into two bf16 terms for the
+bf16 matrix cores; for FP8 it decodes e4m3 exactly to f16 and scales each
+64-input block's product by its row's scale. Acceptance as for every round: relative
 L2 of the logits <= 1e-2 and ids equal wherever the oracle's top-1/top-2 gap
 exceeds 1e-2.
 """
@@ -24,10 +26,10 @@ pytestmark = pytest.mark.gpu
 C = synth.CONFIGS
 
 
-@pytest.fixture(scope="module")
-def hbC():
+@pytest.fixture(scope="module", params=["bf16", "fp8"])
+def hbC(request):
     require_gpu()
-    return Harness("C", max_streams=256, head="bf16")
+    return Harness("C", max_streams=256, head=request.param)
 
 
 def test_bf16_head_b4(hbC):

@@ -228,3 +228,16 @@ def test_bf16_head_is_the_full_head_gathered():
     Mq = oracle.OracleModel({k: v for k, v in mnp.items() if k != "head_format"})
     lq, _ = oracle.oracle_round(Mq, inp)
     assert 0 < np.abs(lq - logits).max() < 0.2 * np.abs(logits).max()
+
+
+def test_fp8_head_decodes_the_block_fp8_rows():
+    m = synth.make_model(D, "B", head="fp8")
+    mnp = synth.to_numpy_model(m)
+    M = oracle.OracleModel(mnp)
+    full = oracle.decode_bf16(mnp["table"])[mnp["vocab"]]
+    # block-FP8 keeps each value within half an e4m3 step of the bf16 row:
+    # 2^-4 relative for normals, half the subnormal step 2^-9 s below 2^-6 s
+    # (s the block's scale), so the head is the bf16 head up to that rounding
+    s = np.repeat(np.asarray(mnp["head_fp8.s"], dtype=np.float64), 64, axis=1)
+    assert np.all(np.abs(M.head - full) <= np.abs(full) * 2.0 ** -4 + s * 2.0 ** -10 + 1e-15)
+    assert not np.array_equal(M.head, full)
