@@ -40,6 +40,7 @@ class Harness:
                  head: str = "nvfp4"):
         t0 = time.time()
         self.variant = variant
+        self.head = head
         self.model = synth.make_model(synth.FULL, variant, device="cuda", head=head)
         quant = {"nvfp4": kdraft.KD_QUANT_NVFP4, "bf16": kdraft.KD_QUANT_BF16,
                  "fp8": kdraft.KD_QUANT_FP8_BLOCK64}[head]

@@ -37,27 +37,27 @@ def test_bf16_head_b4(hbC):
     lg, ids = hbC.run(inp)
     assert hbC.drafter.last_path() == 1
     ref, rid = oracle.oracle_round(hbC.oracle, synth.to_numpy_inputs(inp))
-    compare(lg, ids, ref, rid, hbC.oracle.vocab, "bf16 head B4")
+    compare(lg, ids, ref, rid, hbC.oracle.vocab, f"{hbC.head} head B4")
 
 
 def test_bf16_head_b1_and_edges(hbC):
     lens = [0, 1, 129, 2048, 6000]
-    cfg = dict(name="bf16 head edges", streams=len(lens), lens=("const", 0), model="C", ingest=0)
+    cfg = dict(name=f"{hbC.head} head edges", streams=len(lens), lens=("const", 0), model="C", ingest=0)
     inp = hbC.inputs(cfg, base=18, lens_override=lens)
     lg, ids = hbC.run(inp)
     ref, rid = oracle.oracle_round(hbC.oracle, synth.to_numpy_inputs(inp))
-    compare(lg, ids, ref, rid, hbC.oracle.vocab, "bf16 head edges")
+    compare(lg, ids, ref, rid, hbC.oracle.vocab, f"{hbC.head} head edges")
     one = hbC.inputs(C[0])
     lg, ids = hbC.run(one)
     ref, rid = oracle.oracle_round(hbC.oracle, synth.to_numpy_inputs(one))
-    compare(lg, ids, ref, rid, hbC.oracle.vocab, "bf16 head B1")
+    compare(lg, ids, ref, rid, hbC.oracle.vocab, f"{hbC.head} head B1")
 
 
 def test_bf16_head_b16_ragged(hbC):
     inp = hbC.inputs(C[2])
     lg, ids = hbC.run(inp)
     ref, rid = oracle.oracle_round(hbC.oracle, synth.to_numpy_inputs(inp))
-    compare(lg, ids, ref, rid, hbC.oracle.vocab, "bf16 head B16-ragged")
+    compare(lg, ids, ref, rid, hbC.oracle.vocab, f"{hbC.head} head B16-ragged")
 
 
 def test_bf16_head_b256_sampled(hbC):
@@ -65,12 +65,12 @@ def test_bf16_head_b256_sampled(hbC):
     lg, ids = hbC.run(inp)
     sample = [0, 5, 99, 200, 255]
     ref, rid = oracle.oracle_round(hbC.oracle, synth.to_numpy_inputs(inp, streams=sample))
-    compare(lg[sample], ids[sample], ref, rid, hbC.oracle.vocab, "bf16 head B256 (sampled)")
+    compare(lg[sample], ids[sample], ref, rid, hbC.oracle.vocab, f"{hbC.head} head B256 (sampled)")
     assert np.all(np.isin(ids, hbC.oracle.vocab))
 
 
 def test_bf16_head_with_a_4bit_cache_and_depth(hbC):
-    cfg = dict(name="bf16 head int4", streams=6, lens=("uniform", 10, 3000), model="C", ingest=0)
+    cfg = dict(name=f"{hbC.head} head int4", streams=6, lens=("uniform", 10, 3000), model="C", ingest=0)
     inp = hbC.inputs(cfg, base=19, kv="int4")
     B = inp["streams"]
     ids = torch.full((B, 4), -7, dtype=torch.int32, device="cuda")
