@@ -572,15 +572,21 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnK a) {
       ls += __shfl_xor(ls, 32, 64);
       l_run = l_run * alpha + ls;
       m_run = m_new;
+      // the outputs are rescaled only when some row's maximum grew
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int j = 0; j < BLK; ++j) {
+          const float aj = __shfl(alpha, j, 64);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[j][e] *= aj;
+        }
+      }
       // lane (g = lg, c = lr) gathers P[j][4g + t] from lane (j, g)
 #pragma unroll
       for (int j = 0; j < BLK; ++j) {
-        const float aj = __shfl(alpha, j, 64);
         float pj[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) pj[t] = __shfl(pe[t], (lg << 4) | j, 64);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[j][e] *= aj;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           float vf[8];
