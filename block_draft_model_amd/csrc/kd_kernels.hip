@@ -757,18 +757,26 @@ __global__ __launch_bounds__(256) void k_attn_split_q4(AttnK a) {
       return (uint32_t)(s_ - (s_ >= a.cap ? a.cap : 0)) * sl;
     };
     // keys past n are clamped to the last visible key and masked in the scores
-    auto load_blk = [&](int bi, u32x4& kr, uint32_t (&vr)[4], uint32_t (&ks)[4], uint32_t (&vs)[4]) {
-      kr = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, row_of(16 * bi + lr) * 64 + 16 * lg, 0, 0));
+    // lane (lr, lg) reads key lr's K codes (dims 32 lg ..) and its scale
+    // and offset pairs; the V codes of keys 4 lg + t (dims 8 lr ..)
+    auto load_blk = [&](int bi, u32x4& kr, uint32_t (&vr)[4], uint32_t& ks, uint32_t& vs) {
+      const uint32_t rk0 = row_of(16 * bi + lr);
+      kr = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, rk0 * 64 + 16 * lg, 0, 0));
+      ks = __builtin_amdgcn_raw_buffer_load_b32(rks, rk0 * 4, 0, 0);
+      vs = __builtin_amdgcn_raw_buffer_load_b32(rvs, rk0 * 4, 0, 0);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const uint32_t ro = row_of(16 * bi + 4 * lg + t);
-        vr[t] = __builtin_amdgcn_raw_buffer_load_b32(rv, ro * 64 + 4 * lr, 0, 0);
-        ks[t] = __builtin_amdgcn_raw_buffer_load_b32(rks, ro * 4, 0, 0);
-        vs[t] = __builtin_amdgcn_raw_buffer_load_b32(rvs, ro * 4, 0, 0);
-      }
+      for (int t = 0; t < 4; ++t)
+        vr[t] = __builtin_amdgcn_raw_buffer_load_b32(rv, row_of(16 * bi + 4 * lg + t) * 64 + 4 * lr, 0, 0);
     };
-    auto process = [&](int bi, const u32x4& kr, const uint32_t (&vr)[4], const uint32_t (&ks)[4],
-                       const uint32_t (&vs)[4]) __attribute__((always_inline)) {
+    auto process = [&](int bi, const u32x4& kr, const uint32_t (&vr)[4], uint32_t ks_l,
+                       uint32_t vs_l) __attribute__((always_inline)) {
+      // the scale and offset pairs of keys 4 lg + e come from lanes 4 lg + e
+      uint32_t ks[4], vs[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ks[e] = __shfl(ks_l, 4 * lg + e, 64);
+        vs[e] = __shfl(vs_l, 4 * lg + e, 64);
+      }
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
@@ -839,7 +847,7 @@ __global__ __launch_bounds__(256) void k_attn_split_q4(AttnK a) {
     const int last = blk1 - 1;
     int bi = blk0 + wave;
     u32x4 kA, kB;
-    uint32_t vA[4], vB[4], ksA[4], ksB[4], vsA[4], vsB[4];
+    uint32_t vA[4], vB[4], ksA, ksB, vsA, vsB;
     load_blk(min(bi, last), kA, vA, ksA, vsA);
     for (; bi <= last; bi += 8) {
       load_blk(min(bi + 4, last), kB, vB, ksB, vsB);
