@@ -14,6 +14,50 @@
 #include "kd_runtime.h"
 #include "kd_small.h"
 
+// Uploads argument blocks to device memory without waiting on the stream:
+// each upload copies from the next of NSTAGE pinned staging buffers, which is
+// reused only after the copy recorded on it has completed (normally long
+// before: NSTAGE uploads later).
+struct ArgStager {
+  static constexpr int NSTAGE = 8;
+  void* buf[NSTAGE] = {};
+  hipEvent_t ev[NSTAGE] = {};
+  bool pending[NSTAGE] = {};
+  int next = 0;
+  size_t bytes = 0;
+
+  bool init(size_t n) {
+    bytes = n;
+    for (int i = 0; i < NSTAGE; ++i) {
+      if (hipHostMalloc(&buf[i], n, hipHostMallocDefault) != hipSuccess) return false;
+      if (hipEventCreateWithFlags(&ev[i], hipEventDisableTiming) != hipSuccess) return false;
+    }
+    return true;
+  }
+  hipError_t upload(void* dev, const void* src, size_t n, hipStream_t st) {
+    if (n > bytes) return hipErrorInvalidValue;
+    const int i = next;
+    next = (next + 1) % NSTAGE;
+    if (pending[i]) {
+      const hipError_t e = hipEventSynchronize(ev[i]);
+      if (e != hipSuccess) return e;
+    }
+    memcpy(buf[i], src, n);
+    hipError_t e = hipMemcpyAsync(dev, buf[i], n, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipEventRecord(ev[i], st);
+    pending[i] = e == hipSuccess;
+    return e;
+  }
+  void destroy() {
+    for (int i = 0; i < NSTAGE; ++i) {
+      if (ev[i]) (void)hipEventDestroy(ev[i]);
+      if (buf[i]) (void)hipHostFree(buf[i]);
+      ev[i] = nullptr;
+      buf[i] = nullptr;
+    }
+  }
+};
+
 struct kd_ctx {
   kd_config cfg{};
   hipStream_t stream = nullptr;
@@ -35,30 +79,42 @@ struct kd_ctx {
   unsigned epoch = 0;        // grid barriers completed by persistent launches so far
   bool mega_ok = false;      // persistent cooperative kernel available
   int path = 0;              // 0 auto, 1 general, 2 small per-phase, 3 small persistent
-  // Device copies of the small-path arguments: slot 0 for a call's first
-  // round, slot 1 for the later rounds of kd_round_depth (predecessors from
-  // the previous round's ids).
-  kd::SmallArgs* args_dev[2] = {nullptr, nullptr};
+  // Device copies of the small-path arguments, one per kind of round so that
+  // a serving loop finds each block unchanged from call to call: slot 0 a
+  // call's only round, 1 the first of several (no logits), 2 a middle round
+  // and 3 the last round of kd_round_depth (predecessors from the previous
+  // round's ids).
+  static constexpr int NSLOT = 4;
+  kd::SmallArgs* args_dev[NSLOT] = {};
+  kd::SmallArgs args_cur[NSLOT];   // what each device slot holds once the queued uploads run
+  bool args_valid[NSLOT] = {};
+  ArgStager stager;
   // The per-phase launches of path 2 as one graph per slot: the kernels read
   // their arguments from args_dev[slot], so a graph depends only on the layer
   // count and the grid; it is captured on a private stream and launched on the
   // caller's.
   hipStream_t cap_stream = nullptr;
-  hipGraphExec_t phase_graph[2] = {nullptr, nullptr};
-  int phase_graph_nl[2] = {-1, -1};
-  kd::SmallArgs* args_host[2] = {nullptr, nullptr};  // pinned host copies last uploaded
-  bool args_valid[2] = {false, false};
+  hipGraphExec_t phase_graph[NSLOT] = {};
+  int phase_graph_nl[NSLOT] = {-1, -1, -1, -1};
+  // Host-mapped status word: a kernel sets it when one of its bounded waits
+  // timed out; the next call reports KD_ERR_HIP and clears it.
+  unsigned* status_host = nullptr;
+  unsigned* status_dev = nullptr;
   unsigned long long* trace = nullptr;  // caller's device buffer for stage timestamps
   int trace_phases = 0;
   // The general path's launches of a round (and of an ingest) as graphs: their
   // kernel arguments hold the caller's pointers, so each graph is kept with the
-  // arguments it was captured for and captured again when they change (a
-  // serving loop that reuses its buffers captures once).
+  // arguments it was captured for. Up to GRAPH_CACHE graphs per kind are kept
+  // (least recently used dropped first), so a serving loop that rotates among
+  // a few buffer sets captures each set once.
   struct CachedGraph {
     hipGraphExec_t exec = nullptr;
     std::vector<unsigned char> key;
+    unsigned long long used = 0;
   };
-  CachedGraph round_graph, ingest_graph;
+  static constexpr int GRAPH_CACHE = 8;
+  CachedGraph round_graph[GRAPH_CACHE], ingest_graph[GRAPH_CACHE];
+  unsigned long long graph_clock = 0;
 };
 
 namespace {
@@ -101,12 +157,25 @@ void key_add_kv(std::vector<unsigned char>& key, const kd::KV& k) {
   }
 }
 
-// Launches `enqueue`'s kernels on st as a graph: captured on the private
-// stream when key differs from the cached graph's, else replayed.
+void drop_graphs(kd_ctx::CachedGraph (&gs)[kd_ctx::GRAPH_CACHE]) {
+  for (auto& g : gs) drop_graph(g);
+}
+
+// Launches `enqueue`'s kernels on st as a graph: replayed from the cache when
+// a graph with this key is there, else captured on the private stream into the
+// least recently used entry.
 template <class F>
-kd_status launch_cached(kd_ctx* c, kd_ctx::CachedGraph& g, std::vector<unsigned char>&& key,
-                        hipStream_t st, F&& enqueue, const char* what) {
-  if (!g.exec || g.key != key) {
+kd_status launch_cached(kd_ctx* c, kd_ctx::CachedGraph (&cache)[kd_ctx::GRAPH_CACHE],
+                        std::vector<unsigned char>&& key, hipStream_t st, F&& enqueue, const char* what) {
+  kd_ctx::CachedGraph* hit = nullptr;
+  kd_ctx::CachedGraph* victim = &cache[0];
+  for (auto& e : cache) {
+    if (e.exec && e.key == key) hit = &e;
+    if (!e.exec || (victim->exec && e.used < victim->used)) victim = &e;
+  }
+  kd_ctx::CachedGraph& g = hit ? *hit : *victim;
+  g.used = ++c->graph_clock;
+  if (!hit) {
     drop_graph(g);
     hipError_t e = hipSuccess;
     if (!c->cap_stream) e = hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking);
@@ -434,12 +503,8 @@ kd_status kd_create(const kd_config* cfg, void* hip_stream, kd_ctx** out) {
   // (stream, head) per workgroup, so the grid must cover every pair
   c->small_ok = c->G >= kd::SB_MAX * kd::NH;
   if (ok && c->small_ok) {
-    ok = dev_alloc(c->work_allocs, &c->small_mem, kd::small_bytes(w.att_nch)) &&
-         dev_alloc(c->work_allocs, &c->args_dev[0], 1) && dev_alloc(c->work_allocs, &c->args_dev[1], 1) &&
-         hipHostMalloc((void**)&c->args_host[0], sizeof(kd::SmallArgs), hipHostMallocDefault) ==
-             hipSuccess &&
-         hipHostMalloc((void**)&c->args_host[1], sizeof(kd::SmallArgs), hipHostMallocDefault) ==
-             hipSuccess;
+    ok = dev_alloc(c->work_allocs, &c->small_mem, kd::small_bytes(w.att_nch));
+    for (int i = 0; i < kd_ctx::NSLOT; ++i) ok = ok && dev_alloc(c->work_allocs, &c->args_dev[i], 1);
     if (ok) {
       kd::small_carve(c->small_mem, w.att_nch, &c->small);
       ok = hipMemset(c->small.bar, 0, 20 * 32 * sizeof(unsigned)) == hipSuccess &&
@@ -449,10 +514,14 @@ kd_status kd_create(const kd_config* cfg, void* hip_stream, kd_ctx** out) {
            hipDeviceSynchronize() == hipSuccess;
     }
   }
+  ok = ok && c->stager.init(sizeof(kd::SmallArgs)) &&
+       hipHostMalloc((void**)&c->status_host, 64, hipHostMallocMapped | hipHostMallocCoherent) == hipSuccess &&
+       hipHostGetDevicePointer((void**)&c->status_dev, c->status_host, 0) == hipSuccess;
+  if (ok) *c->status_host = 0u;
   if (!ok) {
     free_all(c->work_allocs);
-    for (int i = 0; i < 2; ++i)
-      if (c->args_host[i]) (void)hipHostFree(c->args_host[i]);
+    c->stager.destroy();
+    if (c->status_host) (void)hipHostFree(c->status_host);
     delete c;
     return KD_ERR_OOM;
   }
@@ -471,15 +540,15 @@ kd_status kd_set_stream(kd_ctx* ctx, void* hip_stream) {
 void kd_destroy(kd_ctx* ctx) {
   if (!ctx) return;
   (void)hipStreamSynchronize(ctx->stream);
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kd_ctx::NSLOT; ++i)
     if (ctx->phase_graph[i]) (void)hipGraphExecDestroy(ctx->phase_graph[i]);
-  drop_graph(ctx->round_graph);
-  drop_graph(ctx->ingest_graph);
+  drop_graphs(ctx->round_graph);
+  drop_graphs(ctx->ingest_graph);
   if (ctx->cap_stream) (void)hipStreamDestroy(ctx->cap_stream);
   free_all(ctx->work_allocs);
   free_all(ctx->weight_allocs);
-  for (int i = 0; i < 2; ++i)
-    if (ctx->args_host[i]) (void)hipHostFree(ctx->args_host[i]);
+  ctx->stager.destroy();
+  if (ctx->status_host) (void)hipHostFree(ctx->status_host);
   delete ctx;
 }
 
@@ -504,6 +573,7 @@ kd_status kd_load_weights(kd_ctx* c, const kd_weights* wt) {
   free_all(c->weight_allocs);
   c->loaded = false;
   kd::DevWeights& d = c->d;
+  d.zrow = nullptr;
 
   kd_status st;
   {
@@ -663,9 +733,17 @@ kd_status kd_load_weights(kd_ctx* c, const kd_weights* wt) {
   d.hb = nullptr;
   }
   d.table = static_cast<const uint16_t*>(wt->embed_table);
-  c->args_valid[0] = c->args_valid[1] = false;
-  drop_graph(c->round_graph);
-  drop_graph(c->ingest_graph);
+  d.V = c->cfg.full_vocab;
+  if (!d.zrow) {
+    uint16_t* z;
+    if (!dev_alloc(c->weight_allocs, &z, (size_t)kd::H)) return fail(c, KD_ERR_OOM, "weight allocation failed");
+    const hipError_t e = hipMemset(z, 0, (size_t)kd::H * sizeof(uint16_t));
+    if (e != hipSuccess) return hip_fail(c, e, "zero row");
+    d.zrow = z;
+  }
+  for (int i = 0; i < kd_ctx::NSLOT; ++i) c->args_valid[i] = false;
+  drop_graphs(c->round_graph);
+  drop_graphs(c->ingest_graph);
   c->loaded = true;
   c->err.clear();
   return KD_OK;
@@ -673,10 +751,23 @@ kd_status kd_load_weights(kd_ctx* c, const kd_weights* wt) {
 
 // `depth` rounds; round r > 0 reads its predecessor ids from out_ids (the
 // previous round's drafts, 4 per stream).
+// A bounded device wait of an earlier call timed out (its rounds wrote -2 ids).
+static kd_status take_device_status(kd_ctx* c) {
+  if (c->status_host && __atomic_load_n(c->status_host, __ATOMIC_ACQUIRE) != 0u) {
+    __atomic_store_n(c->status_host, 0u, __ATOMIC_RELEASE);
+    return fail(c, KD_ERR_HIP, "a device wait of an earlier round timed out; that round wrote -2 ids");
+  }
+  return KD_OK;
+}
+
 static kd_status round_impl(kd_ctx* c, int depth, int B, const void* taps, const int32_t* anchor,
                             const int32_t* pred, const kd_kv* kv, const int32_t* lens,
                             int32_t* out_ids, float* out_logits) {
   if (!c->loaded) return fail(c, KD_ERR_STATE, "kd_round before kd_load_weights");
+  {
+    const kd_status ds = take_device_status(c);
+    if (ds != KD_OK) return ds;
+  }
   if (B < 1 || B > c->cfg.max_streams) return fail(c, KD_ERR_ARG, "streams out of range");
   if (!taps || !anchor || !pred || !lens || !out_ids)
     return fail(c, KD_ERR_ARG, "NULL device pointer");
@@ -703,7 +794,8 @@ static kd_status round_impl(kd_ctx* c, int depth, int B, const void* taps, const
   if (path != 1) {
     (void)hipGetLastError();
     for (int r = 0; r < depth; ++r) {
-      const int slot = r == 0 ? 0 : 1;
+      const bool first = r == 0, last = r + 1 == depth;
+      const int slot = first && last ? 0 : first ? 1 : last ? 3 : 2;
       kd::SmallArgs a;
       memset(&a, 0, sizeof a);
       a.B = B;
@@ -725,17 +817,16 @@ static kd_status round_impl(kd_ctx* c, int depth, int B, const void* taps, const
       a.out_logits = r + 1 == depth ? out_logits : nullptr;
       a.d = d;
       a.s = c->small;
+      a.status = c->status_dev;
       a.trace = c->trace;
       a.trace_phases = c->trace_phases;
       // upload the argument block only when it changed (a serving loop that
-      // reuses its buffers uploads it once)
-      if (!c->args_valid[slot] || memcmp(c->args_host[slot], &a, sizeof a) != 0) {
-        hipError_t e = hipStreamSynchronize(st);   // the pinned copy may still be in flight
-        if (e == hipSuccess) {
-          memcpy(c->args_host[slot], &a, sizeof a);
-          e = hipMemcpyAsync(c->args_dev[slot], c->args_host[slot], sizeof a, hipMemcpyHostToDevice, st);
-        }
+      // reuses its buffers uploads it once); the upload is queued on the
+      // stream ahead of the launches that read it
+      if (!c->args_valid[slot] || memcmp(&c->args_cur[slot], &a, sizeof a) != 0) {
+        const hipError_t e = c->stager.upload(c->args_dev[slot], &a, sizeof a, st);
         if (e != hipSuccess) return hip_fail(c, e, "argument upload");
+        c->args_cur[slot] = a;
         c->args_valid[slot] = true;
       }
       const int np = kd::small_phase_count(a.nl);
@@ -822,7 +913,7 @@ static kd_status round_impl(kd_ctx* c, int depth, int B, const void* taps, const
       }
       if (nl == 0) kd::launch_norm_rows(st, w.x, R, d.final_norm, eps, w.af_x);
       kd::launch_head(st, w, d, R, r + 1 == depth ? out_logits : nullptr);
-      kd::launch_finalize(st, w, d, R, out_ids);
+      kd::launch_finalize(st, w, d, R, out_ids, anchor, pred_r, pred_stride);
     }
   };
   std::vector<unsigned char> key;
@@ -862,6 +953,10 @@ kd_status kd_ingest(kd_ctx* c, int B, int n_new, const void* taps, const int32_t
                     const kd_kv* kv, int32_t* lens) {
   if (!c) return KD_ERR_ARG;
   if (!c->loaded) return fail(c, KD_ERR_STATE, "kd_ingest before kd_load_weights");
+  {
+    const kd_status ds = take_device_status(c);
+    if (ds != KD_OK) return ds;
+  }
   if (B < 1 || B > c->cfg.max_streams) return fail(c, KD_ERR_ARG, "streams out of range");
   if (n_new < 1 || n_new > KD_MAX_INGEST) return fail(c, KD_ERR_ARG, "n_new out of range");
   if (!taps || !next_ids || !lens) return fail(c, KD_ERR_ARG, "NULL device pointer");

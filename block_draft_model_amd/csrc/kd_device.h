@@ -61,6 +61,25 @@ __device__ __forceinline__ uint32_t pack_hi16(float e0, float e1) {
   return __builtin_amdgcn_perm(f2u(e1), f2u(e0), 0x07060302u);
 }
 
+// Embedding-table row of a token id, or the zero row when the id lies
+// outside [0, V): ids are caller data (or a previous round's drafts, which
+// may be the -1 / -2 sentinels) and are never used unchecked as an index.
+template <class T>
+__device__ __forceinline__ T* table_row(T* table, T* zrow, int id, int V, int H_) {
+  return (id >= 0 && id < V) ? table + (size_t)id * H_ : zrow;
+}
+// Block row j of stream b reads the anchor (through row 0) and the
+// predecessor ids of rows 1..j; its draft is valid only if all lie in [0, V).
+template <class P>
+__device__ __forceinline__ bool id_row_valid(P anchor, P pred, int pred_stride, int b, int j, int V) {
+  bool ok = anchor[b] >= 0 && anchor[b] < V;
+  for (int i = 0; i < j; ++i) {
+    const int p = pred[b * pred_stride + i];
+    ok = ok && p >= 0 && p < V;
+  }
+  return ok;
+}
+
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 

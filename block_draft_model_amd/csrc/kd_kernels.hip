@@ -143,7 +143,8 @@ void launch_prep(hipStream_t st, const Work& w, const DevWeights& d, int B, cons
 // [f ; E[pred_j]] for j = 0..2 (input of [A_p | B_p]).
 __global__ __launch_bounds__(320) void k_post_fuse(const float* part, int splits, int B, float* f,
                                                    uint16_t* af_fc, uint16_t* af_ab,
-                                                   const uint16_t* table, const int32_t* anchor,
+                                                   const uint16_t* table, const uint16_t* zrow,
+                                                   int V, const int32_t* anchor,
                                                    const int32_t* pred, int pred_stride) {
   const int b = blockIdx.x, c0 = threadIdx.x * 8;
   constexpr int KT = 2 * H / 32;
@@ -158,19 +159,20 @@ __global__ __launch_bounds__(320) void k_post_fuse(const float* part, int splits
 #pragma unroll
   for (int i = 0; i < 8; ++i) f[(size_t)b * H + c0 + i] = v[i];
   store_afrag8(af_fc, KT, b, c0, v);
-  const u32x4 ea = *reinterpret_cast<const u32x4*>(table + (size_t)anchor[b] * H + c0);
+  const u32x4 ea = *reinterpret_cast<const u32x4*>(table_row(table, zrow, anchor[b], V, H) + c0);
   store_afrag8_bf16(af_fc, KT, b, H + c0, ea);
   for (int j = 0; j < BLK - 1; ++j) {
     store_afrag8(af_ab, KT, b * 3 + j, c0, v);
-    const u32x4 ep = *reinterpret_cast<const u32x4*>(table + (size_t)pred[b * pred_stride + j] * H + c0);
+    const u32x4 ep =
+        *reinterpret_cast<const u32x4*>(table_row(table, zrow, pred[b * pred_stride + j], V, H) + c0);
     store_afrag8_bf16(af_ab, KT, b * 3 + j, H + c0, ep);
   }
 }
 
 void launch_post_fuse(hipStream_t st, const Work& w, const DevWeights& d, int B, int splits,
                       const int32_t* anchor, const int32_t* pred, int pred_stride) {
-  k_post_fuse<<<B, 320, 0, st>>>(w.part, splits, B, w.f, w.af_fc, w.af_ab, d.table, anchor, pred,
-                                 pred_stride);
+  k_post_fuse<<<B, 320, 0, st>>>(w.part, splits, B, w.f, w.af_fc, w.af_ab, d.table, d.zrow, d.V, anchor,
+                                 pred, pred_stride);
 }
 
 // afrag of silu(sum of partials) for a rank-256 hidden vector.
@@ -1159,15 +1161,19 @@ void launch_head(hipStream_t st, const Work& w, const DevWeights& d, int R, floa
 }
 
 __global__ void k_finalize(const unsigned long long* keys, const int32_t* vocab, int R,
-                           int32_t* out) {
+                           int32_t* out, const int32_t* anchor, const int32_t* pred,
+                           int pred_stride, int V) {
   const int r = blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= R) return;
   const unsigned long long k = keys[r];
-  out[r] = k ? vocab[0xffffffffu - (uint32_t)(k & 0xffffffffu)] : -1;
+  const bool ok = id_row_valid(anchor, pred, pred_stride, r / BLK, r % BLK, V);
+  out[r] = k && ok ? vocab[0xffffffffu - (uint32_t)(k & 0xffffffffu)] : -1;
 }
 
-void launch_finalize(hipStream_t st, const Work& w, const DevWeights& d, int R, int32_t* out_ids) {
-  k_finalize<<<(R + 255) / 256, 256, 0, st>>>(w.keys, d.vocab, R, out_ids);
+void launch_finalize(hipStream_t st, const Work& w, const DevWeights& d, int R, int32_t* out_ids,
+                     const int32_t* anchor, const int32_t* pred, int pred_stride) {
+  k_finalize<<<(R + 255) / 256, 256, 0, st>>>(w.keys, d.vocab, R, out_ids, anchor, pred, pred_stride,
+                                               d.V);
 }
 
 // ---------------------------------------------------------------------------
@@ -1189,6 +1195,7 @@ void launch_ingest_prep(hipStream_t st, const Work& w, int rows, const uint16_t*
 
 __global__ __launch_bounds__(320) void k_ingest_post_fuse(const float* part, int splits, int rows,
                                                           uint16_t* af_fc, const uint16_t* table,
+                                                          const uint16_t* zrow, int V,
                                                           const int32_t* next_ids) {
   const int r = blockIdx.x, c0 = threadIdx.x * 8;
   constexpr int KT = 2 * H / 32;
@@ -1201,13 +1208,13 @@ __global__ __launch_bounds__(320) void k_ingest_post_fuse(const float* part, int
     for (int i = 0; i < 8; ++i) v[i] += p[i];
   }
   store_afrag8(af_fc, KT, r, c0, v);
-  const u32x4 e = *reinterpret_cast<const u32x4*>(table + (size_t)next_ids[r] * H + c0);
+  const u32x4 e = *reinterpret_cast<const u32x4*>(table_row(table, zrow, next_ids[r], V, H) + c0);
   store_afrag8_bf16(af_fc, KT, r, H + c0, e);
 }
 
 void launch_ingest_post_fuse(hipStream_t st, const Work& w, const DevWeights& d, int rows,
                              int splits, const int32_t* next_ids) {
-  k_ingest_post_fuse<<<rows, 320, 0, st>>>(w.part, splits, rows, w.af_fc, d.table, next_ids);
+  k_ingest_post_fuse<<<rows, 320, 0, st>>>(w.part, splits, rows, w.af_fc, d.table, d.zrow, d.V, next_ids);
 }
 
 __global__ __launch_bounds__(320) void k_ingest_c(const float* part, int splits, int rows,

@@ -47,6 +47,8 @@ struct DevWeightsT {
   int VD = 0, VT = 0;                     // draft vocab rows, 16-row tiles
   P<const int32_t> vocab = nullptr;
   P<const uint16_t> table = nullptr;      // borrowed bf16 [full_vocab][H]
+  P<const uint16_t> zrow = nullptr;       // bf16 zeros [H]: read in place of an out-of-range id's row
+  int V = 0;                              // rows of the table (full vocabulary)
   P<const float> kv_signs = nullptr;      // [NL][DH] +-1 of the rotated 4-bit cache, or null
   int head_fmt = 0;                       // 0 NVFP4 (hq, hs, hg), 1 bf16 (hb), 2 FP8 (hf8)
   P<const uint16_t> hb = nullptr;         // bf16 head [VT][H/32][64 lanes][8]
@@ -130,7 +132,10 @@ void launch_resid_norm(hipStream_t st, const Work& w, int R, int splits, const f
                        float eps, uint16_t* af_out, int spine_rows);
 void launch_swiglu(hipStream_t st, const Work& w, int R, int splits);
 void launch_head(hipStream_t st, const Work& w, const DevWeights& d, int R, float* logits);
-void launch_finalize(hipStream_t st, const Work& w, const DevWeights& d, int R, int32_t* out_ids);
+// Writes out_ids; a row whose anchor or earlier predecessor ids lie outside
+// the table (see id_row_valid) gets -1.
+void launch_finalize(hipStream_t st, const Work& w, const DevWeights& d, int R, int32_t* out_ids,
+                     const int32_t* anchor, const int32_t* pred, int pred_stride);
 // ingest
 void launch_ingest_prep(hipStream_t st, const Work& w, int rows, const uint16_t* taps);
 void launch_ingest_post_fuse(hipStream_t st, const Work& w, const DevWeights& d, int rows,

@@ -68,6 +68,9 @@ struct SmallArgsT {
   P<float> out_logits;
   DevWeightsT<P> d;
   SmallBufsT<P> s;
+  // Host-visible status word (mapped pinned memory): set to 1 when a bounded
+  // wait of the round timed out.
+  P<unsigned> status;
   // Optional stage timestamps (100 MHz wall clock), [phase slot][G][8]; null = off.
   P<unsigned long long> trace;
   int trace_phases;

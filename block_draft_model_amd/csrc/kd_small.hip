@@ -322,15 +322,20 @@ struct ASrc {
   gptr<const int32_t> ids;
   int kb_off;           // weight block of column 0
   int R;
+  gptr<const uint16_t> zrow = nullptr;  // modes 3, 4: read for an id outside [0, V)
+  int V = 0;
 };
 
-__device__ __forceinline__ size_t a_row(const ASrc& A, int r) {
+// The lane's activation row: modes 3 and 4 take a table row by token id (the
+// zero row for an out-of-range id), the others a row of A.base.
+__device__ __forceinline__ gptr<const uint16_t> a_row_ptr(const ASrc& A, int r) {
+  auto base = static_cast<gptr<const uint16_t>>(A.base);
   switch (A.mode) {
-    case 1: return (size_t)(r / 3);
-    case 2: return (size_t)(4 * (r / 3) + r % 3);
-    case 3: return (size_t)A.ids[r];
-    case 4: return (size_t)A.ids[4 * (r / 3) + r % 3];
-    default: return (size_t)r;
+    case 1: return base + (size_t)(r / 3) * A.ld;
+    case 2: return base + (size_t)(4 * (r / 3) + r % 3) * A.ld;
+    case 3: return table_row(base, A.zrow, A.ids[r], A.V, A.ld);
+    case 4: return table_row(base, A.zrow, A.ids[4 * (r / 3) + r % 3], A.V, A.ld);
+    default: return base + (size_t)r * A.ld;
   }
 }
 
@@ -340,8 +345,7 @@ __device__ __forceinline__ void a_issue(const ASrc& A, int kb, u32x4 (&raw)[2]) 
   // rows past R repeat row R-1; they only feed output rows that are discarded
   const int lane = threadIdx.x & 63, r = min(lane & 15, A.R - 1);
   const int c0 = (kb - A.kb_off) * 64 + 8 * (lane >> 4);
-  const size_t row = a_row(A, r);
-  auto p = static_cast<gptr<const uint16_t>>(A.base) + row * A.ld + c0;
+  auto p = a_row_ptr(A, r) + c0;
   raw[0] = *reinterpret_cast<gptr<const u32x4>>(p);
   raw[1] = *reinterpret_cast<gptr<const u32x4>>(p + 32);
 }
@@ -500,6 +504,9 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_pre0(Args& a_, lds
   auto& s = a.s;
   auto& d = a.d;
   const int B = a.B, R = a.R;
+  // a new round: no bounded wait of it has timed out yet
+  if (wg == 0 && threadIdx.x == 0)
+    __hip_atomic_store(&s.bar[18 * 32], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // RoPE table for every block row: positions len + j, angles in fp64.
   if (wg == G - 1) {
     for (int t = threadIdx.x; t < R * (DH / 2); t += SMALL_WG) {
@@ -531,14 +538,14 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_pre0(Args& a_, lds
                                 });
     } else if (u < n_fuse + n_fce) {
       const int t = u - n_fuse;
-      const ASrc A{d.table, H, 3, a.anchor, 40, B};
+      const ASrc A{d.table, H, 3, a.anchor, 40, B, d.zrow, d.V};
       gemm_unit<1, 5, 8, true>(a, sy, false, d.fc, t, 1, 40, A, red, no_rms(),
                                [&](int, int m, int n, float v) {
                                  if (m < B) st_wt(&s.fce[m * H + t * 16 + n], v);
                                });
     } else {
       const int t = u - n_fuse - n_fce;
-      const ASrc A{d.table, H, a.pred_stride == 4 ? 4 : 3, a.pred, 40, 3 * B};
+      const ASrc A{d.table, H, a.pred_stride == 4 ? 4 : 3, a.pred, 40, 3 * B, d.zrow, d.V};
       gemm_unit<1, 5, 8, true>(a, sy, false, d.pred_ab, t, 1, 40, A, red, no_rms(),
                                [&](int, int m, int n, float v) {
                                  if (m < 3 * B) st_wt(&s.pb[m * RK + t * 16 + n], v);
@@ -1662,8 +1669,12 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_head(Args& a_, lds
 #pragma unroll
   for (int m = 16; m >= 1; m >>= 1) k = u64_max(k, shfl_xor_u64s(k, m));
   const bool failed = ld_rlx(&s.bar[18 * 32]) != 0u;
-  if (r < R && l32 == 0)
-    a.out_ids[r] = failed ? -2 : (k ? d.vocab[0xffffffffu - (uint32_t)(k & 0xffffffffu)] : -1);
+  if (failed && t == 0 && a.status)
+    __hip_atomic_store(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  if (r < R && l32 == 0) {
+    const bool ok = id_row_valid(a.anchor, a.pred, a.pred_stride, r / BLK, r % BLK, d.V);
+    a.out_ids[r] = failed ? -2 : (k && ok ? d.vocab[0xffffffffu - (uint32_t)(k & 0xffffffffu)] : -1);
+  }
 }
 
 // ---------------------------------------------------------------------------

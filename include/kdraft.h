@@ -25,12 +25,18 @@
  * Conventions (all entry points):
  *  - Device pointers are HIP device addresses the caller owns (for example
  *    torch tensors). Host pointers are only read during the call.
- *  - Calls enqueue work on the context's HIP stream and return; argument and
- *    state errors are reported synchronously and enqueue nothing. A fault on
- *    the device surfaces as KD_ERR_HIP on a later call.
+ *  - Calls enqueue work on the context's HIP stream and return without
+ *    waiting for the device (argument blocks are staged through pinned
+ *    buffers; graphs are cached per set of caller pointers, so a loop that
+ *    rotates among a few buffer sets captures each once). Argument and state
+ *    errors are reported synchronously and enqueue nothing. A fault on the
+ *    device surfaces as KD_ERR_HIP on a later call, and so does a bounded
+ *    device wait that timed out (the rounds that saw it wrote -2 ids).
  *  - A context is not thread-safe. kd_round / kd_ingest never allocate.
- *  - Ids and lengths on the device are not range-checked: ids must lie in
- *    [0, full_vocab), lengths must be >= 0.
+ *  - Token ids on the device are checked before they index the embedding
+ *    table: an id outside [0, full_vocab) reads a zero row, and every block
+ *    row whose anchor or earlier predecessor ids (rows 1..j for row j) are out
+ *    of range gets out_ids -1. Lengths must be >= 0.
  */
 #ifndef KDRAFT_H
 #define KDRAFT_H
@@ -175,10 +181,19 @@ typedef struct {
 kd_status kd_create(const kd_config* cfg, void* hip_stream, kd_ctx** out);
 
 /* Copies, validates and repacks the weights into device memory (synchronous).
- * May be called again to replace them. */
+ * May be called again to replace them. The roles follow the model card
+ * "Kolibri-1 block drafter", section Architecture (Input, Positions 2-4,
+ * Predecessor head, Spine, Body, Output) and its Serving paragraph for the
+ * formats: block-FP8 body matrices and the NVFP4 head slice are quantised
+ * outside the library (the card's section Files: FP8 and NVFP4 are made at
+ * load time), so the library decodes exactly the codes it is given.
+ * Errors: KD_ERR_ARG for NULL or invalid data (NaN codes, non-finite scales,
+ * vocabulary ids out of range), KD_ERR_OOM, KD_ERR_HIP. */
 kd_status kd_load_weights(kd_ctx* ctx, const kd_weights* w);
 
-/* One round for `streams` streams (1 <= streams <= max_streams).
+/* One round for `streams` streams (1 <= streams <= max_streams): the model
+ * card "Kolibri-1 block drafter", section Architecture (Input through
+ * Output), with every stream in one batched pass (its Serving paragraph).
  *   tapped_states [streams][taps][hidden] bf16 (order: layers 44, 47, 49)
  *   anchor_ids    [streams]     int32, target-vocabulary ids (row 0's token)
  *   pred_ids      [streams][3]  int32, pred_ids[b][j-1] is the token before
@@ -186,7 +201,10 @@ kd_status kd_load_weights(kd_ctx* ctx, const kd_weights* w);
  *   ctx_kv        the K/V cache (struct on the host, tensors on the device)
  *   ctx_lens      [streams] int32, tokens seen; block row j is at position len + j
  *   out_ids       [streams][4] int32: target-vocabulary id of each row's
- *                 argmax (lowest draft index on ties; -1 if no logit is finite)
+ *                 argmax (lowest draft index on ties); -1 if no logit is
+ *                 finite or an id the row reads is out of range; -2 for
+ *                 every row of a round whose bounded device wait timed out
+ *                 (the next call then returns KD_ERR_HIP)
  *   out_logits    [streams][4][draft_vocab] fp32 in draft-vocabulary order, or NULL
  * All arrays are device pointers except ctx_kv itself. */
 kd_status kd_round(kd_ctx* ctx, int streams, const void* tapped_states,
@@ -208,7 +226,10 @@ kd_status kd_round_depth(kd_ctx* ctx, int depth, int streams, const void* tapped
                          const kd_kv* ctx_kv, const int32_t* ctx_lens,
                          int32_t* out_ids, float* out_logits);
 
-/* Appends n_new context rows per stream (1 <= n_new <= KD_MAX_INGEST): row i
+/* Appends n_new context rows per stream (1 <= n_new <= KD_MAX_INGEST), the
+ * context-row form of the model card's Architecture section (Input: fused
+ * state and next-token embedding, 5120 -> 2560; Body: each layer's K/V of a
+ * context row, RoPE at its position): row i
  * of stream b is [fuse(taps[b][i]) ; embed(next_ids[b][i])] -> fc, projected
  * through each layer's attention RMSNorm and W_k / W_v, K rotated at position
  * len + i, both rounded to bf16 (or, for KD_KV_INT4_ROT, K turned by R and

@@ -277,6 +277,21 @@ def test_round_parity_b256_sampled(hA):
     assert np.all(ids >= 0) and np.all(np.isin(ids, hA.oracle.vocab))
 
 
+def test_round_parity_b100_partial_row_block(hA):
+    """100 streams = 400 block rows: the projections take the widest tiled
+    kernel (more than 256 rows), whose last 64-row block is a quarter full
+    (rows 384..399 = streams 96..99). Sampled streams in the first and the
+    partial block."""
+    cfg = dict(name="B100", streams=100, lens=("uniform", 512, 2048), model="A", ingest=0)
+    inp = hA.inputs(cfg, base=53)
+    lg, ids = hA.run(inp)
+    assert hA.drafter.last_path() == 1
+    sample = [0, 37, 95, 96, 97, 99]
+    ref, rid = oracle.oracle_round(hA.oracle, synth.to_numpy_inputs(inp, streams=sample))
+    compare(lg[sample], ids[sample], ref, rid, hA.oracle.vocab, "B100 (sampled, partial row block)")
+    assert np.all(np.isin(ids, hA.oracle.vocab))
+
+
 @pytest.mark.parametrize("path", PATHS)
 def test_deterministic_and_logits_optional(hC, path):
     cfg = dict(name="det", streams=3, lens=("uniform", 100, 2500), model="C", ingest=0)

@@ -130,3 +130,29 @@ def test_attention_closed_forms():
     kb2 = rng.standard_normal((rows, heads, d)) * 0.01
     o2 = oracle.attention(q2, kc2, vc, kb2, vb)
     assert np.allclose(o2, np.broadcast_to(vc[:, 2], (rows, heads, d)), atol=1e-9)
+
+
+def test_top2_gap_hand_worked_rows():
+    """The gap that decides which rows the id rule gates (the card's Output
+    bullet: the draft is the argmax of the restricted logits). Hand-worked
+    rows: the top two of each row by hand, non-finite logits ignored."""
+    rows = np.array([
+        [1.0, 3.0, 2.5, -7.0],                     # top 3.0, second 2.5
+        [2.0, 2.0, 1.0, 0.0],                      # exact tie at the top
+        [np.nan, 1.0, 0.25, 0.5],                  # NaN never counts
+        [-np.inf, 5.0, -np.inf, -np.inf],          # one finite logit: nothing competes
+        [-3.0, -1.0, -2.0, -1.5],                  # all negative: -1 vs -1.5
+        [np.inf, 1.0, 0.0, -1.0],                  # +inf is not a finite logit
+        [0.0, -0.5, 0.0625, 0.0],                  # the top one is not first
+    ])
+    want = np.array([0.5, 0.0, 0.5, np.inf, 0.5, 1.0, 0.0625])
+    got = oracle.top2_gap(rows)
+    assert got.shape == (7,)
+    assert np.array_equal(got, want)
+    # no finite logit at all: no gap (NaN), so such a row is never gated
+    assert np.isnan(oracle.top2_gap(np.array([[np.nan, -np.inf, np.inf]])))[0]
+    # works on the last axis of any batch shape
+    batch = rows.reshape(7, 1, 4).repeat(3, axis=1)
+    assert np.array_equal(oracle.top2_gap(batch), np.repeat(want[:, None], 3, axis=1))
+    # the gate the GPU tests apply: gap > 1e-2
+    assert (oracle.top2_gap(rows) > 1e-2).tolist() == [True, False, True, True, True, True, True]
