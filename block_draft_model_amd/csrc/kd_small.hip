@@ -903,29 +903,27 @@ __device__ __attribute__((noinline, not_tail_called)) void attn_merge(Args& a_, 
   }
   auto seg_chunk = [&](int k) { return one_each ? k : max(((w0 + k) * U) / G, u0) - u0; };
   const int j = threadIdx.x >> 7, dd = threadIdx.x & 127;
+  const int lane = threadIdx.x & 63;
   constexpr int MAXS = 16;
   float pm[MAXS], pl[MAXS], po[MAXS];
   const size_t base = (size_t)(b * NH + h) * nch;
   auto am = s.am[l] + base * 4 + j;
   auto al = s.al[l] + base * 4 + j;
   auto ao = s.ao[l] + (base * 4 + j) * DH + dd;
-  // every load issued together: segments past the last one re-read it and
-  // are masked afterwards
+  // lane k < nseg loads segment k's max and sum of row j (every lane of a
+  // wave has the same row), each thread its segments' outputs: one load
+  // instruction per segment instead of three
   const int klast = max(nseg - 1, 0);
+  const int ck = seg_chunk(min(lane, klast));
+  const float m_lane = am[ck * 4], l_lane = al[ck * 4];
+#pragma unroll
+  for (int k = 0; k < MAXS; ++k) po[k] = k < nseg ? ao[(size_t)seg_chunk(k) * 4 * DH] : 0.f;
 #pragma unroll
   for (int k = 0; k < MAXS; ++k) {
-    const int cc = seg_chunk(min(k, klast));
-    pm[k] = am[cc * 4];
-    pl[k] = al[cc * 4];
-    po[k] = ao[(size_t)cc * 4 * DH];
+    pm[k] = k < nseg ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_lane), k))
+                     : -__builtin_inff();
+    pl[k] = k < nseg ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l_lane), k)) : 0.f;
   }
-#pragma unroll
-  for (int k = 0; k < MAXS; ++k)
-    if (k >= nseg) {
-      pm[k] = -__builtin_inff();
-      pl[k] = 0.f;
-      po[k] = 0.f;
-    }
   for (int k = MAXS; k < nseg; ++k) {  // more segments than registers: fold the rest in
     const int cc = seg_chunk(k);
     const float m1 = am[cc * 4];
@@ -1663,9 +1661,16 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_head(Args& a_, lds
   lds_sync();
   if (!*s_flag) return;
   const int t = threadIdx.x, r = t >> 5, l32 = t & 31;
+  // every candidate load is issued before the first is needed
+  unsigned long long kc[MAX_G / 32];
+#pragma unroll
+  for (int i = 0; i < MAX_G / 32; ++i) {
+    const int gi = l32 + 32 * i;
+    kc[i] = r < R && gi < G ? s.cand[gi * SR_MAX + r] : 0ull;
+  }
   unsigned long long k = 0ull;
-  if (r < R)
-    for (int gi = l32; gi < G; gi += 32) k = u64_max(k, s.cand[gi * SR_MAX + r]);
+#pragma unroll
+  for (int i = 0; i < MAX_G / 32; ++i) k = u64_max(k, kc[i]);
 #pragma unroll
   for (int m = 16; m >= 1; m >>= 1) k = u64_max(k, shfl_xor_u64s(k, m));
   const bool failed = ld_rlx(&s.bar[18 * 32]) != 0u;
