@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <type_traits>
 #include <vector>
@@ -1017,6 +1018,48 @@ kd_status kd_copy_draft(kd_ctx* c, int B, const int32_t* tokens, long long strid
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(c, e, "kd_copy_draft launch");
   return KD_OK;
+}
+
+// The per-stream match keys of kd_copy_draft_noalloc (two per stream): one
+// fixed array on every GPU the library runs on. Host code never uses this
+// name as an address; it uses the device address looked up per device below.
+static __device__ __align__(256) unsigned long long scratch[2 * KD_COPY_NOALLOC_MAX_STREAMS];
+
+static constexpr int KD_SCRATCH_DEVICES = 64;
+static std::mutex g_scratch_mu;
+static unsigned long long* g_scratch_ptr[KD_SCRATCH_DEVICES] = {};   // address of `scratch` per device
+
+// The device address of `scratch` on the current device, looked up on the
+// first call there (with that device current).
+static kd_status scratch_on_current_device(unsigned long long** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return KD_ERR_HIP;
+  if (dev < 0 || dev >= KD_SCRATCH_DEVICES) return KD_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KD_ERR_HIP;
+    g_scratch_ptr[dev] = static_cast<unsigned long long*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return KD_OK;
+}
+
+kd_status kd_copy_draft_noalloc(void* stream, int B, const int32_t* tokens, long long stride,
+                                const int32_t* lens, const int32_t* corpus, long long corpus_len, int K,
+                                int32_t* out_ids, int32_t* out_info) {
+  if (B < 1 || B > KD_COPY_NOALLOC_MAX_STREAMS) return KD_ERR_ARG;
+  if (K < 1 || K > KD_MAX_COPY) return KD_ERR_ARG;
+  if (stride < 0 || stride >= (1ll << 31) || corpus_len < 0 || corpus_len >= (1ll << 31)) return KD_ERR_ARG;
+  if ((stride > 0 && !tokens) || !lens || !out_ids || !out_info || (corpus_len > 0 && !corpus))
+    return KD_ERR_ARG;
+  unsigned long long* keys = nullptr;
+  const kd_status s = scratch_on_current_device(&keys);
+  if (s != KD_OK) return s;
+  (void)hipGetLastError();
+  kd::launch_copy_draft(static_cast<hipStream_t>(stream), B, tokens, stride, lens,
+                        corpus_len > 0 ? corpus : nullptr, corpus_len, K, keys, out_ids, out_info);
+  return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_HIP;
 }
 
 void kd_copy_guard_init(kd_copy_guard* g, int window, float min_accept, int pause) {

@@ -61,7 +61,7 @@ EXPORTS = ["kd_default_config", "kd_create", "kd_load_weights", "kd_round", "kd_
            "kd_set_stream", "kd_destroy", "kd_status_string", "kd_last_error",
            "kd_probe_decode_e4m3", "kd_probe_decode_e4m3_f16", "kd_probe_decode_nvfp4", "kd_debug_set_layers",
            "kd_debug_buffers", "kd_debug_set_path", "kd_debug_last_path",
-           "kd_debug_set_trace"]
+           "kd_debug_set_trace", "kd_copy_draft_noalloc"]
 
 KD_MAX_COPY = 48
 KD_GUARD_MAX_WINDOW = 64
@@ -114,6 +114,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kd_copy_draft.argtypes = [c_void_p, c_int, c_void_p, ctypes.c_longlong, c_void_p, c_void_p,
                                   ctypes.c_longlong, c_int, c_void_p, c_void_p]
     lib.kd_copy_draft.restype = c_int
+    lib.kd_copy_draft_noalloc.argtypes = [c_void_p, c_int, c_void_p, ctypes.c_longlong, c_void_p, c_void_p,
+                                          ctypes.c_longlong, c_int, c_void_p, c_void_p]
+    lib.kd_copy_draft_noalloc.restype = c_int
     lib.kd_copy_guard_init.argtypes = [P(KdCopyGuard), c_int, c_float, c_int]
     lib.kd_copy_guard_init.restype = None
     lib.kd_copy_guard_armed.argtypes = [P(KdCopyGuard)]
@@ -177,6 +180,19 @@ def _stream_handle(stream):
         import torch
         return torch.cuda.current_stream().cuda_stream
     return getattr(stream, "cuda_stream", stream)
+
+
+KD_COPY_NOALLOC_MAX_STREAMS = 1024
+
+
+def copy_draft_noalloc(streams, tokens, stride, lens, corpus, corpus_len, K, out_ids, out_info,
+                       stream=None) -> int:
+    """kd_copy_draft_noalloc on `stream` (default: torch's current stream);
+    returns the kd_status code (no context, so no message)."""
+    lib = load_library()
+    return int(lib.kd_copy_draft_noalloc(_stream_handle(stream), int(streams), _ptr(tokens), int(stride),
+                                         _ptr(lens), _ptr(corpus), int(corpus_len), int(K), _ptr(out_ids),
+                                         _ptr(out_info)))
 
 
 def kv_struct(k_layers, v_layers) -> KdKV:

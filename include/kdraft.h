@@ -264,6 +264,23 @@ kd_status kd_copy_draft(kd_ctx* ctx, int streams, const int32_t* tokens, long lo
                         const int32_t* lens, const int32_t* corpus, long long corpus_len, int K,
                         int32_t* out_ids, int32_t* out_info);
 
+/* kd_copy_draft without a context, for callers that cannot allocate device
+ * memory (code under HIP graph capture, serving loops that forbid hipMalloc):
+ * it allocates nothing. Arguments and results are kd_copy_draft's; `stream`
+ * is a hipStream_t (NULL: the null stream) of the current device. The
+ * per-stream match keys live in a fixed device array of
+ * KD_COPY_NOALLOC_MAX_STREAMS entries, one array per GPU, held until the
+ * process ends and shared by every call on that GPU: calls that overlap on one
+ * GPU race (serialize them, e.g. on one stream). Each call clears the keys it
+ * uses before its scans. Errors: KD_ERR_ARG for streams outside
+ * 1..KD_COPY_NOALLOC_MAX_STREAMS and the argument errors of kd_copy_draft;
+ * KD_ERR_HIP if the array's device address cannot be found or a launch fails;
+ * KD_ERR_UNSUPPORTED on a device index of 64 or more. */
+#define KD_COPY_NOALLOC_MAX_STREAMS 1024
+kd_status kd_copy_draft_noalloc(void* stream, int streams, const int32_t* tokens, long long stride,
+                                const int32_t* lens, const int32_t* corpus, long long corpus_len,
+                                int K, int32_t* out_ids, int32_t* out_info);
+
 /* The copy source's pause guard (frozen-corpus drafting article: when fewer
  * than min_accept of the tokens proposed over the last `window` proposals were
  * accepted, the source pauses for `pause` decoded tokens, then re-arms with an
