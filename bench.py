@@ -98,10 +98,18 @@ def measured_traffic(workload, kernel):
     return None
 
 
-def cpu_baseline(model, inp, max_seconds=20.0, max_rounds=8):
+GAP_MIN = 1e-2        # rows whose top-2 logit gap is at most this may pick either id
+REL_L2_MAX = 1e-2     # per-row relative L2 bound of the logits
+
+
+def cpu_baseline(model, inp, gpu_logits=None, gpu_ids=None, max_seconds=20.0, max_rounds=8):
     """The oracle, as it stands, on this host: rounds of the same workload
     until about max_seconds have passed. Weight decoding to fp64 is timed as a
-    separate one-off load step."""
+    separate one-off load step. With the GPU's logits and ids of the same
+    inputs, also the parity of that round against the oracle's first round:
+    per-row relative L2 of the logits, and the ids on every row whose top-2
+    gap exceeds GAP_MIN."""
+    import numpy as np
     import oracle
     import synth
     try:
@@ -114,11 +122,13 @@ def cpu_baseline(model, inp, max_seconds=20.0, max_rounds=8):
     load_s = time.perf_counter() - t0
     inp_np = synth.to_numpy_inputs(inp)
     times = []
+    first = None
     t_start = time.perf_counter()
     while len(times) < max_rounds and (time.perf_counter() - t_start) < max_seconds:
         t1 = time.perf_counter()
-        oracle.oracle_round(M, inp_np)
+        out = oracle.oracle_round(M, inp_np)
         times.append(time.perf_counter() - t1)
+        first = out if first is None else first
     per_round = sum(times) / len(times)
     cpu = platform.processor() or ""
     try:
@@ -129,10 +139,75 @@ def cpu_baseline(model, inp, max_seconds=20.0, max_rounds=8):
                     break
     except OSError:
         pass
-    return {"value": 1.0 / per_round, "unit": "rounds/s", "cores": threads, "kind": "oracle",
+    base = {"value": 1.0 / per_round, "unit": "rounds/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(times)} full rounds of the same workload in fp64 NumPy "
                       f"({per_round:.2f} s/round); weight decode to fp64 {load_s:.1f} s "
                       f"as a separate load step; host CPU: {cpu}"}
+    parity = None
+    if gpu_logits is not None:
+        ref_logits, ref_ids = first
+        g = np.asarray(gpu_logits, dtype=np.float64).reshape(-1, ref_logits.shape[-1])
+        r = np.asarray(ref_logits).reshape(g.shape)
+        rel = np.linalg.norm(g - r, axis=1) / np.linalg.norm(r, axis=1)
+        top2 = -np.sort(-r, axis=1)[:, :2]
+        gated = (top2[:, 0] - top2[:, 1]) > GAP_MIN
+        differ = np.asarray(gpu_ids).reshape(-1) != np.asarray(ref_ids).reshape(-1)
+        parity = {"rows": int(len(rel)), "max_rel_l2": float(rel.max()), "rel_l2_bound": REL_L2_MAX,
+                  "gated_rows": int(gated.sum()), "mismatches": int(np.sum(differ & gated)),
+                  "exempt_near_tie_rows": int(np.sum(~gated)),
+                  "exempt_rows_differing": int(np.sum(differ & ~gated)),
+                  "finite": bool(np.all(np.isfinite(g)))}
+    return base, parity
+
+
+def run_workload(kdraft, synth, torch, drafter, model, cfg, steps, warmup, kv_fmt, head, keep=False):
+    """Times `steps` rounds of one workload after `warmup`: HIP events around
+    the whole timed region (ms per step) and around each step (p10/p50/p90).
+    keep: also return the inputs, for a parity round outside the timed region."""
+    dims = synth.FULL
+    inp = synth.make_inputs(cfg, dims, device="cuda", vocab=model["vocab"], kv=kv_fmt)
+    B = inp["streams"]
+    stream = torch.cuda.current_stream()
+    if kv_fmt == "int4":
+        kv = kdraft.kv_struct_int4(inp["k"], inp["v"], inp["k_so"], inp["v_so"])
+    else:
+        kv = kdraft.kv_struct(inp["k"], inp["v"])
+    ids = torch.empty(B, 4, dtype=torch.int32, device="cuda")
+    n_ingest = cfg.get("ingest", 0)
+    # the lengths the timed rounds see (an ingesting step appends its rows
+    # first; the window keeps the visible rows at min(len, 2048) as they grow)
+    lens_host = [l + n_ingest for l in inp["lens"].cpu().tolist()]
+
+    def step():
+        if n_ingest:
+            drafter.ingest(B, n_ingest, inp["ingest_taps"], inp["ingest_ids"], kv, inp["lens"])
+        drafter.round(B, inp["taps"], inp["anchor"], inp["pred"], kv, inp["lens"], ids, None)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(steps):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev[0].elapsed_time(ev[-1]) / steps
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    q = lambda f: per[min(len(per) - 1, int(f * len(per)))]
+    res = dict(B=B, ms=ms, p10=q(0.1), p50=q(0.5), p90=q(0.9), wall=wall, lens=lens_host,
+               ingest=n_ingest, path=drafter.last_path())
+    if keep:
+        res["inp"], res["kv"] = inp, kv
+    else:
+        del inp, kv
+    return res
+
+
+PATH_NAME = {1: "general multi-kernel", 2: "small-batch phases, one launch each",
+             3: "small-batch persistent kernel"}
 
 
 def main():
@@ -140,7 +215,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--config", type=int, default=None,
+                    help="time only this workload (index into the five); default: the 4-stream "
+                         "workload as the headline, then every workload in the configs list")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB 5 times and "
@@ -160,6 +237,7 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    import numpy as np
     import torch
 
     import synth
@@ -178,47 +256,29 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
         return
-    cfg = synth.CONFIGS[args.config]
     dims = synth.FULL
-    model = synth.make_model(dims, cfg["model"], device="cuda", head=args.head)
-    inp = synth.make_inputs(cfg, dims, device="cuda", vocab=model["vocab"], kv=args.kv)
-    B = inp["streams"]
+    head_q = {"nvfp4": kdraft.KD_QUANT_NVFP4, "bf16": kdraft.KD_QUANT_BF16,
+              "fp8": kdraft.KD_QUANT_FP8_BLOCK64}[args.head]
     stream = torch.cuda.current_stream()
-    drafter = kdraft.Drafter(max_streams=B, stream=stream,
-                             head_quant={"nvfp4": kdraft.KD_QUANT_NVFP4, "bf16": kdraft.KD_QUANT_BF16,
-                                         "fp8": kdraft.KD_QUANT_FP8_BLOCK64}[args.head])
-    drafter.load_weights(model)
-    drafter.debug_set_path(args.path)
-    if args.kv == "int4":
-        kv = kdraft.kv_struct_int4(inp["k"], inp["v"], inp["k_so"], inp["v_so"])
-    else:
-        kv = kdraft.kv_struct(inp["k"], inp["v"])
-    ids = torch.empty(B, 4, dtype=torch.int32, device="cuda")
-    n_ingest = cfg.get("ingest", 0)
-    # the lengths the timed rounds see (an ingesting step appends its rows
-    # first; the window keeps the visible rows at min(len, 2048) as they grow)
-    lens_host = [l + n_ingest for l in inp["lens"].cpu().tolist()]
+    models, drafters = {}, {}
 
-    def step():
-        if n_ingest:
-            drafter.ingest(B, n_ingest, inp["ingest_taps"], inp["ingest_ids"], kv, inp["lens"])
-        drafter.round(B, inp["taps"], inp["anchor"], inp["pred"], kv, inp["lens"], ids, None)
+    def drafter_for(name):
+        if name not in drafters:
+            models[name] = synth.make_model(dims, name, device="cuda", head=args.head)
+            d = kdraft.Drafter(max_streams=max(c["streams"] for c in synth.CONFIGS), stream=stream,
+                               head_quant=head_q)
+            d.load_weights(models[name])
+            d.debug_set_path(args.path)
+            drafters[name] = d
+        return drafters[name], models[name]
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = start.elapsed_time(end) / args.steps
-
-    path = drafter.last_path()
-    ab = algorithmic_bytes(dims, lens_host, B, n_ingest, args.kv, args.head)
+    head_i = 1 if args.config is None else args.config
+    cfg = synth.CONFIGS[head_i]
+    drafter, model = drafter_for(cfg["model"])
+    r = run_workload(kdraft, synth, torch, drafter, model, cfg, args.steps, args.warmup, args.kv, args.head,
+                     keep=not args.no_cpu_baseline)
+    B, ms, path = r["B"], r["ms"], r["path"]
+    ab = algorithmic_bytes(dims, r["lens"], B, r["ingest"], args.kv, args.head)
     rounds_s = 1000.0 / ms
     # roofline of the round's kernel: algorithmic bytes per launch over the
     # average launch duration (the HIP-event time of the timed rounds on the
@@ -234,6 +294,7 @@ def main():
                 "kernel": KERNEL_NAME.get(path, "several kernels per round"),
                 "launches_per_round": launches, "bytes_per_launch": round(per_launch),
                 "avg_launch_us": round(launch_us, 3)}
+    n_ingest = r["ingest"]
     out = {"metric": METRIC, "value": round(rounds_s, 2), "unit": "rounds/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -244,19 +305,60 @@ def main():
            "config": {"workload": f"{cfg['name']}: {B} streams x 1 round"
                                   + (f" after ingesting {n_ingest} context rows per stream" if n_ingest else "")
                                   + ", draft block 4, "
-                                  f"context rows per stream {sorted(set(min(l, 2048) for l in lens_host))}, "
+                                  f"context rows per stream {sorted(set(min(l, 2048) for l in r['lens']))}, "
                                   f"block-FP8 body, {dict(nvfp4='NVFP4', bf16='bf16', fp8='block-FP8')[args.head]} head (60,614 rows)"
                                   + (", rotated 4-bit K/V cache" if args.kv == "int4" else ""),
                       "streams": B, "draft_tokens_per_round": 4 * B, "kv_cache": args.kv, "head": args.head,
-                      "path": {1: "general multi-kernel", 2: "small-batch phases, one launch each",
-                               3: "small-batch persistent kernel"}[path]},
+                      "path": PATH_NAME[path]},
            "draft_tokens_per_s": round(4 * B * rounds_s, 1),
            "bytes_per_round": ab, "hbm_roofline_frac": round(achieved / HBM_PEAK_GBS, 4),
-           "wall_s": round(wall, 3), "roofline": roofline}
+           "wall_s": round(r["wall"], 3), "roofline": roofline}
+
+    # the parity round of the headline workload (outside the timed region)
+    gpu_logits = gpu_ids = None
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(model, inp)
+        inp, kv = r["inp"], r["kv"]
+        lg = torch.empty(B, 4, dims.draft_vocab, dtype=torch.float32, device="cuda")
+        ids = torch.empty(B, 4, dtype=torch.int32, device="cuda")
+        drafter.round(B, inp["taps"], inp["anchor"], inp["pred"], kv, inp["lens"], ids, lg)
+        torch.cuda.synchronize()
+        gpu_logits, gpu_ids = lg.cpu().numpy(), ids.cpu().numpy()
+        del lg
+    head_inp = r.pop("inp", None)
+    r.pop("kv", None)
+
+    # every workload: median and spread of the round time, throughput, roofline
+    if args.config is None:
+        rows = []
+        for i, c in enumerate(synth.CONFIGS):
+            if i == head_i:
+                rr = r
+            else:
+                d, m = drafter_for(c["model"])
+                big = c["streams"] >= 64
+                rr = run_workload(kdraft, synth, torch, d, m, c, min(args.steps, 30) if big else args.steps,
+                                  min(args.warmup, 5) if big else args.warmup, args.kv, args.head)
+                torch.cuda.empty_cache()
+            b = algorithmic_bytes(dims, rr["lens"], rr["B"], rr["ingest"], args.kv, args.head)["total"]
+            rows.append({"workload": c["name"], "streams": rr["B"],
+                         "ingest_rows_per_stream": rr["ingest"],
+                         "steps": args.steps if i == head_i or rr["B"] < 64 else min(args.steps, 30),
+                         "ms_p10": round(rr["p10"], 4), "ms_p50": round(rr["p50"], 4),
+                         "ms_p90": round(rr["p90"], 4), "ms_mean": round(rr["ms"], 4),
+                         "rounds_per_s": round(1000.0 / rr["p50"], 1),
+                         "draft_tokens_per_s": round(4 * rr["B"] * 1000.0 / rr["p50"], 1),
+                         "bytes_per_round": b,
+                         "hbm_roofline_frac": round(b / (rr["p50"] * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+                         "path": PATH_NAME[rr["path"]]})
+        out["configs"] = rows
+    if not args.no_cpu_baseline:
+        base, parity = cpu_baseline(model, head_inp, gpu_logits, gpu_ids)
+        out["cpu_baseline"] = base
+        out["parity"] = dict(parity, workload=cfg["name"],
+                             rule="per row relative L2 <= 1e-2; ids equal where the oracle's top-2 gap > 1e-2")
     print(json.dumps(out), flush=True)
-    drafter.close()
+    for d in drafters.values():
+        d.close()
 
 
 if __name__ == "__main__":
