@@ -30,8 +30,9 @@ KERNEL_NAME = {2: "kd::k_small_phase", 3: "kd::k_small_mega"}
 LAUNCHES_PER_ROUND = {2: 30, 3: 1}
 
 
-def algorithmic_bytes(dims, lens, streams, ingest=0, kv="bf16", head="nvfp4"):
-    """Bytes a step must move: weights once (block-FP8 body with scales, NVFP4
+def algorithmic_bytes(dims, lens, streams, ingest=0, kv="bf16", head="nvfp4", body="fp8"):
+    """Bytes a step must move: weights once (block-FP8 body with scales, or an
+    NVFP4 / bf16 body in its own format, NVFP4
     head with block and tensor scales, fp32 vectors), 40,960 B of bf16 K/V per
     visible context row per stream (4 layers x K,V x 20 heads x 128 x 2 B;
     with the rotated 4-bit cache 10,880 B: 64 code bytes and a 4-byte fp16
@@ -43,7 +44,7 @@ def algorithmic_bytes(dims, lens, streams, ingest=0, kv="bf16", head="nvfp4"):
     writes (the weights they use are the round's, counted once); `lens` are the
     lengths the round sees."""
     import synth
-    mb = synth.model_bytes(dims)
+    mb = synth.model_bytes(dims, body)
     if head == "bf16":
         mb["head"] = dims.draft_vocab * dims.hidden * 2
     elif head == "fp8":
@@ -227,6 +228,8 @@ def main():
                          "scale and offset per row (read by the general path)")
     ap.add_argument("--head", choices=("nvfp4", "bf16", "fp8"), default="nvfp4",
                     help="head slice format: NVFP4, or bf16 / block-FP8 (read by the general path)")
+    ap.add_argument("--body", choices=("fp8", "nvfp4", "bf16"), default="fp8",
+                    help="body weight format: block-FP8, or NVFP4 / bf16 (read by the general path)")
     ap.add_argument("--path", type=int, default=0,
                     help="0 automatic; 1 general multi-kernel; 2 small-batch phases as "
                          "separate launches; 3 small-batch persistent kernel")
@@ -257,16 +260,16 @@ def main():
         print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
         return
     dims = synth.FULL
-    head_q = {"nvfp4": kdraft.KD_QUANT_NVFP4, "bf16": kdraft.KD_QUANT_BF16,
-              "fp8": kdraft.KD_QUANT_FP8_BLOCK64}[args.head]
+    quant = {"nvfp4": kdraft.KD_QUANT_NVFP4, "bf16": kdraft.KD_QUANT_BF16, "fp8": kdraft.KD_QUANT_FP8_BLOCK64}
+    head_q, body_q = quant[args.head], quant[args.body]
     stream = torch.cuda.current_stream()
     models, drafters = {}, {}
 
     def drafter_for(name):
         if name not in drafters:
-            models[name] = synth.make_model(dims, name, device="cuda", head=args.head)
+            models[name] = synth.make_model(dims, name, device="cuda", head=args.head, body=args.body)
             d = kdraft.Drafter(max_streams=max(c["streams"] for c in synth.CONFIGS), stream=stream,
-                               head_quant=head_q)
+                               head_quant=head_q, body_quant=body_q)
             d.load_weights(models[name])
             d.debug_set_path(args.path)
             drafters[name] = d
@@ -278,7 +281,7 @@ def main():
     r = run_workload(kdraft, synth, torch, drafter, model, cfg, args.steps, args.warmup, args.kv, args.head,
                      keep=not args.no_cpu_baseline)
     B, ms, path = r["B"], r["ms"], r["path"]
-    ab = algorithmic_bytes(dims, r["lens"], B, r["ingest"], args.kv, args.head)
+    ab = algorithmic_bytes(dims, r["lens"], B, r["ingest"], args.kv, args.head, args.body)
     rounds_s = 1000.0 / ms
     # roofline of the round's kernel: algorithmic bytes per launch over the
     # average launch duration (the HIP-event time of the timed rounds on the
@@ -306,9 +309,11 @@ def main():
                                   + (f" after ingesting {n_ingest} context rows per stream" if n_ingest else "")
                                   + ", draft block 4, "
                                   f"context rows per stream {sorted(set(min(l, 2048) for l in r['lens']))}, "
-                                  f"block-FP8 body, {dict(nvfp4='NVFP4', bf16='bf16', fp8='block-FP8')[args.head]} head (60,614 rows)"
+                                  f"{dict(nvfp4='NVFP4', bf16='bf16', fp8='block-FP8')[args.body]} body, "
+                                  f"{dict(nvfp4='NVFP4', bf16='bf16', fp8='block-FP8')[args.head]} head (60,614 rows)"
                                   + (", rotated 4-bit K/V cache" if args.kv == "int4" else ""),
                       "streams": B, "draft_tokens_per_round": 4 * B, "kv_cache": args.kv, "head": args.head,
+                      "body": args.body,
                       "path": PATH_NAME[path]},
            "draft_tokens_per_s": round(4 * B * rounds_s, 1),
            "bytes_per_round": ab, "hbm_roofline_frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -339,7 +344,7 @@ def main():
                 rr = run_workload(kdraft, synth, torch, d, m, c, min(args.steps, 30) if big else args.steps,
                                   min(args.warmup, 5) if big else args.warmup, args.kv, args.head)
                 torch.cuda.empty_cache()
-            b = algorithmic_bytes(dims, rr["lens"], rr["B"], rr["ingest"], args.kv, args.head)["total"]
+            b = algorithmic_bytes(dims, rr["lens"], rr["B"], rr["ingest"], args.kv, args.head, args.body)["total"]
             rows.append({"workload": c["name"], "streams": rr["B"],
                          "ingest_rows_per_stream": rr["ingest"],
                          "steps": args.steps if i == head_i or rr["B"] < 64 else min(args.steps, 30),

@@ -274,80 +274,172 @@ bool floats_ok(const float* s, size_t n) {
     if (!std::isfinite(s[i])) return false;
   return true;
 }
+bool bf16_ok(const uint8_t* q, size_t n) {   // n values, 2 bytes each, little-endian
+  for (size_t i = 0; i < n; ++i)
+    if ((q[2 * i + 1] & 0x7f) == 0x7f && (q[2 * i] & 0x80)) return false;   // exponent all ones
+  return true;
+}
 
-// Host staging of a (possibly concatenated) block-FP8 matrix before upload.
+// Host staging of a (possibly joined) weight matrix before upload, row-major.
 struct HostMat {
-  std::vector<uint8_t> q;
-  std::vector<float> s;
+  int fmt = kd::WF_FP8;
   int N = 0, K = 0;
+  int ks = 0;                  // NVFP4: first 64-input block of the second tensor scale
+  std::vector<uint8_t> q;      // per row: K code bytes (FP8), K/2 (NVFP4), 2K value bytes (bf16)
+  std::vector<float> s;        // FP8: [N][K/64] block scales
+  std::vector<uint8_t> s4;     // NVFP4: [N][K/16] block-scale codes
+  std::vector<float> g0, g1;   // NVFP4: per row, the tensor scale before / from block ks
+  size_t row_bytes(int k) const { return fmt == kd::WF_FP8 ? (size_t)k : (fmt == kd::WF_NVFP4 ? (size_t)k / 2 : (size_t)k * 2); }
 };
 
-bool append_rows(HostMat& m, const kd_fp8_matrix& src, int rows, int cols) {
-  if (!src.q || !src.s) return false;
+// A host matrix in format fmt, rows x cols: pointers present, values valid
+// (no NaN codes, finite scales and bf16 values).
+bool mat_ok(const kd_matrix& x, int fmt, int rows, int cols) {
+  const size_t n = (size_t)rows * cols;
+  if (!x.q) return false;
+  if (fmt == kd::WF_FP8) return x.s && fp8_codes_ok(x.q, n) && floats_ok(x.s, n / 64);
+  if (fmt == kd::WF_NVFP4) return x.s4 && fp8_codes_ok(x.s4, n / 16) && std::isfinite(x.g);
+  return bf16_ok(x.q, n);
+}
+
+bool append_rows(HostMat& m, const kd_matrix& src, int rows, int cols) {
   if (m.K == 0) m.K = cols;
-  if (m.K != cols) return false;
-  if (!fp8_codes_ok(src.q, (size_t)rows * cols) || !floats_ok(src.s, (size_t)rows * cols / 64))
-    return false;
-  m.q.insert(m.q.end(), src.q, src.q + (size_t)rows * cols);
-  m.s.insert(m.s.end(), src.s, src.s + (size_t)rows * cols / 64);
+  if (m.K != cols || !mat_ok(src, m.fmt, rows, cols)) return false;
+  const size_t rb = m.row_bytes(cols);
+  m.q.insert(m.q.end(), src.q, src.q + (size_t)rows * rb);
+  if (m.fmt == kd::WF_FP8) m.s.insert(m.s.end(), src.s, src.s + (size_t)rows * cols / 64);
+  if (m.fmt == kd::WF_NVFP4) {
+    m.s4.insert(m.s4.end(), src.s4, src.s4 + (size_t)rows * cols / 16);
+    m.g0.insert(m.g0.end(), rows, src.g);
+    m.g1.insert(m.g1.end(), rows, src.g);
+    m.ks = cols / 64;
+  }
   m.N += rows;
   return true;
 }
 
 // [a | b] along the input dimension (same row count).
-bool concat_cols(HostMat& m, const kd_fp8_matrix& a, const kd_fp8_matrix& b, int rows, int ca,
-                 int cb) {
-  if (!a.q || !a.s || !b.q || !b.s) return false;
-  if (!fp8_codes_ok(a.q, (size_t)rows * ca) || !fp8_codes_ok(b.q, (size_t)rows * cb) ||
-      !floats_ok(a.s, (size_t)rows * ca / 64) || !floats_ok(b.s, (size_t)rows * cb / 64))
-    return false;
+bool concat_cols(HostMat& m, const kd_matrix& a, const kd_matrix& b, int rows, int ca, int cb) {
+  if (!mat_ok(a, m.fmt, rows, ca) || !mat_ok(b, m.fmt, rows, cb)) return false;
   m.N = rows;
   m.K = ca + cb;
-  m.q.resize((size_t)rows * m.K);
-  m.s.resize((size_t)rows * m.K / 64);
+  const size_t ra = m.row_bytes(ca), rb = m.row_bytes(cb);
+  m.q.resize((size_t)rows * (ra + rb));
   for (int r = 0; r < rows; ++r) {
-    memcpy(&m.q[(size_t)r * m.K], a.q + (size_t)r * ca, ca);
-    memcpy(&m.q[(size_t)r * m.K + ca], b.q + (size_t)r * cb, cb);
-    memcpy(&m.s[(size_t)r * m.K / 64], a.s + (size_t)r * ca / 64, ca / 64 * sizeof(float));
-    memcpy(&m.s[(size_t)r * m.K / 64 + ca / 64], b.s + (size_t)r * cb / 64,
-           cb / 64 * sizeof(float));
+    memcpy(&m.q[(size_t)r * (ra + rb)], a.q + (size_t)r * ra, ra);
+    memcpy(&m.q[(size_t)r * (ra + rb) + ra], b.q + (size_t)r * rb, rb);
+  }
+  if (m.fmt == kd::WF_FP8) {
+    m.s.resize((size_t)rows * m.K / 64);
+    for (int r = 0; r < rows; ++r) {
+      memcpy(&m.s[(size_t)r * m.K / 64], a.s + (size_t)r * ca / 64, ca / 64 * sizeof(float));
+      memcpy(&m.s[(size_t)r * m.K / 64 + ca / 64], b.s + (size_t)r * cb / 64, cb / 64 * sizeof(float));
+    }
+  }
+  if (m.fmt == kd::WF_NVFP4) {
+    m.s4.resize((size_t)rows * m.K / 16);
+    for (int r = 0; r < rows; ++r) {
+      memcpy(&m.s4[(size_t)r * m.K / 16], a.s4 + (size_t)r * ca / 16, ca / 16);
+      memcpy(&m.s4[(size_t)r * m.K / 16 + ca / 16], b.s4 + (size_t)r * cb / 16, cb / 16);
+    }
+    m.g0.assign(rows, a.g);   // a's tensor scale on its blocks, b's from block ca / 64 on
+    m.g1.assign(rows, b.g);
+    m.ks = ca / 64;
   }
   return true;
 }
 
 // Reorders rows: row p of the result is row nat(p) of m.
 void permute_rows(HostMat& m, int (*nat)(int)) {
-  HostMat o;
-  o.N = m.N;
-  o.K = m.K;
-  o.q.resize(m.q.size());
-  o.s.resize(m.s.size());
+  HostMat o = m;
+  const size_t rb = m.row_bytes(m.K);
   for (int p = 0; p < m.N; ++p) {
     const int r = nat(p);
-    memcpy(&o.q[(size_t)p * m.K], &m.q[(size_t)r * m.K], m.K);
-    memcpy(&o.s[(size_t)p * m.K / 64], &m.s[(size_t)r * m.K / 64], m.K / 64 * sizeof(float));
+    memcpy(&o.q[(size_t)p * rb], &m.q[(size_t)r * rb], rb);
+    if (m.fmt == kd::WF_FP8)
+      memcpy(&o.s[(size_t)p * m.K / 64], &m.s[(size_t)r * m.K / 64], m.K / 64 * sizeof(float));
+    if (m.fmt == kd::WF_NVFP4) {
+      memcpy(&o.s4[(size_t)p * m.K / 16], &m.s4[(size_t)r * m.K / 16], m.K / 16);
+      o.g0[p] = m.g0[r];
+      o.g1[p] = m.g1[r];
+    }
   }
   m = std::move(o);
 }
 
-kd_status upload_mat(kd_ctx* c, const HostMat& m, kd::Fp8Mat* out) {
-  std::vector<uint8_t> wq((size_t)m.N * m.K);
-  std::vector<float> ws((size_t)m.N * m.K / 64);
-  repack_fp8(m.q.data(), m.s.data(), m.N, m.K, wq.data(), ws.data());
-  uint8_t* dw;
-  float* ds;
+// NVFP4 repack (layout in kd_device.h): codes [N/16][K/64][64 lanes][8],
+// block-scale codes [N/16][K/64][16][4].
+void repack_nvfp4(const uint8_t* q, const uint8_t* s4, int N, int K, uint8_t* wo, uint8_t* so) {
+  const int KB = K / 64;
+  for (int nt = 0; nt < N / 16; ++nt)
+    for (int b = 0; b < KB; ++b) {
+      const size_t blk = (size_t)nt * KB + b;
+      for (int lane = 0; lane < 64; ++lane) {
+        const int n = nt * 16 + (lane & 15), g = lane >> 4;
+        const uint8_t* src = q + (size_t)n * (K / 2) + (64 * b + 8 * g) / 2;
+        memcpy(wo + blk * 512 + lane * 8, src, 4);
+        memcpy(wo + blk * 512 + lane * 8 + 4, src + 16, 4);
+      }
+      for (int j = 0; j < 16; ++j) memcpy(so + blk * 64 + j * 4, s4 + (size_t)(nt * 16 + j) * (K / 16) + 4 * b, 4);
+    }
+}
+
+// bf16 repack: [N/16][K/64][2 k tiles][64 lanes][8 values].
+void repack_bf16(const uint8_t* q, int N, int K, uint8_t* wo) {
+  const int KB = K / 64;
+  for (int nt = 0; nt < N / 16; ++nt)
+    for (int b = 0; b < KB; ++b)
+      for (int j = 0; j < 2; ++j)
+        for (int lane = 0; lane < 64; ++lane) {
+          const int n = nt * 16 + (lane & 15), g = lane >> 4;
+          memcpy(wo + (((size_t)nt * KB + b) * 2 + j) * 1024 + lane * 16,
+                 q + ((size_t)n * K + 64 * b + 32 * j + 8 * g) * 2, 16);
+        }
+}
+
+// An empty staging matrix in the context's body format.
+HostMat body_mat(const kd_ctx* c) {
+  HostMat m;
+  m.fmt = c->cfg.body_quant == KD_QUANT_NVFP4 ? kd::WF_NVFP4
+                                             : (c->cfg.body_quant == KD_QUANT_BF16 ? kd::WF_BF16 : kd::WF_FP8);
+  return m;
+}
+
+kd_status upload_mat(kd_ctx* c, const HostMat& m, kd::WMat* out) {
+  std::vector<uint8_t> wq(m.row_bytes(m.K) * m.N);
+  std::vector<float> ws;
+  std::vector<uint8_t> ws4;
+  if (m.fmt == kd::WF_FP8) {
+    ws.resize((size_t)m.N * m.K / 64);
+    repack_fp8(m.q.data(), m.s.data(), m.N, m.K, wq.data(), ws.data());
+  } else if (m.fmt == kd::WF_NVFP4) {
+    ws4.resize((size_t)m.N * m.K / 16);
+    repack_nvfp4(m.q.data(), m.s4.data(), m.N, m.K, wq.data(), ws4.data());
+    ws = m.g0;
+    ws.insert(ws.end(), m.g1.begin(), m.g1.end());
+  } else {
+    repack_bf16(m.q.data(), m.N, m.K, wq.data());
+  }
+  uint8_t* dw = nullptr;
+  float* ds = nullptr;
+  uint8_t* ds4 = nullptr;
   // scales get 1 KB of slack: the streamed round copies them in whole 1 KB
   // chunks, the last of which may run past the matrix
   if (!dev_alloc(c->weight_allocs, &dw, wq.size()) ||
-      !dev_alloc(c->weight_allocs, &ds, ws.size() + 256))
+      (!ws.empty() && !dev_alloc(c->weight_allocs, &ds, ws.size() + 256)) ||
+      (!ws4.empty() && !dev_alloc(c->weight_allocs, &ds4, ws4.size())))
     return fail(c, KD_ERR_OOM, "weight allocation failed");
   hipError_t e = hipMemcpy(dw, wq.data(), wq.size(), hipMemcpyHostToDevice);
-  if (e == hipSuccess) e = hipMemcpy(ds, ws.data(), ws.size() * sizeof(float), hipMemcpyHostToDevice);
+  if (e == hipSuccess && ds) e = hipMemcpy(ds, ws.data(), ws.size() * sizeof(float), hipMemcpyHostToDevice);
+  if (e == hipSuccess && ds4) e = hipMemcpy(ds4, ws4.data(), ws4.size(), hipMemcpyHostToDevice);
   if (e != hipSuccess) return hip_fail(c, e, "weight upload");
   out->w = dw;
   out->s = ds;
+  out->s4 = ds4;
   out->N = m.N;
   out->K = m.K;
+  out->fmt = m.fmt;
+  out->ks = m.fmt == kd::WF_NVFP4 ? m.ks : m.K / 64;
   return KD_OK;
 }
 
@@ -455,7 +547,8 @@ kd_status kd_create(const kd_config* cfg, void* hip_stream, kd_ctx** out) {
   *out = nullptr;
   if (!cfg) return KD_ERR_ARG;
   if (!shape_is_supported(*cfg)) return KD_ERR_UNSUPPORTED;
-  if (cfg->body_quant != KD_QUANT_FP8_BLOCK64 ||
+  if ((cfg->body_quant != KD_QUANT_FP8_BLOCK64 && cfg->body_quant != KD_QUANT_NVFP4 &&
+       cfg->body_quant != KD_QUANT_BF16) ||
       (cfg->head_quant != KD_QUANT_NVFP4 && cfg->head_quant != KD_QUANT_BF16 &&
        cfg->head_quant != KD_QUANT_FP8_BLOCK64))
     return KD_ERR_UNSUPPORTED;
@@ -578,23 +671,23 @@ kd_status kd_load_weights(kd_ctx* c, const kd_weights* wt) {
 
   kd_status st;
   {
-    HostMat m;
+    HostMat m = body_mat(c);
     if (!append_rows(m, wt->fuse, H, kd::NTAP * H)) return fail(c, KD_ERR_ARG, "bad fuse matrix");
     if ((st = upload_mat(c, m, &d.fuse)) != KD_OK) return st;
   }
   {
-    HostMat m;
+    HostMat m = body_mat(c);
     if (!append_rows(m, wt->fc, H, 2 * H)) return fail(c, KD_ERR_ARG, "bad fc matrix");
     if ((st = upload_mat(c, m, &d.fc)) != KD_OK) return st;
   }
   {
-    HostMat m;
+    HostMat m = body_mat(c);
     if (!concat_cols(m, wt->pred_a, wt->pred_b, r, H, H))
       return fail(c, KD_ERR_ARG, "bad predecessor A/B matrix");
     if ((st = upload_mat(c, m, &d.pred_ab)) != KD_OK) return st;
   }
   {
-    HostMat m;
+    HostMat m = body_mat(c);
     if (!append_rows(m, wt->pred_u, H, r)) return fail(c, KD_ERR_ARG, "bad predecessor U matrix");
     if ((st = upload_mat(c, m, &d.pred_u)) != KD_OK) return st;
   }
@@ -602,7 +695,7 @@ kd_status kd_load_weights(kd_ctx* c, const kd_weights* wt) {
   for (int l = 0; l < kd::NL; ++l) {
     const kd_layer_weights& L = wt->layer[l];
     kd::DevLayer& D = d.layer[l];
-    HostMat qkv, wo, gu, dn;
+    HostMat qkv = body_mat(c), wo = qkv, gu = qkv, dn = qkv;
     if (!append_rows(qkv, L.wq, H, H) || !append_rows(qkv, L.wk, H, H) ||
         !append_rows(qkv, L.wv, H, H))
       return fail(c, KD_ERR_ARG, "bad q/k/v matrix");
@@ -619,7 +712,7 @@ kd_status kd_load_weights(kd_ctx* c, const kd_weights* wt) {
         (st = upload_vec(c, L.ffn_norm, H, &D.ffn_norm)) != KD_OK)
       return st;
     if (l >= 1) {
-      HostMat sa, su;
+      HostMat sa = body_mat(c), su = sa;
       if (!append_rows(sa, L.spine_a, r, H) || !append_rows(su, L.spine_u, H, r))
         return fail(c, KD_ERR_ARG, "bad spine matrix");
       if ((st = upload_mat(c, sa, &D.sa)) != KD_OK || (st = upload_mat(c, su, &D.su)) != KD_OK)
@@ -641,7 +734,7 @@ kd_status kd_load_weights(kd_ctx* c, const kd_weights* wt) {
   }
 
   const int VT = (VD + 15) / 16;
-  d.hf8 = kd::Fp8Mat();
+  d.hf8 = kd::WMat();
   if (head_fp8) {
     // block-FP8 head rows, zero rows (code 0, scale 1) up to whole 16-row
     // tiles, repacked as a body matrix
@@ -791,6 +884,7 @@ static kd_status round_impl(kd_ctx* c, int depth, int B, const void* taps, const
   if (path != 1 && B > kd::SB_MAX) path = 1;
   if (k.fmt == KD_KV_INT4_ROT) path = 1;   // the 4-bit cache is read by the general path
   if (d.head_fmt != 0) path = 1;           // so are the bf16 and FP8 heads
+  if (d.fuse.fmt != kd::WF_FP8) path = 1;  // and the NVFP4 and bf16 bodies
   c->last_path = path;
   if (path != 1) {
     (void)hipGetLastError();

@@ -16,6 +16,18 @@
 //    are W[16*nt + l%16][64*b + 8*(l/16) + e] for e = 0..7 (k tile 2b), then
 //    the same for k tile 2b+1 (+32). Scales: [N/16][K/64][16] fp32.
 //
+//  * NVFP4 body weights W[N][K] (e2m1 codes, an e4m3 scale per 16 inputs of
+//    a row, an fp32 tensor scale): codes [N/16][K/64][64 lanes][8 bytes],
+//    lane l's bytes 0..3 holding W[16*nt + l%16][64*b + 8*(l/16) + e],
+//    e = 0..7, even e in the low nibble (k tile 2b), bytes 4..7 the same at
+//    +32 (k tile 2b+1); block-scale codes [N/16][K/64][16 rows][4 bytes],
+//    byte i the scale of inputs 64*b + 16*i .. + 15; the tensor scale per
+//    output row, twice ([2][N]: for blocks before the matrix's split block
+//    and from it on, where two matrices are joined along K).
+//
+//  * bf16 body weights W[N][K]: [N/16][K/64][2 k tiles][64 lanes][8 bf16],
+//    lane l holding W[16*nt + l%16][64*b + 32*j + 8*(l/16) + e].
+//
 //  * NVFP4 head rows are repacked to [V/16][K/128][64 lanes][16 bytes] of
 //    e2m1 nibbles (lane l, k tile t = 4*g + i: bytes 4i..4i+3 hold
 //    W[16*vt + l%16][32*t + 8*(l/16) + e], e = 0..7, even e in the low
@@ -39,6 +51,9 @@ constexpr int NTAP = 3;      // tapped target layers
 constexpr int QKV = 3 * H;   // fused q|k|v output width
 constexpr int GU = 2 * FF;   // fused gate|up output width
 constexpr int ATT_CH = 128;  // context keys per attention workgroup
+
+// Body-matrix formats (layouts above).
+enum { WF_FP8 = 0, WF_NVFP4 = 1, WF_BF16 = 2 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -132,6 +147,84 @@ __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
 }
 __device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// An f16 operand as two exact bf16 terms for the bf16 matrix cores: hi keeps
+// the top 8 significant bits of each value, lo the rest (at most 3 bits), so
+// W * hi + W * lo is W * a exactly in fp32.
+__device__ __forceinline__ void split_f16_bf16(f16x8 a, bf16x8& hi, bf16x8& lo) {
+  u32x4 h, l;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float v0 = (float)a[2 * e], v1 = (float)a[2 * e + 1];
+    const float h0 = u2f(f2u(v0) & 0xffff0000u), h1 = u2f(f2u(v1) & 0xffff0000u);
+    h[e] = pack_hi16(h0, h1);
+    l[e] = pack_hi16(v0 - h0, v1 - h1);
+  }
+  hi = __builtin_bit_cast(bf16x8, h);
+  lo = __builtin_bit_cast(bf16x8, l);
+}
+
+// One 64-input block of a 16x16 output tile: the f16 activation fragments
+// a0, a1 (k tiles 2b, 2b+1) times the block's weights, as an fp32 partial sum
+// before any block or tensor scale.
+template <int WF>
+struct WBlock;
+template <>
+struct WBlock<WF_FP8> {   // 16 e4m3 codes
+  u32x4 q;
+  __device__ __forceinline__ f32x4 mul(f16x8 a0, f16x8 a1) const {
+    f32x4 t = {0.f, 0.f, 0.f, 0.f};
+    t = mfma_f16(a0, e4m3x8_f16(q.x, q.y), t);
+    return mfma_f16(a1, e4m3x8_f16(q.z, q.w), t);
+  }
+};
+template <>
+struct WBlock<WF_NVFP4> {   // 16 e2m1 codes and the lane's two e4m3 block scales
+  uint32_t q0, q1, sc;
+  __device__ __forceinline__ f32x4 mul(f16x8 a0, f16x8 a1) const {
+    f32x4 t = {0.f, 0.f, 0.f, 0.f};
+    t = mfma_f16(a0, nvfp4x8_f16(q0, sc & 0xffu), t);
+    return mfma_f16(a1, nvfp4x8_f16(q1, sc >> 8), t);
+  }
+};
+template <>
+struct WBlock<WF_BF16> {   // 16 bf16 values
+  u32x4 w0, w1;
+  __device__ __forceinline__ f32x4 mul(f16x8 a0, f16x8 a1) const {
+    bf16x8 h0, l0, h1, l1;
+    split_f16_bf16(a0, h0, l0);
+    split_f16_bf16(a1, h1, l1);
+    f32x4 t = {0.f, 0.f, 0.f, 0.f};
+    t = mfma_bf16(h0, __builtin_bit_cast(bf16x8, w0), t);
+    t = mfma_bf16(l0, __builtin_bit_cast(bf16x8, w0), t);
+    t = mfma_bf16(h1, __builtin_bit_cast(bf16x8, w1), t);
+    return mfma_bf16(l1, __builtin_bit_cast(bf16x8, w1), t);
+  }
+};
+
+// Lane `lane`'s part of block (nt, b) of a repacked matrix. NVFP4: the lane's
+// inputs 8 (lane/16) .. + 8 of k tile 2b lie in 16-input scale block
+// (lane/16)/2, those of k tile 2b+1 in block 2 + (lane/16)/2.
+template <int WF>
+__device__ __forceinline__ WBlock<WF> load_wblock(const uint8_t* w, const uint8_t* s4, int KB, int nt, int b,
+                                                  int lane) {
+  const size_t blk = (size_t)nt * KB + b;
+  WBlock<WF> r;
+  if constexpr (WF == WF_FP8) {
+    r.q = *reinterpret_cast<const u32x4*>(w + blk * 1024 + lane * 16);
+  } else if constexpr (WF == WF_NVFP4) {
+    const uint2 q = *reinterpret_cast<const uint2*>(w + blk * 512 + lane * 8);
+    const uint32_t sw = *reinterpret_cast<const uint32_t*>(s4 + blk * 64 + (lane & 15) * 4);
+    const int sh = 8 * ((lane >> 4) >> 1);
+    r.q0 = q.x;
+    r.q1 = q.y;
+    r.sc = ((sw >> sh) & 0xffu) | (((sw >> (sh + 16)) & 0xffu) << 8);
+  } else {
+    r.w0 = *reinterpret_cast<const u32x4*>(w + blk * 2048 + lane * 16);
+    r.w1 = *reinterpret_cast<const u32x4*>(w + blk * 2048 + 1024 + lane * 16);
+  }
+  return r;
 }
 
 // Element offset of afrag(row, k).

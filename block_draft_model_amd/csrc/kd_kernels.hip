@@ -18,21 +18,24 @@
 namespace kd {
 
 // ---------------------------------------------------------------------------
-// Block-FP8 projection: part[split][r][n] = sum over the split's inputs of
-// X[r][k] * W[n_off*16 + n][k].
+// Projection: part[split][r][n] = sum over the split's inputs of
+// X[r][k] * W[n_off*16 + n][k], W in one of the body formats (WF).
 // ---------------------------------------------------------------------------
 struct GemmK {
   const uint16_t* af;
   int R, KT;
   const uint8_t* w;
   const float* s;
+  const uint8_t* s4;
   int KB;        // 64-input blocks per weight row
   int N;         // output columns of this launch (multiple of 64)
   int n_off;     // first 16-row weight tile
+  int WN, ks;    // NVFP4: rows of the whole matrix, first block of its second tensor scale
   float* part;
   int splits, kbs;
 };
 
+template <int WF>
 __global__ __launch_bounds__(256) void k_gemm(GemmK g) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ngroups = g.N >> 6;
@@ -46,25 +49,32 @@ __global__ __launch_bounds__(256) void k_gemm(GemmK g) {
   const int b0 = sp * g.kbs;
   const int row = mt * 16 + (lane & 15);
   const bool rv = row < g.R;
-  const uint8_t* wp = g.w + ((size_t)ntw * g.KB + b0) * 1024 + lane * 16;
+  // the block multiplier: FP8 its block scale; NVFP4 the column's tensor
+  // scale of the block's side of the split; bf16 none
   const float* spp = g.s + ((size_t)ntw * g.KB + b0) * 16 + (lane & 15);
+  float gt0 = 1.f, gt1 = 1.f;
+  if constexpr (WF == WF_NVFP4) {
+    gt0 = g.s[ntw * 16 + (lane & 15)];
+    gt1 = g.s[g.WN + ntw * 16 + (lane & 15)];
+  }
   const uint16_t* ap = g.af + ((size_t)mt * g.KT + 2 * b0) * 512 + lane * 8;
   const f16x8 zero = __builtin_bit_cast(f16x8, u32x4{0u, 0u, 0u, 0u});
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
   for (int i = 0; i < g.kbs; ++i) {
-    const u32x4 wv = *reinterpret_cast<const u32x4*>(wp + (size_t)i * 1024);
-    const float sc = spp[i * 16];
+    const WBlock<WF> wb = load_wblock<WF>(g.w, g.s4, g.KB, ntw, b0 + i, lane);
+    float sc = 1.f;
+    if constexpr (WF == WF_FP8) sc = spp[i * 16];
+    if constexpr (WF == WF_NVFP4) sc = b0 + i < g.ks ? gt0 : gt1;
     f16x8 a0 = zero, a1 = zero;
     if (rv) {
       const uint16_t* a = ap + (size_t)i * 1024;
       a0 = *reinterpret_cast<const f16x8*>(a);
       a1 = *reinterpret_cast<const f16x8*>(a + 512);
     }
-    f32x4 t = {0.f, 0.f, 0.f, 0.f};
-    t = mfma_f16(a0, e4m3x8_f16(wv.x, wv.y), t);
-    t = mfma_f16(a1, e4m3x8_f16(wv.z, wv.w), t);
-    acc += sc * t;
+    const f32x4 t = wb.mul(a0, a1);
+    if constexpr (WF == WF_BF16) acc += t;
+    else acc += sc * t;
   }
   float* out = g.part + (size_t)sp * g.R * g.N + nt * 16 + (lane & 15);
 #pragma unroll
@@ -93,7 +103,7 @@ int gemm_splits(int K, int N, int R) {
   return splits_for(KB, mt == 1 ? base : base / mt);
 }
 
-void launch_gemm(hipStream_t st, const uint16_t* af, int R, const Fp8Mat& W, int n_off_tiles,
+void launch_gemm(hipStream_t st, const uint16_t* af, int R, const WMat& W, int n_off_tiles,
                  int N, float* part, int splits) {
   if (gemm_mm_fits(R, N)) return launch_gemm_mm(st, af, R, W, n_off_tiles, N, part, splits);
   GemmK g;
@@ -102,14 +112,19 @@ void launch_gemm(hipStream_t st, const uint16_t* af, int R, const Fp8Mat& W, int
   g.KT = W.K / 32;
   g.w = W.w;
   g.s = W.s;
+  g.s4 = W.s4;
   g.KB = W.K / 64;
   g.N = N;
   g.n_off = n_off_tiles;
+  g.WN = W.N;
+  g.ks = W.ks;
   g.part = part;
   g.splits = splits;
   g.kbs = g.KB / splits;
   const int blocks = mtiles(R) * splits * (N / 64);
-  k_gemm<<<blocks, 256, 0, st>>>(g);
+  if (W.fmt == WF_NVFP4) k_gemm<WF_NVFP4><<<blocks, 256, 0, st>>>(g);
+  else if (W.fmt == WF_BF16) k_gemm<WF_BF16><<<blocks, 256, 0, st>>>(g);
+  else k_gemm<WF_FP8><<<blocks, 256, 0, st>>>(g);
 }
 
 // ---------------------------------------------------------------------------

@@ -54,23 +54,26 @@ static int mm_grid(int R, int CB, int S) {
 }
 
 // ---------------------------------------------------------------------------
-// Block-FP8 projection: part[split][r][n] = sum over the split's inputs of
-// X[r][k] * W[n_off*16 + n][k]; one step is one 64-input block (the block's
-// fp32 scale multiplies its partial sum, as the scale is defined per row and
-// 64 inputs).
+// Projection: part[split][r][n] = sum over the split's inputs of
+// X[r][k] * W[n_off*16 + n][k], W in one of the body formats (WF); one step
+// is one 64-input block (a block-FP8 block's fp32 scale multiplies its
+// partial sum, as the scale is defined per row and 64 inputs; an NVFP4
+// block's partial sum is multiplied by its column's tensor scale).
 // ---------------------------------------------------------------------------
 struct GemmMM {
   const uint16_t* af;   // afrag of X: [mtiles(R)][KT][512] f16
   int R, KT;
-  const uint8_t* w;     // repacked codes [N/16][KB][64][16]
-  const float* s;       // scales [N/16][KB][16]
+  const uint8_t* w;     // repacked weights (layout per format in kd_device.h)
+  const float* s;       // FP8 scales [N/16][KB][16]; NVFP4 tensor scales [2][WN]
+  const uint8_t* s4;    // NVFP4 block-scale codes
   int KB;
   int N, n_off;         // output columns (a multiple of the workgroup's), first weight tile
+  int WN, ks;           // NVFP4: rows of the matrix, first block of its second tensor scale
   float* part;
   int splits, kbs;
 };
 
-template <int CT, int D>
+template <int CT, int D, int WF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_mm(GemmMM g) {
   constexpr int COLS = 16 * CT * MM_WAVES;
   // [buffer][row tile][k tile t, t+1][lane]
@@ -86,9 +89,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int mt_ld = min(m.rb * MM_RT + wave, MT - 1);
   const uint16_t* ap = g.af + ((size_t)mt_ld * g.KT + 2 * b0) * 512 + lane * 8;
   const int nt0 = g.n_off + m.cb * (COLS / 16) + wave * CT;
-  const uint8_t* wp = g.w + ((size_t)nt0 * g.KB + b0) * 1024 + lane * 16;
   const float* spp = g.s + ((size_t)nt0 * g.KB + b0) * 16 + (lane & 15);
-  const size_t wt_stride = (size_t)g.KB * 1024, st_stride = (size_t)g.KB * 16;
+  const size_t st_stride = (size_t)g.KB * 16;
+  float gt[CT][2];   // NVFP4: the columns' tensor scales before / from the split block
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    gt[c][0] = gt[c][1] = 1.f;
+    if constexpr (WF == WF_NVFP4) {
+      gt[c][0] = g.s[(nt0 + c) * 16 + (lane & 15)];
+      gt[c][1] = g.s[g.WN + (nt0 + c) * 16 + (lane & 15)];
+    }
+  }
 
   f32x4 acc[MM_RT][CT];
 #pragma unroll
@@ -102,16 +113,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   // matrix cores while D - 1 later steps are in flight. Loads past the last
   // step re-load it (unconditional loads keep the compiler from waiting for
   // them at a join).
-  u32x4 ar[D][2], wr[D][CT];
+  u32x4 ar[D][2];
+  WBlock<WF> wr[D][CT];
   float sr[D][CT];
   auto load = [&](int st, int d) __attribute__((always_inline)) {
-    const size_t sc = (size_t)min(st, nb - 1);
+    const int sc = min(st, nb - 1);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) ar[d][j] = *reinterpret_cast<const u32x4*>(ap + sc * 1024 + j * 512);
+    for (int j = 0; j < 2; ++j) ar[d][j] = *reinterpret_cast<const u32x4*>(ap + (size_t)sc * 1024 + j * 512);
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
-      wr[d][c] = *reinterpret_cast<const u32x4*>(wp + c * wt_stride + sc * 1024);
-      sr[d][c] = spp[c * st_stride + sc * 16];
+      wr[d][c] = load_wblock<WF>(g.w, g.s4, g.KB, nt0 + c, b0 + sc, lane);
+      if constexpr (WF == WF_FP8) sr[d][c] = spp[c * st_stride + (size_t)sc * 16];
+      if constexpr (WF == WF_NVFP4) sr[d][c] = b0 + sc < g.ks ? gt[c][0] : gt[c][1];
     }
   };
 #pragma unroll
@@ -125,12 +138,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     for (int d = 0; d < D; ++d) {
       const int i = i0 + d;
       if (i < nb) {
-        f16x8 w0[CT], w1[CT];
+        WBlock<WF> wv[CT];
         float sc[CT];
 #pragma unroll
         for (int c = 0; c < CT; ++c) {
-          w0[c] = e4m3x8_f16(wr[d][c].x, wr[d][c].y);
-          w1[c] = e4m3x8_f16(wr[d][c].z, wr[d][c].w);
+          wv[c] = wr[d][c];
           sc[c] = sr[d][c];
         }
         // the slot's activations went to LDS a step ago: refill it
@@ -142,10 +154,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
           const f16x8 a1 = __builtin_bit_cast(f16x8, sa[buf][r * 2 + 1][lane]);
 #pragma unroll
           for (int c = 0; c < CT; ++c) {
-            f32x4 t = {0.f, 0.f, 0.f, 0.f};
-            t = mfma_f16(a0, w0[c], t);
-            t = mfma_f16(a1, w1[c], t);
-            acc[r][c] += sc[c] * t;
+            const f32x4 t = wv[c].mul(a0, a1);
+            if constexpr (WF == WF_BF16) acc[r][c] += t;
+            else acc[r][c] += sc[c] * t;
           }
         }
         if (i + 1 < nb) {
@@ -184,7 +195,7 @@ int gemm_mm_splits(int K, int N, int R) {
 
 bool gemm_mm_fits(int R, int N) { return R > 32 && N % (64 * mm_ct(R)) == 0; }
 
-void launch_gemm_mm(hipStream_t st, const uint16_t* af, int R, const Fp8Mat& W, int n_off_tiles,
+void launch_gemm_mm(hipStream_t st, const uint16_t* af, int R, const WMat& W, int n_off_tiles,
                     int N, float* part, int splits) {
   GemmMM g;
   g.af = af;
@@ -192,16 +203,30 @@ void launch_gemm_mm(hipStream_t st, const uint16_t* af, int R, const Fp8Mat& W, 
   g.KT = W.K / 32;
   g.w = W.w;
   g.s = W.s;
+  g.s4 = W.s4;
   g.KB = W.K / 64;
   g.N = N;
   g.n_off = n_off_tiles;
+  g.WN = W.N;
+  g.ks = W.ks;
   g.part = part;
   g.splits = splits;
   g.kbs = g.KB / splits;
-  if (mm_ct(R) == 4)
-    k_gemm_mm<4, 2><<<mm_grid(R, N / 256, splits), 256, 0, st>>>(g);
-  else
-    k_gemm_mm<1, 4><<<mm_grid(R, N / 64, splits), 256, 0, st>>>(g);
+  const bool wide = mm_ct(R) == 4;
+  const dim3 grid(mm_grid(R, N / (wide ? 256 : 64), splits));
+  switch (W.fmt) {
+    case WF_NVFP4:
+      if (wide) k_gemm_mm<4, 2, WF_NVFP4><<<grid, 256, 0, st>>>(g);
+      else k_gemm_mm<1, 4, WF_NVFP4><<<grid, 256, 0, st>>>(g);
+      break;
+    case WF_BF16:
+      if (wide) k_gemm_mm<4, 2, WF_BF16><<<grid, 256, 0, st>>>(g);
+      else k_gemm_mm<1, 4, WF_BF16><<<grid, 256, 0, st>>>(g);
+      break;
+    default:
+      if (wide) k_gemm_mm<4, 2, WF_FP8><<<grid, 256, 0, st>>>(g);
+      else k_gemm_mm<1, 4, WF_FP8><<<grid, 256, 0, st>>>(g);
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "kd_device.h"
+
 namespace kd {
 
 // Device code reads the structures below through global-address-space
@@ -19,17 +21,20 @@ namespace kd {
 template <class T> using HostPtr = T*;
 template <class T> using GlobalPtr = KD_GLOBAL T*;
 
-// A repacked block-FP8 matrix on the device (layout in kd_device.h).
+// A repacked weight matrix on the device.
 template <template <class> class P>
-struct Fp8MatT {
-  P<const uint8_t> w = nullptr;
-  P<const float> s = nullptr;
+struct WMatT {
+  P<const uint8_t> w = nullptr;   // codes (FP8, NVFP4) or bf16 values
+  P<const float> s = nullptr;     // FP8: block scales; NVFP4: tensor scales [2][N]
+  P<const uint8_t> s4 = nullptr;  // NVFP4: block-scale codes
   int N = 0, K = 0;
+  int fmt = WF_FP8;
+  int ks = 0;                     // NVFP4: first 64-input block of the second tensor scale
 };
 
 template <template <class> class P>
 struct DevLayerT {
-  Fp8MatT<P> qkv, wo, gu, down, sa, su;
+  WMatT<P> qkv, wo, gu, down, sa, su;
   P<const float> attn_norm = nullptr;
   P<const float> ffn_norm = nullptr;
   P<const float> spine_norm = nullptr;
@@ -37,7 +42,7 @@ struct DevLayerT {
 
 template <template <class> class P>
 struct DevWeightsT {
-  Fp8MatT<P> fuse, fc, pred_ab, pred_u;   // pred_ab = [A_p | B_p] along K
+  WMatT<P> fuse, fc, pred_ab, pred_u;   // pred_ab = [A_p | B_p] along K
   P<const float> mask = nullptr;
   DevLayerT<P> layer[4];
   P<const float> final_norm = nullptr;
@@ -52,7 +57,7 @@ struct DevWeightsT {
   P<const float> kv_signs = nullptr;      // [NL][DH] +-1 of the rotated 4-bit cache, or null
   int head_fmt = 0;                       // 0 NVFP4 (hq, hs, hg), 1 bf16 (hb), 2 FP8 (hf8)
   P<const uint16_t> hb = nullptr;         // bf16 head [VT][H/32][64 lanes][8]
-  Fp8MatT<P> hf8;                         // block-FP8 head, VT * 16 rows (zero-padded)
+  WMatT<P> hf8;                           // block-FP8 head, VT * 16 rows (zero-padded)
 };
 
 // Context K/V description passed to kernels. fmt 0: bf16 elements, strides
@@ -69,7 +74,7 @@ struct KVT {
   P<const uint16_t> vso[4] = {};
 };
 
-using Fp8Mat = Fp8MatT<HostPtr>;
+using WMat = WMatT<HostPtr>;
 using DevLayer = DevLayerT<HostPtr>;
 using DevWeights = DevWeightsT<HostPtr>;
 using KV = KVT<HostPtr>;
@@ -113,7 +118,7 @@ inline size_t afrag_elems(int R, int K) { return (size_t)mtiles(R) * (K / 32) * 
 int gemm_splits(int K, int N, int R);
 
 // ---- launchers (kd_kernels.hip) ----
-void launch_gemm(hipStream_t st, const uint16_t* af, int R, const Fp8Mat& W, int n_off_tiles,
+void launch_gemm(hipStream_t st, const uint16_t* af, int R, const WMat& W, int n_off_tiles,
                  int N, float* part, int splits);
 void launch_prep(hipStream_t st, const Work& w, const DevWeights& d, int B, const uint16_t* taps,
                  const int32_t* lens, float theta);
@@ -149,7 +154,7 @@ void launch_bump_lens(hipStream_t st, int32_t* lens, int B, int n);
 // many block rows (kd_mm.hip): matrix-core tiles of 64 rows x 256 columns
 bool gemm_mm_fits(int R, int N);
 int gemm_mm_splits(int K, int N, int R);
-void launch_gemm_mm(hipStream_t st, const uint16_t* af, int R, const Fp8Mat& W, int n_off_tiles,
+void launch_gemm_mm(hipStream_t st, const uint16_t* af, int R, const WMat& W, int n_off_tiles,
                     int N, float* part, int splits);
 bool head_mm_fits(int R);
 void launch_head_mm(hipStream_t st, const uint16_t* af, int R, const DevWeights& d, float* logits,

@@ -49,7 +49,7 @@ namespace kd {
 // loads), global-address-space pointers inside.
 typedef const SmallArgsT<GlobalPtr> KD_CONST Args;
 typedef const SmallBufsT<GlobalPtr> KD_CONST Bufs;
-typedef const Fp8MatT<GlobalPtr> KD_CONST Mat;
+typedef const WMatT<GlobalPtr> KD_CONST Mat;
 typedef KD_LDS float* lds_f;
 typedef const KD_LDS float* lds_cf;
 template <class T> using gptr = KD_GLOBAL T*;

@@ -28,22 +28,22 @@ class KdConfig(ctypes.Structure):
         ("rope_theta", c_float), ("rms_eps", c_float), ("body_quant", c_int), ("head_quant", c_int)]
 
 
-class KdFp8Matrix(ctypes.Structure):
-    _fields_ = [("q", c_void_p), ("s", c_void_p)]
+class KdMatrix(ctypes.Structure):
+    _fields_ = [("q", c_void_p), ("s", c_void_p), ("s4", c_void_p), ("g", c_float)]
 
 
 class KdLayerWeights(ctypes.Structure):
-    _fields_ = [(n, KdFp8Matrix) for n in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")] + [
+    _fields_ = [(n, KdMatrix) for n in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")] + [
         ("attn_norm", c_void_p), ("ffn_norm", c_void_p), ("spine_norm", c_void_p),
-        ("spine_a", KdFp8Matrix), ("spine_u", KdFp8Matrix)]
+        ("spine_a", KdMatrix), ("spine_u", KdMatrix)]
 
 
 class KdWeights(ctypes.Structure):
-    _fields_ = [(n, KdFp8Matrix) for n in ("fuse", "fc", "pred_a", "pred_b", "pred_u")] + [
+    _fields_ = [(n, KdMatrix) for n in ("fuse", "fc", "pred_a", "pred_b", "pred_u")] + [
         ("mask_row", c_void_p), ("layer", KdLayerWeights * 4), ("final_norm", c_void_p),
         ("head_q4", c_void_p), ("head_s4", c_void_p), ("head_g", c_float),
         ("draft_vocab", c_void_p), ("embed_table", c_void_p), ("kv_rot_signs", c_void_p),
-        ("head_bf16", c_void_p), ("head_fp8", KdFp8Matrix)]
+        ("head_bf16", c_void_p), ("head_fp8", KdMatrix)]
 
 
 KD_KV_BF16, KD_KV_INT4_ROT = 0, 1
@@ -281,22 +281,34 @@ class Drafter:
             return a.ctypes.data
 
         def fp8(name):
-            return KdFp8Matrix(h(model[name + ".q"]), h(model[name + ".s"]))
+            return KdMatrix(h(model[name + ".q"]), h(model[name + ".s"]), None, 0.0)
+
+        body = model.get("body_format", "fp8")
+
+        def mat(name):
+            """A body matrix in the model's body format (the context's body_quant)."""
+            if body == "nvfp4":
+                return KdMatrix(h(model[name + ".q4"]), None, h(model[name + ".s4"]), float(model[name + ".g"]))
+            if body == "bf16":
+                import torch
+                v = model[name + ".bf16"]
+                return KdMatrix(h(v.view(torch.int16) if isinstance(v, torch.Tensor) else v), None, None, 0.0)
+            return fp8(name)
 
         w = KdWeights()
-        w.fuse, w.fc = fp8("fuse"), fp8("fc")
-        w.pred_a, w.pred_b, w.pred_u = fp8("pred_a"), fp8("pred_b"), fp8("pred_u")
+        w.fuse, w.fc = mat("fuse"), mat("fc")
+        w.pred_a, w.pred_b, w.pred_u = mat("pred_a"), mat("pred_b"), mat("pred_u")
         w.mask_row = h(model["mask"])
         for l in range(4):
             p = f"layers.{l}."
             L = w.layer[l]
             for nm in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down"):
-                setattr(L, nm, fp8(p + nm))
+                setattr(L, nm, mat(p + nm))
             L.attn_norm, L.ffn_norm = h(model[p + "attn_norm"]), h(model[p + "ffn_norm"])
             if l >= 1:
                 sp = f"spine.{l}."
                 L.spine_norm = h(model[sp + "norm"])
-                L.spine_a, L.spine_u = fp8(sp + "a"), fp8(sp + "u")
+                L.spine_a, L.spine_u = mat(sp + "a"), mat(sp + "u")
         w.final_norm = h(model["final_norm"])
         w.head_q4, w.head_s4 = h(model["head.q4"]), h(model["head.s4"])
         w.head_g = float(model["head.g"])

@@ -85,7 +85,9 @@ typedef struct {
   int max_streams;   /* largest `streams` any call will pass */
   float rope_theta;  /* 10000 */
   float rms_eps;     /* 1e-6 */
-  int body_quant;    /* KD_QUANT_FP8_BLOCK64 */
+  int body_quant;    /* KD_QUANT_FP8_BLOCK64 (default), or KD_QUANT_NVFP4 /
+                        KD_QUANT_BF16 (these run the general path at every
+                        batch size) */
   int head_quant;    /* KD_QUANT_NVFP4, or KD_QUANT_BF16 / KD_QUANT_FP8_BLOCK64
                         (the card's Use section offers bf16, FP8 and NVFP4
                         head slices; the bf16 and FP8 heads run the general
@@ -95,34 +97,46 @@ typedef struct {
 /* Fills *cfg with the model card's shape, max_streams = 256. */
 void kd_default_config(kd_config* cfg);
 
-/* A block-FP8 matrix W[rows][cols] on the host: q = e4m3 codes, row-major
- * [rows][cols]; s = fp32 scales [rows][cols/64]; W = e4m3(q) * s[r][c/64]. */
+/* A weight matrix W[rows][cols] on the host, row-major, in the format
+ * kd_config.body_quant names (the block-FP8 head slice, head_fp8, is always
+ * block-FP8); fields a format does not use are ignored (model card, section
+ * Use: FP8, NVFP4 and bf16 bodies):
+ *   KD_QUANT_FP8_BLOCK64: q = e4m3 codes [rows][cols]; s = fp32 scales
+ *     [rows][cols/64]; W = e4m3(q) * s[r][c/64].
+ *   KD_QUANT_NVFP4: q = e2m1 codes [rows][cols/2], column 2m in the low
+ *     nibble of byte m; s4 = e4m3 scale codes [rows][cols/16]; g = fp32
+ *     tensor scale; W = e2m1(q) * e4m3(s4[r][c/16]) * g.
+ *   KD_QUANT_BF16: q = bf16 values [rows][cols], 2 bytes each (little-endian).
+ * kd_load_weights rejects NaN e4m3 codes, non-finite scales and non-finite
+ * bf16 values. */
 typedef struct {
   const uint8_t* q;
   const float* s;
-} kd_fp8_matrix;
+  const uint8_t* s4;
+  float g;
+} kd_matrix;
 
 typedef struct {
-  kd_fp8_matrix wq, wk, wv, wo;  /* [hidden][hidden] */
-  kd_fp8_matrix w_gate, w_up;    /* [ffn][hidden] */
-  kd_fp8_matrix w_down;          /* [hidden][ffn] */
+  kd_matrix wq, wk, wv, wo;  /* [hidden][hidden] */
+  kd_matrix w_gate, w_up;    /* [ffn][hidden] */
+  kd_matrix w_down;          /* [hidden][ffn] */
   const float* attn_norm;        /* [hidden] RMSNorm gains */
   const float* ffn_norm;         /* [hidden] */
   /* Spine applied before this layer (layers 1..3); ignored for layer 0. */
   const float* spine_norm;       /* [hidden] */
-  kd_fp8_matrix spine_a;         /* [rank][hidden] */
-  kd_fp8_matrix spine_u;         /* [hidden][rank] */
+  kd_matrix spine_a;         /* [rank][hidden] */
+  kd_matrix spine_u;         /* [hidden][rank] */
 } kd_layer_weights;
 
 /* Host copies of the weights (copied and repacked by kd_load_weights), except
  * the embedding table, which is borrowed: it is the target's frozen bf16
  * table, a device pointer that must outlive the context. */
 typedef struct {
-  kd_fp8_matrix fuse;            /* [hidden][taps*hidden] */
-  kd_fp8_matrix fc;              /* [hidden][2*hidden]: input [fused ; embedding] */
-  kd_fp8_matrix pred_a;          /* [rank][hidden] applied to the fused state */
-  kd_fp8_matrix pred_b;          /* [rank][hidden] applied to embed(predecessor) */
-  kd_fp8_matrix pred_u;          /* [hidden][rank] */
+  kd_matrix fuse;            /* [hidden][taps*hidden] */
+  kd_matrix fc;              /* [hidden][2*hidden]: input [fused ; embedding] */
+  kd_matrix pred_a;          /* [rank][hidden] applied to the fused state */
+  kd_matrix pred_b;          /* [rank][hidden] applied to embed(predecessor) */
+  kd_matrix pred_u;          /* [hidden][rank] */
   const float* mask_row;         /* [hidden] */
   kd_layer_weights layer[4];
   const float* final_norm;       /* [hidden] */
@@ -139,7 +153,7 @@ typedef struct {
   const void* head_bf16;
   /* head_quant = KD_QUANT_FP8_BLOCK64: the head slice in block-FP8,
    * [draft_vocab][hidden], as the body matrices. */
-  kd_fp8_matrix head_fp8;
+  kd_matrix head_fp8;
 } kd_weights;
 
 /* The context K/V cache (device), one K and one V tensor per layer. A

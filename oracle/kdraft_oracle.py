@@ -175,7 +175,15 @@ class OracleModel:
 
     def __init__(self, m: dict, decode_table: bool = False):
         self.dims = d = m["dims"]
-        W = lambda name: block_fp8(m[name + ".q"], m[name + ".s"])
+        # body matrices: block-FP8 (the card's serving format) or, as its Use
+        # section allows, NVFP4 or bf16
+        body = m.get("body_format", "fp8")
+        if body == "nvfp4":
+            W = lambda name: nvfp4(m[name + ".q4"], m[name + ".s4"], m[name + ".g"])
+        elif body == "bf16":
+            W = lambda name: decode_bf16(m[name + ".bf16"])
+        else:
+            W = lambda name: block_fp8(m[name + ".q"], m[name + ".s"])
         self.fuse = W("fuse")
         self.fc = W("fc")
         self.pred_a, self.pred_b, self.pred_u = W("pred_a"), W("pred_b"), W("pred_u")

@@ -134,18 +134,26 @@ def quant_nvfp4(w: torch.Tensor, g: float | None = None):
 # Model
 # ----------------------------------------------------------------------------
 
-def _fp8(model, name, rows, cols, device, base, zero=False):
+def _fp8(model, name, rows, cols, device, base, zero=False, body="fp8"):
+    """One body matrix, N(0, 0.02) (or zero), in the body format: block-FP8
+    (.q, .s), NVFP4 (.q4, .s4, .g, one tensor scale per matrix) or bf16
+    (.bf16, round to nearest even). Every format quantises the same draws."""
     if zero:
         w = torch.zeros(rows, cols, device=device)
     else:
         w = _normal((rows, cols), 0.02, device, base, name)
-    q, s = quant_block_fp8(w)
-    model[name + ".q"] = q
-    model[name + ".s"] = s
+    if body == "nvfp4":
+        model[name + ".q4"], model[name + ".s4"], model[name + ".g"] = quant_nvfp4(w)
+    elif body == "bf16":
+        model[name + ".bf16"] = w.to(torch.bfloat16).contiguous()
+    else:
+        q, s = quant_block_fp8(w)
+        model[name + ".q"] = q
+        model[name + ".s"] = s
 
 
 def make_model(dims: Dims = FULL, variant: str = "A", device="cpu", base: int = 0,
-               head: str = "nvfp4"):
+               head: str = "nvfp4", body: str = "fp8"):
     """Synthetic drafter weights.
 
     variant "A": predecessor and spine output projections U are zero (the
@@ -160,16 +168,18 @@ def make_model(dims: Dims = FULL, variant: str = "A", device="cpu", base: int = 
     head="bf16": the head slice is also given unquantised, head_bf16 = the
     table's bf16 rows at the draft vocabulary (head_format "bf16");
     head="fp8": also as block-FP8 of those rows (head_fp8.q / .s).
+    body="nvfp4" / "bf16": the body matrices in that format instead of
+    block-FP8 (body_format), quantised from the same draws.
     """
-    assert variant in ("A", "B", "C")
+    assert variant in ("A", "B", "C") and body in ("fp8", "nvfp4", "bf16")
     H, F, r, L = dims.hidden, dims.ffn, dims.rank, dims.layers
     zero_u = variant == "A"
-    m: dict = {"dims": dims, "variant": variant}
-    _fp8(m, "fuse", H, dims.taps * H, device, base)
-    _fp8(m, "fc", H, 2 * H, device, base)
-    _fp8(m, "pred_a", r, H, device, base)
-    _fp8(m, "pred_b", r, H, device, base)
-    _fp8(m, "pred_u", H, r, device, base, zero=zero_u)
+    m: dict = {"dims": dims, "variant": variant, "body_format": body}
+    _fp8(m, "fuse", H, dims.taps * H, device, base, body=body)
+    _fp8(m, "fc", H, 2 * H, device, base, body=body)
+    _fp8(m, "pred_a", r, H, device, base, body=body)
+    _fp8(m, "pred_b", r, H, device, base, body=body)
+    _fp8(m, "pred_u", H, r, device, base, zero=zero_u, body=body)
     m["mask"] = _normal((H,), 0.02, device, base, "mask")
 
     def gain(name):
@@ -183,12 +193,12 @@ def make_model(dims: Dims = FULL, variant: str = "A", device="cpu", base: int = 
         m[p + "ffn_norm"] = gain(p + "ffn_norm")
         for nm, (ro, co) in dict(wq=(H, H), wk=(H, H), wv=(H, H), wo=(H, H),
                                  w_gate=(F, H), w_up=(F, H), w_down=(H, F)).items():
-            _fp8(m, p + nm, ro, co, device, base)
+            _fp8(m, p + nm, ro, co, device, base, body=body)
         if l >= 1:
             sp = f"spine.{l}."
             m[sp + "norm"] = gain(sp + "norm")
-            _fp8(m, sp + "a", r, H, device, base)
-            _fp8(m, sp + "u", H, r, device, base, zero=zero_u)
+            _fp8(m, sp + "a", r, H, device, base, body=body)
+            _fp8(m, sp + "u", H, r, device, base, zero=zero_u, body=body)
     m["final_norm"] = gain("final_norm")
 
     table = _normal((dims.full_vocab, H), 0.02, device, base, "table").to(torch.bfloat16)
@@ -210,18 +220,25 @@ def make_model(dims: Dims = FULL, variant: str = "A", device="cpu", base: int = 
     return m
 
 
-def model_bytes(dims: Dims = FULL):
+def model_bytes(dims: Dims = FULL, body: str = "fp8"):
     """Bytes the round reads for weights: block-FP8 body (1 B per value + 4 B
-    per 64 values), NVFP4 head (0.5 B per value + 1 B per 16 + 4 B), fp32
-    vectors (mask row and gains)."""
+    per 64 values; NVFP4: 0.5 B per value + 1 B per 16 + 4 B per matrix;
+    bf16: 2 B per value), NVFP4 head (0.5 B per value + 1 B per 16 + 4 B),
+    fp32 vectors (mask row and gains)."""
     H, F, r, L, T = dims.hidden, dims.ffn, dims.rank, dims.layers, dims.taps
     vals = H * T * H + H * 2 * H + 2 * r * H + H * r
     vals += L * (4 * H * H + 3 * F * H)
     vals += (L - 1) * 2 * r * H
-    body = vals + vals // 64 * 4
+    mats = 5 + 7 * L + 2 * (L - 1)
+    if body == "nvfp4":
+        body_b = vals // 2 + vals // 16 + 4 * mats
+    elif body == "bf16":
+        body_b = 2 * vals
+    else:
+        body_b = vals + vals // 64 * 4
     head = dims.draft_vocab * H // 2 + dims.draft_vocab * H // 16 + 4
     vectors = 4 * H * (1 + 2 * L + (L - 1) + 1)
-    return dict(body=body, head=head, vectors=vectors)
+    return dict(body=body_b, head=head, vectors=vectors)
 
 
 # ----------------------------------------------------------------------------

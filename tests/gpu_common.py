@@ -37,14 +37,16 @@ class Harness:
     """A synthetic model on the GPU, loaded into one kd_ctx, plus its oracle."""
 
     def __init__(self, variant: str, max_streams: int = 256, window: int = 2048,
-                 head: str = "nvfp4"):
+                 head: str = "nvfp4", body: str = "fp8"):
         t0 = time.time()
         self.variant = variant
         self.head = head
-        self.model = synth.make_model(synth.FULL, variant, device="cuda", head=head)
+        self.body = body
+        self.model = synth.make_model(synth.FULL, variant, device="cuda", head=head, body=body)
         quant = {"nvfp4": kdraft.KD_QUANT_NVFP4, "bf16": kdraft.KD_QUANT_BF16,
-                 "fp8": kdraft.KD_QUANT_FP8_BLOCK64}[head]
-        self.drafter = kdraft.Drafter(max_streams=max_streams, window=window, head_quant=quant)
+                 "fp8": kdraft.KD_QUANT_FP8_BLOCK64}
+        self.drafter = kdraft.Drafter(max_streams=max_streams, window=window, head_quant=quant[head],
+                                      body_quant=quant[body])
         self.drafter.load_weights(self.model)
         self._oracle = None
         log(f"model {variant} ready in {time.time() - t0:.1f}s")

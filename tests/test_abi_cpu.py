@@ -59,15 +59,14 @@ def test_host_side_argument_errors(lib):
         assert lib.kd_create(ctypes.byref(cfg), None, ctypes.byref(h)) == kdraft.KD_ERR_UNSUPPORTED
     cfg = kdraft.default_config(head_quant=99)
     assert lib.kd_create(ctypes.byref(cfg), None, ctypes.byref(h)) == kdraft.KD_ERR_UNSUPPORTED
-    # the body is block-FP8 only; bf16 and NVFP4 bodies are not built
-    for body in (kdraft.KD_QUANT_BF16, kdraft.KD_QUANT_NVFP4):
-        cfg = kdraft.default_config(body_quant=body)
-        assert lib.kd_create(ctypes.byref(cfg), None, ctypes.byref(h)) == kdraft.KD_ERR_UNSUPPORTED
-    # every head slice format passes the format check (the window check
+    cfg = kdraft.default_config(body_quant=99)
+    assert lib.kd_create(ctypes.byref(cfg), None, ctypes.byref(h)) == kdraft.KD_ERR_UNSUPPORTED
+    # every body and head format passes the format check (the window check
     # below still rejects this config before any device work)
-    for head in (kdraft.KD_QUANT_NVFP4, kdraft.KD_QUANT_BF16, kdraft.KD_QUANT_FP8_BLOCK64):
-        cfg = kdraft.default_config(head_quant=head, window=0)
-        assert lib.kd_create(ctypes.byref(cfg), None, ctypes.byref(h)) == kdraft.KD_ERR_ARG
+    for body in (kdraft.KD_QUANT_FP8_BLOCK64, kdraft.KD_QUANT_BF16, kdraft.KD_QUANT_NVFP4):
+        for head in (kdraft.KD_QUANT_NVFP4, kdraft.KD_QUANT_BF16, kdraft.KD_QUANT_FP8_BLOCK64):
+            cfg = kdraft.default_config(body_quant=body, head_quant=head, window=0)
+            assert lib.kd_create(ctypes.byref(cfg), None, ctypes.byref(h)) == kdraft.KD_ERR_ARG
     cfg = kdraft.default_config(window=0)
     assert lib.kd_create(ctypes.byref(cfg), None, ctypes.byref(h)) == kdraft.KD_ERR_ARG
     cfg = kdraft.default_config(max_streams=1 << 30)

@@ -241,3 +241,42 @@ def test_fp8_head_decodes_the_block_fp8_rows():
     s = np.repeat(np.asarray(mnp["head_fp8.s"], dtype=np.float64), 64, axis=1)
     assert np.all(np.abs(M.head - full) <= np.abs(full) * 2.0 ** -4 + s * 2.0 ** -10 + 1e-15)
     assert not np.array_equal(M.head, full)
+
+
+def test_body_formats_agree_where_all_three_are_exact():
+    """The card's Use section allows FP8, NVFP4 and bf16 bodies. With weights
+    every format holds exactly (an e2m1 value times a power-of-two scale per 16
+    inputs times a power of two per matrix), the three decodes are the same
+    matrices, so the rounds are identical in fp64. Block scales that vary
+    every 16 inputs and tensor scales that vary by matrix make a wrong nibble
+    order, scale repeat or dropped tensor scale show up."""
+    base = synth.to_numpy_model(synth.make_model(D, "C"))
+    rng = np.random.default_rng(5)
+    mags = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    models = {f: dict(base, body_format=f) for f in ("fp8", "nvfp4", "bf16")}
+    names = [k[:-2] for k in base if k.endswith(".q") and not k.startswith("head")]
+    assert len(names) == 5 + 7 * D.layers + 2 * (D.layers - 1)
+    e4m3 = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+    for name in names:
+        rows, cols = base[name + ".q"].shape
+        codes = rng.integers(0, 16, (rows, cols)).astype(np.uint8)
+        val = np.where(codes >= 8, -1.0, 1.0) * mags[codes & 7]
+        blk = np.exp2(rng.integers(-1, 3, (rows, cols // 16)).astype(np.float64))
+        g = float(np.exp2(rng.integers(-9, -5)))
+        w = val * np.repeat(blk, 16, axis=1) * g
+        models["fp8"][name + ".q"] = e4m3(val * np.repeat(blk, 16, axis=1))
+        models["fp8"][name + ".s"] = np.full((rows, cols // 64), g, dtype=np.float32)
+        models["nvfp4"][name + ".q4"] = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+        models["nvfp4"][name + ".s4"] = e4m3(blk)
+        models["nvfp4"][name + ".g"] = g
+        models["bf16"][name + ".bf16"] = synth.bf16_bits(torch.from_numpy(w)).numpy().view(np.uint16)
+    inp = synth.to_numpy_inputs(synth.make_inputs(CFG, D, vocab=torch.from_numpy(base["vocab"])))
+    out = {f: oracle.oracle_round(oracle.OracleModel(m), inp) for f, m in models.items()}
+    Ms = {f: oracle.OracleModel(m) for f, m in models.items()}
+    assert np.array_equal(Ms["fp8"].fuse, Ms["nvfp4"].fuse) and np.array_equal(Ms["fp8"].fuse, Ms["bf16"].fuse)
+    for f in ("nvfp4", "bf16"):
+        assert np.array_equal(out[f][0], out["fp8"][0]), f
+        assert np.array_equal(out[f][1], out["fp8"][1]), f
+    # and the weights are not trivially shared: the decoded matrices differ from the model's own
+    assert not np.array_equal(Ms["fp8"].fuse, oracle.OracleModel(base).fuse)
