@@ -536,6 +536,7 @@ const char* kd_status_string(kd_status s) {
     case KD_ERR_OOM: return "out of device memory";
     case KD_ERR_HIP: return "HIP runtime error";
     case KD_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KD_ERR_RANGE: return "an activation left the f16 range";
   }
   return "unknown status";
 }
@@ -611,7 +612,7 @@ kd_status kd_create(const kd_config* cfg, void* hip_stream, kd_ctx** out) {
   ok = ok && c->stager.init(sizeof(kd::SmallArgs)) &&
        hipHostMalloc((void**)&c->status_host, 64, hipHostMallocMapped | hipHostMallocCoherent) == hipSuccess &&
        hipHostGetDevicePointer((void**)&c->status_dev, c->status_host, 0) == hipSuccess;
-  if (ok) *c->status_host = 0u;
+  if (ok) c->status_host[0] = c->status_host[1] = 0u;
   if (!ok) {
     free_all(c->work_allocs);
     c->stager.destroy();
@@ -846,11 +847,18 @@ kd_status kd_load_weights(kd_ctx* c, const kd_weights* wt) {
 // `depth` rounds; round r > 0 reads its predecessor ids from out_ids (the
 // previous round's drafts, 4 per stream).
 // A bounded device wait of an earlier call timed out (its rounds wrote -2 ids).
+// The status words earlier rounds left in mapped host memory: [0] a bounded
+// wait timed out, [1] an f16 activation store saturated. Each is read and
+// cleared once.
 static kd_status take_device_status(kd_ctx* c) {
-  if (c->status_host && __atomic_load_n(c->status_host, __ATOMIC_ACQUIRE) != 0u) {
-    __atomic_store_n(c->status_host, 0u, __ATOMIC_RELEASE);
-    return fail(c, KD_ERR_HIP, "a device wait of an earlier round timed out; that round wrote -2 ids");
-  }
+  if (!c->status_host) return KD_OK;
+  const unsigned timeout = __atomic_exchange_n(&c->status_host[0], 0u, __ATOMIC_ACQ_REL);
+  const unsigned range = __atomic_exchange_n(&c->status_host[1], 0u, __ATOMIC_ACQ_REL);
+  if (timeout) return fail(c, KD_ERR_HIP, "a device wait of an earlier round timed out; that round wrote -2 ids");
+  if (range)
+    return fail(c, KD_ERR_RANGE,
+                "an earlier round stored an f16 activation beyond +-65504 or not finite (stored saturated); "
+                "its drafts are unreliable");
   return KD_OK;
 }
 
@@ -1008,7 +1016,7 @@ static kd_status round_impl(kd_ctx* c, int depth, int B, const void* taps, const
       }
       if (nl == 0) kd::launch_norm_rows(st, w.x, R, d.final_norm, eps, w.af_x);
       kd::launch_head(st, w, d, R, r + 1 == depth ? out_logits : nullptr);
-      kd::launch_finalize(st, w, d, R, out_ids, anchor, pred_r, pred_stride);
+      kd::launch_finalize(st, w, d, R, out_ids, anchor, pred_r, pred_stride, c->status_dev + 1);
     }
   };
   std::vector<unsigned char> key;

@@ -234,11 +234,32 @@ __device__ __forceinline__ size_t afrag_off(int row, int k, int KT) {
   return (size_t)(mt * KT + t) * 512 + lane * 8 + (k & 7);
 }
 
+// f16 range of activation stores. A value beyond the largest finite f16
+// (65504) or not finite is stored saturated (NaN as +65504) and sets this
+// translation unit's flag; the round's last kernel moves the flag into the
+// context's host-visible range word, which the next call reports.
+static __device__ unsigned g_f16_range = 0u;
+__device__ __forceinline__ _Float16 f16_checked(float v) {
+  if (!(fabsf(v) <= 65504.0f)) {
+    __hip_atomic_fetch_or(&g_f16_range, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    v = v < 0.0f ? -65504.0f : 65504.0f;
+  }
+  return (_Float16)v;
+}
+// Moves this translation unit's f16 range flag into *range_word (one thread;
+// a plain store, no read-modify-write on host memory).
+__device__ __forceinline__ void flush_f16_range(unsigned* range_word) {
+  if (__hip_atomic_load(&g_f16_range, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+    __hip_atomic_store(&g_f16_range, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (range_word) __hip_atomic_store(range_word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+}
+
 // Stores 8 consecutive fp32 values X[row][k0..k0+8) (k0 % 8 == 0) as f16.
 __device__ __forceinline__ void store_afrag8(uint16_t* af, int KT, int row, int k0, const float* v) {
   f16x8 h;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) h[i] = (_Float16)v[i];
+  for (int i = 0; i < 8; ++i) h[i] = f16_checked(v[i]);
   *reinterpret_cast<f16x8*>(af + afrag_off(row, k0, KT)) = h;
 }
 

@@ -487,7 +487,7 @@ __device__ __forceinline__ void attn_merge(const AttnK& a, AttnLds& s, float m_r
     }
     if (a.S == 1) {
       const float out = attn_block_merge(s.blk, a.vb, qrow0, j, d, M, L, O);
-      a.af_o[afrag_off(b * BLK + j, h * DH + d, H / 32)] = __builtin_bit_cast(uint16_t, (_Float16)out);
+      a.af_o[afrag_off(b * BLK + j, h * DH + d, H / 32)] = __builtin_bit_cast(uint16_t, f16_checked(out));
     } else {
       const size_t pb = ((size_t)(b * NH + h) * a.nch + seg) * BLK + j;
       a.po[pb * DH + d] = O;
@@ -951,7 +951,7 @@ __global__ __launch_bounds__(128) void k_attn_combine(const float* q, const floa
     }
     t += j + 1;
     const float out = O / L;
-    af_o[afrag_off(b * BLK + j, h * DH + d, H / 32)] = __builtin_bit_cast(uint16_t, (_Float16)out);
+    af_o[afrag_off(b * BLK + j, h * DH + d, H / 32)] = __builtin_bit_cast(uint16_t, f16_checked(out));
   }
 }
 
@@ -1177,8 +1177,9 @@ void launch_head(hipStream_t st, const Work& w, const DevWeights& d, int R, floa
 
 __global__ void k_finalize(const unsigned long long* keys, const int32_t* vocab, int R,
                            int32_t* out, const int32_t* anchor, const int32_t* pred,
-                           int pred_stride, int V) {
+                           int pred_stride, int V, unsigned* range_word) {
   const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r == 0) flush_f16_range(range_word);   // the round's (and earlier ingests') f16 stores are done
   if (r >= R) return;
   const unsigned long long k = keys[r];
   const bool ok = id_row_valid(anchor, pred, pred_stride, r / BLK, r % BLK, V);
@@ -1186,9 +1187,9 @@ __global__ void k_finalize(const unsigned long long* keys, const int32_t* vocab,
 }
 
 void launch_finalize(hipStream_t st, const Work& w, const DevWeights& d, int R, int32_t* out_ids,
-                     const int32_t* anchor, const int32_t* pred, int pred_stride) {
+                     const int32_t* anchor, const int32_t* pred, int pred_stride, unsigned* range_word) {
   k_finalize<<<(R + 255) / 256, 256, 0, st>>>(w.keys, d.vocab, R, out_ids, anchor, pred, pred_stride,
-                                               d.V);
+                                               d.V, range_word);
 }
 
 // ---------------------------------------------------------------------------
@@ -1329,7 +1330,7 @@ __device__ __forceinline__ float wave_max(float v) {
 __device__ __forceinline__ void store_row_q4(float x0, float x1, int lane, uint8_t* codes,
                                              uint32_t* so) {
   const float mn = wave_min(fminf(x0, x1)), mx = wave_max(fmaxf(x0, x1));
-  const _Float16 sc_h = (_Float16)((mx - mn) / 15.0f), of_h = (_Float16)mn;
+  const _Float16 sc_h = f16_checked((mx - mn) / 15.0f), of_h = f16_checked(mn);
   const float sc = (float)sc_h, of = (float)of_h;
   auto code = [&](float x) -> uint32_t {
     if (!(sc > 0.f)) return 0u;

@@ -139,8 +139,10 @@ void launch_swiglu(hipStream_t st, const Work& w, int R, int splits);
 void launch_head(hipStream_t st, const Work& w, const DevWeights& d, int R, float* logits);
 // Writes out_ids; a row whose anchor or earlier predecessor ids lie outside
 // the table (see id_row_valid) gets -1.
+// range_word: host-visible word set to 1 when an f16 activation store of
+// this round (or of an ingest since the last round) saturated.
 void launch_finalize(hipStream_t st, const Work& w, const DevWeights& d, int R, int32_t* out_ids,
-                     const int32_t* anchor, const int32_t* pred, int pred_stride);
+                     const int32_t* anchor, const int32_t* pred, int pred_stride, unsigned* range_word);
 // ingest
 void launch_ingest_prep(hipStream_t st, const Work& w, int rows, const uint16_t* taps);
 void launch_ingest_post_fuse(hipStream_t st, const Work& w, const DevWeights& d, int rows,

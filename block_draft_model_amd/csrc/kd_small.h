@@ -68,8 +68,9 @@ struct SmallArgsT {
   P<float> out_logits;
   DevWeightsT<P> d;
   SmallBufsT<P> s;
-  // Host-visible status word (mapped pinned memory): set to 1 when a bounded
-  // wait of the round timed out.
+  // Host-visible status words (mapped pinned memory): [0] set to 1 when a
+  // bounded wait of the round timed out, [1] when an f16 activation store
+  // saturated.
   P<unsigned> status;
   // Optional stage timestamps (100 MHz wall clock), [phase slot][G][8]; null = off.
   P<unsigned long long> trace;

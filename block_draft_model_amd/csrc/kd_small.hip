@@ -88,7 +88,7 @@ __device__ __forceinline__ void st_wt(gptr<float> p, float v) {
 }
 // f16 bits of v (round to nearest even), written through like st_wt.
 __device__ __forceinline__ void st_wt_h(gptr<uint16_t> p, float v) {
-  __hip_atomic_store(p, __builtin_bit_cast(uint16_t, (_Float16)v), __ATOMIC_RELAXED,
+  __hip_atomic_store(p, __builtin_bit_cast(uint16_t, f16_checked(v)), __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void st_wt64(gptr<unsigned long long> p, unsigned long long v) {
@@ -1676,6 +1676,8 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_head(Args& a_, lds
   const bool failed = ld_rlx(&s.bar[18 * 32]) != 0u;
   if (failed && t == 0 && a.status)
     __hip_atomic_store(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  // every workgroup's f16 stores of the round are done: status[1] is the range word
+  if (t == 0) flush_f16_range(a.status ? a.status + 1 : nullptr);
   if (r < R && l32 == 0) {
     const bool ok = id_row_valid(a.anchor, a.pred, a.pred_stride, r / BLK, r % BLK, d.V);
     a.out_ids[r] = failed ? -2 : (k && ok ? d.vocab[0xffffffffu - (uint32_t)(k & 0xffffffffu)] : -1);

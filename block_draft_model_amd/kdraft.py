@@ -14,7 +14,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkdraft.so")
 
-KD_OK, KD_ERR_ARG, KD_ERR_STATE, KD_ERR_OOM, KD_ERR_HIP, KD_ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5
+KD_OK, KD_ERR_ARG, KD_ERR_STATE, KD_ERR_OOM, KD_ERR_HIP, KD_ERR_UNSUPPORTED, KD_ERR_RANGE = 0, -1, -2, -3, -4, -5, -6
 KD_QUANT_FP8_BLOCK64, KD_QUANT_NVFP4, KD_QUANT_BF16 = 1, 2, 3
 KD_MAX_INGEST = 8
 

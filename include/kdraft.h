@@ -55,7 +55,14 @@ typedef enum {
   KD_ERR_STATE = -2,       /* e.g. kd_round before kd_load_weights */
   KD_ERR_OOM = -3,         /* device allocation failed (create / load only) */
   KD_ERR_HIP = -4,         /* a HIP runtime call failed */
-  KD_ERR_UNSUPPORTED = -5  /* a shape or format this build does not implement */
+  KD_ERR_UNSUPPORTED = -5, /* a shape or format this build does not implement */
+  KD_ERR_RANGE = -6        /* an earlier round (or ingest) stored an activation beyond the
+                              f16 range (+-65504) or not finite; it was stored saturated
+                              and that round's drafts are unreliable. Returned once by the
+                              next kd_round / kd_round_depth / kd_ingest, which then does
+                              nothing else. The flag is kept per device: with several
+                              contexts on one device, the next round of any of them may
+                              report it. */
 } kd_status;
 
 enum { KD_QUANT_FP8_BLOCK64 = 1, KD_QUANT_NVFP4 = 2, KD_QUANT_BF16 = 3 };

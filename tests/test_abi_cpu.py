@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for s in (0, -1, -2, -3, -4, -5):
+    for s in (0, -1, -2, -3, -4, -5, -6):
         assert kdraft.status_string(s) not in ("", "unknown status")
     assert kdraft.status_string(-99) == "unknown status"
 
