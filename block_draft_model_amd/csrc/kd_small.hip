@@ -875,33 +875,21 @@ __device__ __attribute__((noinline, not_tail_called)) BlockPart attn_block(Block
 }
 
 // Merge of the partials of one (stream, head) with the block's part; thread
-// (j, d). The partials are those of the segments of its chunks that the
-// workgroups' ranges cut out, each stored at the slot of its first chunk; u0
-// is the pair's first unit and U all units.
+// (j, d). Each of the pair's chunks stored its own partial at its slot.
 __device__ __attribute__((noinline, not_tail_called)) void attn_merge(Args& a_, int l_, int b_, int h_, int n_,
-                                                     int u0_, int U_, BlockPart bp) {
+                                                     BlockPart bp) {
   const auto l = uni(l_);
   const auto b = uni(b_);
   const auto h = uni(h_);
   const auto n = uni(n_);
-  const auto u0 = uni(u0_);
-  const auto U = uni(U_);
   Args& a = uni(a_);
   auto& s = a.s;
-  const int G = gridDim.x;
   const int nch = a.nch;
+  // every chunk of the pair stored its own partial: they are merged in chunk
+  // order, which depends only on the stream's length, never on the batch
   const int nc = (n + ATT_CH - 1) / ATT_CH;
-  // segments: with at least as many units as workgroups every range is
-  // non-empty, and the pair's segments are those of workgroups owner(u0) ..
-  // owner(u0 + nc - 1), segment k starting at chunk max(start(w0 + k), u0) - u0;
-  // with fewer, a range holds at most one unit and every chunk is a segment
-  const bool one_each = U < G;
-  int w0 = 0, nseg = 0;
-  if (nc > 0) {
-    w0 = ((u0 + 1) * G - 1) / U;
-    nseg = one_each ? nc : ((u0 + nc) * G - 1) / U - w0 + 1;
-  }
-  auto seg_chunk = [&](int k) { return one_each ? k : max(((w0 + k) * U) / G, u0) - u0; };
+  const int nseg = nc;
+  auto seg_chunk = [&](int k) { return k; };
   const int j = threadIdx.x >> 7, dd = threadIdx.x & 127;
   const int lane = threadIdx.x & 63;
   constexpr int MAXS = 16;
@@ -1189,9 +1177,12 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
   for (int u = ub; u < ue; ++u, slot ^= 1) {
     int b, c, h;
     sl.unit(u, b, c, h);
-    const int n = sl.vis(b), nc = sl.chunks(b);
-    const bool seg_start = u == ub || c == 0;
-    const bool seg_end = u + 1 == ue || c == nc - 1;
+    const int n = sl.vis(b);
+    // every chunk is a segment of its own: its partial is stored and merged
+    // later in chunk order, so a stream's result does not depend on how the
+    // batch's chunks fall to workgroups. The queries are read again only when
+    // the (stream, head) pair changes.
+    const bool new_pair = u == ub || c == 0;
     // Vector memory operations issued after this unit's copies, which its
     // wait lets stay in flight: the next unit's copies (8 per wave, 10 for
     // wave 0 with its query blocks; in the persistent kernel wave 0's first
@@ -1203,7 +1194,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
     const int nwait = !next ? 0 : (wave_s != 0 ? 8 : (sync && u == ub ? 2 : 10)) + stores;
     att_wait_vm(uni(nwait));
     stores = 0;
-    if (seg_start) {
+    if (new_pair) {
       // wave 0's query copy has landed for every wave; the previous
       // segment's readers of the shared LDS areas are done
       lds_sync();
@@ -1222,14 +1213,14 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
         }
         split_bf16(qv, qh[kb], ql[kb]);
       }
-      m_run = -__builtin_inff();
-      l_run = 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
-      seg_c0 = c;
     }
+    m_run = -__builtin_inff();
+    l_run = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
+    seg_c0 = c;
     u32x4 kr[4], vr[4];
     att_read_kv(ring0 + slot * ATT_SLOT_BYTES + wave * ATT_WAVE_BLOCKS * 1024 + lane * 16, kr, vr);
     if (u == ub) trace_mark(a, sy, 3);
@@ -1300,7 +1291,10 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
         for (int e = 0; e < 8; ++e) o[j][e] += pj[j][t] * vf[e];
     }
 
-    if (seg_end) {
+    {
+      // the previous chunk's readers of the shared LDS areas are done (a new
+      // pair's query read above waited for them already)
+      if (!new_pair) lds_sync();
       // sum the 4 key groups: groups g and g^2 exchange, g < 2 keeping rows
       // 0, 1 and g >= 2 rows 2, 3; then g and g^1, odd groups keeping the
       // second of their rows -- group g ends with row g
@@ -1351,7 +1345,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
         att_store(s.al[l] + pb, Ls);
       }
       stores = 3;
-      // the next segment starts with a barrier before the LDS areas are reused
+      // the next chunk waits at a barrier before it reuses the LDS areas
     }
   }
   // completion counters: one per (stream, head) and layer, counting the
@@ -1399,7 +1393,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
       }
       lds_sync();
     }
-    attn_merge(a, l, b, h, n, u0, U, bp);
+    attn_merge(a, l, b, h, n, bp);
   }
   trace_mark(a, sy, 6);
   trace_mark(a, sy, 4);
