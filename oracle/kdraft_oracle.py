@@ -243,7 +243,7 @@ def _context_kv(M: OracleModel, inp: dict, l: int, b: int, slots):
 
 
 def oracle_round(M: OracleModel, inp: dict, block: int | None = None,
-                 spine: bool = True, return_hidden: bool = False):
+                 spine: bool = True, return_hidden: bool = False, act=None):
     """One round for every stream; returns (logits [B][rows][VD], ids [B][rows]).
 
     Steps in the order of the model card's "Architecture" section:
@@ -254,7 +254,11 @@ def oracle_round(M: OracleModel, inp: dict, block: int | None = None,
       Output: RMSNorm -> head restricted to the draft vocabulary -> argmax.
     ``block`` < 4 runs a shorter block (block=1 is the chain-drafter row alone);
     ``spine=False`` zeroes the spine's contribution.
+    ``act``: a function applied to every input of a weight product before it
+    (a model of an activation number format, for precision studies); None
+    keeps them exact.
     """
+    q_ = (lambda t: t) if act is None else act
     d = M.dims
     R = d.block if block is None else block
     B = int(inp["streams"])
@@ -265,23 +269,23 @@ def oracle_round(M: OracleModel, inp: dict, block: int | None = None,
     lens = np.asarray(inp["lens"]).reshape(B)
 
     # Input: tap fuse, then the anchor row in the EAGLE-3 context-row form.
-    f = taps @ M.fuse.T                                               # [B][H]
+    f = q_(taps) @ M.fuse.T                                           # [B][H]
     x = np.zeros((B, R, H))
-    x[:, 0] = np.concatenate([f, M.embed(anchor)], axis=1) @ M.fc.T
+    x[:, 0] = q_(np.concatenate([f, M.embed(anchor)], axis=1)) @ M.fc.T
     # Positions 2-4: mask row + anchor's fused state + predecessor term.
     for j in range(1, R):
-        u = f @ M.pred_a.T + M.embed(pred[:, j - 1]) @ M.pred_b.T
-        x[:, j] = M.mask + f + silu(u) @ M.pred_u.T
+        u = q_(f) @ M.pred_a.T + q_(M.embed(pred[:, j - 1])) @ M.pred_b.T
+        x[:, j] = M.mask + f + q_(silu(u)) @ M.pred_u.T
 
     pos_blk = lens[:, None] + np.arange(R)[None, :]                   # [B][R]
     for l, L in enumerate(M.layers):
         if l >= 1 and spine:
             # Spine: row j reads row j-1 of the layer input (simultaneous update).
             src = x[:, : R - 1]
-            add = silu(rmsnorm(src, L["spine_norm"], d.rms_eps) @ L["spine_a"].T) @ L["spine_u"].T
+            add = q_(silu(q_(rmsnorm(src, L["spine_norm"], d.rms_eps)) @ L["spine_a"].T)) @ L["spine_u"].T
             x = x.copy()
             x[:, 1:] += add
-        a = rmsnorm(x, L["attn_norm"], d.rms_eps)
+        a = q_(rmsnorm(x, L["attn_norm"], d.rms_eps))
         q = (a @ L["wq"].T).reshape(B, R, NH, Dh)
         k = (a @ L["wk"].T).reshape(B, R, NH, Dh)
         v = (a @ L["wv"].T).reshape(B, R, NH, Dh)
@@ -292,12 +296,12 @@ def oracle_round(M: OracleModel, inp: dict, block: int | None = None,
             _, slots = _visible(lens[b], d)
             kc, vc = _context_kv(M, inp, l, b, slots)
             o[b] = attention(q[b], kc, vc, k[b], v[b])
-        x = x + o.reshape(B, R, H) @ L["wo"].T
-        c = rmsnorm(x, L["ffn_norm"], d.rms_eps)
-        x = x + (silu(c @ L["w_gate"].T) * (c @ L["w_up"].T)) @ L["w_down"].T
+        x = x + q_(o.reshape(B, R, H)) @ L["wo"].T
+        c = q_(rmsnorm(x, L["ffn_norm"], d.rms_eps))
+        x = x + q_(silu(c @ L["w_gate"].T) * (c @ L["w_up"].T)) @ L["w_down"].T
 
     z = rmsnorm(x, M.final_norm, d.rms_eps)
-    logits = z @ M.head.T                                             # [B][R][VD]
+    logits = q_(z) @ M.head.T                                         # [B][R][VD]
     masked = np.where(np.isfinite(logits), logits, -np.inf)
     best = np.argmax(masked, axis=-1)                                 # first maximum
     ok = np.isfinite(masked.max(axis=-1))
