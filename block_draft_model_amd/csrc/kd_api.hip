@@ -69,6 +69,7 @@ struct kd_ctx {
   std::vector<void*> weight_allocs;
   bool loaded = false;
   int debug_layers = -1;
+  int fused_proj = 1;        // general path above 32 rows: q|k|v and gate|up epilogues fused
   int last_streams = 0;
   int last_path = 0;
   std::string err;
@@ -969,6 +970,8 @@ static kd_status round_impl(kd_ctx* c, int depth, int B, const void* taps, const
   float* partA = w.part;
   float* partB = w.part + w.part_elems / 2;
   const int nl = c->debug_layers < 0 ? kd::NL : c->debug_layers;
+  // more than two row tiles: q|k|v and gate|up run with their epilogues fused
+  const bool fused = R > 32 && c->fused_proj;
   (void)hipGetLastError();
   auto enqueue = [&](hipStream_t st) {
     for (int r = 0; r < depth; ++r) {
@@ -997,16 +1000,35 @@ static kd_status round_impl(kd_ctx* c, int depth, int B, const void* taps, const
           kd::launch_gemm(st, w.af_rank, B3, L.su, 0, L.su.N, partA, s_su);
           kd::launch_spine_add_norm(st, w, B, s_su, L.attn_norm, eps);
         }
-        const int s_qkv = kd::gemm_splits(L.qkv.K, L.qkv.N, R);
-        kd::launch_gemm(st, w.af_x, R, L.qkv, 0, L.qkv.N, partA, s_qkv);
-        kd::launch_qkv_post(st, w, B, s_qkv);
+        if (fused) {
+          // one split, RoPE in the projection's epilogue
+          kd::ProjEpi e;
+          e.kind = kd::PE_QKV;
+          e.rope = w.rope;
+          e.q = w.q;
+          e.kb = w.kb;
+          e.vb = w.vb;
+          kd::launch_proj(st, w.af_x, R, L.qkv, e);
+        } else {
+          const int s_qkv = kd::gemm_splits(L.qkv.K, L.qkv.N, R);
+          kd::launch_gemm(st, w.af_x, R, L.qkv, 0, L.qkv.N, partA, s_qkv);
+          kd::launch_qkv_post(st, w, B, s_qkv);
+        }
         kd::launch_attention(st, w, d, B, k, l, lens, c->cfg.window);
         const int s_o = kd::gemm_splits(L.wo.K, L.wo.N, R);
         kd::launch_gemm(st, w.af_o, R, L.wo, 0, L.wo.N, partA, s_o);
         kd::launch_resid_norm(st, w, R, s_o, L.ffn_norm, eps, w.af_x, 0);
-        const int s_gu = kd::gemm_splits(L.gu.K, L.gu.N, R);
-        kd::launch_gemm(st, w.af_x, R, L.gu, 0, L.gu.N, partA, s_gu);
-        kd::launch_swiglu(st, w, R, s_gu);
+        if (fused) {
+          // one split, SwiGLU in the projection's epilogue
+          kd::ProjEpi e;
+          e.kind = kd::PE_SWIGLU;
+          e.af = w.af_h;
+          kd::launch_proj(st, w.af_x, R, L.gu, e);
+        } else {
+          const int s_gu = kd::gemm_splits(L.gu.K, L.gu.N, R);
+          kd::launch_gemm(st, w.af_x, R, L.gu, 0, L.gu.N, partA, s_gu);
+          kd::launch_swiglu(st, w, R, s_gu);
+        }
         const int s_d = kd::gemm_splits(L.down.K, L.down.N, R);
         kd::launch_gemm(st, w.af_h, R, L.down, 0, L.down.N, partA, s_d);
         if (l + 1 < nl)
@@ -1246,6 +1268,12 @@ kd_status kd_debug_set_path(kd_ctx* c, int path) {
     return fail(c, KD_ERR_UNSUPPORTED, "the window is too long for the small-batch path");
   if (path == 3 && !c->mega_ok) return fail(c, KD_ERR_UNSUPPORTED, "no cooperative launch");
   c->path = path;
+  return KD_OK;
+}
+
+kd_status kd_debug_set_fused(kd_ctx* c, int on) {
+  if (!c) return KD_ERR_ARG;
+  c->fused_proj = on ? 1 : 0;
   return KD_OK;
 }
 

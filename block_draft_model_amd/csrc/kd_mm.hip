@@ -73,22 +73,22 @@ struct GemmMM {
   int splits, kbs;
 };
 
+// The projection's main loop for one (row block rb, column block cb, split
+// sp): acc[r][c] = sum over the split's 64-input steps of the row tile r x
+// column tile c products (each block-FP8 or NVFP4 step's partial sum times
+// its scale). sa: the workgroup's double-buffered activation tile in LDS.
 template <int CT, int D, int WF>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_mm(GemmMM g) {
+__device__ __forceinline__ void mm_accumulate(const GemmMM& g, int rb, int cb, int sp,
+                                              f32x4 (&acc)[MM_RT][CT], u32x4 (*sa)[MM_RT * 2][64]) {
   constexpr int COLS = 16 * CT * MM_WAVES;
-  // [buffer][row tile][k tile t, t+1][lane]
-  __shared__ __attribute__((aligned(16))) u32x4 sa[2][MM_RT * 2][64];
-  const int RB = (g.R + 63) / 64, CB = g.N / COLS;
-  const MmMap m = mm_map(RB, CB, g.splits);
-  if (!m.ok) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int MT = mtiles(g.R);
-  const int b0 = m.sp * g.kbs, nb = g.kbs;
+  const int b0 = sp * g.kbs, nb = g.kbs;
   // wave w stages row tile rb*4 + w (clamped: a tile past the last repeats it,
   // and its output rows are past R and discarded)
-  const int mt_ld = min(m.rb * MM_RT + wave, MT - 1);
+  const int mt_ld = min(rb * MM_RT + wave, MT - 1);
   const uint16_t* ap = g.af + ((size_t)mt_ld * g.KT + 2 * b0) * 512 + lane * 8;
-  const int nt0 = g.n_off + m.cb * (COLS / 16) + wave * CT;
+  const int nt0 = g.n_off + cb * (COLS / 16) + wave * CT;
   const float* spp = g.s + ((size_t)nt0 * g.KB + b0) * 16 + (lane & 15);
   const size_t st_stride = (size_t)g.KB * 16;
   float gt[CT][2];   // NVFP4: the columns' tensor scales before / from the split block
@@ -101,7 +101,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
   }
 
-  f32x4 acc[MM_RT][CT];
 #pragma unroll
   for (int r = 0; r < MM_RT; ++r)
 #pragma unroll
@@ -168,6 +167,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       }
     }
   }
+}
+
+template <int CT, int D, int WF>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_mm(GemmMM g) {
+  constexpr int COLS = 16 * CT * MM_WAVES;
+  // [buffer][row tile][k tile t, t+1][lane]
+  __shared__ __attribute__((aligned(16))) u32x4 sa[2][MM_RT * 2][64];
+  const int RB = (g.R + 63) / 64, CB = g.N / COLS;
+  const MmMap m = mm_map(RB, CB, g.splits);
+  if (!m.ok) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  f32x4 acc[MM_RT][CT];
+  mm_accumulate<CT, D, WF>(g, m.rb, m.cb, m.sp, acc, sa);
 
   float* out = g.part + (size_t)m.sp * g.R * g.N;
 #pragma unroll
@@ -226,6 +238,103 @@ void launch_gemm_mm(hipStream_t st, const uint16_t* af, int R, const WMat& W, in
     default:
       if (wide) k_gemm_mm<4, 2, WF_FP8><<<grid, 256, 0, st>>>(g);
       else k_gemm_mm<1, 4, WF_FP8><<<grid, 256, 0, st>>>(g);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Projections with their epilogue fused (model card "Kolibri-1 block
+// drafter", section Architecture: Body; every stream's block rows in one
+// batched pass): q|k|v followed by RoPE on q and k, and gate|up followed by
+// SwiGLU. The main loop is k_gemm_mm's over the whole input range (one split,
+// so no partial sums leave the workgroup); the workgroup stages its output
+// tile in LDS and applies the epilogue per 16-column tile, which holds the
+// RoPE partners (d, d + 64) or a gate row block and its up rows.
+// ---------------------------------------------------------------------------
+template <int CT, int D, int WF>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_proj(GemmMM g, ProjEpi e) {
+  constexpr int COLS = 16 * CT * MM_WAVES;
+  constexpr int TP = COLS + 4;                        // LDS row pitch of the staged tile (floats)
+  constexpr int SA_BYTES = 2 * MM_RT * 2 * 64 * 16;
+  constexpr int T_BYTES = 64 * TP * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[SA_BYTES > T_BYTES ? SA_BYTES : T_BYTES];
+  auto sa = reinterpret_cast<u32x4(*)[MM_RT * 2][64]>(lds);
+  float* T = reinterpret_cast<float*>(lds);
+  const int RB = (g.R + 63) / 64, CB = g.N / COLS;
+  const MmMap m = mm_map(RB, CB, 1);
+  if (!m.ok) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  f32x4 acc[MM_RT][CT];
+  mm_accumulate<CT, D, WF>(g, m.rb, m.cb, 0, acc, sa);   // ends at a barrier: LDS is free
+#pragma unroll
+  for (int r = 0; r < MM_RT; ++r)
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        T[(r * 16 + 4 * (lane >> 4) + q) * TP + (wave * CT + c) * 16 + (lane & 15)] = acc[r][c][q];
+  __syncthreads();
+  // items: (row, 16-column tile)
+  constexpr int NT = COLS / 16;
+  for (int it = threadIdx.x; it < 64 * NT; it += 256) {
+    const int rl = it / NT, ti = it - rl * NT, row = m.rb * 64 + rl;
+    if (row >= g.R) continue;
+    const float* tp = T + rl * TP + ti * 16;
+    const int tg = m.cb * NT + ti;
+    if (e.kind == PE_SWIGLU) {
+      float h[8];
+#pragma unroll
+      for (int n = 0; n < 8; ++n) h[n] = silu(tp[n]) * tp[8 + n];
+      store_afrag8(e.af, FF / 32, row, 8 * tg, h);
+    } else {
+      const int nat = qkv_natural(tg * 16), sec = nat / H, c = nat - sec * H;
+      float* dst = (sec == 0 ? e.q : sec == 1 ? e.kb : e.vb) + (size_t)row * H + c;
+      const float* rp = e.rope + ((size_t)((row >> 2) * BLK + (row & 3)) * (DH / 2) + c % DH) * 2;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const float a = tp[n], b = tp[8 + n];
+        if (sec < 2) {
+          const float cs = rp[2 * n], sn = rp[2 * n + 1];
+          dst[n] = a * cs - b * sn;
+          dst[n + DH / 2] = a * sn + b * cs;
+        } else {
+          dst[n] = a;
+          dst[n + DH / 2] = b;
+        }
+      }
+    }
+  }
+}
+
+void launch_proj(hipStream_t st, const uint16_t* af, int R, const WMat& W, const ProjEpi& e) {
+  GemmMM g;
+  g.af = af;
+  g.R = R;
+  g.KT = W.K / 32;
+  g.w = W.w;
+  g.s = W.s;
+  g.s4 = W.s4;
+  g.KB = W.K / 64;
+  g.N = W.N;
+  g.n_off = 0;
+  g.WN = W.N;
+  g.ks = W.ks;
+  g.part = nullptr;
+  g.splits = 1;
+  g.kbs = g.KB;
+  const bool wide = mm_ct(R) == 4;
+  const dim3 grid(mm_grid(R, W.N / (wide ? 256 : 64), 1));
+  switch (W.fmt) {
+    case WF_NVFP4:
+      if (wide) k_proj<4, 2, WF_NVFP4><<<grid, 256, 0, st>>>(g, e);
+      else k_proj<1, 4, WF_NVFP4><<<grid, 256, 0, st>>>(g, e);
+      break;
+    case WF_BF16:
+      if (wide) k_proj<4, 2, WF_BF16><<<grid, 256, 0, st>>>(g, e);
+      else k_proj<1, 4, WF_BF16><<<grid, 256, 0, st>>>(g, e);
+      break;
+    default:
+      if (wide) k_proj<4, 2, WF_FP8><<<grid, 256, 0, st>>>(g, e);
+      else k_proj<1, 4, WF_FP8><<<grid, 256, 0, st>>>(g, e);
   }
 }
 

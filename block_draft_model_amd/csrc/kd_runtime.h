@@ -117,6 +117,20 @@ inline size_t afrag_elems(int R, int K) { return (size_t)mtiles(R) * (K / 32) * 
 // the batch around it; fewer splits as row tiles multiply.
 int gemm_splits(int K, int N, int R);
 
+// Epilogue of a fused projection (launch_proj).
+enum ProjEpiKind {
+  PE_QKV = 0,     // RoPE on q and k -> q, kb, vb
+  PE_SWIGLU = 1,  // silu(gate) * up -> af (afrag [R][FF])
+};
+struct ProjEpi {
+  int kind = PE_QKV;
+  const float* rope = nullptr;
+  float* q = nullptr;
+  float* kb = nullptr;
+  float* vb = nullptr;
+  uint16_t* af = nullptr;
+};
+
 // ---- launchers (kd_kernels.hip) ----
 void launch_gemm(hipStream_t st, const uint16_t* af, int R, const WMat& W, int n_off_tiles,
                  int N, float* part, int splits);
@@ -158,6 +172,8 @@ bool gemm_mm_fits(int R, int N);
 int gemm_mm_splits(int K, int N, int R);
 void launch_gemm_mm(hipStream_t st, const uint16_t* af, int R, const WMat& W, int n_off_tiles,
                     int N, float* part, int splits);
+// Projection of R rows (more than 32) with its epilogue fused, in one split.
+void launch_proj(hipStream_t st, const uint16_t* af, int R, const WMat& W, const ProjEpi& e);
 bool head_mm_fits(int R);
 void launch_head_mm(hipStream_t st, const uint16_t* af, int R, const DevWeights& d, float* logits,
                     unsigned long long* keys);

@@ -61,7 +61,7 @@ EXPORTS = ["kd_default_config", "kd_create", "kd_load_weights", "kd_round", "kd_
            "kd_set_stream", "kd_destroy", "kd_status_string", "kd_last_error",
            "kd_probe_decode_e4m3", "kd_probe_decode_e4m3_f16", "kd_probe_decode_nvfp4", "kd_debug_set_layers",
            "kd_debug_buffers", "kd_debug_set_path", "kd_debug_last_path",
-           "kd_debug_set_trace", "kd_copy_draft_noalloc"]
+           "kd_debug_set_trace", "kd_copy_draft_noalloc", "kd_debug_set_fused"]
 
 KD_MAX_COPY = 48
 KD_GUARD_MAX_WINDOW = 64
@@ -147,6 +147,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kd_debug_buffers.restype = c_int
     lib.kd_debug_set_path.argtypes = [c_void_p, c_int]
     lib.kd_debug_set_path.restype = c_int
+    lib.kd_debug_set_fused.argtypes = [c_void_p, c_int]
+    lib.kd_debug_set_fused.restype = c_int
     lib.kd_debug_last_path.argtypes = [c_void_p]
     lib.kd_debug_last_path.restype = c_int
     lib.kd_debug_set_trace.argtypes = [c_void_p, c_void_p, c_int, P(c_int)]
@@ -356,6 +358,11 @@ class Drafter:
         """0 automatic, 1 general multi-kernel, 2 small-batch phases as launches,
         3 small-batch persistent kernel (paths 2-3 only for <= 4 streams)."""
         self._check(self.lib.kd_debug_set_path(self.ctx, int(path)), "kd_debug_set_path")
+
+    def debug_set_fused(self, on: bool):
+        """General path above 32 block rows: fused projection epilogues (True,
+        the default) or the separate epilogue kernels (False)."""
+        self._check(self.lib.kd_debug_set_fused(self.ctx, int(bool(on))), "kd_debug_set_fused")
 
     def debug_set_trace(self, buf, phases: int) -> int:
         """Stage timestamps of later rounds into buf (device uint64 [phases][G][8]);

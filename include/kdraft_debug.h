@@ -46,6 +46,12 @@ kd_status kd_debug_buffers(kd_ctx* ctx, const float** hidden, const float** fuse
  * launch. */
 kd_status kd_debug_set_path(kd_ctx* ctx, int path);
 
+/* General path with more than 32 block rows: on = 1 (the default) runs the
+ * q|k|v and gate|up projections in one split each with RoPE and SwiGLU
+ * applied in the projection kernel; on = 0 runs split projections followed by
+ * the separate reduction and epilogue kernels. For comparing the two. */
+kd_status kd_debug_set_fused(kd_ctx* ctx, int on);
+
 /* The path the last round ran on (1, 2 or 3; 0 before any round). */
 int kd_debug_last_path(const kd_ctx* ctx);
 
