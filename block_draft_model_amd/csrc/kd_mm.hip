@@ -158,7 +158,10 @@ __device__ __forceinline__ void mm_accumulate(const GemmMM& g, int rb, int cb, i
             else acc[r][c] += sc[c] * t;
           }
         }
-        if (i + 1 < nb) {
+        // wide tiles store unconditionally (after the last step, an unused
+        // re-loaded copy of it): with no branch in the step, the compiler
+        // interleaves the scale multiply-adds with the matrix-core work
+        if (CT == 4 || i + 1 < nb) {
           const int dn = d + 1 == D ? 0 : d + 1;
 #pragma unroll
           for (int j = 0; j < 2; ++j) sa[buf ^ 1][wave * 2 + j][lane] = ar[dn][j];
