@@ -122,6 +122,30 @@ __device__ __forceinline__ void split_bf16(const float* v, bf16x8& hi, bf16x8& l
 __device__ __forceinline__ unsigned long long u64_max(unsigned long long a, unsigned long long b) {
   return a > b ? a : b;
 }
+// Exchanges between the wave's lane halves (pl32: lanes l and l ^ 32) or
+// 16-lane rows (pl16: l and l ^ 16) in one instruction each, without the LDS
+// crossbar: r0 = (a of the lower lane, b of the lower lane), r1 = (a of the
+// upper lane, b of the upper lane) of each pair, as seen from both lanes of
+// the pair (lower lane: r0 = its own a, r1 = the upper lane's a; upper lane:
+// r0 = the lower lane's b, r1 = its own b).
+// (the pair of results is bit-cast to floats as one vector: bit-casting the
+// two elements one by one has been compiled to code that reads the first
+// result twice)
+__device__ __forceinline__ void pl32(float a, float b, float& r0, float& r1) {
+  const f32x2 r = __builtin_bit_cast(
+      f32x2, __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b),
+                                              false, false));
+  r0 = r[0];
+  r1 = r[1];
+}
+__device__ __forceinline__ void pl16(float a, float b, float& r0, float& r1) {
+  const f32x2 r = __builtin_bit_cast(
+      f32x2, __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b),
+                                              false, false));
+  r0 = r[0];
+  r1 = r[1];
+}
+
 __device__ __forceinline__ unsigned long long shfl_xor_u64s(unsigned long long v, int m) {
   const uint32_t lo = __shfl_xor((uint32_t)v, m, 64);
   const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
@@ -1246,8 +1270,13 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
       sc[e] = key < n ? acc[e] : -__builtin_inff();
       mx = fmaxf(mx, sc[e]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    {
+      float r0, r1;
+      pl16(mx, mx, r0, r1);   // the max over lane rows (l, l ^ 16)
+      mx = fmaxf(r0, r1);
+      pl32(mx, mx, r0, r1);   // and over lane halves
+      mx = fmaxf(r0, r1);
+    }
     const float m_new = fmaxf(m_run, mx);
     // rescale of the state so far (0 while it is empty)
     const float alpha = m_run == -__builtin_inff() ? 0.f : exp2f(m_run - m_new);
@@ -1257,8 +1286,13 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
       pe[e] = sc[e] == -__builtin_inff() ? 0.f : exp2f(sc[e] - m_new);
       ls += pe[e];
     }
-    ls += __shfl_xor(ls, 16, 64);
-    ls += __shfl_xor(ls, 32, 64);
+    {
+      float r0, r1;
+      pl16(ls, ls, r0, r1);
+      ls = r0 + r1;
+      pl32(ls, ls, r0, r1);
+      ls = r0 + r1;
+    }
     l_run = l_run * alpha + ls;
     m_run = m_new;
     if (lr < 4)
@@ -1298,22 +1332,24 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
       // sum the 4 key groups: groups g and g^2 exchange, g < 2 keeping rows
       // 0, 1 and g >= 2 rows 2, 3; then g and g^1, odd groups keeping the
       // second of their rows -- group g ends with row g
-      const bool upper = lg >= 2, odd = lg & 1;
+      // (with pl32(o[jj], o[2 + jj]) the lower lane of a pair gets its own
+      // row jj and the upper lane's row jj, the upper lane the lower lane's
+      // row 2 + jj and its own: the two add to the pair's sum of that row)
       float r1[2][8];
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float keep = upper ? o[2 + jj][e] : o[jj][e];
-          const float send = upper ? o[jj][e] : o[2 + jj][e];
-          r1[jj][e] = keep + __shfl_xor(send, 32, 64);
+          float x0, x1;
+          pl32(o[jj][e], o[2 + jj][e], x0, x1);
+          r1[jj][e] = x0 + x1;
         }
       f32x4 r2a, r2b;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float keep = odd ? r1[1][e] : r1[0][e];
-        const float send = odd ? r1[0][e] : r1[1][e];
-        const float v = keep + __shfl_xor(send, 16, 64);
+        float x0, x1;
+        pl16(r1[0][e], r1[1][e], x0, x1);
+        const float v = x0 + x1;
         if (e < 4) r2a[e] = v; else r2b[e - 4] = v;
       }
       *reinterpret_cast<KD_LDS f32x4*>(s_o + (wave * 4 + lg) * DH + 8 * lr) = r2a;
