@@ -146,6 +146,24 @@ __device__ __forceinline__ void pl16(float a, float b, float& r0, float& r1) {
   r1 = r[1];
 }
 
+// Lane moves within 16-lane rows by data-parallel primitives (no LDS):
+// quad_perm xor 1 and xor 2, rotations by 8 and 4, and the row's half and
+// full mirrors. A butterfly step v + move(v) equals v + v(l ^ m) when
+// move(l) = l ^ m, or when the earlier steps left v equal on the lanes that
+// move(l) and l ^ m name.
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_ROR4 = 0x124, DPP_ROR8 = 0x128,
+              DPP_MIRROR = 0x140, DPP_HALF_MIRROR = 0x141;
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long v) {
+  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
 __device__ __forceinline__ unsigned long long shfl_xor_u64s(unsigned long long v, int m) {
   const uint32_t lo = __shfl_xor((uint32_t)v, m, 64);
   const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
@@ -458,8 +476,16 @@ struct RmsRows {
     if (!ssq) return;
     const int r = threadIdx.x >> 5, l32 = threadIdx.x & 31;
     float sum = v[0] + v[1] + v[2] + v[3] + v[4];
-#pragma unroll
-    for (int m = 16; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 64);
+    // butterfly over the 32 lanes l32 (xor 16, 8, 4, 2, 1)
+    {
+      float r0, r1;
+      pl16(sum, sum, r0, r1);
+      sum = r0 + r1;
+    }
+    sum += dpp_f<DPP_ROR8>(sum);   // = lane ^ 8
+    sum += dpp_f<DPP_ROR4>(sum);   // lanes 8 apart now agree: = lane ^ 4
+    sum += dpp_f<DPP_XOR2>(sum);
+    sum += dpp_f<DPP_XOR1>(sum);
     if (r < nrows && l32 == 0) inv[r] = 1.0f / sqrtf(sum / H + eps);
     lds_sync();
   }
@@ -468,8 +494,11 @@ struct RmsRows {
 // Sum of squares of this tile's 16 columns for the item's row (all lanes).
 __device__ __forceinline__ float tile_ssq(float x) {
   float s = x * x;
-#pragma unroll
-  for (int m = 1; m <= 8; m <<= 1) s += __shfl_xor(s, m, 64);
+  // butterfly over the 16-lane row (xor 1, 2, 4, 8)
+  s += dpp_f<DPP_XOR1>(s);
+  s += dpp_f<DPP_XOR2>(s);
+  s += dpp_f<DPP_HALF_MIRROR>(s);   // quads now agree: = lane ^ 4
+  s += dpp_f<DPP_MIRROR>(s);        // halves now agree: = lane ^ 8
   return s;
 }
 
@@ -738,7 +767,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_qkv(Args& a_, int 
           const int t = u * NT + i, sec = t / HT;
           const int nat = qkv_natural(t * 16 + n) - sec * H;  // column within q, k or v
           const float val = m < R ? v * inv[m] : 0.f;
-          const float partner = __shfl_xor(val, 8, 64);
+          const float partner = dpp_f<DPP_ROR8>(val);
           float out = val;
           if (sec < 2) {
             const int fi = (nat % DH) & 63;
@@ -1554,7 +1583,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_gu(Args& a_, int l
         [&](int i, int m, int n, float v) {
           const int t = u * NT + i;
           const float val = m < R ? v * inv[m] : 0.f;
-          const float up = __shfl_xor(val, 8, 64);
+          const float up = dpp_f<DPP_ROR8>(val);
           if (m < R && n < 8) st_wt_h(&s.h[l][m * FF + 8 * t + n], silu(val) * up);
         });
     first = false;
@@ -1661,8 +1690,11 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_head(Args& a_, lds
       const float logit = ok ? v * inv[m] * d.hg : 0.f;
       if (ok && a.out_logits) a.out_logits[(size_t)m * VD + voc] = logit;
       unsigned long long key = ok ? argmax_key(logit, (uint32_t)voc) : 0ull;
-#pragma unroll
-      for (int mm = 1; mm <= 8; mm <<= 1) key = u64_max(key, shfl_xor_u64s(key, mm));
+      // max over the 16-lane row (xor 1, 2, then the mirrors of agreeing quads and halves)
+      key = u64_max(key, dpp_u64<DPP_XOR1>(key));
+      key = u64_max(key, dpp_u64<DPP_XOR2>(key));
+      key = u64_max(key, dpp_u64<DPP_HALF_MIRROR>(key));
+      key = u64_max(key, dpp_u64<DPP_MIRROR>(key));
       if (n == 0 && key)
         __hip_atomic_fetch_max(&best[m], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     });
