@@ -892,7 +892,6 @@ static kd_status round_impl(kd_ctx* c, int depth, int B, const void* taps, const
   if (path == 3 && !c->mega_ok) path = 2;
   if (path != 1 && B > kd::SB_MAX) path = 1;
   if (k.fmt == KD_KV_INT4_ROT) path = 1;   // the 4-bit cache is read by the general path
-  if (d.head_fmt != 0) path = 1;           // so are the bf16 and FP8 heads
   if (d.fuse.fmt != kd::WF_FP8) path = 1;  // and the NVFP4 and bf16 bodies
   c->last_path = path;
   if (path != 1) {

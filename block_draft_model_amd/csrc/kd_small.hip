@@ -1591,6 +1591,54 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_gu(Args& a_, int l
   if (first) grid_sync(a, sy);
 }
 
+// The end of every head phase: the workgroup's per-row argmax candidates go
+// out; the last workgroup to finish reduces every workgroup's candidates to
+// the target ids (and publishes a timed-out wait and the f16 range flag).
+__device__ __forceinline__ void head_finish(Args& a, KD_LDS unsigned long long* best, KD_LDS unsigned* s_flag,
+                                            SyncState sy) {
+  const int G = gridDim.x, wg = blockIdx.x;
+  auto& s = a.s;
+  auto& d = a.d;
+  const int R = a.R;
+  lds_sync();
+  if (threadIdx.x < SR_MAX) st_wt64(&s.cand[wg * SR_MAX + threadIdx.x], best[threadIdx.x]);
+  trace_mark(a, sy, 4);
+  // the last workgroup to finish reduces every workgroup's candidates
+  __builtin_amdgcn_s_waitcnt(0);  // the candidate stores are acknowledged
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    auto cnt = &s.bar[19 * 32];
+    const unsigned v = add_rlx(cnt, 1u);
+    const bool last = v == (unsigned)(G - 1);
+    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = last ? 1u : 0u;
+  }
+  lds_sync();
+  if (!*s_flag) return;
+  const int t = threadIdx.x, r = t >> 5, l32 = t & 31;
+  // every candidate load is issued before the first is needed
+  unsigned long long kc[MAX_G / 32];
+#pragma unroll
+  for (int i = 0; i < MAX_G / 32; ++i) {
+    const int gi = l32 + 32 * i;
+    kc[i] = r < R && gi < G ? s.cand[gi * SR_MAX + r] : 0ull;
+  }
+  unsigned long long k = 0ull;
+#pragma unroll
+  for (int i = 0; i < MAX_G / 32; ++i) k = u64_max(k, kc[i]);
+#pragma unroll
+  for (int m = 16; m >= 1; m >>= 1) k = u64_max(k, shfl_xor_u64s(k, m));
+  const bool failed = ld_rlx(&s.bar[18 * 32]) != 0u;
+  if (failed && t == 0 && a.status)
+    __hip_atomic_store(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  // every workgroup's f16 stores of the round are done: status[1] is the range word
+  if (t == 0) flush_f16_range(a.status ? a.status + 1 : nullptr);
+  if (r < R && l32 == 0) {
+    const bool ok = id_row_valid(a.anchor, a.pred, a.pred_stride, r / BLK, r % BLK, d.V);
+    a.out_ids[r] = failed ? -2 : (k && ok ? d.vocab[0xffffffffu - (uint32_t)(k & 0xffffffffu)] : -1);
+  }
+}
+
 // NVFP4 head over 16-row vocab tiles (HEAD_NT per unit): wave w takes the
 // 128-input groups kg0(w)..kg1(w); the next unit's codes are loaded while one
 // is computed. Argmax candidates per row are kept per workgroup; the last
@@ -1707,43 +1755,153 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_head(Args& a_, lds
     load_unit(min(u + 2 * G, ulast), qa, sa);
     unit_body(u + G, qb, sb);
   }
-  lds_sync();
-  if (threadIdx.x < SR_MAX) st_wt64(&s.cand[wg * SR_MAX + threadIdx.x], best[threadIdx.x]);
-  trace_mark(a, sy, 4);
-  // the last workgroup to finish reduces every workgroup's candidates
-  __builtin_amdgcn_s_waitcnt(0);  // the candidate stores are acknowledged
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    auto cnt = &s.bar[19 * 32];
-    const unsigned v = add_rlx(cnt, 1u);
-    const bool last = v == (unsigned)(G - 1);
-    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *s_flag = last ? 1u : 0u;
-  }
-  lds_sync();
-  if (!*s_flag) return;
-  const int t = threadIdx.x, r = t >> 5, l32 = t & 31;
-  // every candidate load is issued before the first is needed
-  unsigned long long kc[MAX_G / 32];
+  head_finish(a, best, s_flag, sy);
+}
+
+// bf16 (HQ = 1) and block-FP8 (HQ = 2) head slices over the same 16-row
+// vocabulary tiles, wave input groups, epilogue and argmax as the NVFP4 head.
+// bf16: each f16 activation is split exactly into two bf16 terms (its top 8
+// significant bits, and the rest) for the bf16 matrix cores; a unit is one
+// tile, whose codes are 4 times the NVFP4 tile's. FP8: e4m3 decoded exactly to
+// f16, each 64-input block's product scaled by its row's fp32 scale. Two
+// register sets of codes alternate, as in the NVFP4 head.
+template <int HQ>
+__device__ __attribute__((noinline, not_tail_called)) void ph_head_q(Args& a_, lds_f red, SyncState sy,
+                                                    bool sync) {
+  Args& a = uni(a_);
+  const int G = gridDim.x, wg = blockIdx.x;
+  auto& s = a.s;
+  auto& d = a.d;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int R = a.R, VT = d.VT, VD = d.VD;
+  constexpr int KG = H / 128;
+  constexpr int NTU = HQ == 1 ? 1 : HEAD_NT;   // vocabulary tiles per unit
+  constexpr int NQ = HQ == 1 ? 4 : 2;          // 16-byte code loads per tile and input group
+  const int wave_s = uni(wave);
+  const int kg0 = (KG * wave_s) >> 3, kg1 = (KG * (wave_s + 1)) >> 3, ng = kg1 - kg0;  // 2 or 3
+  const int src = a.nl == 0 ? 0 : xs_d(a.nl - 1);
+  const int nunits = (VT + NTU - 1) / NTU;
+  lds_f inv = red + 8192;
+  KD_LDS unsigned long long* best = reinterpret_cast<KD_LDS unsigned long long*>(red + 8192 + 32);  // [16]
+  KD_LDS unsigned* s_flag = reinterpret_cast<KD_LDS unsigned*>(red + 8192 + 64);
+
+  // unit u < nunits (tiles past the last repeat it and are masked; a wave
+  // with 2 input groups repeats its last group in slot 2 and skips it)
+  auto load_unit = [&](int u, u32x4 (&q)[NTU][3][NQ], float (&sv)[NTU][3][2]) {
 #pragma unroll
-  for (int i = 0; i < MAX_G / 32; ++i) {
-    const int gi = l32 + 32 * i;
-    kc[i] = r < R && gi < G ? s.cand[gi * SR_MAX + r] : 0ull;
-  }
-  unsigned long long k = 0ull;
+    for (int i = 0; i < NTU; ++i)
 #pragma unroll
-  for (int i = 0; i < MAX_G / 32; ++i) k = u64_max(k, kc[i]);
+      for (int gg = 0; gg < 3; ++gg) {
+        const int vt = min(u * NTU + i, VT - 1);
+        const int kg = kg0 + min(gg, ng - 1);
+        if constexpr (HQ == 1) {
 #pragma unroll
-  for (int m = 16; m >= 1; m >>= 1) k = u64_max(k, shfl_xor_u64s(k, m));
-  const bool failed = ld_rlx(&s.bar[18 * 32]) != 0u;
-  if (failed && t == 0 && a.status)
-    __hip_atomic_store(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-  // every workgroup's f16 stores of the round are done: status[1] is the range word
-  if (t == 0) flush_f16_range(a.status ? a.status + 1 : nullptr);
-  if (r < R && l32 == 0) {
-    const bool ok = id_row_valid(a.anchor, a.pred, a.pred_stride, r / BLK, r % BLK, d.V);
-    a.out_ids[r] = failed ? -2 : (k && ok ? d.vocab[0xffffffffu - (uint32_t)(k & 0xffffffffu)] : -1);
+          for (int t = 0; t < 4; ++t)
+            q[i][gg][t] = *(uni(reinterpret_cast<gptr<const u32x4>>(d.hb + ((size_t)vt * (H / 32) + kg * 4 + t) * 512)) + lane);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const size_t blk = (size_t)vt * (H / 64) + kg * 2 + j;
+            q[i][gg][j] = *(uni(reinterpret_cast<gptr<const u32x4>>(d.hf8.w + blk * 1024)) + lane);
+            sv[i][gg][j] = d.hf8.s[blk * 16 + (lane & 15)];
+          }
+        }
+      }
+  };
+
+  if (sync) {
+    grid_arrive(a, sy);
+    if (is_poll_wave()) grid_poll(a, sy);
+    lds_sync();
   }
+  trace_mark(a, sy, 2);
+  if (threadIdx.x < SR_MAX) best[threadIdx.x] = 0ull;
+  RmsRows rms{s.ssq[src], R, 0, a.eps, inv, {}};
+  rms.issue();
+  const int ar = min(lane & 15, R - 1);
+  // A operand (g_o * x in f16) for this wave's inputs, kept for all units
+  f16x8 ah[3][4];
+#pragma unroll
+  for (int gg = 0; gg < 3; ++gg)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int c0 = (kg0 + min(gg, ng - 1)) * 128 + t * 32 + 8 * (lane >> 4);
+      ah[gg][t] = *reinterpret_cast<gptr<const f16x8>>(s.xg[src] + ar * H + c0);
+    }
+  u32x4 qa[NTU][3][NQ], qb[NTU][3][NQ];
+  float sa[NTU][3][2], sb[NTU][3][2];
+  const int ulast = max(nunits - 1, 0);
+  load_unit(min(wg, ulast), qa, sa);
+  rms.finish();
+  // bf16: the activations' exact two-term split, once for all units
+  bf16x8 ahh[HQ == 1 ? 3 : 1][4], ahl[HQ == 1 ? 3 : 1][4];
+  if constexpr (HQ == 1) {
+#pragma unroll
+    for (int gg = 0; gg < 3; ++gg)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) split_f16_bf16(ah[gg][t], ahh[gg][t], ahl[gg][t]);
+  }
+  trace_mark(a, sy, 3);
+  auto unit_body = [&](int u, const u32x4 (&q)[NTU][3][NQ], const float (&sv)[NTU][3][2])
+                       __attribute__((always_inline)) {
+    f32x4 acc[NTU];
+#pragma unroll
+    for (int i = 0; i < NTU; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int gg = 0; gg < 3; ++gg) {
+      if (gg < ng) {
+        if constexpr (HQ == 1) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int i = 0; i < NTU; ++i) {
+              const bf16x8 w = __builtin_bit_cast(bf16x8, q[i][gg][t]);
+              acc[i] = mfma_bf16(ahh[gg][t], w, acc[i]);
+              acc[i] = mfma_bf16(ahl[gg][t], w, acc[i]);
+            }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int i = 0; i < NTU; ++i) {
+              const u32x4 c = q[i][gg][j];
+              f32x4 t = {0.f, 0.f, 0.f, 0.f};
+              t = mfma_f16(ah[gg][2 * j], e4m3x8_f16(c.x, c.y), t);
+              t = mfma_f16(ah[gg][2 * j + 1], e4m3x8_f16(c.z, c.w), t);
+              acc[i] += sv[i][gg][j] * t;
+            }
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NTU; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[((wave * NTU + i) * 4 + e) * 64 + lane] = acc[i][e];
+    lds_sync();
+    gemm_epilogue<NTU>(red, [&](int i, int m, int n, float v) {
+      const int voc = (u * NTU + i) * 16 + n;
+      const bool ok = m < R && voc < VD;
+      const float logit = ok ? v * inv[m] * d.hg : 0.f;
+      if (ok && a.out_logits) a.out_logits[(size_t)m * VD + voc] = logit;
+      unsigned long long key = ok ? argmax_key(logit, (uint32_t)voc) : 0ull;
+      // max over the 16-lane row (xor 1, 2, then the mirrors of agreeing quads and halves)
+      key = u64_max(key, dpp_u64<DPP_XOR1>(key));
+      key = u64_max(key, dpp_u64<DPP_XOR2>(key));
+      key = u64_max(key, dpp_u64<DPP_HALF_MIRROR>(key));
+      key = u64_max(key, dpp_u64<DPP_MIRROR>(key));
+      if (n == 0 && key)
+        __hip_atomic_fetch_max(&best[m], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    });
+    if (u == wg) trace_mark(a, sy, 5);
+  };
+  for (int u = wg; u < nunits; u += 2 * G) {
+    load_unit(min(u + G, ulast), qb, sb);
+    unit_body(u, qa, sa);
+    if (u + G >= nunits) break;
+    load_unit(min(u + 2 * G, ulast), qa, sa);
+    unit_body(u + G, qb, sb);
+  }
+  head_finish(a, best, s_flag, sy);
 }
 
 // ---------------------------------------------------------------------------
@@ -1753,7 +1911,12 @@ __device__ void run_phase(Args& a, int p, lds_f red, SyncState sy, bool sync) {
   if (p == PH_PRE0) return ph_pre0(a, red, sy);
   if (p == PH_PRE1) return ph_pre1(a, red, sy, sync);
   if (p == PH_PRE2) return ph_pre2(a, red, sy, sync);
-  if (p == PH_HEAD) return ph_head(a, red, sy, sync);
+  if (p == PH_HEAD) {
+    const int hf = uni(a.d.head_fmt);
+    if (hf == 1) return ph_head_q<1>(a, red, sy, sync);
+    if (hf == 2) return ph_head_q<2>(a, red, sy, sync);
+    return ph_head(a, red, sy, sync);
+  }
   const int l = (p - 3) >> 3, k = (p - 3) & 7;
   switch (k) {
     case PH_SA: return ph_sa(a, l, red, sy, sync);

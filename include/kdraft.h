@@ -97,8 +97,8 @@ typedef struct {
                         batch size) */
   int head_quant;    /* KD_QUANT_NVFP4, or KD_QUANT_BF16 / KD_QUANT_FP8_BLOCK64
                         (the card's Use section offers bf16, FP8 and NVFP4
-                        head slices; the bf16 and FP8 heads run the general
-                        path at every batch size) */
+                        head slices; every head runs on both the small-batch
+                        and the general path) */
 } kd_config;
 
 /* Fills *cfg with the model card's shape, max_streams = 256. */

@@ -3,10 +3,12 @@
 NVFP4; Serving: the NVFP4 head keeps the drafts at a quarter of the bf16
 bytes).
 
-These heads run the general path at every batch size. For bf16 the tiled
-head kernel splits each f16 activation exactly into two bf16 terms for the
-bf16 matrix cores; for FP8 it decodes e4m3 exactly to f16 and scales each
-64-input block's product by its row's scale. Acceptance as for every round: relative
+Up to 4 streams these heads run in the small-batch path's head phase (per
+phase launches, path 2, and the persistent kernel, path 3), above 4 in the
+general path's tiled head kernel. For bf16 each f16 activation is split
+exactly into two bf16 terms for the bf16 matrix cores; for FP8 e4m3 is
+decoded exactly to f16 and each 64-input block's product is scaled by its
+row's scale. Acceptance as for every round: relative
 L2 of the logits <= 1e-2 and ids equal wherever the oracle's top-1/top-2 gap
 exceeds 1e-2.
 """
@@ -32,12 +34,37 @@ def hbC(request):
     return Harness("C", max_streams=256, head=request.param)
 
 
-def test_bf16_head_b4(hbC):
+@pytest.mark.parametrize("path", [1, 2, 3])
+def test_bf16_head_b4(hbC, path):
     inp = hbC.inputs(C[1])
-    lg, ids = hbC.run(inp)
-    assert hbC.drafter.last_path() == 1
+    hbC.drafter.debug_set_path(path)
+    try:
+        lg, ids = hbC.run(inp)
+        assert hbC.drafter.last_path() == path
+    finally:
+        hbC.drafter.debug_set_path(0)
     ref, rid = oracle.oracle_round(hbC.oracle, synth.to_numpy_inputs(inp))
-    compare(lg, ids, ref, rid, hbC.oracle.vocab, f"{hbC.head} head B4")
+    compare(lg, ids, ref, rid, hbC.oracle.vocab, f"{hbC.head} head B4 path {path}")
+
+
+def test_small_path_heads_agree_bitwise_and_per_stream(hbC):
+    """The two small-batch forms run the same head phase: identical logits;
+    and a stream drafted alone equals the same stream in a batch of 4."""
+    inp = hbC.inputs(C[1], base=23)
+    out = {}
+    for path in (2, 3):
+        hbC.drafter.debug_set_path(path)
+        try:
+            out[path] = hbC.run(inp)
+        finally:
+            hbC.drafter.debug_set_path(0)
+    assert np.array_equal(out[2][0], out[3][0]) and np.array_equal(out[2][1], out[3][1])
+    one = {k: (v[1:2] if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    one["k"] = [t[1:2] for t in inp["k"]]
+    one["v"] = [t[1:2] for t in inp["v"]]
+    one["streams"] = 1
+    lg1, ids1 = hbC.run(one)
+    assert np.array_equal(lg1[0], out[2][0][1]) and np.array_equal(ids1[0], out[2][1][1])
 
 
 def test_bf16_head_b1_and_edges(hbC):
