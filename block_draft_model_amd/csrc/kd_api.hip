@@ -892,7 +892,6 @@ static kd_status round_impl(kd_ctx* c, int depth, int B, const void* taps, const
   if (path == 3 && !c->mega_ok) path = 2;
   if (path != 1 && B > kd::SB_MAX) path = 1;
   if (k.fmt == KD_KV_INT4_ROT) path = 1;   // the 4-bit cache is read by the general path
-  if (d.fuse.fmt != kd::WF_FP8) path = 1;  // and the NVFP4 and bf16 bodies
   c->last_path = path;
   if (path != 1) {
     (void)hipGetLastError();
@@ -934,7 +933,7 @@ static kd_status round_impl(kd_ctx* c, int depth, int B, const void* taps, const
       }
       const int np = kd::small_phase_count(a.nl);
       if (path == 3) {
-        const hipError_t e = kd::launch_small_mega(st, c->args_dev[slot], c->G, c->epoch);
+        const hipError_t e = kd::launch_small_mega(st, c->args_dev[slot], c->G, c->epoch, d.fuse.fmt);
         if (e != hipSuccess) return hip_fail(c, e, "persistent round launch");
         c->epoch += (unsigned)(np - 1);
       } else {
@@ -949,7 +948,8 @@ static kd_status round_impl(kd_ctx* c, int depth, int B, const void* taps, const
           if (e == hipSuccess) e = hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal);
           if (e == hipSuccess) {
             for (int i = 0; i < np; ++i)
-              kd::launch_small_phase(c->cap_stream, c->args_dev[slot], c->G, kd::small_phase_id(a.nl, i), i);
+              kd::launch_small_phase(c->cap_stream, c->args_dev[slot], c->G, kd::small_phase_id(a.nl, i), i,
+                                     d.fuse.fmt);
             e = hipStreamEndCapture(c->cap_stream, &g);
           }
           if (e == hipSuccess) e = hipGraphInstantiate(&c->phase_graph[slot], g, nullptr, nullptr, 0);

@@ -86,10 +86,10 @@ void small_carve(char* base, int nch, SmallBufs* s);
 __host__ __device__ int small_phase_count(int nl);
 __host__ __device__ int small_phase_id(int nl, int i);
 // dev_args: a device copy of the SmallArgs.
-void launch_small_phase(hipStream_t st, const SmallArgs* dev_args, int G, int phase, int slot);
+void launch_small_phase(hipStream_t st, const SmallArgs* dev_args, int G, int phase, int slot, int body_fmt);
 // epoch0: grid barriers completed by earlier persistent launches on these
 // buffers (each launch completes small_phase_count(nl) - 1).
-hipError_t launch_small_mega(hipStream_t st, const SmallArgs* dev_args, int G, unsigned epoch0);
+hipError_t launch_small_mega(hipStream_t st, const SmallArgs* dev_args, int G, unsigned epoch0, int body_fmt);
 int small_mega_occupancy();
 
 

@@ -296,10 +296,15 @@ __device__ __forceinline__ void touch(gptr<const uint8_t> p, size_t bytes) {
 }
 // The weights and scales of tiles [t0, t0 + ntile), input blocks [kb0, kb0 + nkb).
 __device__ __forceinline__ void touch_tiles(Mat& W, int t0, int ntile, int kb0, int nkb) {
-  const int KB = W.K >> 6;
+  const int KB = W.K >> 6, fmt = uni(W.fmt);
+  // code bytes per 16 outputs x 64 inputs: block-FP8 1024 (+ 64 of scales),
+  // NVFP4 512 (+ 64 of scale codes), bf16 2048
+  const size_t cb = fmt == WF_NVFP4 ? 512 : (fmt == WF_BF16 ? 2048 : 1024);
   for (int t = t0; t < t0 + ntile; ++t) {
-    touch(W.w + ((size_t)t * KB + kb0) * 1024, (size_t)nkb * 1024);
-    touch(reinterpret_cast<gptr<const uint8_t>>(W.s + ((size_t)t * KB + kb0) * 16), (size_t)nkb * 64);
+    const size_t blk = (size_t)t * KB + kb0;
+    touch(W.w + blk * cb, (size_t)nkb * cb);
+    if (fmt == WF_FP8) touch(reinterpret_cast<gptr<const uint8_t>>(W.s + blk * 16), (size_t)nkb * 64);
+    if (fmt == WF_NVFP4) touch(W.s4 + blk * 64, (size_t)nkb * 64);
   }
 }
 // Idle workgroups [i0, G): workgroup w on XCD x = w % 8 takes the units
@@ -327,30 +332,68 @@ __device__ __forceinline__ void warm_qkv(Args& a, int l, int i0, int u0, int u1)
 // Projection units: NT consecutive 16-row weight tiles; wave w (< AW) takes
 // the 64-input blocks kb0 + w*KBS .. + KBS.
 // ---------------------------------------------------------------------------
+template <int WF, int NT, int KBS>
+struct WRegs;
 template <int NT, int KBS>
-struct WRegs {
+struct WRegs<WF_FP8, NT, KBS> {   // 16 e4m3 codes and the block's scale per lane
   u32x4 w[NT][KBS];
   float s[NT][KBS];
+};
+template <int NT, int KBS>
+struct WRegs<WF_NVFP4, NT, KBS> {  // 16 e2m1 codes and two e4m3 scale codes per lane
+  uint2 q[NT][KBS];
+  uint32_t sc[NT][KBS];
+  float g[NT][2];                  // the column's tensor scales (blocks before / from ks)
+};
+template <int NT, int KBS>
+struct WRegs<WF_BF16, NT, KBS> {   // 16 bf16 values per lane
+  u32x4 w0[NT][KBS], w1[NT][KBS];
 };
 
 // Loads are unconditional (indices clamped into range): a load inside a
 // conditional block with a fallback value makes the compiler wait for it at the
 // join, which would serialise the prefetch. Waves past AW load wave AW-1's
 // blocks and ignore them; tiles past ntv repeat the last valid tile, whose
-// results the epilogue discards.
-template <int NT, int KBS, int AW>
-__device__ __forceinline__ void load_w(WRegs<NT, KBS>& r, Mat& W, int tile0, int ntv,
+// results the epilogue discards. The lane's part of a block is laid out as in
+// the general path's tiles (kd_device.h: load_wblock).
+template <int WF, int NT, int KBS, int AW>
+__device__ __forceinline__ void load_w(WRegs<WF, NT, KBS>& r, Mat& W, int tile0, int ntv,
                                        int kb0) {
   const int lane = threadIdx.x & 63, wave = min((int)(threadIdx.x >> 6), AW - 1);
   const int KB = W.K >> 6;
 #pragma unroll
-  for (int i = 0; i < NT; ++i)
+  for (int i = 0; i < NT; ++i) {
+    const int nt = tile0 + min(i, ntv - 1);
+    if constexpr (WF == WF_NVFP4) {
+      r.g[i][0] = W.s[nt * 16 + (lane & 15)];
+      r.g[i][1] = W.s[W.N + nt * 16 + (lane & 15)];
+    }
 #pragma unroll
     for (int j = 0; j < KBS; ++j) {
-      const size_t blk = (size_t)(tile0 + min(i, ntv - 1)) * KB + kb0 + wave * KBS + j;
-      r.w[i][j] = *reinterpret_cast<gptr<const u32x4>>(W.w + blk * 1024 + lane * 16);
-      r.s[i][j] = W.s[blk * 16 + (lane & 15)];
+      const size_t blk = (size_t)nt * KB + kb0 + wave * KBS + j;
+      if constexpr (WF == WF_FP8) {
+        r.w[i][j] = *reinterpret_cast<gptr<const u32x4>>(W.w + blk * 1024 + lane * 16);
+        r.s[i][j] = W.s[blk * 16 + (lane & 15)];
+      } else if constexpr (WF == WF_NVFP4) {
+        r.q[i][j] = *reinterpret_cast<gptr<const uint2>>(W.w + blk * 512 + lane * 8);
+        const uint32_t sw = *reinterpret_cast<gptr<const uint32_t>>(W.s4 + blk * 64 + (lane & 15) * 4);
+        const int sh = 8 * ((lane >> 4) >> 1);
+        r.sc[i][j] = ((sw >> sh) & 0xffu) | (((sw >> (sh + 16)) & 0xffu) << 8);
+      } else {
+        r.w0[i][j] = *reinterpret_cast<gptr<const u32x4>>(W.w + blk * 2048 + lane * 16);
+        r.w1[i][j] = *reinterpret_cast<gptr<const u32x4>>(W.w + blk * 2048 + 1024 + lane * 16);
+      }
     }
+  }
+}
+
+// The bf16 bits of 8 f16 values that need no more than 8 significant bits
+// (NVFP4 values: at most 6).
+__device__ __forceinline__ bf16x8 f16x8_to_bf16_exact(f16x8 v) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (__bf16)(float)v[i];
+  return r;
 }
 
 // Activation rows of the A operand: bf16 (the tapped states and embedding
@@ -394,11 +437,13 @@ __device__ __forceinline__ void a_issue(const ASrc& A, int kb, u32x4 (&raw)[2]) 
 
 // Partial products of each wave into LDS: red[((wave*NT + i)*4 + e)*64 + lane].
 // The A loads of up to C blocks are in flight together. ABF: bf16 activations
-// (weights decoded to bf16), else f16 (weights decoded to f16); both decodes
-// are exact.
-template <int NT, int KBS, int AW, bool ABF>
-__device__ __forceinline__ void gemm_compute(const WRegs<NT, KBS>& r, const ASrc& A, int kb0,
-                                             lds_f red) {
+// (weights decoded to bf16), else f16 (weights decoded to f16; bf16 weights
+// take each f16 activation as two exact bf16 terms); every decode is exact.
+// Each block's product is scaled by its block-FP8 scale or its column's
+// NVFP4 tensor scale.
+template <int WF, int NT, int KBS, int AW, bool ABF>
+__device__ __forceinline__ void gemm_compute(const WRegs<WF, NT, KBS>& r, const ASrc& A, int kb0,
+                                             lds_f red, int ks) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int C = KBS < 8 ? KBS : 8;
   f32x4 acc[NT];
@@ -416,18 +461,48 @@ __device__ __forceinline__ void gemm_compute(const WRegs<NT, KBS>& r, const ASrc
         if (c0 + j < KBS) {
 #pragma unroll
           for (int i = 0; i < NT; ++i) {
-            const u32x4 wv = r.w[i][c0 + j];
             f32x4 t = {0.f, 0.f, 0.f, 0.f};
-            if (ABF) {
-              t = mfma_bf16(__builtin_bit_cast(bf16x8, raw[j][0]), e4m3x8_bf16(wv.x, wv.y), t);
-              t = mfma_bf16(__builtin_bit_cast(bf16x8, raw[j][1]), e4m3x8_bf16(wv.z, wv.w), t);
+            if constexpr (WF == WF_FP8) {
+              const u32x4 wv = r.w[i][c0 + j];
+              if (ABF) {
+                t = mfma_bf16(__builtin_bit_cast(bf16x8, raw[j][0]), e4m3x8_bf16(wv.x, wv.y), t);
+                t = mfma_bf16(__builtin_bit_cast(bf16x8, raw[j][1]), e4m3x8_bf16(wv.z, wv.w), t);
+              } else {
+                t = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, raw[j][0]),
+                                                           e4m3x8_f16(wv.x, wv.y), t, 0, 0, 0);
+                t = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, raw[j][1]),
+                                                           e4m3x8_f16(wv.z, wv.w), t, 0, 0, 0);
+              }
+              acc[i] += r.s[i][c0 + j] * t;
+            } else if constexpr (WF == WF_NVFP4) {
+              const uint2 q = r.q[i][c0 + j];
+              const uint32_t sc = r.sc[i][c0 + j];
+              const f16x8 w0 = nvfp4x8_f16(q.x, sc & 0xffu), w1 = nvfp4x8_f16(q.y, sc >> 8);
+              if (ABF) {
+                t = mfma_bf16(__builtin_bit_cast(bf16x8, raw[j][0]), f16x8_to_bf16_exact(w0), t);
+                t = mfma_bf16(__builtin_bit_cast(bf16x8, raw[j][1]), f16x8_to_bf16_exact(w1), t);
+              } else {
+                t = mfma_f16(__builtin_bit_cast(f16x8, raw[j][0]), w0, t);
+                t = mfma_f16(__builtin_bit_cast(f16x8, raw[j][1]), w1, t);
+              }
+              acc[i] += (kb0 + wave * KBS + c0 + j < ks ? r.g[i][0] : r.g[i][1]) * t;
             } else {
-              t = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, raw[j][0]),
-                                                         e4m3x8_f16(wv.x, wv.y), t, 0, 0, 0);
-              t = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, raw[j][1]),
-                                                         e4m3x8_f16(wv.z, wv.w), t, 0, 0, 0);
+              const bf16x8 w0 = __builtin_bit_cast(bf16x8, r.w0[i][c0 + j]);
+              const bf16x8 w1 = __builtin_bit_cast(bf16x8, r.w1[i][c0 + j]);
+              if (ABF) {
+                t = mfma_bf16(__builtin_bit_cast(bf16x8, raw[j][0]), w0, t);
+                t = mfma_bf16(__builtin_bit_cast(bf16x8, raw[j][1]), w1, t);
+              } else {
+                bf16x8 h0, l0, h1, l1;
+                split_f16_bf16(__builtin_bit_cast(f16x8, raw[j][0]), h0, l0);
+                split_f16_bf16(__builtin_bit_cast(f16x8, raw[j][1]), h1, l1);
+                t = mfma_bf16(h0, w0, t);
+                t = mfma_bf16(l0, w0, t);
+                t = mfma_bf16(h1, w1, t);
+                t = mfma_bf16(l1, w1, t);
+              }
+              acc[i] += t;
             }
-            acc[i] += r.s[i][c0 + j] * t;
           }
         }
       }
@@ -455,6 +530,7 @@ __device__ __forceinline__ void gemm_epilogue(lds_cf red, F&& f) {
   }
   lds_sync();
 }
+
 
 // 1/rms of up to 16 rows of a residual stage from its per-tile sums of
 // squares. issue() loads, finish() reduces into LDS inv[16].
@@ -505,7 +581,19 @@ __device__ __forceinline__ float tile_ssq(float x) {
 // One projection unit: if this is the workgroup's first unit of the phase,
 // arrive at the barrier, issue the weight loads, then wait; compute; reduce;
 // run `epi`.
-template <int NT, int KBS, int AW, bool ABF, class Epi>
+template <int WF, int NT, int KBS, int AW, bool ABF>
+__device__ __forceinline__ void gemm_body(Args& a, SyncState sy, bool sync, Mat& W, int tile0, int ntv,
+                                          int kb0, const ASrc& A, lds_f red, RmsRows& rms) {
+  WRegs<WF, NT, KBS> r;
+  load_w<WF, NT, KBS, AW>(r, W, tile0, ntv, kb0);
+  if (sync) lds_sync();
+  trace_mark(a, sy, 2);
+  rms.issue();
+  gemm_compute<WF, NT, KBS, AW, ABF>(r, A, kb0, red, W.ks);
+  rms.finish();
+}
+
+template <int WF, int NT, int KBS, int AW, bool ABF, class Epi>
 __device__ __forceinline__ void gemm_unit(Args& a, SyncState sy, bool sync,
                                           Mat& W, int tile0, int ntv, int kb0,
                                           const ASrc& A, lds_f red, RmsRows rms, Epi&& epi) {
@@ -513,13 +601,7 @@ __device__ __forceinline__ void gemm_unit(Args& a, SyncState sy, bool sync,
     grid_arrive(a, sy);
     if (is_poll_wave()) grid_poll(a, sy);
   }
-  WRegs<NT, KBS> r;
-  load_w<NT, KBS, AW>(r, W, tile0, ntv, kb0);
-  if (sync) lds_sync();
-  trace_mark(a, sy, 2);
-  rms.issue();
-  gemm_compute<NT, KBS, AW, ABF>(r, A, kb0, red);
-  rms.finish();
+  gemm_body<WF, NT, KBS, AW, ABF>(a, sy, sync, W, tile0, ntv, kb0, A, red, rms);
   trace_mark(a, sy, 3);
   gemm_epilogue<NT>(red, epi);
   trace_mark(a, sy, 4);
@@ -551,6 +633,7 @@ __device__ __forceinline__ gptr<const float> gain_after_down(Args& a, int l) {
 // Phases. `sync` is true when the phase must wait at a grid barrier first
 // (persistent kernel); every workgroup then passes exactly one barrier.
 // ---------------------------------------------------------------------------
+template <int WF>
 __device__ __attribute__((noinline, not_tail_called)) void ph_pre0(Args& a_, lds_f red, SyncState sy) {
   Args& a = uni(a_);
   const int G = gridDim.x, wg = blockIdx.x;
@@ -582,7 +665,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_pre0(Args& a_, lds
   for (int u = u_first; u < u_end; u += u_step) {
     if (u < n_fuse) {
       const ASrc A{a.taps, NTAP * H, 0, nullptr, 0, B};
-      gemm_unit<1, 15, 8, true>(a, sy, false, d.fuse, u, 1, 0, A, red, no_rms(),
+      gemm_unit<WF, 1, 15, 8, true>(a, sy, false, d.fuse, u, 1, 0, A, red, no_rms(),
                                 [&](int, int m, int n, float v) {
                                   if (m < B) {
                                     st_wt(&s.f[m * H + u * 16 + n], v);
@@ -592,14 +675,14 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_pre0(Args& a_, lds
     } else if (u < n_fuse + n_fce) {
       const int t = u - n_fuse;
       const ASrc A{d.table, H, 3, a.anchor, 40, B, d.zrow, d.V};
-      gemm_unit<1, 5, 8, true>(a, sy, false, d.fc, t, 1, 40, A, red, no_rms(),
+      gemm_unit<WF, 1, 5, 8, true>(a, sy, false, d.fc, t, 1, 40, A, red, no_rms(),
                                [&](int, int m, int n, float v) {
                                  if (m < B) st_wt(&s.fce[m * H + t * 16 + n], v);
                                });
     } else {
       const int t = u - n_fuse - n_fce;
       const ASrc A{d.table, H, a.pred_stride == 4 ? 4 : 3, a.pred, 40, 3 * B, d.zrow, d.V};
-      gemm_unit<1, 5, 8, true>(a, sy, false, d.pred_ab, t, 1, 40, A, red, no_rms(),
+      gemm_unit<WF, 1, 5, 8, true>(a, sy, false, d.pred_ab, t, 1, 40, A, red, no_rms(),
                                [&](int, int m, int n, float v) {
                                  if (m < 3 * B) st_wt(&s.pb[m * RK + t * 16 + n], v);
                                });
@@ -607,6 +690,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_pre0(Args& a_, lds
   }
 }
 
+template <int WF>
 __device__ __attribute__((noinline, not_tail_called)) void ph_pre1(Args& a_, lds_f red, SyncState sy,
                                                   bool sync) {
   Args& a = uni(a_);
@@ -619,7 +703,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_pre1(Args& a_, lds
   for (int u = wg; u < HT + RK / 16; u += G) {
     if (u < HT) {
       const ASrc A{s.fh, H, 0, nullptr, 0, B};
-      gemm_unit<1, 5, 8, false>(a, sy, first, d.fc, u, 1, 0, A, red, no_rms(),
+      gemm_unit<WF, 1, 5, 8, false>(a, sy, first, d.fc, u, 1, 0, A, red, no_rms(),
                                 [&](int, int m, int n, float v) {
                                   const int col = u * 16 + n;
                                   const float x = v + (m < B ? s.fce[m * H + col] : 0.f);
@@ -628,7 +712,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_pre1(Args& a_, lds
     } else {
       const int t = u - HT;
       const ASrc A{s.fh, H, 1, nullptr, 0, 3 * B};
-      gemm_unit<1, 5, 8, false>(a, sy, first, d.pred_ab, t, 1, 0, A, red, no_rms(),
+      gemm_unit<WF, 1, 5, 8, false>(a, sy, first, d.pred_ab, t, 1, 0, A, red, no_rms(),
                                 [&](int, int m, int n, float v) {
                                   if (m < 3 * B) {
                                     const int c = t * 16 + n;
@@ -646,6 +730,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_pre1(Args& a_, lds
   }
 }
 
+template <int WF>
 __device__ __attribute__((noinline, not_tail_called)) void ph_pre2(Args& a_, lds_f red, SyncState sy,
                                                   bool sync) {
   Args& a = uni(a_);
@@ -657,7 +742,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_pre2(Args& a_, lds
   bool first = sync;
   for (int u = wg; u < HT; u += G) {
     const ASrc A{s.sp, RK, 0, nullptr, 0, 3 * B};
-    gemm_unit<1, 1, 4, false>(a, sy, first, d.pred_u, u, 1, 0, A, red, no_rms(),
+    gemm_unit<WF, 1, 1, 4, false>(a, sy, first, d.pred_u, u, 1, 0, A, red, no_rms(),
                               [&](int, int m, int n, float v) {
                                 const int col = u * 16 + n;
                                 const bool ok = m < 3 * B;
@@ -675,6 +760,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_pre2(Args& a_, lds
 }
 
 // Spine A: ss = silu(A_s (g_s * x_{j-1}) / rms(x_{j-1})) for rows j = 1..3.
+template <int WF>
 __device__ __attribute__((noinline, not_tail_called)) void ph_sa(Args& a_, int l_, lds_f red,
                                                 SyncState sy, bool sync) {
   const auto l = uni(l_);
@@ -687,7 +773,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_sa(Args& a_, int l
   bool first = sync;
   for (int u = wg; u < RK / 16; u += G) {
     const ASrc A{s.xg[src], H, 2, nullptr, 0, 3 * B};
-    gemm_unit<1, 5, 8, false>(a, sy, first, L.sa, u, 1, 0, A, red,
+    gemm_unit<WF, 1, 5, 8, false>(a, sy, first, L.sa, u, 1, 0, A, red,
                               RmsRows{s.ssq[src], 3 * B, 2, a.eps, inv, {}},
                               [&](int, int m, int n, float v) {
                                 if (m < 3 * B) st_wt_h(&s.ss[l][m * RK + u * 16 + n], silu(v * inv[m]));
@@ -706,6 +792,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_sa(Args& a_, int l
 }
 
 // Spine U: x_j (j = 1..3) += U_s ss; row 0 copied into the new stage.
+template <int WF>
 __device__ __attribute__((noinline, not_tail_called)) void ph_su(Args& a_, int l_, lds_f red,
                                                 SyncState sy, bool sync) {
   const auto l = uni(l_);
@@ -718,7 +805,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_su(Args& a_, int l
   bool first = sync;
   for (int u = wg; u < HT; u += G) {
     const ASrc A{s.ss[l], RK, 0, nullptr, 0, 3 * B};
-    gemm_unit<1, 1, 4, false>(a, sy, first, L.su, u, 1, 0, A, red, no_rms(),
+    gemm_unit<WF, 1, 1, 4, false>(a, sy, first, L.su, u, 1, 0, A, red, no_rms(),
                               [&](int, int m, int n, float v) {
                                 const int col = u * 16 + n;
                                 const int row = 4 * (m / 3) + m % 3 + 1;
@@ -748,6 +835,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_su(Args& a_, int l
 }
 
 // q|k|v = W (g_a * x) / rms(x); RoPE on q and k inside each paired tile.
+template <int WF>
 __device__ __attribute__((noinline, not_tail_called)) void ph_qkv(Args& a_, int l_, lds_f red,
                                                  SyncState sy, bool sync) {
   const auto l = uni(l_);
@@ -761,7 +849,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_qkv(Args& a_, int 
   bool first = sync;
   for (int u = wg; u < NU; u += G) {
     const ASrc A{s.xg[src], H, 0, nullptr, 0, R};
-    gemm_unit<NT, 5, 8, false>(
+    gemm_unit<WF, NT, 5, 8, false>(
         a, sy, first, L.qkv, u * NT, NT, 0, A, red, RmsRows{s.ssq[src], R, 0, a.eps, inv, {}},
         [&](int i, int m, int n, float v) {
           const int t = u * NT + i, sec = t / HT;
@@ -1467,6 +1555,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
 // Output projection: x_{out} = x_{in} + W_o o, with the gained copy and
 // per-tile sums of squares; one 16-column tile per unit. The workgroups
 // without a tile warm the weights of the down projection two phases on.
+template <int WF>
 __device__ __attribute__((noinline, not_tail_called)) void ph_o(Args& a_, int l_, lds_f red, SyncState sy,
                                                bool sync) {
   const auto l = uni(l_);
@@ -1479,7 +1568,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_o(Args& a_, int l_
   bool first = sync;
   for (int u = wg; u < HT; u += G) {
     const ASrc A{s.o[l], H, 0, nullptr, 0, R};
-    gemm_unit<1, 5, 8, false>(a, sy, first, L.wo, u, 1, 0, A, red, no_rms(),
+    gemm_unit<WF, 1, 5, 8, false>(a, sy, first, L.wo, u, 1, 0, A, red, no_rms(),
                               [&](int, int m, int n, float v) {
                                 const int col = u * 16 + n;
                                 const bool ok = m < R;
@@ -1508,6 +1597,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_o(Args& a_, int l_
 // each loads a third of the activations. Every unit stores its partial; the
 // last of a pair's units to finish (counter) adds the thirds in a fixed order
 // and runs the residual epilogue.
+template <int WF>
 __device__ __attribute__((noinline, not_tail_called)) void ph_down(Args& a_, int l_, lds_f red, SyncState sy,
                                                   bool sync) {
   const auto l = uni(l_);
@@ -1530,7 +1620,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_down(Args& a_, int
     // thread (i, m, n) = (tid / 256, (tid / 16) % 16, tid % 16) holds one
     // output of the pair after the epilogue's reduction over the 8 waves
     float mine = 0.f;
-    gemm_unit<NT, KBS, 8, false>(a, sy, first, L.down, tp * NT, NT, p * KBS * 8, A, red, no_rms(),
+    gemm_unit<WF, NT, KBS, 8, false>(a, sy, first, L.down, tp * NT, NT, p * KBS * 8, A, red, no_rms(),
                                  [&](int i, int m, int n, float v) {
                                    mine = v;
                                    if (m < R) st_wt(&part[((size_t)p * SR_MAX + m) * H + (tp * NT + i) * 16 + n], v);
@@ -1565,6 +1655,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_down(Args& a_, int
 }
 
 // h = silu(gate / rms) * (up / rms) with gate, up = W (g_f * x).
+template <int WF>
 __device__ __attribute__((noinline, not_tail_called)) void ph_gu(Args& a_, int l_, lds_f red,
                                                 SyncState sy, bool sync) {
   const auto l = uni(l_);
@@ -1578,7 +1669,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_gu(Args& a_, int l
   bool first = sync;
   for (int u = wg; u < NU; u += G) {
     const ASrc A{s.xg[src], H, 0, nullptr, 0, R};
-    gemm_unit<NT, 5, 8, false>(
+    gemm_unit<WF, NT, 5, 8, false>(
         a, sy, first, L.gu, u * NT, NT, 0, A, red, RmsRows{s.ssq[src], R, 0, a.eps, inv, {}},
         [&](int i, int m, int n, float v) {
           const int t = u * NT + i;
@@ -1907,10 +1998,11 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_head_q(Args& a_, l
 // ---------------------------------------------------------------------------
 // Phase dispatch
 // ---------------------------------------------------------------------------
+template <int WF>
 __device__ void run_phase(Args& a, int p, lds_f red, SyncState sy, bool sync) {
-  if (p == PH_PRE0) return ph_pre0(a, red, sy);
-  if (p == PH_PRE1) return ph_pre1(a, red, sy, sync);
-  if (p == PH_PRE2) return ph_pre2(a, red, sy, sync);
+  if (p == PH_PRE0) return ph_pre0<WF>(a, red, sy);
+  if (p == PH_PRE1) return ph_pre1<WF>(a, red, sy, sync);
+  if (p == PH_PRE2) return ph_pre2<WF>(a, red, sy, sync);
   if (p == PH_HEAD) {
     const int hf = uni(a.d.head_fmt);
     if (hf == 1) return ph_head_q<1>(a, red, sy, sync);
@@ -1919,13 +2011,13 @@ __device__ void run_phase(Args& a, int p, lds_f red, SyncState sy, bool sync) {
   }
   const int l = (p - 3) >> 3, k = (p - 3) & 7;
   switch (k) {
-    case PH_SA: return ph_sa(a, l, red, sy, sync);
-    case PH_SU: return ph_su(a, l, red, sy, sync);
-    case PH_QKV: return ph_qkv(a, l, red, sy, sync);
+    case PH_SA: return ph_sa<WF>(a, l, red, sy, sync);
+    case PH_SU: return ph_su<WF>(a, l, red, sy, sync);
+    case PH_QKV: return ph_qkv<WF>(a, l, red, sy, sync);
     case PH_ATTN: return ph_attn(a, l, sy, sync);
-    case PH_O: return ph_o(a, l, red, sy, sync);
-    case PH_GU: return ph_gu(a, l, red, sy, sync);
-    case PH_DOWN: return ph_down(a, l, red, sy, sync);
+    case PH_O: return ph_o<WF>(a, l, red, sy, sync);
+    case PH_GU: return ph_gu<WF>(a, l, red, sy, sync);
+    case PH_DOWN: return ph_down<WF>(a, l, red, sy, sync);
   }
 }
 
@@ -1958,45 +2050,60 @@ __device__ __forceinline__ lds_f red_area() { return (lds_f)&g_att_ring[0][0][0]
 
 // The argument block lives in device memory (read through scalar loads), so
 // no per-lane copy of it is made when it is passed down to the phases.
+template <int WF>
 __global__ __launch_bounds__(SMALL_WG) void k_small_phase(const SmallArgs* __restrict__ ap, int p,
                                                          int slot) {
   const unsigned long long t_entry = wall_clock64();
   const SyncState sy{0u, slot};
   Args& a = *(Args*)ap;
-  run_phase(a, p, red_area(), sy, false);
+  run_phase<WF>(a, p, red_area(), sy, false);
   // stage 0 (the barrier arrival of the persistent kernel) holds the entry time
   if (a.trace && threadIdx.x == 0 && slot < a.trace_phases)
     a.trace[((size_t)slot * gridDim.x + blockIdx.x) * 8] = t_entry;
   trace_mark(a, sy, 7);
 }
 
+template <int WF>
 __global__ __launch_bounds__(SMALL_WG) void k_small_mega(const SmallArgs* __restrict__ ap,
                                                         unsigned epoch0) {
   Args& a = *(Args*)ap;
   const int np = small_phase_count(a.nl);
   for (int i = 0; i < np; ++i) {
     const SyncState sy{epoch0, i};
-    run_phase(a, small_phase_id(a.nl, i), red_area(), sy, i > 0);
+    run_phase<WF>(a, small_phase_id(a.nl, i), red_area(), sy, i > 0);
     trace_mark(a, sy, 7);
   }
 }
 
-void launch_small_phase(hipStream_t st, const SmallArgs* dev_args, int G, int phase, int slot) {
-  k_small_phase<<<G, SMALL_WG, 0, st>>>(dev_args, phase, slot);
+// One instance of the phase kernels per body format (the projections'
+// loads and matrix-core loops differ; nothing else does).
+void launch_small_phase(hipStream_t st, const SmallArgs* dev_args, int G, int phase, int slot, int body_fmt) {
+  if (body_fmt == WF_NVFP4) k_small_phase<WF_NVFP4><<<G, SMALL_WG, 0, st>>>(dev_args, phase, slot);
+  else if (body_fmt == WF_BF16) k_small_phase<WF_BF16><<<G, SMALL_WG, 0, st>>>(dev_args, phase, slot);
+  else k_small_phase<WF_FP8><<<G, SMALL_WG, 0, st>>>(dev_args, phase, slot);
 }
 
-hipError_t launch_small_mega(hipStream_t st, const SmallArgs* dev_args, int G, unsigned epoch0) {
+static const void* mega_kernel(int body_fmt) {
+  if (body_fmt == WF_NVFP4) return reinterpret_cast<const void*>(k_small_mega<WF_NVFP4>);
+  if (body_fmt == WF_BF16) return reinterpret_cast<const void*>(k_small_mega<WF_BF16>);
+  return reinterpret_cast<const void*>(k_small_mega<WF_FP8>);
+}
+
+hipError_t launch_small_mega(hipStream_t st, const SmallArgs* dev_args, int G, unsigned epoch0, int body_fmt) {
   const SmallArgs* p = dev_args;
   void* args[] = {&p, &epoch0};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_small_mega), dim3(G),
-                                    dim3(SMALL_WG), args, 0, st);
+  return hipLaunchCooperativeKernel(mega_kernel(body_fmt), dim3(G), dim3(SMALL_WG), args, 0, st);
 }
 
 int small_mega_occupancy() {
-  int occ = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_small_mega, SMALL_WG, 0) != hipSuccess)
-    return 0;
-  return occ;
+  // the smallest over the three instances
+  int best = 1 << 30;
+  for (int f : {WF_FP8, WF_NVFP4, WF_BF16}) {
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, mega_kernel(f), SMALL_WG, 0) != hipSuccess) return 0;
+    best = occ < best ? occ : best;
+  }
+  return best;
 }
 
 // ---------------------------------------------------------------------------

@@ -93,8 +93,8 @@ typedef struct {
   float rope_theta;  /* 10000 */
   float rms_eps;     /* 1e-6 */
   int body_quant;    /* KD_QUANT_FP8_BLOCK64 (default), or KD_QUANT_NVFP4 /
-                        KD_QUANT_BF16 (these run the general path at every
-                        batch size) */
+                        KD_QUANT_BF16 (every body format runs on both the
+                        small-batch and the general path) */
   int head_quant;    /* KD_QUANT_NVFP4, or KD_QUANT_BF16 / KD_QUANT_FP8_BLOCK64
                         (the card's Use section offers bf16, FP8 and NVFP4
                         head slices; every head runs on both the small-batch

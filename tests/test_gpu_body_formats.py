@@ -2,7 +2,9 @@
 block drafter", section Use: the block body can be served in bf16, FP8 or
 NVFP4; FP8 is the serving default).
 
-These bodies run the general path at every batch size. NVFP4 codes times
+Up to 4 streams these bodies run in the small-batch path's projection units
+(per-phase launches, path 2, and the persistent kernel, path 3), above 4 in
+the general path's tiled kernels. NVFP4 codes times
 their e4m3 block scale decode exactly to f16 for the f16 matrix cores, and
 each matrix's fp32 tensor scale multiplies the fp32 partial sums (the
 predecessor adapter joins two matrices with their own tensor scales along
@@ -16,6 +18,7 @@ from __future__ import annotations
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 import synth
@@ -32,13 +35,42 @@ def hb(request):
     return Harness("C", max_streams=256, body=request.param)
 
 
-def test_body_b4_and_b1(hb):
-    for cfg in (C[1], C[0]):
-        inp = hb.inputs(cfg)
-        lg, ids = hb.run(inp)
-        assert hb.drafter.last_path() == 1
-        ref, rid = oracle.oracle_round(hb.oracle, synth.to_numpy_inputs(inp))
-        compare(lg, ids, ref, rid, hb.oracle.vocab, f"{hb.body} body {cfg['name']}")
+@pytest.mark.parametrize("path", [1, 2, 3])
+def test_body_b4_and_b1(hb, path):
+    hb.drafter.debug_set_path(path)
+    try:
+        for cfg in (C[1], C[0]):
+            inp = hb.inputs(cfg)
+            lg, ids = hb.run(inp)
+            assert hb.drafter.last_path() == path
+            ref, rid = oracle.oracle_round(hb.oracle, synth.to_numpy_inputs(inp))
+            compare(lg, ids, ref, rid, hb.oracle.vocab, f"{hb.body} body {cfg['name']} path {path}")
+    finally:
+        hb.drafter.debug_set_path(0)
+
+
+def test_small_path_bodies_agree_bitwise_and_per_stream(hb):
+    """Paths 2 and 3 run the same phase code: identical logits; a stream
+    drafted alone equals the same stream in a batch of 4; the small-path
+    adapters with their gains (model C) on a ragged batch."""
+    cfg = dict(name=f"{hb.body} small", streams=4, lens=("uniform", 10, 2600), model="C", ingest=0)
+    inp = hb.inputs(cfg, base=29)
+    out = {}
+    for path in (2, 3):
+        hb.drafter.debug_set_path(path)
+        try:
+            out[path] = hb.run(inp)
+        finally:
+            hb.drafter.debug_set_path(0)
+    assert np.array_equal(out[2][0], out[3][0]) and np.array_equal(out[2][1], out[3][1])
+    ref, rid = oracle.oracle_round(hb.oracle, synth.to_numpy_inputs(inp))
+    compare(out[2][0], out[2][1], ref, rid, hb.oracle.vocab, f"{hb.body} body ragged B4, small path")
+    one = {k: (v[2:3] if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    one["k"] = [t[2:3] for t in inp["k"]]
+    one["v"] = [t[2:3] for t in inp["v"]]
+    one["streams"] = 1
+    lg1, ids1 = hb.run(one)
+    assert np.array_equal(lg1[0], out[2][0][2]) and np.array_equal(ids1[0], out[2][1][2])
 
 
 def test_body_context_edges(hb):
