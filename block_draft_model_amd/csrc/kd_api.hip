@@ -891,7 +891,6 @@ static kd_status round_impl(kd_ctx* c, int depth, int B, const void* taps, const
   if (!c->small_ok) path = 1;
   if (path == 3 && !c->mega_ok) path = 2;
   if (path != 1 && B > kd::SB_MAX) path = 1;
-  if (k.fmt == KD_KV_INT4_ROT) path = 1;   // the 4-bit cache is read by the general path
   c->last_path = path;
   if (path != 1) {
     (void)hipGetLastError();

@@ -307,6 +307,63 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 }
 
 // ---------------------------------------------------------------------------
+// Rotated 4-bit K/V (the 4-bit KV article, "What we do": keys turned by a
+// signed Walsh-Hadamard rotation, every row coded to 4 bits with an fp16
+// scale and offset per row and head).
+// ---------------------------------------------------------------------------
+// In-wave Walsh-Hadamard transform of 128 values: lane l holds x[l] (y0) and
+// x[l + 64] (y1) and ends with (H x)[l], (H x)[l + 64], H[i][k] =
+// (-1)^popcount(i & k). One butterfly per index bit: (a, c) -> (a + c, a - c)
+// for the pair differing in that bit; bit 6 pairs the two registers, bits
+// 5..0 pair lanes.
+__device__ __forceinline__ void fwht128(float& y0, float& y1, int lane) {
+  const float a = y0, c = y1;
+  y0 = a + c;
+  y1 = a - c;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const float p0 = __shfl_xor(y0, m, 64), p1 = __shfl_xor(y1, m, 64);
+    const bool up = (lane & m) != 0;
+    y0 = up ? p0 - y0 : y0 + p0;
+    y1 = up ? p1 - y1 : y1 + p1;
+  }
+}
+
+// 8 4-bit codes (one dword, dim 2i in the low nibble of byte i) -> 8 f16
+// values code * 2^-24: each code becomes the mantissa of an f16 subnormal
+// (exact; the matrix cores take f16 subnormals as they are). Users scale
+// the products by 2^24.
+__device__ __forceinline__ f16x8 nib8_f16(uint32_t w) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  const f16x2 p0 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(hi, lo, 0x0C040C00u));
+  const f16x2 p1 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(hi, lo, 0x0C050C01u));
+  const f16x2 p2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(hi, lo, 0x0C060C02u));
+  const f16x2 p3 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(hi, lo, 0x0C070C03u));
+  return f16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+constexpr float KD_2P24 = 16777216.0f;
+
+// (scale, offset) fp16 pair in one dword -> two floats.
+__device__ __forceinline__ void so_unpack(uint32_t w, float& sc, float& of) {
+  sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+  of = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma_16x16x16_f16(f16x4 a, f16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+// Byte m of x0 and of x1 (each a code 0..15) -> f16x2 of the two codes
+// times 2^-24 (f16 subnormals, as in nib8_f16).
+template <int M>
+__device__ __forceinline__ f16x2 byte_pair_f16(uint32_t x0, uint32_t x1) {
+  constexpr uint32_t sel = 0x0C000C00u | ((uint32_t)(4 + M) << 16) | (uint32_t)M;
+  return __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(x1, x0, sel));
+}
+
+// ---------------------------------------------------------------------------
 // Output-row order of the repacked q|k|v and gate|up matrices.
 //
 // q|k|v: a 16-row tile holds 8 dims of one head and their rotate-half

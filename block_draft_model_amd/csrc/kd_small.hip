@@ -1206,6 +1206,100 @@ __device__ __forceinline__ void att_read_mlo(unsigned ma, unsigned oa, float (&m
 // partial per segment, stored at the slot of the segment's first chunk; the
 // pair's counter then counts the segment, and a designated workgroup per
 // (stream, head) merges its segments with the block's own keys.
+// The chunk's partial: thread (j, d) merges the 8 waves' (max, sum, output)
+// of row j, dim d that the caller left in LDS (max at s_m + 16 w + j, sum at
+// s_m + 32 + ..., output at s_o + (4 w + j) DH + d) and stores them in the
+// chunk's slot: three store instructions per wave, counted by the caller.
+__device__ __forceinline__ void chunk_partial_store(Args& a, int l, int b, int h, int seg_c0, lds_f s_m,
+                                                    lds_f s_o) {
+  auto& s = a.s;
+  const int lane = threadIdx.x & 63;
+  const int nch = a.nch;
+  // thread (j, d): merge of the 8 waves, stored as the segment's partial
+  const int j = threadIdx.x >> 7, dd = threadIdx.x & 127;
+  float mw[8], lw[8], ow[8];
+  att_read_mlo((unsigned)(uintptr_t)(s_m + j), (unsigned)(uintptr_t)(s_o + j * DH + dd), mw, lw, ow);
+  float M = -__builtin_inff();
+#pragma unroll
+  for (int w = 0; w < 8; ++w) M = fmaxf(M, mw[w]);
+  float Ls = 0.f, O = 0.f;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    if (mw[w] != -__builtin_inff()) {
+      const float f = exp2f(mw[w] - M);
+      Ls += lw[w] * f;
+      O += ow[w] * f;
+    }
+  }
+  // three store instructions per wave: the output by every lane, the max
+  // and sum of row j by lane 0 (waves 2j and 2j + 1 store the same values)
+  const size_t pb = ((size_t)(b * NH + h) * nch + seg_c0) * 4 + j;
+  att_store(s.ao[l] + pb * DH + dd, O);
+  if (lane == 0) {
+    att_store(s.am[l] + pb, M);
+    att_store(s.al[l] + pb, Ls);
+  }
+}
+
+// After a workgroup's chunks: its completion counters (one per (stream, head)
+// and layer, once every partial store is done); then the non-merging
+// workgroups warm the next phases' weights and the merging ones merge their
+// pair once its counter shows every segment stored.
+__device__ __forceinline__ void attn_finish(Args& a, int l, const StreamLens& sl, int ub, int ue, BlockRows& br,
+                                            SyncState sy, bool sync) {
+  const int G = gridDim.x, wg = blockIdx.x;
+  auto& s = a.s;
+  const int nbh = a.B * NH, mi = wg;
+  const bool merges = wg < nbh;
+  // completion counters: one per (stream, head) and layer, counting the
+  // segments; taken once every partial store of the workgroup is done
+  __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0): stores acknowledged
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int u = ub; u < ue;) {
+      int b, c, h;
+      sl.unit(u, b, c, h);
+      (void)add_rlx(&s.att_cnt[((l * SB_MAX + b) * NH + h) * 32], 1u);
+      u += sl.chunks(b) - c;
+    }
+  }
+  trace_mark(a, sy, 5);
+  // The other workgroups warm the next phases' weights on the XCDs that will
+  // read them: the output projection (one tile per unit) and gate|up (three).
+  if (!merges && !sync) {
+    auto& L = a.d.layer[l];
+    warm(nbh, HT, [&](int u) { touch_tiles(L.wo, u, 1, 0, H / 64); });
+    warm(nbh, GU / 16 / 3, [&](int u) { touch_tiles(L.gu, 3 * u, 3, 0, H / 64); });
+    warm_done();
+  }
+  // Merge: one (stream, head) per workgroup, all in parallel, once its
+  // counter shows every segment stored. The merging workgroup resets the
+  // counter for the next round. Streams with an empty context attend to the
+  // block only.
+  if (merges) {
+    const int b = mi / NH, h = mi % NH, n = sl.vis(b);
+    const int u0 = n > 0 ? sl.first_unit(b, h) : 0;
+    const BlockPart bp = attn_block(br, (lds_f)g_att_small);
+    if (n > 0) {
+      if (threadIdx.x == 0) {
+        auto cnt = &s.att_cnt[((l * SB_MAX + b) * NH + h) * 32];
+        const unsigned need = (unsigned)sl.segments(u0, sl.chunks(b), G);
+        const unsigned long long t0 = wall_clock64();
+        for (unsigned it = 1; ld_rlx(cnt) < need; ++it) {
+          if ((it & 63) == 0 && wall_clock64() - t0 > 20000000ull) {  // 0.2 s
+            __hip_atomic_store(&s.bar[18 * 32], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+        }
+        __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      lds_sync();
+    }
+    attn_merge(a, l, b, h, n, bp);
+  }
+}
+
 __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int l_, SyncState sy,
                                                   bool sync) {
   const auto l = uni(l_);
@@ -1473,81 +1567,254 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
       *reinterpret_cast<KD_LDS f32x4*>(s_o + (wave * 4 + lg) * DH + 8 * lr + 4) = r2b;
       if (lr < 4 && lg == 0) att_write_ml((unsigned)(uintptr_t)(s_m + wave * 4 + lr), m_run, l_run);
       lds_sync();
-      // thread (j, d): merge of the 8 waves, stored as the segment's partial
-      const int j = threadIdx.x >> 7, dd = threadIdx.x & 127;
-      float mw[8], lw[8], ow[8];
-      att_read_mlo((unsigned)(uintptr_t)(s_m + j), (unsigned)(uintptr_t)(s_o + j * DH + dd), mw, lw, ow);
-      float M = -__builtin_inff();
-#pragma unroll
-      for (int w = 0; w < 8; ++w) M = fmaxf(M, mw[w]);
-      float Ls = 0.f, O = 0.f;
-#pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        if (mw[w] != -__builtin_inff()) {
-          const float f = exp2f(mw[w] - M);
-          Ls += lw[w] * f;
-          O += ow[w] * f;
-        }
-      }
-      // three store instructions per wave: the output by every lane, the max
-      // and sum of row j by lane 0 (waves 2j and 2j + 1 store the same values)
-      const size_t pb = ((size_t)(b * NH + h) * nch + seg_c0) * 4 + j;
-      att_store(s.ao[l] + pb * DH + dd, O);
-      if (lane == 0) {
-        att_store(s.am[l] + pb, M);
-        att_store(s.al[l] + pb, Ls);
-      }
+      chunk_partial_store(a, l, b, h, seg_c0, s_m, s_o);
       stores = 3;
       // the next chunk waits at a barrier before it reuses the LDS areas
     }
   }
-  // completion counters: one per (stream, head) and layer, counting the
-  // segments; taken once every partial store of the workgroup is done
-  __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0): stores acknowledged
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int u = ub; u < ue;) {
-      int b, c, h;
-      sl.unit(u, b, c, h);
-      (void)add_rlx(&s.att_cnt[((l * SB_MAX + b) * NH + h) * 32], 1u);
-      u += sl.chunks(b) - c;
-    }
+  attn_finish(a, l, sl, ub, ue, br, sy, sync);
+  trace_mark(a, sy, 6);
+  trace_mark(a, sy, 4);
+}
+
+// Attention over the rotated 4-bit cache (the 4-bit KV article, "What we do"):
+// the same units, per-chunk partials, counters and merges as ph_attn. Per unit
+// wave w takes the chunk's keys 16 w .. 16 w + 15 straight into registers
+// (buffer loads: K codes, V codes, each key's fp16 scale and offset), one unit
+// ahead. Where the (stream, head) pair changes, waves 0..3 turn the block rows'
+// queries by the layer's rotation (signs, then an in-wave Walsh-Hadamard
+// transform) into LDS, and every wave takes them as the B operand (f16 hi +
+// lo). Scores = scale * (q_rot . codes) + offset * sum(q_rot), with the codes
+// as f16 subnormals on the matrix cores; P V on the matrix cores as well
+// (16x16x16, V codes as the A operand, p * scale as the B operand), the
+// offsets' share added per row.
+__device__ __attribute__((noinline, not_tail_called)) void ph_attn_q4(Args& a_, int l_, SyncState sy,
+                                                     bool sync) {
+  const auto l = uni(l_);
+  Args& a = uni(a_);
+  const int G = gridDim.x, wg = blockIdx.x;
+  auto& s = a.s;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wave_s = uni(wave);
+  const int lr = lane & 15, lg = lane >> 4;
+  const float qs = 0.08838834764831845f * 1.4426950408889634f;
+  lds_f s_o = (lds_f)g_att_small;      // [8][4][128] per-wave outputs
+  lds_f s_m = s_o + 8 * 4 * DH;        // [8][4] maxima, then [8][4] sums
+  lds_f s_q = (lds_f)&g_att_ring[0][0][0];   // [4][128] rotated queries, then [4] their sums
+  lds_f s_qs = s_q + 4 * DH;
+
+  StreamLens sl;
+  sl.load(a);  // an input: read before the arrival
+  const int U = sl.total;
+  const int ub = U > 0 ? sl.start(wg, G) : 0, ue = U > 0 ? sl.start(wg + 1, G) : 0;
+  const uint8_t* k_l = reinterpret_cast<const uint8_t*>(a.kv.k[l]);
+  const uint8_t* v_l = reinterpret_cast<const uint8_t*>(a.kv.v[l]);
+  const uint16_t* ks_l = a.kv.kso[l];
+  const uint16_t* vs_l = a.kv.vso[l];
+  const long long kv_ss = a.kv.ss, kv_sh = a.kv.sh;
+  const uint32_t kv_sl = (uint32_t)a.kv.sl;
+  const int kv_cap = a.kv.cap;
+  const uint32_t span = (uint32_t)((kv_cap - 1) * a.kv.sl + 1);   // rows of one (stream, head)
+  auto q_l = s.q[l];
+  const float* signs = a.d.kv_signs + l * DH;
+
+  // Unit u's keys for this wave, straight into registers; keys past the
+  // visible rows are clamped to the last one and masked in the scores. The
+  // rows of one (stream, head) are read through buffer resources (32-bit
+  // offsets; the hardware returns 0 past the span, which the host checks
+  // fits 4 GiB).
+  struct KvRegs {
+    u32x4 k;          // key lr's codes, dims 32 lg ..
+    uint32_t v[4];    // keys 4 lg + t, dims 8 lr ..
+    uint32_t ks, vs;  // key lr's (scale, offset) pairs
+  };
+  auto load_unit = [&](int u, KvRegs& r) __attribute__((always_inline)) {
+    int b, c, h;
+    sl.unit(u, b, c, h);
+    const int n = sl.vis(b), fp = sl.first(b);
+    const size_t row0 = (size_t)(b * kv_ss + h * kv_sh);
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(k_l + row0 * 64), (short)0, span * 64, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(v_l + row0 * 64), (short)0, span * 64, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rks =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(ks_l + row0 * 2), (short)0, span * 4, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rvs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vs_l + row0 * 2), (short)0, span * 4, 0x00020000);
+    const int s0 = (fp + c * ATT_CH) % kv_cap;
+    const int last = n - 1 - c * ATT_CH;
+    auto row_of = [&](int off) {
+      const int r_ = s0 + min(off, last);
+      return (uint32_t)(r_ - (r_ >= kv_cap ? kv_cap : 0)) * kv_sl;
+    };
+    const uint32_t rk0 = row_of(wave * 16 + lr);
+    r.k = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, rk0 * 64 + 16 * lg, 0, 0));
+    r.ks = __builtin_amdgcn_raw_buffer_load_b32(rks, rk0 * 4, 0, 0);
+    r.vs = __builtin_amdgcn_raw_buffer_load_b32(rvs, rk0 * 4, 0, 0);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      r.v[t] = __builtin_amdgcn_raw_buffer_load_b32(rv, row_of(wave * 16 + 4 * lg + t) * 64 + 4 * lr, 0, 0);
+  };
+
+  const int nbh = a.B * NH;
+  const int mi = wg;
+  const bool merges = wg < nbh;
+  BlockRows br{};
+  if (merges && !sync) br.load(a, l, mi / NH, mi % NH);
+  if (sync) {
+    grid_arrive(a, sy);
+    if (is_poll_wave()) grid_poll(a, sy);
   }
-  trace_mark(a, sy, 5);
-  // The other workgroups warm the next phases' weights on the XCDs that will
-  // read them: the output projection (one tile per unit) and gate|up (three).
-  if (!merges && !sync) {
-    auto& L = a.d.layer[l];
-    warm(nbh, HT, [&](int u) { touch_tiles(L.wo, u, 1, 0, H / 64); });
-    warm(nbh, GU / 16 / 3, [&](int u) { touch_tiles(L.gu, 3 * u, 3, 0, H / 64); });
-    warm_done();
+  KvRegs cur, nxt;
+  const int ulast = max(ue - 1, ub);
+  if (ub < ue) load_unit(ub, cur);
+  if (sync) {
+    lds_sync();
+    if (merges) br.load(a, l, mi / NH, mi % NH);
   }
-  // Merge: one (stream, head) per workgroup, all in parallel, once its
-  // counter shows every segment stored. The merging workgroup resets the
-  // counter for the next round. Streams with an empty context attend to the
-  // block only.
-  if (merges) {
-    const int b = mi / NH, h = mi % NH, n = sl.vis(b);
-    const int u0 = n > 0 ? sl.first_unit(b, h) : 0;
-    const BlockPart bp = attn_block(br, (lds_f)g_att_small);
-    if (n > 0) {
-      if (threadIdx.x == 0) {
-        auto cnt = &s.att_cnt[((l * SB_MAX + b) * NH + h) * 32];
-        const unsigned need = (unsigned)sl.segments(u0, sl.chunks(b), G);
-        const unsigned long long t0 = wall_clock64();
-        for (unsigned it = 1; ld_rlx(cnt) < need; ++it) {
-          if ((it & 63) == 0 && wall_clock64() - t0 > 20000000ull) {  // 0.2 s
-            __hip_atomic_store(&s.bar[18 * 32], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
-          }
-          __builtin_amdgcn_s_sleep(2);
-        }
-        __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  trace_mark(a, sy, 2);
+
+  f16x8 qh[4], ql[4];
+  float qsum = 0.f;
+  int stores = 0;
+  for (int u = ub; u < ue; ++u) {
+    int b, c, h;
+    sl.unit(u, b, c, h);
+    const int n = sl.vis(b);
+    const bool new_pair = u == ub || c == 0;
+    // the next unit's keys go out before this one is computed
+    load_unit(min(u + 1, ulast), nxt);
+    (void)stores;
+    if (new_pair) {
+      // the previous chunk's readers of the shared LDS areas are done
+      if (u != ub) lds_sync();
+      if (wave_s < BLK) {
+        // wave j turns block row j's query: R q = H (s * q) / sqrt(128),
+        // scaled like the scores (1/sqrt(128) * log2(e))
+        const float* qp = q_l + (size_t)(b * BLK + wave_s) * H + h * DH;
+        float y0 = qp[lane] * signs[lane], y1 = qp[lane + 64] * signs[lane + 64];
+        fwht128(y0, y1, lane);
+        const float f = 0.08838834764831845f * qs;
+        y0 *= f;
+        y1 *= f;
+        s_q[wave_s * DH + lane] = y0;
+        s_q[wave_s * DH + lane + 64] = y1;
+        const float t = wave_sum(y0 + y1);
+        if (lane == 0) s_qs[wave_s] = t;
       }
       lds_sync();
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = lr < BLK ? s_q[lr * DH + 32 * lg + 8 * kb + e] : 0.f;
+          const _Float16 hh = (_Float16)v;
+          qh[kb][e] = hh;
+          ql[kb][e] = (_Float16)(v - (float)hh);
+        }
+      qsum = lr < BLK ? s_qs[lr] : 0.f;
     }
-    attn_merge(a, l, b, h, n, bp);
+    if (u == ub) trace_mark(a, sy, 3);
+    // the scale and offset pairs of keys 4 lg + e come from lanes 4 lg + e
+    uint32_t ks[4], vs[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ks[e] = __shfl(cur.ks, 4 * lg + e, 64);
+      vs[e] = __shfl(cur.vs, 4 * lg + e, 64);
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const f16x8 kk = nib8_f16(cur.k[kb]);
+      acc = mfma_f16(kk, qh[kb], acc);
+      acc = mfma_f16(kk, ql[kb], acc);
+    }
+    // lane (lr, lg): acc[e] = q_rot[lr] . codes[key 4 lg + e] * 2^-24
+    float sc[4], mx = -__builtin_inff();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float ksc, kof;
+      so_unpack(ks[e], ksc, kof);
+      const int key = c * ATT_CH + wave * 16 + 4 * lg + e;
+      sc[e] = key < n ? (ksc * KD_2P24) * acc[e] + kof * qsum : -__builtin_inff();
+      mx = fmaxf(mx, sc[e]);
+    }
+    {
+      float r0, r1;
+      pl16(mx, mx, r0, r1);
+      mx = fmaxf(r0, r1);
+      pl32(mx, mx, r0, r1);
+      mx = fmaxf(r0, r1);
+    }
+    // every chunk is a segment of its own: the wave's state starts here
+    f16x4 pb;
+    float ls = 0.f, ws = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p = sc[e] == -__builtin_inff() ? 0.f : exp2f(sc[e] - mx);
+      float vsc, vof;
+      so_unpack(vs[e], vsc, vof);
+      ls += p;
+      ws += p * vof;
+      pb[e] = (_Float16)(p * vsc);
+    }
+    {
+      float r0, r1;
+      pl16(ls, ls, r0, r1);
+      ls = r0 + r1;
+      pl32(ls, ls, r0, r1);
+      ls = r0 + r1;
+      pl16(ws, ws, r0, r1);
+      ws = r0 + r1;
+      pl32(ws, ws, r0, r1);
+      ws = r0 + r1;
+    }
+    // even nibbles (dims 8 lr + 2m) and odd nibbles (8 lr + 2m + 1) per key
+    uint32_t ev[4], od[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ev[e] = cur.v[e] & 0x0F0F0F0Fu;
+      od[e] = (cur.v[e] >> 4) & 0x0F0F0F0Fu;
+    }
+    f32x4 oa[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) oa[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#define KD_PV_TILE(T, X, M)                                                    \
+  {                                                                            \
+    const f16x2 lo = byte_pair_f16<M>(X[0], X[1]);                             \
+    const f16x2 hi = byte_pair_f16<M>(X[2], X[3]);                             \
+    oa[T] = mfma_16x16x16_f16(f16x4{lo.x, lo.y, hi.x, hi.y}, pb, oa[T]);       \
   }
+    KD_PV_TILE(0, ev, 0)
+    KD_PV_TILE(1, od, 0)
+    KD_PV_TILE(2, ev, 1)
+    KD_PV_TILE(3, od, 1)
+    KD_PV_TILE(4, ev, 2)
+    KD_PV_TILE(5, od, 2)
+    KD_PV_TILE(6, ev, 3)
+    KD_PV_TILE(7, od, 3)
+#undef KD_PV_TILE
+    // the previous chunk's readers of the shared LDS areas are done (a new
+    // pair's query read above waited for them already)
+    if (!new_pair) lds_sync();
+    // lane (lr < 4, lg) holds dims 32 lg + 8 e + t of row lr, times 2^-24
+    if (lr < BLK) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float v[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) v[t] = oa[t][e] * KD_2P24 + ws;
+        lds_f dst = s_o + (wave * 4 + lr) * DH + 32 * lg + 8 * e;
+        *reinterpret_cast<KD_LDS f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<KD_LDS f32x4*>(dst + 4) = f32x4{v[4], v[5], v[6], v[7]};
+      }
+      if (lg == 0) att_write_ml((unsigned)(uintptr_t)(s_m + wave * 4 + lr), mx, ls);
+    }
+    lds_sync();
+    chunk_partial_store(a, l, b, h, c, s_m, s_o);
+    cur = nxt;
+  }
+  attn_finish(a, l, sl, ub, ue, br, sy, sync);
   trace_mark(a, sy, 6);
   trace_mark(a, sy, 4);
 }
@@ -2014,7 +2281,9 @@ __device__ void run_phase(Args& a, int p, lds_f red, SyncState sy, bool sync) {
     case PH_SA: return ph_sa<WF>(a, l, red, sy, sync);
     case PH_SU: return ph_su<WF>(a, l, red, sy, sync);
     case PH_QKV: return ph_qkv<WF>(a, l, red, sy, sync);
-    case PH_ATTN: return ph_attn(a, l, sy, sync);
+    case PH_ATTN:
+      if (uni(a.kv.fmt) == 1) return ph_attn_q4(a, l, sy, sync);
+      return ph_attn(a, l, sy, sync);
     case PH_O: return ph_o<WF>(a, l, red, sy, sync);
     case PH_GU: return ph_gu<WF>(a, l, red, sy, sync);
     case PH_DOWN: return ph_down<WF>(a, l, red, sy, sync);

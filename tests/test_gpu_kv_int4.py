@@ -58,6 +58,48 @@ def test_int4_round_context_length_edges(hC):
     compare(lg, ids, ref, rid, hC.oracle.vocab, "int4 length edges")
 
 
+@pytest.mark.parametrize("path", [1, 2, 3])
+def test_int4_small_batches(hC, path):
+    """Up to 4 streams the 4-bit cache runs in the small-batch path's
+    attention phase (path 2 per-phase launches, path 3 the persistent
+    kernel): context-length edges (empty, one row, 16-key and 128-key
+    boundaries, the full window, past the ring's capacity) and B = 1."""
+    hC.drafter.debug_set_path(path)
+    try:
+        for i, lens in enumerate(([0, 1, 15, 16], [17, 129, 2047, 6000], [2048])):
+            cfg = dict(name=f"int4 small {lens}", streams=len(lens), lens=("const", 0), model="C", ingest=0)
+            inp = hC.inputs(cfg, base=40 + i, lens_override=lens, kv="int4")
+            lg, ids = hC.run(inp)
+            assert hC.drafter.last_path() == path
+            ref, rid = oracle.oracle_round(hC.oracle, synth.to_numpy_inputs(inp))
+            compare(lg, ids, ref, rid, hC.oracle.vocab, f"int4 path {path} lens {lens}")
+    finally:
+        hC.drafter.debug_set_path(0)
+
+
+def test_int4_small_path_bitwise(hC):
+    """Paths 2 and 3 run the same phase code (identical logits); a stream
+    alone equals the same stream in a batch of 4 (its chunk partials do not
+    depend on the batch)."""
+    cfg = dict(name="int4 inv", streams=4, lens=("uniform", 10, 2600), model="C", ingest=0)
+    inp = hC.inputs(cfg, base=44, kv="int4")
+    out = {}
+    for path in (2, 3):
+        hC.drafter.debug_set_path(path)
+        try:
+            out[path] = hC.run(inp)
+        finally:
+            hC.drafter.debug_set_path(0)
+    assert np.array_equal(out[2][0], out[3][0]) and np.array_equal(out[2][1], out[3][1])
+    for b in (0, 3):
+        one = {k: (v[b:b + 1] if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+        for key in ("k", "v", "k_so", "v_so"):
+            one[key] = [t[b:b + 1] for t in inp[key]]
+        one["streams"] = 1
+        lg1, ids1 = hC.run(one)
+        assert np.array_equal(lg1[0], out[2][0][b]) and np.array_equal(ids1[0], out[2][1][b])
+
+
 def test_int4_round_b16_ragged(hC):
     inp = hC.inputs(C[2], kv="int4")
     log("int4 B16 lens", inp["lens"].cpu().numpy().tolist())
