@@ -590,6 +590,9 @@ kd_status kd_create(const kd_config* cfg, void* hip_stream, kd_ctx** out) {
             dev_alloc(c->work_allocs, &w.att_l, (size_t)w.Bmax * kd::NH * w.att_nch * kd::BLK) &&
             dev_alloc(c->work_allocs, &w.att_o,
                       (size_t)w.Bmax * kd::NH * w.att_nch * kd::BLK * kd::DH) &&
+            dev_alloc(c->work_allocs, &w.att_cnt, (size_t)w.Bmax * kd::NH * 32) &&
+            hipMemset(w.att_cnt, 0, (size_t)w.Bmax * kd::NH * 32 * sizeof(unsigned)) == hipSuccess &&
+            hipDeviceSynchronize() == hipSuccess &&
             dev_alloc(c->work_allocs, &w.keys, (size_t)w.Rmax) &&
             dev_alloc(c->work_allocs, &w.copy_keys, (size_t)2 * w.Bmax);
   hipDeviceProp_t prop;

@@ -354,7 +354,9 @@ void launch_qkv_post(hipStream_t st, const Work& w, int B, int splits) {
 // Cross-attention over the context window (model card, Architecture, Body:
 // every block row attends to the last window rows of its stream's cached K/V
 // and causally to the block). A workgroup takes one segment of one (stream,
-// head): S segments split the window's 16-key blocks evenly. Wave w takes the
+// head): segments of equal length (segb 16-key blocks, chosen per launch so
+// that a full window gives enough workgroups to fill the chip), as many as
+// the stream's visible context needs. Wave w takes the
 // segment's blocks w, w + 4, ..., with the next block's keys and values in
 // flight while one is computed:
 //   scores  S^T[key][j] = K Q^T on the matrix cores (16x16x32 bf16): keys as
@@ -368,7 +370,8 @@ void launch_qkv_post(hipStream_t st, const Work& w, int B, int splits) {
 // The 4 waves' states are merged in LDS. With one segment the workgroup also
 // adds the block's own keys (row j sees block rows 0..j), normalises, and
 // writes the output rows; otherwise it stores the segment's max m, sum l and
-// unnormalised output o for k_attn_combine.
+// unnormalised output o, and the workgroup that stores the pair's last
+// segment merges them with the block's own keys.
 // ---------------------------------------------------------------------------
 struct AttnK {
   const float* q;
@@ -380,11 +383,13 @@ struct AttnK {
   const uint16_t* vso;
   const float* signs;     // rotated 4-bit cache: the layer's [DH] signs
   int64_t ss, sh, sl;
-  int cap, window, nch, S;
+  int cap, window, nch;
+  int segb;               // 16-key blocks per segment (a pair has ceil(blocks / segb) segments)
   const int32_t* lens;
   float* pm;
   float* pl;
   float* po;
+  unsigned* cnt;          // [B][NH][32] segments stored per pair, zero between launches
   uint16_t* af_o;
 };
 
@@ -418,14 +423,15 @@ struct AttnLds {
   float o[4][BLK][DH];           // per wave: unnormalised output of each row
   float m[4][BLK], l[4][BLK];    // per wave: running max and sum of each row
   float blk[BLK * BLK];          // the block's own scores
+  int last;                      // this workgroup stored its pair's last segment
 };
 
 __device__ __forceinline__ void attn_merge(const AttnK& a, AttnLds& s, float m_run, float l_run,
-                                           int seg, int h, int b, size_t qrow0);
+                                           int seg, int nseg, int h, int b, size_t qrow0);
 
 __device__ __forceinline__ void attn_finish(const AttnK& a, AttnLds& s, float (&o)[BLK][8],
-                                            float m_run, float l_run, int seg, int h, int b,
-                                            size_t qrow0) {
+                                            float m_run, float l_run, int seg, int nseg, int h,
+                                            int b, size_t qrow0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   // sum the 4 key groups of the wave: lanes lg = 0 end with o[j][8 lr + e]
@@ -443,33 +449,43 @@ __device__ __forceinline__ void attn_finish(const AttnK& a, AttnLds& s, float (&
       *reinterpret_cast<f32x4*>(&s.o[wave][j][8 * lr + 4]) = f32x4{o[j][4], o[j][5], o[j][6], o[j][7]};
     }
   }
-  attn_merge(a, s, m_run, l_run, seg, h, b, qrow0);
+  attn_merge(a, s, m_run, l_run, seg, nseg, h, b, qrow0);
+}
+
+// The block's own scores s.blk[j][i] (i <= j), scaled like the context's:
+// wave j, lane l covers dims 2l, 2l+1.
+__device__ __forceinline__ void attn_block_scores(const AttnK& a, AttnLds& s, size_t qrow0) {
+  const int lane = threadIdx.x & 63, j = threadIdx.x >> 6;
+  const float qs = 0.08838834764831845f * 1.4426950408889634f;  // 1/sqrt(128) * log2(e)
+  const float q0 = a.q[qrow0 + (size_t)j * H + 2 * lane], q1 = a.q[qrow0 + (size_t)j * H + 2 * lane + 1];
+#pragma unroll
+  for (int i = 0; i < BLK; ++i) {
+    if (i > j) break;
+    const float* kp = a.kb + qrow0 + (size_t)i * H + 2 * lane;
+    const float p = wave_sum(q0 * kp[0] + q1 * kp[1]);
+    if (lane == 0) s.blk[j * BLK + i] = p * qs;
+  }
 }
 
 // Wave w's s.o[w] must hold its rows' unnormalised outputs; m_run / l_run
-// are row lr's (lanes lr < 4). Merges the 4 waves and finishes the segment.
+// are row lr's (lanes lr < 4). Merges the 4 waves and finishes the segment:
+// a pair with one segment adds the block's own keys and writes the output
+// rows; otherwise the segment's (m, l, o) is stored (written through to the
+// device-coherent level), the pair's counter counts it, and the workgroup
+// that stores the pair's last segment merges all of them in segment order
+// (so the result does not depend on which one that is) and resets the
+// counter for the next launch.
 __device__ __forceinline__ void attn_merge(const AttnK& a, AttnLds& s, float m_run, float l_run,
-                                           int seg, int h, int b, size_t qrow0) {
+                                           int seg, int nseg, int h, int b, size_t qrow0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const float qs = 0.08838834764831845f * 1.4426950408889634f;  // 1/sqrt(128) * log2(e)
   // row lr's max and sum live in every lane with lane % 16 == lr
   if (lane < BLK) {
     s.m[wave][lane] = m_run;
     s.l[wave][lane] = l_run;
   }
-  // the block's own scores s[j][i] (i <= j): wave j, lane l covers dims 2l, 2l+1
-  if (a.S == 1) {
-    const int j = wave;
-    const float q0 = a.q[qrow0 + (size_t)j * H + 2 * lane], q1 = a.q[qrow0 + (size_t)j * H + 2 * lane + 1];
-#pragma unroll
-    for (int i = 0; i < BLK; ++i) {
-      if (i > j) break;
-      const float* kp = a.kb + qrow0 + (size_t)i * H + 2 * lane;
-      const float p = wave_sum(q0 * kp[0] + q1 * kp[1]);
-      if (lane == 0) s.blk[j * BLK + i] = p * qs;
-    }
-  }
+  if (nseg == 1) attn_block_scores(a, s, qrow0);
   __syncthreads();
+  const size_t pair = (size_t)(b * NH + h);
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
     const int j = (threadIdx.x >> 7) + 2 * it, d = threadIdx.x & 127;
@@ -485,17 +501,78 @@ __device__ __forceinline__ void attn_merge(const AttnK& a, AttnLds& s, float m_r
         O += s.o[w][j][d] * f;
       }
     }
-    if (a.S == 1) {
+    if (nseg == 1) {
       const float out = attn_block_merge(s.blk, a.vb, qrow0, j, d, M, L, O);
       a.af_o[afrag_off(b * BLK + j, h * DH + d, H / 32)] = __builtin_bit_cast(uint16_t, f16_checked(out));
     } else {
-      const size_t pb = ((size_t)(b * NH + h) * a.nch + seg) * BLK + j;
-      a.po[pb * DH + d] = O;
+      const size_t pb = (pair * a.nch + seg) * BLK + j;
+      __hip_atomic_store(&a.po[pb * DH + d], O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (d == 0) {
-        a.pm[pb] = M;
-        a.pl[pb] = L;
+        __hip_atomic_store(&a.pm[pb], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&a.pl[pb], L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
+  }
+  if (nseg == 1) return;
+  // count the segment once every store of the workgroup is acknowledged
+  __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0)
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned* cnt = a.cnt + pair * 32;
+    const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = prev == (unsigned)(nseg - 1);
+    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s.last = last;
+  }
+  __syncthreads();
+  if (!s.last) return;
+  // thread (j, d) of rows j = tid / 128 and j + 2: every segment's partial
+  // loaded at once (indices clamped to the last segment, the extra ones
+  // masked; lane c < 16 loads segment c's max and sum of row j, lane 16 + c
+  // those of row j + 2), with the block's own scores in flight, then merged
+  // in segment order
+  constexpr int MAXS = 16;
+  const size_t pbl = pair * a.nch * BLK + (threadIdx.x >> 7) + 2 * ((lane >> 4) & 1) +
+                     (size_t)min(lane & 15, nseg - 1) * BLK;
+  const float m_lane = __hip_atomic_load(&a.pm[pbl], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const float l_lane = __hip_atomic_load(&a.pl[pbl], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  float po[2][MAXS];
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int j = (threadIdx.x >> 7) + 2 * it, d = threadIdx.x & 127;
+    const size_t pb0 = pair * a.nch * BLK + j;
+#pragma unroll
+    for (int c = 0; c < MAXS; ++c) {
+      const size_t pb = pb0 + (size_t)min(c, nseg - 1) * BLK;
+      po[it][c] = __hip_atomic_load(&a.po[pb * DH + d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  attn_block_scores(a, s, qrow0);
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int j = (threadIdx.x >> 7) + 2 * it, d = threadIdx.x & 127;
+    float pm[MAXS], pl[MAXS];
+#pragma unroll
+    for (int c = 0; c < MAXS; ++c) {
+      pm[c] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_lane), 16 * it + c));
+      pl[c] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l_lane), 16 * it + c));
+    }
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int c = 0; c < MAXS; ++c)
+      if (c < nseg) M = fmaxf(M, pm[c]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int c = 0; c < MAXS; ++c) {
+      if (c < nseg && pm[c] != -__builtin_inff()) {
+        const float f = exp2f(pm[c] - M);
+        L += pl[c] * f;
+        O += po[it][c] * f;
+      }
+    }
+    const float out = attn_block_merge(s.blk, a.vb, qrow0, j, d, M, L, O);
+    a.af_o[afrag_off(b * BLK + j, h * DH + d, H / 32)] = __builtin_bit_cast(uint16_t, f16_checked(out));
   }
 }
 
@@ -507,7 +584,11 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnK a) {
   const int len = a.lens[b];
   const int n = min(len, a.window);
   const int nblk = (n + 15) >> 4;
-  const int blk0 = (int)(((long long)seg * nblk) / a.S), blk1 = (int)(((long long)(seg + 1) * nblk) / a.S);
+  // segments of a.segb blocks; workgroups past the pair's last segment have
+  // no work (an empty context still has one segment: the block's own keys)
+  const int nseg = max(1, (nblk + a.segb - 1) / a.segb);
+  if (seg >= nseg) return;
+  const int blk0 = seg * a.segb, blk1 = min(nblk, blk0 + a.segb);
   const float qs = 0.08838834764831845f * 1.4426950408889634f;  // 1/sqrt(128) * log2(e)
   const size_t qrow0 = (size_t)(b * BLK) * H + h * DH;
 
@@ -627,7 +708,7 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnK a) {
       process(bi + 4, kB, vB);
     }
   }
-  attn_finish(a, lds, o, m_run, l_run, seg, h, b, qrow0);
+  attn_finish(a, lds, o, m_run, l_run, seg, nseg, h, b, qrow0);
 }
 
 
@@ -665,7 +746,11 @@ __global__ __launch_bounds__(256) void k_attn_split_q4(AttnK a) {
   const int len = a.lens[b];
   const int n = min(len, a.window);
   const int nblk = (n + 15) >> 4;
-  const int blk0 = (int)(((long long)seg * nblk) / a.S), blk1 = (int)(((long long)(seg + 1) * nblk) / a.S);
+  // segments of a.segb blocks; workgroups past the pair's last segment have
+  // no work (an empty context still has one segment: the block's own keys)
+  const int nseg = max(1, (nblk + a.segb - 1) / a.segb);
+  if (seg >= nseg) return;
+  const int blk0 = seg * a.segb, blk1 = min(nblk, blk0 + a.segb);
   const float qs = 0.08838834764831845f * 1.4426950408889634f;  // 1/sqrt(128) * log2(e)
   const size_t qrow0 = (size_t)(b * BLK) * H + h * DH;
 
@@ -837,71 +922,11 @@ __global__ __launch_bounds__(256) void k_attn_split_q4(AttnK a) {
       *reinterpret_cast<f32x4*>(dst + 4) = f32x4{v[4], v[5], v[6], v[7]};
     }
   }
-  attn_merge(a, lds, m_run, l_run, seg, h, b, qrow0);
+  attn_merge(a, lds, m_run, l_run, seg, nseg, h, b, qrow0);
 }
 
-// Merge of the chunk partials with the block's own keys (row j sees block rows
-// 0..j), normalisation, and afrag of the attention output.
-__global__ __launch_bounds__(128) void k_attn_combine(const float* q, const float* kb,
-                                                      const float* vb, const float* pm,
-                                                      const float* pl, const float* po, int nch,
-                                                      const int32_t* lens, int window,
-                                                      int nseg, uint16_t* af_o) {
-  __shared__ float red[2][10];
-  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = min(lens[b], window);
-  // the segment partials (an empty segment stored m = -inf, l = 0, o = 0)
-  const int nc = n > 0 ? nseg : 0;
-  const float qs = 0.08838834764831845f * 1.4426950408889634f;
-  float qv[BLK], kv[BLK], vv[BLK];
-#pragma unroll
-  for (int j = 0; j < BLK; ++j) {
-    const size_t off = (size_t)(b * BLK + j) * H + h * DH + d;
-    qv[j] = q[off];
-    kv[j] = kb[off];
-    vv[j] = vb[off];
-  }
-  float sb[10];
-  int t = 0;
-#pragma unroll
-  for (int j = 0; j < BLK; ++j)
-#pragma unroll
-    for (int i = 0; i <= j; ++i) sb[t++] = qv[j] * kv[i];
-#pragma unroll
-  for (int t2 = 0; t2 < 10; ++t2) {
-    float v = wave_sum(sb[t2]);
-    if (lane == 0) red[wave][t2] = v;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int t2 = 0; t2 < 10; ++t2) sb[t2] = (red[0][t2] + red[1][t2]) * qs;
-  t = 0;
-#pragma unroll
-  for (int j = 0; j < BLK; ++j) {
-    float M = -__builtin_inff();
-    for (int c = 0; c < nc; ++c) M = fmaxf(M, pm[((size_t)(b * NH + h) * nch + c) * BLK + j]);
-#pragma unroll
-    for (int i = 0; i <= j; ++i) M = fmaxf(M, sb[t + i]);
-    float L = 0.f, O = 0.f;
-    for (int c = 0; c < nc; ++c) {
-      const size_t pb = ((size_t)(b * NH + h) * nch + c) * BLK + j;
-      if (pm[pb] == -__builtin_inff()) continue;
-      const float f = exp2f(pm[pb] - M);
-      L += pl[pb] * f;
-      O += po[pb * DH + d] * f;
-    }
-#pragma unroll
-    for (int i = 0; i <= j; ++i) {
-      const float f = exp2f(sb[t + i] - M);
-      L += f;
-      O += f * vv[i];
-    }
-    t += j + 1;
-    const float out = O / L;
-    af_o[afrag_off(b * BLK + j, h * DH + d, H / 32)] = __builtin_bit_cast(uint16_t, f16_checked(out));
-  }
-}
+// workgroups a full window of every pair is split into (a few per CU)
+constexpr int ATT_WG = 2048;
 
 void launch_attention(hipStream_t st, const Work& w, const DevWeights& dw, int B, const KV& kv,
                       int layer, const int32_t* lens, int window) {
@@ -920,25 +945,26 @@ void launch_attention(hipStream_t st, const Work& w, const DevWeights& dw, int B
   a.cap = kv.cap;
   a.window = window;
   a.nch = w.att_nch;
-  // segments per (stream, head): enough workgroups to fill the chip (about
-  // 1024), at most 8 and at most the partial slots per (stream, head)
+  // segments of equal length (segb blocks of 16 keys): a full window splits
+  // into as many segments as keep the pairs' workgroups at or below ATT_WG
+  // (one segment once the pairs alone reach it), at most the partial slots
+  // per pair; shorter contexts take fewer segments
   const int pairs = B * NH;
-  int S = (1024 + pairs - 1) / pairs;
-  S = S < 1 ? 1 : (S > 8 ? 8 : S);
-  if (S > w.att_nch) S = w.att_nch;
-  a.S = S;
+  const int wb = (window + 15) / 16;
+  int S = ATT_WG / pairs;
+  S = std::max(1, std::min(S, w.att_nch));
+  a.segb = (wb + S - 1) / S;
+  S = (wb + a.segb - 1) / a.segb;
   a.lens = lens;
   a.pm = w.att_m;
   a.pl = w.att_l;
   a.po = w.att_o;
+  a.cnt = w.att_cnt;
   a.af_o = w.af_o;
   if (kv.fmt == 1)
     k_attn_split_q4<<<dim3(S, NH, B), 256, 0, st>>>(a);
   else
     k_attn_split<<<dim3(S, NH, B), 256, 0, st>>>(a);
-  if (S > 1)
-    k_attn_combine<<<dim3(NH, B), 128, 0, st>>>(w.q, w.kb, w.vb, w.att_m, w.att_l, w.att_o,
-                                                w.att_nch, lens, window, S, w.af_o);
 }
 
 // x += sum of partials; afrag of RMSNorm(x; gain). spine_rows: write row

@@ -103,6 +103,8 @@ struct Work {
   float* att_l = nullptr;             // [Bmax][NH][nch][BLK]
   float* att_o = nullptr;             // [Bmax][NH][nch][BLK][DH]
   int att_nch = 0;                    // chunks per (stream, head) = ceil(window / ATT_CH)
+  unsigned* att_cnt = nullptr;        // [Bmax][NH][32] segments stored per (stream, head);
+                                      // zero between attention launches
   unsigned long long* keys = nullptr; // [Rmax] argmax keys
   unsigned long long* copy_keys = nullptr;  // [2 Bmax] copy-draft (match, position) keys
 };

@@ -1309,7 +1309,6 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wave_s = uni(wave);
   const int lr = lane & 15, lg = lane >> 4;
-  const int nch = a.nch;
   const float qs = 0.08838834764831845f * 1.4426950408889634f;
   lds_f s_o = (lds_f)g_att_small;      // [8][4][128] per-wave outputs
   lds_f s_m = s_o + 8 * 4 * DH;        // [8][4]
