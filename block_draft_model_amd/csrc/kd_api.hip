@@ -567,6 +567,7 @@ kd_status kd_create(const kd_config* cfg, void* hip_stream, kd_ctx** out) {
   w.Bmax = cfg->max_streams;
   w.Rmax = kd::BLK * w.Bmax;
   w.Imax = KD_MAX_INGEST * w.Bmax;
+  w.af_ing_layer = kd::afrag_elems(w.Imax, kd::H);
   w.att_nch = (cfg->window + kd::ATT_CH - 1) / kd::ATT_CH;
   const int BI = std::max(w.Bmax, w.Imax), RI = std::max(w.Rmax, w.Imax);
   w.part_elems = 2 * part_region_elems(w.Bmax);
@@ -590,6 +591,7 @@ kd_status kd_create(const kd_config* cfg, void* hip_stream, kd_ctx** out) {
             dev_alloc(c->work_allocs, &w.att_l, (size_t)w.Bmax * kd::NH * w.att_nch * kd::BLK) &&
             dev_alloc(c->work_allocs, &w.att_o,
                       (size_t)w.Bmax * kd::NH * w.att_nch * kd::BLK * kd::DH) &&
+            dev_alloc(c->work_allocs, &w.af_ing, kd::NL * kd::afrag_elems(w.Imax, kd::H)) &&
             dev_alloc(c->work_allocs, &w.att_cnt, (size_t)w.Bmax * kd::NH * 32) &&
             hipMemset(w.att_cnt, 0, (size_t)w.Bmax * kd::NH * 32 * sizeof(unsigned)) == hipSuccess &&
             hipDeviceSynchronize() == hipSuccess &&
@@ -1104,12 +1106,25 @@ kd_status kd_ingest(kd_ctx* c, int B, int n_new, const void* taps, const int32_t
     const int s_fc = kd::gemm_splits(d.fc.K, d.fc.N, rows);
     kd::launch_gemm(st, w.af_fc, rows, d.fc, 0, d.fc.N, w.part, s_fc);
     kd::launch_ingest_c(st, w, rows, s_fc);
-    for (int l = 0; l < kd::NL; ++l) {
-      const kd::DevLayer& L = d.layer[l];
-      kd::launch_norm_rows(st, w.c, rows, L.attn_norm, c->cfg.rms_eps, w.af_x);
+    if (rows > 32 && c->fused_proj) {
+      // every layer's normed rows, then every layer's k|v projection with the
+      // cache store in one launch
+      kd::launch_norm_rows_layers(st, w.c, rows, d, c->cfg.rms_eps, w.af_ing, w.af_ing_layer);
+      kd::IngestEpi e;
+      e.n_new = n_new;
+      e.lens = lens;
+      e.theta = c->cfg.rope_theta;
+      e.kv = k;
+      e.signs = d.kv_signs;
+      kd::launch_ingest_proj(st, w.af_ing, w.af_ing_layer, rows, d, e);
+    } else {
+      for (int l = 0; l < kd::NL; ++l) {
+        const kd::DevLayer& L = d.layer[l];
+        kd::launch_norm_rows(st, w.c, rows, L.attn_norm, c->cfg.rms_eps, w.af_x);
       const int s_kv = kd::gemm_splits(L.qkv.K, 2 * kd::H, rows);
       kd::launch_gemm(st, w.af_x, rows, L.qkv, kd::H / 16, 2 * kd::H, w.part, s_kv);
-      kd::launch_ingest_store(st, w, d, B, n_new, s_kv, k, l, lens, c->cfg.rope_theta);
+        kd::launch_ingest_store(st, w, d, B, n_new, s_kv, k, l, lens, c->cfg.rope_theta);
+      }
     }
     kd::launch_bump_lens(st, lens, B, n_new);
   };

@@ -329,6 +329,43 @@ __device__ __forceinline__ void fwht128(float& y0, float& y1, int lane) {
   }
 }
 
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fminf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+// Codes one 128-value row held as (x0 at dim lane, x1 at dim lane + 64):
+// scale = fp16((max - min)/15), offset = fp16(min), codes clamp(rne((x -
+// offset)/scale), 0, 15) (0 for a zero scale), dims 2m and 2m + 1 in the low
+// and high nibble of byte m; writes the 64 code bytes and the (scale,
+// offset) pair.
+__device__ __forceinline__ void store_row_q4(float x0, float x1, int lane, uint8_t* codes,
+                                             uint32_t* so) {
+  const float mn = wave_min(fminf(x0, x1)), mx = wave_max(fmaxf(x0, x1));
+  const _Float16 sc_h = f16_checked((mx - mn) / 15.0f), of_h = f16_checked(mn);
+  const float sc = (float)sc_h, of = (float)of_h;
+  auto code = [&](float x) -> uint32_t {
+    if (!(sc > 0.f)) return 0u;
+    const float c = __builtin_rintf((x - of) / sc);
+    return (uint32_t)fminf(fmaxf(c, 0.f), 15.f);
+  };
+  const uint32_t c0 = code(x0), c1 = code(x1);
+  // dims (2m, 2m + 1) meet in the even lane
+  const uint32_t n0 = __shfl_xor(c0, 1, 64), n1 = __shfl_xor(c1, 1, 64);
+  if ((lane & 1) == 0) {
+    codes[lane >> 1] = (uint8_t)(c0 | (n0 << 4));
+    codes[32 + (lane >> 1)] = (uint8_t)(c1 | (n1 << 4));
+  }
+  if (lane == 0)
+    *so = (uint32_t)__builtin_bit_cast(uint16_t, sc_h) | ((uint32_t)__builtin_bit_cast(uint16_t, of_h) << 16);
+}
+
 // 8 4-bit codes (one dword, dim 2i in the low nibble of byte i) -> 8 f16
 // values code * 2^-24: each code becomes the mantissa of an f16 subnormal
 // (exact; the matrix cores take f16 subnormals as they are). Users scale

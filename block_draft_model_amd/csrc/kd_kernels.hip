@@ -1248,6 +1248,34 @@ void launch_norm_rows(hipStream_t st, const float* x, int rows, const float* gai
   k_norm_rows<<<rows, 320, 0, st>>>(x, gain, eps, af);
 }
 
+// One row's RMS, then the row with every layer's attention gain (afrag).
+__global__ __launch_bounds__(320) void k_norm_rows_layers(const float* x, DevWeights d, float eps,
+                                                          uint16_t* af, size_t af_layer) {
+  __shared__ float red[8];
+  const int r = blockIdx.x, c0 = threadIdx.x * 8;
+  float v[8], ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[i] = x[(size_t)r * H + c0 + i];
+    ss += v[i] * v[i];
+  }
+  ss = block_sum<5>(ss, red);
+  const float inv = 1.0f / sqrtf(ss / H + eps);
+#pragma unroll
+  for (int l = 0; l < NL; ++l) {
+    const float* gain = d.layer[l].attn_norm;
+    float y[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = gain[c0 + i] * v[i] * inv;
+    store_afrag8(af + l * af_layer, H / 32, r, c0, y);
+  }
+}
+
+void launch_norm_rows_layers(hipStream_t st, const float* x, int rows, const DevWeights& d,
+                             float eps, uint16_t* af, size_t af_layer) {
+  k_norm_rows_layers<<<rows, 320, 0, st>>>(x, d, eps, af, af_layer);
+}
+
 // k|v partials (N = 2H) -> RoPE(k) at position len + i -> bf16 (nearest even)
 // into the ring.
 __global__ __launch_bounds__(256) void k_ingest_store(const float* part, int splits, int rows,
@@ -1256,6 +1284,7 @@ __global__ __launch_bounds__(256) void k_ingest_store(const float* part, int spl
                                                       const int32_t* lens, float theta) {
   const int r = blockIdx.x, b = r / n_new, i = r % n_new;
   const long pos = (long)lens[b] + i;
+  if (pos < 0) return;   // a negative length stores nothing
   const int slot = (int)(pos % cap);
   for (int p = threadIdx.x; p < NH * DH / 2; p += blockDim.x) {
     const int h = p >> 6, fi = p & 63;
@@ -1288,40 +1317,6 @@ __global__ __launch_bounds__(256) void k_ingest_store(const float* part, int spl
 // by R = H diag(s)/sqrt(128); K and V rows then get scale = fp16((max -
 // min)/15), offset = fp16(min) and codes clamp(rne((x - offset)/scale), 0,
 // 15) (0 for a zero scale).
-__device__ __forceinline__ float wave_min(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fminf(v, __shfl_xor(v, m, 64));
-  return v;
-}
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-  return v;
-}
-
-// Codes the row held as (x0 at dim lane, x1 at dim lane + 64) and writes its
-// 64 code bytes and (scale, offset) pair.
-__device__ __forceinline__ void store_row_q4(float x0, float x1, int lane, uint8_t* codes,
-                                             uint32_t* so) {
-  const float mn = wave_min(fminf(x0, x1)), mx = wave_max(fmaxf(x0, x1));
-  const _Float16 sc_h = f16_checked((mx - mn) / 15.0f), of_h = f16_checked(mn);
-  const float sc = (float)sc_h, of = (float)of_h;
-  auto code = [&](float x) -> uint32_t {
-    if (!(sc > 0.f)) return 0u;
-    const float c = __builtin_rintf((x - of) / sc);
-    return (uint32_t)fminf(fmaxf(c, 0.f), 15.f);
-  };
-  const uint32_t c0 = code(x0), c1 = code(x1);
-  // dims (2m, 2m + 1) meet in the even lane
-  const uint32_t n0 = __shfl_xor(c0, 1, 64), n1 = __shfl_xor(c1, 1, 64);
-  if ((lane & 1) == 0) {
-    codes[lane >> 1] = (uint8_t)(c0 | (n0 << 4));
-    codes[32 + (lane >> 1)] = (uint8_t)(c1 | (n1 << 4));
-  }
-  if (lane == 0)
-    *so = (uint32_t)__builtin_bit_cast(uint16_t, sc_h) | ((uint32_t)__builtin_bit_cast(uint16_t, of_h) << 16);
-}
-
 __global__ __launch_bounds__(256) void k_ingest_store_q4(const float* part, int splits, int rows,
                                                          int n_new, uint8_t* kc, uint8_t* vc,
                                                          uint32_t* kso, uint32_t* vso,
@@ -1330,6 +1325,7 @@ __global__ __launch_bounds__(256) void k_ingest_store_q4(const float* part, int 
                                                          float theta, const float* signs) {
   const int r = blockIdx.x, b = r / n_new, i = r % n_new;
   const long pos = (long)lens[b] + i;
+  if (pos < 0) return;   // a negative length stores nothing
   const int slot = (int)(pos % cap);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int fi = lane;

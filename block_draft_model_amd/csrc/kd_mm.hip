@@ -342,6 +342,163 @@ void launch_proj(hipStream_t st, const uint16_t* af, int R, const WMat& W, const
 }
 
 // ---------------------------------------------------------------------------
+// The ingest's k|v projections of every layer in one launch (model card
+// "Kolibri-1 block drafter", section Architecture: Body, the cached K/V each
+// layer attends to; every layer projects the same context row through its
+// attention RMSNorm and W_k, W_v). Workgroup (column block, row block) of
+// layer blockIdx.y: the main loop of k_proj over the layer's k|v rows of
+// q|k|v (256 output columns, one split), the output tile staged in LDS. A
+// 256-column block is two whole heads of k or of v (a head's RoPE pairs
+// (d, d + 64) are one 16-column tile, its 8 tiles consecutive), so the
+// epilogue finishes the rows there: RoPE on k at the row's absolute position
+// (angle pos * theta^(-f/64), the frequency in double precision, the angle
+// reduced in double precision, its sine and cosine in single precision),
+// then either bf16 (nearest even) at the row's ring slot, or, for the
+// rotated 4-bit cache (the article "Serving Kolibri-1 with a 4-bit KV
+// cache", section What we do), k turned by the layer's R and both rows coded
+// to 4 bits with their fp16 scale and offset.
+// ---------------------------------------------------------------------------
+struct IngestProj {
+  GemmMM g[NL];
+  IngestEpi e;
+};
+
+template <int WF>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_ingest_proj(IngestProj p) {
+  constexpr int CT = 4, COLS = 256, TP = COLS + 4;
+  constexpr int SA_BYTES = 2 * MM_RT * 2 * 64 * 16;
+  constexpr int T_BYTES = 64 * TP * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[SA_BYTES > T_BYTES ? SA_BYTES : T_BYTES];
+  __shared__ double s_invf[DH / 2];
+  auto sa = reinterpret_cast<u32x4(*)[MM_RT * 2][64]>(lds);
+  float* T = reinterpret_cast<float*>(lds);
+  const int l = blockIdx.y;
+  GemmMM g = p.g[0];
+#pragma unroll
+  for (int i = 1; i < NL; ++i)
+    if (l == i) g = p.g[i];
+  const IngestEpi& e = p.e;
+  const int RB = (g.R + 63) / 64, CB = g.N / COLS;
+  const MmMap m = mm_map(RB, CB, 1);
+  if (!m.ok) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (threadIdx.x < DH / 2) s_invf[threadIdx.x] = pow((double)e.theta, -(double)threadIdx.x / (DH / 2));
+  f32x4 acc[MM_RT][CT];
+  mm_accumulate<CT, 2, WF>(g, m.rb, m.cb, 0, acc, sa);   // ends at a barrier: LDS is free
+#pragma unroll
+  for (int r = 0; r < MM_RT; ++r)
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        T[(r * 16 + 4 * (lane >> 4) + q) * TP + (wave * CT + c) * 16 + (lane & 15)] = acc[r][c][q];
+  __syncthreads();
+  // the block's first column in q|k|v order: section (1 = k, 2 = v) and head
+  const int nat0 = qkv_natural((g.n_off + m.cb * (COLS / 16)) * 16);
+  const int sec = nat0 / H, h0 = (nat0 - sec * H) / DH;
+  const bool is_k = sec == 1;
+  constexpr double TWO_PI = 6.283185307179586;
+  auto angle = [&](long pos, int fi, float& cs, float& sn) {
+    const double a = (double)pos * s_invf[fi];
+    const float red = (float)(a - rint(a * (1.0 / TWO_PI)) * TWO_PI);
+    sn = sinf(red);
+    cs = cosf(red);
+  };
+  if (e.kv.fmt == 0) {
+    // items (row, 8-dim group pg): dims 8 pg .. 8 pg + 7 and their partners
+    // + 64 of both heads (tiles pg and 8 + pg), one angle per dim
+    for (int it = threadIdx.x; it < 64 * 8; it += 256) {
+      const int rl = it >> 3, pg = it & 7, row = m.rb * 64 + rl;
+      if (row >= g.R) continue;
+      const int b = row / e.n_new, i = row - b * e.n_new;
+      const long pos = (long)e.lens[b] + i;
+      if (pos < 0) continue;   // a negative length stores nothing
+      const int slot = (int)(pos % e.kv.cap);
+      float cs[8], sn[8];
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        cs[n] = 1.f;
+        sn[n] = 0.f;
+        if (is_k) angle(pos, 8 * pg + n, cs[n], sn[n]);
+      }
+      uint16_t* cache = const_cast<uint16_t*>(is_k ? e.kv.k[l] : e.kv.v[l]);
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const float* tp = T + rl * TP + (8 * hh + pg) * 16;
+        uint32_t lo[4], hi[4];
+#pragma unroll
+        for (int n = 0; n < 8; n += 2) {
+          const float a0 = tp[n], b0 = tp[8 + n], a1 = tp[n + 1], b1 = tp[9 + n];
+          lo[n / 2] = bf16_rne(a0 * cs[n] - b0 * sn[n]) | (bf16_rne(a1 * cs[n + 1] - b1 * sn[n + 1]) << 16);
+          hi[n / 2] = bf16_rne(a0 * sn[n] + b0 * cs[n]) | (bf16_rne(a1 * sn[n + 1] + b1 * cs[n + 1]) << 16);
+        }
+        uint16_t* dst = cache + (size_t)b * e.kv.ss + (size_t)(h0 + hh) * e.kv.sh + (size_t)slot * e.kv.sl + 8 * pg;
+        *reinterpret_cast<u32x4*>(dst) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+        *reinterpret_cast<u32x4*>(dst + DH / 2) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+      }
+    }
+  } else {
+    // items (row, head) per wave; lane l holds dims l and l + 64 (tile l / 8
+    // of the head, columns l % 8 and 8 + l % 8)
+    const float s0 = is_k ? e.signs[l * DH + lane] : 1.f, s1 = is_k ? e.signs[l * DH + lane + DH / 2] : 1.f;
+    uint8_t* codes = reinterpret_cast<uint8_t*>(const_cast<uint16_t*>(is_k ? e.kv.k[l] : e.kv.v[l]));
+    uint32_t* so = reinterpret_cast<uint32_t*>(const_cast<uint16_t*>(is_k ? e.kv.kso[l] : e.kv.vso[l]));
+    for (int it = wave; it < 64 * 2; it += 4) {
+      const int rl = it >> 1, hh = it & 1, row = m.rb * 64 + rl;
+      if (row >= g.R) continue;   // uniform per wave
+      const int b = row / e.n_new, i = row - b * e.n_new;
+      const long pos = (long)e.lens[b] + i;
+      if (pos < 0) continue;   // a negative length stores nothing (uniform per wave)
+      const int slot = (int)(pos % e.kv.cap);
+      const float* tp = T + rl * TP + (8 * hh + (lane >> 3)) * 16 + (lane & 7);
+      float y0 = tp[0], y1 = tp[8];
+      if (is_k) {
+        float cs, sn;
+        angle(pos, lane, cs, sn);
+        const float k0 = y0 * cs - y1 * sn, k1 = y0 * sn + y1 * cs;
+        y0 = k0 * s0;
+        y1 = k1 * s1;
+        fwht128(y0, y1, lane);
+        y0 *= 0.08838834764831845f;
+        y1 *= 0.08838834764831845f;
+      }
+      const size_t crow = (size_t)b * e.kv.ss + (size_t)(h0 + hh) * e.kv.sh + (size_t)slot * e.kv.sl;
+      store_row_q4(y0, y1, lane, codes + crow * 64, so + crow);
+    }
+  }
+}
+
+void launch_ingest_proj(hipStream_t st, const uint16_t* af, size_t af_layer, int R,
+                        const DevWeights& d, const IngestEpi& e) {
+  IngestProj p;
+  for (int l = 0; l < NL; ++l) {
+    const WMat& W = d.layer[l].qkv;
+    GemmMM& g = p.g[l];
+    g.af = af + l * af_layer;
+    g.R = R;
+    g.KT = W.K / 32;
+    g.w = W.w;
+    g.s = W.s;
+    g.s4 = W.s4;
+    g.KB = W.K / 64;
+    g.N = 2 * H;          // the k and v sections of q|k|v
+    g.n_off = H / 16;
+    g.WN = W.N;
+    g.ks = W.ks;
+    g.part = nullptr;
+    g.splits = 1;
+    g.kbs = g.KB;
+  }
+  p.e = e;
+  const dim3 grid(mm_grid(R, 2 * H / 256, 1), NL);
+  switch (d.layer[0].qkv.fmt) {
+    case WF_NVFP4: k_ingest_proj<WF_NVFP4><<<grid, 256, 0, st>>>(p); break;
+    case WF_BF16: k_ingest_proj<WF_BF16><<<grid, 256, 0, st>>>(p); break;
+    default: k_ingest_proj<WF_FP8><<<grid, 256, 0, st>>>(p);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // NVFP4 head over the draft vocabulary with a fused per-row argmax:
 // logits[r][v] = g * sum_k z[r][k] * e2m1(q) * e4m3(s). One step is one
 // 128-input group (the repacked code layout's unit). The f16 activations

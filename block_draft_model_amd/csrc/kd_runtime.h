@@ -105,6 +105,8 @@ struct Work {
   int att_nch = 0;                    // chunks per (stream, head) = ceil(window / ATT_CH)
   unsigned* att_cnt = nullptr;        // [Bmax][NH][32] segments stored per (stream, head);
                                       // zero between attention launches
+  uint16_t* af_ing = nullptr;         // afrag [NL][Imax][H]: ingest rows, RMSNorm with each layer's
+  size_t af_ing_layer = 0;            //   attention gain; elements per layer
   unsigned long long* keys = nullptr; // [Rmax] argmax keys
   unsigned long long* copy_keys = nullptr;  // [2 Bmax] copy-draft (match, position) keys
 };
@@ -131,6 +133,17 @@ struct ProjEpi {
   float* kb = nullptr;
   float* vb = nullptr;
   uint16_t* af = nullptr;
+};
+
+// Epilogue of the ingest's k|v projections of every layer in one launch
+// (launch_ingest_proj): RoPE on k at each row's absolute position len + i,
+// then the cache format's store at the row's ring slot.
+struct IngestEpi {
+  int n_new = 1;                  // rows per stream; row r is stream r / n_new, row r % n_new
+  const int32_t* lens = nullptr;  // lengths before the ingest
+  float theta = 0.f;
+  KV kv;
+  const float* signs = nullptr;   // rotated 4-bit cache: [NL][DH] signs of R
 };
 
 // ---- launchers (kd_kernels.hip) ----
@@ -164,6 +177,9 @@ void launch_ingest_prep(hipStream_t st, const Work& w, int rows, const uint16_t*
 void launch_ingest_post_fuse(hipStream_t st, const Work& w, const DevWeights& d, int rows,
                              int splits, const int32_t* next_ids);
 void launch_ingest_c(hipStream_t st, const Work& w, int rows, int splits);
+// RMSNorm of each row with every layer's attention gain: af + l * af_layer.
+void launch_norm_rows_layers(hipStream_t st, const float* x, int rows, const DevWeights& d,
+                             float eps, uint16_t* af, size_t af_layer);
 void launch_norm_rows(hipStream_t st, const float* x, int rows, const float* gain, float eps,
                       uint16_t* af);
 void launch_ingest_store(hipStream_t st, const Work& w, const DevWeights& d, int B, int n_new, int splits, const KV& kv,
@@ -176,6 +192,10 @@ void launch_gemm_mm(hipStream_t st, const uint16_t* af, int R, const WMat& W, in
                     int N, float* part, int splits);
 // Projection of R rows (more than 32) with its epilogue fused, in one split.
 void launch_proj(hipStream_t st, const uint16_t* af, int R, const WMat& W, const ProjEpi& e);
+// The ingest's k|v projections of R rows (more than 32) for every layer in one
+// launch (layer l reads af + l * af_layer), stored into the cache.
+void launch_ingest_proj(hipStream_t st, const uint16_t* af, size_t af_layer, int R,
+                        const DevWeights& d, const IngestEpi& e);
 bool head_mm_fits(int R);
 void launch_head_mm(hipStream_t st, const uint16_t* af, int R, const DevWeights& d, float* logits,
                     unsigned long long* keys);
