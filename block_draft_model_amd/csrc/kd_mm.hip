@@ -363,6 +363,92 @@ struct IngestProj {
   IngestEpi e;
 };
 
+// N rows at once (independent lane-exchange chains interleave): the in-wave
+// Walsh-Hadamard transform of fwht128 and the 4-bit coding of store_row_q4
+// (rows with ok[i] false take part in the exchanges and store nothing).
+template <int N>
+__device__ __forceinline__ void fwht128_n(float (&y0)[N], float (&y1)[N], int lane) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float a = y0[i], c = y1[i];
+    y0[i] = a + c;
+    y1[i] = a - c;
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    float p0[N], p1[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      p0[i] = __shfl_xor(y0[i], m, 64);
+      p1[i] = __shfl_xor(y1[i], m, 64);
+    }
+    const bool up = (lane & m) != 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      y0[i] = up ? p0[i] - y0[i] : y0[i] + p0[i];
+      y1[i] = up ? p1[i] - y1[i] : y1[i] + p1[i];
+    }
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void store_rows_q4_n(const float (&x0)[N], const float (&x1)[N], const bool (&ok)[N],
+                                                int lane, uint8_t* const (&codes)[N], uint32_t* const (&so)[N]) {
+  float mn[N], mx[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    mn[i] = fminf(x0[i], x1[i]);
+    mx[i] = fmaxf(x0[i], x1[i]);
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    float pn[N], px[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      pn[i] = __shfl_xor(mn[i], m, 64);
+      px[i] = __shfl_xor(mx[i], m, 64);
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      mn[i] = fminf(mn[i], pn[i]);
+      mx[i] = fmaxf(mx[i], px[i]);
+    }
+  }
+  uint32_t c0[N], c1[N];
+  _Float16 sc_h[N], of_h[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    sc_h[i] = f16_checked((mx[i] - mn[i]) / 15.0f);
+    of_h[i] = f16_checked(mn[i]);
+    const float sc = (float)sc_h[i], of = (float)of_h[i];
+    auto code = [&](float x) -> uint32_t {
+      if (!(sc > 0.f)) return 0u;
+      const float c = __builtin_rintf((x - of) / sc);
+      return (uint32_t)fminf(fmaxf(c, 0.f), 15.f);
+    };
+    c0[i] = code(x0[i]);
+    c1[i] = code(x1[i]);
+  }
+  // dims (2m, 2m + 1) meet in the even lane
+  uint32_t n0[N], n1[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    n0[i] = __shfl_xor(c0[i], 1, 64);
+    n1[i] = __shfl_xor(c1[i], 1, 64);
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (!ok[i]) continue;
+    if ((lane & 1) == 0) {
+      codes[i][lane >> 1] = (uint8_t)(c0[i] | (n0[i] << 4));
+      codes[i][32 + (lane >> 1)] = (uint8_t)(c1[i] | (n1[i] << 4));
+    }
+    if (lane == 0)
+      *so[i] = (uint32_t)__builtin_bit_cast(uint16_t, sc_h[i]) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, of_h[i]) << 16);
+  }
+}
+
 template <int WF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_ingest_proj(IngestProj p) {
   constexpr int CT = 4, COLS = 256, TP = COLS + 4;
@@ -438,32 +524,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       }
     }
   } else {
-    // items (row, head) per wave; lane l holds dims l and l + 64 (tile l / 8
-    // of the head, columns l % 8 and 8 + l % 8)
+    // items (row, head): wave w takes items w, w + 4, ..., NI at a time; lane
+    // l holds dims l and l + 64 (tile l / 8 of the head, columns l % 8 and
+    // 8 + l % 8)
+    constexpr int NI = 4;
     const float s0 = is_k ? e.signs[l * DH + lane] : 1.f, s1 = is_k ? e.signs[l * DH + lane + DH / 2] : 1.f;
     uint8_t* codes = reinterpret_cast<uint8_t*>(const_cast<uint16_t*>(is_k ? e.kv.k[l] : e.kv.v[l]));
     uint32_t* so = reinterpret_cast<uint32_t*>(const_cast<uint16_t*>(is_k ? e.kv.kso[l] : e.kv.vso[l]));
-    for (int it = wave; it < 64 * 2; it += 4) {
-      const int rl = it >> 1, hh = it & 1, row = m.rb * 64 + rl;
-      if (row >= g.R) continue;   // uniform per wave
-      const int b = row / e.n_new, i = row - b * e.n_new;
-      const long pos = (long)e.lens[b] + i;
-      if (pos < 0) continue;   // a negative length stores nothing (uniform per wave)
-      const int slot = (int)(pos % e.kv.cap);
-      const float* tp = T + rl * TP + (8 * hh + (lane >> 3)) * 16 + (lane & 7);
-      float y0 = tp[0], y1 = tp[8];
-      if (is_k) {
-        float cs, sn;
-        angle(pos, lane, cs, sn);
-        const float k0 = y0 * cs - y1 * sn, k1 = y0 * sn + y1 * cs;
-        y0 = k0 * s0;
-        y1 = k1 * s1;
-        fwht128(y0, y1, lane);
-        y0 *= 0.08838834764831845f;
-        y1 *= 0.08838834764831845f;
+    for (int it0 = wave; it0 < 64 * 2; it0 += 4 * NI) {
+      float y0[NI], y1[NI];
+      bool ok[NI];
+      uint8_t* cp[NI];
+      uint32_t* sp[NI];
+#pragma unroll
+      for (int n = 0; n < NI; ++n) {
+        const int it = it0 + 4 * n, rl = it >> 1, hh = it & 1, row = m.rb * 64 + rl;
+        const int b = min(row, g.R - 1) / e.n_new, i = min(row, g.R - 1) - b * e.n_new;
+        const long pos = (long)e.lens[b] + i;
+        ok[n] = row < g.R && pos >= 0;   // a negative length stores nothing
+        const int slot = (int)((pos < 0 ? 0 : pos) % e.kv.cap);
+        const float* tp = T + rl * TP + (8 * hh + (lane >> 3)) * 16 + (lane & 7);
+        y0[n] = tp[0];
+        y1[n] = tp[8];
+        if (is_k) {
+          float cs, sn;
+          angle(pos, lane, cs, sn);
+          const float k0 = y0[n] * cs - y1[n] * sn, k1 = y0[n] * sn + y1[n] * cs;
+          y0[n] = k0 * s0;
+          y1[n] = k1 * s1;
+        }
+        const size_t crow = (size_t)b * e.kv.ss + (size_t)(h0 + hh) * e.kv.sh + (size_t)slot * e.kv.sl;
+        cp[n] = codes + crow * 64;
+        sp[n] = so + crow;
       }
-      const size_t crow = (size_t)b * e.kv.ss + (size_t)(h0 + hh) * e.kv.sh + (size_t)slot * e.kv.sl;
-      store_row_q4(y0, y1, lane, codes + crow * 64, so + crow);
+      if (is_k) {
+        fwht128_n<NI>(y0, y1, lane);
+#pragma unroll
+        for (int n = 0; n < NI; ++n) {
+          y0[n] *= 0.08838834764831845f;
+          y1[n] *= 0.08838834764831845f;
+        }
+      }
+      store_rows_q4_n<NI>(y0, y1, ok, lane, cp, sp);
     }
   }
 }
