@@ -248,12 +248,12 @@ __device__ __forceinline__ void grid_sync(Args& a, SyncState sy) {
   grid_wait(a, sy);
 }
 
-// LDS of the attention phase. Keys, values and queries arrive by global-to-LDS
-// copies into a two-slot ring (slot = parity of the workgroup's unit count):
-// per slot, 8 blocks of 1 KB per wave for its 16 keys (4 key blocks, 4 value
-// blocks; a copy puts lane l's 16 bytes at l * 16, and the same lane reads
-// them back), then 2 blocks of queries ([4][128] fp32, copied by wave 0).
-// The ring is also the reduction area of every other phase.
+// LDS of the attention phase: 16 ring slots of 8 KB, two per wave (slot s at
+// half s / 8, blocks 8 (s % 8) ..), each holding one 16-key block as it
+// arrives by global-to-LDS copies (4 key blocks, 4 value blocks of 1 KB; a
+// copy puts lane l's 16 bytes at l * 16, and the same lane reads them back).
+// The last 2 KB of each half are spare. The ring is also the reduction area
+// of every other phase.
 constexpr int ATT_WAVE_BLOCKS = 8;
 constexpr int ATT_SLOT_BLOCKS = 8 * ATT_WAVE_BLOCKS + 2;
 constexpr unsigned ATT_SLOT_BYTES = ATT_SLOT_BLOCKS * 1024u;
@@ -267,6 +267,20 @@ template <int N>
 __device__ __forceinline__ void att_wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+// Waits until at most n blocks' copies (8 per 16-key block, n = 0..7,
+// wave-uniform) of this wave are in flight.
+__device__ __forceinline__ void att_wait_blocks(int n) {
+  switch (n) {
+    case 0: att_wait_vm<0>(); break;
+    case 1: att_wait_vm<8>(); break;
+    case 2: att_wait_vm<16>(); break;
+    case 3: att_wait_vm<24>(); break;
+    case 4: att_wait_vm<32>(); break;
+    case 5: att_wait_vm<40>(); break;
+    case 6: att_wait_vm<48>(); break;
+    default: att_wait_vm<56>(); break;
+  }
 }
 // (n is wave-uniform; values the attention loop uses: 0, 2, 5, 8, 10, 11, 13)
 __device__ __forceinline__ void att_wait_vm(int n) {
@@ -1106,24 +1120,6 @@ __device__ __forceinline__ void att_read_kv(unsigned kva, u32x4 (&kr)[4], u32x4 
       : "v"(kva)
       : "memory");
 }
-// Reads 8 x 16 B of one query row (at qa: dims 32 kb + 8 (lane / 16) .. + 8
-// for kb = 0..3) and waits for the reads.
-__device__ __forceinline__ void att_read_q(unsigned qa, u32x4 (&qv)[8]) {
-  asm volatile(
-      "ds_read_b128 %0, %8\n\t"
-      "ds_read_b128 %1, %8 offset:16\n\t"
-      "ds_read_b128 %2, %8 offset:128\n\t"
-      "ds_read_b128 %3, %8 offset:144\n\t"
-      "ds_read_b128 %4, %8 offset:256\n\t"
-      "ds_read_b128 %5, %8 offset:272\n\t"
-      "ds_read_b128 %6, %8 offset:384\n\t"
-      "ds_read_b128 %7, %8 offset:400\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(qv[0]), "=&v"(qv[1]), "=&v"(qv[2]), "=&v"(qv[3]), "=&v"(qv[4]), "=&v"(qv[5]),
-        "=&v"(qv[6]), "=&v"(qv[7])
-      : "v"(qa)
-      : "memory");
-}
 
 // LDS reads of the attention phase that the compiler must not see: it would
 // make every LDS read wait for all global-to-LDS copies in flight. Each reads
@@ -1245,8 +1241,11 @@ __device__ __forceinline__ void chunk_partial_store(Args& a, int l, int b, int h
 // and layer, once every partial store is done); then the non-merging
 // workgroups warm the next phases' weights and the merging ones merge their
 // pair once its counter shows every segment stored.
+// per_chunk: each chunk's wave counted its chunk itself (the counter of a
+// pair then reaches its number of chunks); otherwise the workgroup counts its
+// segments here.
 __device__ __forceinline__ void attn_finish(Args& a, int l, const StreamLens& sl, int ub, int ue, BlockRows& br,
-                                            SyncState sy, bool sync) {
+                                            SyncState sy, bool sync, bool per_chunk = false) {
   const int G = gridDim.x, wg = blockIdx.x;
   auto& s = a.s;
   const int nbh = a.B * NH, mi = wg;
@@ -1255,7 +1254,7 @@ __device__ __forceinline__ void attn_finish(Args& a, int l, const StreamLens& sl
   // segments; taken once every partial store of the workgroup is done
   __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0): stores acknowledged
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (threadIdx.x == 0 && !per_chunk) {
     for (int u = ub; u < ue;) {
       int b, c, h;
       sl.unit(u, b, c, h);
@@ -1283,7 +1282,7 @@ __device__ __forceinline__ void attn_finish(Args& a, int l, const StreamLens& sl
     if (n > 0) {
       if (threadIdx.x == 0) {
         auto cnt = &s.att_cnt[((l * SB_MAX + b) * NH + h) * 32];
-        const unsigned need = (unsigned)sl.segments(u0, sl.chunks(b), G);
+        const unsigned need = per_chunk ? (unsigned)sl.chunks(b) : (unsigned)sl.segments(u0, sl.chunks(b), G);
         const unsigned long long t0 = wall_clock64();
         for (unsigned it = 1; ld_rlx(cnt) < need; ++it) {
           if ((it & 63) == 0 && wall_clock64() - t0 > 20000000ull) {  // 0.2 s
@@ -1300,6 +1299,30 @@ __device__ __forceinline__ void attn_finish(Args& a, int l, const StreamLens& sl
   }
 }
 
+// A four-float write-through store (one vector memory instruction).
+__device__ __forceinline__ void att_store4(gptr<float> p, f32x4 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
+}
+
+// Attention of the block rows to the context. Unit u = (stream, head, chunk
+// of ATT_CH keys); wave w of workgroup g takes the units g + G (w + 8 i),
+// each on its own: the chunk's 8 blocks of 16 keys in key order through the
+// wave's two LDS ring slots (global-to-LDS copies, the next block in flight
+// while one is computed), per block
+//   scores  S^T[key][j] = K Q^T on the matrix cores (16x16x32 bf16): keys as
+//           the A operand (lane: key lane%16, dims 32kb + 8(lane/16)), the
+//           queries (pre-scaled by log2(e)/sqrt(128)) split into bf16 hi + lo
+//           as the B operand (column j < 4 of the 4 block rows), the hi and
+//           lo products in two accumulators added at the end;
+//   softmax running max and sum per row j (log2 units), the output rescaled
+//           by the growth of the max;
+//   P V     on the vector units: lane (g, c) adds keys 4g..4g+3 of the block
+//           for dims 8c..8c+7 of all 4 rows (the probabilities pass through
+//           the wave's own LDS area).
+// The chunk's partial (max, sum, unnormalised output of each row) is stored
+// at its slot and the pair's counter counts it; the workgroup that merges
+// the pair waits for all its chunks and merges them in chunk order (so a
+// stream's result does not depend on the batch around it).
 __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int l_, SyncState sy,
                                                   bool sync) {
   const auto l = uni(l_);
@@ -1310,63 +1333,16 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
   const int wave_s = uni(wave);
   const int lr = lane & 15, lg = lane >> 4;
   const float qs = 0.08838834764831845f * 1.4426950408889634f;
-  lds_f s_o = (lds_f)g_att_small;      // [8][4][128] per-wave outputs
-  lds_f s_m = s_o + 8 * 4 * DH;        // [8][4]
-  lds_f s_l = s_m + 32;                // [8][4]
-  lds_f s_p = s_l + 32;                // [8][4][16] probabilities
+  lds_f s_p = (lds_f)g_att_small + wave_s * 64;   // the wave's probabilities [4][16]
 
   StreamLens sl;
   sl.load(a);  // an input: read before the arrival
   const int U = sl.total;
-  const int ub = U > 0 ? sl.start(wg, G) : 0, ue = U > 0 ? sl.start(wg + 1, G) : 0;
   auto kb_l = a.kv.k[l], vb_l = a.kv.v[l];
   const long long kv_ss = a.kv.ss, kv_sh = a.kv.sh, kv_sl = a.kv.sl;
   const int kv_cap = a.kv.cap;
+  const int nch = a.nch;
   auto q_l = s.q[l];
-  // Copies the keys and values of unit u into ring slot `slot`: keys past the
-  // visible rows are clamped to the last one and masked out of the scores.
-  // Keys and values are inputs, so the first units' copies go out before the
-  // barrier; the queries come from the previous phase.
-  auto copy_kv = [&](int u, int slot) {
-    int b, c, h;
-    sl.unit(u, b, c, h);
-    const int n = sl.vis(b), fp = sl.first(b);
-    auto kbase = kb_l + b * kv_ss + h * kv_sh;
-    auto vbase = vb_l + b * kv_ss + h * kv_sh;
-    // slot of the chunk's first key; visible keys are less than cap past it
-    const int s0 = (fp + c * ATT_CH) % kv_cap;
-    const int last = n - 1 - c * ATT_CH;
-    auto slot_of = [&](int off) {
-      int sl_ = s0 + min(off, last);
-      return sl_ - (sl_ >= kv_cap ? kv_cap : 0);
-    };
-    KD_LDS u32x4* dst = (KD_LDS u32x4*)&g_att_ring[slot][wave_s * ATT_WAVE_BLOCKS][0];
-    const size_t krow = (size_t)slot_of(wave * 16 + lr) * kv_sl;
-    // key block kb: lane (key lr, group lg) brings dims 32 kb + 8 lg .. + 8
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(kbase + krow + 32 * kb + 8 * lg),
-                                       (KD_LDS void*)(dst + kb * 64), 16, 0, 0);
-    // value block t: lane (group g = lg, c = lr) brings key 4g + t, dims 8c .. + 8
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<const void*>(vbase + (size_t)slot_of(wave * 16 + 4 * lg + t) * kv_sl + 8 * lr),
-          (KD_LDS void*)(dst + (4 + t) * 64), 16, 0, 0);
-  };
-  // wave 0 copies the unit's 4 query rows (2 x 1 KB) into the slot
-  auto copy_q = [&](int u, int slot) {
-    if (wave_s != 0) return;
-    int b, c, h;
-    sl.unit(u, b, c, h);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int e = i * 256 + lane * 4, j = e >> 7, d = e & 127;
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(q_l + (b * 4 + j) * H + h * DH + d),
-                                       (KD_LDS void*)(KD_LDS u32x4*)&g_att_ring[slot][8 * ATT_WAVE_BLOCKS + i][0], 16, 0,
-                                       0);
-    }
-  };
   const unsigned ring0 = (unsigned)(uintptr_t)&g_att_ring[0][0][0];
 
   // the (stream, head) this workgroup merges, if any: (stream, head) i is
@@ -1374,204 +1350,200 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
   const int nbh = a.B * NH;
   const int mi = wg;
   const bool merges = wg < nbh;
-  // the block rows of that pair are loaded before the copies (once the
-  // previous phase has written them) and used after the workgroup's chunks
   BlockRows br{};
   if (merges && !sync) br.load(a, l, mi / NH, mi % NH);
-
   if (sync) {
     grid_arrive(a, sy);
-    if (is_poll_wave()) grid_poll(a, sy);
-  }
-  if (ub < ue) {
-    copy_kv(ub, 0);
-    if (!sync) copy_q(ub, 0);
-  }
-  if (ub + 1 < ue) {
-    copy_kv(ub + 1, 1);
-    if (!sync) copy_q(ub + 1, 1);
-  }
-  if (sync) {
-    lds_sync();
+    grid_wait(a, sy);
     if (merges) br.load(a, l, mi / NH, mi % NH);
-    if (ub < ue) copy_q(ub, 0);
-    if (ub + 1 < ue) copy_q(ub + 1, 1);
   }
   trace_mark(a, sy, 2);
 
-  // the wave's running state for the current segment: scaled queries as the
-  // B operand, max and sum of row lr (lanes lr < 4), output of rows 0..3 for
-  // the lane's dims 8 (lane % 16) .. + 8 over its key group lane / 16
-  bf16x8 qh[4], ql[4];
-  float m_run = -__builtin_inff(), l_run = 0.f;
-  float o[4][8];
-  int seg_c0 = 0;
-  int slot = 0;
-  int stores = 0;  // store instructions the previous unit issued after its copies
-  for (int u = ub; u < ue; ++u, slot ^= 1) {
+  // the workgroup's units wg, wg + G, ...: wave w takes the w-th, (w + 8)-th,
+  // ...; each wave owns two LDS ring slots of 8 KB (one 16-key block each):
+  // one block is computed while the next is in flight. (More slots for the
+  // active waves when fewer are active measured slower.)
+  constexpr int ns = 2;
+  const int slot0 = wave_s * ns;
+  for (int u = wg + G * wave_s; u < U; u += 8 * G) {
     int b, c, h;
     sl.unit(u, b, c, h);
-    const int n = sl.vis(b);
-    // every chunk is a segment of its own: its partial is stored and merged
-    // later in chunk order, so a stream's result does not depend on how the
-    // batch's chunks fall to workgroups. The queries are read again only when
-    // the (stream, head) pair changes.
-    const bool new_pair = u == ub || c == 0;
-    // Vector memory operations issued after this unit's copies, which its
-    // wait lets stay in flight: the next unit's copies (8 per wave, 10 for
-    // wave 0 with its query blocks; in the persistent kernel wave 0's first
-    // two query copies follow both key/value sets, so its first unit allows
-    // only the second unit's queries), then the previous unit's partial
-    // stores, issued after those copies. Counting fewer than were issued
-    // would only make the wait stricter.
-    const bool next = u + 1 < ue;
-    const int nwait = !next ? 0 : (wave_s != 0 ? 8 : (sync && u == ub ? 2 : 10)) + stores;
-    att_wait_vm(uni(nwait));
-    stores = 0;
-    if (new_pair) {
-      // wave 0's query copy has landed for every wave; the previous
-      // segment's readers of the shared LDS areas are done
-      lds_sync();
-      u32x4 qw[8];
-      att_read_q(ring0 + slot * ATT_SLOT_BYTES + 8 * ATT_WAVE_BLOCKS * 1024 + min(lr, 3) * 512 + lg * 32,
-                 qw);
-      // no wave copies the next queries into this slot before all have read them
-      lds_sync();
+    const int n = sl.vis(b), fp = sl.first(b);
+    auto kbase = kb_l + b * kv_ss + h * kv_sh;
+    auto vbase = vb_l + b * kv_ss + h * kv_sh;
+    // slot of the chunk's first key; keys past the visible rows are clamped
+    // to the last one and masked out of the scores
+    const int s0 = (fp + c * ATT_CH) % kv_cap;
+    const int last = n - 1 - c * ATT_CH;
+    auto slot_of = [&](int off) {
+      int sl_ = s0 + min(off, last);
+      return sl_ - (sl_ >= kv_cap ? kv_cap : 0);
+    };
+    // block k (16 keys) of the chunk comes by global-to-LDS copies into the
+    // wave's ring slot k % ns: lane (key lr, group lg) brings key
+    // dims 32 kb + 8 lg .. + 8 (kb = 0..3), lane (group g = lg, c = lr)
+    // brings key 4 g + t, dims 8 c .. + 8 (t = 0..3); 8 copies per block
+    constexpr int NB = ATT_CH / 16;
+    auto slot_addr = [&](int k) {   // byte offset of block k's slot in the ring
+      const int sl_ = slot0 + k % ns;
+      return (unsigned)((sl_ >> 3) * ATT_SLOT_BYTES + (sl_ & 7) * ATT_WAVE_BLOCKS * 1024);
+    };
+    auto copy_blk = [&](int k) __attribute__((always_inline)) {
+      KD_LDS u32x4* dst = (KD_LDS u32x4*)((KD_LDS char*)&g_att_ring[0][0][0] + slot_addr(k));
+      const size_t krow = (size_t)slot_of(16 * k + lr) * kv_sl;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(kbase + krow + 32 * kb + 8 * lg),
+                                         (KD_LDS void*)(dst + kb * 64), 16, 0, 0);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        __builtin_amdgcn_global_load_lds(
+            reinterpret_cast<const void*>(vbase + (size_t)slot_of(16 * k + 4 * lg + t) * kv_sl + 8 * lr),
+            (KD_LDS void*)(dst + (4 + t) * 64), 16, 0, 0);
+    };
+    // the pair's 4 query rows as the B operand: lane (lr < 4, lg) takes row
+    // lr, dims 32 kb + 8 lg .. + 8 (loaded before the first two blocks'
+    // copies, so the first block's wait covers them)
+    bf16x8 qh[4], ql[4];
+    {
+      const float* qp = q_l + (size_t)(b * 4 + min(lr, 3)) * H + h * DH + 8 * lg;
+      f32x4 qx[8];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
+        qx[2 * kb] = *reinterpret_cast<const f32x4*>(qp + 32 * kb);
+        qx[2 * kb + 1] = *reinterpret_cast<const f32x4*>(qp + 32 * kb + 4);
+      }
+      for (int k = 0; k < ns; ++k) copy_blk(k);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const f32x4 x0 = qx[2 * kb], x1 = qx[2 * kb + 1];
         float qv[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          qv[e] = lr < 4 ? u2f(qw[2 * kb][e]) * qs : 0.f;
-          qv[4 + e] = lr < 4 ? u2f(qw[2 * kb + 1][e]) * qs : 0.f;
+          qv[e] = lr < 4 ? x0[e] * qs : 0.f;
+          qv[4 + e] = lr < 4 ? x1[e] * qs : 0.f;
         }
         split_bf16(qv, qh[kb], ql[kb]);
       }
     }
-    m_run = -__builtin_inff();
-    l_run = 0.f;
+    float m_run = -__builtin_inff(), l_run = 0.f;
+    float o[4][8];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
-    seg_c0 = c;
-    u32x4 kr[4], vr[4];
-    att_read_kv(ring0 + slot * ATT_SLOT_BYTES + wave * ATT_WAVE_BLOCKS * 1024 + lane * 16, kr, vr);
-    if (u == ub) trace_mark(a, sy, 3);
-    // the unit's keys and values are in registers and every wave has read
-    // its queries: the slot is free, so the unit after next is copied into
-    // it before this one is computed
-    if (u + 2 < ue) {
-      copy_kv(u + 2, slot);
-      copy_q(u + 2, slot);
-    }
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+    for (int k = 0; k < NB; ++k) {
+      // block k has landed once at most the later blocks' copies (8 each)
+      // are in flight; its slot is refilled with block k + ns after the read
+      att_wait_blocks(min(ns - 1, NB - 1 - k));
+      u32x4 kk[4], vv[4];
+      att_read_kv(ring0 + slot_addr(k) + lane * 16, kk, vv);
+      if (k + ns < NB) copy_blk(k + ns);
+      // two independent accumulation chains (the queries' bf16 high and low
+      // parts), added at the end
+      f32x4 acch = {0.f, 0.f, 0.f, 0.f}, accl = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const bf16x8 kk = __builtin_bit_cast(bf16x8, kr[kb]);
-      acc = mfma_bf16(kk, qh[kb], acc);
-      acc = mfma_bf16(kk, ql[kb], acc);
-    }
-    // lane holds S^T[key 4 lg + e][j = lr] of the wave's 16 keys
-    float sc[4], mx = -__builtin_inff();
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int key = c * ATT_CH + wave * 16 + 4 * lg + e;
-      sc[e] = key < n ? acc[e] : -__builtin_inff();
-      mx = fmaxf(mx, sc[e]);
-    }
-    {
-      float r0, r1;
-      pl16(mx, mx, r0, r1);   // the max over lane rows (l, l ^ 16)
-      mx = fmaxf(r0, r1);
-      pl32(mx, mx, r0, r1);   // and over lane halves
-      mx = fmaxf(r0, r1);
-    }
-    const float m_new = fmaxf(m_run, mx);
-    // rescale of the state so far (0 while it is empty)
-    const float alpha = m_run == -__builtin_inff() ? 0.f : exp2f(m_run - m_new);
-    float pe[4], ls = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      pe[e] = sc[e] == -__builtin_inff() ? 0.f : exp2f(sc[e] - m_new);
-      ls += pe[e];
-    }
-    {
-      float r0, r1;
-      pl16(ls, ls, r0, r1);
-      ls = r0 + r1;
-      pl32(ls, ls, r0, r1);
-      ls = r0 + r1;
-    }
-    l_run = l_run * alpha + ls;
-    m_run = m_new;
-    if (lr < 4)
-      *reinterpret_cast<KD_LDS f32x4*>(s_p + (wave * 4 + lr) * 16 + 4 * lg) =
-          f32x4{pe[0], pe[1], pe[2], pe[3]};
-    // the rescale factor of row j lives in lane j
-    float aj[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) aj[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), j));
-    // P V: lane (g, c) = (lane / 16, lane % 16) adds its keys 4g..4g+3 for
-    // dims 8c..8c+7 and all 4 rows (the wave's own probabilities: LDS
-    // operations of a wave complete in order)
-    f32x4 pj[4];  // pj[j] = probabilities of row j, keys 4g .. 4g+3
-    att_read_p((unsigned)(uintptr_t)(s_p + wave * 64 + 4 * lg), pj);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[j][e] *= aj[j];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      float vf[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        vf[2 * i] = u2f(vr[t][i] << 16);
-        vf[2 * i + 1] = u2f(vr[t][i] & 0xffff0000u);
+      for (int kb = 0; kb < 4; ++kb) {
+        const bf16x8 kx = __builtin_bit_cast(bf16x8, kk[kb]);
+        acch = mfma_bf16(kx, qh[kb], acch);
+        accl = mfma_bf16(kx, ql[kb], accl);
       }
+      // lane holds S^T[key 4 lg + e][j = lr] of the block's 16 keys
+      float sc[4], mx = -__builtin_inff();
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sc[e] = 16 * k + 4 * lg + e <= last ? acch[e] + accl[e] : -__builtin_inff();
+        mx = fmaxf(mx, sc[e]);
+      }
+      {
+        float r0, r1;
+        pl16(mx, mx, r0, r1);   // the max over lane rows (l, l ^ 16)
+        mx = fmaxf(r0, r1);
+        pl32(mx, mx, r0, r1);   // and over lane halves
+        mx = fmaxf(r0, r1);
+      }
+      const float m_new = fmaxf(m_run, mx);
+      // rescale of the state so far (0 while it is empty)
+      const float alpha = m_run == -__builtin_inff() ? 0.f : exp2f(m_run - m_new);
+      float pe[4], ls = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pe[e] = sc[e] == -__builtin_inff() ? 0.f : exp2f(sc[e] - m_new);
+        ls += pe[e];
+      }
+      {
+        float r0, r1;
+        pl16(ls, ls, r0, r1);
+        ls = r0 + r1;
+        pl32(ls, ls, r0, r1);
+        ls = r0 + r1;
+      }
+      l_run = l_run * alpha + ls;
+      m_run = m_new;
+      if (lr < 4) *reinterpret_cast<KD_LDS f32x4*>(s_p + lr * 16 + 4 * lg) = f32x4{pe[0], pe[1], pe[2], pe[3]};
+      // the rescale factor of row j lives in lane j
+      float aj[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        aj[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), j));
+      // P V: pj[j] = probabilities of row j, keys 4g .. 4g+3 (the wave's own
+      // LDS writes complete before its reads)
+      f32x4 pj[4];
+      att_read_p((unsigned)(uintptr_t)(s_p + 4 * lg), pj);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[j][e] += pj[j][t] * vf[e];
-    }
-
-    {
-      // the previous chunk's readers of the shared LDS areas are done (a new
-      // pair's query read above waited for them already)
-      if (!new_pair) lds_sync();
-      // sum the 4 key groups: groups g and g^2 exchange, g < 2 keeping rows
-      // 0, 1 and g >= 2 rows 2, 3; then g and g^1, odd groups keeping the
-      // second of their rows -- group g ends with row g
-      // (with pl32(o[jj], o[2 + jj]) the lower lane of a pair gets its own
-      // row jj and the upper lane's row jj, the upper lane the lower lane's
-      // row 2 + jj and its own: the two add to the pair's sum of that row)
-      float r1[2][8];
+        for (int e = 0; e < 8; ++e) o[j][e] *= aj[j];
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
+      for (int t = 0; t < 4; ++t) {
+        float vf[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float x0, x1;
-          pl32(o[jj][e], o[2 + jj][e], x0, x1);
-          r1[jj][e] = x0 + x1;
+        for (int i = 0; i < 4; ++i) {
+          vf[2 * i] = u2f(vv[t][i] << 16);
+          vf[2 * i + 1] = u2f(vv[t][i] & 0xffff0000u);
         }
-      f32x4 r2a, r2b;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[j][e] += pj[j][t] * vf[e];
+      }
+    }
+    // sum the 4 key groups: groups g and g^2 exchange, g < 2 keeping rows
+    // 0, 1 and g >= 2 rows 2, 3; then g and g^1, odd groups keeping the
+    // second of their rows -- group g ends with row g, dims 8 lr .. + 8
+    float r1[2][8];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float x0, x1;
-        pl16(r1[0][e], r1[1][e], x0, x1);
-        const float v = x0 + x1;
-        if (e < 4) r2a[e] = v; else r2b[e - 4] = v;
+        pl32(o[jj][e], o[2 + jj][e], x0, x1);
+        r1[jj][e] = x0 + x1;
       }
-      *reinterpret_cast<KD_LDS f32x4*>(s_o + (wave * 4 + lg) * DH + 8 * lr) = r2a;
-      *reinterpret_cast<KD_LDS f32x4*>(s_o + (wave * 4 + lg) * DH + 8 * lr + 4) = r2b;
-      if (lr < 4 && lg == 0) att_write_ml((unsigned)(uintptr_t)(s_m + wave * 4 + lr), m_run, l_run);
-      lds_sync();
-      chunk_partial_store(a, l, b, h, seg_c0, s_m, s_o);
-      stores = 3;
-      // the next chunk waits at a barrier before it reuses the LDS areas
+    f32x4 r2a, r2b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x0, x1;
+      pl16(r1[0][e], r1[1][e], x0, x1);
+      const float v = x0 + x1;
+      if (e < 4) r2a[e] = v; else r2b[e - 4] = v;
     }
+    // the chunk's partial at its slot: rows lg, dims 8 lr .. + 8; max and
+    // sum of row lr from lanes lr < 4 of group 0
+    const size_t pb = ((size_t)(b * NH + h) * nch + c) * 4;
+    att_store4(s.ao[l] + (pb + lg) * DH + 8 * lr, r2a);
+    att_store4(s.ao[l] + (pb + lg) * DH + 8 * lr + 4, r2b);
+    if (lg == 0 && lr < 4) {
+      att_store(s.am[l] + pb + lr, m_run);
+      att_store(s.al[l] + pb + lr, l_run);
+    }
+    // counted once the wave's stores are acknowledged
+    __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0)
+    if (lane == 0) (void)add_rlx(&s.att_cnt[((l * SB_MAX + b) * NH + h) * 32], 1u);
   }
-  attn_finish(a, l, sl, ub, ue, br, sy, sync);
+  trace_mark(a, sy, 3);
+  attn_finish(a, l, sl, 0, 0, br, sy, sync, true);
   trace_mark(a, sy, 6);
   trace_mark(a, sy, 4);
 }
