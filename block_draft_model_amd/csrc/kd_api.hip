@@ -604,10 +604,10 @@ kd_status kd_create(const kd_config* cfg, void* hip_stream, kd_ctx** out) {
   // (stream, head) per workgroup, so the grid must cover every pair
   c->small_ok = c->G >= kd::SB_MAX * kd::NH;
   if (ok && c->small_ok) {
-    ok = dev_alloc(c->work_allocs, &c->small_mem, kd::small_bytes(w.att_nch));
+    ok = dev_alloc(c->work_allocs, &c->small_mem, kd::small_bytes(kd::small_nch(cfg->window)));
     for (int i = 0; i < kd_ctx::NSLOT; ++i) ok = ok && dev_alloc(c->work_allocs, &c->args_dev[i], 1);
     if (ok) {
-      kd::small_carve(c->small_mem, w.att_nch, &c->small);
+      kd::small_carve(c->small_mem, kd::small_nch(cfg->window), &c->small);
       ok = hipMemset(c->small.bar, 0, 20 * 32 * sizeof(unsigned)) == hipSuccess &&
            hipMemset(c->small.att_cnt, 0, kd::NL * kd::SB_MAX * kd::NH * 32 * sizeof(unsigned)) ==
                hipSuccess &&
@@ -908,9 +908,8 @@ static kd_status round_impl(kd_ctx* c, int depth, int B, const void* taps, const
       a.R = R;
       a.nl = c->debug_layers < 0 ? kd::NL : c->debug_layers;
       a.window = c->cfg.window;
-      // partial slots per (stream, head), padded to whole 128-byte lines of the
-      // per-chunk max and sum (8 chunks): different pairs never share a line
-      a.nch = (w.att_nch + 7) / 8 * 8;
+      // partial slots per (stream, head), as the buffers were carved
+      a.nch = kd::small_nch(c->cfg.window);
       a.eps = eps;
       a.theta = c->cfg.rope_theta;
       a.taps = static_cast<const uint16_t*>(taps);

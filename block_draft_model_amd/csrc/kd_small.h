@@ -16,6 +16,11 @@ constexpr int HEAD_NT = 2;     // vocab tiles per head unit
 constexpr int MAX_G = 256;     // workgroups (one per CU); barrier tree is 16 x 16
 constexpr int DOWN_KS = 3;     // the down projection's inputs split in thirds across workgroups
 
+// Attention partial slots per (stream, head) for a window: one per 128-key
+// chunk, padded to whole 128-byte lines of the per-chunk max and sum (8
+// chunks), so different pairs never share a line.
+__host__ __device__ inline int small_nch(int window) { return ((window + ATT_CH - 1) / ATT_CH + 7) / 8 * 8; }
+
 // Stage index of the residual stream: the layer input, after O, after down.
 __host__ __device__ inline int xs_in(int l) { return l == 0 ? 0 : 3 * l; }
 __host__ __device__ inline int xs_o(int l) { return 3 * l + 1; }

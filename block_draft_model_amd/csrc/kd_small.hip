@@ -907,6 +907,13 @@ __device__ __forceinline__ float row16_sum(float x) {
   x += dpp<0x140>(x);  // row_mirror
   return x;
 }
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp<0xB1>(x));
+  x = fmaxf(x, dpp<0x4E>(x));
+  x = fmaxf(x, dpp<0x141>(x));
+  x = fmaxf(x, dpp<0x140>(x));
+  return x;
+}
 __device__ __forceinline__ float rows_sum_to_row3(float x) {
   const unsigned xb = __builtin_bit_cast(unsigned, x);
   const float s = x + __builtin_bit_cast(float, __builtin_amdgcn_permlane16_swap(xb, xb, false, false)[0]);
@@ -928,10 +935,11 @@ __device__ __forceinline__ float rows_sum4(float x) {
 __device__ __forceinline__ int pick4(int b, int x0, int x1, int x2, int x3) {
   return b == 0 ? x0 : (b == 1 ? x1 : (b == 2 ? x2 : x3));
 }
-struct StreamLens {
+template <int CH>
+struct StreamLensT {
   int n0, n1, n2, n3;      // visible context rows min(len, window)
   int f0, f1, f2, f3;      // position of the first visible row
-  int c0, c1, c2, c3;      // chunks of ATT_CH rows per (stream, head)
+  int c0, c1, c2, c3;      // chunks of CH rows per (stream, head)
   int o1, o2, o3, total;   // first attention unit of streams 1..3; all units
   __device__ __forceinline__ void load(Args& a) {
     const int B = a.B, W = a.window;
@@ -945,10 +953,10 @@ struct StreamLens {
     const int l3 = B > 3 ? __builtin_amdgcn_readlane(mine, 3) : 0;
     n0 = min(l0, W); n1 = min(l1, W); n2 = min(l2, W); n3 = min(l3, W);
     f0 = l0 - n0; f1 = l1 - n1; f2 = l2 - n2; f3 = l3 - n3;
-    c0 = (n0 + ATT_CH - 1) / ATT_CH;
-    c1 = (n1 + ATT_CH - 1) / ATT_CH;
-    c2 = (n2 + ATT_CH - 1) / ATT_CH;
-    c3 = (n3 + ATT_CH - 1) / ATT_CH;
+    c0 = (n0 + CH - 1) / CH;
+    c1 = (n1 + CH - 1) / CH;
+    c2 = (n2 + CH - 1) / CH;
+    c3 = (n3 + CH - 1) / CH;
     o1 = NH * c0;
     o2 = o1 + NH * c1;
     o3 = o2 + NH * c2;
@@ -980,6 +988,8 @@ struct StreamLens {
     return total < G ? nc : owner(u0 + nc - 1, G) - owner(u0, G) + 1;
   }
 };
+// Attention units are chunks of ATT_CH = 128 keys.
+using StreamLens = StreamLensT<ATT_CH>;
 
 // The block's own part of the attention of one (stream, head) for thread
 // (j, d): scores s[j][i] = q_j . k_i of block rows i <= j (log2 units, -inf
@@ -1299,16 +1309,188 @@ __device__ __forceinline__ void attn_finish(Args& a, int l, const StreamLens& sl
   }
 }
 
+// Merge of one (stream, head) pair by a single wave: the chunk partials in
+// chunk order (groups of 16, each group's maximum first), then the block's
+// own keys (causal within the block). Lane (j, r) = (lane / 16, lane % 16)
+// makes dims 8 r .. 8 r + 7 of block row j and stores them as f16.
+__device__ __forceinline__ void attn_merge_wave(Args& a_, int l_, int b_, int h_,
+                                                          int n_) {
+  const auto l = uni(l_);
+  const auto b = uni(b_);
+  const auto h = uni(h_);
+  const auto n = uni(n_);
+  Args& a = uni(a_);
+  auto& s = a.s;
+  const int lane = threadIdx.x & 63, j = lane >> 4, r = lane & 15;
+  const int nch = a.nch, nc = (n + ATT_CH - 1) / ATT_CH;
+  const float qs = 0.08838834764831845f * 1.4426950408889634f;  // 1/sqrt(128) * log2(e)
+  // the block's own rows: query j, keys and values 0..3 (fp32, dims 8 r ..)
+  const size_t hb = (size_t)b * BLK * H + h * DH + 8 * r;
+  f32x4 qv[2], kv4[4][2], vv4[4][2];
+  qv[0] = *reinterpret_cast<const f32x4*>(s.q[l] + hb + j * H);
+  qv[1] = *reinterpret_cast<const f32x4*>(s.q[l] + hb + j * H + 4);
+#pragma unroll
+  for (int i = 0; i < BLK; ++i) {
+    kv4[i][0] = *reinterpret_cast<const f32x4*>(s.k[l] + hb + i * H);
+    kv4[i][1] = *reinterpret_cast<const f32x4*>(s.k[l] + hb + i * H + 4);
+    vv4[i][0] = *reinterpret_cast<const f32x4*>(s.v[l] + hb + i * H);
+    vv4[i][1] = *reinterpret_cast<const f32x4*>(s.v[l] + hb + i * H + 4);
+  }
+  // the block part: s_i = q_j . k_i for i <= j
+  float sb[BLK];
+#pragma unroll
+  for (int i = 0; i < BLK; ++i) {
+    float d = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) d += qv[0][e] * kv4[i][0][e] + qv[1][e] * kv4[i][1][e];
+    sb[i] = i <= j ? row16_sum(d) * qs : -__builtin_inff();
+  }
+  float M = -__builtin_inff(), Ls = 0.f, O[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) O[e] = 0.f;
+  const size_t pb = (size_t)(b * NH + h) * nch * 4 + j;   // (pair, chunk c, row j) at pb + 4 c
+  for (int c0 = 0; c0 < nc; c0 += 16) {
+    const int cn = min(16, nc - c0);
+    // lane (j, r) takes chunk c0 + r's max and sum of row j
+    const int cr = c0 + min(r, cn - 1);
+    float mc = s.am[l][pb + 4 * cr], lc = s.al[l][pb + 4 * cr];
+    if (r >= cn) {
+      mc = -__builtin_inff();
+      lc = 0.f;
+    }
+    f32x4 oc[16][2];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const size_t po = (pb + 4 * (size_t)(c0 + min(k, cn - 1))) * DH + 8 * r;
+      oc[k][0] = *reinterpret_cast<const f32x4*>(s.ao[l] + po);
+      oc[k][1] = *reinterpret_cast<const f32x4*>(s.ao[l] + po + 4);
+    }
+    const float Mn = fmaxf(M, row16_max(mc));
+    const float fs = M == -__builtin_inff() ? 0.f : exp2f(M - Mn);
+    const float fc = mc == -__builtin_inff() ? 0.f : exp2f(mc - Mn);
+    Ls = Ls * fs + row16_sum(lc * fc);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) O[e] *= fs;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float fk = __shfl(fc, (lane & 48) | k, 64);   // 0 past the group's chunks
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        O[e] += fk * oc[k][0][e];
+        O[4 + e] += fk * oc[k][1][e];
+      }
+    }
+    M = Mn;
+  }
+  float Mb = M;
+#pragma unroll
+  for (int i = 0; i < BLK; ++i) Mb = fmaxf(Mb, sb[i]);
+  const float fs = M == -__builtin_inff() ? 0.f : exp2f(M - Mb);
+  Ls *= fs;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) O[e] *= fs;
+#pragma unroll
+  for (int i = 0; i < BLK; ++i) {
+    if (i <= j) {
+      const float p = exp2f(sb[i] - Mb);
+      Ls += p;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        O[e] += p * vv4[i][0][e];
+        O[4 + e] += p * vv4[i][1][e];
+      }
+    }
+  }
+  u32x4 packed;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t lo = __builtin_bit_cast(uint16_t, f16_checked(O[2 * e] / Ls));
+    const uint32_t hi = __builtin_bit_cast(uint16_t, f16_checked(O[2 * e + 1] / Ls));
+    packed[e] = lo | (hi << 16);
+  }
+  gptr<uint16_t> dst = s.o[l] + (size_t)(b * BLK + j) * H + h * DH + 8 * r;
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(dst), "v"(packed) : "memory");
+  // the attention loop's waits count only its own copies
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
+// Waits until the LDS word *p equals want (set by another wave of the
+// workgroup); after 0.2 s it sets the round's error word and goes on, so the
+// wave still ends.
+__device__ __forceinline__ void lds_wait_eq(Args& a, KD_LDS unsigned* p, unsigned want) {
+  const unsigned long long t0 = wall_clock64();
+  for (unsigned it = 1; __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != want; ++it) {
+    if ((it & 63) == 0 && wall_clock64() - t0 > 20000000ull) {
+      __hip_atomic_store(&a.s.bar[18 * 32], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// The state of one half (64 keys) of a chunk after the 4 key groups are
+// summed: lane (g, r) holds row g's unnormalised output at dims 8 r .. + 8
+// and the row's max (log2 units) and sum. A chunk's partial is always
+// half_merge(first half, second half), whichever waves computed the halves.
+struct HalfState {
+  f32x4 o0, o1;
+  float m, l;
+};
+// o[j][e]: the wave's per-key-group sums (lane (g, c): keys 4g..4g+3, dims
+// 8c..8c+7 of row j); m_run, l_run: row lr's max and sum in lane lr.
+__device__ __forceinline__ HalfState half_reduce(const float (&o)[4][8], float m_run, float l_run, int lg) {
+  // sum the 4 key groups: groups g and g^2 exchange, g < 2 keeping rows
+  // 0, 1 and g >= 2 rows 2, 3; then g and g^1, odd groups keeping the
+  // second of their rows -- group g ends with row g, dims 8 lr .. + 8
+  float r1[2][8];
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x0, x1;
+      pl32(o[jj][e], o[2 + jj][e], x0, x1);
+      r1[jj][e] = x0 + x1;
+    }
+  HalfState r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float x0, x1;
+    pl16(r1[0][e], r1[1][e], x0, x1);
+    const float v = x0 + x1;
+    if (e < 4) r.o0[e] = v; else r.o1[e - 4] = v;
+  }
+  // row lg's max and sum from lane lg
+  const int mi = __builtin_bit_cast(int, m_run), li = __builtin_bit_cast(int, l_run);
+  r.m = __builtin_bit_cast(float, pick4(lg, __builtin_amdgcn_readlane(mi, 0), __builtin_amdgcn_readlane(mi, 1),
+                                        __builtin_amdgcn_readlane(mi, 2), __builtin_amdgcn_readlane(mi, 3)));
+  r.l = __builtin_bit_cast(float, pick4(lg, __builtin_amdgcn_readlane(li, 0), __builtin_amdgcn_readlane(li, 1),
+                                        __builtin_amdgcn_readlane(li, 2), __builtin_amdgcn_readlane(li, 3)));
+  return r;
+}
+__device__ __forceinline__ HalfState half_merge(const HalfState& A, const HalfState& B) {
+  const float M = fmaxf(A.m, B.m);
+  const float fa = A.m == -__builtin_inff() ? 0.f : exp2f(A.m - M);
+  const float fb = B.m == -__builtin_inff() ? 0.f : exp2f(B.m - M);
+  HalfState r;
+  r.m = M;
+  r.l = A.l * fa + B.l * fb;
+  r.o0 = A.o0 * fa + B.o0 * fb;
+  r.o1 = A.o1 * fa + B.o1 * fb;
+  return r;
+}
+
 // A four-float write-through store (one vector memory instruction).
 __device__ __forceinline__ void att_store4(gptr<float> p, f32x4 v) {
   asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
 }
 
 // Attention of the block rows to the context. Unit u = (stream, head, chunk
-// of ATT_CH keys); wave w of workgroup g takes the units g + G (w + 8 i),
-// each on its own: the chunk's 8 blocks of 16 keys in key order through the
-// wave's two LDS ring slots (global-to-LDS copies, the next block in flight
-// while one is computed), per block
+// of ATT_CH = 128 keys), computed as two halves of 4 blocks of 16 keys: with
+// at most 4 units per workgroup wave pair (2v, 2v + 1) of workgroup g takes
+// the units g + G (v + 4 i), one half each; otherwise wave w takes the units
+// g + G (w + 8 i), both halves in turn. Each half runs in key order through
+// the wave's two LDS ring slots (global-to-LDS copies, the next block in
+// flight while one is computed), per block
 //   scores  S^T[key][j] = K Q^T on the matrix cores (16x16x32 bf16): keys as
 //           the A operand (lane: key lane%16, dims 32kb + 8(lane/16)), the
 //           queries (pre-scaled by log2(e)/sqrt(128)) split into bf16 hi + lo
@@ -1319,10 +1501,12 @@ __device__ __forceinline__ void att_store4(gptr<float> p, f32x4 v) {
 //   P V     on the vector units: lane (g, c) adds keys 4g..4g+3 of the block
 //           for dims 8c..8c+7 of all 4 rows (the probabilities pass through
 //           the wave's own LDS area).
-// The chunk's partial (max, sum, unnormalised output of each row) is stored
-// at its slot and the pair's counter counts it; the workgroup that merges
-// the pair waits for all its chunks and merges them in chunk order (so a
-// stream's result does not depend on the batch around it).
+// The chunk's partial (max, sum, unnormalised output of each row) is the
+// merge of its two half states, the same arithmetic whichever waves computed
+// them; it is stored at its slot and the pair's counter counts it. The wave
+// that counts the pair's last chunk merges the pair's partials in chunk order
+// (so a stream's result does not depend on the batch around it) with the
+// block's own keys.
 __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int l_, SyncState sy,
                                                   bool sync) {
   const auto l = uni(l_);
@@ -1345,27 +1529,34 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
   auto q_l = s.q[l];
   const unsigned ring0 = (unsigned)(uintptr_t)&g_att_ring[0][0][0];
 
-  // the (stream, head) this workgroup merges, if any: (stream, head) i is
-  // merged by workgroup i (B * NH <= G)
-  const int nbh = a.B * NH;
-  const int mi = wg;
-  const bool merges = wg < nbh;
-  BlockRows br{};
-  if (merges && !sync) br.load(a, l, mi / NH, mi % NH);
+  // With at most 4 units per workgroup the two halves of a unit run on the
+  // wave pair (2v, 2v + 1) and the second half's state reaches the first
+  // wave through LDS (x_area: [64 lanes][8] outputs, [4] maxima, [4] sums,
+  // then a ready flag and an acknowledgement); otherwise one wave computes
+  // both halves, one after the other.
+  const bool split = U <= 4 * G;
+  const int pv = wave_s >> 1, half = wave_s & 1;
+  lds_f x_area = (lds_f)g_att_small + 512 + pv * 528;
+  KD_LDS unsigned* x_flag = reinterpret_cast<KD_LDS unsigned*>(x_area + 520);
+  KD_LDS unsigned* x_ack = x_flag + 1;
   if (sync) {
     grid_arrive(a, sy);
     grid_wait(a, sy);
-    if (merges) br.load(a, l, mi / NH, mi % NH);
   }
+  if (threadIdx.x < 4) {
+    lds_f xa = (lds_f)g_att_small + 512 + threadIdx.x * 528;
+    *reinterpret_cast<KD_LDS unsigned*>(xa + 520) = 0u;
+    *reinterpret_cast<KD_LDS unsigned*>(xa + 521) = 0u;
+  }
+  lds_sync();
   trace_mark(a, sy, 2);
-
-  // the workgroup's units wg, wg + G, ...: wave w takes the w-th, (w + 8)-th,
-  // ...; each wave owns two LDS ring slots of 8 KB (one 16-key block each):
-  // one block is computed while the next is in flight. (More slots for the
-  // active waves when fewer are active measured slower.)
+  // each wave owns two LDS ring slots of 8 KB (one 16-key block each): one
+  // block is computed while the next is in flight
   constexpr int ns = 2;
   const int slot0 = wave_s * ns;
-  for (int u = wg + G * wave_s; u < U; u += 8 * G) {
+  const int k0 = split ? 4 * half : 0, k1 = split ? k0 + 4 : 8;
+  unsigned iter = 0;
+  for (int u = split ? wg + G * pv : wg + G * wave_s; u < U; u += split ? 4 * G : 8 * G, ++iter) {
     int b, c, h;
     sl.unit(u, b, c, h);
     const int n = sl.vis(b), fp = sl.first(b);
@@ -1380,12 +1571,11 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
       return sl_ - (sl_ >= kv_cap ? kv_cap : 0);
     };
     // block k (16 keys) of the chunk comes by global-to-LDS copies into the
-    // wave's ring slot k % ns: lane (key lr, group lg) brings key
+    // wave's ring slot (k - k0) % ns: lane (key lr, group lg) brings key
     // dims 32 kb + 8 lg .. + 8 (kb = 0..3), lane (group g = lg, c = lr)
     // brings key 4 g + t, dims 8 c .. + 8 (t = 0..3); 8 copies per block
-    constexpr int NB = ATT_CH / 16;
     auto slot_addr = [&](int k) {   // byte offset of block k's slot in the ring
-      const int sl_ = slot0 + k % ns;
+      const int sl_ = slot0 + (k - k0) % ns;
       return (unsigned)((sl_ >> 3) * ATT_SLOT_BYTES + (sl_ & 7) * ATT_WAVE_BLOCKS * 1024);
     };
     auto copy_blk = [&](int k) __attribute__((always_inline)) {
@@ -1413,7 +1603,7 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
         qx[2 * kb] = *reinterpret_cast<const f32x4*>(qp + 32 * kb);
         qx[2 * kb + 1] = *reinterpret_cast<const f32x4*>(qp + 32 * kb + 4);
       }
-      for (int k = 0; k < ns; ++k) copy_blk(k);
+      for (int k = k0; k < k0 + ns; ++k) copy_blk(k);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const f32x4 x0 = qx[2 * kb], x1 = qx[2 * kb + 1];
@@ -1432,14 +1622,24 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
+    HalfState hA;   // the first half's state when one wave computes both
 #pragma unroll 1
-    for (int k = 0; k < NB; ++k) {
+    for (int k = k0; k < k1; ++k) {
+      if (k == 4 && !split) {
+        hA = half_reduce(o, m_run, l_run, lg);
+        m_run = -__builtin_inff();
+        l_run = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
+      }
       // block k has landed once at most the later blocks' copies (8 each)
       // are in flight; its slot is refilled with block k + ns after the read
-      att_wait_blocks(min(ns - 1, NB - 1 - k));
+      att_wait_blocks(min(ns - 1, k1 - 1 - k));
       u32x4 kk[4], vv[4];
       att_read_kv(ring0 + slot_addr(k) + lane * 16, kk, vv);
-      if (k + ns < NB) copy_blk(k + ns);
+      if (k + ns < k1) copy_blk(k + ns);
       // two independent accumulation chains (the queries' bf16 high and low
       // parts), added at the end
       f32x4 acch = {0.f, 0.f, 0.f, 0.f}, accl = {0.f, 0.f, 0.f, 0.f};
@@ -1509,42 +1709,58 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
           for (int e = 0; e < 8; ++e) o[j][e] += pj[j][t] * vf[e];
       }
     }
-    // sum the 4 key groups: groups g and g^2 exchange, g < 2 keeping rows
-    // 0, 1 and g >= 2 rows 2, 3; then g and g^1, odd groups keeping the
-    // second of their rows -- group g ends with row g, dims 8 lr .. + 8
-    float r1[2][8];
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float x0, x1;
-        pl32(o[jj][e], o[2 + jj][e], x0, x1);
-        r1[jj][e] = x0 + x1;
+    HalfState hB = half_reduce(o, m_run, l_run, lg);
+    if (split) {
+      if (half == 1) {
+        // the second half's state to the first wave of the pair, once it
+        // has taken the previous one
+        lds_wait_eq(a, x_ack, iter);
+        *reinterpret_cast<KD_LDS f32x4*>(x_area + lane * 8) = hB.o0;
+        *reinterpret_cast<KD_LDS f32x4*>(x_area + lane * 8 + 4) = hB.o1;
+        if (lr == 0) {
+          x_area[512 + lg] = hB.m;
+          x_area[516 + lg] = hB.l;
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the writes have landed
+        if (lane == 0) __hip_atomic_store(x_flag, iter + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        continue;
       }
-    f32x4 r2a, r2b;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float x0, x1;
-      pl16(r1[0][e], r1[1][e], x0, x1);
-      const float v = x0 + x1;
-      if (e < 4) r2a[e] = v; else r2b[e - 4] = v;
+      hA = hB;
+      lds_wait_eq(a, x_flag, iter + 1);
+      hB.o0 = *reinterpret_cast<KD_LDS f32x4*>(x_area + lane * 8);
+      hB.o1 = *reinterpret_cast<KD_LDS f32x4*>(x_area + lane * 8 + 4);
+      hB.m = x_area[512 + lg];
+      hB.l = x_area[516 + lg];
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      if (lane == 0) __hip_atomic_store(x_ack, iter + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
-    // the chunk's partial at its slot: rows lg, dims 8 lr .. + 8; max and
-    // sum of row lr from lanes lr < 4 of group 0
+    const HalfState hc = half_merge(hA, hB);
+    // the chunk's partial at its slot: row lg, dims 8 lr .. + 8; the row's
+    // max and sum from lane (lg, 0)
     const size_t pb = ((size_t)(b * NH + h) * nch + c) * 4;
-    att_store4(s.ao[l] + (pb + lg) * DH + 8 * lr, r2a);
-    att_store4(s.ao[l] + (pb + lg) * DH + 8 * lr + 4, r2b);
-    if (lg == 0 && lr < 4) {
-      att_store(s.am[l] + pb + lr, m_run);
-      att_store(s.al[l] + pb + lr, l_run);
+    att_store4(s.ao[l] + (pb + lg) * DH + 8 * lr, hc.o0);
+    att_store4(s.ao[l] + (pb + lg) * DH + 8 * lr + 4, hc.o1);
+    if (lr == 0) {
+      att_store(s.am[l] + pb + lg, hc.m);
+      att_store(s.al[l] + pb + lg, hc.l);
     }
-    // counted once the wave's stores are acknowledged
+    // counted once the wave's stores are acknowledged; the wave that counts
+    // the pair's last chunk merges the pair and resets its counter
     __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0)
-    if (lane == 0) (void)add_rlx(&s.att_cnt[((l * SB_MAX + b) * NH + h) * 32], 1u);
+    auto cnt = &s.att_cnt[((l * SB_MAX + b) * NH + h) * 32];
+    unsigned before = 0;
+    if (lane == 0) before = add_rlx(cnt, 1u);
+    before = (unsigned)__builtin_amdgcn_readlane((int)before, 0);
+    if (before + 1 == (unsigned)sl.chunks(b)) {
+      if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      attn_merge_wave(a, l, b, h, n);
+    }
   }
   trace_mark(a, sy, 3);
-  attn_finish(a, l, sl, 0, 0, br, sy, sync, true);
-  trace_mark(a, sy, 6);
+  // pairs of streams with no visible context attend to the block only:
+  // (stream, head) i by wave 0 of workgroup i
+  const int nbh = a.B * NH;
+  if (wg < nbh && wave_s == 0 && sl.vis(wg / NH) == 0) attn_merge_wave(a, l, wg / NH, wg % NH, 0);
   trace_mark(a, sy, 4);
 }
 
