@@ -1479,6 +1479,38 @@ __device__ __forceinline__ HalfState half_merge(const HalfState& A, const HalfSt
   return r;
 }
 
+
+// Read-ahead by single waves, after their own work: worker (workgroup w, wave
+// v < nwk) on XCD w % 8 takes the units u = w % 8 (mod 8) of a later phase in
+// turn with that XCD's other workers; touch_unit(u) reads what unit u will
+// load, one dword per 128-byte line, into the wave's own LDS scratch, with at
+// most 8 copies in flight so that the other waves' loads are not held up.
+template <class F>
+__device__ __forceinline__ void warm_waves(int nwk, int nunits, F&& touch_unit) {
+  const int wave = threadIdx.x >> 6;
+  const int w = blockIdx.x, G = gridDim.x, x = w & 7;
+  const int k = (w >> 3) * nwk + wave, nk = ((G - 1 - x) / 8 + 1) * nwk;
+  for (int u = x + 8 * k; u < nunits; u += 8 * nk) touch_unit(u);
+}
+__device__ __forceinline__ void touch_wave(gptr<const uint8_t> p, size_t bytes, KD_LDS void* dump) {
+  for (size_t off = (size_t)(threadIdx.x & 63) * 128; off < bytes; off += 64 * 128) {
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(p + off), dump, 4, 0, 0);
+    att_wait_vm<8>();
+  }
+}
+__device__ __forceinline__ void touch_tiles_wave(Mat& W, int t0, int ntile, KD_LDS void* dump) {
+  const int KB = W.K >> 6, fmt = uni(W.fmt);
+  const size_t cb = fmt == WF_NVFP4 ? 512 : (fmt == WF_BF16 ? 2048 : 1024);
+  for (int t = t0; t < t0 + ntile; ++t) {
+    const size_t blk = (size_t)t * KB;
+    touch_wave(W.w + blk * cb, (size_t)KB * cb, dump);
+    if (fmt == WF_FP8) touch_wave(reinterpret_cast<gptr<const uint8_t>>(W.s + blk * 16), (size_t)KB * 64, dump);
+    if (fmt == WF_NVFP4) touch_wave(W.s4 + blk * 64, (size_t)KB * 64, dump);
+  }
+}
+
+// Byte offset of wave w's first attention ring slot.
+__device__ __forceinline__ unsigned slot0_bytes(int w) { return (unsigned)(((2 * w) >> 3) * ATT_SLOT_BYTES + ((2 * w) & 7) * ATT_WAVE_BLOCKS * 1024); }
 // A four-float write-through store (one vector memory instruction).
 __device__ __forceinline__ void att_store4(gptr<float> p, f32x4 v) {
   asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
@@ -1556,8 +1588,10 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
   const int slot0 = wave_s * ns;
   const int k0 = split ? 4 * half : 0, k1 = split ? k0 + 4 : 8;
   unsigned iter = 0;
+  bool merged = false, worked = false;
   for (int u = split ? wg + G * pv : wg + G * wave_s; u < U; u += split ? 4 * G : 8 * G, ++iter) {
     int b, c, h;
+    worked = true;
     sl.unit(u, b, c, h);
     const int n = sl.vis(b), fp = sl.first(b);
     auto kbase = kb_l + b * kv_ss + h * kv_sh;
@@ -1754,9 +1788,20 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
     if (before + 1 == (unsigned)sl.chunks(b)) {
       if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       attn_merge_wave(a, l, b, h, n);
+      merged = true;
     }
   }
   trace_mark(a, sy, 3);
+  // the waves that computed units and merged none read ahead the output
+  // projection's weights (one tile per unit) on the XCDs that will load them
+  // (not in the persistent kernel, where a late arrival holds up the barrier)
+  if (!sync && worked && !merged) {
+    const int nwk = min(8, split ? 2 * ((U + G - 1) / G) : (U + G - 1) / G);
+    KD_LDS void* dump = (KD_LDS void*)((KD_LDS char*)&g_att_ring[0][0][0] + slot0_bytes(wave_s));
+    auto& L = a.d.layer[l];
+    warm_waves(nwk, HT, [&](int u) { touch_tiles_wave(L.wo, u, 1, dump); });
+    warm_done();
+  }
   // pairs of streams with no visible context attend to the block only:
   // (stream, head) i by wave 0 of workgroup i
   const int nbh = a.B * NH;
