@@ -2191,21 +2191,32 @@ __device__ __forceinline__ void head_finish(Args& a, KD_LDS unsigned long long* 
   auto& d = a.d;
   const int R = a.R;
   lds_sync();
-  if (threadIdx.x < SR_MAX) st_wt64(&s.cand[wg * SR_MAX + threadIdx.x], best[threadIdx.x]);
+  const int t = threadIdx.x;
+  if (t < SR_MAX) st_wt64(&s.cand[wg * SR_MAX + t], best[t]);
   trace_mark(a, sy, 4);
+  // what the last workgroup needs besides the candidates is final before
+  // this phase (the timed-out-wait word, the f16 range flag, the caller's
+  // ids): read now, off its path
+  unsigned failed = 0u, ranged = 0u;
+  if (t == 0) {
+    failed = ld_rlx(&s.bar[18 * 32]);
+    ranged = __hip_atomic_load(&g_f16_range, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  const int r = t >> 5, l32 = t & 31;
+  const bool ok = r < R && l32 == 0 && id_row_valid(a.anchor, a.pred, a.pred_stride, r / BLK, r % BLK, d.V);
   // the last workgroup to finish reduces every workgroup's candidates
   __builtin_amdgcn_s_waitcnt(0);  // the candidate stores are acknowledged
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (t == 0) {
     auto cnt = &s.bar[19 * 32];
     const unsigned v = add_rlx(cnt, 1u);
     const bool last = v == (unsigned)(G - 1);
     if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *s_flag = last ? 1u : 0u;
+    s_flag[0] = last ? 1u : 0u;
+    s_flag[1] = failed;
   }
   lds_sync();
-  if (!*s_flag) return;
-  const int t = threadIdx.x, r = t >> 5, l32 = t & 31;
+  if (!s_flag[0]) return;
   // every candidate load is issued before the first is needed
   unsigned long long kc[MAX_G / 32];
 #pragma unroll
@@ -2218,15 +2229,19 @@ __device__ __forceinline__ void head_finish(Args& a, KD_LDS unsigned long long* 
   for (int i = 0; i < MAX_G / 32; ++i) k = u64_max(k, kc[i]);
 #pragma unroll
   for (int m = 16; m >= 1; m >>= 1) k = u64_max(k, shfl_xor_u64s(k, m));
-  const bool failed = ld_rlx(&s.bar[18 * 32]) != 0u;
-  if (failed && t == 0 && a.status)
-    __hip_atomic_store(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-  // every workgroup's f16 stores of the round are done: status[1] is the range word
-  if (t == 0) flush_f16_range(a.status ? a.status + 1 : nullptr);
-  if (r < R && l32 == 0) {
-    const bool ok = id_row_valid(a.anchor, a.pred, a.pred_stride, r / BLK, r % BLK, d.V);
-    a.out_ids[r] = failed ? -2 : (k && ok ? d.vocab[0xffffffffu - (uint32_t)(k & 0xffffffffu)] : -1);
+  const bool fail = s_flag[1] != 0u;
+  if (t == 0 && a.status) {
+    if (fail) __hip_atomic_store(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    // every workgroup's f16 stores of the round are done: status[1] is the range word
+    if (ranged) {
+      __hip_atomic_store(&g_f16_range, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.status + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+  } else if (t == 0 && ranged) {
+    __hip_atomic_store(&g_f16_range, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  if (r < R && l32 == 0)
+    a.out_ids[r] = fail ? -2 : (k && ok ? d.vocab[0xffffffffu - (uint32_t)(k & 0xffffffffu)] : -1);
 }
 
 // NVFP4 head over 16-row vocab tiles (HEAD_NT per unit): wave w takes the
