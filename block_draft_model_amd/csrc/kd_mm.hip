@@ -77,13 +77,18 @@ struct GemmMM {
 // sp): acc[r][c] = sum over the split's 64-input steps of the row tile r x
 // column tile c products (each block-FP8 or NVFP4 step's partial sum times
 // its scale). sa: the workgroup's double-buffered activation tile in LDS.
-template <int CT, int D, int WF>
+// KS = 2: the workgroup has two groups of four waves, group q taking the
+// q-th half of the split's steps with its own activation buffers (sa + 2q);
+// each group's sums are its own (the caller adds them).
+template <int CT, int D, int WF, int KS = 1>
 __device__ __forceinline__ void mm_accumulate(const GemmMM& g, int rb, int cb, int sp,
-                                              f32x4 (&acc)[MM_RT][CT], u32x4 (*sa)[MM_RT * 2][64]) {
+                                              f32x4 (&acc)[MM_RT][CT], u32x4 (*sa_all)[MM_RT * 2][64]) {
   constexpr int COLS = 16 * CT * MM_WAVES;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = (threadIdx.x >> 6) & (MM_WAVES - 1);
+  const int grp = KS == 1 ? 0 : (int)(threadIdx.x >> 8);
+  u32x4 (*sa)[MM_RT * 2][64] = sa_all + 2 * grp;
   const int MT = mtiles(g.R);
-  const int b0 = sp * g.kbs, nb = g.kbs;
+  const int nb = g.kbs / KS, b0 = sp * g.kbs + grp * nb;
   // wave w stages row tile rb*4 + w (clamped: a tile past the last repeats it,
   // and its output rows are past R and discarded)
   const int mt_ld = min(rb * MM_RT + wave, MT - 1);
@@ -253,11 +258,15 @@ void launch_gemm_mm(hipStream_t st, const uint16_t* af, int R, const WMat& W, in
 // tile in LDS and applies the epilogue per 16-column tile, which holds the
 // RoPE partners (d, d + 64) or a gate row block and its up rows.
 // ---------------------------------------------------------------------------
-template <int CT, int D, int WF>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_proj(GemmMM g, ProjEpi e) {
+// KS = 2 (used for at most 64 rows, where the 64-column tiles leave the
+// grid small and each wave's chain of steps long): 8 waves, the input range
+// split between two groups of four, the second group's sums added to the
+// first's in LDS before the epilogue.
+template <int CT, int D, int WF, int KS>
+__global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(2))) void k_proj(GemmMM g, ProjEpi e) {
   constexpr int COLS = 16 * CT * MM_WAVES;
   constexpr int TP = COLS + 4;                        // LDS row pitch of the staged tile (floats)
-  constexpr int SA_BYTES = 2 * MM_RT * 2 * 64 * 16;
+  constexpr int SA_BYTES = KS * 2 * MM_RT * 2 * 64 * 16;
   constexpr int T_BYTES = 64 * TP * 4;
   __shared__ __attribute__((aligned(16))) unsigned char lds[SA_BYTES > T_BYTES ? SA_BYTES : T_BYTES];
   auto sa = reinterpret_cast<u32x4(*)[MM_RT * 2][64]>(lds);
@@ -265,20 +274,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int RB = (g.R + 63) / 64, CB = g.N / COLS;
   const MmMap m = mm_map(RB, CB, 1);
   if (!m.ok) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = (threadIdx.x >> 6) & (MM_WAVES - 1);
   f32x4 acc[MM_RT][CT];
-  mm_accumulate<CT, D, WF>(g, m.rb, m.cb, 0, acc, sa);   // ends at a barrier: LDS is free
+  mm_accumulate<CT, D, WF, KS>(g, m.rb, m.cb, 0, acc, sa);   // ends at a barrier: LDS is free
+  auto tix = [&](int r, int c, int q) { return (r * 16 + 4 * (lane >> 4) + q) * TP + (wave * CT + c) * 16 + (lane & 15); };
+  if (KS == 1 || threadIdx.x >= 256) {
 #pragma unroll
-  for (int r = 0; r < MM_RT; ++r)
+    for (int r = 0; r < MM_RT; ++r)
 #pragma unroll
-    for (int c = 0; c < CT; ++c)
+      for (int c = 0; c < CT; ++c)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        T[(r * 16 + 4 * (lane >> 4) + q) * TP + (wave * CT + c) * 16 + (lane & 15)] = acc[r][c][q];
+        for (int q = 0; q < 4; ++q) T[tix(r, c, q)] = acc[r][c][q];
+  }
   __syncthreads();
+  if (KS == 2 && threadIdx.x < 256) {
+#pragma unroll
+    for (int r = 0; r < MM_RT; ++r)
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) T[tix(r, c, q)] = acc[r][c][q] + T[tix(r, c, q)];
+  }
+  if (KS == 2) __syncthreads();
   // items: (row, 16-column tile)
   constexpr int NT = COLS / 16;
-  for (int it = threadIdx.x; it < 64 * NT; it += 256) {
+  for (int it = threadIdx.x; it < 64 * NT; it += 256 * KS) {
     const int rl = it / NT, ti = it - rl * NT, row = m.rb * 64 + rl;
     if (row >= g.R) continue;
     const float* tp = T + rl * TP + ti * 16;
@@ -325,19 +345,24 @@ void launch_proj(hipStream_t st, const uint16_t* af, int R, const WMat& W, const
   g.splits = 1;
   g.kbs = g.KB;
   const bool wide = mm_ct(R) == 4;
+  // at most one row block: the input range in two halves inside the workgroup
+  const bool halves = !wide && R <= 64 && g.KB % 2 == 0;
   const dim3 grid(mm_grid(R, W.N / (wide ? 256 : 64), 1));
   switch (W.fmt) {
     case WF_NVFP4:
-      if (wide) k_proj<4, 2, WF_NVFP4><<<grid, 256, 0, st>>>(g, e);
-      else k_proj<1, 4, WF_NVFP4><<<grid, 256, 0, st>>>(g, e);
+      if (wide) k_proj<4, 2, WF_NVFP4, 1><<<grid, 256, 0, st>>>(g, e);
+      else if (halves) k_proj<1, 4, WF_NVFP4, 2><<<grid, 512, 0, st>>>(g, e);
+      else k_proj<1, 4, WF_NVFP4, 1><<<grid, 256, 0, st>>>(g, e);
       break;
     case WF_BF16:
-      if (wide) k_proj<4, 2, WF_BF16><<<grid, 256, 0, st>>>(g, e);
-      else k_proj<1, 4, WF_BF16><<<grid, 256, 0, st>>>(g, e);
+      if (wide) k_proj<4, 2, WF_BF16, 1><<<grid, 256, 0, st>>>(g, e);
+      else if (halves) k_proj<1, 4, WF_BF16, 2><<<grid, 512, 0, st>>>(g, e);
+      else k_proj<1, 4, WF_BF16, 1><<<grid, 256, 0, st>>>(g, e);
       break;
     default:
-      if (wide) k_proj<4, 2, WF_FP8><<<grid, 256, 0, st>>>(g, e);
-      else k_proj<1, 4, WF_FP8><<<grid, 256, 0, st>>>(g, e);
+      if (wide) k_proj<4, 2, WF_FP8, 1><<<grid, 256, 0, st>>>(g, e);
+      else if (halves) k_proj<1, 4, WF_FP8, 2><<<grid, 512, 0, st>>>(g, e);
+      else k_proj<1, 4, WF_FP8, 1><<<grid, 256, 0, st>>>(g, e);
   }
 }
 
