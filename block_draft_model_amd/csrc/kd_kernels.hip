@@ -925,12 +925,10 @@ __global__ __launch_bounds__(256) void k_attn_split_q4(AttnK a) {
   attn_merge(a, lds, m_run, l_run, seg, nseg, h, b, qrow0);
 }
 
-// workgroups a full window of every pair is split into (a few per CU); up to
-// 5 streams every pair then takes 16 segments, so a stream's partials do not
-// depend on the batch there (B16 with ragged contexts measured 0.672 ms per
-// step at 1024, three segments per pair, against 0.695 ms here, but then the
-// segments of 4 streams differ from those of 1)
-constexpr int ATT_WG = 2048;
+// workgroups a full window of every pair is split into (about four per CU;
+// B16 with ragged contexts measured 0.695 ms per step at 2048, six segments
+// per pair, and 0.672 ms at 1024, three)
+constexpr int ATT_WG = 1024;
 
 void launch_attention(hipStream_t st, const Work& w, const DevWeights& dw, int B, const KV& kv,
                       int layer, const int32_t* lens, int window) {
@@ -953,9 +951,12 @@ void launch_attention(hipStream_t st, const Work& w, const DevWeights& dw, int B
   // into as many segments as keep the pairs' workgroups at or below ATT_WG
   // (one segment once the pairs alone reach it), at most the partial slots
   // per pair; shorter contexts take fewer segments
+  // up to 4 streams (a comparison path there: the small-batch path serves
+  // them) every pair takes the most segments, so that a stream's partials are
+  // the same alone and among up to 4
   const int pairs = B * NH;
   const int wb = (window + 15) / 16;
-  int S = ATT_WG / pairs;
+  int S = B <= 4 ? w.att_nch : ATT_WG / pairs;
   S = std::max(1, std::min(S, w.att_nch));
   a.segb = (wb + S - 1) / S;
   S = (wb + a.segb - 1) / a.segb;
