@@ -206,6 +206,36 @@ def test_small_path_stream_alone_equals_stream_in_batch(hC, path):
         hC.drafter.debug_set_path(0)
 
 
+@pytest.mark.parametrize("path", [2, 3])
+def test_small_path_full_batch_equals_streams_alone(hC, path):
+    # 4 streams with full windows make 1,280 attention units, more than 4
+    # per workgroup: one wave computes both halves of each chunk; a stream
+    # alone (320 units) splits every chunk over a wave pair. A chunk's partial
+    # is the same merge of its two half states either way, so the drafts
+    # agree bit for bit. Positions past the ring's capacity wrap.
+    lens = [2048, 2500, 4100, 9000]
+    cfg = dict(name="inv-full", streams=4, lens=("const", 0), model="C", ingest=0)
+    inp = hC.inputs(cfg, base=41, lens_override=lens)
+    hC.drafter.debug_set_path(path)
+    try:
+        batch, ib = hC.run(inp)
+        assert hC.drafter.last_path() == path
+        for b in range(4):
+            one = {k: (v[b:b + 1] if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+            one["k"] = [t[b:b + 1] for t in inp["k"]]
+            one["v"] = [t[b:b + 1] for t in inp["v"]]
+            one["streams"] = 1
+            alone, ia = hC.run(one)
+            rel = np.linalg.norm(alone[0] - batch[b], axis=1) / np.linalg.norm(batch[b], axis=1)
+            log(f"path {path} full-window stream {b} alone vs in batch: max rel L2 {rel.max():.2e}")
+            assert np.array_equal(alone[0], batch[b])
+            assert np.array_equal(ia[0], ib[b])
+    finally:
+        hC.drafter.debug_set_path(0)
+    ref, rid = oracle.oracle_round(hC.oracle, synth.to_numpy_inputs(inp))
+    compare(batch, ib, ref, rid, hC.oracle.vocab, f"full windows path {path}")
+
+
 def test_round_parity_adapters_and_gains_active(hC):
     cfg = dict(name="C-B5", streams=5, lens=("uniform", 0, 3000), model="C", ingest=0)
     inp = hC.inputs(cfg, base=7)
