@@ -177,17 +177,36 @@ __device__ __forceinline__ void mm_accumulate(const GemmMM& g, int rb, int cb, i
   }
 }
 
-template <int CT, int D, int WF>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_mm(GemmMM g) {
+// KS = 2 (at most 64 rows): 8 waves, the split's inputs in two halves, the
+// second group's sums added to the first's through LDS before the store.
+template <int CT, int D, int WF, int KS>
+__global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_mm(GemmMM g) {
   constexpr int COLS = 16 * CT * MM_WAVES;
-  // [buffer][row tile][k tile t, t+1][lane]
-  __shared__ __attribute__((aligned(16))) u32x4 sa[2][MM_RT * 2][64];
+  // [group][buffer][row tile][k tile t, t+1][lane]
+  __shared__ __attribute__((aligned(16))) u32x4 sa[2 * KS][MM_RT * 2][64];
   const int RB = (g.R + 63) / 64, CB = g.N / COLS;
   const MmMap m = mm_map(RB, CB, g.splits);
   if (!m.ok) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = (threadIdx.x >> 6) & (MM_WAVES - 1);
   f32x4 acc[MM_RT][CT];
-  mm_accumulate<CT, D, WF>(g, m.rb, m.cb, m.sp, acc, sa);
+  mm_accumulate<CT, D, WF, KS>(g, m.rb, m.cb, m.sp, acc, sa);   // ends at a barrier: LDS is free
+  if constexpr (KS == 2) {
+    static_assert(sizeof(sa) >= MM_WAVES * MM_RT * CT * 64 * sizeof(f32x4), "staging area");
+    f32x4* T = reinterpret_cast<f32x4*>(&sa[0][0][0]);
+    auto tix = [&](int r, int c) { return ((wave * MM_RT + r) * CT + c) * 64 + lane; };
+    if (threadIdx.x >= 256) {
+#pragma unroll
+      for (int r = 0; r < MM_RT; ++r)
+#pragma unroll
+        for (int c = 0; c < CT; ++c) T[tix(r, c)] = acc[r][c];
+    }
+    __syncthreads();
+    if (threadIdx.x >= 256) return;
+#pragma unroll
+    for (int r = 0; r < MM_RT; ++r)
+#pragma unroll
+      for (int c = 0; c < CT; ++c) acc[r][c] += T[tix(r, c)];
+  }
 
   float* out = g.part + (size_t)m.sp * g.R * g.N;
 #pragma unroll
@@ -203,13 +222,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
 }
 
+// Up to 64 rows the workgroups have 8 waves (the split's inputs in two
+// halves), so half as many splits keep the same waves in flight with half the
+// partial sums.
+static bool mm_halves(int R) { return R <= 64; }
+
 int gemm_mm_splits(int K, int N, int R) {
   const int KB = K / 64;
   const int wgs = ((R + 63) / 64) * (N / (64 * mm_ct(R)));
-  int want = (512 + wgs - 1) / wgs;          // about two workgroups per CU
+  const int per_cu = mm_halves(R) ? 256 : 512;   // about two workgroups (of 4 or 8 waves) per CU
+  int want = (per_cu + wgs - 1) / wgs;
   want = std::min(want, std::max(KB / 4, 1));  // at least 4 blocks per split
   int s = std::max(want, 1);
-  while (KB % s) --s;
+  while (s > 1 && (KB % s || (mm_halves(R) && (KB / s) % 2))) --s;
   return s;
 }
 
@@ -233,19 +258,23 @@ void launch_gemm_mm(hipStream_t st, const uint16_t* af, int R, const WMat& W, in
   g.splits = splits;
   g.kbs = g.KB / splits;
   const bool wide = mm_ct(R) == 4;
+  const bool halves = !wide && mm_halves(R) && g.kbs % 2 == 0;
   const dim3 grid(mm_grid(R, N / (wide ? 256 : 64), splits));
   switch (W.fmt) {
     case WF_NVFP4:
-      if (wide) k_gemm_mm<4, 2, WF_NVFP4><<<grid, 256, 0, st>>>(g);
-      else k_gemm_mm<1, 4, WF_NVFP4><<<grid, 256, 0, st>>>(g);
+      if (wide) k_gemm_mm<4, 2, WF_NVFP4, 1><<<grid, 256, 0, st>>>(g);
+      else if (halves) k_gemm_mm<1, 4, WF_NVFP4, 2><<<grid, 512, 0, st>>>(g);
+      else k_gemm_mm<1, 4, WF_NVFP4, 1><<<grid, 256, 0, st>>>(g);
       break;
     case WF_BF16:
-      if (wide) k_gemm_mm<4, 2, WF_BF16><<<grid, 256, 0, st>>>(g);
-      else k_gemm_mm<1, 4, WF_BF16><<<grid, 256, 0, st>>>(g);
+      if (wide) k_gemm_mm<4, 2, WF_BF16, 1><<<grid, 256, 0, st>>>(g);
+      else if (halves) k_gemm_mm<1, 4, WF_BF16, 2><<<grid, 512, 0, st>>>(g);
+      else k_gemm_mm<1, 4, WF_BF16, 1><<<grid, 256, 0, st>>>(g);
       break;
     default:
-      if (wide) k_gemm_mm<4, 2, WF_FP8><<<grid, 256, 0, st>>>(g);
-      else k_gemm_mm<1, 4, WF_FP8><<<grid, 256, 0, st>>>(g);
+      if (wide) k_gemm_mm<4, 2, WF_FP8, 1><<<grid, 256, 0, st>>>(g);
+      else if (halves) k_gemm_mm<1, 4, WF_FP8, 2><<<grid, 512, 0, st>>>(g);
+      else k_gemm_mm<1, 4, WF_FP8, 1><<<grid, 256, 0, st>>>(g);
   }
 }
 
@@ -346,7 +375,7 @@ void launch_proj(hipStream_t st, const uint16_t* af, int R, const WMat& W, const
   g.kbs = g.KB;
   const bool wide = mm_ct(R) == 4;
   // at most one row block: the input range in two halves inside the workgroup
-  const bool halves = !wide && R <= 64 && g.KB % 2 == 0;
+  const bool halves = !wide && mm_halves(R) && g.KB % 2 == 0;
   const dim3 grid(mm_grid(R, W.N / (wide ? 256 : 64), 1));
   switch (W.fmt) {
     case WF_NVFP4:
