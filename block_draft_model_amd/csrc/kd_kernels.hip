@@ -17,6 +17,34 @@
 
 namespace kd {
 
+// v[0..8) += the 8 floats at p + s * stride for s = 0 .. n-1, added in that
+// order (so the sum is the same as a plain loop's), with the loads of up to
+// 16 partials issued before the first add: the reductions of split-K
+// partial sums are bound by load latency, not by the adds.
+__device__ __forceinline__ void add_splits8(const float* p, size_t stride, int n, float (&v)[8]) {
+  constexpr int MAXS = 16;
+  for (int s0 = 0; s0 < n; s0 += MAXS) {
+    const int m = min(MAXS, n - s0);
+    f32x4 a[MAXS][2];
+#pragma unroll
+    for (int k = 0; k < MAXS; ++k) {
+      const float* q = p + (size_t)(s0 + min(k, m - 1)) * stride;
+      a[k][0] = *reinterpret_cast<const f32x4*>(q);
+      a[k][1] = *reinterpret_cast<const f32x4*>(q + 4);
+    }
+#pragma unroll
+    for (int k = 0; k < MAXS; ++k) {
+      if (k < m) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[i] += a[k][0][i];
+          v[4 + i] += a[k][1][i];
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Projection: part[split][r][n] = sum over the split's inputs of
 // X[r][k] * W[n_off*16 + n][k], W in one of the body formats (WF).
@@ -166,11 +194,7 @@ __global__ __launch_bounds__(320) void k_post_fuse(const float* part, int splits
   float v[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    const float* p = part + ((size_t)s * B + b) * H + c0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] += p[i];
-  }
+  add_splits8(part + (size_t)b * H + c0, (size_t)B * H, splits, v);
 #pragma unroll
   for (int i = 0; i < 8; ++i) f[(size_t)b * H + c0 + i] = v[i];
   store_afrag8(af_fc, KT, b, c0, v);
@@ -197,11 +221,7 @@ __global__ __launch_bounds__(32) void k_silu_rank(const float* part, int splits,
   float v[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    const float* p = part + ((size_t)s * rows + r) * RK + c0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] += p[i];
-  }
+  add_splits8(part + (size_t)r * RK + c0, (size_t)rows * RK, splits, v);
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] = silu(v[i]);
   store_afrag8(af, RK / 32, r, c0, v);
@@ -245,19 +265,11 @@ __global__ __launch_bounds__(320) void k_rowbuild(const float* part_fc, int spli
   float v[4][8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[0][i] = 0.f;
-  for (int s = 0; s < splits_fc; ++s) {
-    const float* p = part_fc + ((size_t)s * B + b) * H + c0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[0][i] += p[i];
-  }
+  add_splits8(part_fc + (size_t)b * H + c0, (size_t)B * H, splits_fc, v[0]);
   for (int j = 1; j < 4; ++j) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[j][i] = 0.f;
-    for (int s = 0; s < splits_u; ++s) {
-      const float* p = part_u + ((size_t)s * 3 * B + b * 3 + j - 1) * H + c0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[j][i] += p[i];
-    }
+    add_splits8(part_u + (size_t)(b * 3 + j - 1) * H + c0, (size_t)3 * B * H, splits_u, v[j]);
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[j][i] = (mask[c0 + i] + f[(size_t)b * H + c0 + i]) + v[j][i];
   }
@@ -291,11 +303,7 @@ __global__ __launch_bounds__(320) void k_spine_add_norm(const float* part, int s
       float add[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) add[i] = 0.f;
-      for (int s = 0; s < splits; ++s) {
-        const float* p = part + ((size_t)s * 3 * B + b * 3 + j - 1) * H + c0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) add[i] += p[i];
-      }
+      add_splits8(part + (size_t)(b * 3 + j - 1) * H + c0, (size_t)3 * B * H, splits, add);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         v[j][i] += add[i];
@@ -983,11 +991,7 @@ __global__ __launch_bounds__(320) void k_resid_norm(float* x, const float* part,
   float v[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    const float* p = part + ((size_t)s * R + r) * H + c0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] += p[i];
-  }
+  add_splits8(part + (size_t)r * H + c0, (size_t)R * H, splits, v);
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -1023,14 +1027,9 @@ __global__ __launch_bounds__(256) void k_swiglu(const float* part, int splits, i
 #pragma unroll
     for (int i = 0; i < 8; ++i) gt[i] = up[i] = 0.f;
     // columns c0..c0+7 of gate and of up sit in one 16-row tile (gu_position)
-    for (int s = 0; s < splits; ++s) {
-      const float* p = part + ((size_t)s * R + r) * GU + gu_position(c0);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        gt[i] += p[i];
-        up[i] += p[8 + i];
-      }
-    }
+    const float* p = part + (size_t)r * GU + gu_position(c0);
+    add_splits8(p, (size_t)R * GU, splits, gt);
+    add_splits8(p + 8, (size_t)R * GU, splits, up);
     float hv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) hv[i] = silu(gt[i]) * up[i];
@@ -1197,11 +1196,7 @@ __global__ __launch_bounds__(320) void k_ingest_post_fuse(const float* part, int
   float v[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    const float* p = part + ((size_t)s * rows + r) * H + c0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] += p[i];
-  }
+  add_splits8(part + (size_t)r * H + c0, (size_t)rows * H, splits, v);
   store_afrag8(af_fc, KT, r, c0, v);
   const u32x4 e = *reinterpret_cast<const u32x4*>(table_row(table, zrow, next_ids[r], V, H) + c0);
   store_afrag8_bf16(af_fc, KT, r, H + c0, e);
@@ -1218,11 +1213,7 @@ __global__ __launch_bounds__(320) void k_ingest_c(const float* part, int splits,
   float v[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    const float* p = part + ((size_t)s * rows + r) * H + c0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] += p[i];
-  }
+  add_splits8(part + (size_t)r * H + c0, (size_t)rows * H, splits, v);
 #pragma unroll
   for (int i = 0; i < 8; ++i) c[(size_t)r * H + c0 + i] = v[i];
 }
