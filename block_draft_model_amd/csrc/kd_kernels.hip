@@ -231,92 +231,81 @@ void launch_silu_rank(hipStream_t st, const float* part, int splits, int rows, u
   k_silu_rank<<<rows, 32, 0, st>>>(part, splits, rows, af);
 }
 
-// Writes RMSNorm(x_j; gain) of the 4 rows of stream b to afrag (320 threads,
-// 8 columns each; the rows are in v[4][8]).
-__device__ __forceinline__ void norm4_store(float (&v)[4][8], int b, const float* gain, float eps,
-                                            uint16_t* af, float* red) {
+// RMSNorm of one row (8 values per thread, 320 threads) with the gain, into
+// afrag row `row`.
+__device__ __forceinline__ void norm_row_store(const float (&v)[8], int row, const float* gain, float eps,
+                                               uint16_t* af, float* red) {
   const int c0 = threadIdx.x * 8;
-  float inv[4];
+  float ss = 0.f;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float ss = 0.f;
+  for (int i = 0; i < 8; ++i) ss += v[i] * v[i];
+  ss = block_sum<5>(ss, red);
+  const float inv = 1.0f / sqrtf(ss / H + eps);
+  float o[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ss += v[j][i] * v[j][i];
-    ss = block_sum<5>(ss, red + 8 * j);
-    inv[j] = 1.0f / sqrtf(ss / H + eps);
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float o[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = gain[c0 + i] * v[j][i] * inv[j];
-    store_afrag8(af, H / 32, b * 4 + j, c0, o);
-  }
+  for (int i = 0; i < 8; ++i) o[i] = gain[c0 + i] * v[i] * inv;
+  store_afrag8(af, H / 32, row, c0, o);
 }
 
 // Block rows: x0 = fc partials; x_j = mask + f + U_p partials (j = 1..3);
-// then the first layer's attention RMSNorm into afrag.
-__global__ __launch_bounds__(320) void k_rowbuild(const float* part_fc, int splits_fc,
-                                                  const float* part_u, int splits_u, int B,
-                                                  const float* f, const float* mask, float* x,
-                                                  const float* gain, float eps, uint16_t* af) {
-  __shared__ float red[64];
-  const int b = blockIdx.x, c0 = threadIdx.x * 8;
-  float v[4][8];
+// then the first layer's attention RMSNorm into afrag. One workgroup per
+// block row (stream b = row / 4, j = row % 4).
+__global__ __launch_bounds__(320) void k_rowbuild(const float* __restrict__ part_fc, int splits_fc,
+                                                  const float* __restrict__ part_u, int splits_u, int B,
+                                                  const float* __restrict__ f, const float* __restrict__ mask,
+                                                  float* __restrict__ x, const float* __restrict__ gain,
+                                                  float eps, uint16_t* __restrict__ af) {
+  __shared__ float red[8];
+  const int row = blockIdx.x, b = row >> 2, j = row & 3, c0 = threadIdx.x * 8;
+  float v[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[0][i] = 0.f;
-  add_splits8(part_fc + (size_t)b * H + c0, (size_t)B * H, splits_fc, v[0]);
-  for (int j = 1; j < 4; ++j) {
+  for (int i = 0; i < 8; ++i) v[i] = 0.f;
+  if (j == 0) {
+    add_splits8(part_fc + (size_t)b * H + c0, (size_t)B * H, splits_fc, v);
+  } else {
+    add_splits8(part_u + (size_t)(b * 3 + j - 1) * H + c0, (size_t)3 * B * H, splits_u, v);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[j][i] = 0.f;
-    add_splits8(part_u + (size_t)(b * 3 + j - 1) * H + c0, (size_t)3 * B * H, splits_u, v[j]);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[j][i] = (mask[c0 + i] + f[(size_t)b * H + c0 + i]) + v[j][i];
+    for (int i = 0; i < 8; ++i) v[i] = (mask[c0 + i] + f[(size_t)b * H + c0 + i]) + v[i];
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[(size_t)(b * 4 + j) * H + c0 + i] = v[j][i];
-  norm4_store(v, b, gain, eps, af, red);
+  for (int i = 0; i < 8; ++i) x[(size_t)row * H + c0 + i] = v[i];
+  norm_row_store(v, row, gain, eps, af, red);
 }
 
 void launch_rowbuild(hipStream_t st, const Work& w, const DevWeights& d, int B, int splits_fc,
                      int splits_u, const float* gain, float eps) {
   const size_t half = w.part_elems / 2;
-  k_rowbuild<<<B, 320, 0, st>>>(w.part, splits_fc, w.part + half, splits_u, B, w.f, d.mask, w.x,
-                                gain, eps, w.af_x);
+  k_rowbuild<<<BLK * B, 320, 0, st>>>(w.part, splits_fc, w.part + half, splits_u, B, w.f, d.mask, w.x,
+                                      gain, eps, w.af_x);
 }
 
 // Spine add (rows 1..3 of each stream) and the layer's attention RMSNorm.
-__global__ __launch_bounds__(320) void k_spine_add_norm(const float* part, int splits, int B,
-                                                        float* x, const float* gain, float eps,
-                                                        uint16_t* af) {
-  __shared__ float red[64];
-  const int b = blockIdx.x, c0 = threadIdx.x * 8;
-  float v[4][8];
+__global__ __launch_bounds__(320) void k_spine_add_norm(const float* __restrict__ part, int splits, int B,
+                                                        float* __restrict__ x, const float* __restrict__ gain,
+                                                        float eps, uint16_t* __restrict__ af) {
+  __shared__ float red[8];
+  const int row = blockIdx.x, b = row >> 2, j = row & 3, c0 = threadIdx.x * 8;
+  float* xr = x + (size_t)row * H + c0;
+  float v[8];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float* xr = x + (size_t)(b * 4 + j) * H + c0;
+  for (int i = 0; i < 8; ++i) v[i] = xr[i];
+  if (j > 0) {
+    float add[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[j][i] = xr[i];
-    if (j > 0) {
-      float add[8];
+    for (int i = 0; i < 8; ++i) add[i] = 0.f;
+    add_splits8(part + (size_t)(b * 3 + j - 1) * H + c0, (size_t)3 * B * H, splits, add);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) add[i] = 0.f;
-      add_splits8(part + (size_t)(b * 3 + j - 1) * H + c0, (size_t)3 * B * H, splits, add);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        v[j][i] += add[i];
-        xr[i] = v[j][i];
-      }
+    for (int i = 0; i < 8; ++i) {
+      v[i] += add[i];
+      xr[i] = v[i];
     }
   }
-  norm4_store(v, b, gain, eps, af, red);
+  norm_row_store(v, row, gain, eps, af, red);
 }
 
 void launch_spine_add_norm(hipStream_t st, const Work& w, int B, int splits, const float* gain,
                            float eps) {
-  k_spine_add_norm<<<B, 320, 0, st>>>(w.part, splits, B, w.x, gain, eps, w.af_x);
+  k_spine_add_norm<<<BLK * B, 320, 0, st>>>(w.part, splits, B, w.x, gain, eps, w.af_x);
 }
 
 // q|k|v partials -> q, k (RoPE, rotate-half) and v for every block row.
