@@ -296,7 +296,7 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(2))) v
   constexpr int COLS = 16 * CT * MM_WAVES;
   constexpr int TP = COLS + 4;                        // LDS row pitch of the staged tile (floats)
   constexpr int SA_BYTES = KS * 2 * MM_RT * 2 * 64 * 16;
-  constexpr int T_BYTES = 64 * TP * 4;
+  constexpr int T_BYTES = KS * 64 * TP * 4;           // one staged tile per group
   __shared__ __attribute__((aligned(16))) unsigned char lds[SA_BYTES > T_BYTES ? SA_BYTES : T_BYTES];
   auto sa = reinterpret_cast<u32x4(*)[MM_RT * 2][64]>(lds);
   float* T = reinterpret_cast<float*>(lds);
@@ -304,27 +304,36 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(2))) v
   const MmMap m = mm_map(RB, CB, 1);
   if (!m.ok) return;
   const int lane = threadIdx.x & 63, wave = (threadIdx.x >> 6) & (MM_WAVES - 1);
+  const int grp = threadIdx.x >> 8;
   f32x4 acc[MM_RT][CT];
   mm_accumulate<CT, D, WF, KS>(g, m.rb, m.cb, 0, acc, sa);   // ends at a barrier: LDS is free
   auto tix = [&](int r, int c, int q) { return (r * 16 + 4 * (lane >> 4) + q) * TP + (wave * CT + c) * 16 + (lane & 15); };
-  if (KS == 1 || threadIdx.x >= 256) {
+  // group q > 0 stages its sums at T + q * 64 * TP; group 0 adds them in group
+  // order and stages the total at T
+  if (KS == 1 || grp > 0) {
+    float* Tg = T + (size_t)grp * 64 * TP;
 #pragma unroll
     for (int r = 0; r < MM_RT; ++r)
 #pragma unroll
       for (int c = 0; c < CT; ++c)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) T[tix(r, c, q)] = acc[r][c][q];
+        for (int q = 0; q < 4; ++q) Tg[tix(r, c, q)] = acc[r][c][q];
   }
   __syncthreads();
-  if (KS == 2 && threadIdx.x < 256) {
+  if (KS > 1 && grp == 0) {
 #pragma unroll
     for (int r = 0; r < MM_RT; ++r)
 #pragma unroll
       for (int c = 0; c < CT; ++c)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) T[tix(r, c, q)] = acc[r][c][q] + T[tix(r, c, q)];
+        for (int q = 0; q < 4; ++q) {
+          float v = acc[r][c][q];
+#pragma unroll
+          for (int k = 1; k < KS; ++k) v += T[k * 64 * TP + tix(r, c, q)];
+          T[tix(r, c, q)] = v;
+        }
   }
-  if (KS == 2) __syncthreads();
+  if (KS > 1) __syncthreads();
   // items: (row, 16-column tile)
   constexpr int NT = COLS / 16;
   for (int it = threadIdx.x; it < 64 * NT; it += 256 * KS) {
