@@ -18,30 +18,38 @@
 namespace kd {
 
 // v[0..8) += the 8 floats at p + s * stride for s = 0 .. n-1, added in that
-// order (so the sum is the same as a plain loop's), with the loads of up to
-// 16 partials issued before the first add: the reductions of split-K
-// partial sums are bound by load latency, not by the adds.
+// order (so the sum is the same as a plain loop's), the loads of up to 8
+// partials issued before the first of them is added: the reductions of
+// split-K partial sums are bound by load latency, not by the adds.
+template <int N>
+__device__ __forceinline__ void add_splits8_n(const float* p, size_t stride, float (&v)[8]) {
+  f32x4 a[N][2];
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    a[k][0] = *reinterpret_cast<const f32x4*>(p + (size_t)k * stride);
+    a[k][1] = *reinterpret_cast<const f32x4*>(p + (size_t)k * stride + 4);
+  }
+#pragma unroll
+  for (int k = 0; k < N; ++k)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] += a[k][0][i];
+      v[4 + i] += a[k][1][i];
+    }
+}
 __device__ __forceinline__ void add_splits8(const float* p, size_t stride, int n, float (&v)[8]) {
-  constexpr int MAXS = 16;
-  for (int s0 = 0; s0 < n; s0 += MAXS) {
-    const int m = min(MAXS, n - s0);
-    f32x4 a[MAXS][2];
-#pragma unroll
-    for (int k = 0; k < MAXS; ++k) {
-      const float* q = p + (size_t)(s0 + min(k, m - 1)) * stride;
-      a[k][0] = *reinterpret_cast<const f32x4*>(q);
-      a[k][1] = *reinterpret_cast<const f32x4*>(q + 4);
-    }
-#pragma unroll
-    for (int k = 0; k < MAXS; ++k) {
-      if (k < m) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[i] += a[k][0][i];
-          v[4 + i] += a[k][1][i];
-        }
-      }
-    }
+  int s0 = 0;
+  for (; n - s0 >= 8; s0 += 8) add_splits8_n<8>(p + (size_t)s0 * stride, stride, v);
+  const float* q = p + (size_t)s0 * stride;
+  switch (n - s0) {
+    case 1: add_splits8_n<1>(q, stride, v); break;
+    case 2: add_splits8_n<2>(q, stride, v); break;
+    case 3: add_splits8_n<3>(q, stride, v); break;
+    case 4: add_splits8_n<4>(q, stride, v); break;
+    case 5: add_splits8_n<5>(q, stride, v); break;
+    case 6: add_splits8_n<6>(q, stride, v); break;
+    case 7: add_splits8_n<7>(q, stride, v); break;
+    default: break;
   }
 }
 
