@@ -977,140 +977,9 @@ struct StreamLensT {
   __device__ __forceinline__ int first_unit(int b, int h) const {
     return pick4(b, 0, o1, o2, o3) + h * chunks(b);
   }
-  // Workgroup w of G takes the units [start(w), start(w + 1)); owner(u) is
-  // the workgroup whose range holds unit u.
-  __device__ __forceinline__ int start(int w, int G) const { return (w * total) / G; }
-  __device__ __forceinline__ int owner(int u, int G) const { return ((u + 1) * G - 1) / total; }
-  // Segments the ranges cut the units [u0, u0 + nc) into: with at least as
-  // many units as workgroups every range is non-empty; with fewer, a range
-  // holds at most one unit.
-  __device__ __forceinline__ int segments(int u0, int nc, int G) const {
-    return total < G ? nc : owner(u0 + nc - 1, G) - owner(u0, G) + 1;
-  }
 };
 // Attention units are chunks of ATT_CH = 128 keys.
 using StreamLens = StreamLensT<ATT_CH>;
-
-// The block's own part of the attention of one (stream, head) for thread
-// (j, d): scores s[j][i] = q_j . k_i of block rows i <= j (log2 units, -inf
-// for i > j) and the values v_i[d]. It needs no context: the workgroup that
-// merges the pair loads the block rows (BlockRows::load) before its own
-// chunks and finishes the part (attn_block) after them.
-struct BlockPart {
-  float s0, s1, s2, s3;
-  float v0, v1, v2, v3;
-};
-struct BlockRows {
-  float q, k0, k1, k2, k3;     // wave w: query row w/2 and the 4 key rows, dim 64 (w%2) + lane
-  float v0, v1, v2, v3;        // thread (j, d): the 4 value rows at dim d
-  __device__ __forceinline__ void load(Args& a, int l, int b, int h) {
-    auto& s = a.s;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int dd = threadIdx.x & 127;
-    const int jw = wave >> 1, dw = 64 * (wave & 1) + lane;
-    const size_t hb = (size_t)b * 4 * H + h * DH;
-    q = s.q[l][hb + jw * H + dw];
-    k0 = s.k[l][hb + 0 * H + dw];
-    k1 = s.k[l][hb + 1 * H + dw];
-    k2 = s.k[l][hb + 2 * H + dw];
-    k3 = s.k[l][hb + 3 * H + dw];
-    v0 = s.v[l][hb + 0 * H + dd];
-    v1 = s.v[l][hb + 1 * H + dd];
-    v2 = s.v[l][hb + 2 * H + dd];
-    v3 = s.v[l][hb + 3 * H + dd];
-  }
-};
-__device__ __attribute__((noinline, not_tail_called)) BlockPart attn_block(BlockRows br, lds_f red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const float qs = 0.08838834764831845f * 1.4426950408889634f;  // 1/sqrt(128) * log2(e)
-  const int j = threadIdx.x >> 7;
-  const float kb4[4] = {br.k0, br.k1, br.k2, br.k3};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float p = wave_sum(br.q * kb4[i]);
-    if (lane == 0) red[wave * 4 + i] = p;
-  }
-  lds_sync();
-  float sb[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    sb[i] = i <= j ? (red[(2 * j) * 4 + i] + red[(2 * j + 1) * 4 + i]) * qs : -__builtin_inff();
-  lds_sync();
-  return BlockPart{sb[0], sb[1], sb[2], sb[3], br.v0, br.v1, br.v2, br.v3};
-}
-
-// Merge of the partials of one (stream, head) with the block's part; thread
-// (j, d). Each of the pair's chunks stored its own partial at its slot.
-__device__ __attribute__((noinline, not_tail_called)) void attn_merge(Args& a_, int l_, int b_, int h_, int n_,
-                                                     BlockPart bp) {
-  const auto l = uni(l_);
-  const auto b = uni(b_);
-  const auto h = uni(h_);
-  const auto n = uni(n_);
-  Args& a = uni(a_);
-  auto& s = a.s;
-  const int nch = a.nch;
-  // every chunk of the pair stored its own partial: they are merged in chunk
-  // order, which depends only on the stream's length, never on the batch
-  const int nc = (n + ATT_CH - 1) / ATT_CH;
-  const int nseg = nc;
-  auto seg_chunk = [&](int k) { return k; };
-  const int j = threadIdx.x >> 7, dd = threadIdx.x & 127;
-  const int lane = threadIdx.x & 63;
-  constexpr int MAXS = 16;
-  float pm[MAXS], pl[MAXS], po[MAXS];
-  const size_t base = (size_t)(b * NH + h) * nch;
-  auto am = s.am[l] + base * 4 + j;
-  auto al = s.al[l] + base * 4 + j;
-  auto ao = s.ao[l] + (base * 4 + j) * DH + dd;
-  // lane k < nseg loads segment k's max and sum of row j (every lane of a
-  // wave has the same row), each thread its segments' outputs: one load
-  // instruction per segment instead of three
-  const int klast = max(nseg - 1, 0);
-  const int ck = seg_chunk(min(lane, klast));
-  const float m_lane = am[ck * 4], l_lane = al[ck * 4];
-#pragma unroll
-  for (int k = 0; k < MAXS; ++k) po[k] = k < nseg ? ao[(size_t)seg_chunk(k) * 4 * DH] : 0.f;
-#pragma unroll
-  for (int k = 0; k < MAXS; ++k) {
-    pm[k] = k < nseg ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_lane), k))
-                     : -__builtin_inff();
-    pl[k] = k < nseg ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l_lane), k)) : 0.f;
-  }
-  for (int k = MAXS; k < nseg; ++k) {  // more segments than registers: fold the rest in
-    const int cc = seg_chunk(k);
-    const float m1 = am[cc * 4];
-    if (m1 == -__builtin_inff()) continue;
-    const float mn = fmaxf(pm[0], m1);
-    const float f0 = pm[0] == -__builtin_inff() ? 0.f : exp2f(pm[0] - mn), f1 = exp2f(m1 - mn);
-    pl[0] = pl[0] * f0 + al[cc * 4] * f1;
-    po[0] = po[0] * f0 + ao[(size_t)cc * 4 * DH] * f1;
-    pm[0] = mn;
-  }
-  const float sb[4] = {bp.s0, bp.s1, bp.s2, bp.s3}, vv[4] = {bp.v0, bp.v1, bp.v2, bp.v3};
-  float M = -__builtin_inff();
-#pragma unroll
-  for (int k = 0; k < MAXS; ++k) M = fmaxf(M, pm[k]);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) M = fmaxf(M, sb[i]);
-  float Ls = 0.f, O = 0.f;
-#pragma unroll
-  for (int k = 0; k < MAXS; ++k) {
-    if (pm[k] != -__builtin_inff()) {
-      const float f = exp2f(pm[k] - M);
-      Ls += pl[k] * f;
-      O += po[k] * f;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    if (i <= j) {
-      const float f = exp2f(sb[i] - M);
-      Ls += f;
-      O += f * vv[i];
-    }
-  st_wt_h(&s.o[l][(b * 4 + j) * H + h * DH + dd], O / Ls);
-}
 
 // Reads the lane's 4 key and 4 value blocks (at kva, 1 KB apart) and waits
 // for the reads. The copies that filled them must have landed.
@@ -1146,169 +1015,11 @@ __device__ __forceinline__ void att_read_p(unsigned addr, f32x4 (&r)[4]) {
       : "v"(addr)
       : "memory");
 }
-// Writes a wave's max at ma and its sum at ma + 128 (kept from the compiler,
-// which would make the writes wait for the global-to-LDS copies in flight).
-__device__ __forceinline__ void att_write_ml(unsigned ma, float m, float l) {
-  asm volatile("ds_write_b32 %0, %1\n\tds_write_b32 %0, %2 offset:128" : : "v"(ma), "v"(m), "v"(l) : "memory");
-}
 // A write-through store that is exactly one vector memory instruction, so the
 // attention loop can count it in its waits.
 __device__ __forceinline__ void att_store(gptr<float> p, float v) {
   asm volatile("global_store_dword %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
 }
-// Eight waves' max (at ma + 16 w), sum (at ma + 128 + 16 w) and output (at
-// oa + 2048 w).
-__device__ __forceinline__ void att_read_mlo(unsigned ma, unsigned oa, float (&m)[8], float (&ls)[8],
-                                             float (&o)[8]) {
-  asm volatile(
-      "ds_read_b32 %0, %24\n\t"
-      "ds_read_b32 %1, %24 offset:16\n\t"
-      "ds_read_b32 %2, %24 offset:32\n\t"
-      "ds_read_b32 %3, %24 offset:48\n\t"
-      "ds_read_b32 %4, %24 offset:64\n\t"
-      "ds_read_b32 %5, %24 offset:80\n\t"
-      "ds_read_b32 %6, %24 offset:96\n\t"
-      "ds_read_b32 %7, %24 offset:112\n\t"
-      "ds_read_b32 %8, %24 offset:128\n\t"
-      "ds_read_b32 %9, %24 offset:144\n\t"
-      "ds_read_b32 %10, %24 offset:160\n\t"
-      "ds_read_b32 %11, %24 offset:176\n\t"
-      "ds_read_b32 %12, %24 offset:192\n\t"
-      "ds_read_b32 %13, %24 offset:208\n\t"
-      "ds_read_b32 %14, %24 offset:224\n\t"
-      "ds_read_b32 %15, %24 offset:240\n\t"
-      "ds_read_b32 %16, %25\n\t"
-      "ds_read_b32 %17, %25 offset:2048\n\t"
-      "ds_read_b32 %18, %25 offset:4096\n\t"
-      "ds_read_b32 %19, %25 offset:6144\n\t"
-      "ds_read_b32 %20, %25 offset:8192\n\t"
-      "ds_read_b32 %21, %25 offset:10240\n\t"
-      "ds_read_b32 %22, %25 offset:12288\n\t"
-      "ds_read_b32 %23, %25 offset:14336\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(m[0]), "=&v"(m[1]), "=&v"(m[2]), "=&v"(m[3]), "=&v"(m[4]), "=&v"(m[5]), "=&v"(m[6]),
-        "=&v"(m[7]), "=&v"(ls[0]), "=&v"(ls[1]), "=&v"(ls[2]), "=&v"(ls[3]), "=&v"(ls[4]),
-        "=&v"(ls[5]), "=&v"(ls[6]), "=&v"(ls[7]), "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]),
-        "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
-      : "v"(ma), "v"(oa)
-      : "memory");
-}
-
-// Attention over the round's units: a unit is one chunk of ATT_CH = 128
-// context keys of one (stream, head), and workgroup w takes the contiguous
-// unit range [start(w), start(w + 1)) in (stream, head, chunk) order, so that
-// its consecutive units are chunks of one (stream, head) pair. Wave v takes
-// keys 16v .. 16v+15 of every unit and keeps an online softmax over them:
-//   scores  S^T[key][j] = K Q^T on the matrix cores (16x16x32 bf16): K rows as
-//           the A operand (lane: key lane%16, dims 32kb + 8(lane/16)), the
-//           queries split into bf16 hi + lo as B (column j < 4 of 4 block rows);
-//   softmax running max and sum per row j, the output rescaled when the max
-//           grows;
-//   P V     on the vector units from 16-byte value rows (8 dims of 4 keys per
-//           lane), probabilities passed through the wave's own LDS area.
-// Keys, values and queries are copied into LDS one unit ahead (global-to-LDS
-// copies hold no registers; the waits on them are explicit). Where a pair's
-// chunks end, or the range does, the 8 waves' states are merged into one
-// partial per segment, stored at the slot of the segment's first chunk; the
-// pair's counter then counts the segment, and a designated workgroup per
-// (stream, head) merges its segments with the block's own keys.
-// The chunk's partial: thread (j, d) merges the 8 waves' (max, sum, output)
-// of row j, dim d that the caller left in LDS (max at s_m + 16 w + j, sum at
-// s_m + 32 + ..., output at s_o + (4 w + j) DH + d) and stores them in the
-// chunk's slot: three store instructions per wave, counted by the caller.
-__device__ __forceinline__ void chunk_partial_store(Args& a, int l, int b, int h, int seg_c0, lds_f s_m,
-                                                    lds_f s_o) {
-  auto& s = a.s;
-  const int lane = threadIdx.x & 63;
-  const int nch = a.nch;
-  // thread (j, d): merge of the 8 waves, stored as the segment's partial
-  const int j = threadIdx.x >> 7, dd = threadIdx.x & 127;
-  float mw[8], lw[8], ow[8];
-  att_read_mlo((unsigned)(uintptr_t)(s_m + j), (unsigned)(uintptr_t)(s_o + j * DH + dd), mw, lw, ow);
-  float M = -__builtin_inff();
-#pragma unroll
-  for (int w = 0; w < 8; ++w) M = fmaxf(M, mw[w]);
-  float Ls = 0.f, O = 0.f;
-#pragma unroll
-  for (int w = 0; w < 8; ++w) {
-    if (mw[w] != -__builtin_inff()) {
-      const float f = exp2f(mw[w] - M);
-      Ls += lw[w] * f;
-      O += ow[w] * f;
-    }
-  }
-  // three store instructions per wave: the output by every lane, the max
-  // and sum of row j by lane 0 (waves 2j and 2j + 1 store the same values)
-  const size_t pb = ((size_t)(b * NH + h) * nch + seg_c0) * 4 + j;
-  att_store(s.ao[l] + pb * DH + dd, O);
-  if (lane == 0) {
-    att_store(s.am[l] + pb, M);
-    att_store(s.al[l] + pb, Ls);
-  }
-}
-
-// After a workgroup's chunks: its completion counters (one per (stream, head)
-// and layer, once every partial store is done); then the non-merging
-// workgroups warm the next phases' weights and the merging ones merge their
-// pair once its counter shows every segment stored.
-// per_chunk: each chunk's wave counted its chunk itself (the counter of a
-// pair then reaches its number of chunks); otherwise the workgroup counts its
-// segments here.
-__device__ __forceinline__ void attn_finish(Args& a, int l, const StreamLens& sl, int ub, int ue, BlockRows& br,
-                                            SyncState sy, bool sync, bool per_chunk = false) {
-  const int G = gridDim.x, wg = blockIdx.x;
-  auto& s = a.s;
-  const int nbh = a.B * NH, mi = wg;
-  const bool merges = wg < nbh;
-  // completion counters: one per (stream, head) and layer, counting the
-  // segments; taken once every partial store of the workgroup is done
-  __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0): stores acknowledged
-  __syncthreads();
-  if (threadIdx.x == 0 && !per_chunk) {
-    for (int u = ub; u < ue;) {
-      int b, c, h;
-      sl.unit(u, b, c, h);
-      (void)add_rlx(&s.att_cnt[((l * SB_MAX + b) * NH + h) * 32], 1u);
-      u += sl.chunks(b) - c;
-    }
-  }
-  trace_mark(a, sy, 5);
-  // The other workgroups warm the next phases' weights on the XCDs that will
-  // read them: the output projection (one tile per unit) and gate|up (three).
-  if (!merges && !sync) {
-    auto& L = a.d.layer[l];
-    warm(nbh, HT, [&](int u) { touch_tiles(L.wo, u, 1, 0, H / 64); });
-    warm(nbh, GU / 16 / 3, [&](int u) { touch_tiles(L.gu, 3 * u, 3, 0, H / 64); });
-    warm_done();
-  }
-  // Merge: one (stream, head) per workgroup, all in parallel, once its
-  // counter shows every segment stored. The merging workgroup resets the
-  // counter for the next round. Streams with an empty context attend to the
-  // block only.
-  if (merges) {
-    const int b = mi / NH, h = mi % NH, n = sl.vis(b);
-    const int u0 = n > 0 ? sl.first_unit(b, h) : 0;
-    const BlockPart bp = attn_block(br, (lds_f)g_att_small);
-    if (n > 0) {
-      if (threadIdx.x == 0) {
-        auto cnt = &s.att_cnt[((l * SB_MAX + b) * NH + h) * 32];
-        const unsigned need = per_chunk ? (unsigned)sl.chunks(b) : (unsigned)sl.segments(u0, sl.chunks(b), G);
-        const unsigned long long t0 = wall_clock64();
-        for (unsigned it = 1; ld_rlx(cnt) < need; ++it) {
-          if ((it & 63) == 0 && wall_clock64() - t0 > 20000000ull) {  // 0.2 s
-            __hip_atomic_store(&s.bar[18 * 32], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
-          }
-          __builtin_amdgcn_s_sleep(2);
-        }
-        __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      lds_sync();
-    }
-    attn_merge(a, l, b, h, n, bp);
-  }
-}
-
 // Merge of one (stream, head) pair by a single wave: the chunk partials in
 // chunk order (groups of 16, each group's maximum first), then the block's
 // own keys (causal within the block). Lane (j, r) = (lane / 16, lane % 16)
@@ -1810,16 +1521,18 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn(Args& a_, int
 }
 
 // Attention over the rotated 4-bit cache (the 4-bit KV article, "What we do"):
-// the same units, per-chunk partials, counters and merges as ph_attn. Per unit
-// wave w takes the chunk's keys 16 w .. 16 w + 15 straight into registers
-// (buffer loads: K codes, V codes, each key's fp16 scale and offset), one unit
-// ahead. Where the (stream, head) pair changes, waves 0..3 turn the block rows'
-// queries by the layer's rotation (signs, then an in-wave Walsh-Hadamard
-// transform) into LDS, and every wave takes them as the B operand (f16 hi +
-// lo). Scores = scale * (q_rot . codes) + offset * sum(q_rot), with the codes
-// as f16 subnormals on the matrix cores; P V on the matrix cores as well
-// (16x16x16, V codes as the A operand, p * scale as the B operand), the
-// offsets' share added per row.
+// the units, chunk partials, counters and last-arriving merges of ph_attn.
+// Wave w of workgroup g takes the units g + G (w + 8 i), each whole: the
+// chunk's 8 blocks of 16 keys in key order, straight into registers by buffer
+// loads (K codes, V codes, each key's fp16 scale and offset), one block
+// ahead of the one computed. Per unit the wave turns the block rows' queries
+// by the layer's rotation (signs, then an in-wave Walsh-Hadamard transform)
+// through its own LDS area and takes them as the B operand (f16 hi + lo). Per block: scores = scale * (q_rot . codes)
+// + offset * sum(q_rot), with the codes as f16 subnormals on the matrix
+// cores; an online softmax; P V on the matrix cores as well (16x16x16, V
+// codes as the A operand, p * scale as the B operand), the offsets' share
+// added per row. One wave makes each chunk's partial, so it does not depend
+// on the batch.
 __device__ __attribute__((noinline, not_tail_called)) void ph_attn_q4(Args& a_, int l_, SyncState sy,
                                                      bool sync) {
   const auto l = uni(l_);
@@ -1830,15 +1543,11 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn_q4(Args& a_, 
   const int wave_s = uni(wave);
   const int lr = lane & 15, lg = lane >> 4;
   const float qs = 0.08838834764831845f * 1.4426950408889634f;
-  lds_f s_o = (lds_f)g_att_small;      // [8][4][128] per-wave outputs
-  lds_f s_m = s_o + 8 * 4 * DH;        // [8][4] maxima, then [8][4] sums
-  lds_f s_q = (lds_f)&g_att_ring[0][0][0];   // [4][128] rotated queries, then [4] their sums
-  lds_f s_qs = s_q + 4 * DH;
+  lds_f s_q = (lds_f)g_att_small + wave_s * 528;   // the wave's rotated queries [4][128], then [4] their sums
 
   StreamLens sl;
   sl.load(a);  // an input: read before the arrival
   const int U = sl.total;
-  const int ub = U > 0 ? sl.start(wg, G) : 0, ue = U > 0 ? sl.start(wg + 1, G) : 0;
   const uint8_t* k_l = reinterpret_cast<const uint8_t*>(a.kv.k[l]);
   const uint8_t* v_l = reinterpret_cast<const uint8_t*>(a.kv.v[l]);
   const uint16_t* ks_l = a.kv.kso[l];
@@ -1849,21 +1558,30 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn_q4(Args& a_, 
   const uint32_t span = (uint32_t)((kv_cap - 1) * a.kv.sl + 1);   // rows of one (stream, head)
   auto q_l = s.q[l];
   const float* signs = a.d.kv_signs + l * DH;
+  const int nch = a.nch;
 
-  // Unit u's keys for this wave, straight into registers; keys past the
-  // visible rows are clamped to the last one and masked in the scores. The
-  // rows of one (stream, head) are read through buffer resources (32-bit
-  // offsets; the hardware returns 0 past the span, which the host checks
-  // fits 4 GiB).
+  if (sync) {
+    grid_arrive(a, sy);
+    grid_wait(a, sy);
+  }
+  trace_mark(a, sy, 2);
+
+  // One block's keys for this wave: key lr's K codes (dims 32 lg ..), keys
+  // 4 lg + t's V codes (dims 8 lr ..), key lr's (scale, offset) pairs.
   struct KvRegs {
-    u32x4 k;          // key lr's codes, dims 32 lg ..
-    uint32_t v[4];    // keys 4 lg + t, dims 8 lr ..
-    uint32_t ks, vs;  // key lr's (scale, offset) pairs
+    u32x4 k;
+    uint32_t v[4];
+    uint32_t ks, vs;
   };
-  auto load_unit = [&](int u, KvRegs& r) __attribute__((always_inline)) {
+  constexpr int NB = ATT_CH / 16;
+  for (int u = wg + G * wave_s; u < U; u += 8 * G) {
     int b, c, h;
     sl.unit(u, b, c, h);
     const int n = sl.vis(b), fp = sl.first(b);
+    // the rows of one (stream, head) are read through buffer resources
+    // (32-bit offsets; the hardware returns 0 past the span, which the host
+    // checks fits 4 GiB); keys past the visible rows are clamped to the last
+    // one and masked in the scores
     const size_t row0 = (size_t)(b * kv_ss + h * kv_sh);
     const __amdgpu_buffer_rsrc_t rk =
         __builtin_amdgcn_make_buffer_rsrc((void*)(k_l + row0 * 64), (short)0, span * 64, 0x00020000);
@@ -1879,62 +1597,36 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn_q4(Args& a_, 
       const int r_ = s0 + min(off, last);
       return (uint32_t)(r_ - (r_ >= kv_cap ? kv_cap : 0)) * kv_sl;
     };
-    const uint32_t rk0 = row_of(wave * 16 + lr);
-    r.k = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, rk0 * 64 + 16 * lg, 0, 0));
-    r.ks = __builtin_amdgcn_raw_buffer_load_b32(rks, rk0 * 4, 0, 0);
-    r.vs = __builtin_amdgcn_raw_buffer_load_b32(rvs, rk0 * 4, 0, 0);
+    auto load_blk = [&](int k, KvRegs& r) __attribute__((always_inline)) {
+      const uint32_t rk0 = row_of(16 * k + lr);
+      r.k = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, rk0 * 64 + 16 * lg, 0, 0));
+      r.ks = __builtin_amdgcn_raw_buffer_load_b32(rks, rk0 * 4, 0, 0);
+      r.vs = __builtin_amdgcn_raw_buffer_load_b32(rvs, rk0 * 4, 0, 0);
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-      r.v[t] = __builtin_amdgcn_raw_buffer_load_b32(rv, row_of(wave * 16 + 4 * lg + t) * 64 + 4 * lr, 0, 0);
-  };
-
-  const int nbh = a.B * NH;
-  const int mi = wg;
-  const bool merges = wg < nbh;
-  BlockRows br{};
-  if (merges && !sync) br.load(a, l, mi / NH, mi % NH);
-  if (sync) {
-    grid_arrive(a, sy);
-    if (is_poll_wave()) grid_poll(a, sy);
-  }
-  KvRegs cur, nxt;
-  const int ulast = max(ue - 1, ub);
-  if (ub < ue) load_unit(ub, cur);
-  if (sync) {
-    lds_sync();
-    if (merges) br.load(a, l, mi / NH, mi % NH);
-  }
-  trace_mark(a, sy, 2);
-
-  f16x8 qh[4], ql[4];
-  float qsum = 0.f;
-  int stores = 0;
-  for (int u = ub; u < ue; ++u) {
-    int b, c, h;
-    sl.unit(u, b, c, h);
-    const int n = sl.vis(b);
-    const bool new_pair = u == ub || c == 0;
-    // the next unit's keys go out before this one is computed
-    load_unit(min(u + 1, ulast), nxt);
-    (void)stores;
-    if (new_pair) {
-      // the previous chunk's readers of the shared LDS areas are done
-      if (u != ub) lds_sync();
-      if (wave_s < BLK) {
-        // wave j turns block row j's query: R q = H (s * q) / sqrt(128),
-        // scaled like the scores (1/sqrt(128) * log2(e))
-        const float* qp = q_l + (size_t)(b * BLK + wave_s) * H + h * DH;
+      for (int t = 0; t < 4; ++t)
+        r.v[t] = __builtin_amdgcn_raw_buffer_load_b32(rv, row_of(16 * k + 4 * lg + t) * 64 + 4 * lr, 0, 0);
+    };
+    KvRegs cur, nxt;
+    load_blk(0, cur);
+    f16x8 qh[4], ql[4];
+    float qsum;
+    {
+      // row j's query turned by R: R q = H (s * q) / sqrt(128), scaled like
+      // the scores (1/sqrt(128) * log2(e)); made again for every unit, so
+      // nothing of it stays live across a merge
+      const float f = 0.08838834764831845f * qs;
+#pragma unroll
+      for (int j = 0; j < BLK; ++j) {
+        const float* qp = q_l + (size_t)(b * BLK + j) * H + h * DH;
         float y0 = qp[lane] * signs[lane], y1 = qp[lane + 64] * signs[lane + 64];
         fwht128(y0, y1, lane);
-        const float f = 0.08838834764831845f * qs;
         y0 *= f;
         y1 *= f;
-        s_q[wave_s * DH + lane] = y0;
-        s_q[wave_s * DH + lane + 64] = y1;
+        s_q[j * DH + lane] = y0;
+        s_q[j * DH + lane + 64] = y1;
         const float t = wave_sum(y0 + y1);
-        if (lane == 0) s_qs[wave_s] = t;
+        if (lane == 0) s_q[BLK * DH + j] = t;
       }
-      lds_sync();
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -1944,110 +1636,136 @@ __device__ __attribute__((noinline, not_tail_called)) void ph_attn_q4(Args& a_, 
           qh[kb][e] = hh;
           ql[kb][e] = (_Float16)(v - (float)hh);
         }
-      qsum = lr < BLK ? s_qs[lr] : 0.f;
+      qsum = lr < BLK ? s_q[BLK * DH + lr] : 0.f;
     }
-    if (u == ub) trace_mark(a, sy, 3);
-    // the scale and offset pairs of keys 4 lg + e come from lanes 4 lg + e
-    uint32_t ks[4], vs[4];
+    float m_run = -__builtin_inff(), l_run = 0.f;
+    float o[8][4];   // lane (lr < 4, lg): row lr, dims 32 lg + 8 e + t at o[t][e]
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      ks[e] = __shfl(cur.ks, 4 * lg + e, 64);
-      vs[e] = __shfl(cur.vs, 4 * lg + e, 64);
-    }
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 8; ++t)
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const f16x8 kk = nib8_f16(cur.k[kb]);
-      acc = mfma_f16(kk, qh[kb], acc);
-      acc = mfma_f16(kk, ql[kb], acc);
-    }
-    // lane (lr, lg): acc[e] = q_rot[lr] . codes[key 4 lg + e] * 2^-24
-    float sc[4], mx = -__builtin_inff();
+      for (int e = 0; e < 4; ++e) o[t][e] = 0.f;
+#pragma unroll 1
+    for (int k = 0; k < NB; ++k) {
+      load_blk(min(k + 1, NB - 1), nxt);   // the next block's keys go out first
+      // the scale and offset pairs of keys 4 lg + e come from lanes 4 lg + e
+      uint32_t ks[4], vs[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float ksc, kof;
-      so_unpack(ks[e], ksc, kof);
-      const int key = c * ATT_CH + wave * 16 + 4 * lg + e;
-      sc[e] = key < n ? (ksc * KD_2P24) * acc[e] + kof * qsum : -__builtin_inff();
-      mx = fmaxf(mx, sc[e]);
-    }
-    {
-      float r0, r1;
-      pl16(mx, mx, r0, r1);
-      mx = fmaxf(r0, r1);
-      pl32(mx, mx, r0, r1);
-      mx = fmaxf(r0, r1);
-    }
-    // every chunk is a segment of its own: the wave's state starts here
-    f16x4 pb;
-    float ls = 0.f, ws = 0.f;
+      for (int e = 0; e < 4; ++e) {
+        ks[e] = __shfl(cur.ks, 4 * lg + e, 64);
+        vs[e] = __shfl(cur.vs, 4 * lg + e, 64);
+      }
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float p = sc[e] == -__builtin_inff() ? 0.f : exp2f(sc[e] - mx);
-      float vsc, vof;
-      so_unpack(vs[e], vsc, vof);
-      ls += p;
-      ws += p * vof;
-      pb[e] = (_Float16)(p * vsc);
-    }
-    {
-      float r0, r1;
-      pl16(ls, ls, r0, r1);
-      ls = r0 + r1;
-      pl32(ls, ls, r0, r1);
-      ls = r0 + r1;
-      pl16(ws, ws, r0, r1);
-      ws = r0 + r1;
-      pl32(ws, ws, r0, r1);
-      ws = r0 + r1;
-    }
-    // even nibbles (dims 8 lr + 2m) and odd nibbles (8 lr + 2m + 1) per key
-    uint32_t ev[4], od[4];
+      for (int kb = 0; kb < 4; ++kb) {
+        const f16x8 kk = nib8_f16(cur.k[kb]);
+        acc = mfma_f16(kk, qh[kb], acc);
+        acc = mfma_f16(kk, ql[kb], acc);
+      }
+      // lane (lr, lg): acc[e] = q_rot[lr] . codes[key 4 lg + e] * 2^-24
+      float sc[4], mx = -__builtin_inff();
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      ev[e] = cur.v[e] & 0x0F0F0F0Fu;
-      od[e] = (cur.v[e] >> 4) & 0x0F0F0F0Fu;
-    }
-    f32x4 oa[8];
+      for (int e = 0; e < 4; ++e) {
+        float ksc, kof;
+        so_unpack(ks[e], ksc, kof);
+        const int key = c * ATT_CH + 16 * k + 4 * lg + e;
+        sc[e] = key < n ? (ksc * KD_2P24) * acc[e] + kof * qsum : -__builtin_inff();
+        mx = fmaxf(mx, sc[e]);
+      }
+      {
+        float r0, r1;
+        pl16(mx, mx, r0, r1);
+        mx = fmaxf(r0, r1);
+        pl32(mx, mx, r0, r1);
+        mx = fmaxf(r0, r1);
+      }
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_run == -__builtin_inff() ? 0.f : exp2f(m_run - m_new);
+      f16x4 pb;
+      float ls = 0.f, ws = 0.f;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) oa[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int e = 0; e < 4; ++e) {
+        const float pe = sc[e] == -__builtin_inff() ? 0.f : exp2f(sc[e] - m_new);
+        float vsc, vof;
+        so_unpack(vs[e], vsc, vof);
+        ls += pe;
+        ws += pe * vof;
+        pb[e] = (_Float16)(pe * vsc);
+      }
+      {
+        float r0, r1;
+        pl16(ls, ls, r0, r1);
+        ls = r0 + r1;
+        pl32(ls, ls, r0, r1);
+        ls = r0 + r1;
+        pl16(ws, ws, r0, r1);
+        ws = r0 + r1;
+        pl32(ws, ws, r0, r1);
+        ws = r0 + r1;
+      }
+      l_run = l_run * alpha + ls;
+      m_run = m_new;
+      // even nibbles (dims 8 lr + 2m) and odd nibbles (8 lr + 2m + 1) per key
+      uint32_t ev[4], od[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ev[e] = cur.v[e] & 0x0F0F0F0Fu;
+        od[e] = (cur.v[e] >> 4) & 0x0F0F0F0Fu;
+      }
+      f32x4 oa[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) oa[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #define KD_PV_TILE(T, X, M)                                                    \
   {                                                                            \
     const f16x2 lo = byte_pair_f16<M>(X[0], X[1]);                             \
     const f16x2 hi = byte_pair_f16<M>(X[2], X[3]);                             \
     oa[T] = mfma_16x16x16_f16(f16x4{lo.x, lo.y, hi.x, hi.y}, pb, oa[T]);       \
   }
-    KD_PV_TILE(0, ev, 0)
-    KD_PV_TILE(1, od, 0)
-    KD_PV_TILE(2, ev, 1)
-    KD_PV_TILE(3, od, 1)
-    KD_PV_TILE(4, ev, 2)
-    KD_PV_TILE(5, od, 2)
-    KD_PV_TILE(6, ev, 3)
-    KD_PV_TILE(7, od, 3)
+      KD_PV_TILE(0, ev, 0)
+      KD_PV_TILE(1, od, 0)
+      KD_PV_TILE(2, ev, 1)
+      KD_PV_TILE(3, od, 1)
+      KD_PV_TILE(4, ev, 2)
+      KD_PV_TILE(5, od, 2)
+      KD_PV_TILE(6, ev, 3)
+      KD_PV_TILE(7, od, 3)
 #undef KD_PV_TILE
-    // the previous chunk's readers of the shared LDS areas are done (a new
-    // pair's query read above waited for them already)
-    if (!new_pair) lds_sync();
-    // lane (lr < 4, lg) holds dims 32 lg + 8 e + t of row lr, times 2^-24
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[t][e] = o[t][e] * alpha + (oa[t][e] * KD_2P24 + ws);
+      cur = nxt;
+    }
+    // the chunk's partial at its slot: lanes (lr < 4, lg) store row lr's
+    // dims 32 lg + 8 e .. + 8; lane (lr, 0) its max and sum
+    const size_t pb = ((size_t)(b * NH + h) * nch + c) * 4;
     if (lr < BLK) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float v[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) v[t] = oa[t][e] * KD_2P24 + ws;
-        lds_f dst = s_o + (wave * 4 + lr) * DH + 32 * lg + 8 * e;
-        *reinterpret_cast<KD_LDS f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
-        *reinterpret_cast<KD_LDS f32x4*>(dst + 4) = f32x4{v[4], v[5], v[6], v[7]};
+        gptr<float> dst = s.ao[l] + (pb + lr) * DH + 32 * lg + 8 * e;
+        att_store4(dst, f32x4{o[0][e], o[1][e], o[2][e], o[3][e]});
+        att_store4(dst + 4, f32x4{o[4][e], o[5][e], o[6][e], o[7][e]});
       }
-      if (lg == 0) att_write_ml((unsigned)(uintptr_t)(s_m + wave * 4 + lr), mx, ls);
+      if (lg == 0) {
+        att_store(s.am[l] + pb + lr, m_run);
+        att_store(s.al[l] + pb + lr, l_run);
+      }
     }
-    lds_sync();
-    chunk_partial_store(a, l, b, h, c, s_m, s_o);
-    cur = nxt;
+    // counted once the stores are acknowledged; the wave that counts the
+    // pair's last chunk merges the pair and resets its counter
+    __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0)
+    auto cnt = &s.att_cnt[((l * SB_MAX + b) * NH + h) * 32];
+    unsigned before = 0;
+    if (lane == 0) before = add_rlx(cnt, 1u);
+    before = (unsigned)__builtin_amdgcn_readlane((int)before, 0);
+    if (before + 1 == (unsigned)sl.chunks(b)) {
+      if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      attn_merge_wave(a, l, b, h, n);
+    }
   }
-  attn_finish(a, l, sl, ub, ue, br, sy, sync);
-  trace_mark(a, sy, 6);
+  trace_mark(a, sy, 3);
+  // pairs of streams with no visible context attend to the block only
+  const int nbh = a.B * NH;
+  if (wg < nbh && wave_s == 0 && sl.vis(wg / NH) == 0) attn_merge_wave(a, l, wg / NH, wg % NH, 0);
   trace_mark(a, sy, 4);
 }
 
