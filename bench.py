@@ -161,9 +161,18 @@ def cpu_baseline(model, inp, gpu_logits=None, gpu_ids=None, max_seconds=20.0, ma
     return base, parity
 
 
-def run_workload(kdraft, synth, torch, drafter, model, cfg, steps, warmup, kv_fmt, head, keep=False):
+# the cold-cache variant sweeps (reads and writes) this many float32 values
+# before each step: 1 GiB, four times the 256 MB last-level cache (MALL) of
+# MI355X, so the step finds neither its weights nor its cache rows in L2 or MALL
+COLD_FLUSH_ELEMS = 1 << 28
+
+
+def run_workload(kdraft, synth, torch, drafter, model, cfg, steps, warmup, kv_fmt, head, keep=False,
+                 cold_steps=0):
     """Times `steps` rounds of one workload after `warmup`: HIP events around
     the whole timed region (ms per step) and around each step (p10/p50/p90).
+    cold_steps: afterwards, time that many steps one by one, each after a
+    sweep over a 1 GiB buffer (events around the step only).
     keep: also return the inputs, for a parity round outside the timed region."""
     dims = synth.FULL
     inp = synth.make_inputs(cfg, dims, device="cuda", vocab=model["vocab"], kv=kv_fmt)
@@ -200,6 +209,21 @@ def run_workload(kdraft, synth, torch, drafter, model, cfg, steps, warmup, kv_fm
     q = lambda f: per[min(len(per) - 1, int(f * len(per)))]
     res = dict(B=B, ms=ms, p10=q(0.1), p50=q(0.5), p90=q(0.9), wall=wall, lens=lens_host,
                ingest=n_ingest, path=drafter.last_path())
+    if cold_steps:
+        flush = torch.zeros(COLD_FLUSH_ELEMS, dtype=torch.float32, device="cuda")
+        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(cold_steps)]
+        for e0, e1 in cev:
+            flush.add_(1.0)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        cper = sorted(e0.elapsed_time(e1) for e0, e1 in cev)
+        cq = lambda f: cper[min(len(cper) - 1, int(f * len(cper)))]
+        res["cold"] = dict(steps=cold_steps, p10=cq(0.1), p50=cq(0.5), p90=cq(0.9),
+                           flush_bytes_per_step=2 * 4 * COLD_FLUSH_ELEMS)
+        del flush
     if keep:
         res["inp"], res["kv"] = inp, kv
     else:
@@ -220,6 +244,8 @@ def main():
                     help="time only this workload (index into the five); default: the 4-stream "
                          "workload as the headline, then every workload in the configs list")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=30,
+                    help="steps of the headline workload timed one by one after a 1 GiB cache sweep (0: none)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB 5 times and "
                          "exit: the calibration kernel for HBM byte counters")
@@ -279,7 +305,7 @@ def main():
     cfg = synth.CONFIGS[head_i]
     drafter, model = drafter_for(cfg["model"])
     r = run_workload(kdraft, synth, torch, drafter, model, cfg, args.steps, args.warmup, args.kv, args.head,
-                     keep=not args.no_cpu_baseline)
+                     keep=not args.no_cpu_baseline, cold_steps=args.cold_steps)
     B, ms, path = r["B"], r["ms"], r["path"]
     ab = algorithmic_bytes(dims, r["lens"], B, r["ingest"], args.kv, args.head, args.body)
     rounds_s = 1000.0 / ms
@@ -318,6 +344,13 @@ def main():
            "draft_tokens_per_s": round(4 * B * rounds_s, 1),
            "bytes_per_round": ab, "hbm_roofline_frac": round(achieved / HBM_PEAK_GBS, 4),
            "wall_s": round(r["wall"], 3), "roofline": roofline}
+    if "cold" in r:
+        c = r["cold"]
+        out["cold_cache"] = {"note": "each step after a read-write sweep of 1 GiB (L2 and the 256 MB MALL "
+                                     "evicted); HIP events around the step only",
+                             "steps": c["steps"], "ms_p10": round(c["p10"], 4), "ms_p50": round(c["p50"], 4),
+                             "ms_p90": round(c["p90"], 4),
+                             "hbm_roofline_frac_p50": round(ab["total"] / (c["p50"] * 1e-3) / (HBM_PEAK_GBS * 1e9), 4)}
 
     # the parity round of the headline workload (outside the timed region)
     gpu_logits = gpu_ids = None
